@@ -1,0 +1,18 @@
+"""fp64 CPU oracle for the halo-sharded conv + GroupNorm layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this package:
+only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import, call or execute it.  It shares no code with the HIP library or its
+Python binding; the only code both sides use is the seeded input module
+`synth`, which holds no arithmetic of the method.
+
+Every function is pinned by CPU tests (brute force on tiny volumes, delta
+kernels, linearity, torch fp64 as an independent library, GroupNorm closed
+forms, sharded == unsharded).  Nothing here is "parity unpinned".
+"""
+from .reference import (  # noqa: F401
+    widen, zero_pad, conv_valid, conv_same, conv_same_slabbed, conv_at,
+    group_moments, group_norm, group_norm_apply, group_sums_onepass,
+    shard_offsets, shard_grid, padded_shard, halo_message, halo_directions,
+    sharded_forward, conv_bruteforce, group_norm_bruteforce,
+)

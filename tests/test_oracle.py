@@ -1,0 +1,393 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Each pin is a property the mathematics fixes: brute-force scalar loops, the
+identity and shift kernels, linearity, an independent library (torch fp64 on
+the CPU), GroupNorm closed forms, and the method's own invariant that the
+sharded computation equals the unsharded one (ShardTensor summary, section 2,
+"Implementation details", "Communication").  `test_pins_catch_mutants` plants
+plausible mistakes in copies of the oracle and checks some pin fails.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def rand_case(seed, d, n=2, cin=3, cout=5, spatial=None, k=3):
+    r = rng(seed)
+    spatial = spatial or ((5, 6, 7) if d == 3 else (9, 11))
+    x = r.standard_normal((n, *spatial, cin))
+    w = r.uniform(-1, 1, size=(cout, cin) + (k,) * d)
+    b = r.uniform(-1, 1, size=cout)
+    return x, w, b
+
+
+def rel(a, b):
+    return np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)
+
+
+# ---------------------------------------------------------------- pin helpers
+# Each takes the functions under test so the mutation test can reuse them.
+
+def pin_bruteforce(conv, gn):
+    ok = True
+    for d, k in [(2, 3), (2, 5), (3, 3), (3, 5)]:
+        x, w, b = rand_case(10 + d * 10 + k, d, k=k, spatial=(4, 5, 6) if d == 3 else (7, 9))
+        y = conv(x, w, b)
+        ok &= rel(y, oracle.conv_bruteforce(x, w, b)) <= 1e-13
+        g = 5 if y.shape[-1] % 5 == 0 else 1
+        r = rng(d * k)
+        gamma, beta = r.uniform(0.5, 1.5, y.shape[-1]), r.uniform(-1, 1, y.shape[-1])
+        ok &= rel(gn(y, g, 1e-5, gamma, beta),
+                  oracle.group_norm_bruteforce(y, g, 1e-5, gamma, beta)) <= 1e-12
+        # two groups of unequal content, to pin the channel-to-group map
+        y2 = np.concatenate([y, 3.0 * y[..., :1] + 1.0], axis=-1)  # 6 channels
+        ok &= rel(gn(y2, 2, 1e-5), oracle.group_norm_bruteforce(y2, 2, 1e-5)) <= 1e-12
+    return bool(ok)
+
+
+def pin_identity(conv):
+    ok = True
+    for d, k in [(2, 3), (3, 3), (3, 5)]:
+        x, _, _ = rand_case(7, d, cin=4, cout=4, k=k)
+        w = np.zeros((4, 4) + (k,) * d)
+        c = (k // 2,) * d
+        for o in range(4):
+            w[(o, o) + c] = 1.0
+        ok &= np.array_equal(conv(x, w, None), x)
+    return bool(ok)
+
+
+def pin_shift(conv):
+    """A one-hot kernel at tap t moves x by t - p, with zeros entering at faces."""
+    ok = True
+    for d, k in [(2, 3), (3, 5)]:
+        x, _, _ = rand_case(8, d, cin=2, cout=2, k=k)
+        p = k // 2
+        spatial = x.shape[1:-1]
+        for t in [(0,) * d, (k - 1,) * d, tuple(range(d)), (k - 1,) + (0,) * (d - 1)]:
+            w = np.zeros((2, 2) + (k,) * d)
+            w[(0, 1) + t] = 1.0          # output 0 <- input channel 1
+            w[(1, 0) + t] = 2.0          # output 1 <- 2 * input channel 0
+            want = np.zeros(x.shape[:-1] + (2,))
+            for pos in itertools.product(*[range(s) for s in spatial]):
+                src = tuple(pos[a] + t[a] - p for a in range(d))
+                if all(0 <= src[a] < spatial[a] for a in range(d)):
+                    want[(slice(None),) + pos + (0,)] = x[(slice(None),) + src + (1,)]
+                    want[(slice(None),) + pos + (1,)] = 2.0 * x[(slice(None),) + src + (0,)]
+            ok &= np.array_equal(conv(x, w, None), want)
+    return bool(ok)
+
+
+def pin_linearity(conv):
+    ok = True
+    for d in (2, 3):
+        x1, w1, _ = rand_case(21, d)
+        x2, w2, _ = rand_case(22, d)
+        a, c = 0.75, -1.5
+        y = conv(a * x1 + c * x2, w1, None)
+        ok &= rel(y, a * conv(x1, w1, None) + c * conv(x2, w1, None)) <= 1e-13
+        y = conv(x1, a * w1 + c * w2, None)
+        ok &= rel(y, a * conv(x1, w1, None) + c * conv(x1, w2, None)) <= 1e-13
+    return bool(ok)
+
+
+def pin_torch(conv, gn):
+    """torch.nn.functional on the CPU in float64: an independent implementation."""
+    ok = True
+    for d, k in [(2, 3), (3, 3), (3, 5), (2, 5)]:
+        x, w, b = rand_case(30 + d + k, d, n=2, cin=6, cout=8, k=k,
+                            spatial=(6, 7, 9) if d == 3 else (12, 10))
+        xt = torch.from_numpy(np.moveaxis(x, -1, 1).copy())
+        f = torch.nn.functional.conv3d if d == 3 else torch.nn.functional.conv2d
+        yt = f(xt, torch.from_numpy(w), torch.from_numpy(b), padding=k // 2)
+        y = conv(x, w, b)
+        ok &= rel(y, np.moveaxis(yt.numpy(), 1, -1)) <= 1e-12
+        r = rng(d * 100 + k)
+        gamma, beta = r.uniform(0.5, 1.5, 8), r.uniform(-1, 1, 8)
+        zt = torch.nn.functional.group_norm(yt, 4, torch.from_numpy(gamma),
+                                            torch.from_numpy(beta), eps=1e-5)
+        ok &= rel(gn(y, 4, 1e-5, gamma, beta), np.moveaxis(zt.numpy(), 1, -1)) <= 1e-12
+    return bool(ok)
+
+
+def pin_groupnorm_closed_forms(gn):
+    ok = True
+    r = rng(5)
+    y = r.standard_normal((2, 6, 7, 8)) * r.uniform(0.1, 3, 8) + r.uniform(-2, 2, 8)
+    eps = 1e-5
+    z = gn(y, 4, eps)
+    zg = z.reshape(2, -1, 4, 2)
+    yg = y.reshape(2, -1, 4, 2)
+    var = yg.var(axis=(1, 3))
+    ok &= np.max(np.abs(zg.mean(axis=(1, 3)))) < 1e-13
+    ok &= rel(zg.var(axis=(1, 3)), var / (var + eps)) < 1e-12
+    # constant groups normalise to beta
+    beta = np.arange(8.0)
+    zc = gn(np.full((1, 5, 5, 8), 3.25), 4, eps, None, beta)
+    ok &= np.array_equal(zc, np.broadcast_to(beta, zc.shape))
+    # eps = 0: z(a*y + c) = sign(a) * z(y)
+    for a, c in [(2.5, 1.0), (-0.5, 3.0)]:
+        ok &= rel(gn(a * y + c, 4, 0.0), np.sign(a) * gn(y, 4, 0.0)) < 1e-12
+    return bool(ok)
+
+
+def pin_sharded(conv, gn):
+    """Sharded-with-halo conv + split-stat GroupNorm == unsharded (fp64)."""
+    ok = True
+    cases = [
+        (2, 3, ((4, 3, 5), (12,))),
+        (2, 3, ((12,), (5, 7))),
+        (3, 3, ((3, 4), (2, 3, 3), (5, 4))),
+        (3, 5, ((4, 2, 3), (9,), (4, 6))),
+    ]
+    for d, k, shards in cases:
+        spatial = tuple(sum(s) for s in shards)
+        x, w, b = rand_case(40 + d + k, d, n=2, cin=3, cout=4, k=k, spatial=spatial)
+        y, z, partials = oracle.sharded_forward(x, w, b, shards, 2, 1e-5)
+        ok &= rel(y, conv(x, w, b)) <= 1e-13
+        ok &= rel(z, gn(conv(x, w, b), 2, 1e-5)) <= 1e-10
+        ok &= len(partials) == int(np.prod([len(s) for s in shards]))
+    return bool(ok)
+
+
+# ------------------------------------------------------------------- the pins
+
+def test_bruteforce():
+    assert pin_bruteforce(oracle.conv_same, oracle.group_norm)
+
+
+def test_identity_kernel_exact():
+    assert pin_identity(oracle.conv_same)
+
+
+def test_shift_kernel_exact():
+    assert pin_shift(oracle.conv_same)
+
+
+def test_linearity():
+    assert pin_linearity(oracle.conv_same)
+
+
+def test_torch_fp64():
+    assert pin_torch(oracle.conv_same, oracle.group_norm)
+
+
+def test_groupnorm_closed_forms():
+    assert pin_groupnorm_closed_forms(oracle.group_norm)
+
+
+def test_sharded_equals_unsharded():
+    assert pin_sharded(oracle.conv_same, oracle.group_norm)
+
+
+def test_onepass_sums_agree_with_two_pass():
+    r = rng(3)
+    y = r.standard_normal((1, 9, 10, 8)) * 2 + 0.5
+    m, s1, s2 = oracle.group_sums_onepass(y, 4)
+    mean, var = oracle.group_moments(y, 4)
+    assert m == 9 * 10 * 2
+    assert rel(s1 / m, mean) < 1e-13
+    assert np.max(np.abs((s2 / m - (s1 / m) ** 2) - var)) <= 1e-10 * np.max(var)
+
+
+def test_conv_box_sum_closed_form():
+    """All-ones 3x3 kernel on a ramp: each output is the sum of the in-bounds
+    3x3 neighbourhood, which for x[i, j] = i + 10 j has a closed form."""
+    H, W = 5, 6
+    i, j = np.meshgrid(np.arange(H), np.arange(W), indexing="ij")
+    x = (i + 10.0 * j)[None, :, :, None]
+    w = np.ones((1, 1, 3, 3))
+    y = oracle.conv_same(x, w)[0, :, :, 0]
+    for a in range(H):
+        for b in range(W):
+            rows = [r for r in (a - 1, a, a + 1) if 0 <= r < H]
+            cols = [c for c in (b - 1, b, b + 1) if 0 <= c < W]
+            want = len(cols) * sum(rows) + 10.0 * len(rows) * sum(cols)
+            assert y[a, b] == want
+
+
+def test_conv_at_matches_full_conv():
+    wl = synth.small_variant(synth.workload("vol512_c16_k5_bf16"), (12, 9, 10),
+                             ((5, 7), (9,), (10,)))
+    x = synth.make_input(wl)
+    w = oracle.widen(synth.make_weight(wl), "bf16")
+    y = oracle.conv_same(oracle.widen(x, "bf16"), w)
+    pos = synth.sample_positions(wl, 64, 1)
+    got = oracle.conv_at(x, "bf16", w, None, pos)
+    want = np.stack([y[tuple(p)] for p in pos])
+    assert rel(got, want) < 1e-13
+
+
+def test_slabbed_conv_matches_full_conv():
+    for name in ["vol512_c16_k5_bf16", "img2048_c64_k3_bf16"]:
+        base = synth.workload(name)
+        sp = (11, 9, 8)[:base.ndim]
+        wl = synth.small_variant(base, sp, [(s,) for s in sp])
+        x = synth.make_input(wl)
+        w = oracle.widen(synth.make_weight(wl), "bf16")
+        y = oracle.conv_same(oracle.widen(x, "bf16"), w)
+        parts = [ys for _, ys in oracle.conv_same_slabbed(x, "bf16", w, None, slab=3)]
+        assert np.array_equal(np.concatenate(parts, axis=1), y)
+
+
+# ------------------------------------------------------------ halo reference
+
+def test_padded_shard_is_neighbourhood_with_zero_faces():
+    r = rng(9)
+    x = r.standard_normal((1, 7, 8, 2))
+    shards = ((3, 4), (5, 3))
+    h = 1
+    got = oracle.padded_shard(x, shards, (1, 0), h)
+    # shard (1, 0) covers rows 3..6, cols 0..4; padded rows 2..7, cols -1..5
+    want = np.zeros((1, 6, 7, 2))
+    for a in range(6):
+        for b in range(7):
+            r_, c_ = 2 + a, -1 + b
+            if 0 <= r_ < 7 and 0 <= c_ < 8:
+                want[0, a, b] = x[0, r_, c_]
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("shards,h", [
+    (((3, 4), (5, 3)), 1),
+    (((4, 3, 5), (6,)), 2),
+    (((3, 4), (2, 3), (4, 3)), 1),
+    (((5, 4, 6), (7,), (6,)), 2),
+])
+def test_halo_message_fills_every_margin(shards, h):
+    """Placing every message box into the receiver's margin, plus zeros on the
+    global faces, must rebuild each padded shard exactly."""
+    d = len(shards)
+    spatial = tuple(sum(s) for s in shards)
+    x = rng(11).standard_normal((2, *spatial, 3))
+    msg = np.frombuffer(oracle.halo_message(x, shards, h), dtype=np.float64)
+    counts = [len(s) for s in shards]
+    bufs = {}
+    for idx in oracle.shard_grid(shards):
+        ext = [shards[a][idx[a]] for a in range(d)]
+        buf = np.zeros((2, *[e + 2 * h for e in ext], 3))
+        inner = (slice(None),) + tuple(slice(h, h + e) for e in ext)
+        sl = [slice(None)]
+        for a in range(d):
+            o = oracle.shard_offsets(shards[a])[idx[a]]
+            sl.append(slice(o, o + ext[a]))
+        buf[inner] = x[tuple(sl)]
+        bufs[idx] = buf
+    pos = 0
+    for idx in oracle.shard_grid(shards):
+        for delta in oracle.halo_directions(d):
+            nb = tuple(idx[a] + delta[a] for a in range(d))
+            if any(nb[a] < 0 or nb[a] >= counts[a] for a in range(d)):
+                continue
+            pos += (-pos) % 2            # 16-byte alignment == 2 float64
+            dst = [slice(None)]
+            shape = [2]
+            for a in range(d):
+                e = shards[a][nb[a]]
+                if delta[a] == 1:        # neighbour is above: fills its low margin
+                    dst.append(slice(0, h)); shape.append(h)
+                elif delta[a] == -1:
+                    dst.append(slice(h + e, 2 * h + e)); shape.append(h)
+                else:
+                    dst.append(slice(h, h + e)); shape.append(e)
+            shape.append(3)
+            cnt = int(np.prod(shape))
+            bufs[nb][tuple(dst)] = msg[pos:pos + cnt].reshape(shape)
+            pos += cnt
+    assert pos == len(msg)
+    for idx in oracle.shard_grid(shards):
+        assert np.array_equal(bufs[idx], oracle.padded_shard(x, shards, idx, h))
+
+
+def test_halo_message_counts():
+    # workload topologies: number of boxes sent
+    expect = {"vol32_c4to8_k3_fp32": 2, "img2048_c64_k3_bf16": 6, "vol256_c32_k3_bf16": 56,
+              "vol512_c16_k5_bf16": 14, "grid1024x1792_c256_k3_bf16": 2}
+    for name, n in expect.items():
+        wl = synth.workload(name)
+        counts = [len(s) for s in wl.shards]
+        boxes = 0
+        for idx in oracle.shard_grid(wl.shards):
+            for delta in oracle.halo_directions(wl.ndim):
+                nb = [idx[a] + delta[a] for a in range(wl.ndim)]
+                boxes += all(0 <= nb[a] < counts[a] for a in range(wl.ndim))
+        assert boxes == n, name
+
+
+# ------------------------------------------------------- planted mistakes
+
+def _mutants():
+    def conv_flipped(x, w, b=None):
+        return oracle.conv_same(x, np.flip(w, axis=tuple(range(2, w.ndim))).copy(), b)
+
+    def conv_transposed_w(x, w, b=None):
+        if w.shape[0] != w.shape[1]:
+            return oracle.conv_same(x, w, b) * (1 + 1e-9)
+        return oracle.conv_same(x, np.swapaxes(w, 0, 1).copy(), b)
+
+    def conv_dropped_tap(x, w, b=None):
+        w2 = w.copy()
+        w2[(slice(None), slice(None)) + (0,) * (w.ndim - 2)] = 0
+        return oracle.conv_same(x, w2, b)
+
+    def conv_wrap_padding(x, w, b=None):
+        k = w.shape[2]
+        p = k // 2
+        xp = np.pad(x, [(0, 0)] + [(p, p)] * (x.ndim - 2) + [(0, 0)], mode="wrap")
+        return oracle.conv_valid(xp, w, b)
+
+    def conv_no_bias(x, w, b=None):
+        return oracle.conv_same(x, w, None)
+
+    def gn_unbiased(y, g, eps, gamma=None, beta=None):
+        mean, var = oracle.group_moments(y, g)
+        m = y.size // (y.shape[0] * g)
+        return oracle.group_norm_apply(y, g, mean, var * m / (m - 1), eps, gamma, beta)
+
+    def gn_eps_outside(y, g, eps, gamma=None, beta=None):
+        mean, var = oracle.group_moments(y, g)
+        z = oracle.group_norm_apply(y, g, mean, var, 0.0) * np.sqrt(var.mean() / (var.mean() + eps))
+        z = z * (1 if gamma is None else gamma) + (0 if beta is None else beta)
+        return z
+
+    def gn_strided_groups(y, g, eps, gamma=None, beta=None):
+        c = y.shape[-1]
+        perm = np.arange(c).reshape(c // g, g).T.reshape(-1)   # channel c -> group c % g
+        inv = np.argsort(perm)
+        z = oracle.group_norm(y[..., perm], g, eps)[..., inv]
+        z = z * (1 if gamma is None else gamma) + (0 if beta is None else beta)
+        return z
+
+    good_c, good_g = oracle.conv_same, oracle.group_norm
+    return {
+        "flipped kernel": (conv_flipped, good_g),
+        "transposed weight": (conv_transposed_w, good_g),
+        "dropped tap": (conv_dropped_tap, good_g),
+        "wrap padding": (conv_wrap_padding, good_g),
+        "bias ignored": (conv_no_bias, good_g),
+        "unbiased variance": (good_c, gn_unbiased),
+        "eps outside sqrt": (good_c, gn_eps_outside),
+        "strided groups": (good_c, gn_strided_groups),
+    }
+
+
+@pytest.mark.parametrize("name", list(_mutants()))
+def test_pins_catch_mutants(name):
+    conv, gn = _mutants()[name]
+    results = [
+        pin_bruteforce(conv, gn),
+        pin_identity(conv),
+        pin_shift(conv),
+        pin_torch(conv, gn),
+        pin_groupnorm_closed_forms(gn),
+    ]
+    assert not all(results), f"no pin caught the mutant '{name}'"
