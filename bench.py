@@ -1,0 +1,181 @@
+"""Throughput of the halo-sharded conv + GroupNorm layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = halo pack + halo unpack + per-shard conv (all shards, one grouped
+launch) + GroupNorm (partials, combine, apply) over the whole sharded volume,
+inputs already resident in HBM.  Prints one JSON line.  Each library call of
+the timed steps is bracketed with HIP events on the stream it runs on, giving
+per-kernel average durations; the longest one is reported in `roofline`
+against its algorithmic bytes (or flops) per launch.  The CPU baseline is the
+fp64 oracle timed on a bounded slab of the same workload on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sharded conv+GroupNorm voxels/s on 1 MI355X; % MFMA peak (conv), % HBM BW (halo/norm)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 (256 CU x 2.4 GHz x 4096 flop/clk)
+FP32_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the oracle's CPU sample")
+    return ap.parse_args()
+
+
+def algorithmic(wl, layer):
+    """Algorithmic HBM bytes and flops per launch of each stage."""
+    import numpy as np
+    esize = 4 if wl.dtype == "f32" else 2
+    vox = wl.voxels
+    x_bytes = vox * wl.cin * esize
+    y_bytes = vox * wl.cout * 4
+    payload = layer.in_plan.msg_bytes
+    return {
+        "halo_pack": {"bytes": 2 * payload},                 # read boxes, write message
+        "halo_unpack": {"bytes": 2 * payload},               # read message, write margins
+        "conv": {"bytes": x_bytes + y_bytes, "flops": wl.conv_flops},
+        "gn_partials": {"bytes": y_bytes},
+        "gn_combine": {"bytes": 0},
+        "gn_apply": {"bytes": 2 * y_bytes},
+    }
+
+
+def cpu_baseline(wl, rows):
+    """The oracle (fp64 numpy) on the first `rows` rows of the outermost axis."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import synth
+
+    sub_shape = (rows,) + tuple(wl.spatial[1:])
+    sub = synth.small_variant(wl, sub_shape, [(s,) for s in sub_shape], name_suffix="cpu_sample")
+    x = synth.make_input(sub)
+    w = oracle.widen(synth.make_weight(wl), wl.dtype)
+    t0 = time.perf_counter()
+    y = oracle.conv_same(oracle.widen(x, wl.dtype), w)
+    z = oracle.group_norm(y, wl.groups, wl.eps)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": sub.voxels / dt, "unit": "voxels/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} rows of the outermost axis ({sub.voxels} voxels, conv + GroupNorm in fp64 "
+                      f"numpy, {dt:.1f} s)", "seconds": round(dt, 2), "checksum": float(np.abs(z).sum())}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    from halo_sharded_conv_amd.layer import ShardedConvGN
+
+    name = args.workload or synth.BENCH_WORKLOAD
+    wl = synth.workload(name)
+    layer = ShardedConvGN(wl)
+    layer.set_weight(synth.make_weight(wl))
+    layer.load_input(synth.make_input(wl))
+    stream = torch.cuda.current_stream()
+
+    stages = [("halo_pack", lambda: layer.exchange_pack()), ("halo_unpack", lambda: layer.exchange_unpack()),
+              ("conv", layer.conv), ("gn_partials", layer.norm_partials), ("gn_combine", layer.norm_combine),
+              ("gn_apply", layer.norm_apply)]
+
+    for _ in range(args.warmup):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+
+    ev = {k: [] for k, _ in stages}
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        for k, fn in stages:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev[k].append((a, b))
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(end) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    per_kernel_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+
+    alg = algorithmic(wl, layer)
+    kernels = {}
+    for k, ms in per_kernel_ms.items():
+        rec = {"ms": round(ms, 5)}
+        if alg[k].get("bytes"):
+            rec["GB/s"] = round(alg[k]["bytes"] / (ms * 1e-3) / 1e9, 1)
+            rec["hbm_frac"] = round(rec["GB/s"] / HBM_PEAK_GBS, 4)
+        if alg[k].get("flops"):
+            peak = FP32_PEAK_TFLOPS if wl.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
+            rec["TFLOP/s"] = round(alg[k]["flops"] / (ms * 1e-3) / 1e12, 2)
+            rec["mfma_frac"] = round(rec["TFLOP/s"] / peak, 4)
+        kernels[k] = rec
+
+    dom = max(per_kernel_ms, key=per_kernel_ms.get)
+    ms = per_kernel_ms[dom]
+    if dom == "conv":
+        conv_ai = alg["conv"]["flops"] / alg["conv"]["bytes"]
+        peak_t = FP32_PEAK_TFLOPS if wl.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
+        ridge = peak_t * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if conv_ai < ridge:
+            roof = {"bound": "hbm", "achieved": kernels["conv"]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        else:
+            roof = {"bound": "mfma", "achieved": kernels["conv"]["TFLOP/s"], "peak": peak_t, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": kernels[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dom
+    roof["traffic"] = None
+
+    out = {
+        "metric": METRIC,
+        "value": wl.voxels / (ms_per_step * 1e-3),
+        "unit": "voxels/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "shape": [wl.batch, wl.cin, *wl.spatial], "cout": wl.cout,
+                   "kernel": wl.ksize, "shards": [list(s) for s in wl.shards], "halo": wl.halo,
+                   "groups": wl.groups, "accumulate": "f32", "outputs": "f32"},
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        rows = args.cpu_rows or max(1, min(wl.spatial[0], int(5.0e5 // (wl.voxels // wl.spatial[0]) + 1)))
+        out["cpu_baseline"] = cpu_baseline(wl, rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

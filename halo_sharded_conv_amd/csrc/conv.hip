@@ -1,0 +1,722 @@
+// Per-shard convolution on halo-padded chunks (one grouped launch).
+//
+// "Technical summary: ShardTensor - domain parallelism for scientific machine
+// learning", section 2, "Implementation details", "Communication": once the
+// halo is in place a shard's convolution output equals the matching slice of
+// the unsharded one.  The pages do not define the convolution; it is the
+// PyTorch one (ShardTensor extends PyTorch's DTensor, section 2):
+// cross-correlation, stride 1, dilation 1, zero 'same' padding, bias.
+//
+// bf16 path: implicit GEMM on the gfx950 matrix cores,
+//   M = output channels (A = packed weights, from LDS)
+//   N = output positions (B = input cells, from an LDS-staged halo box)
+//   K = kernel taps x input channels,
+// with v_mfma_f32_16x16x32_bf16 and fp32 accumulation.  A workgroup owns a
+// box of TD x TH x TW output positions (64 per wave, 16 per MFMA column
+// block, each 16-run along W) and BN output channels; its input box
+// (TD+k-1) x (TH+k-1) x (TW+k-1) x CK is staged once per channel chunk and
+// every tap reads a shifted window of it.  Each output accumulates its
+// K-steps in one fixed order (taps lexicographic, channels ascending), so its
+// bits do not depend on which tile, shard or plan it belongs to.
+// Workgroups are persistent; tiles are dealt out so that the 32 workgroups of
+// one XCD work on neighbouring tiles and share halo rows in that XCD's L2.
+//
+// fp32 path (and bf16 shapes without a matrix-core instance): a direct
+// kernel, one thread per output position, fp32 FMA in the same fixed order.
+//
+// Epilogue: optional bias, fp32 store, and max |y| per (n, group) via
+// integer atomicMax on the float bits (order-free).
+#include <algorithm>
+
+#include "internal.h"
+
+namespace st {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct ConvShardArg {
+  const uint16_t* in;    // padded input, [N][Pd][Ph][Pw][Cin] (bf16 bits or f32 via cast)
+  float* out;            // [N][Ed][Eh][Ew][Cout]
+  int32_t tile_begin;
+  int32_t tiles_d, tiles_h, tiles_w;
+  int32_t ext[3];
+  int32_t pad[3];
+};
+
+struct ConvArgs {
+  int32_t nshards;
+  int32_t total_tiles;
+  int32_t groups;
+  int32_t origin[3];          // halo - ksize/2 per axis
+  const uint16_t* w;          // packed weights
+  const float* bias;          // or null
+  uint32_t* ymax;             // or null
+  ConvShardArg sh[ST_MAX_SHARDS];
+};
+
+__global__ void fill_u32(uint32_t* __restrict__ p, uint32_t v, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// --------------------------------------------------------------------------
+// matrix-core implicit GEMM
+// --------------------------------------------------------------------------
+
+template <int NDIM_, int CIN_, int COUT_, int KS_, int TD_, int TH_, int TW_, int BN_, int CK_, int WN_>
+struct Cfg {
+  static constexpr int NDIM = NDIM_, CIN = CIN_, COUT = COUT_, KS = KS_;
+  static constexpr int TD = TD_, TH = TH_, TW = TW_, BN = BN_, CK = CK_, WN = WN_;
+  static constexpr int KD = NDIM == 3 ? KS : 1;
+  static constexpr int TAPS = KD * KS * KS;
+  static constexpr int BOX_D = TD + KD - 1, BOX_H = TH + KS - 1, BOX_W = TW + KS - 1;
+  static constexpr int BOX = BOX_D * BOX_H * BOX_W;
+  static constexpr int POS = TD * TH * TW;
+  static constexpr int WP = POS / 64;
+  static constexpr int NWAVES = WP * WN;
+  static constexpr int NT = NWAVES * 64;
+  static constexpr int NW = BN / WN;
+  static constexpr int MB = NW / 16;
+  static constexpr int NB = 4;
+  static constexpr int KV = TAPS * CK;
+  static constexpr int KSTEPS = (KV + 31) / 32;
+  // K-steps unrolled per iteration of the K loop: all of them when few,
+  // otherwise the largest divisor <= 9 (bounds register pressure)
+  static constexpr int KU = KSTEPS <= 18 ? KSTEPS
+                            : KSTEPS % 9 == 0 ? 9 : KSTEPS % 7 == 0 ? 7 : KSTEPS % 5 == 0 ? 5
+                            : KSTEPS % 3 == 0 ? 3 : KSTEPS % 2 == 0 ? 2 : 1;
+  static constexpr int KVP = (KV + 63) / 64 * 64;
+  static constexpr int NCH = CK / 8;
+  static constexpr int KEYDIV = NCH >= 8 ? 1 : 8 / NCH;
+  static constexpr int NCHUNK = CIN / CK;
+  static constexpr int NCB = COUT / BN;
+  static constexpr bool RESIDENT = NCHUNK == 1 && NCB == 1;
+  static constexpr int LDS_W = BN * KVP * 2;
+  static constexpr int LDS_X = BOX * CK * 2;
+  static_assert(NDIM == 3 || TD == 1, "2D tiles have depth 1");
+  static_assert(POS % 64 == 0 && TW % 16 == 0, "a wave covers 64 positions in 16-runs along W");
+  static_assert(BN % WN == 0 && NW % 16 == 0 && COUT % BN == 0, "cout blocking");
+  static_assert(CK % 8 == 0 && CIN % CK == 0 && (CK >= 32 ? CK % 32 == 0 : 32 % CK == 0), "channel chunks");
+  static_assert(LDS_W + LDS_X + BN * 4 <= 160 * 1024, "LDS budget");
+  static_assert(NT <= 1024, "block size");
+};
+
+// swizzled LDS element index of 16-byte chunk j of input-box cell q
+template <class C>
+__device__ __forceinline__ int xoff(int q, int j) {
+  return q * C::CK + 8 * (j ^ ((q / C::KEYDIV) % C::NCH));
+}
+
+template <class C>
+__device__ __forceinline__ void stage_w(uint16_t* sw, const uint16_t* __restrict__ w, int cc, int cb) {
+  constexpr int CPR = C::KVP / 8;
+  const uint16_t* src = w + ((size_t)cc * C::COUT + (size_t)cb * C::BN) * C::KVP;
+  for (int i = threadIdx.x; i < C::BN * CPR; i += C::NT) {
+    const int m = i / CPR, j = i - m * CPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)m * C::KVP + 8 * j);
+    *reinterpret_cast<uint4*>(sw + m * C::KVP + 8 * (j ^ (m & 7))) = v;
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void stage_x(uint16_t* sx, const ConvShardArg& sh, const int* origin,
+                                        int n, int d0, int h0, int w0, int cc) {
+  const int pd = sh.pad[0], ph = sh.pad[1], pw = sh.pad[2];
+  for (int i = threadIdx.x; i < C::BOX * C::NCH; i += C::NT) {
+    const int q = i / C::NCH, j = i - q * C::NCH;
+    const int qw = q % C::BOX_W;
+    const int qh = (q / C::BOX_W) % C::BOX_H;
+    const int qd = q / (C::BOX_W * C::BOX_H);
+    const int gd = d0 + qd + origin[0], gh = h0 + qh + origin[1], gw = w0 + qw + origin[2];
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (gd < pd && gh < ph && gw < pw) {
+      const size_t cell = (((size_t)n * pd + gd) * ph + gh) * pw + gw;
+      v = *reinterpret_cast<const uint4*>(sh.in + cell * C::CIN + cc * C::CK + 8 * j);
+    }
+    *reinterpret_cast<uint4*>(sx + xoff<C>(q, j)) = v;
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void conv_mfma(const ConvArgs args) {
+  __shared__ __attribute__((aligned(16))) uint16_t sw[C::LDS_W / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t sx[C::LDS_X / 2];
+  __shared__ uint32_t smax[C::BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wp = wave % C::WP;
+  const int wn = wave / C::WP;
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+  const bool want_max = args.ymax != nullptr;
+
+  for (int i = tid; i < C::BN; i += C::NT) smax[i] = 0u;
+
+  // per-lane geometry of the B operand: cell of each 16-run in the box
+  int qbase[C::NB];
+  int pdd[C::NB], phh[C::NB], pww[C::NB];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) {
+    const int p = wp * 64 + nb * 16 + l16;
+    pww[nb] = p % C::TW;
+    phh[nb] = (p / C::TW) % C::TH;
+    pdd[nb] = p / (C::TW * C::TH);
+    qbase[nb] = (pdd[nb] * C::BOX_H + phh[nb]) * C::BOX_W + pww[nb];
+  }
+
+  // persistent tile loop, XCD-aware: XCD x (= block % 8) takes a contiguous
+  // eighth of the tiles and its workgroups walk it side by side.
+  const int total = args.total_tiles;
+  int t0 = blockIdx.x, tstride = gridDim.x, t_end = total;
+  if (gridDim.x >= 8 && (gridDim.x & 7) == 0) {
+    const int xcd = blockIdx.x & 7;
+    t0 = (int)((int64_t)total * xcd / 8) + (blockIdx.x >> 3);
+    tstride = gridDim.x >> 3;
+    t_end = (int)((int64_t)total * (xcd + 1) / 8);
+  }
+
+  if (C::RESIDENT) stage_w<C>(sw, args.w, 0, 0);
+
+  float runmax[C::MB][4];
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) runmax[mb][i] = 0.f;
+  int cur_key = -1, cur_n = 0, cur_cb = 0;
+
+  auto flush = [&](int n, int cb) {
+    // max over the 16 lanes that share output channels
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = runmax[mb][i];
+        v = fmaxf(v, __shfl_xor(v, 1));
+        v = fmaxf(v, __shfl_xor(v, 2));
+        v = fmaxf(v, __shfl_xor(v, 4));
+        v = fmaxf(v, __shfl_xor(v, 8));
+        runmax[mb][i] = v;
+      }
+    __syncthreads();
+    if (l16 == 0) {
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          atomicMax(&smax[wn * C::NW + mb * 16 + 4 * g4 + i], __float_as_uint(runmax[mb][i]));
+    }
+    __syncthreads();
+    const int gs = C::COUT / args.groups;
+    const int c_lo = cb * C::BN;
+    const int g_lo = c_lo / gs, g_hi = (c_lo + C::BN - 1) / gs;
+    for (int g = g_lo + tid; g <= g_hi; g += C::NT) {
+      uint32_t m = 0;
+      const int a = max(g * gs, c_lo), b = min((g + 1) * gs, c_lo + C::BN);
+      for (int c = a; c < b; ++c) m = max(m, smax[c - c_lo]);
+      atomicMax(&args.ymax[n * args.groups + g], m);
+    }
+    __syncthreads();
+    for (int i = tid; i < C::BN; i += C::NT) smax[i] = 0u;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) runmax[mb][i] = 0.f;
+  };
+
+  for (int t = t0; t < t_end; t += tstride) {
+    // decode tile -> shard, n, spatial tile, cout block (innermost)
+    int s = 0;
+    while (s + 1 < args.nshards && args.sh[s + 1].tile_begin <= t) ++s;
+    const ConvShardArg& sh = args.sh[s];
+    const int tiles_sp = sh.tiles_d * sh.tiles_h * sh.tiles_w;
+    int r = t - sh.tile_begin;
+    const int cb = r % C::NCB;
+    r /= C::NCB;
+    const int n = r / tiles_sp;
+    r -= n * tiles_sp;
+    const int td = r / (sh.tiles_h * sh.tiles_w);
+    r -= td * sh.tiles_h * sh.tiles_w;
+    const int th = r / sh.tiles_w;
+    const int tw = r - th * sh.tiles_w;
+    const int d0 = td * C::TD, h0 = th * C::TH, w0 = tw * C::TW;
+
+    if (want_max) {
+      const int key = n * C::NCB + cb;
+      if (key != cur_key) {
+        if (cur_key >= 0) flush(cur_n, cur_cb);
+        cur_key = key;
+        cur_n = n;
+        cur_cb = cb;
+      }
+    }
+
+    f32x4 acc[C::MB][C::NB];
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int cc = 0; cc < C::NCHUNK; ++cc) {
+      __syncthreads();
+      if (!C::RESIDENT) stage_w<C>(sw, args.w, cc, cb);
+      stage_x<C>(sx, sh, args.origin, n, d0, h0, w0, cc);
+      __syncthreads();
+
+#pragma unroll 1
+      for (int ko = 0; ko < C::KSTEPS; ko += C::KU)
+#pragma unroll
+      for (int ki = 0; ki < C::KU; ++ki) {
+        const int ks = ko + ki;
+        const int vk = 32 * ks + 8 * g4;
+        const int tap = vk / C::CK;
+        const int c0 = vk - tap * C::CK;
+        const bool valid = tap < C::TAPS;
+        const int kw = tap % C::KS;
+        const int kh = (tap / C::KS) % C::KS;
+        const int kd = tap / (C::KS * C::KS);
+        const int qtap = (kd * C::BOX_H + kh) * C::BOX_W + kw;
+        bf16x8 a[C::MB], b[C::NB];
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) {
+          const int m = wn * C::NW + mb * 16 + l16;
+          a[mb] = *reinterpret_cast<const bf16x8*>(sw + m * C::KVP + 8 * ((4 * ks + g4) ^ (lane & 7)));
+        }
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+          const int q = qbase[nb] + qtap;
+          if (valid) b[nb] = *reinterpret_cast<const bf16x8*>(sx + xoff<C>(q, c0 >> 3));
+          else b[nb] = bf16x8{};
+        }
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+      }
+    }
+
+    // epilogue: lane holds rows (channels) 4*g4..+3 of column (position) l16
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+      const int od = d0 + pdd[nb], oh = h0 + phh[nb], ow = w0 + pww[nb];
+      if (od >= sh.ext[0] || oh >= sh.ext[1] || ow >= sh.ext[2]) continue;
+      const size_t cell = (((size_t)n * sh.ext[0] + od) * sh.ext[1] + oh) * sh.ext[2] + ow;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        const int co = cb * C::BN + wn * C::NW + mb * 16 + 4 * g4;
+        f32x4 v = acc[mb][nb];
+        if (args.bias) {
+          v[0] += args.bias[co + 0];
+          v[1] += args.bias[co + 1];
+          v[2] += args.bias[co + 2];
+          v[3] += args.bias[co + 3];
+        }
+        *reinterpret_cast<f32x4*>(sh.out + cell * C::COUT + co) = v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) runmax[mb][i] = fmaxf(runmax[mb][i], fabsf(v[i]));
+      }
+    }
+  }
+  if (want_max && cur_key >= 0) flush(cur_n, cur_cb);
+}
+
+// --------------------------------------------------------------------------
+// direct kernel (fp32 operands, or bf16 shapes without a matrix-core instance)
+// --------------------------------------------------------------------------
+
+struct DirectShardArg {
+  const void* in;
+  float* out;
+  int64_t pos_begin;        // first output position (over N and space) of this shard
+  int32_t ext[3];
+  int32_t pad[3];
+};
+
+struct DirectArgs {
+  int32_t nshards, cin, cout, ks, taps, groups;
+  int32_t origin[3];
+  int64_t total_pos;
+  const void* w;            // [Cout][taps][Cin]
+  const float* bias;
+  uint32_t* ymax;
+  DirectShardArg sh[ST_MAX_SHARDS];
+};
+
+__device__ __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float ld(const uint16_t* p, size_t i) {
+  return __uint_as_float(((uint32_t)p[i]) << 16);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void conv_direct(const DirectArgs a) {
+  extern __shared__ uint32_t dmax[];   // cout entries
+  const int tid = threadIdx.x;
+  for (int i = tid; i < a.cout; i += 256) dmax[i] = 0u;
+  __syncthreads();
+  const int64_t gid = (int64_t)blockIdx.x * 256 + tid;
+  // shard lookup is uniform per block only when a block does not straddle
+  // shards, so it is done per thread
+  if (gid < a.total_pos) {
+    int s = 0;
+    while (s + 1 < a.nshards && a.sh[s + 1].pos_begin <= gid) ++s;
+    const DirectShardArg& sh = a.sh[s];
+    int64_t r = gid - sh.pos_begin;
+    const int64_t per_n = (int64_t)sh.ext[0] * sh.ext[1] * sh.ext[2];
+    const int n = (int)(r / per_n);
+    r -= n * per_n;
+    const int od = (int)(r / ((int64_t)sh.ext[1] * sh.ext[2]));
+    r -= (int64_t)od * sh.ext[1] * sh.ext[2];
+    const int oh = (int)(r / sh.ext[2]);
+    const int ow = (int)(r - (int64_t)oh * sh.ext[2]);
+    const T* in = static_cast<const T*>(sh.in);
+    const T* w = static_cast<const T*>(a.w);
+    const int kd_n = a.taps / (a.ks * a.ks);
+    const size_t cell_out = (((size_t)n * sh.ext[0] + od) * sh.ext[1] + oh) * sh.ext[2] + ow;
+    for (int o0 = 0; o0 < a.cout; o0 += 8) {
+      float acc[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+      for (int kd = 0; kd < kd_n; ++kd)
+        for (int kh = 0; kh < a.ks; ++kh)
+          for (int kw = 0; kw < a.ks; ++kw) {
+            const int t = (kd * a.ks + kh) * a.ks + kw;
+            const size_t cell = (((size_t)n * sh.pad[0] + od + kd + a.origin[0]) * sh.pad[1] +
+                                 oh + kh + a.origin[1]) * sh.pad[2] + ow + kw + a.origin[2];
+            for (int c = 0; c < a.cin; ++c) {
+              const float xv = ld(in, cell * a.cin + c);
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                if (o0 + j < a.cout)
+                  acc[j] = fmaf(ld(w, ((size_t)(o0 + j) * a.taps + t) * a.cin + c), xv, acc[j]);
+            }
+          }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (o0 + j >= a.cout) break;
+        float v = acc[j];
+        if (a.bias) v += a.bias[o0 + j];
+        sh.out[cell_out * a.cout + o0 + j] = v;
+        if (a.ymax) atomicMax(&dmax[o0 + j], __float_as_uint(fabsf(v)));
+      }
+    }
+  }
+  if (!a.ymax) return;
+  __syncthreads();
+  // one atomic per (block, group); the block may straddle two batch items or
+  // shards, so the batch index is resolved per position run below
+  const int64_t first = (int64_t)blockIdx.x * 256;
+  const int64_t last = min(first + 256, a.total_pos) - 1;
+  // batch item of the first and last position of the block
+  auto batch_of = [&](int64_t g) {
+    int s = 0;
+    while (s + 1 < a.nshards && a.sh[s + 1].pos_begin <= g) ++s;
+    const int64_t per_n = (int64_t)a.sh[s].ext[0] * a.sh[s].ext[1] * a.sh[s].ext[2];
+    return (int)((g - a.sh[s].pos_begin) / per_n);
+  };
+  const int n0 = batch_of(first), n1 = batch_of(last);
+  const int gs = a.cout / a.groups;
+  if (n0 == n1) {
+    for (int g = tid; g < a.groups; g += 256) {
+      uint32_t m = 0;
+      for (int c = g * gs; c < (g + 1) * gs; ++c) m = max(m, dmax[c]);
+      atomicMax(&a.ymax[n0 * a.groups + g], m);
+    }
+  }
+  if (n0 != n1) {
+    // rare (a block spanning two batch items): attribute each position
+    // directly
+    __syncthreads();
+    if (gid < a.total_pos) {
+      const int n = batch_of(gid);
+      int s = 0;
+      while (s + 1 < a.nshards && a.sh[s + 1].pos_begin <= gid) ++s;
+      const int64_t per_n = (int64_t)a.sh[s].ext[0] * a.sh[s].ext[1] * a.sh[s].ext[2];
+      const int64_t r = gid - a.sh[s].pos_begin - (int64_t)n * per_n;
+      const float* y = a.sh[s].out + (((size_t)n * per_n) + r) * a.cout;
+      for (int c = 0; c < a.cout; ++c)
+        atomicMax(&a.ymax[n * a.groups + c / gs], __float_as_uint(fabsf(y[c])));
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// weight packing
+// --------------------------------------------------------------------------
+
+// [Cout][Cin][taps] -> [Cin/CK][Cout][KVP], k index = tap*CK + (cin % CK)
+__global__ void pack_w_mfma(const uint16_t* __restrict__ w, uint16_t* __restrict__ out, int cin,
+                            int cout, int taps, int ck, int kvp, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int vk = (int)(i % kvp);
+  const int64_t r = i / kvp;
+  const int o = (int)(r % cout);
+  const int cc = (int)(r / cout);
+  uint16_t v = 0;
+  if (vk < taps * ck) {
+    const int t = vk / ck, c = cc * ck + vk % ck;
+    v = w[((int64_t)o * cin + c) * taps + t];
+  }
+  out[i] = v;
+}
+
+// [Cout][Cin][taps] -> [Cout][taps][Cin]
+template <typename T>
+__global__ void pack_w_direct(const T* __restrict__ w, T* __restrict__ out, int cin, int cout,
+                              int taps, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int c = (int)(i % cin);
+  const int t = (int)((i / cin) % taps);
+  const int o = (int)(i / ((int64_t)cin * taps));
+  out[i] = w[((int64_t)o * cin + c) * taps + t];
+}
+
+// --------------------------------------------------------------------------
+// instance table
+// --------------------------------------------------------------------------
+
+struct Instance {
+  int ndim, cin, cout, ks;
+  int ck, kvp, nt;
+  int td, th, tw, ncb;
+  int lds;
+  st_status (*run)(ConvArgs&, const st_plan*, hipStream_t);
+};
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus[dev] = prop.multiProcessorCount;
+    else cus[dev] = 256;
+  }
+  return cus[dev];
+}
+
+template <class C>
+st_status run_mfma(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
+  int tiles = 0;
+  for (size_t s = 0; s < in_plan->shards.size(); ++s) {
+    const Shard& sd = in_plan->shards[s];
+    ConvShardArg& sh = a.sh[s];
+    sh.tiles_d = (int)((sd.ext[0] + C::TD - 1) / C::TD);
+    sh.tiles_h = (int)((sd.ext[1] + C::TH - 1) / C::TH);
+    sh.tiles_w = (int)((sd.ext[2] + C::TW - 1) / C::TW);
+    sh.tile_begin = tiles;
+    const int64_t t = (int64_t)in_plan->batch * sh.tiles_d * sh.tiles_h * sh.tiles_w * C::NCB;
+    if ((int64_t)tiles + t > INT32_MAX) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: too many tiles");
+    tiles += (int)t;
+  }
+  a.total_tiles = tiles;
+  if (tiles == 0) return ST_OK;
+  int occ = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, conv_mfma<C>, C::NT, 0) != hipSuccess || occ < 1)
+    occ = 1;
+  int grid = std::min(tiles, device_cus() * occ);
+  if (grid >= 8) grid &= ~7;
+  hipLaunchKernelGGL(conv_mfma<C>, dim3(grid), dim3(C::NT), 0, stream, a);
+  return launch_check("st_conv_sharded: conv_mfma launch");
+}
+
+template <class C>
+constexpr Instance inst() {
+  return Instance{C::NDIM, C::CIN, C::COUT, C::KS, C::CK, C::KVP, C::NT,
+                  C::TD, C::TH, C::TW, C::NCB, C::LDS_W + C::LDS_X, &run_mfma<C>};
+}
+
+// 2D 64->64 k3: one 8x64 output box per workgroup, weights resident in LDS
+using CfgImg64 = Cfg<2, 64, 64, 3, 1, 8, 64, 64, 64, 1>;
+// 3D 32->32 k3: 2x8x32 box, weights resident
+using CfgVol32 = Cfg<3, 32, 32, 3, 2, 8, 32, 32, 32, 1>;
+// 3D 16->16 k5: 4x4x32 box, weights resident, two taps per K-step
+using CfgVol16k5 = Cfg<3, 16, 16, 5, 4, 4, 32, 16, 16, 1>;
+// 2D 256->256 k3: 2x128 box, 128 output channels per block, 32-channel chunks
+using CfgImg256 = Cfg<2, 256, 256, 3, 1, 2, 128, 128, 32, 2>;
+
+const Instance kInstances[] = {
+    inst<CfgImg64>(),
+    inst<CfgVol32>(),
+    inst<CfgVol16k5>(),
+    inst<CfgImg256>(),
+};
+
+const Instance* find_instance(int ndim, int cin, int cout, int ks) {
+  for (const Instance& i : kInstances)
+    if (i.ndim == ndim && i.cin == cin && i.cout == cout && i.ks == ks) return &i;
+  return nullptr;
+}
+
+int64_t taps_of(int ndim, int ks) { return ndim == 3 ? (int64_t)ks * ks * ks : (int64_t)ks * ks; }
+
+}  // namespace
+}  // namespace st
+
+using namespace st;
+
+extern "C" {
+
+size_t st_conv_weight_bytes(int32_t ndim, int32_t cin, int32_t cout, int32_t ksize, st_dtype dtype) {
+  if ((ndim != 2 && ndim != 3) || cin < 1 || cout < 1 || ksize < 1 || ksize % 2 == 0) return 0;
+  if (dtype != ST_F32 && dtype != ST_BF16) return 0;
+  const int64_t taps = taps_of(ndim, ksize);
+  if (dtype == ST_BF16) {
+    if (const Instance* i = find_instance(ndim, cin, cout, ksize))
+      return (size_t)(cin / i->ck) * cout * i->kvp * 2;
+    return (size_t)cout * taps * cin * 2;
+  }
+  return (size_t)cout * taps * cin * 4;
+}
+
+st_status st_conv_pack_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t ksize,
+                               st_dtype dtype, const void* weight, void* packed, void* stream) {
+  const size_t bytes = st_conv_weight_bytes(ndim, cin, cout, ksize, dtype);
+  if (bytes == 0) return fail(ST_ERR_UNSUPPORTED, "st_conv_pack_weights: unsupported ndim/ksize/dtype");
+  if (!weight || !packed) return fail(ST_ERR_INVALID_ARG, "st_conv_pack_weights: NULL pointer");
+  if (!aligned16(weight) || !aligned16(packed))
+    return fail(ST_ERR_ALIGNMENT, "st_conv_pack_weights: pointers must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int taps = (int)taps_of(ndim, ksize);
+  if (dtype == ST_BF16) {
+    if (const Instance* i = find_instance(ndim, cin, cout, ksize)) {
+      const int64_t total = (int64_t)(cin / i->ck) * cout * i->kvp;
+      hipLaunchKernelGGL(pack_w_mfma, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                         static_cast<const uint16_t*>(weight), static_cast<uint16_t*>(packed), cin, cout,
+                         taps, i->ck, i->kvp, total);
+      return launch_check("st_conv_pack_weights: launch");
+    }
+    const int64_t total = (int64_t)cout * taps * cin;
+    hipLaunchKernelGGL(pack_w_direct<uint16_t>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(weight), static_cast<uint16_t*>(packed), cin, cout, taps,
+                       total);
+    return launch_check("st_conv_pack_weights: launch");
+  }
+  const int64_t total = (int64_t)cout * taps * cin;
+  hipLaunchKernelGGL(pack_w_direct<float>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const float*>(weight), static_cast<float*>(packed), cin, cout, taps, total);
+  return launch_check("st_conv_pack_weights: launch");
+}
+
+st_status st_conv_sharded(const st_plan* in_plan, const void* const* in_bufs,
+                          const void* packed_weight, const float* bias_or_null,
+                          int32_t cout, int32_t ksize, const st_plan* out_plan,
+                          float* const* y_bufs, uint32_t* ymax_or_null, int32_t groups,
+                          void* stream) {
+  if (!in_plan || !out_plan || !in_bufs || !y_bufs || !packed_weight)
+    return fail(ST_ERR_INVALID_ARG, "st_conv_sharded: NULL argument");
+  if (ksize < 1 || ksize % 2 == 0) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: kernel size must be odd");
+  if (cout < 1) return fail(ST_ERR_INVALID_ARG, "st_conv_sharded: cout < 1");
+  const int ndim = in_plan->ndim;
+  // geometry checks: same shards, halo wide enough, output plan fp32 halo 0
+  if (out_plan->ndim != ndim || out_plan->batch != in_plan->batch ||
+      out_plan->shards.size() != in_plan->shards.size())
+    return fail(ST_ERR_BAD_SHAPE, "st_conv_sharded: output plan does not match the input plan");
+  if (out_plan->dtype != ST_F32 || out_plan->channels != cout)
+    return fail(ST_ERR_BAD_SHAPE, "st_conv_sharded: output plan must be fp32 with C = cout");
+  for (int a = 0; a < kAxes; ++a) {
+    if (out_plan->halo[a] != 0) return fail(ST_ERR_BAD_SHAPE, "st_conv_sharded: output plan must have halo 0");
+    if (out_plan->sizes[a] != in_plan->sizes[a])
+      return fail(ST_ERR_BAD_SHAPE, "st_conv_sharded: output shard sizes differ from the input's");
+    const bool real = a >= kAxes - ndim;
+    if (real && in_plan->halo[a] < ksize / 2)
+      return fail(ST_ERR_BAD_SHAPE, "st_conv_sharded: input halo narrower than ksize/2");
+  }
+  if (ymax_or_null) {
+    if (groups < 1 || cout % groups != 0)
+      return fail(ST_ERR_INVALID_ARG, "st_conv_sharded: groups must divide cout");
+  }
+  if (!aligned16(packed_weight) || (bias_or_null && !aligned16(bias_or_null)) ||
+      (ymax_or_null && (reinterpret_cast<uintptr_t>(ymax_or_null) & 3)))
+    return fail(ST_ERR_ALIGNMENT, "st_conv_sharded: misaligned weight/bias/ymax");
+  for (size_t s = 0; s < in_plan->shards.size(); ++s) {
+    if (!in_bufs[s] || !y_bufs[s]) return fail(ST_ERR_INVALID_ARG, "st_conv_sharded: NULL shard buffer");
+    if (!aligned16(in_bufs[s]) || !aligned16(y_bufs[s]))
+      return fail(ST_ERR_ALIGNMENT, "st_conv_sharded: shard buffers must be 16-byte aligned");
+  }
+  for (size_t s = 0; s < in_plan->shards.size(); ++s)
+    for (int a = 0; a < kAxes; ++a)
+      if (in_plan->shards[s].pad[a] > INT32_MAX / 2)
+        return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: extent too large");
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int cin = (int)in_plan->channels;
+  if (ymax_or_null) {
+    const int n = (int)(in_plan->batch * groups);
+    hipLaunchKernelGGL(fill_u32, dim3((n + 255) / 256), dim3(256), 0, st, ymax_or_null, 0u, n);
+    st_status s = launch_check("st_conv_sharded: ymax clear");
+    if (s != ST_OK) return s;
+  }
+
+  const Instance* inst =
+      in_plan->dtype == ST_BF16 ? find_instance(ndim, cin, cout, ksize) : nullptr;
+  if (inst) {
+    ConvArgs a{};
+    a.nshards = (int)in_plan->shards.size();
+    a.groups = groups;
+    for (int ax = 0; ax < kAxes; ++ax) {
+      const bool real = ax >= kAxes - ndim;
+      a.origin[ax] = real ? in_plan->halo[ax] - ksize / 2 : 0;
+    }
+    a.w = static_cast<const uint16_t*>(packed_weight);
+    a.bias = bias_or_null;
+    a.ymax = ymax_or_null;
+    for (size_t s = 0; s < in_plan->shards.size(); ++s) {
+      const Shard& sd = in_plan->shards[s];
+      ConvShardArg& sh = a.sh[s];
+      sh.in = static_cast<const uint16_t*>(in_bufs[s]);
+      sh.out = y_bufs[s];
+      for (int ax = 0; ax < kAxes; ++ax) {
+        sh.ext[ax] = (int)sd.ext[ax];
+        sh.pad[ax] = (int)sd.pad[ax];
+      }
+    }
+    return inst->run(a, in_plan, st);
+  }
+
+  DirectArgs a{};
+  a.nshards = (int)in_plan->shards.size();
+  a.cin = cin;
+  a.cout = cout;
+  a.ks = ksize;
+  a.taps = (int)taps_of(ndim, ksize);
+  a.groups = ymax_or_null ? groups : 1;
+  for (int ax = 0; ax < kAxes; ++ax) {
+    const bool real = ax >= kAxes - ndim;
+    a.origin[ax] = real ? in_plan->halo[ax] - ksize / 2 : 0;
+  }
+  a.w = packed_weight;
+  a.bias = bias_or_null;
+  a.ymax = ymax_or_null;
+  int64_t pos = 0;
+  for (size_t s = 0; s < in_plan->shards.size(); ++s) {
+    const Shard& sd = in_plan->shards[s];
+    DirectShardArg& sh = a.sh[s];
+    sh.in = in_bufs[s];
+    sh.out = y_bufs[s];
+    sh.pos_begin = pos;
+    for (int ax = 0; ax < kAxes; ++ax) {
+      sh.ext[ax] = (int)sd.ext[ax];
+      sh.pad[ax] = (int)sd.pad[ax];
+    }
+    pos += in_plan->batch * sd.ext[0] * sd.ext[1] * sd.ext[2];
+  }
+  a.total_pos = pos;
+  if (pos == 0) return ST_OK;
+  const int64_t blocks = (pos + 255) / 256;
+  if (blocks > INT32_MAX) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: volume too large for the direct kernel");
+  const size_t shmem = (size_t)cout * 4;
+  if (shmem > 64 * 1024) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: cout too large for the direct kernel");
+  if (in_plan->dtype == ST_F32)
+    hipLaunchKernelGGL(conv_direct<float>, dim3((unsigned)blocks), dim3(256), shmem, st, a);
+  else
+    hipLaunchKernelGGL(conv_direct<uint16_t>, dim3((unsigned)blocks), dim3(256), shmem, st, a);
+  return launch_check("st_conv_sharded: conv_direct launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,525 @@
+// Split-statistics GroupNorm over all shards.
+//
+// "Technical summary: ShardTensor - domain parallelism for scientific machine
+// learning", section 2, "Implementation details", "Communication":
+// normalisation stays consistent with the unsharded model because per-chunk
+// statistics are combined with a collective (all-reduce).  On one GPU the
+// all-reduce is the combine kernel below, summing the per-shard partials in
+// HBM.  GroupNorm itself (contiguous channel groups, biased variance, eps
+// inside the square root, per-channel affine) is the standard definition;
+// the pages only say "normalisation".
+//
+// Exact statistics.  For a group with element count M (over all shards) and
+// m = max |y|, let L be the bit length of M and e the exponent with
+// 2^(e-1) <= m < 2^e.  Each element contributes
+//     q1 = rint(y   * 2^(52 - L - e))       |q1| <= 2^(52-L)
+//     q2 = rint(y^2 * 2^(52 - L - 2e))      |q2| <= 2^(52-L)
+// so every partial sum of at most M terms is an integer of magnitude below
+// 2^52.  fp64 adds such integers exactly, in any order and grouping, so the
+// per-shard partials, their combine and the final (mean, rstd) are the same
+// bits for every shard plan.  y^2 of an fp32 value is exact in fp64.
+//
+// Kernels (all HBM-streaming over y, float4 per lane):
+//   gn_fill    zero the partial sums (and the max scratch)
+//   gn_max     max |y| per (n, group)   (only when the conv did not fuse it)
+//   gn_stats   per-shard sum q1, sum q2 per (n, group)
+//   gn_combine sum over shards; mean, var, rstd in fp64 -> fp32
+//   gn_apply   z = (y - mean_g) * (rstd_g * gamma_c) + beta_c
+#include <algorithm>
+
+#include "internal.h"
+
+namespace st {
+namespace {
+
+constexpr int kNT = 256;        // threads per block
+constexpr int kIter = 16;       // vectors per thread per item
+
+struct GnShard {
+  const float* y;
+  float* z;
+  int64_t vecs_per_n;           // vectors in one batch item of this shard
+  int32_t item_begin;           // first item of this shard
+  int32_t items_per_n;
+};
+
+struct GnArgs {
+  int32_t nshards, batch, channels, groups;
+  int32_t total_items;
+  int32_t lbits;                // bit length of the per-group element count M
+  double m_count;               // M (exact in fp64)
+  double eps;
+  double* partials;             // [S][N][G][2]
+  float* stats;                 // [N][G][2]
+  int32_t* scales;              // [N][G][2]
+  uint32_t* ymax;               // [N][G]
+  float4* chan;                 // [N][C] (mean, scale, beta, 0)
+  const float* gamma;
+  const float* beta;
+  GnShard sh[ST_MAX_SHARDS];
+};
+
+template <int VW> struct Vec;
+template <> struct Vec<4> {
+  using T = float4;
+  static __device__ __forceinline__ float get(const T& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+  }
+};
+template <> struct Vec<1> {
+  using T = float;
+  static __device__ __forceinline__ float get(const T& v, int) { return v; }
+};
+
+__device__ __forceinline__ void decode_item(const GnArgs& a, int item, int& s, int& n, int& k) {
+  s = 0;
+  while (s + 1 < a.nshards && a.sh[s + 1].item_begin <= item) ++s;
+  const int r = item - a.sh[s].item_begin;
+  n = r / a.sh[s].items_per_n;
+  k = r - n * a.sh[s].items_per_n;
+}
+
+// exponents (e1, e2) of a group from its max |y| (bits)
+__device__ __forceinline__ void group_scales(uint32_t mbits, int lbits, int& e1, int& e2) {
+  const float m = __uint_as_float(mbits);
+  if (!(m > 0.f)) { e1 = 0; e2 = 0; return; }
+  int e;
+  (void)frexpf(m, &e);            // m = f * 2^e, f in [0.5, 1)
+  e1 = 52 - lbits - e;
+  e2 = 52 - lbits - 2 * e;
+}
+
+__global__ void gn_fill(uint32_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+template <int VW, bool FIXED>
+__global__ __launch_bounds__(kNT) void gn_max(const GnArgs a) {
+  using V = Vec<VW>;
+  __shared__ uint32_t smax[1024];
+  const int tid = threadIdx.x;
+  const int C = a.channels;
+  for (int i = tid; i < C; i += kNT) smax[i] = 0u;
+  float mx[VW];
+#pragma unroll
+  for (int j = 0; j < VW; ++j) mx[j] = 0.f;
+  int cur = -1, cur_n = 0;
+  auto flush = [&](int n) {
+    __syncthreads();
+    if (FIXED) {
+      const int c0 = (tid * VW) % C;
+#pragma unroll
+      for (int j = 0; j < VW; ++j) atomicMax(&smax[c0 + j], __float_as_uint(mx[j]));
+    }
+    __syncthreads();
+    const int gs = C / a.groups;
+    for (int g = tid; g < a.groups; g += kNT) {
+      uint32_t m = 0;
+      for (int c = g * gs; c < (g + 1) * gs; ++c) m = max(m, smax[c]);
+      atomicMax(&a.ymax[n * a.groups + g], m);
+    }
+    __syncthreads();
+    for (int i = tid; i < C; i += kNT) smax[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < VW; ++j) mx[j] = 0.f;
+  };
+  for (int item = blockIdx.x; item < a.total_items; item += gridDim.x) {
+    int s, n, k;
+    decode_item(a, item, s, n, k);
+    const int key = s * a.batch + n;
+    if (key != cur) {
+      if (cur >= 0) flush(cur_n);
+      cur = key;
+      cur_n = n;
+    }
+    const GnShard& sh = a.sh[s];
+    const typename V::T* y = reinterpret_cast<const typename V::T*>(sh.y) + n * sh.vecs_per_n;
+    const int64_t v0 = (int64_t)k * kNT * kIter;
+#pragma unroll 4
+    for (int i = 0; i < kIter; ++i) {
+      const int64_t v = v0 + i * kNT + tid;
+      if (v >= sh.vecs_per_n) break;
+      const typename V::T val = y[v];
+#pragma unroll
+      for (int j = 0; j < VW; ++j) {
+        const float f = fabsf(V::get(val, j));
+        if (FIXED) mx[j] = fmaxf(mx[j], f);
+        else atomicMax(&smax[(int)((v * VW + j) % C)], __float_as_uint(f));
+      }
+    }
+  }
+  if (cur >= 0) flush(cur_n);
+}
+
+template <int VW, bool FIXED>
+__global__ __launch_bounds__(kNT) void gn_stats(const GnArgs a) {
+  using V = Vec<VW>;
+  __shared__ double s1[1024];
+  __shared__ double s2[1024];
+  __shared__ double sc1[1024];   // 2^e1 per channel of the current batch item
+  __shared__ double sc2[1024];
+  const int tid = threadIdx.x;
+  const int C = a.channels;
+  const int gs = C / a.groups;
+  if (blockIdx.x == 0) {
+    for (int i = tid; i < a.batch * a.groups; i += kNT) {
+      int e1, e2;
+      group_scales(a.ymax[i], a.lbits, e1, e2);
+      a.scales[2 * i + 0] = e1;
+      a.scales[2 * i + 1] = e2;
+    }
+  }
+  for (int i = tid; i < C; i += kNT) { s1[i] = 0.0; s2[i] = 0.0; }
+  double acc1[VW], acc2[VW];
+#pragma unroll
+  for (int j = 0; j < VW; ++j) { acc1[j] = 0.0; acc2[j] = 0.0; }
+  int cur = -1, cur_s = 0, cur_n = 0;
+  double f1[VW], f2[VW];
+  auto flush = [&](int s, int n) {
+    __syncthreads();
+    if (FIXED) {
+      const int c0 = (tid * VW) % C;
+#pragma unroll
+      for (int j = 0; j < VW; ++j) {
+        atomicAdd(&s1[c0 + j], acc1[j]);
+        atomicAdd(&s2[c0 + j], acc2[j]);
+      }
+    }
+    __syncthreads();
+    for (int g = tid; g < a.groups; g += kNT) {
+      double t1 = 0.0, t2 = 0.0;
+      for (int c = g * gs; c < (g + 1) * gs; ++c) { t1 += s1[c]; t2 += s2[c]; }
+      double* p = a.partials + (((size_t)s * a.batch + n) * a.groups + g) * 2;
+      atomicAdd(p + 0, t1);
+      atomicAdd(p + 1, t2);
+    }
+    __syncthreads();
+    for (int i = tid; i < C; i += kNT) { s1[i] = 0.0; s2[i] = 0.0; }
+#pragma unroll
+    for (int j = 0; j < VW; ++j) { acc1[j] = 0.0; acc2[j] = 0.0; }
+  };
+  for (int item = blockIdx.x; item < a.total_items; item += gridDim.x) {
+    int s, n, k;
+    decode_item(a, item, s, n, k);
+    const int key = s * a.batch + n;
+    if (key != cur) {
+      if (cur >= 0) flush(cur_s, cur_n);
+      __syncthreads();
+      for (int c = tid; c < C; c += kNT) {
+        int e1, e2;
+        group_scales(a.ymax[n * a.groups + c / gs], a.lbits, e1, e2);
+        sc1[c] = ldexp(1.0, e1);
+        sc2[c] = ldexp(1.0, e2);
+      }
+      __syncthreads();
+      if (FIXED) {
+        const int c0 = (tid * VW) % C;
+#pragma unroll
+        for (int j = 0; j < VW; ++j) { f1[j] = sc1[c0 + j]; f2[j] = sc2[c0 + j]; }
+      }
+      cur = key;
+      cur_s = s;
+      cur_n = n;
+    }
+    const GnShard& sh = a.sh[s];
+    const typename V::T* y = reinterpret_cast<const typename V::T*>(sh.y) + n * sh.vecs_per_n;
+    const int64_t v0 = (int64_t)k * kNT * kIter;
+#pragma unroll 4
+    for (int i = 0; i < kIter; ++i) {
+      const int64_t v = v0 + i * kNT + tid;
+      if (v >= sh.vecs_per_n) break;
+      const typename V::T val = y[v];
+#pragma unroll
+      for (int j = 0; j < VW; ++j) {
+        const double d = (double)V::get(val, j);
+        if (FIXED) {
+          acc1[j] += rint(d * f1[j]);
+          acc2[j] += rint((d * d) * f2[j]);
+        } else {
+          const int c = (int)((v * VW + j) % C);
+          atomicAdd(&s1[c], rint(d * sc1[c]));
+          atomicAdd(&s2[c], rint((d * d) * sc2[c]));
+        }
+      }
+    }
+  }
+  if (cur >= 0) flush(cur_s, cur_n);
+}
+
+__global__ void gn_combine(const GnArgs a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.batch * a.groups) return;
+  const int n = i / a.groups, g = i - n * a.groups;
+  double t1 = 0.0, t2 = 0.0;
+  for (int s = 0; s < a.nshards; ++s) {
+    const double* p = a.partials + (((size_t)s * a.batch + n) * a.groups + g) * 2;
+    t1 += p[0];
+    t2 += p[1];
+  }
+  const int e1 = a.scales[2 * i + 0], e2 = a.scales[2 * i + 1];
+  const double mean = ldexp(t1, -e1) / a.m_count;
+  const double ey2 = ldexp(t2, -e2) / a.m_count;
+  double var = ey2 - mean * mean;
+  if (var < 0.0) var = 0.0;
+  const double rstd = 1.0 / sqrt(var + a.eps);
+  a.stats[2 * i + 0] = (float)mean;
+  a.stats[2 * i + 1] = (float)rstd;
+  const int gs = a.channels / a.groups;
+  for (int c = g * gs; c < (g + 1) * gs; ++c) {
+    const double gam = a.gamma ? (double)a.gamma[c] : 1.0;
+    const float bet = a.beta ? a.beta[c] : 0.f;
+    a.chan[(size_t)n * a.channels + c] = make_float4((float)mean, (float)(rstd * gam), bet, 0.f);
+  }
+}
+
+template <int VW, bool FIXED>
+__global__ __launch_bounds__(kNT) void gn_apply(const GnArgs a) {
+  using V = Vec<VW>;
+  const int tid = threadIdx.x;
+  const int C = a.channels;
+  int cur = -1;
+  float4 p[VW];
+  for (int item = blockIdx.x; item < a.total_items; item += gridDim.x) {
+    int s, n, k;
+    decode_item(a, item, s, n, k);
+    const int key = s * a.batch + n;
+    if (FIXED && key != cur) {
+      const int c0 = (tid * VW) % C;
+#pragma unroll
+      for (int j = 0; j < VW; ++j) p[j] = a.chan[(size_t)n * C + c0 + j];
+      cur = key;
+    }
+    const GnShard& sh = a.sh[s];
+    const typename V::T* y = reinterpret_cast<const typename V::T*>(sh.y) + n * sh.vecs_per_n;
+    typename V::T* z = reinterpret_cast<typename V::T*>(sh.z) + n * sh.vecs_per_n;
+    const int64_t v0 = (int64_t)k * kNT * kIter;
+#pragma unroll 4
+    for (int i = 0; i < kIter; ++i) {
+      const int64_t v = v0 + i * kNT + tid;
+      if (v >= sh.vecs_per_n) break;
+      typename V::T val = y[v];
+      float out[VW];
+#pragma unroll
+      for (int j = 0; j < VW; ++j) {
+        float4 q;
+        if (FIXED) q = p[j];
+        else q = a.chan[(size_t)n * C + (int)((v * VW + j) % C)];
+        out[j] = fmaf(V::get(val, j) - q.x, q.y, q.z);
+      }
+      if constexpr (VW == 4) z[v] = make_float4(out[0], out[1], out[2], out[3]);
+      else z[v] = out[0];
+    }
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+st_gn_layout layout_of(const st_plan* p, int groups) {
+  st_gn_layout l{};
+  const size_t S = p->shards.size(), N = (size_t)p->batch, G = (size_t)groups, C = (size_t)p->channels;
+  size_t off = 0;
+  l.partials_offset = off; off = align256(off + S * N * G * 2 * sizeof(double));
+  l.ymax_offset = off;     off = align256(off + N * G * sizeof(uint32_t));
+  l.stats_offset = off;    off = align256(off + N * G * 2 * sizeof(float));
+  l.scales_offset = off;   off = align256(off + N * G * 2 * sizeof(int32_t));
+  l.chan_offset = off;     off = align256(off + N * C * sizeof(float4));
+  l.total_bytes = off;
+  return l;
+}
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    hipDeviceProp_t prop;
+    cus[dev] = hipGetDeviceProperties(&prop, dev) == hipSuccess ? prop.multiProcessorCount : 256;
+  }
+  return cus[dev];
+}
+
+// Validates the arguments shared by the three stages and fills GnArgs.
+st_status prepare(const st_plan* y_plan, const float* const* y_bufs, float* const* z_bufs,
+                  const uint32_t* ymax, int32_t groups, float eps, const float* gamma,
+                  const float* beta, void* workspace, size_t workspace_bytes, const char* who,
+                  GnArgs& a, int& vw, bool& fixed) {
+  auto err = [&](st_status s, const char* m) { return fail(s, std::string(who) + ": " + m); };
+  if (!y_plan) return err(ST_ERR_INVALID_ARG, "NULL plan");
+  if (y_plan->dtype != ST_F32) return err(ST_ERR_BAD_SHAPE, "y must be fp32");
+  for (int ax = 0; ax < kAxes; ++ax)
+    if (y_plan->halo[ax] != 0) return err(ST_ERR_BAD_SHAPE, "y plan must have halo 0");
+  const int C = (int)y_plan->channels;
+  if (groups < 1 || C % groups) return err(ST_ERR_INVALID_ARG, "groups must divide C");
+  if (C > 1024) return err(ST_ERR_UNSUPPORTED, "more than 1024 channels");
+  if (!(eps >= 0.f)) return err(ST_ERR_INVALID_ARG, "eps must be >= 0");
+  const st_gn_layout l = layout_of(y_plan, groups);
+  if (!workspace || workspace_bytes < l.total_bytes) return err(ST_ERR_WORKSPACE, "workspace missing or too small");
+  if (!aligned16(workspace)) return err(ST_ERR_ALIGNMENT, "workspace not 16-byte aligned");
+  for (size_t s = 0; s < y_plan->shards.size(); ++s) {
+    if (y_bufs) {
+      if (!y_bufs[s]) return err(ST_ERR_INVALID_ARG, "NULL y buffer");
+      if (!aligned16(y_bufs[s])) return err(ST_ERR_ALIGNMENT, "y buffers must be 16-byte aligned");
+    }
+    if (z_bufs) {
+      if (!z_bufs[s]) return err(ST_ERR_INVALID_ARG, "NULL z buffer");
+      if (!aligned16(z_bufs[s])) return err(ST_ERR_ALIGNMENT, "z buffers must be 16-byte aligned");
+    }
+  }
+  if ((gamma && (reinterpret_cast<uintptr_t>(gamma) & 3)) || (beta && (reinterpret_cast<uintptr_t>(beta) & 3)) ||
+      (ymax && (reinterpret_cast<uintptr_t>(ymax) & 3)))
+    return err(ST_ERR_ALIGNMENT, "misaligned gamma/beta/ymax");
+
+  char* ws = static_cast<char*>(workspace);
+  a = GnArgs{};
+  a.nshards = (int)y_plan->shards.size();
+  a.batch = (int)y_plan->batch;
+  a.channels = C;
+  a.groups = groups;
+  int64_t positions = 1;
+  for (int ax = 0; ax < kAxes; ++ax) positions *= y_plan->spatial[ax];
+  const uint64_t M = (uint64_t)(C / groups) * (uint64_t)positions;
+  int lbits = 0;
+  while (lbits < 64 && (M >> lbits) != 0) ++lbits;
+  if (lbits > 50) return err(ST_ERR_UNSUPPORTED, "group too large for exact sums");
+  a.lbits = lbits;
+  a.m_count = (double)M;
+  a.eps = (double)eps;
+  a.partials = reinterpret_cast<double*>(ws + l.partials_offset);
+  a.stats = reinterpret_cast<float*>(ws + l.stats_offset);
+  a.scales = reinterpret_cast<int32_t*>(ws + l.scales_offset);
+  a.ymax = ymax ? const_cast<uint32_t*>(ymax) : reinterpret_cast<uint32_t*>(ws + l.ymax_offset);
+  a.chan = reinterpret_cast<float4*>(ws + l.chan_offset);
+  a.gamma = gamma;
+  a.beta = beta;
+  vw = C % 4 == 0 ? 4 : 1;
+  fixed = (vw * kNT) % C == 0;
+  const int64_t item_vecs = (int64_t)kNT * kIter;
+  int64_t items = 0;
+  for (size_t s = 0; s < y_plan->shards.size(); ++s) {
+    const Shard& sd = y_plan->shards[s];
+    GnShard& g = a.sh[s];
+    g.y = y_bufs ? y_bufs[s] : nullptr;
+    g.z = z_bufs ? z_bufs[s] : nullptr;
+    g.vecs_per_n = sd.ext[0] * sd.ext[1] * sd.ext[2] * C / vw;
+    g.items_per_n = (int32_t)((g.vecs_per_n + item_vecs - 1) / item_vecs);
+    g.item_begin = (int32_t)items;
+    items += (int64_t)g.items_per_n * a.batch;
+    if (items > INT32_MAX) return err(ST_ERR_UNSUPPORTED, "volume too large");
+  }
+  a.total_items = (int)items;
+  return ST_OK;
+}
+
+int grid_of(const GnArgs& a) { return std::max(1, std::min(a.total_items, device_cus() * 8)); }
+
+template <int VW, bool FIXED>
+st_status launch_partials(GnArgs& a, bool need_max, hipStream_t st) {
+  const int grid = grid_of(a);
+  if (need_max) {
+    hipLaunchKernelGGL((gn_max<VW, FIXED>), dim3(grid), dim3(kNT), 0, st, a);
+    st_status s = launch_check("st_groupnorm_partials: max launch");
+    if (s != ST_OK) return s;
+  }
+  hipLaunchKernelGGL((gn_stats<VW, FIXED>), dim3(grid), dim3(kNT), 0, st, a);
+  return launch_check("st_groupnorm_partials: stats launch");
+}
+
+template <int VW, bool FIXED>
+st_status launch_apply(GnArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((gn_apply<VW, FIXED>), dim3(grid_of(a)), dim3(kNT), 0, st, a);
+  return launch_check("st_groupnorm_apply: launch");
+}
+
+}  // namespace
+}  // namespace st
+
+using namespace st;
+
+extern "C" {
+
+size_t st_groupnorm_workspace_bytes(const st_plan* y_plan, int32_t groups) {
+  if (!y_plan || groups < 1) return 0;
+  return layout_of(y_plan, groups).total_bytes;
+}
+
+st_status st_groupnorm_workspace_layout(const st_plan* y_plan, int32_t groups, st_gn_layout* out) {
+  if (!y_plan || !out) return fail(ST_ERR_INVALID_ARG, "st_groupnorm_workspace_layout: NULL argument");
+  if (groups < 1 || y_plan->channels % groups)
+    return fail(ST_ERR_INVALID_ARG, "st_groupnorm_workspace_layout: groups must divide C");
+  *out = layout_of(y_plan, groups);
+  return ST_OK;
+}
+
+st_status st_groupnorm_partials(const st_plan* y_plan, const float* const* y_bufs,
+                                const uint32_t* ymax_or_null, int32_t groups, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!y_bufs) return fail(ST_ERR_INVALID_ARG, "st_groupnorm_partials: NULL y array");
+  GnArgs a;
+  int vw;
+  bool fixed;
+  st_status s = prepare(y_plan, y_bufs, nullptr, ymax_or_null, groups, 0.f, nullptr, nullptr, workspace,
+                        workspace_bytes, "st_groupnorm_partials", a, vw, fixed);
+  if (s != ST_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // clear the partial sums (and the max scratch when this call computes it)
+  const st_gn_layout l = layout_of(y_plan, groups);
+  const int64_t words = (int64_t)(l.ymax_offset + (ymax_or_null ? 0 : (size_t)a.batch * groups * 4)) / 4;
+  hipLaunchKernelGGL(gn_fill, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<uint32_t*>(workspace), words);
+  s = launch_check("st_groupnorm_partials: clear launch");
+  if (s != ST_OK) return s;
+  const bool need_max = ymax_or_null == nullptr;
+  if (vw == 4) return fixed ? launch_partials<4, true>(a, need_max, st) : launch_partials<4, false>(a, need_max, st);
+  return fixed ? launch_partials<1, true>(a, need_max, st) : launch_partials<1, false>(a, need_max, st);
+}
+
+st_status st_groupnorm_combine(const st_plan* y_plan, int32_t groups, float eps, const float* gamma_or_null,
+                               const float* beta_or_null, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  GnArgs a;
+  int vw;
+  bool fixed;
+  st_status s = prepare(y_plan, nullptr, nullptr, nullptr, groups, eps, gamma_or_null, beta_or_null, workspace,
+                        workspace_bytes, "st_groupnorm_combine", a, vw, fixed);
+  if (s != ST_OK) return s;
+  const int ng = a.batch * a.groups;
+  hipLaunchKernelGGL(gn_combine, dim3((ng + 63) / 64), dim3(64), 0, static_cast<hipStream_t>(stream), a);
+  return launch_check("st_groupnorm_combine: launch");
+}
+
+st_status st_groupnorm_apply(const st_plan* y_plan, const float* const* y_bufs, int32_t groups,
+                             float* const* z_bufs, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!y_bufs || !z_bufs) return fail(ST_ERR_INVALID_ARG, "st_groupnorm_apply: NULL buffer array");
+  GnArgs a;
+  int vw;
+  bool fixed;
+  st_status s = prepare(y_plan, y_bufs, z_bufs, nullptr, groups, 0.f, nullptr, nullptr, workspace,
+                        workspace_bytes, "st_groupnorm_apply", a, vw, fixed);
+  if (s != ST_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (vw == 4) return fixed ? launch_apply<4, true>(a, st) : launch_apply<4, false>(a, st);
+  return fixed ? launch_apply<1, true>(a, st) : launch_apply<1, false>(a, st);
+}
+
+st_status st_groupnorm_sharded(const st_plan* y_plan, const float* const* y_bufs,
+                               const uint32_t* ymax_or_null, int32_t groups, float eps,
+                               const float* gamma_or_null, const float* beta_or_null,
+                               float* const* z_bufs, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!y_bufs || !z_bufs) return fail(ST_ERR_INVALID_ARG, "st_groupnorm_sharded: NULL buffer array");
+  GnArgs a;
+  int vw;
+  bool fixed;
+  // validate everything up front so a failure enqueues nothing
+  st_status s = prepare(y_plan, y_bufs, z_bufs, ymax_or_null, groups, eps, gamma_or_null, beta_or_null,
+                        workspace, workspace_bytes, "st_groupnorm_sharded", a, vw, fixed);
+  if (s != ST_OK) return s;
+  s = st_groupnorm_partials(y_plan, y_bufs, ymax_or_null, groups, workspace, workspace_bytes, stream);
+  if (s != ST_OK) return s;
+  s = st_groupnorm_combine(y_plan, groups, eps, gamma_or_null, beta_or_null, workspace, workspace_bytes, stream);
+  if (s != ST_OK) return s;
+  return st_groupnorm_apply(y_plan, y_bufs, groups, z_bufs, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,279 @@
+/*
+ * shardconv.h - C-ABI of the halo-sharded conv + GroupNorm library (gfx950).
+ *
+ * One GPU's share of a domain-sharded spatial layer, after "Technical summary:
+ * ShardTensor - domain parallelism for scientific machine learning"
+ * (gist.science paper 2605.11111):
+ *   - section 2, "Design principles": a batch-1 volume is split along its
+ *     spatial axes into chunks whose per-chunk shapes ("sharding shapes") may
+ *     be uneven;
+ *   - section 2, "Implementation details", "Communication": neighbouring
+ *     cells are exchanged as halos and statistics are combined with
+ *     collectives so that convolution and normalisation give the unsharded
+ *     result.
+ * On one GPU every shard is its own HBM buffer: the halo exchange is a pack
+ * into a message buffer and an unpack into the neighbours' margins, and the
+ * statistics combine is an on-device reduction over the per-shard partials.
+ *
+ * Conventions for every entry point
+ *   - Buffers are device pointers owned by the caller; the library never frees
+ *     or retains them.  The library owns only plans (st_plan_destroy).
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *     stream) with no host synchronisation.  Results are defined once the
+ *     stream reaches that point.
+ *   - Every call returns an st_status.  Nothing throws or aborts across the
+ *     ABI.  On failure st_last_error() returns a thread-local message; all
+ *     argument, shape and alignment checks run on the host before any launch,
+ *     so a failed check enqueues nothing.  Launch failures map to ST_ERR_HIP.
+ *   - Layout: channels-last.  A shard buffer holds [N][Dp][Hp][Wp][C] (3D) or
+ *     [N][Hp][Wp][C] (2D), where each padded extent is the shard's extent plus
+ *     2*halo on that axis.  Every spatial axis is padded, also where the shard
+ *     touches the global boundary (those margins hold zeros after
+ *     st_halo_unpack with zero_global_margins != 0).
+ *   - Device pointers must be 16-byte aligned.
+ *   - Shards are numbered row-major over the shard grid (axis 0 outermost);
+ *     along each axis the first size is the lowest-index shard.
+ */
+#ifndef SHARDCONV_H
+#define SHARDCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ST_MAX_SHARDS 64   /* shards per plan */
+#define ST_MAX_NDIM 3
+
+typedef enum st_status {
+  ST_OK = 0,
+  ST_ERR_INVALID_ARG = 1,      /* null pointer, bad enum, negative size */
+  ST_ERR_BAD_SHAPE = 2,        /* sizes that do not add up or plans that do not match */
+  ST_ERR_SHARD_TOO_SMALL = 3,  /* a shard thinner than the halo along a split axis */
+  ST_ERR_UNSUPPORTED = 4,      /* ndim not 2/3, even kernel, too many shards, ... */
+  ST_ERR_WORKSPACE = 5,        /* workspace missing or too small */
+  ST_ERR_HIP = 6,              /* a HIP runtime call or kernel launch failed */
+  ST_ERR_ALIGNMENT = 7         /* a device pointer is not 16-byte aligned */
+} st_status;
+
+typedef enum st_dtype { ST_F32 = 0, ST_BF16 = 1 } st_dtype;
+
+typedef struct st_plan st_plan; /* opaque, library-owned */
+
+typedef struct st_shard_info {
+  int32_t index;          /* linear shard index */
+  int32_t grid[3];        /* coordinate in the shard grid per spatial axis (unused axes: 0) */
+  int64_t offset[3];      /* global start of the interior per spatial axis */
+  int64_t extent[3];      /* interior extent per spatial axis (unused axes: 1) */
+  int64_t padded[3];      /* extent + 2*halo per spatial axis (unused axes: 1) */
+  int64_t elems;          /* elements of the padded buffer: N * prod(padded) * C */
+  int64_t bytes;          /* elems * element size */
+} st_shard_info;
+
+typedef struct st_halo_box {
+  int32_t src_shard;      /* shard whose interior cells are sent; -1 for a zero box */
+  int32_t dst_shard;      /* shard whose margin receives them */
+  int32_t dir[3];         /* direction from src to dst (from dst outwards for zero boxes) */
+  int64_t dst_lo[3];      /* box origin in the receiver's padded coordinates */
+  int64_t src_lo[3];      /* box origin in the sender's padded coordinates (zero box: unused) */
+  int64_t ext[3];         /* box extent per spatial axis */
+  int64_t msg_offset;     /* byte offset of the box in the message (zero box: -1) */
+} st_halo_box;
+
+/* ------------------------------------------------------------------ misc */
+
+const char* st_version(void);
+/* Message of the last failed call on this thread ("" if none). */
+const char* st_last_error(void);
+const char* st_status_string(st_status s);
+
+/* ------------------------------------------------------------ planning */
+
+/*
+ * st_plan_shards - sharding shapes and halo geometry (host only, no GPU call).
+ *
+ * Section 2 ("Design principles") of the ShardTensor summary: a per-chunk
+ * local shape along each sharded axis, allowing uneven chunks.
+ *
+ *   ndim              2 or 3 spatial axes (else ST_ERR_UNSUPPORTED)
+ *   batch, channels   N >= 1 and C >= 1
+ *   spatial[ndim]     global extents, axis 0 outermost ((H, W) or (D, H, W))
+ *   nshards_per_axis[ndim]  number of shards along each axis (>= 1); their
+ *                     product is at most ST_MAX_SHARDS
+ *   sizes_concat      the per-axis shard sizes concatenated: axis 0's
+ *                     nshards_per_axis[0] sizes, then axis 1's, ...; each
+ *                     axis must sum to spatial[axis]
+ *   halo_per_axis[ndim]  margin width h per axis (>= 0); a conv with odd
+ *                     kernel k needs h >= k/2.  Along an axis with more than
+ *                     one shard every shard must be at least h thick
+ *                     (ST_ERR_SHARD_TOO_SMALL)
+ *   dtype             element type of the shard buffers
+ *   out               receives the plan; release it with st_plan_destroy
+ *
+ * The plan enumerates, for every shard and every neighbour direction in
+ * {-1,0,1}^ndim \ {0}, either a halo box (the neighbour exists: its interior
+ * cells are sent) or a zero box (global face: the margin is zero padding).
+ * Message layout: boxes ordered by sending shard, then by direction
+ * (lexicographic, -1 < 0 < 1), each box channels-last and starting at a
+ * 16-byte-aligned byte offset.
+ */
+st_status st_plan_shards(int32_t ndim, int64_t batch, int64_t channels, const int64_t* spatial,
+                         const int32_t* nshards_per_axis, const int64_t* sizes_concat,
+                         const int32_t* halo_per_axis, st_dtype dtype, st_plan** out);
+
+/* Frees the plan and its device descriptor table (if one was uploaded). */
+st_status st_plan_destroy(st_plan* plan);
+
+/* Plan queries; return -1 for a null plan. */
+int64_t st_plan_num_shards(const st_plan* plan);
+int64_t st_plan_msg_bytes(const st_plan* plan);
+int64_t st_plan_num_halo_boxes(const st_plan* plan);  /* boxes sent */
+int64_t st_plan_num_zero_boxes(const st_plan* plan);  /* global-face margins */
+st_status st_plan_shard_info(const st_plan* plan, int32_t shard, st_shard_info* out);
+/* i in [0, halo boxes): sent boxes in message order; then the zero boxes. */
+st_status st_plan_halo_box(const st_plan* plan, int32_t i, st_halo_box* out);
+
+/* ---------------------------------------------------------- halo exchange */
+
+/*
+ * st_halo_pack - copy every sent box out of its shard's interior into `msg`.
+ * Section 2, "Implementation details", "Communication" (halo exchange: the
+ * cells next to a chunk's boundary are fetched from the adjacent chunk).
+ *
+ *   shard_bufs[num_shards]  padded shard buffers (read)
+ *   msg                      st_plan_msg_bytes(plan) bytes (written; gaps
+ *                            between boxes are not touched)
+ * Raw bit copy.  The first device call on a plan uploads its descriptor table
+ * (one small allocation owned by the plan, on the current device).
+ */
+st_status st_halo_pack(st_plan* plan, const void* const* shard_bufs, void* msg, void* stream);
+
+/*
+ * st_halo_unpack - copy every box of `msg` into the receiving shard's margin;
+ * with zero_global_margins != 0 also write zeros into the margins on the
+ * global faces (the conv's zero padding).  Same section as st_halo_pack.
+ *   msg                      as written by st_halo_pack (read)
+ *   shard_bufs[num_shards]  padded shard buffers (margins written, interiors
+ *                            untouched)
+ */
+st_status st_halo_unpack(st_plan* plan, const void* msg, void* const* shard_bufs,
+                         int32_t zero_global_margins, void* stream);
+
+/* ------------------------------------------------------------------ conv */
+
+/*
+ * Packed weights.  Weights are given as [Cout][Cin][k]^ndim (PyTorch's
+ * logical order) in `dtype` and repacked once into the layout the kernels
+ * read.  st_conv_weight_bytes returns 0 for unsupported arguments.
+ */
+size_t st_conv_weight_bytes(int32_t ndim, int32_t cin, int32_t cout, int32_t ksize, st_dtype dtype);
+st_status st_conv_pack_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t ksize,
+                               st_dtype dtype, const void* weight, void* packed, void* stream);
+
+/*
+ * st_conv_sharded - per-shard convolution on the halo-padded chunks.
+ * Section 2, "Implementation details", "Communication": with the halo in
+ * place every shard's output equals the matching slice of the unsharded
+ * convolution.
+ *
+ * Cross-correlation, stride 1, dilation 1, odd cubic kernel `ksize`, zero
+ * padding ksize/2 supplied by the shard margins:
+ *   y[n, i, o] = bias[o] + sum_t sum_c W[o, c, t] * x[n, i + t - ksize/2, c]
+ *
+ *   in_plan, in_bufs   padded input shards, C = Cin, halo >= ksize/2 per axis
+ *   packed_weight      from st_conv_pack_weights (same ndim, cin, cout, ksize, dtype)
+ *   bias_or_null       Cout floats or NULL (zero bias)
+ *   out_plan, y_bufs   fp32 outputs: a plan with the same shard sizes, batch,
+ *                      C = Cout, halo 0, dtype ST_F32
+ *   ymax_or_null       if not NULL: [N][groups] uint32 receiving the bit
+ *                      pattern of max |y| per (n, group) over all shards
+ *                      (groups: contiguous blocks of Cout/groups channels)
+ * bf16 operands accumulate in fp32 on the matrix cores; fp32 operands use
+ * fp32 FMA.  Each output's accumulation order depends only on its kernel
+ * taps, so a shard's output is bitwise independent of the shard plan.
+ */
+st_status st_conv_sharded(const st_plan* in_plan, const void* const* in_bufs,
+                          const void* packed_weight, const float* bias_or_null,
+                          int32_t cout, int32_t ksize, const st_plan* out_plan,
+                          float* const* y_bufs, uint32_t* ymax_or_null, int32_t groups,
+                          void* stream);
+
+/* ------------------------------------------------------------- GroupNorm */
+
+/*
+ * Workspace of st_groupnorm_sharded.  Leading regions (byte offsets from
+ * st_groupnorm_workspace_layout):
+ *   partials  [S][N][G][2] double: per-shard (sum q1, sum q2), exact integers
+ *   stats     [N][G][2]   float:  (mean, rstd) after the combine
+ *   scales    [N][G][2]   int32:  fixed-point exponents (e1, e2)
+ *   ymax      [N][G]      uint32: max |y| when the caller passes no ymax
+ */
+typedef struct st_gn_layout {
+  size_t partials_offset, stats_offset, scales_offset, ymax_offset, chan_offset, total_bytes;
+} st_gn_layout;
+size_t st_groupnorm_workspace_bytes(const st_plan* y_plan, int32_t groups);
+st_status st_groupnorm_workspace_layout(const st_plan* y_plan, int32_t groups, st_gn_layout* out);
+
+/*
+ * st_groupnorm_sharded - split-statistics GroupNorm over all shards.
+ * Section 2, "Implementation details", "Communication": normalisation stays
+ * consistent with the unsharded model by combining per-chunk statistics with
+ * a collective.  GroupNorm itself is not defined on the pages; this is the
+ * standard one: contiguous channel groups, biased variance, eps inside the
+ * square root, per-channel affine:
+ *   z = (y - mean_g) / sqrt(var_g + eps) * gamma_c + beta_c
+ *
+ * Statistics are exact: every y contributes q1 = rint(y * 2^e1) and
+ * q2 = rint(y^2 * 2^e2), with e1, e2 chosen from the global max |y| and the
+ * element count so that every partial sum is an integer below 2^53; sums of
+ * such integers do not depend on their order, so the per-shard partials and
+ * their combine give the same bits for any shard plan.  mean, the biased
+ * variance and rstd are then formed in fp64 and rounded once to fp32.
+ *
+ *   y_plan, y_bufs      fp32 conv outputs (halo-0 plan, C = Cout)
+ *   ymax_or_null        max |y| bits from st_conv_sharded, or NULL to have
+ *                       this call compute it (one more read of y)
+ *   groups              divides C
+ *   eps                 added to the variance
+ *   gamma/beta_or_null  C floats or NULL (1 and 0)
+ *   z_bufs              fp32 outputs, same layout as y; may alias y_bufs
+ *   workspace           >= st_groupnorm_workspace_bytes(y_plan, groups) bytes
+ */
+st_status st_groupnorm_sharded(const st_plan* y_plan, const float* const* y_bufs,
+                               const uint32_t* ymax_or_null, int32_t groups, float eps,
+                               const float* gamma_or_null, const float* beta_or_null,
+                               float* const* z_bufs, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * The three steps of st_groupnorm_sharded as separate calls, in this order
+ * on one stream (same plan, groups and workspace).  Between partials and
+ * combine is where a multi-device run would all-reduce the per-shard
+ * partials (section 2, "Implementation details", "Communication").
+ *
+ * st_groupnorm_partials  clears the partials, computes max |y| into the
+ *                        workspace when ymax_or_null is NULL, then writes
+ *                        the per-shard exact (sum q1, sum q2) and the
+ *                        exponents (e1, e2) into the workspace.
+ * st_groupnorm_combine   sums the partials over shards and writes (mean,
+ *                        rstd) per (n, group) and the per-channel
+ *                        (mean, rstd*gamma, beta) the apply reads.
+ * st_groupnorm_apply     z = (y - mean) * rstd * gamma + beta; z may alias y.
+ */
+st_status st_groupnorm_partials(const st_plan* y_plan, const float* const* y_bufs,
+                                const uint32_t* ymax_or_null, int32_t groups, void* workspace,
+                                size_t workspace_bytes, void* stream);
+st_status st_groupnorm_combine(const st_plan* y_plan, int32_t groups, float eps,
+                               const float* gamma_or_null, const float* beta_or_null,
+                               void* workspace, size_t workspace_bytes, void* stream);
+st_status st_groupnorm_apply(const st_plan* y_plan, const float* const* y_bufs, int32_t groups,
+                             float* const* z_bufs, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHARDCONV_H */

@@ -1,0 +1,70 @@
+"""Shared helpers of the GPU tests: workloads, oracle results, comparisons."""
+from __future__ import annotations
+
+import dataclasses
+import math
+import sys
+
+import numpy as np
+
+import oracle
+import synth
+
+# Tolerances on max |gpu - oracle| / rms(oracle), as the target states them:
+# fp32 operands 1e-5, bf16 operands (fp32 accumulation, fp32 outputs) 1e-2.
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(got, want) -> float:
+    want = np.asarray(want, np.float64)
+    rms = math.sqrt(float(np.mean(want * want)))
+    return float(np.max(np.abs(np.asarray(got, np.float64) - want))) / max(rms, 1e-300)
+
+
+def small_cases():
+    """Small versions of every workload: same channels, kernel, groups and
+    dtype; shard topologies like the full ones; extents that leave ragged
+    tails against every conv tile shape; some with batch 2."""
+    W = synth.WORKLOADS
+    return {
+        "vol32_full": W["vol32_c4to8_k3_fp32"],
+        "vol32_b2": synth.small_variant(W["vol32_c4to8_k3_fp32"], (9, 10, 11), ((5, 4), (10,), (11,)), batch=2),
+        "img64_small": synth.small_variant(W["img2048_c64_k3_bf16"], (37, 70), ((11, 7, 9, 10), (70,))),
+        "img64_b2": synth.small_variant(W["img2048_c64_k3_bf16"], (20, 130), ((8, 12), (130,)), batch=2),
+        "vol32_grid": synth.small_variant(W["vol256_c32_k3_bf16"], (9, 19, 37), ((4, 5), (11, 8), (17, 20))),
+        "vol16k5": synth.small_variant(W["vol512_c16_k5_bf16"], (23, 13, 40), ((2, 5, 3, 4, 2, 3, 2, 2), (13,), (40,))),
+        "grid256_small": synth.small_variant(W["grid1024x1792_c256_k3_bf16"], (5, 150), ((5,), (80, 70))),
+    }
+
+
+def direct_cases():
+    """bf16 shapes without a matrix-core instance (direct kernel)."""
+    base = synth.WORKLOADS["img2048_c64_k3_bf16"]
+    a = dataclasses.replace(base, name="img_c5to12_k3", cin=5, cout=12, groups=3, spatial=(13, 17),
+                            shards=((6, 7), (9, 8)))
+    b = dataclasses.replace(synth.WORKLOADS["vol512_c16_k5_bf16"], name="vol_c3to4_k5", cin=3, cout=4,
+                            groups=2, spatial=(7, 8, 9), shards=((3, 4), (8,), (2, 7)))
+    return {"img_c5to12_k3": a, "vol_c3to4_k5": b}
+
+
+def oracle_forward(wl, x, w, bias=None, gamma=None, beta=None):
+    """fp64 y and z of the unsharded definition."""
+    xf = oracle.widen(x, wl.dtype)
+    wf = oracle.widen(w, wl.dtype)
+    y = oracle.conv_same(xf, wf, bias)
+    z = oracle.group_norm(y, wl.groups, wl.eps, gamma, beta)
+    return y, z
+
+
+def bits_equal(a, b) -> bool:
+    return np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
+
+
+def torch_bits_equal(t1, t2) -> bool:
+    import torch
+    return bool(torch.equal(t1.view(torch.int32), t2.view(torch.int32)))

@@ -1,0 +1,162 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host with the documented status codes (CPU only: no call
+here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import halo_sharded_conv_amd as hsc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "shardconv.h")
+
+OK, INVALID, BAD_SHAPE, TOO_SMALL, UNSUPPORTED, WORKSPACE, HIP, ALIGN = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(st_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["st_plan_shards", "st_halo_pack", "st_halo_unpack", "st_conv_sharded",
+              "st_groupnorm_sharded"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(hsc.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in hsc.st_version()
+    for s in range(8):
+        assert hsc.lib.st_status_string(s)
+
+
+def _plan_raw(ndim, batch, ch, spatial, counts, sizes, halo, dtype=1):
+    out = ctypes.c_void_p()
+    sp = (ctypes.c_int64 * 3)(*spatial)
+    ct = (ctypes.c_int32 * 3)(*counts)
+    sz = (ctypes.c_int64 * max(1, len(sizes)))(*sizes)
+    hl = (ctypes.c_int32 * 3)(*halo)
+    st = hsc.lib.st_plan_shards(ndim, batch, ch, sp, ct, sz, hl, dtype, ctypes.byref(out))
+    return st, out
+
+
+@pytest.mark.parametrize("args,status,text", [
+    ((1, 1, 4, [8, 0, 0], [1, 0, 0], [8], [1, 0, 0]), UNSUPPORTED, "ndim"),
+    ((4, 1, 4, [8, 8, 8], [1, 1, 1], [8, 8, 8], [1, 1, 1]), UNSUPPORTED, "ndim"),
+    ((2, 0, 4, [8, 8, 0], [1, 1, 0], [8, 8], [1, 1, 0]), INVALID, "batch"),
+    ((2, 1, 0, [8, 8, 0], [1, 1, 0], [8, 8], [1, 1, 0]), INVALID, "channels"),
+    ((2, 1, 4, [8, 8, 0], [2, 1, 0], [3, 4, 8], [1, 1, 0]), BAD_SHAPE, "sum"),
+    ((2, 1, 4, [8, 8, 0], [2, 1, 0], [7, 1, 8], [2, 2, 0]), TOO_SMALL, "halo"),
+    ((2, 1, 4, [8, 8, 0], [2, 1, 0], [8, 0, 8], [1, 1, 0]), BAD_SHAPE, "size"),
+    ((2, 1, 4, [8, 8, 0], [1, 1, 0], [8, 8], [-1, 1, 0]), INVALID, "halo"),
+    ((2, 1, 4, [8, 8, 0], [0, 1, 0], [8], [1, 1, 0]), INVALID, "count"),
+    ((3, 1, 4, [65, 1, 1], [65, 1, 1], [1] * 65 + [1, 1], [0, 0, 0]), UNSUPPORTED, "ST_MAX_SHARDS"),
+])
+def test_plan_errors(args, status, text):
+    st, out = _plan_raw(*args)
+    assert st == status
+    assert not out.value
+    assert text.lower() in hsc.lib.st_last_error().decode().lower()
+
+
+def test_plan_null_and_dtype_errors():
+    out = ctypes.c_void_p()
+    assert hsc.lib.st_plan_shards(2, 1, 4, None, None, None, None, 1, ctypes.byref(out)) == INVALID
+    assert hsc.lib.st_plan_shards(2, 1, 4, None, None, None, None, 1, None) == INVALID
+    st, _ = _plan_raw(2, 1, 4, [8, 8, 0], [1, 1, 0], [8, 8], [1, 1, 0], dtype=7)
+    assert st == INVALID
+    assert hsc.lib.st_plan_destroy(None) == INVALID
+    assert hsc.lib.st_plan_num_shards(None) == -1
+    assert hsc.lib.st_plan_msg_bytes(None) == -1
+
+
+def test_single_shard_thinner_than_halo_is_allowed():
+    # the halo only needs neighbour cells along split axes
+    p = hsc.st_plan_shards(2, 1, 4, [1, 8], [[1], [8]], [2, 2], "f32")
+    assert p.num_shards == 1 and p.num_halo_boxes == 0 and p.num_zero_boxes == 8
+
+
+def test_python_errors_raise():
+    with pytest.raises(hsc.ShardConvError) as e:
+        hsc.st_plan_shards(2, 1, 4, [8, 8], [[3, 4], [8]], [1, 1], "bf16")
+    assert e.value.status == BAD_SHAPE
+
+
+def test_device_calls_reject_bad_arguments_before_any_launch():
+    p = hsc.st_plan_shards(2, 1, 8, [8, 8], [[4, 4], [8]], [1, 1], "bf16")
+    q = hsc.st_plan_shards(2, 1, 16, [8, 8], [[4, 4], [8]], [0, 0], "f32")
+    q_bad = hsc.st_plan_shards(2, 1, 16, [8, 8], [[3, 5], [8]], [0, 0], "f32")
+    L = hsc.lib
+    PP = ctypes.c_void_p * 2
+    aligned = PP(0x10000, 0x20000)
+    misaligned = PP(0x10000, 0x20004)
+    nulls = PP(0, 0)
+    s = None
+    # halo
+    assert L.st_halo_pack(None, aligned, ctypes.c_void_p(0x30000), s) == INVALID
+    assert L.st_halo_pack(p.handle, None, ctypes.c_void_p(0x30000), s) == INVALID
+    assert L.st_halo_pack(p.handle, nulls, ctypes.c_void_p(0x30000), s) == INVALID
+    assert L.st_halo_pack(p.handle, misaligned, ctypes.c_void_p(0x30000), s) == ALIGN
+    assert L.st_halo_pack(p.handle, aligned, None, s) == INVALID
+    assert L.st_halo_pack(p.handle, aligned, ctypes.c_void_p(0x30008), s) == ALIGN
+    assert L.st_halo_unpack(p.handle, None, aligned, 1, s) == INVALID
+    assert L.st_halo_unpack(p.handle, ctypes.c_void_p(0x30008), aligned, 1, s) == ALIGN
+    # conv
+    w = ctypes.c_void_p(0x40000)
+    assert L.st_conv_sharded(p.handle, aligned, w, None, 16, 2, q.handle, aligned, None, 1, s) == UNSUPPORTED
+    assert L.st_conv_sharded(p.handle, aligned, w, None, 16, 5, q.handle, aligned, None, 1, s) == BAD_SHAPE
+    assert L.st_conv_sharded(p.handle, aligned, w, None, 32, 3, q.handle, aligned, None, 1, s) == BAD_SHAPE
+    assert L.st_conv_sharded(p.handle, aligned, w, None, 16, 3, q_bad.handle, aligned, None, 1, s) == BAD_SHAPE
+    assert L.st_conv_sharded(p.handle, aligned, w, None, 16, 3, p.handle, aligned, None, 1, s) == BAD_SHAPE
+    assert L.st_conv_sharded(p.handle, aligned, w, None, 16, 3, q.handle, aligned,
+                             ctypes.c_void_p(0x50000), 3, s) == INVALID
+    assert L.st_conv_sharded(p.handle, aligned, ctypes.c_void_p(0x40008), None, 16, 3, q.handle, aligned,
+                             None, 1, s) == ALIGN
+    assert L.st_conv_sharded(p.handle, misaligned, w, None, 16, 3, q.handle, aligned, None, 1, s) == ALIGN
+    assert L.st_conv_sharded(None, aligned, w, None, 16, 3, q.handle, aligned, None, 1, s) == INVALID
+    # weights
+    assert L.st_conv_weight_bytes(2, 8, 16, 2, 1) == 0
+    assert L.st_conv_weight_bytes(4, 8, 16, 3, 1) == 0
+    assert L.st_conv_weight_bytes(2, 8, 16, 3, 9) == 0
+    assert L.st_conv_pack_weights(2, 8, 16, 4, 1, w, w, s) == UNSUPPORTED
+    assert L.st_conv_pack_weights(2, 8, 16, 3, 1, None, w, s) == INVALID
+    assert L.st_conv_pack_weights(2, 8, 16, 3, 1, ctypes.c_void_p(0x40002), w, s) == ALIGN
+    # groupnorm
+    need = L.st_groupnorm_workspace_bytes(q.handle, 4)
+    assert need > 0
+    ws = ctypes.c_void_p(0x60000)
+    gn = L.st_groupnorm_sharded
+    assert gn(q.handle, aligned, None, 4, 1e-5, None, None, aligned, ws, need - 1, s) == WORKSPACE
+    assert gn(q.handle, aligned, None, 4, 1e-5, None, None, aligned, None, need, s) == WORKSPACE
+    assert gn(q.handle, aligned, None, 5, 1e-5, None, None, aligned, ws, need, s) == INVALID
+    assert gn(q.handle, aligned, None, 4, -1.0, None, None, aligned, ws, need, s) == INVALID
+    assert gn(p.handle, aligned, None, 4, 1e-5, None, None, aligned, ws, need, s) == BAD_SHAPE
+    assert gn(q.handle, misaligned, None, 4, 1e-5, None, None, aligned, ws, need, s) == ALIGN
+    assert gn(q.handle, aligned, None, 4, 1e-5, None, None, aligned, ctypes.c_void_p(0x60008), need, s) == ALIGN
+    assert gn(q.handle, aligned, ctypes.c_void_p(0x70002), 4, 1e-5, None, None, aligned, ws, need, s) == ALIGN
+
+
+def test_workspace_layout_regions_are_disjoint():
+    q = hsc.st_plan_shards(3, 2, 32, [6, 7, 8], [[3, 3], [7], [4, 4]], [0, 0, 0], "f32")
+    lay = hsc.st_groupnorm_workspace_layout(q, 8)
+    S, N, G, C = 4, 2, 8, 32
+    regions = sorted([
+        (lay["partials_offset"], S * N * G * 16), (lay["ymax_offset"], N * G * 4),
+        (lay["stats_offset"], N * G * 8), (lay["scales_offset"], N * G * 8),
+        (lay["chan_offset"], N * C * 16)])
+    for (o1, n1), (o2, _) in zip(regions, regions[1:]):
+        assert o1 + n1 <= o2
+    assert regions[-1][0] + regions[-1][1] <= lay["total_bytes"]
+    assert hsc.st_groupnorm_workspace_bytes(q, 8) == lay["total_bytes"]
+    with pytest.raises(hsc.ShardConvError):
+        hsc.st_groupnorm_workspace_layout(q, 5)
