@@ -49,10 +49,27 @@ class _GnLayout(ctypes.Structure):
                 ("chan_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t)]
 
 
+def _hip_runtimes() -> list:
+    """Paths of every HIP runtime library mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python halo_sharded_conv_amd/build.py`")
+    # torch ships its own HIP runtime and its libraries ask for it by a name
+    # that does not match an already loaded libamdhip64.so.7.  Loading torch
+    # first lets this library bind to torch's runtime (same soname), so
+    # torch's streams and allocations and these kernels share one runtime.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise ImportError(f"two HIP runtimes are loaded ({runtimes}); import torch before any other HIP library")
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     PP = ctypes.POINTER(ctypes.c_void_p)
     sig = {

@@ -160,3 +160,15 @@ def test_workspace_layout_regions_are_disjoint():
     assert hsc.st_groupnorm_workspace_bytes(q, 8) == lay["total_bytes"]
     with pytest.raises(hsc.ShardConvError):
         hsc.st_groupnorm_workspace_layout(q, 5)
+
+
+def test_one_hip_runtime_in_process():
+    """The binding must share torch's HIP runtime: a second runtime in the
+    process would see torch's streams and allocations as foreign objects."""
+    import subprocess
+    import sys
+    code = ("import halo_sharded_conv_amd as h, torch;"
+            "print(len(h._hip_runtimes()))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "1"
