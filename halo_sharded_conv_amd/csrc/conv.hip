@@ -477,6 +477,282 @@ __global__ void pack_w_direct(const T* __restrict__ w, T* __restrict__ out, int 
 }
 
 // --------------------------------------------------------------------------
+// matrix-core implicit GEMM, streaming along the outermost spatial axis
+// --------------------------------------------------------------------------
+//
+// For shapes whose packed weights fit in LDS next to the input.  A job is one
+// strip of the shard (BW output columns, and BH output rows in 3D) over RC
+// consecutive output slices of the outermost axis (H in 2D, D in 3D).  The
+// workgroup walks the strip TS slices per step and keeps a ring of
+// RING = 2*TS + k - 1 input slices in LDS: the TS + k - 1 slices the current
+// step reads, plus the TS slices of the next step, which are loaded into
+// registers at the start of the step and written to LDS after its MFMAs and
+// stores.  HBM loads, matrix-core work and stores of consecutive steps
+// therefore overlap, and every input cell is read from HBM about once.
+
+template <int NDIM_, int CIN_, int COUT_, int KS_, int BH_, int BW_, int TS_, int RC_>
+struct RingCfg {
+  static constexpr int NDIM = NDIM_, CIN = CIN_, COUT = COUT_, KS = KS_;
+  static constexpr int BH = NDIM == 3 ? BH_ : 1;   // output rows per slice
+  static constexpr int BW = BW_;                    // output columns per slice
+  static constexpr int TS = TS_;                    // output slices per step
+  static constexpr int RC = RC_;                    // output slices per job
+  static constexpr int KH = NDIM == 3 ? KS : 1;     // taps along H inside a slice
+  static constexpr int SH = BH + KH - 1, SW = BW + KS - 1, SLICE = SH * SW;
+  static constexpr int RING = 2 * TS + KS - 1;
+  static constexpr int POS = TS * BH * BW;
+  static constexpr int NWAVES = POS / 64, NT = NWAVES * 64;
+  static constexpr int MB = COUT / 16, NB = 4;
+  static constexpr int TAPS = KS * KH * KS;
+  static constexpr int CK = CIN, KV = TAPS * CK;
+  static constexpr int KSTEPS = (KV + 31) / 32;
+  static constexpr int KU = KSTEPS <= 18 ? KSTEPS
+                            : KSTEPS % 9 == 0 ? 9 : KSTEPS % 7 == 0 ? 7 : KSTEPS % 5 == 0 ? 5
+                            : KSTEPS % 3 == 0 ? 3 : KSTEPS % 2 == 0 ? 2 : 1;
+  static constexpr int KVP = (KV + 63) / 64 * 64;
+  static constexpr int NCH = CK / 8;
+  static constexpr int KEYDIV = NCH >= 8 ? 1 : 8 / NCH;
+  static constexpr int LDS_W = COUT * KVP * 2;
+  static constexpr int LDS_X = RING * SLICE * CK * 2;
+  static constexpr int STEP_CHUNKS = TS * SLICE * NCH;
+  static constexpr int PF = (STEP_CHUNKS + NT - 1) / NT;
+  // weight packing shares the layout of the tile kernel (one channel chunk)
+  static constexpr int NCHUNK = 1, NCB = 1, TD = 1, TH = 1, TW = BW, BN = COUT;
+  static_assert(POS % 64 == 0 && BW % 16 == 0, "a wave covers 64 positions in 16-runs along W");
+  static_assert(COUT % 16 == 0 && CK % 8 == 0 && (CK >= 32 ? CK % 32 == 0 : 32 % CK == 0), "shape");
+  static_assert(RC % TS == 0, "job length");
+  static_assert(LDS_W + LDS_X + COUT * 4 <= 160 * 1024, "LDS budget");
+};
+
+template <class C>
+__device__ __forceinline__ int rxoff(int q, int j) {
+  return q * C::CK + 8 * (j ^ ((q / C::KEYDIV) % C::NCH));
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void conv_ring(const ConvArgs args) {
+  __shared__ __attribute__((aligned(16))) uint16_t sw[C::LDS_W / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t sx[C::LDS_X / 2];
+  __shared__ uint32_t smax[C::COUT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+  const bool want_max = args.ymax != nullptr;
+  constexpr int RA = C::NDIM == 3 ? 0 : 1;          // internal index of the streamed axis
+
+  for (int i = tid; i < C::COUT; i += C::NT) smax[i] = 0u;
+  {  // resident weights, rows swizzled by (row & 7)
+    constexpr int CPR = C::KVP / 8;
+    for (int i = tid; i < C::COUT * CPR; i += C::NT) {
+      const int m = i / CPR, j = i - m * CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(args.w + (size_t)m * C::KVP + 8 * j);
+      *reinterpret_cast<uint4*>(sw + m * C::KVP + 8 * (j ^ (m & 7))) = v;
+    }
+  }
+
+  // this lane's B-operand positions: slice ts, row ph, column pw of the step
+  int tsl[C::NB], qoff[C::NB], phh[C::NB], pww[C::NB];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) {
+    const int p = wave * 64 + nb * 16 + l16;
+    tsl[nb] = p / (C::BH * C::BW);
+    phh[nb] = (p / C::BW) % C::BH;
+    pww[nb] = p % C::BW;
+    qoff[nb] = phh[nb] * C::SW + pww[nb];
+  }
+
+  const int total = args.total_tiles;
+  int j0 = blockIdx.x, jstride = gridDim.x, j_end = total;
+  if (gridDim.x >= 8 && (gridDim.x & 7) == 0) {
+    const int xcd = blockIdx.x & 7;
+    j0 = (int)((int64_t)total * xcd / 8) + (blockIdx.x >> 3);
+    jstride = gridDim.x >> 3;
+    j_end = (int)((int64_t)total * (xcd + 1) / 8);
+  }
+
+  float runmax[C::MB][4];
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) runmax[mb][i] = 0.f;
+  int cur_n = -1;
+
+  auto flush = [&](int n) {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = runmax[mb][i];
+        v = fmaxf(v, __shfl_xor(v, 1));
+        v = fmaxf(v, __shfl_xor(v, 2));
+        v = fmaxf(v, __shfl_xor(v, 4));
+        v = fmaxf(v, __shfl_xor(v, 8));
+        runmax[mb][i] = 0.f;
+        if (l16 == 0) atomicMax(&smax[mb * 16 + 4 * g4 + i], __float_as_uint(v));
+      }
+    __syncthreads();
+    const int gs = C::COUT / args.groups;
+    for (int g = tid; g < args.groups; g += C::NT) {
+      uint32_t m = 0;
+      for (int c = g * gs; c < (g + 1) * gs; ++c) m = max(m, smax[c]);
+      atomicMax(&args.ymax[n * args.groups + g], m);
+    }
+    __syncthreads();
+    for (int i = tid; i < C::COUT; i += C::NT) smax[i] = 0u;
+  };
+
+  for (int job = j0; job < j_end; job += jstride) {
+    int s = 0;
+    while (s + 1 < args.nshards && args.sh[s + 1].tile_begin <= job) ++s;
+    const ConvShardArg& sh = args.sh[s];
+    // job -> (n, chunk of slices, strip row, strip column); columns innermost
+    const int strips = sh.tiles_h * sh.tiles_w;
+    int r = job - sh.tile_begin;
+    const int per_n = sh.tiles_d * strips;
+    const int n = r / per_n;
+    r -= n * per_n;
+    const int chunk = r / strips;
+    r -= chunk * strips;
+    const int sth = r / sh.tiles_w;
+    const int stw = r - sth * sh.tiles_w;
+    const int ext_ring = sh.ext[RA];
+    const int s_begin = chunk * C::RC;
+    const int s_end = min(s_begin + C::RC, ext_ring);
+    const int h0 = sth * C::BH, w0 = stw * C::BW;
+    const int o_ring = args.origin[RA], o_h = args.origin[1], o_w = args.origin[2];
+    const int p0 = sh.pad[0], p1 = sh.pad[1], p2 = sh.pad[2];
+    const int a_lim = s_end + C::KS - 1;           // input slices this job needs: [s_begin, a_lim)
+
+    if (want_max && n != cur_n) {
+      if (cur_n >= 0) flush(cur_n);
+      cur_n = n;
+    }
+
+    // global element offset of 16-byte piece u of input slice a (or -1)
+    auto piece = [&](int a, int u, int& slot_q, int& j) -> int64_t {
+      const int q = u / C::NCH;
+      j = u - q * C::NCH;
+      const int qr = q / C::SW, qc = q - qr * C::SW;
+      slot_q = (a % C::RING) * C::SLICE + q;
+      const int gr = a + o_ring;
+      const int gh = C::NDIM == 3 ? h0 + qr + o_h : gr;
+      const int gd = C::NDIM == 3 ? gr : 0;
+      const int gw = w0 + qc + o_w;
+      if (a >= a_lim || gd >= p0 || gh >= p1 || gw >= p2) return -1;
+      return ((((int64_t)n * p0 + gd) * p1 + gh) * p2 + gw) * C::CIN + 8 * j;
+    };
+
+    // prologue: the first step's TS + k - 1 slices
+    for (int u = tid; u < (C::TS + C::KS - 1) * C::SLICE * C::NCH; u += C::NT) {
+      const int rel = u / (C::SLICE * C::NCH);
+      int q, j;
+      const int64_t off = piece(s_begin + rel, u - rel * C::SLICE * C::NCH, q, j);
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (off >= 0) v = *reinterpret_cast<const uint4*>(sh.in + off);
+      *reinterpret_cast<uint4*>(sx + rxoff<C>(q, j)) = v;
+    }
+    __syncthreads();
+
+    for (int cur = s_begin; cur < s_end; cur += C::TS) {
+      // 1. prefetch the next step's new slices into registers
+      uint4 pf[C::PF];
+      int pf_q[C::PF], pf_j[C::PF];
+      const bool more = cur + C::TS < s_end;
+#pragma unroll
+      for (int k = 0; k < C::PF; ++k) {
+        const int u = tid + k * C::NT;
+        pf[k] = uint4{0u, 0u, 0u, 0u};
+        pf_q[k] = -1;
+        pf_j[k] = 0;
+        if (more && u < C::STEP_CHUNKS) {
+          const int rel = u / (C::SLICE * C::NCH);
+          int q, j;
+          const int64_t off = piece(cur + C::TS + C::KS - 1 + rel, u - rel * C::SLICE * C::NCH, q, j);
+          pf_q[k] = q;
+          pf_j[k] = j;
+          if (off >= 0) pf[k] = *reinterpret_cast<const uint4*>(sh.in + off);
+        }
+      }
+
+      // 2. matrix-core work of this step
+      f32x4 acc[C::MB][C::NB];
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int base = cur % C::RING;
+#pragma unroll 1
+      for (int ko = 0; ko < C::KSTEPS; ko += C::KU)
+#pragma unroll
+        for (int ki = 0; ki < C::KU; ++ki) {
+          const int ks = ko + ki;
+          const int tap_lo = (32 * ks) / C::CK;
+          const int tap = C::CK >= 32 ? tap_lo : tap_lo + (g4 >> 1);
+          const int c0 = C::CK >= 32 ? (32 * ks) % C::CK + 8 * g4 : 8 * (g4 & 1);
+          const bool valid = tap < C::TAPS;
+          const int tw = tap % C::KS;
+          const int th = (tap / C::KS) % C::KH;
+          const int tr = tap / (C::KS * C::KH);
+          bf16x8 a[C::MB], b[C::NB];
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb) {
+            const int m = mb * 16 + l16;
+            a[mb] = *reinterpret_cast<const bf16x8*>(sw + m * C::KVP + 8 * ((4 * ks + g4) ^ (lane & 7)));
+          }
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb) {
+            int slot = base + tsl[nb] + tr;
+            slot -= slot >= C::RING ? C::RING : 0;
+            const int q = slot * C::SLICE + qoff[nb] + th * C::SW + tw;
+            if (valid) b[nb] = *reinterpret_cast<const bf16x8*>(sx + rxoff<C>(q, c0 >> 3));
+            else b[nb] = bf16x8{};
+          }
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+        }
+
+      // 3. epilogue: bias, fp32 stores, running max
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) {
+        const int osl = cur + tsl[nb];
+        const int oh = C::NDIM == 3 ? h0 + phh[nb] : osl;
+        const int od = C::NDIM == 3 ? osl : 0;
+        const int ow = w0 + pww[nb];
+        if (osl >= s_end || oh >= sh.ext[1] || ow >= sh.ext[2]) continue;
+        const size_t cell = (((size_t)n * sh.ext[0] + od) * sh.ext[1] + oh) * sh.ext[2] + ow;
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) {
+          const int co = mb * 16 + 4 * g4;
+          f32x4 v = acc[mb][nb];
+          if (args.bias) {
+            v[0] += args.bias[co + 0];
+            v[1] += args.bias[co + 1];
+            v[2] += args.bias[co + 2];
+            v[3] += args.bias[co + 3];
+          }
+          *reinterpret_cast<f32x4*>(sh.out + cell * C::COUT + co) = v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) runmax[mb][i] = fmaxf(runmax[mb][i], fabsf(v[i]));
+        }
+      }
+
+      // 4. the prefetched slices go into the ring slots this step did not read
+#pragma unroll
+      for (int k = 0; k < C::PF; ++k)
+        if (pf_q[k] >= 0) *reinterpret_cast<uint4*>(sx + rxoff<C>(pf_q[k], pf_j[k])) = pf[k];
+      __syncthreads();
+    }
+  }
+  if (want_max && cur_n >= 0) flush(cur_n);
+}
+
+// --------------------------------------------------------------------------
 // instance table
 // --------------------------------------------------------------------------
 
@@ -526,6 +802,38 @@ st_status run_mfma(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
 }
 
 template <class C>
+st_status run_ring(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
+  constexpr int RA = C::NDIM == 3 ? 0 : 1;
+  int jobs = 0;
+  for (size_t s = 0; s < in_plan->shards.size(); ++s) {
+    const Shard& sd = in_plan->shards[s];
+    ConvShardArg& sh = a.sh[s];
+    sh.tiles_d = (int)((sd.ext[RA] + C::RC - 1) / C::RC);          // slice chunks
+    sh.tiles_h = C::NDIM == 3 ? (int)((sd.ext[1] + C::BH - 1) / C::BH) : 1;
+    sh.tiles_w = (int)((sd.ext[2] + C::BW - 1) / C::BW);
+    sh.tile_begin = jobs;
+    const int64_t t = (int64_t)in_plan->batch * sh.tiles_d * sh.tiles_h * sh.tiles_w;
+    if ((int64_t)jobs + t > INT32_MAX) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: too many jobs");
+    jobs += (int)t;
+  }
+  a.total_tiles = jobs;
+  if (jobs == 0) return ST_OK;
+  int occ = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, conv_ring<C>, C::NT, 0) != hipSuccess || occ < 1)
+    occ = 1;
+  int grid = std::min(jobs, device_cus() * occ);
+  if (grid >= 8) grid &= ~7;
+  hipLaunchKernelGGL(conv_ring<C>, dim3(grid), dim3(C::NT), 0, stream, a);
+  return launch_check("st_conv_sharded: conv_ring launch");
+}
+
+template <class C>
+constexpr Instance inst_ring() {
+  return Instance{C::NDIM, C::CIN, C::COUT, C::KS, C::CK, C::KVP, C::NT,
+                  1, C::BH, C::BW, 1, C::LDS_W + C::LDS_X, &run_ring<C>};
+}
+
+template <class C>
 constexpr Instance inst() {
   return Instance{C::NDIM, C::CIN, C::COUT, C::KS, C::CK, C::KVP, C::NT,
                   C::TD, C::TH, C::TW, C::NCB, C::LDS_W + C::LDS_X, &run_mfma<C>};
@@ -540,11 +848,23 @@ using CfgVol16k5 = Cfg<3, 16, 16, 5, 4, 4, 32, 16, 16, 1>;
 // 2D 256->256 k3: 2x128 box, 128 output channels per block, 32-channel chunks
 using CfgImg256 = Cfg<2, 256, 256, 3, 1, 2, 128, 128, 32, 2>;
 
+// streaming instances (weights resident, ring of input slices)
+// 2D 64->64 k3: 64-column strips, 4 rows per step, 32 rows per job
+using RingImg64 = RingCfg<2, 64, 64, 3, 1, 64, 4, 32>;
+// 3D 32->32 k3: 8x32 strips, 1 plane per step, 16 planes per job
+using RingVol32 = RingCfg<3, 32, 32, 3, 8, 32, 1, 16>;
+// 3D 16->16 k5: 8x32 strips, 1 plane per step, 16 planes per job
+using RingVol16k5 = RingCfg<3, 16, 16, 5, 8, 32, 1, 16>;
+
+// first match wins
 const Instance kInstances[] = {
+    inst_ring<RingImg64>(),
+    inst_ring<RingVol32>(),
+    inst_ring<RingVol16k5>(),
+    inst<CfgImg256>(),
     inst<CfgImg64>(),
     inst<CfgVol32>(),
     inst<CfgVol16k5>(),
-    inst<CfgImg256>(),
 };
 
 const Instance* find_instance(int ndim, int cin, int cout, int ks) {

@@ -97,7 +97,7 @@ __global__ void gn_fill(uint32_t* __restrict__ p, int64_t n) {
 template <int VW, bool FIXED>
 __global__ __launch_bounds__(kNT) void gn_max(const GnArgs a) {
   using V = Vec<VW>;
-  __shared__ uint32_t smax[1024];
+  extern __shared__ uint32_t smax[];   // C entries
   const int tid = threadIdx.x;
   const int C = a.channels;
   for (int i = tid; i < C; i += kNT) smax[i] = 0u;
@@ -135,17 +135,21 @@ __global__ __launch_bounds__(kNT) void gn_max(const GnArgs a) {
     }
     const GnShard& sh = a.sh[s];
     const typename V::T* y = reinterpret_cast<const typename V::T*>(sh.y) + n * sh.vecs_per_n;
-    const int64_t v0 = (int64_t)k * kNT * kIter;
-#pragma unroll 4
+    const int64_t v0 = (int64_t)k * kNT * kIter + tid;
+    typename V::T val[kIter];
+#pragma unroll
     for (int i = 0; i < kIter; ++i) {
-      const int64_t v = v0 + i * kNT + tid;
-      if (v >= sh.vecs_per_n) break;
-      const typename V::T val = y[v];
+      const int64_t v = v0 + i * kNT;
+      val[i] = v < sh.vecs_per_n ? y[v] : typename V::T{};
+    }
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      const int64_t v = v0 + i * kNT;
 #pragma unroll
       for (int j = 0; j < VW; ++j) {
-        const float f = fabsf(V::get(val, j));
+        const float f = fabsf(V::get(val[i], j));
         if (FIXED) mx[j] = fmaxf(mx[j], f);
-        else atomicMax(&smax[(int)((v * VW + j) % C)], __float_as_uint(f));
+        else if (v < sh.vecs_per_n) atomicMax(&smax[(int)((v * VW + j) % C)], __float_as_uint(f));
       }
     }
   }
@@ -155,12 +159,13 @@ __global__ __launch_bounds__(kNT) void gn_max(const GnArgs a) {
 template <int VW, bool FIXED>
 __global__ __launch_bounds__(kNT) void gn_stats(const GnArgs a) {
   using V = Vec<VW>;
-  __shared__ double s1[1024];
-  __shared__ double s2[1024];
-  __shared__ double sc1[1024];   // 2^e1 per channel of the current batch item
-  __shared__ double sc2[1024];
+  extern __shared__ double gn_lds[];   // 4*C: sums, sums of squares, 2^e1, 2^e2 per channel
   const int tid = threadIdx.x;
   const int C = a.channels;
+  double* s1 = gn_lds;
+  double* s2 = gn_lds + C;
+  double* sc1 = gn_lds + 2 * C;
+  double* sc2 = gn_lds + 3 * C;
   const int gs = C / a.groups;
   if (blockIdx.x == 0) {
     for (int i = tid; i < a.batch * a.groups; i += kNT) {
@@ -224,19 +229,23 @@ __global__ __launch_bounds__(kNT) void gn_stats(const GnArgs a) {
     }
     const GnShard& sh = a.sh[s];
     const typename V::T* y = reinterpret_cast<const typename V::T*>(sh.y) + n * sh.vecs_per_n;
-    const int64_t v0 = (int64_t)k * kNT * kIter;
-#pragma unroll 4
+    const int64_t v0 = (int64_t)k * kNT * kIter + tid;
+    typename V::T val[kIter];
+#pragma unroll
     for (int i = 0; i < kIter; ++i) {
-      const int64_t v = v0 + i * kNT + tid;
-      if (v >= sh.vecs_per_n) break;
-      const typename V::T val = y[v];
+      const int64_t v = v0 + i * kNT;
+      val[i] = v < sh.vecs_per_n ? y[v] : typename V::T{};   // zeros contribute 0
+    }
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      const int64_t v = v0 + i * kNT;
 #pragma unroll
       for (int j = 0; j < VW; ++j) {
-        const double d = (double)V::get(val, j);
+        const double d = (double)V::get(val[i], j);
         if (FIXED) {
           acc1[j] += rint(d * f1[j]);
           acc2[j] += rint((d * d) * f2[j]);
-        } else {
+        } else if (v < sh.vecs_per_n) {
           const int c = (int)((v * VW + j) % C);
           atomicAdd(&s1[c], rint(d * sc1[c]));
           atomicAdd(&s2[c], rint((d * d) * sc2[c]));
@@ -293,22 +302,30 @@ __global__ __launch_bounds__(kNT) void gn_apply(const GnArgs a) {
     const GnShard& sh = a.sh[s];
     const typename V::T* y = reinterpret_cast<const typename V::T*>(sh.y) + n * sh.vecs_per_n;
     typename V::T* z = reinterpret_cast<typename V::T*>(sh.z) + n * sh.vecs_per_n;
-    const int64_t v0 = (int64_t)k * kNT * kIter;
-#pragma unroll 4
+    const int64_t v0 = (int64_t)k * kNT * kIter + tid;
+    typename V::T val[kIter];
+#pragma unroll
     for (int i = 0; i < kIter; ++i) {
-      const int64_t v = v0 + i * kNT + tid;
+      const int64_t v = v0 + i * kNT;
+      val[i] = v < sh.vecs_per_n ? y[v] : typename V::T{};
+    }
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      const int64_t v = v0 + i * kNT;
       if (v >= sh.vecs_per_n) break;
-      typename V::T val = y[v];
       float out[VW];
 #pragma unroll
       for (int j = 0; j < VW; ++j) {
         float4 q;
         if (FIXED) q = p[j];
         else q = a.chan[(size_t)n * C + (int)((v * VW + j) % C)];
-        out[j] = fmaf(V::get(val, j) - q.x, q.y, q.z);
+        out[j] = fmaf(V::get(val[i], j) - q.x, q.y, q.z);
       }
-      if constexpr (VW == 4) z[v] = make_float4(out[0], out[1], out[2], out[3]);
-      else z[v] = out[0];
+      if constexpr (VW == 4) {
+        typedef float nf4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(nf4{out[0], out[1], out[2], out[3]}, reinterpret_cast<nf4*>(&z[v]));
+      }
+      else __builtin_nontemporal_store(out[0], &z[v]);
     }
   }
 }
@@ -417,11 +434,11 @@ template <int VW, bool FIXED>
 st_status launch_partials(GnArgs& a, bool need_max, hipStream_t st) {
   const int grid = grid_of(a);
   if (need_max) {
-    hipLaunchKernelGGL((gn_max<VW, FIXED>), dim3(grid), dim3(kNT), 0, st, a);
+    hipLaunchKernelGGL((gn_max<VW, FIXED>), dim3(grid), dim3(kNT), (size_t)a.channels * 4, st, a);
     st_status s = launch_check("st_groupnorm_partials: max launch");
     if (s != ST_OK) return s;
   }
-  hipLaunchKernelGGL((gn_stats<VW, FIXED>), dim3(grid), dim3(kNT), 0, st, a);
+  hipLaunchKernelGGL((gn_stats<VW, FIXED>), dim3(grid), dim3(kNT), (size_t)a.channels * 32, st, a);
   return launch_check("st_groupnorm_partials: stats launch");
 }
 

@@ -85,9 +85,10 @@ def conv_valid(xp: np.ndarray, w: np.ndarray, bias=None) -> np.ndarray:
         y += np.asarray(bias, dtype=np.float64)
     for t in _taps(k, d):
         window = xp[(slice(None),) + tuple(slice(t[a], t[a] + s_out[a]) for a in range(d))]
-        wt = w[(slice(None), slice(None)) + t]            # [Cout, Cin]
+        # [Cin, Cout] of this tap, contiguous so the product goes to BLAS
+        wt = np.ascontiguousarray(w[(slice(None), slice(None)) + t].T)
         rows = np.ascontiguousarray(window).reshape(-1, cin)
-        y += (rows @ wt.T).reshape(y.shape)
+        y += (rows @ wt).reshape(y.shape)
     return y
 
 
