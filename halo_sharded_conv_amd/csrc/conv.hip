@@ -49,6 +49,7 @@ struct ConvArgs {
   int32_t nshards;
   int32_t total_tiles;
   int32_t groups;
+  int32_t batch;
   int32_t origin[3];          // halo - ksize/2 per axis
   const uint16_t* w;          // packed weights
   const float* bias;          // or null
@@ -87,9 +88,9 @@ struct Cfg {
   static constexpr int KU = KSTEPS <= 18 ? KSTEPS
                             : KSTEPS % 9 == 0 ? 9 : KSTEPS % 7 == 0 ? 7 : KSTEPS % 5 == 0 ? 5
                             : KSTEPS % 3 == 0 ? 3 : KSTEPS % 2 == 0 ? 2 : 1;
-  static constexpr int KVP = (KV + 63) / 64 * 64;
+  static constexpr int KVP = ((KV + 63) / 64) % 2 == 1 ? (KV + 63) / 64 * 64 : (KV + 63) / 64 * 64 + 64;
   static constexpr int NCH = CK / 8;
-  static constexpr int KEYDIV = NCH >= 8 ? 1 : 8 / NCH;
+  static constexpr int KEYDIV = NCH >= 16 ? 1 : 16 / NCH;
   static constexpr int NCHUNK = CIN / CK;
   static constexpr int NCB = COUT / BN;
   static constexpr bool RESIDENT = NCHUNK == 1 && NCB == 1;
@@ -116,7 +117,7 @@ __device__ __forceinline__ void stage_w(uint16_t* sw, const uint16_t* __restrict
   for (int i = threadIdx.x; i < C::BN * CPR; i += C::NT) {
     const int m = i / CPR, j = i - m * CPR;
     const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)m * C::KVP + 8 * j);
-    *reinterpret_cast<uint4*>(sw + m * C::KVP + 8 * (j ^ (m & 7))) = v;
+    *reinterpret_cast<uint4*>(sw + m * C::KVP + 8 * (j ^ ((m >> 1) & 7))) = v;
   }
 }
 
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(C::NT) void conv_mfma(const ConvArgs args) {
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb) {
           const int m = wn * C::NW + mb * 16 + l16;
-          a[mb] = *reinterpret_cast<const bf16x8*>(sw + m * C::KVP + 8 * ((4 * ks + g4) ^ (lane & 7)));
+          a[mb] = *reinterpret_cast<const bf16x8*>(sw + m * C::KVP + 8 * ((4 * ks + g4) ^ ((lane & 15) >> 1)));
         }
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
@@ -509,9 +510,9 @@ struct RingCfg {
   static constexpr int KU = KSTEPS <= 18 ? KSTEPS
                             : KSTEPS % 9 == 0 ? 9 : KSTEPS % 7 == 0 ? 7 : KSTEPS % 5 == 0 ? 5
                             : KSTEPS % 3 == 0 ? 3 : KSTEPS % 2 == 0 ? 2 : 1;
-  static constexpr int KVP = (KV + 63) / 64 * 64;
+  static constexpr int KVP = ((KV + 63) / 64) % 2 == 1 ? (KV + 63) / 64 * 64 : (KV + 63) / 64 * 64 + 64;
   static constexpr int NCH = CK / 8;
-  static constexpr int KEYDIV = NCH >= 8 ? 1 : 8 / NCH;
+  static constexpr int KEYDIV = NCH >= 16 ? 1 : 16 / NCH;
   static constexpr int LDS_W = COUT * KVP * 2;
   static constexpr int LDS_X = RING * SLICE * CK * 2;
   static constexpr int STEP_CHUNKS = TS * SLICE * NCH;
@@ -544,12 +545,12 @@ __global__ __launch_bounds__(C::NT) void conv_ring(const ConvArgs args) {
   constexpr int RA = C::NDIM == 3 ? 0 : 1;          // internal index of the streamed axis
 
   for (int i = tid; i < C::COUT; i += C::NT) smax[i] = 0u;
-  {  // resident weights, rows swizzled by (row & 7)
+  {  // resident weights, chunk j of row m stored at j ^ ((m >> 1) & 7)
     constexpr int CPR = C::KVP / 8;
     for (int i = tid; i < C::COUT * CPR; i += C::NT) {
       const int m = i / CPR, j = i - m * CPR;
       const uint4 v = *reinterpret_cast<const uint4*>(args.w + (size_t)m * C::KVP + 8 * j);
-      *reinterpret_cast<uint4*>(sw + m * C::KVP + 8 * (j ^ (m & 7))) = v;
+      *reinterpret_cast<uint4*>(sw + m * C::KVP + 8 * (j ^ ((m >> 1) & 7))) = v;
     }
   }
 
@@ -700,7 +701,7 @@ __global__ __launch_bounds__(C::NT) void conv_ring(const ConvArgs args) {
 #pragma unroll
           for (int mb = 0; mb < C::MB; ++mb) {
             const int m = mb * 16 + l16;
-            a[mb] = *reinterpret_cast<const bf16x8*>(sw + m * C::KVP + 8 * ((4 * ks + g4) ^ (lane & 7)));
+            a[mb] = *reinterpret_cast<const bf16x8*>(sw + m * C::KVP + 8 * ((4 * ks + g4) ^ ((lane & 15) >> 1)));
           }
 #pragma unroll
           for (int nb = 0; nb < C::NB; ++nb) {
@@ -751,6 +752,33 @@ __global__ __launch_bounds__(C::NT) void conv_ring(const ConvArgs args) {
   }
   if (want_max && cur_n >= 0) flush(cur_n);
 }
+
+// --------------------------------------------------------------------------
+// helpers of the v_mfma_f32_32x32x16_bf16 kernels
+// --------------------------------------------------------------------------
+//
+// All global traffic of these kernels uses range-checked buffer instructions:
+// a lane whose cell lies outside the shard gets an out-of-range offset, so
+// its load returns 0 and its store is dropped, and the loop bodies carry no
+// branches around memory operations.
+//
+// Output layout of a 32x32 block in a lane: column (position) = lane % 32,
+// rows (channels) 8j + 4*(lane/32) + i for accumulator element 4j + i.
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr uint32_t kOob = 0x80000000u;        // offset beyond every num_records used
+constexpr uint32_t kBufFlags = 0x00020000u;   // raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, (int)kBufFlags);
+}
+
+// Swizzle of input cells: chunk j of the cell in strip column qc sits at
+// chunk j ^ key(qc).  16 lanes reading 16 consecutive columns at one chunk
+// then hit 16 distinct 16-byte slots of a 256-byte LDS window.
+template <class C>
+__device__ __forceinline__ int cell_key(int qc) { return (qc / C::KD) % C::NCH; }
 
 // --------------------------------------------------------------------------
 // instance table
@@ -827,6 +855,447 @@ st_status run_ring(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
   return launch_check("st_conv_sharded: conv_ring launch");
 }
 
+
+// --------------------------------------------------------------------------
+// streaming implicit GEMM with operand reuse along the streamed axis
+// --------------------------------------------------------------------------
+//
+// A wave owns RW consecutive output slices (rows in 2D, planes in 3D) of one
+// 32-position run along W, for every output channel.  Along the streamed axis
+// the kernel's taps shift by whole slices, so for one in-slice tap and one
+// 16-channel K chunk the wave reads the RW + k - 1 input fragments of its
+// slices once and the k weight fragments of the streamed-axis taps once, and
+// issues RW * k matrix instructions per 32 output channels from them:
+// (RW + k - 1 + k * MB) LDS reads per RW * k * MB MFMAs instead of
+// (MB + 1) per MB.
+//
+// The ring holds exactly the TS + k - 1 input slices one step reads.  The
+// TS slices of the next step are fetched into registers while the step
+// computes and written over the TS oldest slices between two barriers; the
+// next job's first TS + k - 1 slices travel the same way during a job's last
+// step, so a block never waits on HBM latency between jobs.
+
+template <int NDIM_, int CIN_, int COUT_, int KS_, int BH_, int BW_, int TS_, int RC_, int RW_>
+struct RowsCfg {
+  static constexpr int NDIM = NDIM_, CIN = CIN_, COUT = COUT_, KS = KS_;
+  static constexpr int BH = NDIM == 3 ? BH_ : 1;
+  static constexpr int BW = BW_, TS = TS_, RC = RC_, RW = RW_;
+  static constexpr int KH = NDIM == 3 ? KS : 1;
+  static constexpr int SH = BH + KH - 1, SW = BW + KS - 1, SLICE = SH * SW;
+  static constexpr int RING = TS + KS - 1;
+  static constexpr int PG = BH * BW / 32;             // 32-position runs per slice
+  static constexpr int RG = TS / RW;                  // slice groups per step
+  static constexpr int NWAVES = PG * RG, NT = NWAVES * 64;
+  static constexpr int MB = COUT / 32;
+  static constexpr int NIN = RW + KS - 1;             // input fragments per K chunk
+  static constexpr int TAPS = KS * KH * KS;
+  static constexpr int CK = CIN, KV = TAPS * CK;
+  static constexpr int KCS = CK / 16;
+  static constexpr int KVP = ((KV + 63) / 64) % 2 == 1 ? (KV + 63) / 64 * 64 : (KV + 63) / 64 * 64 + 64;
+  static constexpr int NCH = CK / 8, CB = CK * 2, KD = 16 / NCH;
+  static constexpr int LDS_W = COUT * KVP * 2;
+  static constexpr int LDS_X = RING * SLICE * CB;
+  static constexpr int STEP_CHUNKS = TS * SLICE * NCH;
+  static constexpr int PRO_CHUNKS = RING * SLICE * NCH;
+  static constexpr int PF = (PRO_CHUNKS + NT - 1) / NT;
+  static constexpr int PFS = (STEP_CHUNKS + NT - 1) / NT;
+  static constexpr int NCHUNK = 1, NCB = 1, TD = 1, TH = 1, TW = BW, BN = COUT;
+  static_assert(CIN % 16 == 0 && NCH <= 16 && COUT % 32 == 0, "shape");
+  static_assert(BW % 32 == 0 && TS % RW == 0 && RC % TS == 0, "tiling");
+  static_assert(NT <= 1024, "block size");
+  static_assert(LDS_W + LDS_X + COUT * 8 <= 160 * 1024, "LDS budget");
+};
+
+// MAXG: the running max|y| is kept per 4, 2 or 1 channels (a divisor of the
+// group size), or not at all (0)
+template <class C, bool BIAS, int MAXG>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NT / 256, C::NT / 256))) void conv_rows(const ConvArgs args) {
+  __shared__ __attribute__((aligned(16))) uint16_t sw[C::LDS_W / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t sx[C::LDS_X / 2];
+  __shared__ __attribute__((aligned(16))) float sbias[C::COUT];
+  __shared__ uint32_t smax[C::COUT];
+  char* const swb = reinterpret_cast<char*>(sw);
+  char* const sxb = reinterpret_cast<char*>(sx);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int pg = wave % C::PG;
+  const int t0 = (wave / C::PG) * C::RW;            // first output slice of this wave within a step
+  const int l32 = lane & 31;
+  const int g2 = lane >> 5;
+  constexpr int RA = C::NDIM == 3 ? 0 : 1;
+  constexpr int RSB = C::KVP * 2;
+  constexpr bool MAXV = MAXG > 0;
+  constexpr int MG = MAXG > 0 ? MAXG : 1;
+  constexpr int NMX = 16 / MG;                      // running-max slots per 32-channel block
+
+  for (int i = tid; i < C::COUT; i += C::NT) {
+    smax[i] = 0u;
+    sbias[i] = BIAS ? args.bias[i] : 0.f;
+  }
+  {  // resident weights: chunk j of row m at chunk (j & ~7) | ((j & 7) ^ ((m >> 1) & 7))
+    constexpr int CPR = C::KVP / 8;
+    for (int i = tid; i < C::COUT * CPR; i += C::NT) {
+      const int m = i / CPR, j = i - m * CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(args.w + (size_t)m * C::KVP + 8 * j);
+      *reinterpret_cast<uint4*>(swb + m * RSB + 16 * ((j & ~7) | ((j & 7) ^ ((m >> 1) & 7)))) = v;
+    }
+  }
+
+  int ybase[C::MB];
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) {
+    const int m = mb * 32 + l32;
+    ybase[mb] = (m * RSB + 16 * ((m >> 1) & 7)) ^ (16 * g2);
+  }
+  const int p = pg * 32 + l32;
+  const int ph = p / C::BW, pw = p % C::BW;
+  int lcol[C::KS];
+#pragma unroll
+  for (int tw = 0; tw < C::KS; ++tw) {
+    const int qc = pw + tw;
+    lcol[tw] = ((ph * C::SW + qc) * C::CB + 16 * cell_key<C>(qc)) ^ (16 * g2);
+  }
+  const int co_lane = 4 * g2;
+
+  const int total = args.total_tiles;
+  int j0 = blockIdx.x, jstride = gridDim.x, j_end = total;
+  if (gridDim.x >= 8 && (gridDim.x & 7) == 0) {
+    const int xcd = blockIdx.x & 7;
+    j0 = (int)((int64_t)total * xcd / 8) + (blockIdx.x >> 3);
+    jstride = gridDim.x >> 3;
+    j_end = (int)((int64_t)total * (xcd + 1) / 8);
+  }
+
+  // slot i covers accumulator elements i*MG .. i*MG+MG-1: channels
+  // co_lane + 32*mb + 8*((i*MG)/4) + (i*MG)%4 and the next MG-1
+  float runmax[C::MB][NMX];
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < NMX; ++i) runmax[mb][i] = 0.f;
+  int cur_n = -1;
+
+  auto flush = [&](int n) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < NMX; ++i) {
+        float v = runmax[mb][i];
+        v = fmaxf(v, __shfl_xor(v, 1));
+        v = fmaxf(v, __shfl_xor(v, 2));
+        v = fmaxf(v, __shfl_xor(v, 4));
+        v = fmaxf(v, __shfl_xor(v, 8));
+        v = fmaxf(v, __shfl_xor(v, 16));
+        runmax[mb][i] = 0.f;
+        const int e = i * MG;
+        if (l32 == 0) atomicMax(&smax[co_lane + mb * 32 + 8 * (e >> 2) + (e & 3)], __float_as_uint(v));
+      }
+    __syncthreads();
+    const int gs = C::COUT / args.groups;
+    for (int g = tid; g < args.groups; g += C::NT) {
+      uint32_t m = 0;
+      for (int c = g * gs; c < (g + 1) * gs; ++c) m = max(m, smax[c]);
+      atomicMax(&args.ymax[n * args.groups + g], m);
+    }
+    __syncthreads();
+    for (int i = tid; i < C::COUT; i += C::NT) smax[i] = 0u;
+  };
+
+  // A job is one strip (h0, w0) of one shard and sample, rows [s_begin, s_end)
+  // of the streamed axis.  Uniform across the workgroup.
+  struct Job {
+    int valid, n, s_begin, s_end, h0, w0, o_ring, o_h, o_w, p1, p2, e1, e2, a_lim, ring_pad;
+    uint32_t in_slice_b;
+    int64_t out_cells;
+    __amdgpu_buffer_rsrc_t rin, rout;
+  };
+  auto make_job = [&](int job) __attribute__((always_inline)) {
+    Job J;
+    J.valid = job < j_end;
+    const int jj = J.valid ? job : j0;
+    int s = 0;
+    while (s + 1 < args.nshards && args.sh[s + 1].tile_begin <= jj) ++s;
+    const ConvShardArg& sh = args.sh[s];
+    const int strips = sh.tiles_h * sh.tiles_w;
+    int r = jj - sh.tile_begin;
+    const int per_n = sh.tiles_d * strips;
+    J.n = r / per_n;
+    r -= J.n * per_n;
+    const int chunk = r / strips;
+    r -= chunk * strips;
+    const int sth = r / sh.tiles_w;
+    const int stw = r - sth * sh.tiles_w;
+    J.s_begin = chunk * C::RC;
+    J.s_end = min(J.s_begin + C::RC, sh.ext[RA]);
+    J.h0 = sth * C::BH;
+    J.w0 = stw * C::BW;
+    J.o_ring = args.origin[RA];
+    J.o_h = args.origin[1];
+    J.o_w = args.origin[2];
+    const int p0 = sh.pad[0];
+    J.p1 = sh.pad[1];
+    J.p2 = sh.pad[2];
+    J.e1 = sh.ext[1];
+    J.e2 = sh.ext[2];
+    J.a_lim = J.s_end + C::KS - 1;
+    J.ring_pad = C::NDIM == 3 ? p0 : J.p1;
+    const int64_t in_slice = C::NDIM == 3 ? (int64_t)J.p1 * J.p2 * C::CIN : (int64_t)J.p2 * C::CIN;
+    const int64_t in_base = C::NDIM == 3 ? ((int64_t)J.n * p0 + J.s_begin + J.o_ring) * in_slice
+                                         : ((int64_t)J.n * J.p1 + J.s_begin + J.o_ring) * in_slice;
+    const int64_t in_total = (int64_t)args.batch * p0 * J.p1 * J.p2 * C::CIN;
+    J.rin = make_rsrc(sh.in + in_base, J.valid ? (in_total - in_base) * 2 : 0);
+    J.out_cells = C::NDIM == 3 ? (int64_t)J.e1 * J.e2 : (int64_t)J.e2;
+    const int64_t out_base = (C::NDIM == 3 ? ((int64_t)J.n * sh.ext[0] + J.s_begin)
+                                           : ((int64_t)J.n * J.e1 + J.s_begin)) * J.out_cells * C::COUT;
+    const int64_t out_total = (int64_t)args.batch * sh.ext[0] * J.e1 * J.e2 * C::COUT;
+    J.rout = make_rsrc(sh.out + out_base, J.valid ? (out_total - out_base) * 4 : 0);
+    J.in_slice_b = (uint32_t)(in_slice * 2);
+    return J;
+  };
+  // global byte offset of 16-byte piece u of the slice run starting at row a0,
+  // or kOob outside the padded shard, the job's rows or the first lim pieces
+  auto piece_off = [&](const Job& J, int u, int lim, int a0) __attribute__((always_inline)) -> uint32_t {
+    const int rel = u / (C::SLICE * C::NCH);
+    const int pc = u - rel * C::SLICE * C::NCH;
+    const int q = pc / C::NCH;
+    const int j = pc - q * C::NCH;
+    const int qr = q / C::SW, qc = q - qr * C::SW;
+    const int gh = J.h0 + qr + J.o_h, gw = J.w0 + qc + J.o_w;
+    const int a = a0 + rel;
+    const bool ok = u < lim && (C::NDIM == 2 || gh < J.p1) && gw < J.p2 && a < J.a_lim && a + J.o_ring < J.ring_pad;
+    const uint32_t goff = (uint32_t)((((C::NDIM == 3 ? (int64_t)gh * J.p2 : 0) + gw) * C::CIN + 8 * j) * 2);
+    return ok ? goff + (uint32_t)(a - J.s_begin) * J.in_slice_b : kOob;
+  };
+  // LDS byte offset of piece u of the slice run starting at row a0
+  auto piece_lds = [&](int u, int a0) __attribute__((always_inline)) -> int {
+    const int rel = u / (C::SLICE * C::NCH);
+    const int pc = u - rel * C::SLICE * C::NCH;
+    const int q = pc / C::NCH;
+    const int j = pc - q * C::NCH;
+    const int qc = q % C::SW;
+    return ((a0 + rel) % C::RING) * (C::SLICE * C::CB) + q * C::CB + 16 * (j ^ cell_key<C>(qc));
+  };
+
+  Job J = make_job(j0);
+  if (!J.valid) return;
+  {  // first job's first TS + k - 1 slices, every load in flight before the first store
+    uint4 v[C::PF];
+#pragma unroll
+    for (int k = 0; k < C::PF; ++k)
+      v[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          J.rin, piece_off(J, tid + k * C::NT, C::PRO_CHUNKS, J.s_begin), 0, 0));
+#pragma unroll
+    for (int k = 0; k < C::PF; ++k)
+      if (tid + k * C::NT < C::PRO_CHUNKS)
+        *reinterpret_cast<uint4*>(sxb + piece_lds(tid + k * C::NT, J.s_begin)) = v[k];
+  }
+  if (MAXV) cur_n = J.n;
+  __syncthreads();
+
+  f32x16 acc[C::RW][C::MB];
+  int job = j0;
+  int cur = J.s_begin;
+  int base = J.s_begin % C::RING;
+  auto step = [&]() __attribute__((always_inline)) -> bool {
+    const bool more = cur + C::TS < J.s_end;
+    Job N = J;
+    if (!more) N = make_job(job + jstride);
+    // 1. the next step's TS slices, or the next job's first TS + k - 1, -> registers;
+    // the loads issue during the first half of the K loop, between MFMAs
+    const int pf_a0 = more ? cur + C::RING : N.s_begin;
+    const int pf_lim = more ? C::STEP_CHUNKS : (N.valid ? C::PRO_CHUNKS : 0);
+    uint4 pf[C::PF];
+    auto issue_pf = [&](int k) __attribute__((always_inline)) {
+      const int u = tid + k * C::NT;
+      const uint32_t off = piece_off(N, u, (more && k >= C::PFS) ? 0 : pf_lim, pf_a0);
+      pf[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(N.rin, off, 0, 0));
+    };
+
+    // 2. matrix-core work; the operands of K chunk i+1 are read during chunk i
+#pragma unroll
+    for (int t = 0; t < C::RW; ++t)
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) acc[t][mb] = f32x16{};
+    int sbase[C::NIN];                                // ring slice byte base of input slice t0 + r
+#pragma unroll
+    for (int r = 0; r < C::NIN; ++r) {
+      int sl = base + t0 + r;
+      sl -= sl >= C::RING ? C::RING : 0;
+      sl -= sl >= C::RING ? C::RING : 0;
+      sbase[r] = sl * (C::SLICE * C::CB);
+    }
+    constexpr int NK = C::KH * C::KS * C::KCS;        // in-slice taps x K chunks
+    auto load_ops = [&](int i, bf16x8 (&a)[C::KS][C::MB], bf16x8 (&b)[C::NIN]) __attribute__((always_inline)) {
+      const int cs = i % C::KCS;
+      const int tw = (i / C::KCS) % C::KS;
+      const int th = i / (C::KCS * C::KS);
+#pragma unroll
+      for (int r = 0; r < C::NIN; ++r)
+        b[r] = *reinterpret_cast<const bf16x8*>(sxb + (((sbase[r] + lcol[tw]) ^ (32 * cs)) + th * C::SW * C::CB));
+#pragma unroll
+      for (int tr = 0; tr < C::KS; ++tr) {
+        const int tap = (tr * C::KH + th) * C::KS + tw;
+        const int jw = tap * C::NCH + 2 * cs;
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+          a[tr][mb] = *reinterpret_cast<const bf16x8*>(swb + ((ybase[mb] ^ (16 * (jw & 7))) + 128 * (jw >> 3)));
+      }
+    };
+    bf16x8 av[2][C::KS][C::MB], bv[2][C::NIN];
+    load_ops(0, av[0], bv[0]);
+    constexpr int NRD = C::NIN + C::KS * C::MB;       // LDS reads per K chunk
+    constexpr int NMF = C::RW * C::KS * C::MB;        // matrix instructions per K chunk
+    constexpr int PF_CHUNKS = NK / 2 > 0 ? NK / 2 : 1;   // K chunks that carry the prefetch loads
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int cb = i & 1;
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < PF_CHUNKS) {
+#pragma unroll
+        for (int k = i * C::PF / PF_CHUNKS; k < (i + 1) * C::PF / PF_CHUNKS; ++k) issue_pf(k);
+      }
+      if (i + 1 < NK) load_ops(i + 1, av[cb ^ 1], bv[cb ^ 1]);
+#pragma unroll
+      for (int tr = 0; tr < C::KS; ++tr)
+#pragma unroll
+        for (int t = 0; t < C::RW; ++t)
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb)
+            acc[t][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cb][tr][mb], bv[cb][t + tr], acc[t][mb], 0, 0, 0);
+      // interleave: the next chunk's reads spread over this chunk's MFMAs
+      if (i + 1 < NK) {
+#pragma unroll
+        for (int g = 0; g < NRD; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, NMF / NRD > 0 ? NMF / NRD : 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // 3. epilogue: bias, range-checked fp32 stores, running max
+    {
+      const int oh = C::NDIM == 3 ? J.h0 + ph : 0;
+      const int ow = J.w0 + pw;
+      const bool in_plane = (C::NDIM == 2 || oh < J.e1) && ow < J.e2;
+#pragma unroll
+      for (int t = 0; t < C::RW; ++t) {
+        const int osl = cur + t0 + t;
+        const bool ok = in_plane && osl < J.s_end;
+        const int64_t cell = (int64_t)(osl - J.s_begin) * J.out_cells + (C::NDIM == 3 ? (int64_t)oh * J.e2 : 0) + ow;
+        const uint32_t cbase = ok ? (uint32_t)((cell * C::COUT + co_lane) * 4) : kOob;
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int co = mb * 32 + 8 * jj;
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = acc[t][mb][4 * jj + i];
+            if (BIAS) {
+              const float4 bv4 = *reinterpret_cast<const float4*>(&sbias[co_lane + co]);
+              v[0] += bv4.x; v[1] += bv4.y; v[2] += bv4.z; v[3] += bv4.w;
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(v, J.rout, cbase + (uint32_t)(co * 4), 0, 0);
+            if (MAXV) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                runmax[mb][(4 * jj + i) / MG] = fmaxf(runmax[mb][(4 * jj + i) / MG], ok ? fabsf(v[i]) : 0.f);
+            }
+          }
+      }
+    }
+
+    // 4. every wave is done with the ring: the fetched slices replace the TS
+    // oldest ones (or the whole ring for the next job)
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int k = 0; k < C::PFS; ++k) {
+        const int u = tid + k * C::NT;
+        if (u < C::STEP_CHUNKS) *reinterpret_cast<uint4*>(sxb + piece_lds(u, cur + C::RING)) = pf[k];
+      }
+      __syncthreads();
+      cur += C::TS;
+      base += C::TS;
+      base -= base >= C::RING ? C::RING : 0;
+    } else {
+      if (!N.valid) return false;
+#pragma unroll
+      for (int k = 0; k < C::PF; ++k) {
+        const int u = tid + k * C::NT;
+        if (u < C::PRO_CHUNKS) *reinterpret_cast<uint4*>(sxb + piece_lds(u, N.s_begin)) = pf[k];
+      }
+      if (MAXV && N.n != cur_n) {
+        flush(cur_n);
+        cur_n = N.n;
+      }
+      __syncthreads();
+      job += jstride;
+      J = N;
+      cur = J.s_begin;
+      base = J.s_begin % C::RING;
+    }
+    return true;
+  };
+  for (;;) {
+    if (!step()) break;
+  }
+  if (MAXV) flush(cur_n);
+}
+
+template <class C>
+st_status run_rows(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
+  constexpr int RA = C::NDIM == 3 ? 0 : 1;
+  int jobs = 0;
+  for (size_t s = 0; s < in_plan->shards.size(); ++s) {
+    const Shard& sd = in_plan->shards[s];
+    ConvShardArg& sh = a.sh[s];
+    // the buffer views of one job must stay below 2 GiB
+    const int64_t in_slice = C::NDIM == 3 ? sd.pad[1] * sd.pad[2] * C::CIN : sd.pad[2] * C::CIN;
+    const int64_t out_slice = C::NDIM == 3 ? sd.ext[1] * sd.ext[2] * C::COUT : sd.ext[2] * C::COUT;
+    if ((C::RC + C::TS + C::KS) * in_slice * 2 >= 0x7FFFFFFF || C::RC * out_slice * 4 >= 0x7FFFFFFF)
+      return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: slices too large for the streaming kernel");
+    sh.tiles_d = (int)((sd.ext[RA] + C::RC - 1) / C::RC);
+    sh.tiles_h = C::NDIM == 3 ? (int)((sd.ext[1] + C::BH - 1) / C::BH) : 1;
+    sh.tiles_w = (int)((sd.ext[2] + C::BW - 1) / C::BW);
+    sh.tile_begin = jobs;
+    const int64_t t = (int64_t)in_plan->batch * sh.tiles_d * sh.tiles_h * sh.tiles_w;
+    if ((int64_t)jobs + t > INT32_MAX) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: too many jobs");
+    jobs += (int)t;
+  }
+  a.total_tiles = jobs;
+  if (jobs == 0) return ST_OK;
+  // one workgroup per CU: the LDS footprint allows no more
+  int grid = std::min(jobs, device_cus());
+  if (grid >= 8) grid &= ~7;
+  // running max per 4 / 2 / 1 channels, whichever divides the group size
+  const int gs = a.ymax ? C::COUT / a.groups : 0;
+  const int g = a.ymax == nullptr ? 0 : gs % 4 == 0 ? 4 : gs % 2 == 0 ? 2 : 1;
+  const dim3 gd(grid), bd(C::NT);
+  if (a.bias) {
+    if (g == 4) hipLaunchKernelGGL((conv_rows<C, true, 4>), gd, bd, 0, stream, a);
+    else if (g == 2) hipLaunchKernelGGL((conv_rows<C, true, 2>), gd, bd, 0, stream, a);
+    else if (g == 1) hipLaunchKernelGGL((conv_rows<C, true, 1>), gd, bd, 0, stream, a);
+    else hipLaunchKernelGGL((conv_rows<C, true, 0>), gd, bd, 0, stream, a);
+  } else {
+    if (g == 4) hipLaunchKernelGGL((conv_rows<C, false, 4>), gd, bd, 0, stream, a);
+    else if (g == 2) hipLaunchKernelGGL((conv_rows<C, false, 2>), gd, bd, 0, stream, a);
+    else if (g == 1) hipLaunchKernelGGL((conv_rows<C, false, 1>), gd, bd, 0, stream, a);
+    else hipLaunchKernelGGL((conv_rows<C, false, 0>), gd, bd, 0, stream, a);
+  }
+  return launch_check("st_conv_sharded: conv_rows launch");
+}
+
+template <class C>
+constexpr Instance inst_rows() {
+  return Instance{C::NDIM, C::CIN, C::COUT, C::KS, C::CK, C::KVP, C::NT,
+                  1, C::BH, C::BW, 1, C::LDS_W + C::LDS_X, &run_rows<C>};
+}
+
+
 template <class C>
 constexpr Instance inst_ring() {
   return Instance{C::NDIM, C::CIN, C::COUT, C::KS, C::CK, C::KVP, C::NT,
@@ -839,32 +1308,21 @@ constexpr Instance inst() {
                   C::TD, C::TH, C::TW, C::NCB, C::LDS_W + C::LDS_X, &run_mfma<C>};
 }
 
-// 2D 64->64 k3: one 8x64 output box per workgroup, weights resident in LDS
-using CfgImg64 = Cfg<2, 64, 64, 3, 1, 8, 64, 64, 64, 1>;
-// 3D 32->32 k3: 2x8x32 box, weights resident
-using CfgVol32 = Cfg<3, 32, 32, 3, 2, 8, 32, 32, 32, 1>;
-// 3D 16->16 k5: 4x4x32 box, weights resident, two taps per K-step
-using CfgVol16k5 = Cfg<3, 16, 16, 5, 4, 4, 32, 16, 16, 1>;
-// 2D 256->256 k3: 2x128 box, 128 output channels per block, 32-channel chunks
+// 2D 256->256 k3: 2x128 output box, 128 output channels per block, 32-channel K chunks
 using CfgImg256 = Cfg<2, 256, 256, 3, 1, 2, 128, 128, 32, 2>;
-
-// streaming instances (weights resident, ring of input slices)
-// 2D 64->64 k3: 64-column strips, 4 rows per step, 32 rows per job
-using RingImg64 = RingCfg<2, 64, 64, 3, 1, 64, 4, 32>;
-// 3D 32->32 k3: 8x32 strips, 1 plane per step, 16 planes per job
-using RingVol32 = RingCfg<3, 32, 32, 3, 8, 32, 1, 16>;
-// 3D 16->16 k5: 8x32 strips, 1 plane per step, 16 planes per job
+// 3D 16->16 k5 (16x16x32 instruction): 8x32 strips, 1 plane per step, 16 planes per job
 using RingVol16k5 = RingCfg<3, 16, 16, 5, 8, 32, 1, 16>;
+// 2D 64->64 k3: 64-column strips, 8 rows per step (4 per wave), 32 rows per job, 4 waves
+using RowsImg64 = RowsCfg<2, 64, 64, 3, 1, 64, 8, 32, 4>;
+// 3D 32->32 k3: 4x32 strips, 4 planes per step (all per wave), 16 planes per job, 4 waves
+using RowsVol32 = RowsCfg<3, 32, 32, 3, 4, 32, 4, 16, 4>;
 
-// first match wins
+// one matrix-core instance per supported (ndim, cin, cout, k)
 const Instance kInstances[] = {
-    inst_ring<RingImg64>(),
-    inst_ring<RingVol32>(),
+    inst_rows<RowsImg64>(),
+    inst_rows<RowsVol32>(),
     inst_ring<RingVol16k5>(),
     inst<CfgImg256>(),
-    inst<CfgImg64>(),
-    inst<CfgVol32>(),
-    inst<CfgVol16k5>(),
 };
 
 const Instance* find_instance(int ndim, int cin, int cout, int ks) {
@@ -979,6 +1437,7 @@ st_status st_conv_sharded(const st_plan* in_plan, const void* const* in_bufs,
     ConvArgs a{};
     a.nshards = (int)in_plan->shards.size();
     a.groups = groups;
+    a.batch = (int)in_plan->batch;
     for (int ax = 0; ax < kAxes; ++ax) {
       const bool real = ax >= kAxes - ndim;
       a.origin[ax] = real ? in_plan->halo[ax] - ksize / 2 : 0;

@@ -93,6 +93,25 @@ def test_unfused_max_gives_same_bits(name):
     assert bits_equal(a.z_host(), b.z_host())
 
 
+@pytest.mark.parametrize("name,groups", [("img64_small", 64), ("img64_small", 16), ("img64_b2", 1),
+                                         ("vol32_grid", 32), ("vol32_grid", 16), ("vol32_grid", 4),
+                                         ("vol16k5", 16), ("grid256_small", 128)])
+def test_fused_max_every_group_size(name, groups):
+    """The conv epilogue keeps its running max|y| per 1, 2 or 4 channels,
+    whichever divides the group size; every granularity must give the same
+    per-group maxima (and so the same GroupNorm bits) as the separate pass."""
+    wl = dataclasses.replace(CASES[name], groups=groups)
+    say(f"fused max: {name} groups={groups}")
+    x, w = synth.make_input(wl), synth.make_weight(wl)
+    a = run(wl, x, w)
+    b = run(wl, x, w, fuse_max=False)
+    y = a.y_host()
+    want = np.abs(y.reshape(wl.batch, -1, groups, wl.cout // groups)).max(axis=(1, 3))
+    assert np.array_equal(a.ymax.cpu().numpy().view(np.float32).reshape(wl.batch, groups), want)
+    assert np.array_equal(a.gn_state()["scales"], b.gn_state()["scales"])
+    assert bits_equal(a.z_host(), b.z_host())
+
+
 @pytest.mark.parametrize("name", ["img64_small", "vol32_full"])
 def test_alias_z_onto_y(name):
     wl = CASES[name]
