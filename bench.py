@@ -35,7 +35,111 @@ def parse():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the oracle's CPU sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (for scaling the HBM byte counters)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter files into a traffic record")
+    ap.add_argument("--record-out", default=None, help="where --record-traffic writes its JSON")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30                 # bytes read (and written) by --calibrate-copy
+STAGE_KERNELS = {                    # kernel-name fragments of each library stage
+    "halo_pack": ("halo_copy",), "halo_unpack": ("halo_copy",),
+    "conv": ("conv_rows", "conv_ring", "conv_mfma", "conv_direct"),
+    "gn_partials": ("gn_max", "gn_stats"), "gn_apply": ("gn_apply",),
+}
+
+
+def source_digest() -> str:
+    """Digest of the library sources: a traffic record is valid only for the
+    kernels it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "halo_sharded_conv_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".cpp", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def _counter_means(path, fragments, pick_max=False):
+    """Mean counter value per dispatch of the kernels whose names contain a
+    fragment (or the largest single dispatch value with pick_max)."""
+    import csv
+    vals = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if fragments and not any(f in r["Kernel_Name"] for f in fragments):
+                continue
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no matching dispatches in {path}")
+    per = {}
+    for (_, name), v in vals.items():
+        per.setdefault(name, []).append(v)
+    if pick_max:
+        return {name: (max(v), len(v)) for name, v in per.items()}
+    return {name: (sum(v) / len(v), len(v)) for name, v in per.items()}
+
+
+def record_traffic(args):
+    """HBM bytes per conv launch from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a plain copy of
+    COPY_BYTES."""
+    import synth
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.record_traffic
+    wl = synth.workload(args.workload or synth.BENCH_WORKLOAD)
+    stage = "conv"
+    f = _counter_means(fetch_csv, STAGE_KERNELS[stage])["FETCH_SIZE"]
+    w = _counter_means(write_csv, STAGE_KERNELS[stage])["WRITE_SIZE"]
+    # the copy is the elementwise dispatch that reads; the fill before it only writes
+    cf = _counter_means(cfetch_csv, ("elementwise",), pick_max=True)["FETCH_SIZE"]
+    cw = _counter_means(cwrite_csv, ("elementwise",), pick_max=True)["WRITE_SIZE"]
+    f_scale = COPY_BYTES / (cf[0] * 1024.0)
+    w_scale = COPY_BYTES / (cw[0] * 1024.0)
+    rec = {
+        "workload": wl.name, "stage": stage, "source_digest": source_digest(),
+        "fetch_kib_per_dispatch": f[0], "write_kib_per_dispatch": w[0], "dispatches": [f[1], w[1]],
+        "copy_bytes": COPY_BYTES, "copy_fetch_kib": cf[0], "copy_write_kib": cw[0],
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "traffic_bytes": f[0] * 1024.0 * f_scale + w[0] * 1024.0 * w_scale,
+    }
+    out = args.record_out or os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
+def calibrate_copy():
+    """A plain 1 GiB device copy b = a * 1 through an elementwise kernel
+    (16 bytes per lane, whole 128-byte lines: the access shape of the
+    library's kernels).  torch's copy_ is avoided: it runs a runtime blit
+    kernel whose read counter scales differently."""
+    import torch
+    n = COPY_BYTES // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}))
+
+
+def load_traffic(wl, stage):
+    """Measured HBM bytes per launch of `stage`, or None when no record exists
+    or the kernels changed since it was taken."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        rec = json.load(fh)
+    if rec.get("stage") != stage or rec.get("source_digest") != source_digest():
+        return None
+    return rec["traffic_bytes"]
 
 
 def algorithmic(wl, layer):
@@ -80,6 +184,12 @@ def cpu_baseline(wl, rows):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(args)
+        return
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -153,7 +263,7 @@ def main():
         roof = {"bound": "hbm", "achieved": kernels[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["kernel"] = dom
-    roof["traffic"] = None
+    roof["traffic"] = load_traffic(wl, dom)
 
     out = {
         "metric": METRIC,
