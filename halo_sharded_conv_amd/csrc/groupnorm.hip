@@ -33,7 +33,7 @@ namespace st {
 namespace {
 
 constexpr int kNT = 256;        // threads per block
-constexpr int kIter = 16;       // vectors per thread per item
+constexpr int kIter = 16;       // vectors per thread per item (even: the apply pass takes halves)
 
 struct GnShard {
   const float* y;
@@ -289,9 +289,14 @@ __global__ __launch_bounds__(kNT) void gn_apply(const GnArgs a) {
   const int C = a.channels;
   int cur = -1;
   float4 p[VW];
-  for (int item = blockIdx.x; item < a.total_items; item += gridDim.x) {
+  // half items (kIter / 2 vectors per thread: more waves in flight), visited
+  // last item first so the pass begins on the part of y the statistics pass
+  // read last
+  constexpr int kHalf = kIter / 2;
+  for (int h = blockIdx.x; h < 2 * a.total_items; h += gridDim.x) {
+    const int hr = 2 * a.total_items - 1 - h;
     int s, n, k;
-    decode_item(a, item, s, n, k);
+    decode_item(a, hr >> 1, s, n, k);
     const int key = s * a.batch + n;
     if (FIXED && key != cur) {
       const int c0 = (tid * VW) % C;
@@ -302,15 +307,15 @@ __global__ __launch_bounds__(kNT) void gn_apply(const GnArgs a) {
     const GnShard& sh = a.sh[s];
     const typename V::T* y = reinterpret_cast<const typename V::T*>(sh.y) + n * sh.vecs_per_n;
     typename V::T* z = reinterpret_cast<typename V::T*>(sh.z) + n * sh.vecs_per_n;
-    const int64_t v0 = (int64_t)k * kNT * kIter + tid;
-    typename V::T val[kIter];
+    const int64_t v0 = (int64_t)k * kNT * kIter + (hr & 1) * kNT * kHalf + tid;
+    typename V::T val[kHalf];
 #pragma unroll
-    for (int i = 0; i < kIter; ++i) {
+    for (int i = 0; i < kHalf; ++i) {
       const int64_t v = v0 + i * kNT;
       val[i] = v < sh.vecs_per_n ? y[v] : typename V::T{};
     }
 #pragma unroll
-    for (int i = 0; i < kIter; ++i) {
+    for (int i = 0; i < kHalf; ++i) {
       const int64_t v = v0 + i * kNT;
       if (v >= sh.vecs_per_n) break;
       float out[VW];
@@ -422,7 +427,7 @@ st_status prepare(const st_plan* y_plan, const float* const* y_bufs, float* cons
     g.items_per_n = (int32_t)((g.vecs_per_n + item_vecs - 1) / item_vecs);
     g.item_begin = (int32_t)items;
     items += (int64_t)g.items_per_n * a.batch;
-    if (items > INT32_MAX) return err(ST_ERR_UNSUPPORTED, "volume too large");
+    if (items > INT32_MAX / 2) return err(ST_ERR_UNSUPPORTED, "volume too large");
   }
   a.total_items = (int)items;
   return ST_OK;
@@ -444,7 +449,8 @@ st_status launch_partials(GnArgs& a, bool need_max, hipStream_t st) {
 
 template <int VW, bool FIXED>
 st_status launch_apply(GnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((gn_apply<VW, FIXED>), dim3(grid_of(a)), dim3(kNT), 0, st, a);
+  const int grid = std::max(1, std::min(2 * a.total_items, device_cus() * 16));
+  hipLaunchKernelGGL((gn_apply<VW, FIXED>), dim3(grid), dim3(kNT), 0, st, a);
   return launch_check("st_groupnorm_apply: launch");
 }
 
