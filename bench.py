@@ -51,17 +51,23 @@ STAGE_KERNELS = {                    # kernel-name fragments of each library sta
 }
 
 
-def source_digest() -> str:
-    """Digest of the library sources: a traffic record is valid only for the
-    kernels it was measured on."""
+STAGE_SOURCES = {                    # library sources that define each stage's kernels and launches
+    "halo_pack": ("halo.hip", "plan.cpp", "internal.h"), "halo_unpack": ("halo.hip", "plan.cpp", "internal.h"),
+    "conv": ("conv.hip", "internal.h"),
+    "gn_partials": ("groupnorm.hip", "internal.h"), "gn_apply": ("groupnorm.hip", "internal.h"),
+}
+
+
+def source_digest(stage: str) -> str:
+    """Digest of the sources of one stage: a traffic record is valid only for
+    the kernels it was measured on."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "halo_sharded_conv_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".cpp", ".h")):
-            h.update(f.encode())
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(fh.read())
+    for f in STAGE_SOURCES[stage]:
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
@@ -102,7 +108,7 @@ def record_traffic(args):
     f_scale = COPY_BYTES / (cf[0] * 1024.0)
     w_scale = COPY_BYTES / (cw[0] * 1024.0)
     rec = {
-        "workload": wl.name, "stage": stage, "source_digest": source_digest(),
+        "workload": wl.name, "stage": stage, "source_digest": source_digest(stage),
         "fetch_kib_per_dispatch": f[0], "write_kib_per_dispatch": w[0], "dispatches": [f[1], w[1]],
         "copy_bytes": COPY_BYTES, "copy_fetch_kib": cf[0], "copy_write_kib": cw[0],
         "fetch_scale": f_scale, "write_scale": w_scale,
@@ -137,7 +143,7 @@ def load_traffic(wl, stage):
         return None
     with open(p) as fh:
         rec = json.load(fh)
-    if rec.get("stage") != stage or rec.get("source_digest") != source_digest():
+    if rec.get("stage") != stage or stage not in STAGE_SOURCES or rec.get("source_digest") != source_digest(stage):
         return None
     return rec["traffic_bytes"]
 
