@@ -875,9 +875,10 @@ st_status run_ring(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
 // next job's first TS + k - 1 slices travel the same way during a job's last
 // step, so a block never waits on HBM latency between jobs.
 
-template <int NDIM_, int CIN_, int COUT_, int KS_, int BH_, int BW_, int TS_, int RC_, int RW_>
+template <int NDIM_, int CIN_, int COUT_, int KS_, int BH_, int BW_, int TS_, int RC_, int RW_, int NH_>
 struct RowsCfg {
   static constexpr int NDIM = NDIM_, CIN = CIN_, COUT = COUT_, KS = KS_;
+  static constexpr int NH = NH_;                      // passes over K per step (output-channel groups)
   static constexpr int BH = NDIM == 3 ? BH_ : 1;
   static constexpr int BW = BW_, TS = TS_, RC = RC_, RW = RW_;
   static constexpr int KH = NDIM == 3 ? KS : 1;
@@ -901,7 +902,7 @@ struct RowsCfg {
   static constexpr int PFS = (STEP_CHUNKS + NT - 1) / NT;
   static constexpr int NCHUNK = 1, NCB = 1, TD = 1, TH = 1, TW = BW, BN = COUT;
   static_assert(CIN % 16 == 0 && NCH <= 16 && COUT % 32 == 0, "shape");
-  static_assert(BW % 32 == 0 && TS % RW == 0 && RC % TS == 0, "tiling");
+  static_assert(BW % 32 == 0 && TS % RW == 0 && RC % TS == 0 && MB % NH == 0, "tiling");
   static_assert(NT <= 1024, "block size");
   static_assert(LDS_W + LDS_X + COUT * 8 <= 160 * 1024, "LDS budget");
 };
@@ -1113,11 +1114,11 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NT / 2
       pf[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(N.rin, off, 0, 0));
     };
 
-    // 2. matrix-core work; the operands of K chunk i+1 are read during chunk i
-#pragma unroll
-    for (int t = 0; t < C::RW; ++t)
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) acc[t][mb] = f32x16{};
+    // 2. matrix-core work in NH passes over K, one per group of MH 32-channel
+    // output blocks.  A pass's results are stored during the next pass, so
+    // the stores run under the matrix instructions and an accumulator is
+    // rewritten only half a step after its stores were issued.  The operands
+    // of K chunk i+1 are read during chunk i.
     int sbase[C::NIN];                                // ring slice byte base of input slice t0 + r
 #pragma unroll
     for (int r = 0; r < C::NIN; ++r) {
@@ -1127,7 +1128,10 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NT / 2
       sbase[r] = sl * (C::SLICE * C::CB);
     }
     constexpr int NK = C::KH * C::KS * C::KCS;        // in-slice taps x K chunks
-    auto load_ops = [&](int i, bf16x8 (&a)[C::KS][C::MB], bf16x8 (&b)[C::NIN]) __attribute__((always_inline)) {
+    constexpr int NH = C::NH, MH = C::MB / C::NH;
+    constexpr int NKT = NH * NK;
+    auto load_ops = [&](int ii, bf16x8 (&a)[C::KS][MH], bf16x8 (&b)[C::NIN]) __attribute__((always_inline)) {
+      const int hh = ii / NK, i = ii % NK;
       const int cs = i % C::KCS;
       const int tw = (i / C::KCS) % C::KS;
       const int th = i / (C::KCS * C::KS);
@@ -1139,74 +1143,91 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NT / 2
         const int tap = (tr * C::KH + th) * C::KS + tw;
         const int jw = tap * C::NCH + 2 * cs;
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-          a[tr][mb] = *reinterpret_cast<const bf16x8*>(swb + ((ybase[mb] ^ (16 * (jw & 7))) + 128 * (jw >> 3)));
+        for (int mm = 0; mm < MH; ++mm)
+          a[tr][mm] = *reinterpret_cast<const bf16x8*>(swb + ((ybase[hh * MH + mm] ^ (16 * (jw & 7))) + 128 * (jw >> 3)));
       }
     };
-    bf16x8 av[2][C::KS][C::MB], bv[2][C::NIN];
+
+    // epilogue pieces: output row t, channel block mb, channel quad jj
+    const int oh = C::NDIM == 3 ? J.h0 + ph : 0;
+    const int ow = J.w0 + pw;
+    const bool in_plane = (C::NDIM == 2 || oh < J.e1) && ow < J.e2;
+    auto store_piece = [&](int t, int mb, int jj) __attribute__((always_inline)) {
+      const int osl = cur + t0 + t;
+      const bool ok = in_plane && osl < J.s_end;
+      const int64_t cell = (int64_t)(osl - J.s_begin) * J.out_cells + (C::NDIM == 3 ? (int64_t)oh * J.e2 : 0) + ow;
+      const uint32_t cbase = ok ? (uint32_t)((cell * C::COUT + co_lane) * 4) : kOob;
+      const int co = mb * 32 + 8 * jj;                // relative to co_lane
+      f32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = acc[t][mb][4 * jj + i];
+      if (BIAS) {
+        const float4 bv4 = *reinterpret_cast<const float4*>(&sbias[co_lane + co]);
+        v[0] += bv4.x; v[1] += bv4.y; v[2] += bv4.z; v[3] += bv4.w;
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(v, J.rout, cbase + (uint32_t)(co * 4), 0, 0);
+      if (MAXV) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          runmax[mb][(4 * jj + i) / MG] = fmaxf(runmax[mb][(4 * jj + i) / MG], ok ? fabsf(v[i]) : 0.f);
+      }
+    };
+    constexpr int NST = C::RW * MH * 4;               // stores of one pass
+    auto store_pass = [&](int hh, int q0, int q1) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = q0; q < q1; ++q) store_piece(q / (MH * 4), hh * MH + (q / 4) % MH, q % 4);
+    };
+
+    bf16x8 av[2][C::KS][MH], bv[2][C::NIN];
     load_ops(0, av[0], bv[0]);
-    constexpr int NRD = C::NIN + C::KS * C::MB;       // LDS reads per K chunk
-    constexpr int NMF = C::RW * C::KS * C::MB;        // matrix instructions per K chunk
+    constexpr int NRD = C::NIN + C::KS * MH;          // LDS reads per K chunk
+    constexpr int NMF = C::RW * C::KS * MH;           // matrix instructions per K chunk
     constexpr int PF_CHUNKS = NK / 2 > 0 ? NK / 2 : 1;   // K chunks that carry the prefetch loads
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int cb = i & 1;
+    for (int ii = 0; ii < NKT; ++ii) {
+      const int hh = ii / NK, i = ii % NK;
+      const int cb = ii & 1;
       __builtin_amdgcn_sched_barrier(0);
-      if (i < PF_CHUNKS) {
+      if (i == 0) {
+#pragma unroll
+        for (int t = 0; t < C::RW; ++t)
+#pragma unroll
+          for (int mm = 0; mm < MH; ++mm) acc[t][hh * MH + mm] = f32x16{};
+      }
+      if (hh == 0 && i < PF_CHUNKS) {
 #pragma unroll
         for (int k = i * C::PF / PF_CHUNKS; k < (i + 1) * C::PF / PF_CHUNKS; ++k) issue_pf(k);
       }
-      if (i + 1 < NK) load_ops(i + 1, av[cb ^ 1], bv[cb ^ 1]);
+      if (hh > 0) store_pass(hh - 1, i * NST / NK, (i + 1) * NST / NK);
+      if (ii + 1 < NKT) load_ops(ii + 1, av[cb ^ 1], bv[cb ^ 1]);
 #pragma unroll
       for (int tr = 0; tr < C::KS; ++tr)
 #pragma unroll
         for (int t = 0; t < C::RW; ++t)
 #pragma unroll
-          for (int mb = 0; mb < C::MB; ++mb)
-            acc[t][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cb][tr][mb], bv[cb][t + tr], acc[t][mb], 0, 0, 0);
-      // interleave: the next chunk's reads spread over this chunk's MFMAs
-      if (i + 1 < NK) {
+          for (int mm = 0; mm < MH; ++mm)
+            acc[t][hh * MH + mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cb][tr][mm], bv[cb][t + tr],
+                                                                           acc[t][hh * MH + mm], 0, 0, 0);
+      // interleave: the next chunk's reads (and the previous pass's stores)
+      // spread over this chunk's MFMAs
+      if (ii + 1 < NKT) {
+        const int nst = hh > 0 ? (i + 1) * NST / NK - i * NST / NK : 0;
 #pragma unroll
         for (int g = 0; g < NRD; ++g) {
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // one LDS read
-          __builtin_amdgcn_sched_group_barrier(0x008, NMF / NRD > 0 ? NMF / NRD : 1, 0);
+          const int nm = (g + 1) * NMF / NRD - g * NMF / NRD;
+          if (nm == 1) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMAs
+          else if (nm == 2) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          else if (nm == 3) __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+          else if (nm >= 4) __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          if (g < nst) __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);    // one store
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // 3. epilogue: bias, range-checked fp32 stores, running max
-    {
-      const int oh = C::NDIM == 3 ? J.h0 + ph : 0;
-      const int ow = J.w0 + pw;
-      const bool in_plane = (C::NDIM == 2 || oh < J.e1) && ow < J.e2;
-#pragma unroll
-      for (int t = 0; t < C::RW; ++t) {
-        const int osl = cur + t0 + t;
-        const bool ok = in_plane && osl < J.s_end;
-        const int64_t cell = (int64_t)(osl - J.s_begin) * J.out_cells + (C::NDIM == 3 ? (int64_t)oh * J.e2 : 0) + ow;
-        const uint32_t cbase = ok ? (uint32_t)((cell * C::COUT + co_lane) * 4) : kOob;
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int co = mb * 32 + 8 * jj;
-            f32x4 v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = acc[t][mb][4 * jj + i];
-            if (BIAS) {
-              const float4 bv4 = *reinterpret_cast<const float4*>(&sbias[co_lane + co]);
-              v[0] += bv4.x; v[1] += bv4.y; v[2] += bv4.z; v[3] += bv4.w;
-            }
-            __builtin_amdgcn_raw_buffer_store_b128(v, J.rout, cbase + (uint32_t)(co * 4), 0, 0);
-            if (MAXV) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                runmax[mb][(4 * jj + i) / MG] = fmaxf(runmax[mb][(4 * jj + i) / MG], ok ? fabsf(v[i]) : 0.f);
-            }
-          }
-      }
-    }
+    // 3. the last pass's results: bias, range-checked fp32 stores, running max
+    store_pass(NH - 1, 0, NST);
 
     // 4. every wave is done with the ring: the fetched slices replace the TS
     // oldest ones (or the whole ring for the next job)
@@ -1312,10 +1333,11 @@ constexpr Instance inst() {
 using CfgImg256 = Cfg<2, 256, 256, 3, 1, 2, 128, 128, 32, 2>;
 // 3D 16->16 k5 (16x16x32 instruction): 8x32 strips, 1 plane per step, 16 planes per job
 using RingVol16k5 = RingCfg<3, 16, 16, 5, 8, 32, 1, 16>;
-// 2D 64->64 k3: 64-column strips, 8 rows per step (4 per wave), 32 rows per job, 4 waves
-using RowsImg64 = RowsCfg<2, 64, 64, 3, 1, 64, 8, 32, 4>;
+// 2D 64->64 k3: 64-column strips, 8 rows per step (4 per wave), 32 rows per job, 4 waves,
+// two passes over K per step (32 output channels each)
+using RowsImg64 = RowsCfg<2, 64, 64, 3, 1, 64, 8, 32, 4, 2>;
 // 3D 32->32 k3: 4x32 strips, 4 planes per step (all per wave), 16 planes per job, 4 waves
-using RowsVol32 = RowsCfg<3, 32, 32, 3, 4, 32, 4, 16, 4>;
+using RowsVol32 = RowsCfg<3, 32, 32, 3, 4, 32, 4, 16, 4, 1>;
 
 // one matrix-core instance per supported (ndim, cin, cout, k)
 const Instance kInstances[] = {
