@@ -8,18 +8,21 @@
 // cross-correlation, stride 1, dilation 1, zero 'same' padding, bias.
 //
 // bf16 path: implicit GEMM on the gfx950 matrix cores,
-//   M = output channels (A = packed weights, from LDS)
-//   N = output positions (B = input cells, from an LDS-staged halo box)
+//   M = output channels (A = packed weights)
+//   N = output positions (B = input cells staged in LDS)
 //   K = kernel taps x input channels,
-// with v_mfma_f32_16x16x32_bf16 and fp32 accumulation.  A workgroup owns a
-// box of TD x TH x TW output positions (64 per wave, 16 per MFMA column
-// block, each 16-run along W) and BN output channels; its input box
-// (TD+k-1) x (TH+k-1) x (TW+k-1) x CK is staged once per channel chunk and
-// every tap reads a shifted window of it.  Each output accumulates its
-// K-steps in one fixed order (taps lexicographic, channels ascending), so its
-// bits do not depend on which tile, shard or plan it belongs to.
-// Workgroups are persistent; tiles are dealt out so that the 32 workgroups of
-// one XCD work on neighbouring tiles and share halo rows in that XCD's L2.
+// with fp32 accumulation.  Three kernel families, one instance per supported
+// layer shape (the instance table at the end):
+//   conv_rows  streams a strip of the shard along its outermost axis with the
+//              weights resident in LDS; 32x32x16 MFMA (64->64 and 32->32 k3)
+//   conv_ring  the same streaming structure on 16x16x32 MFMA for 16-channel
+//              layers (3D 16->16 k5)
+//   conv_gemm  tiles with the weights streamed through LDS per 16-channel K
+//              chunk, for layers whose weights do not fit in LDS (2D 256->256)
+// Each output accumulates its K-steps in one fixed order (taps
+// lexicographic, channels ascending), so its bits do not depend on which
+// tile, job, shard or plan it belongs to.  Workgroups are persistent and deal
+// out their work per XCD, so neighbouring tiles share halo rows in one L2.
 //
 // fp32 path (and bf16 shapes without a matrix-core instance): a direct
 // kernel, one thread per output position, fp32 FMA in the same fixed order.
@@ -27,6 +30,7 @@
 // Epilogue: optional bias, fp32 store, and max |y| per (n, group) via
 // integer atomicMax on the float bits (order-free).
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -60,269 +64,6 @@ struct ConvArgs {
 __global__ void fill_u32(uint32_t* __restrict__ p, uint32_t v, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
-}
-
-// --------------------------------------------------------------------------
-// matrix-core implicit GEMM
-// --------------------------------------------------------------------------
-
-template <int NDIM_, int CIN_, int COUT_, int KS_, int TD_, int TH_, int TW_, int BN_, int CK_, int WN_>
-struct Cfg {
-  static constexpr int NDIM = NDIM_, CIN = CIN_, COUT = COUT_, KS = KS_;
-  static constexpr int TD = TD_, TH = TH_, TW = TW_, BN = BN_, CK = CK_, WN = WN_;
-  static constexpr int KD = NDIM == 3 ? KS : 1;
-  static constexpr int TAPS = KD * KS * KS;
-  static constexpr int BOX_D = TD + KD - 1, BOX_H = TH + KS - 1, BOX_W = TW + KS - 1;
-  static constexpr int BOX = BOX_D * BOX_H * BOX_W;
-  static constexpr int POS = TD * TH * TW;
-  static constexpr int WP = POS / 64;
-  static constexpr int NWAVES = WP * WN;
-  static constexpr int NT = NWAVES * 64;
-  static constexpr int NW = BN / WN;
-  static constexpr int MB = NW / 16;
-  static constexpr int NB = 4;
-  static constexpr int KV = TAPS * CK;
-  static constexpr int KSTEPS = (KV + 31) / 32;
-  // K-steps unrolled per iteration of the K loop: all of them when few,
-  // otherwise the largest divisor <= 9 (bounds register pressure)
-  static constexpr int KU = KSTEPS <= 18 ? KSTEPS
-                            : KSTEPS % 9 == 0 ? 9 : KSTEPS % 7 == 0 ? 7 : KSTEPS % 5 == 0 ? 5
-                            : KSTEPS % 3 == 0 ? 3 : KSTEPS % 2 == 0 ? 2 : 1;
-  static constexpr int KVP = ((KV + 63) / 64) % 2 == 1 ? (KV + 63) / 64 * 64 : (KV + 63) / 64 * 64 + 64;
-  static constexpr int NCH = CK / 8;
-  static constexpr int KEYDIV = NCH >= 16 ? 1 : 16 / NCH;
-  static constexpr int NCHUNK = CIN / CK;
-  static constexpr int NCB = COUT / BN;
-  static constexpr bool RESIDENT = NCHUNK == 1 && NCB == 1;
-  static constexpr int LDS_W = BN * KVP * 2;
-  static constexpr int LDS_X = BOX * CK * 2;
-  static_assert(NDIM == 3 || TD == 1, "2D tiles have depth 1");
-  static_assert(POS % 64 == 0 && TW % 16 == 0, "a wave covers 64 positions in 16-runs along W");
-  static_assert(BN % WN == 0 && NW % 16 == 0 && COUT % BN == 0, "cout blocking");
-  static_assert(CK % 8 == 0 && CIN % CK == 0 && (CK >= 32 ? CK % 32 == 0 : 32 % CK == 0), "channel chunks");
-  static_assert(LDS_W + LDS_X + BN * 4 <= 160 * 1024, "LDS budget");
-  static_assert(NT <= 1024, "block size");
-};
-
-// swizzled LDS element index of 16-byte chunk j of input-box cell q
-template <class C>
-__device__ __forceinline__ int xoff(int q, int j) {
-  return q * C::CK + 8 * (j ^ ((q / C::KEYDIV) % C::NCH));
-}
-
-template <class C>
-__device__ __forceinline__ void stage_w(uint16_t* sw, const uint16_t* __restrict__ w, int cc, int cb) {
-  constexpr int CPR = C::KVP / 8;
-  const uint16_t* src = w + ((size_t)cc * C::COUT + (size_t)cb * C::BN) * C::KVP;
-  for (int i = threadIdx.x; i < C::BN * CPR; i += C::NT) {
-    const int m = i / CPR, j = i - m * CPR;
-    const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)m * C::KVP + 8 * j);
-    *reinterpret_cast<uint4*>(sw + m * C::KVP + 8 * (j ^ ((m >> 1) & 7))) = v;
-  }
-}
-
-template <class C>
-__device__ __forceinline__ void stage_x(uint16_t* sx, const ConvShardArg& sh, const int* origin,
-                                        int n, int d0, int h0, int w0, int cc) {
-  const int pd = sh.pad[0], ph = sh.pad[1], pw = sh.pad[2];
-  for (int i = threadIdx.x; i < C::BOX * C::NCH; i += C::NT) {
-    const int q = i / C::NCH, j = i - q * C::NCH;
-    const int qw = q % C::BOX_W;
-    const int qh = (q / C::BOX_W) % C::BOX_H;
-    const int qd = q / (C::BOX_W * C::BOX_H);
-    const int gd = d0 + qd + origin[0], gh = h0 + qh + origin[1], gw = w0 + qw + origin[2];
-    uint4 v = {0u, 0u, 0u, 0u};
-    if (gd < pd && gh < ph && gw < pw) {
-      const size_t cell = (((size_t)n * pd + gd) * ph + gh) * pw + gw;
-      v = *reinterpret_cast<const uint4*>(sh.in + cell * C::CIN + cc * C::CK + 8 * j);
-    }
-    *reinterpret_cast<uint4*>(sx + xoff<C>(q, j)) = v;
-  }
-}
-
-template <class C>
-__global__ __launch_bounds__(C::NT) void conv_mfma(const ConvArgs args) {
-  __shared__ __attribute__((aligned(16))) uint16_t sw[C::LDS_W / 2];
-  __shared__ __attribute__((aligned(16))) uint16_t sx[C::LDS_X / 2];
-  __shared__ uint32_t smax[C::BN];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wp = wave % C::WP;
-  const int wn = wave / C::WP;
-  const int l16 = lane & 15;
-  const int g4 = lane >> 4;
-  const bool want_max = args.ymax != nullptr;
-
-  for (int i = tid; i < C::BN; i += C::NT) smax[i] = 0u;
-
-  // per-lane geometry of the B operand: cell of each 16-run in the box
-  int qbase[C::NB];
-  int pdd[C::NB], phh[C::NB], pww[C::NB];
-#pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) {
-    const int p = wp * 64 + nb * 16 + l16;
-    pww[nb] = p % C::TW;
-    phh[nb] = (p / C::TW) % C::TH;
-    pdd[nb] = p / (C::TW * C::TH);
-    qbase[nb] = (pdd[nb] * C::BOX_H + phh[nb]) * C::BOX_W + pww[nb];
-  }
-
-  // persistent tile loop, XCD-aware: XCD x (= block % 8) takes a contiguous
-  // eighth of the tiles and its workgroups walk it side by side.
-  const int total = args.total_tiles;
-  int t0 = blockIdx.x, tstride = gridDim.x, t_end = total;
-  if (gridDim.x >= 8 && (gridDim.x & 7) == 0) {
-    const int xcd = blockIdx.x & 7;
-    t0 = (int)((int64_t)total * xcd / 8) + (blockIdx.x >> 3);
-    tstride = gridDim.x >> 3;
-    t_end = (int)((int64_t)total * (xcd + 1) / 8);
-  }
-
-  if (C::RESIDENT) stage_w<C>(sw, args.w, 0, 0);
-
-  float runmax[C::MB][4];
-#pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) runmax[mb][i] = 0.f;
-  int cur_key = -1, cur_n = 0, cur_cb = 0;
-
-  auto flush = [&](int n, int cb) {
-    // max over the 16 lanes that share output channels
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = runmax[mb][i];
-        v = fmaxf(v, __shfl_xor(v, 1));
-        v = fmaxf(v, __shfl_xor(v, 2));
-        v = fmaxf(v, __shfl_xor(v, 4));
-        v = fmaxf(v, __shfl_xor(v, 8));
-        runmax[mb][i] = v;
-      }
-    __syncthreads();
-    if (l16 == 0) {
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          atomicMax(&smax[wn * C::NW + mb * 16 + 4 * g4 + i], __float_as_uint(runmax[mb][i]));
-    }
-    __syncthreads();
-    const int gs = C::COUT / args.groups;
-    const int c_lo = cb * C::BN;
-    const int g_lo = c_lo / gs, g_hi = (c_lo + C::BN - 1) / gs;
-    for (int g = g_lo + tid; g <= g_hi; g += C::NT) {
-      uint32_t m = 0;
-      const int a = max(g * gs, c_lo), b = min((g + 1) * gs, c_lo + C::BN);
-      for (int c = a; c < b; ++c) m = max(m, smax[c - c_lo]);
-      atomicMax(&args.ymax[n * args.groups + g], m);
-    }
-    __syncthreads();
-    for (int i = tid; i < C::BN; i += C::NT) smax[i] = 0u;
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) runmax[mb][i] = 0.f;
-  };
-
-  for (int t = t0; t < t_end; t += tstride) {
-    // decode tile -> shard, n, spatial tile, cout block (innermost)
-    int s = 0;
-    while (s + 1 < args.nshards && args.sh[s + 1].tile_begin <= t) ++s;
-    const ConvShardArg& sh = args.sh[s];
-    const int tiles_sp = sh.tiles_d * sh.tiles_h * sh.tiles_w;
-    int r = t - sh.tile_begin;
-    const int cb = r % C::NCB;
-    r /= C::NCB;
-    const int n = r / tiles_sp;
-    r -= n * tiles_sp;
-    const int td = r / (sh.tiles_h * sh.tiles_w);
-    r -= td * sh.tiles_h * sh.tiles_w;
-    const int th = r / sh.tiles_w;
-    const int tw = r - th * sh.tiles_w;
-    const int d0 = td * C::TD, h0 = th * C::TH, w0 = tw * C::TW;
-
-    if (want_max) {
-      const int key = n * C::NCB + cb;
-      if (key != cur_key) {
-        if (cur_key >= 0) flush(cur_n, cur_cb);
-        cur_key = key;
-        cur_n = n;
-        cur_cb = cb;
-      }
-    }
-
-    f32x4 acc[C::MB][C::NB];
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int cc = 0; cc < C::NCHUNK; ++cc) {
-      __syncthreads();
-      if (!C::RESIDENT) stage_w<C>(sw, args.w, cc, cb);
-      stage_x<C>(sx, sh, args.origin, n, d0, h0, w0, cc);
-      __syncthreads();
-
-#pragma unroll 1
-      for (int ko = 0; ko < C::KSTEPS; ko += C::KU)
-#pragma unroll
-      for (int ki = 0; ki < C::KU; ++ki) {
-        const int ks = ko + ki;
-        const int vk = 32 * ks + 8 * g4;
-        const int tap = vk / C::CK;
-        const int c0 = vk - tap * C::CK;
-        const bool valid = tap < C::TAPS;
-        const int kw = tap % C::KS;
-        const int kh = (tap / C::KS) % C::KS;
-        const int kd = tap / (C::KS * C::KS);
-        const int qtap = (kd * C::BOX_H + kh) * C::BOX_W + kw;
-        bf16x8 a[C::MB], b[C::NB];
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) {
-          const int m = wn * C::NW + mb * 16 + l16;
-          a[mb] = *reinterpret_cast<const bf16x8*>(sw + m * C::KVP + 8 * ((4 * ks + g4) ^ ((lane & 15) >> 1)));
-        }
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-          const int q = qbase[nb] + qtap;
-          if (valid) b[nb] = *reinterpret_cast<const bf16x8*>(sx + xoff<C>(q, c0 >> 3));
-          else b[nb] = bf16x8{};
-        }
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
-      }
-    }
-
-    // epilogue: lane holds rows (channels) 4*g4..+3 of column (position) l16
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) {
-      const int od = d0 + pdd[nb], oh = h0 + phh[nb], ow = w0 + pww[nb];
-      if (od >= sh.ext[0] || oh >= sh.ext[1] || ow >= sh.ext[2]) continue;
-      const size_t cell = (((size_t)n * sh.ext[0] + od) * sh.ext[1] + oh) * sh.ext[2] + ow;
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) {
-        const int co = cb * C::BN + wn * C::NW + mb * 16 + 4 * g4;
-        f32x4 v = acc[mb][nb];
-        if (args.bias) {
-          v[0] += args.bias[co + 0];
-          v[1] += args.bias[co + 1];
-          v[2] += args.bias[co + 2];
-          v[3] += args.bias[co + 3];
-        }
-        *reinterpret_cast<f32x4*>(sh.out + cell * C::COUT + co) = v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) runmax[mb][i] = fmaxf(runmax[mb][i], fabsf(v[i]));
-      }
-    }
-  }
-  if (want_max && cur_key >= 0) flush(cur_n, cur_cb);
 }
 
 // --------------------------------------------------------------------------
@@ -463,6 +204,23 @@ __global__ void pack_w_mfma(const uint16_t* __restrict__ w, uint16_t* __restrict
     v = w[((int64_t)o * cin + c) * taps + t];
   }
   out[i] = v;
+}
+
+// [Cout][Cin][taps] -> [Cout/bn][Cin/ck][taps][bn][ck]: each (cout block, K chunk)
+// slab is contiguous and already in the order its LDS stage holds it
+__global__ void pack_w_gemm(const uint16_t* __restrict__ w, uint16_t* __restrict__ out, int cin, int cout,
+                            int taps, int ck, int bn, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int c = (int)(i % ck);
+  int64_t r = i / ck;
+  const int m = (int)(r % bn);
+  r /= bn;
+  const int t = (int)(r % taps);
+  r /= taps;
+  const int cc = (int)(r % (cin / ck));
+  const int cb = (int)(r / (cin / ck));
+  out[i] = w[((int64_t)(cb * bn + m) * cin + cc * ck + c) * taps + t];
 }
 
 // [Cout][Cin][taps] -> [Cout][taps][Cin]
@@ -790,6 +548,7 @@ struct Instance {
   int td, th, tw, ncb;
   int lds;
   st_status (*run)(ConvArgs&, const st_plan*, hipStream_t);
+  int bn = 0;                 // > 0: weights packed [Cout/bn][Cin/ck][tap][bn][ck] (streamed-weight kernels)
 };
 
 int device_cus() {
@@ -802,31 +561,6 @@ int device_cus() {
     else cus[dev] = 256;
   }
   return cus[dev];
-}
-
-template <class C>
-st_status run_mfma(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
-  int tiles = 0;
-  for (size_t s = 0; s < in_plan->shards.size(); ++s) {
-    const Shard& sd = in_plan->shards[s];
-    ConvShardArg& sh = a.sh[s];
-    sh.tiles_d = (int)((sd.ext[0] + C::TD - 1) / C::TD);
-    sh.tiles_h = (int)((sd.ext[1] + C::TH - 1) / C::TH);
-    sh.tiles_w = (int)((sd.ext[2] + C::TW - 1) / C::TW);
-    sh.tile_begin = tiles;
-    const int64_t t = (int64_t)in_plan->batch * sh.tiles_d * sh.tiles_h * sh.tiles_w * C::NCB;
-    if ((int64_t)tiles + t > INT32_MAX) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: too many tiles");
-    tiles += (int)t;
-  }
-  a.total_tiles = tiles;
-  if (tiles == 0) return ST_OK;
-  int occ = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, conv_mfma<C>, C::NT, 0) != hipSuccess || occ < 1)
-    occ = 1;
-  int grid = std::min(tiles, device_cus() * occ);
-  if (grid >= 8) grid &= ~7;
-  hipLaunchKernelGGL(conv_mfma<C>, dim3(grid), dim3(C::NT), 0, stream, a);
-  return launch_check("st_conv_sharded: conv_mfma launch");
 }
 
 template <class C>
@@ -1323,14 +1057,387 @@ constexpr Instance inst_ring() {
                   1, C::BH, C::BW, 1, C::LDS_W + C::LDS_X, &run_ring<C>};
 }
 
-template <class C>
-constexpr Instance inst() {
-  return Instance{C::NDIM, C::CIN, C::COUT, C::KS, C::CK, C::KVP, C::NT,
-                  C::TD, C::TH, C::TW, C::NCB, C::LDS_W + C::LDS_X, &run_mfma<C>};
+
+// --------------------------------------------------------------------------
+// tiled implicit GEMM with streamed weights (wide 2D layers)
+// --------------------------------------------------------------------------
+//
+// For layers whose weights do not fit in LDS (2D 256->256 k3: 1.2 MB).  A
+// workgroup owns TR rows x TW columns of output positions and BN output
+// channels; wave w owns row w (TW/32 runs of 32 positions) and all BN
+// channels (BN/32 blocks), so one K step reads BN/32 + TW/32 fragments for
+// (BN/32)*(TW/32) MFMAs.  K is streamed in 16-channel chunks: per chunk the
+// input box (TR + k - 1) x (TW + k - 1) cells x 16 channels and the chunk's
+// weights (BN x k^2 x 16) sit in one of two LDS stages.  The next chunk's
+// pieces (or the next tile's first chunk) are loaded into registers at the
+// start of a chunk and written to the other stage in its middle; one barrier
+// per chunk.  Cout blocks are the innermost tile index, so the tiles that
+// share an input box run side by side on one XCD and read it from its L2.
+
+template <int CIN_, int COUT_, int KS_, int TR_, int TW_, int BN_>
+struct GemmCfg {
+  static constexpr int NDIM = 2, CIN = CIN_, COUT = COUT_, KS = KS_;
+  static constexpr int TR = TR_, TW = TW_, BN = BN_;
+  static constexpr int CK = 16;                       // channels per K chunk (one 32x32x16 K step per tap)
+  static constexpr int TAPS = KS * KS;
+  static constexpr int KVP = TAPS * CK;               // packed weight row: [tap][16 channels]
+  static constexpr int NCHUNK = CIN / CK, NCB = COUT / BN;
+  static constexpr int BOXH = TR + KS - 1, BOXW = TW + KS - 1;
+  static constexpr int MB = BN / 32, NB = TW / 32;
+  static constexpr int NWAVES = TR, NT = NWAVES * 64;
+  static constexpr int X_CELLS = BOXH * BOXW;         // cells of a chunk's input box
+  static constexpr int STAGE_W = BN * TAPS * 32;                  // bytes of a chunk's weights
+  static constexpr int STAGE_X = (BOXH * BOXW * 32 + 1023) / 1024 * 1024;   // input box, whole KiB
+  static constexpr int STAGE = STAGE_W + STAGE_X;
+  static constexpr int NJ = STAGE / 1024, NJW = STAGE_W / 1024;   // 1 KiB LDS-DMA transfers per stage
+  static constexpr int JPW = (NJ + TR - 1) / TR;                  // transfers per wave
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int CK_ = CK, TD = 1, TH = TR;
+  static_assert(CIN % CK == 0 && COUT % BN == 0 && BN % 32 == 0 && TW % 32 == 0, "shape");
+  static_assert(STAGE_W % 1024 == 0, "weight slab in whole KiB");
+  static_assert(LDS + BN * 8 <= 160 * 1024, "LDS budget");
+  static_assert(NT <= 1024, "block size");
+};
+
+template <class C, bool BIAS, int MAXG>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void conv_gemm(const ConvArgs args) {
+  // two LDS stages, separate objects so the compiler can tell the stage being
+  // read from the one being filled
+  __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
+  __shared__ __attribute__((aligned(16))) float sbias[C::BN];
+  __shared__ uint32_t smax[C::BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;                             // output row of the tile
+  const int l32 = lane & 31;
+  const int g2 = lane >> 5;
+  constexpr bool MAXV = MAXG > 0;
+  constexpr int MG = MAXG > 0 ? MAXG : 1;
+  constexpr int NMX = 16 / MG;
+
+  for (int i = tid; i < C::BN; i += C::NT) smax[i] = 0u;
+
+  // fragment addresses within a stage.  A: [tap][BN][16 ch], B: box cells of
+  // 16 channels; the two 16-byte halves of a 32-byte row are swapped when bit
+  // 3 of the row (channel / column) is set, so 16 consecutive rows read by 16
+  // lanes cover all 64 banks.
+  int aoff[C::MB];
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) {
+    const int m = mb * 32 + l32;
+    aoff[mb] = m * 32 + 16 * (g2 ^ ((m >> 3) & 1));
+  }
+  int boff[C::NB][C::KS];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int dx = 0; dx < C::KS; ++dx) {
+      const int c = nb * 32 + l32 + dx;
+      boff[nb][dx] = C::STAGE_W + (w * C::BOXW + c) * 32 + 16 * (g2 ^ ((c >> 3) & 1));
+    }
+
+  const int total = args.total_tiles;
+  int t0 = blockIdx.x, tstride = gridDim.x, t_end = total;
+  if (gridDim.x >= 8 && (gridDim.x & 7) == 0) {
+    const int xcd = blockIdx.x & 7;
+    t0 = (int)((int64_t)total * xcd / 8) + (blockIdx.x >> 3);
+    tstride = gridDim.x >> 3;
+    t_end = (int)((int64_t)total * (xcd + 1) / 8);
+  }
+
+  // A tile: shard s, sample n, cout block cb, top-left output (h0, w0).
+  // Buffer descriptors and extents are rebuilt from the shard table when used.
+  struct Tile {
+    int valid, s, n, cb, h0, w0;
+  };
+  auto make_tile = [&](int t) __attribute__((always_inline)) {
+    Tile T;
+    T.valid = t < t_end;
+    const int tt = T.valid ? t : t0;
+    int s = 0;
+    while (s + 1 < args.nshards && args.sh[s + 1].tile_begin <= tt) ++s;
+    const ConvShardArg& sh = args.sh[s];
+    const int tiles_sp = sh.tiles_h * sh.tiles_w;
+    int r = tt - sh.tile_begin;
+    T.s = s;
+    T.cb = r % C::NCB;
+    r /= C::NCB;
+    T.n = r / tiles_sp;
+    r -= T.n * tiles_sp;
+    const int th = r / sh.tiles_w;
+    T.h0 = th * C::TR;
+    T.w0 = (r - th * sh.tiles_w) * C::TW;
+    return T;
+  };
+  auto rsrc_in = [&](const Tile& T) __attribute__((always_inline)) {
+    const ConvShardArg& sh = args.sh[T.s];
+    const int64_t in_n = (int64_t)sh.pad[1] * sh.pad[2] * C::CIN;
+    return make_rsrc(sh.in + T.n * in_n, T.valid ? in_n * 2 : 0);
+  };
+  auto rsrc_w = [&](const Tile& T) __attribute__((always_inline)) {
+    return make_rsrc(args.w + (size_t)T.cb * C::NCHUNK * C::STAGE_W / 2, T.valid ? (int64_t)C::NCHUNK * C::STAGE_W : 0);
+  };
+
+  constexpr uint32_t W_CHUNK = C::STAGE_W;            // bytes between chunks in the packed weights
+  // Stage filling by LDS-DMA: transfer j of a stage moves 1 KiB; lane l writes
+  // 16-byte slot s = 64 j + l.  Weights (j < NJW): slot s holds row s / 2
+  // (tap * BN + m), half (s & 1) ^ bit 3 of m.  Input (j >= NJW): slot s holds
+  // box cell q = s / 2 - 32 NJW, half (s & 1) ^ bit 3 of its column.  Lanes
+  // outside the box or the padded shard get an out-of-range offset: the
+  // transfer writes zeros there.  Wave w moves transfers w, w + TR, ...
+  auto fetch = [&](char* dst, int i, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rin, int gh0, int gw0,
+                   int p1, int p2, int cc) __attribute__((always_inline)) {
+    const int j = w + i * C::TR;
+    if (j >= C::NJ) return;
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    lds_ptr ldst = (lds_ptr)(dst + j * 1024);
+    const int slot = 64 * j + lane;
+    if (j < C::NJW) {
+      const int row = slot >> 1, m = row % C::BN;
+      const uint32_t off = (uint32_t)(row * 2 + ((slot & 1) ^ ((m >> 3) & 1))) * 16 + (uint32_t)cc * W_CHUNK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, ldst, 16, off, 0, 0, 0);
+    } else {
+      const int q = (slot >> 1) - 32 * C::NJW;
+      const int r = q / C::BOXW, c = q - r * C::BOXW;
+      const int h = (slot & 1) ^ ((c >> 3) & 1);
+      const int gh = gh0 + r, gw = gw0 + c;
+      const bool ok = q < C::X_CELLS && gh < p1 && gw < p2;
+      const uint32_t off = ok ? (uint32_t)((gh * p2 + gw) * C::CIN * 2 + 16 * h + cc * 32) : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rin, ldst, 16, off, 0, 0, 0);
+    }
+  };
+  auto wait_fetches = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0): this wave's transfers are in LDS
+    __syncthreads();
+  };
+
+
+  Tile T = make_tile(t0);
+  if (!T.valid) return;
+  for (int i = tid; i < C::BN; i += C::NT) sbias[i] = BIAS ? args.bias[T.cb * C::BN + i] : 0.f;
+#pragma unroll
+  for (int i = 0; i < C::JPW; ++i)
+    fetch(stage0, i, rsrc_w(T), rsrc_in(T), T.h0 + args.origin[1], T.w0 + args.origin[2], args.sh[T.s].pad[1],
+          args.sh[T.s].pad[2], 0);
+  wait_fetches();
+  int cur_key = MAXV ? T.n * C::NCB + T.cb : -1;
+
+  // per-(n, cout block) maxima collect in smax (one LDS atomic per slot and
+  // tile) and go to ymax when the block moves to another (n, cout block)
+  auto flush = [&](int n, int cb) __attribute__((always_inline)) {
+    __syncthreads();
+    const int gs = C::COUT / args.groups;
+    const int c_lo = cb * C::BN;
+    const int g_lo = c_lo / gs, g_hi = (c_lo + C::BN - 1) / gs;
+    for (int g = g_lo + tid; g <= g_hi; g += C::NT) {
+      uint32_t m = 0;
+      const int a = max(g * gs, c_lo), b = min((g + 1) * gs, c_lo + C::BN);
+      for (int c = a; c < b; ++c) m = max(m, smax[c - c_lo]);
+      atomicMax(&args.ymax[n * args.groups + g], m);
+    }
+    __syncthreads();
+    for (int i = tid; i < C::BN; i += C::NT) smax[i] = 0u;
+  };
+
+  int t = t0;
+  for (;;) {
+    f32x16 acc[C::MB][C::NB];
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) acc[mb][nb] = f32x16{};
+    // the current tile's transfer parameters (the last chunk fetches the next tile's first)
+    const __amdgpu_buffer_rsrc_t rwT = rsrc_w(T), rinT = rsrc_in(T);
+    const int gh0T = T.h0 + args.origin[1], gw0T = T.w0 + args.origin[2];
+    const int p1T = args.sh[T.s].pad[1], p2T = args.sh[T.s].pad[2];
+    Tile N = T;
+    // Per chunk: a barrier (every wave is done with the previous chunk, which
+    // read the other stage), the next chunk's transfers into the other stage
+    // during taps 0-2, and before the last tap a wait for them and a barrier;
+    // the last tap reads the next chunk's first operands.  Tap 0 runs on
+    // operands already in registers, so neither barrier stalls the matrix
+    // cores for an LDS round trip.  A tile has an even number of chunks and
+    // starts in stage 0; chunk cc reads stage cc & 1.
+    constexpr int TI1 = 3;                            // transfers issued during taps [0, TI1)
+    bf16x8 av[2][C::MB], bv[2][C::NB];
+    auto load_ops = [&](const char* sb, int tap, bf16x8 (&a)[C::MB], bf16x8 (&b)[C::NB]) __attribute__((always_inline)) {
+      const int dy = tap / C::KS, dx = tap - dy * C::KS;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+        a[mb] = *reinterpret_cast<const bf16x8*>(sb + tap * (C::BN * 32) + aoff[mb]);
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+        b[nb] = *reinterpret_cast<const bf16x8*>(sb + dy * (C::BOXW * 32) + boff[nb][dx]);
+    };
+    load_ops(stage0, 0, av[0], bv[0]);
+    auto chunk = [&](int cc, auto P) __attribute__((always_inline)) {
+      constexpr int par = decltype(P)::value;
+      char* const cur = par ? stage1 : stage0;
+      char* const nxt = par ? stage0 : stage1;
+      const bool last = cc + 1 == C::NCHUNK;
+      __amdgpu_buffer_rsrc_t rw = rwT, rin = rinT;
+      int gh0 = gh0T, gw0 = gw0T, p1 = p1T, p2 = p2T;
+      if (last) {
+        N = make_tile(t + tstride);
+        rw = rsrc_w(N);
+        rin = rsrc_in(N);
+        gh0 = N.h0 + args.origin[1];
+        gw0 = N.w0 + args.origin[2];
+        p1 = args.sh[N.s].pad[1];
+        p2 = args.sh[N.s].pad[2];
+      }
+      const int cn = last ? 0 : cc + 1;
+      constexpr int NRD = C::MB + C::NB, NMF = C::MB * C::NB;
+#pragma unroll
+      for (int tap = 0; tap < C::TAPS; ++tap) {
+        const int cb = (tap + par) & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        if (tap == 0) __syncthreads();
+        if (tap < TI1) {
+#pragma unroll
+          for (int i = tap * C::JPW / TI1; i < (tap + 1) * C::JPW / TI1; ++i)
+            fetch(nxt, i, rw, rin, gh0, gw0, p1, p2, cn);
+        }
+        if (tap + 1 == C::TAPS) wait_fetches();
+        // operands of the next tap; after the last tap, the next chunk's first
+        load_ops(tap + 1 < C::TAPS ? cur : nxt, tap + 1 < C::TAPS ? tap + 1 : 0, av[cb ^ 1], bv[cb ^ 1]);
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cb][mb], bv[cb][nb], acc[mb][nb], 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < NRD; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, NMF / NRD > 0 ? NMF / NRD : 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    static_assert(C::NCHUNK % 2 == 0 && C::TAPS % 2 == 1, "chunks pair up: stages and operand buffers alternate");
+#pragma unroll 1
+    for (int cc = 0; cc < C::NCHUNK; cc += 2) {
+      chunk(cc, std::integral_constant<int, 0>{});
+      chunk(cc + 1, std::integral_constant<int, 1>{});
+    }
+
+    // epilogue: bias, range-checked fp32 stores, running max
+    const int e1 = args.sh[T.s].ext[1], e2 = args.sh[T.s].ext[2];
+    const __amdgpu_buffer_rsrc_t rout = make_rsrc(args.sh[T.s].out + (int64_t)T.n * e1 * e2 * C::COUT,
+                                                  (int64_t)e1 * e2 * C::COUT * 4);
+    const int oh = T.h0 + w;
+    const bool row_ok = oh < e1;
+    float tmax[C::MB][NMX];                           // this tile's max|y| per slot of MG channels
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < NMX; ++i) tmax[mb][i] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+      const int ow = T.w0 + nb * 32 + l32;
+      const bool ok = row_ok && ow < e2;
+      const uint32_t cbase = ok ? (uint32_t)((((int64_t)oh * e2 + ow) * C::COUT + T.cb * C::BN + 4 * g2) * 4) : kOob;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int co = mb * 32 + 8 * jj;
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[mb][nb][4 * jj + i];
+          if (BIAS) {
+            const float4 bv4 = *reinterpret_cast<const float4*>(&sbias[4 * g2 + co]);
+            v[0] += bv4.x; v[1] += bv4.y; v[2] += bv4.z; v[3] += bv4.w;
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(v, rout, cbase + (uint32_t)(co * 4), 0, 0);
+          if (MAXV) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              tmax[mb][(4 * jj + i) / MG] = fmaxf(tmax[mb][(4 * jj + i) / MG], ok ? fabsf(v[i]) : 0.f);
+          }
+        }
+    }
+    if (MAXV) {
+      // over the 32 lanes that share the channels, then one LDS atomic per slot
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < NMX; ++i) {
+          float v = tmax[mb][i];
+          v = fmaxf(v, __shfl_xor(v, 1));
+          v = fmaxf(v, __shfl_xor(v, 2));
+          v = fmaxf(v, __shfl_xor(v, 4));
+          v = fmaxf(v, __shfl_xor(v, 8));
+          v = fmaxf(v, __shfl_xor(v, 16));
+          const int e = i * MG;
+          if (l32 == 0) atomicMax(&smax[4 * g2 + mb * 32 + 8 * (e >> 2) + (e & 3)], __float_as_uint(v));
+        }
+    }
+    if (!N.valid) break;
+    if (MAXV && N.n * C::NCB + N.cb != cur_key) {
+      flush(cur_key / C::NCB, cur_key % C::NCB);
+      cur_key = N.n * C::NCB + N.cb;
+    }
+    if (BIAS && N.cb != T.cb) {
+      __syncthreads();
+      for (int i = tid; i < C::BN; i += C::NT) sbias[i] = args.bias[N.cb * C::BN + i];
+      __syncthreads();
+    }
+    t += tstride;
+    T = N;
+  }
+  if (MAXV) flush(cur_key / C::NCB, cur_key % C::NCB);
 }
 
-// 2D 256->256 k3: 2x128 output box, 128 output channels per block, 32-channel K chunks
-using CfgImg256 = Cfg<2, 256, 256, 3, 1, 2, 128, 128, 32, 2>;
+template <class C>
+st_status run_gemm(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
+  int tiles = 0;
+  for (size_t s = 0; s < in_plan->shards.size(); ++s) {
+    const Shard& sd = in_plan->shards[s];
+    ConvShardArg& sh = a.sh[s];
+    const int64_t in_n = (int64_t)sd.pad[1] * sd.pad[2] * C::CIN;
+    const int64_t out_n = (int64_t)sd.ext[1] * sd.ext[2] * C::COUT;
+    if (in_n * 2 >= 0x7FFFFFFF || out_n * 4 >= 0x7FFFFFFF)
+      return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: shard too large for the tiled kernel");
+    sh.tiles_d = 1;
+    sh.tiles_h = (int)((sd.ext[1] + C::TR - 1) / C::TR);
+    sh.tiles_w = (int)((sd.ext[2] + C::TW - 1) / C::TW);
+    sh.tile_begin = tiles;
+    const int64_t t = (int64_t)in_plan->batch * sh.tiles_h * sh.tiles_w * C::NCB;
+    if ((int64_t)tiles + t > INT32_MAX) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: too many tiles");
+    tiles += (int)t;
+  }
+  a.total_tiles = tiles;
+  if (tiles == 0) return ST_OK;
+  int grid = std::min(tiles, device_cus());
+  if (grid >= 8) grid &= ~7;
+  const int gs = a.ymax ? C::COUT / a.groups : 0;
+  const int g = a.ymax == nullptr ? 0 : gs % 4 == 0 ? 4 : gs % 2 == 0 ? 2 : 1;
+  const dim3 gd(grid), bd(C::NT);
+  if (a.bias) {
+    if (g == 4) hipLaunchKernelGGL((conv_gemm<C, true, 4>), gd, bd, 0, stream, a);
+    else if (g == 2) hipLaunchKernelGGL((conv_gemm<C, true, 2>), gd, bd, 0, stream, a);
+    else if (g == 1) hipLaunchKernelGGL((conv_gemm<C, true, 1>), gd, bd, 0, stream, a);
+    else hipLaunchKernelGGL((conv_gemm<C, true, 0>), gd, bd, 0, stream, a);
+  } else {
+    if (g == 4) hipLaunchKernelGGL((conv_gemm<C, false, 4>), gd, bd, 0, stream, a);
+    else if (g == 2) hipLaunchKernelGGL((conv_gemm<C, false, 2>), gd, bd, 0, stream, a);
+    else if (g == 1) hipLaunchKernelGGL((conv_gemm<C, false, 1>), gd, bd, 0, stream, a);
+    else hipLaunchKernelGGL((conv_gemm<C, false, 0>), gd, bd, 0, stream, a);
+  }
+  return launch_check("st_conv_sharded: conv_gemm launch");
+}
+
+template <class C>
+constexpr Instance inst_gemm() {
+  return Instance{C::NDIM, C::CIN, C::COUT, C::KS, C::CK, C::KVP, C::NT,
+                  1, C::TR, C::TW, C::NCB, C::LDS, &run_gemm<C>, C::BN};
+}
+
+// 2D 256->256 k3: 4x96 output tiles x 128 output channels, 16-channel K chunks
+using GemmImg256 = GemmCfg<256, 256, 3, 4, 96, 128>;
 // 3D 16->16 k5 (16x16x32 instruction): 8x32 strips, 1 plane per step, 16 planes per job
 using RingVol16k5 = RingCfg<3, 16, 16, 5, 8, 32, 1, 16>;
 // 2D 64->64 k3: 64-column strips, 8 rows per step (4 per wave), 32 rows per job, 4 waves,
@@ -1344,7 +1451,7 @@ const Instance kInstances[] = {
     inst_rows<RowsImg64>(),
     inst_rows<RowsVol32>(),
     inst_ring<RingVol16k5>(),
-    inst<CfgImg256>(),
+    inst_gemm<GemmImg256>(),
 };
 
 const Instance* find_instance(int ndim, int cin, int cout, int ks) {
@@ -1385,6 +1492,13 @@ st_status st_conv_pack_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t 
   const int taps = (int)taps_of(ndim, ksize);
   if (dtype == ST_BF16) {
     if (const Instance* i = find_instance(ndim, cin, cout, ksize)) {
+      if (i->bn > 0) {
+        const int64_t total = (int64_t)cout * taps * cin;
+        hipLaunchKernelGGL(pack_w_gemm, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const uint16_t*>(weight), static_cast<uint16_t*>(packed), cin, cout,
+                           taps, i->ck, i->bn, total);
+        return launch_check("st_conv_pack_weights: launch");
+      }
       const int64_t total = (int64_t)(cin / i->ck) * cout * i->kvp;
       hipLaunchKernelGGL(pack_w_mfma, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
                          static_cast<const uint16_t*>(weight), static_cast<uint16_t*>(packed), cin, cout,
