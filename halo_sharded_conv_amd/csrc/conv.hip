@@ -15,13 +15,14 @@
 // layer shape (the instance table at the end):
 //   conv_rows  streams a strip of the shard along its outermost axis with the
 //              weights resident in LDS; 32x32x16 MFMA (64->64 and 32->32 k3)
-//   conv_ring  the same streaming structure on 16x16x32 MFMA for 16-channel
-//              layers (3D 16->16 k5)
+//   conv_pairs streams a 3D strip over the whole shard depth with 16x16
+//              channel blocks stacked two output planes per MFMA and the
+//              weights streamed per kernel row (3D 16->16 k5)
 //   conv_gemm  tiles with the weights streamed through LDS per 16-channel K
 //              chunk, for layers whose weights do not fit in LDS (2D 256->256)
-// Each output accumulates its K-steps in one fixed order (taps
-// lexicographic, channels ascending), so its bits do not depend on which
-// tile, job, shard or plan it belongs to.  Workgroups are persistent and deal
+// Each output accumulates its K-steps in an order fixed by the layer shape
+// alone (taps in one fixed order, channels ascending), so its bits do not
+// depend on which tile, job, shard or plan it belongs to.  Workgroups are persistent and deal
 // out their work per XCD, so neighbouring tiles share halo rows in one L2.
 //
 // fp32 path (and bf16 shapes without a matrix-core instance): a direct
@@ -223,6 +224,23 @@ __global__ void pack_w_gemm(const uint16_t* __restrict__ w, uint16_t* __restrict
   out[i] = w[((int64_t)(cb * bn + m) * cin + cc * ck + c) * taps + t];
 }
 
+// [Cout][Cin][kd][kh][kw] -> [kh][kd][kw][Cout][Cin]: the weights of one kernel
+// row dy are contiguous
+__global__ void pack_w_pairs(const uint16_t* __restrict__ w, uint16_t* __restrict__ out, int cin, int cout,
+                             int ks, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int c = (int)(i % cin);
+  int64_t r = i / cin;
+  const int o = (int)(r % cout);
+  r /= cout;
+  const int dx = (int)(r % ks);
+  r /= ks;
+  const int dz = (int)(r % ks);
+  const int dy = (int)(r / ks);
+  out[i] = w[((int64_t)o * cin + c) * ks * ks * ks + (dz * ks + dy) * ks + dx];
+}
+
 // [Cout][Cin][taps] -> [Cout][taps][Cin]
 template <typename T>
 __global__ void pack_w_direct(const T* __restrict__ w, T* __restrict__ out, int cin, int cout,
@@ -233,282 +251,6 @@ __global__ void pack_w_direct(const T* __restrict__ w, T* __restrict__ out, int 
   const int t = (int)((i / cin) % taps);
   const int o = (int)(i / ((int64_t)cin * taps));
   out[i] = w[((int64_t)o * cin + c) * taps + t];
-}
-
-// --------------------------------------------------------------------------
-// matrix-core implicit GEMM, streaming along the outermost spatial axis
-// --------------------------------------------------------------------------
-//
-// For shapes whose packed weights fit in LDS next to the input.  A job is one
-// strip of the shard (BW output columns, and BH output rows in 3D) over RC
-// consecutive output slices of the outermost axis (H in 2D, D in 3D).  The
-// workgroup walks the strip TS slices per step and keeps a ring of
-// RING = 2*TS + k - 1 input slices in LDS: the TS + k - 1 slices the current
-// step reads, plus the TS slices of the next step, which are loaded into
-// registers at the start of the step and written to LDS after its MFMAs and
-// stores.  HBM loads, matrix-core work and stores of consecutive steps
-// therefore overlap, and every input cell is read from HBM about once.
-
-template <int NDIM_, int CIN_, int COUT_, int KS_, int BH_, int BW_, int TS_, int RC_>
-struct RingCfg {
-  static constexpr int NDIM = NDIM_, CIN = CIN_, COUT = COUT_, KS = KS_;
-  static constexpr int BH = NDIM == 3 ? BH_ : 1;   // output rows per slice
-  static constexpr int BW = BW_;                    // output columns per slice
-  static constexpr int TS = TS_;                    // output slices per step
-  static constexpr int RC = RC_;                    // output slices per job
-  static constexpr int KH = NDIM == 3 ? KS : 1;     // taps along H inside a slice
-  static constexpr int SH = BH + KH - 1, SW = BW + KS - 1, SLICE = SH * SW;
-  static constexpr int RING = 2 * TS + KS - 1;
-  static constexpr int POS = TS * BH * BW;
-  static constexpr int NWAVES = POS / 64, NT = NWAVES * 64;
-  static constexpr int MB = COUT / 16, NB = 4;
-  static constexpr int TAPS = KS * KH * KS;
-  static constexpr int CK = CIN, KV = TAPS * CK;
-  static constexpr int KSTEPS = (KV + 31) / 32;
-  static constexpr int KU = KSTEPS <= 18 ? KSTEPS
-                            : KSTEPS % 9 == 0 ? 9 : KSTEPS % 7 == 0 ? 7 : KSTEPS % 5 == 0 ? 5
-                            : KSTEPS % 3 == 0 ? 3 : KSTEPS % 2 == 0 ? 2 : 1;
-  static constexpr int KVP = ((KV + 63) / 64) % 2 == 1 ? (KV + 63) / 64 * 64 : (KV + 63) / 64 * 64 + 64;
-  static constexpr int NCH = CK / 8;
-  static constexpr int KEYDIV = NCH >= 16 ? 1 : 16 / NCH;
-  static constexpr int LDS_W = COUT * KVP * 2;
-  static constexpr int LDS_X = RING * SLICE * CK * 2;
-  static constexpr int STEP_CHUNKS = TS * SLICE * NCH;
-  static constexpr int PF = (STEP_CHUNKS + NT - 1) / NT;
-  // weight packing shares the layout of the tile kernel (one channel chunk)
-  static constexpr int NCHUNK = 1, NCB = 1, TD = 1, TH = 1, TW = BW, BN = COUT;
-  static_assert(POS % 64 == 0 && BW % 16 == 0, "a wave covers 64 positions in 16-runs along W");
-  static_assert(COUT % 16 == 0 && CK % 8 == 0 && (CK >= 32 ? CK % 32 == 0 : 32 % CK == 0), "shape");
-  static_assert(RC % TS == 0, "job length");
-  static_assert(LDS_W + LDS_X + COUT * 4 <= 160 * 1024, "LDS budget");
-};
-
-template <class C>
-__device__ __forceinline__ int rxoff(int q, int j) {
-  return q * C::CK + 8 * (j ^ ((q / C::KEYDIV) % C::NCH));
-}
-
-template <class C>
-__global__ __launch_bounds__(C::NT) void conv_ring(const ConvArgs args) {
-  __shared__ __attribute__((aligned(16))) uint16_t sw[C::LDS_W / 2];
-  __shared__ __attribute__((aligned(16))) uint16_t sx[C::LDS_X / 2];
-  __shared__ uint32_t smax[C::COUT];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l16 = lane & 15;
-  const int g4 = lane >> 4;
-  const bool want_max = args.ymax != nullptr;
-  constexpr int RA = C::NDIM == 3 ? 0 : 1;          // internal index of the streamed axis
-
-  for (int i = tid; i < C::COUT; i += C::NT) smax[i] = 0u;
-  {  // resident weights, chunk j of row m stored at j ^ ((m >> 1) & 7)
-    constexpr int CPR = C::KVP / 8;
-    for (int i = tid; i < C::COUT * CPR; i += C::NT) {
-      const int m = i / CPR, j = i - m * CPR;
-      const uint4 v = *reinterpret_cast<const uint4*>(args.w + (size_t)m * C::KVP + 8 * j);
-      *reinterpret_cast<uint4*>(sw + m * C::KVP + 8 * (j ^ ((m >> 1) & 7))) = v;
-    }
-  }
-
-  // this lane's B-operand positions: slice ts, row ph, column pw of the step
-  int tsl[C::NB], qoff[C::NB], phh[C::NB], pww[C::NB];
-#pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) {
-    const int p = wave * 64 + nb * 16 + l16;
-    tsl[nb] = p / (C::BH * C::BW);
-    phh[nb] = (p / C::BW) % C::BH;
-    pww[nb] = p % C::BW;
-    qoff[nb] = phh[nb] * C::SW + pww[nb];
-  }
-
-  const int total = args.total_tiles;
-  int j0 = blockIdx.x, jstride = gridDim.x, j_end = total;
-  if (gridDim.x >= 8 && (gridDim.x & 7) == 0) {
-    const int xcd = blockIdx.x & 7;
-    j0 = (int)((int64_t)total * xcd / 8) + (blockIdx.x >> 3);
-    jstride = gridDim.x >> 3;
-    j_end = (int)((int64_t)total * (xcd + 1) / 8);
-  }
-
-  float runmax[C::MB][4];
-#pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) runmax[mb][i] = 0.f;
-  int cur_n = -1;
-
-  auto flush = [&](int n) {
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = runmax[mb][i];
-        v = fmaxf(v, __shfl_xor(v, 1));
-        v = fmaxf(v, __shfl_xor(v, 2));
-        v = fmaxf(v, __shfl_xor(v, 4));
-        v = fmaxf(v, __shfl_xor(v, 8));
-        runmax[mb][i] = 0.f;
-        if (l16 == 0) atomicMax(&smax[mb * 16 + 4 * g4 + i], __float_as_uint(v));
-      }
-    __syncthreads();
-    const int gs = C::COUT / args.groups;
-    for (int g = tid; g < args.groups; g += C::NT) {
-      uint32_t m = 0;
-      for (int c = g * gs; c < (g + 1) * gs; ++c) m = max(m, smax[c]);
-      atomicMax(&args.ymax[n * args.groups + g], m);
-    }
-    __syncthreads();
-    for (int i = tid; i < C::COUT; i += C::NT) smax[i] = 0u;
-  };
-
-  for (int job = j0; job < j_end; job += jstride) {
-    int s = 0;
-    while (s + 1 < args.nshards && args.sh[s + 1].tile_begin <= job) ++s;
-    const ConvShardArg& sh = args.sh[s];
-    // job -> (n, chunk of slices, strip row, strip column); columns innermost
-    const int strips = sh.tiles_h * sh.tiles_w;
-    int r = job - sh.tile_begin;
-    const int per_n = sh.tiles_d * strips;
-    const int n = r / per_n;
-    r -= n * per_n;
-    const int chunk = r / strips;
-    r -= chunk * strips;
-    const int sth = r / sh.tiles_w;
-    const int stw = r - sth * sh.tiles_w;
-    const int ext_ring = sh.ext[RA];
-    const int s_begin = chunk * C::RC;
-    const int s_end = min(s_begin + C::RC, ext_ring);
-    const int h0 = sth * C::BH, w0 = stw * C::BW;
-    const int o_ring = args.origin[RA], o_h = args.origin[1], o_w = args.origin[2];
-    const int p0 = sh.pad[0], p1 = sh.pad[1], p2 = sh.pad[2];
-    const int a_lim = s_end + C::KS - 1;           // input slices this job needs: [s_begin, a_lim)
-
-    if (want_max && n != cur_n) {
-      if (cur_n >= 0) flush(cur_n);
-      cur_n = n;
-    }
-
-    // global element offset of 16-byte piece u of input slice a (or -1)
-    auto piece = [&](int a, int u, int& slot_q, int& j) -> int64_t {
-      const int q = u / C::NCH;
-      j = u - q * C::NCH;
-      const int qr = q / C::SW, qc = q - qr * C::SW;
-      slot_q = (a % C::RING) * C::SLICE + q;
-      const int gr = a + o_ring;
-      const int gh = C::NDIM == 3 ? h0 + qr + o_h : gr;
-      const int gd = C::NDIM == 3 ? gr : 0;
-      const int gw = w0 + qc + o_w;
-      if (a >= a_lim || gd >= p0 || gh >= p1 || gw >= p2) return -1;
-      return ((((int64_t)n * p0 + gd) * p1 + gh) * p2 + gw) * C::CIN + 8 * j;
-    };
-
-    // prologue: the first step's TS + k - 1 slices
-    for (int u = tid; u < (C::TS + C::KS - 1) * C::SLICE * C::NCH; u += C::NT) {
-      const int rel = u / (C::SLICE * C::NCH);
-      int q, j;
-      const int64_t off = piece(s_begin + rel, u - rel * C::SLICE * C::NCH, q, j);
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (off >= 0) v = *reinterpret_cast<const uint4*>(sh.in + off);
-      *reinterpret_cast<uint4*>(sx + rxoff<C>(q, j)) = v;
-    }
-    __syncthreads();
-
-    for (int cur = s_begin; cur < s_end; cur += C::TS) {
-      // 1. prefetch the next step's new slices into registers
-      uint4 pf[C::PF];
-      int pf_q[C::PF], pf_j[C::PF];
-      const bool more = cur + C::TS < s_end;
-#pragma unroll
-      for (int k = 0; k < C::PF; ++k) {
-        const int u = tid + k * C::NT;
-        pf[k] = uint4{0u, 0u, 0u, 0u};
-        pf_q[k] = -1;
-        pf_j[k] = 0;
-        if (more && u < C::STEP_CHUNKS) {
-          const int rel = u / (C::SLICE * C::NCH);
-          int q, j;
-          const int64_t off = piece(cur + C::TS + C::KS - 1 + rel, u - rel * C::SLICE * C::NCH, q, j);
-          pf_q[k] = q;
-          pf_j[k] = j;
-          if (off >= 0) pf[k] = *reinterpret_cast<const uint4*>(sh.in + off);
-        }
-      }
-
-      // 2. matrix-core work of this step
-      f32x4 acc[C::MB][C::NB];
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int base = cur % C::RING;
-#pragma unroll 1
-      for (int ko = 0; ko < C::KSTEPS; ko += C::KU)
-#pragma unroll
-        for (int ki = 0; ki < C::KU; ++ki) {
-          const int ks = ko + ki;
-          const int tap_lo = (32 * ks) / C::CK;
-          const int tap = C::CK >= 32 ? tap_lo : tap_lo + (g4 >> 1);
-          const int c0 = C::CK >= 32 ? (32 * ks) % C::CK + 8 * g4 : 8 * (g4 & 1);
-          const bool valid = tap < C::TAPS;
-          const int tw = tap % C::KS;
-          const int th = (tap / C::KS) % C::KH;
-          const int tr = tap / (C::KS * C::KH);
-          bf16x8 a[C::MB], b[C::NB];
-#pragma unroll
-          for (int mb = 0; mb < C::MB; ++mb) {
-            const int m = mb * 16 + l16;
-            a[mb] = *reinterpret_cast<const bf16x8*>(sw + m * C::KVP + 8 * ((4 * ks + g4) ^ ((lane & 15) >> 1)));
-          }
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) {
-            int slot = base + tsl[nb] + tr;
-            slot -= slot >= C::RING ? C::RING : 0;
-            const int q = slot * C::SLICE + qoff[nb] + th * C::SW + tw;
-            if (valid) b[nb] = *reinterpret_cast<const bf16x8*>(sx + rxoff<C>(q, c0 >> 3));
-            else b[nb] = bf16x8{};
-          }
-#pragma unroll
-          for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
-        }
-
-      // 3. epilogue: bias, fp32 stores, running max
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        const int osl = cur + tsl[nb];
-        const int oh = C::NDIM == 3 ? h0 + phh[nb] : osl;
-        const int od = C::NDIM == 3 ? osl : 0;
-        const int ow = w0 + pww[nb];
-        if (osl >= s_end || oh >= sh.ext[1] || ow >= sh.ext[2]) continue;
-        const size_t cell = (((size_t)n * sh.ext[0] + od) * sh.ext[1] + oh) * sh.ext[2] + ow;
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) {
-          const int co = mb * 16 + 4 * g4;
-          f32x4 v = acc[mb][nb];
-          if (args.bias) {
-            v[0] += args.bias[co + 0];
-            v[1] += args.bias[co + 1];
-            v[2] += args.bias[co + 2];
-            v[3] += args.bias[co + 3];
-          }
-          *reinterpret_cast<f32x4*>(sh.out + cell * C::COUT + co) = v;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) runmax[mb][i] = fmaxf(runmax[mb][i], fabsf(v[i]));
-        }
-      }
-
-      // 4. the prefetched slices go into the ring slots this step did not read
-#pragma unroll
-      for (int k = 0; k < C::PF; ++k)
-        if (pf_q[k] >= 0) *reinterpret_cast<uint4*>(sx + rxoff<C>(pf_q[k], pf_j[k])) = pf[k];
-      __syncthreads();
-    }
-  }
-  if (want_max && cur_n >= 0) flush(cur_n);
 }
 
 // --------------------------------------------------------------------------
@@ -548,7 +290,9 @@ struct Instance {
   int td, th, tw, ncb;
   int lds;
   st_status (*run)(ConvArgs&, const st_plan*, hipStream_t);
-  int bn = 0;                 // > 0: weights packed [Cout/bn][Cin/ck][tap][bn][ck] (streamed-weight kernels)
+  int bn = 0;                 // cout block of the streamed-weight layout
+  int kind = 0;               // weight layout: 0 [Cin/ck][Cout][kvp]; 1 [Cout/bn][Cin/ck][tap][bn][ck];
+                              // 2 [kh][kd][kw][Cout][Cin] (plane pairs)
 };
 
 int device_cus() {
@@ -563,31 +307,6 @@ int device_cus() {
   return cus[dev];
 }
 
-template <class C>
-st_status run_ring(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
-  constexpr int RA = C::NDIM == 3 ? 0 : 1;
-  int jobs = 0;
-  for (size_t s = 0; s < in_plan->shards.size(); ++s) {
-    const Shard& sd = in_plan->shards[s];
-    ConvShardArg& sh = a.sh[s];
-    sh.tiles_d = (int)((sd.ext[RA] + C::RC - 1) / C::RC);          // slice chunks
-    sh.tiles_h = C::NDIM == 3 ? (int)((sd.ext[1] + C::BH - 1) / C::BH) : 1;
-    sh.tiles_w = (int)((sd.ext[2] + C::BW - 1) / C::BW);
-    sh.tile_begin = jobs;
-    const int64_t t = (int64_t)in_plan->batch * sh.tiles_d * sh.tiles_h * sh.tiles_w;
-    if ((int64_t)jobs + t > INT32_MAX) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: too many jobs");
-    jobs += (int)t;
-  }
-  a.total_tiles = jobs;
-  if (jobs == 0) return ST_OK;
-  int occ = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, conv_ring<C>, C::NT, 0) != hipSuccess || occ < 1)
-    occ = 1;
-  int grid = std::min(jobs, device_cus() * occ);
-  if (grid >= 8) grid &= ~7;
-  hipLaunchKernelGGL(conv_ring<C>, dim3(grid), dim3(C::NT), 0, stream, a);
-  return launch_check("st_conv_sharded: conv_ring launch");
-}
 
 
 // --------------------------------------------------------------------------
@@ -1051,11 +770,6 @@ constexpr Instance inst_rows() {
 }
 
 
-template <class C>
-constexpr Instance inst_ring() {
-  return Instance{C::NDIM, C::CIN, C::COUT, C::KS, C::CK, C::KVP, C::NT,
-                  1, C::BH, C::BW, 1, C::LDS_W + C::LDS_X, &run_ring<C>};
-}
 
 
 // --------------------------------------------------------------------------
@@ -1433,13 +1147,441 @@ st_status run_gemm(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
 template <class C>
 constexpr Instance inst_gemm() {
   return Instance{C::NDIM, C::CIN, C::COUT, C::KS, C::CK, C::KVP, C::NT,
-                  1, C::TR, C::TW, C::NCB, C::LDS, &run_gemm<C>, C::BN};
+                  1, C::TR, C::TW, C::NCB, C::LDS, &run_gemm<C>, C::BN, 1};
+}
+
+// --------------------------------------------------------------------------
+// 3D layers with 16 output channels: output-plane pairs on 32x32x16 MFMA
+// --------------------------------------------------------------------------
+//
+// With Cout = 16 one 32-row MFMA block would be half empty.  Here its 32
+// rows are two neighbouring output planes o, o+1 x 16 channels: the A operand
+// of input plane i stacks the weights of taps dz = i - o and dz = i - o - 1
+// (a zero block where that tap does not exist), so one input fragment (B)
+// feeds both planes.  A wave owns one row of a BH x BW strip (BW = 32
+// positions) and RW consecutive output planes (RW / 2 pairs): per in-plane tap
+// (dy, dx) it reads RW + k - 1 input fragments and k + 1 stacked weight
+// fragments for 3 RW MFMAs (83% of them useful for k = 5).  Every output
+// accumulates taps in the order (dy, dx, dz), whether it is the first or the
+// second plane of its pair; the zero blocks add exact zeros.
+//
+// The ring in LDS holds the TS + k - 1 input planes of one step (TS = RW, all
+// waves on the same planes); the next step's TS planes are fetched into
+// registers during the step and written over the oldest ones between two
+// barriers.  The weights (the same for every job) are streamed per kernel row
+// dy from L2 into two LDS stages by LDS-DMA, the next row's while the current
+// one is used.  A job is one strip of a shard over its whole depth.
+
+template <int CIN_, int COUT_, int KS_, int BH_, int BW_, int RW_>
+struct PairsCfg {
+  static constexpr int NDIM = 3, CIN = CIN_, COUT = COUT_, KS = KS_;
+  static constexpr int BH = BH_, BW = BW_, RW = RW_, TS = RW;
+  static constexpr int SH = BH + KS - 1, SW = BW + KS - 1, SLICE = SH * SW;
+  static constexpr int CB = CIN * 2;                  // bytes per input cell
+  static constexpr int SLICE_B = SLICE * CB;
+  static constexpr int RING = TS + KS - 1;
+  static constexpr int NPAIR = RW / 2, NE = KS + 1, NIN = RW + KS - 1;
+  static constexpr int NWAVES = BH, NT = NWAVES * 64;
+  static constexpr int TAPS = KS * KS * KS;
+  static constexpr int WROW = KS * KS * COUT * CB;    // weight bytes of one kernel row dy: [dz][dx][cout][cin]
+  static constexpr int WSTAGE = (WROW + 1023) / 1024 * 1024;
+  static constexpr int NJ = WSTAGE / 1024;            // 1 KiB LDS-DMA transfers per weight stage
+  static constexpr int JPW = (NJ + NWAVES - 1) / NWAVES;
+  static constexpr int LDS_X = RING * SLICE_B;
+  static constexpr int LDS = LDS_X + 2 * WSTAGE + 512;   // + a zero block for absent taps
+  static constexpr int STEP_CHUNKS = TS * SLICE * 2;  // 16-byte pieces of a step's new planes
+  static constexpr int PRO_CHUNKS = RING * SLICE * 2;
+  static constexpr int PF = (STEP_CHUNKS + NT - 1) / NT;
+  static constexpr int CK = CIN, KVP = TAPS * CIN, TD = 1, TH = BH, TW = BW, NCB = 1;
+  static_assert(CIN == 16 && COUT == 16, "one 16-channel K step per tap and 2 x 16 output rows per MFMA");
+  static_assert(BW == 32 && RW % 2 == 0, "tiling");
+  static_assert(NT <= 1024 && LDS + COUT * 8 <= 160 * 1024, "resources");
+};
+
+template <class C, bool BIAS, int MAXG>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void conv_pairs(const ConvArgs args) {
+  __shared__ __attribute__((aligned(1024))) char sring[C::LDS_X];
+  __shared__ __attribute__((aligned(1024))) char sw0[C::WSTAGE];
+  __shared__ __attribute__((aligned(1024))) char sw1[C::WSTAGE];
+  __shared__ __attribute__((aligned(16))) char szero[512];
+  __shared__ __attribute__((aligned(16))) float sbias[C::COUT];
+  __shared__ uint32_t smax[C::COUT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;                             // the wave's row in the strip
+  const int l32 = lane & 31;
+  const int g2 = lane >> 5;
+  constexpr bool MAXV = MAXG > 0;
+  constexpr int MG = MAXG > 0 ? MAXG : 1;
+  constexpr int NMX = 8 / MG;                         // running-max slots per lane (8 channels)
+
+  for (int i = tid; i < C::COUT; i += C::NT) {
+    smax[i] = 0u;
+    sbias[i] = BIAS ? args.bias[i] : 0.f;
+  }
+  for (int i = tid; i < 512 / 16; i += C::NT) reinterpret_cast<uint4*>(szero)[i] = make_uint4(0, 0, 0, 0);
+
+  // A rows: m = 16 p + c (p: which plane of the pair, c: output channel); the
+  // 16-byte halves of a 32-byte row swap when bit 3 of c is set
+  const int ap = l32 >> 4, ac = l32 & 15;
+  const int arow = ac * 32 + 16 * (g2 ^ ((ac >> 3) & 1));   // within a (dz, dx) block of 16 rows
+  // B: cell column of this lane for each dx, and its swapped half
+  int bcol[C::KS];
+#pragma unroll
+  for (int dx = 0; dx < C::KS; ++dx) {
+    const int c = l32 + dx;
+    bcol[dx] = c * 32 + 16 * (g2 ^ ((c >> 3) & 1));
+  }
+
+  const int total = args.total_tiles;
+  int j0 = blockIdx.x, jstride = gridDim.x, j_end = total;
+  if (gridDim.x >= 8 && (gridDim.x & 7) == 0) {
+    const int xcd = blockIdx.x & 7;
+    j0 = (int)((int64_t)total * xcd / 8) + (blockIdx.x >> 3);
+    jstride = gridDim.x >> 3;
+    j_end = (int)((int64_t)total * (xcd + 1) / 8);
+  }
+
+  float runmax[NMX];
+#pragma unroll
+  for (int i = 0; i < NMX; ++i) runmax[i] = 0.f;
+  int cur_n = -1;
+  auto flush = [&](int n) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NMX; ++i) {
+      float v = runmax[i];
+      v = fmaxf(v, __shfl_xor(v, 1));
+      v = fmaxf(v, __shfl_xor(v, 2));
+      v = fmaxf(v, __shfl_xor(v, 4));
+      v = fmaxf(v, __shfl_xor(v, 8));
+      v = fmaxf(v, __shfl_xor(v, 16));
+      runmax[i] = 0.f;
+      // slot i: channels 8 (i*MG / 4) + 4 g2 + (i*MG) % 4 .. + MG - 1
+      const int e = i * MG;
+      if (l32 == 0) atomicMax(&smax[8 * (e >> 2) + 4 * g2 + (e & 3)], __float_as_uint(v));
+    }
+    __syncthreads();
+    const int gs = C::COUT / args.groups;
+    for (int g = tid; g < args.groups; g += C::NT) {
+      uint32_t m = 0;
+      for (int c = g * gs; c < (g + 1) * gs; ++c) m = max(m, smax[c]);
+      atomicMax(&args.ymax[n * args.groups + g], m);
+    }
+    __syncthreads();
+    for (int i = tid; i < C::COUT; i += C::NT) smax[i] = 0u;
+  };
+
+  // A job: shard s, sample n, strip (h0, w0), all planes of the shard
+  // job's buffers start at its sample's first plane; each step rebases them
+  // at its own first plane so that in-step offsets stay below 2^31
+  struct Job {
+    int valid, n, h0, w0, depth, e1, e2, p1, p2, gh0, gw0;
+    uint32_t in_plane_b, out_plane_b;
+    int64_t out_cells, in_bytes, out_bytes;
+    const char* in;
+    char* out;
+  };
+  auto make_job = [&](int job) __attribute__((always_inline)) {
+    Job J;
+    J.valid = job < j_end;
+    const int jj = J.valid ? job : j0;
+    int s = 0;
+    while (s + 1 < args.nshards && args.sh[s + 1].tile_begin <= jj) ++s;
+    const ConvShardArg& sh = args.sh[s];
+    const int strips = sh.tiles_h * sh.tiles_w;
+    int r = jj - sh.tile_begin;
+    J.n = r / strips;
+    r -= J.n * strips;
+    const int sth = r / sh.tiles_w;
+    J.h0 = sth * C::BH;
+    J.w0 = (r - sth * sh.tiles_w) * C::BW;
+    J.depth = sh.ext[0];
+    J.e1 = sh.ext[1];
+    J.e2 = sh.ext[2];
+    const int p0 = sh.pad[0];
+    J.p1 = sh.pad[1];
+    J.p2 = sh.pad[2];
+    J.gh0 = J.h0 + args.origin[1];
+    J.gw0 = J.w0 + args.origin[2];
+    const int64_t in_plane = (int64_t)J.p1 * J.p2 * C::CIN;
+    const int64_t in_base = ((int64_t)J.n * p0 + args.origin[0]) * in_plane;
+    const int64_t in_total = (int64_t)args.batch * p0 * in_plane;
+    J.in_plane_b = (uint32_t)(in_plane * 2);
+    J.in = reinterpret_cast<const char*>(sh.in + in_base);
+    J.in_bytes = J.valid ? (in_total - in_base) * 2 : 0;
+    J.out_cells = (int64_t)J.e1 * J.e2;
+    J.out_plane_b = (uint32_t)(J.out_cells * C::COUT * 4);
+    const int64_t out_base = (int64_t)J.n * J.depth * J.out_cells * C::COUT;
+    J.out = reinterpret_cast<char*>(sh.out + out_base);
+    J.out_bytes = J.valid ? (int64_t)J.depth * J.out_cells * C::COUT * 4 : 0;
+    return J;
+  };
+  auto in_rsrc = [&](const Job& J, int c0) __attribute__((always_inline)) {
+    return make_rsrc(J.in + (int64_t)c0 * J.in_plane_b, J.in_bytes - (int64_t)c0 * J.in_plane_b);
+  };
+  // 16-byte piece u of a run of planes starting at input plane a0 (relative
+  // to the shard's first output plane): offset from input plane c0 (or kOob)
+  // and ring slot
+  auto piece_off = [&](const Job& J, int u, int lim, int a0, int c0) __attribute__((always_inline)) -> uint32_t {
+    const int rel = u / (C::SLICE * 2);
+    const int pc = u - rel * C::SLICE * 2;
+    const int q = pc >> 1, h = pc & 1;
+    const int qr = q / C::SW, qc = q - qr * C::SW;
+    const int gh = J.gh0 + qr, gw = J.gw0 + qc;
+    const int a = a0 + rel;
+    const bool ok = u < lim && gh < J.p1 && gw < J.p2 && a < J.depth + C::KS - 1;
+    return ok ? (uint32_t)(a - c0) * J.in_plane_b + (uint32_t)((gh * J.p2 + gw) * C::CIN * 2 + 16 * h) : kOob;
+  };
+  auto piece_lds = [&](int u, int a0) __attribute__((always_inline)) -> int {
+    const int rel = u / (C::SLICE * 2);
+    const int pc = u - rel * C::SLICE * 2;
+    const int q = pc >> 1, h = pc & 1;
+    const int qc = q % C::SW;
+    return ((a0 + rel) % C::RING) * C::SLICE_B + q * 32 + 16 * (h ^ ((qc >> 3) & 1));
+  };
+  // weights of kernel row dy -> a stage, by LDS-DMA; packed [dy][dz][dx][cout][cin]
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(args.w, (int64_t)C::KS * C::WROW);
+  auto fetch_w = [&](char* dst, int dy) __attribute__((always_inline)) {
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+#pragma unroll
+    for (int i = 0; i < C::JPW; ++i) {
+      const int j = w + i * C::NWAVES;
+      if (j < C::NJ) {
+        const int slot = 64 * j + lane;
+        const int row = slot >> 1, c = row & 15;
+        const bool ok = row < C::WROW / 32;
+        const uint32_t off = ok ? (uint32_t)(dy * C::WROW + (row * 2 + ((slot & 1) ^ ((c >> 3) & 1))) * 16) : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(dst + j * 1024), 16, off, 0, 0, 0);
+      }
+    }
+  };
+
+  Job J = make_job(j0);
+  if (!J.valid) return;
+  fetch_w(sw0, 0);
+  {  // first job's first TS + k - 1 planes
+    const __amdgpu_buffer_rsrc_t rin0 = in_rsrc(J, 0);
+    constexpr int PRO = (C::PRO_CHUNKS + C::NT - 1) / C::NT;
+    uint4 v[PRO];
+#pragma unroll
+    for (int k = 0; k < PRO; ++k)
+      v[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rin0, piece_off(J, tid + k * C::NT, C::PRO_CHUNKS, 0, 0), 0, 0));
+#pragma unroll
+    for (int k = 0; k < PRO; ++k)
+      if (tid + k * C::NT < C::PRO_CHUNKS) *reinterpret_cast<uint4*>(sring + piece_lds(tid + k * C::NT, 0)) = v[k];
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
+  if (MAXV) cur_n = J.n;
+  __syncthreads();
+
+  f32x16 acc[C::NPAIR];
+  int job = j0;
+  int cur = 0;                                        // first output plane of the step
+  // stage holding the current kernel row; with an odd number of rows per step
+  // the first row of a step alternates between the two stages
+  int sp = 0;
+  for (;;) {
+    const bool more = cur + C::TS < J.depth;
+    const __amdgpu_buffer_rsrc_t rin = in_rsrc(J, cur);
+    const __amdgpu_buffer_rsrc_t rout =
+        make_rsrc(J.out + (int64_t)cur * J.out_plane_b, J.out_bytes - (int64_t)cur * J.out_plane_b);
+    const int base = cur % C::RING;
+    int sbase[C::NIN];
+#pragma unroll
+    for (int r = 0; r < C::NIN; ++r) {
+      int sl = base + r;
+      sl -= sl >= C::RING ? C::RING : 0;
+      sbase[r] = sl * C::SLICE_B + w * (C::SW * 32);
+    }
+    // next step's planes -> registers, issued during kernel rows 0 and 1
+    uint4 pf[C::PF];
+    constexpr int PF0 = C::PF / 2, PF1 = C::PF - C::PF / 2;   // loads issued in rows 0 and 1
+    auto issue_pf = [&](int k) __attribute__((always_inline)) {
+      pf[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rin, piece_off(J, tid + k * C::NT, more ? C::STEP_CHUNKS : 0,
+                                                          cur + C::RING, cur), 0, 0));
+    };
+#pragma unroll
+    for (int q = 0; q < C::NPAIR; ++q) acc[q] = f32x16{};
+
+    bf16x8 av[2][C::NE];
+    bf16x8 bv[C::NIN];
+#pragma unroll
+    for (int dy = 0; dy < C::KS; ++dy) {
+      char* const wcur = sp ? sw1 : sw0;
+      char* const wnxt = sp ? sw0 : sw1;
+      // the stage of this row is complete on every wave, and every wave is
+      // done with the previous row (whose stage the next fetch overwrites)
+      __builtin_amdgcn_sched_barrier(0);
+      if (dy == 0) {
+        // this row's weights were fetched before the previous step's 4 * NPAIR
+        // stores: those may stay in flight
+        constexpr int NS = 4 * C::NPAIR;
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (NS & 15) | ((NS >> 4) << 14));
+      } else if (dy == 1) {
+        if (PF0 == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+        else __builtin_amdgcn_s_waitcnt(0x0F70 | (PF0 & 15) | ((PF0 >> 4) << 14));
+      } else if (dy == 2) {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (PF1 & 15) | ((PF1 >> 4) << 14));
+      } else if (dy > 2) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      fetch_w(wnxt, dy + 1 < C::KS ? dy + 1 : 0);     // the last row fetches the next step's first
+      if (dy == 0) {
+#pragma unroll
+        for (int k = 0; k < PF0; ++k) issue_pf(k);
+      } else if (dy == 1) {
+#pragma unroll
+        for (int k = PF0; k < C::PF; ++k) issue_pf(k);
+      }
+#pragma unroll
+      for (int dx = 0; dx < C::KS; ++dx) {
+        const int cb = dx & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        // A: stacked weights for every pair offset e (rows 0-15: tap e, rows 16-31: tap e-1)
+#pragma unroll
+        for (int e = 0; e < C::NE; ++e) {
+          const int dz = e - ap;
+          const char* p = (dz >= 0 && dz < C::KS) ? wcur + (dz * C::KS + dx) * (16 * 32) + arow : szero + 16 * g2;
+          av[cb][e] = *reinterpret_cast<const bf16x8*>(p);
+        }
+#pragma unroll
+        for (int i = 0; i < C::NIN; ++i)
+          bv[i] = *reinterpret_cast<const bf16x8*>(sring + sbase[i] + dy * (C::SW * 32) + bcol[dx]);
+#pragma unroll
+        for (int i = 0; i < C::NIN; ++i)
+#pragma unroll
+          for (int q = 0; q < C::NPAIR; ++q) {
+            const int e = i - 2 * q;
+            if (e >= 0 && e < C::NE)
+              acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cb][e], bv[i], acc[q], 0, 0, 0);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sp ^= 1;
+    }
+
+    // epilogue: pair q covers planes cur + 2q (rows 0-15) and cur + 2q + 1
+    {
+      const int oh = J.h0 + w, ow = J.w0 + l32;
+      const bool in_plane = oh < J.e1 && ow < J.e2;
+      const int64_t cell = (int64_t)oh * J.e2 + ow;
+#pragma unroll
+      for (int q = 0; q < C::NPAIR; ++q)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int plane = cur + 2 * q + (jj >> 1);
+          const bool ok = in_plane && plane < J.depth;
+          const int co = 8 * (jj & 1) + 4 * g2;
+          const uint32_t off = ok ? (uint32_t)((plane - cur) * J.out_plane_b + (cell * C::COUT + co) * 4) : kOob;
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[q][4 * jj + i];
+          if (BIAS) {
+            const float4 b4 = *reinterpret_cast<const float4*>(&sbias[co]);
+            v[0] += b4.x; v[1] += b4.y; v[2] += b4.z; v[3] += b4.w;
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(v, rout, off, 0, 0);
+          if (MAXV) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int slot = (4 * (jj & 1) + i) / MG;
+              runmax[slot] = fmaxf(runmax[slot], ok ? fabsf(v[i]) : 0.f);
+            }
+          }
+        }
+    }
+
+    // next step: fetched planes over the oldest TS; or the next job's ring
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int k = 0; k < C::PF; ++k) {
+        const int u = tid + k * C::NT;
+        if (u < C::STEP_CHUNKS) *reinterpret_cast<uint4*>(sring + piece_lds(u, cur + C::RING)) = pf[k];
+      }
+      __syncthreads();
+      cur += C::TS;
+    } else {
+      job += jstride;
+      const Job N = make_job(job);
+      if (!N.valid) break;
+      if (MAXV && N.n != cur_n) {
+        flush(cur_n);
+        cur_n = N.n;
+      }
+      J = N;
+      cur = 0;
+      const __amdgpu_buffer_rsrc_t rin0 = in_rsrc(J, 0);
+      constexpr int PRO = (C::PRO_CHUNKS + C::NT - 1) / C::NT;
+      uint4 v[PRO];
+#pragma unroll
+      for (int k = 0; k < PRO; ++k)
+        v[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rin0, piece_off(J, tid + k * C::NT, C::PRO_CHUNKS, 0, 0), 0, 0));
+#pragma unroll
+      for (int k = 0; k < PRO; ++k)
+        if (tid + k * C::NT < C::PRO_CHUNKS) *reinterpret_cast<uint4*>(sring + piece_lds(tid + k * C::NT, 0)) = v[k];
+      __syncthreads();
+    }
+  }
+  if (MAXV && cur_n >= 0) flush(cur_n);
+}
+
+template <class C>
+st_status run_pairs(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
+  int jobs = 0;
+  for (size_t s = 0; s < in_plan->shards.size(); ++s) {
+    const Shard& sd = in_plan->shards[s];
+    ConvShardArg& sh = a.sh[s];
+    // in-step offsets span RING + TS input planes and TS output planes
+    const int64_t in_plane_b = (int64_t)sd.pad[1] * sd.pad[2] * C::CIN * 2;
+    const int64_t out_plane_b = (int64_t)sd.ext[1] * sd.ext[2] * C::COUT * 4;
+    if (in_plane_b * (C::RING + C::TS) >= 0x7FFFFFFF || out_plane_b * C::TS >= 0x7FFFFFFF)
+      return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: shard planes too large for the plane-pair kernel");
+    sh.tiles_d = 1;
+    sh.tiles_h = (int)((sd.ext[1] + C::BH - 1) / C::BH);
+    sh.tiles_w = (int)((sd.ext[2] + C::BW - 1) / C::BW);
+    sh.tile_begin = jobs;
+    const int64_t t = (int64_t)in_plan->batch * sh.tiles_h * sh.tiles_w;
+    if ((int64_t)jobs + t > INT32_MAX) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: too many jobs");
+    jobs += (int)t;
+  }
+  a.total_tiles = jobs;
+  if (jobs == 0) return ST_OK;
+  int grid = std::min(jobs, device_cus());
+  if (grid >= 8) grid &= ~7;
+  const int gs = a.ymax ? C::COUT / a.groups : 0;
+  const int g = a.ymax == nullptr ? 0 : gs % 4 == 0 ? 4 : gs % 2 == 0 ? 2 : 1;
+  const dim3 gd(grid), bd(C::NT);
+  if (a.bias) {
+    if (g == 4) hipLaunchKernelGGL((conv_pairs<C, true, 4>), gd, bd, 0, stream, a);
+    else if (g == 2) hipLaunchKernelGGL((conv_pairs<C, true, 2>), gd, bd, 0, stream, a);
+    else if (g == 1) hipLaunchKernelGGL((conv_pairs<C, true, 1>), gd, bd, 0, stream, a);
+    else hipLaunchKernelGGL((conv_pairs<C, true, 0>), gd, bd, 0, stream, a);
+  } else {
+    if (g == 4) hipLaunchKernelGGL((conv_pairs<C, false, 4>), gd, bd, 0, stream, a);
+    else if (g == 2) hipLaunchKernelGGL((conv_pairs<C, false, 2>), gd, bd, 0, stream, a);
+    else if (g == 1) hipLaunchKernelGGL((conv_pairs<C, false, 1>), gd, bd, 0, stream, a);
+    else hipLaunchKernelGGL((conv_pairs<C, false, 0>), gd, bd, 0, stream, a);
+  }
+  return launch_check("st_conv_sharded: conv_pairs launch");
+}
+
+template <class C>
+constexpr Instance inst_pairs() {
+  return Instance{C::NDIM, C::CIN, C::COUT, C::KS, C::CK, C::KVP, C::NT,
+                  1, C::BH, C::BW, 1, C::LDS, &run_pairs<C>, 0, 2};
 }
 
 // 2D 256->256 k3: 4x96 output tiles x 128 output channels, 16-channel K chunks
 using GemmImg256 = GemmCfg<256, 256, 3, 4, 96, 128>;
-// 3D 16->16 k5 (16x16x32 instruction): 8x32 strips, 1 plane per step, 16 planes per job
-using RingVol16k5 = RingCfg<3, 16, 16, 5, 8, 32, 1, 16>;
+// 3D 16->16 k5: 4x32 strips, 8 output planes per step (4 pairs per wave), whole shard depth per job
+using PairsVol16k5 = PairsCfg<16, 16, 5, 4, 32, 8>;
 // 2D 64->64 k3: 64-column strips, 8 rows per step (4 per wave), 32 rows per job, 4 waves,
 // two passes over K per step (32 output channels each)
 using RowsImg64 = RowsCfg<2, 64, 64, 3, 1, 64, 8, 32, 4, 2>;
@@ -1450,7 +1592,7 @@ using RowsVol32 = RowsCfg<3, 32, 32, 3, 4, 32, 4, 16, 4, 1>;
 const Instance kInstances[] = {
     inst_rows<RowsImg64>(),
     inst_rows<RowsVol32>(),
-    inst_ring<RingVol16k5>(),
+    inst_pairs<PairsVol16k5>(),
     inst_gemm<GemmImg256>(),
 };
 
@@ -1492,7 +1634,14 @@ st_status st_conv_pack_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t 
   const int taps = (int)taps_of(ndim, ksize);
   if (dtype == ST_BF16) {
     if (const Instance* i = find_instance(ndim, cin, cout, ksize)) {
-      if (i->bn > 0) {
+      if (i->kind == 2) {
+        const int64_t total = (int64_t)cout * taps * cin;
+        hipLaunchKernelGGL(pack_w_pairs, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const uint16_t*>(weight), static_cast<uint16_t*>(packed), cin, cout,
+                           ksize, total);
+        return launch_check("st_conv_pack_weights: launch");
+      }
+      if (i->kind == 1) {
         const int64_t total = (int64_t)cout * taps * cin;
         hipLaunchKernelGGL(pack_w_gemm, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
                            static_cast<const uint16_t*>(weight), static_cast<uint16_t*>(packed), cin, cout,
