@@ -1188,12 +1188,19 @@ struct PairsCfg {
   static constexpr int NJ = WSTAGE / 1024;            // 1 KiB LDS-DMA transfers per weight stage
   static constexpr int JPW = (NJ + NWAVES - 1) / NWAVES;
   static constexpr int LDS_X = RING * SLICE_B;
-  static constexpr int LDS = LDS_X + 2 * WSTAGE + 512;   // + a zero block for absent taps
+  static constexpr int NSTAGE = 3;                    // weight stages: rows 0-4 use stages 0, 1, 2, 0, 1
+  static constexpr int LDS = LDS_X + NSTAGE * WSTAGE;
+  // the transfers past a row's weights write zeros (out-of-range lanes), so
+  // every stage ends in a zero block that stands for absent taps
+  static_assert(WSTAGE - WROW >= 32, "room for the zero block");
   static constexpr int STEP_CHUNKS = TS * SLICE * 2;  // 16-byte pieces of a step's new planes
   static constexpr int PRO_CHUNKS = RING * SLICE * 2;
   static constexpr int PF = (STEP_CHUNKS + NT - 1) / NT;
+  static constexpr int PFH = PF / 2;                  // loads per half: slice rows 0-3, then rows 4-7
+  static_assert(SH == 8 && STEP_CHUNKS == 2 * PFH * NT, "halves of whole slice rows");
   static constexpr int CK = CIN, KVP = TAPS * CIN, TD = 1, TH = BH, TW = BW, NCB = 1;
   static_assert(CIN == 16 && COUT == 16, "one 16-channel K step per tap and 2 x 16 output rows per MFMA");
+  static_assert(KS == 5, "the weight-stage schedule is written for five kernel rows");
   static_assert(BW == 32 && RW % 2 == 0, "tiling");
   static_assert(NT <= 1024 && LDS + COUT * 8 <= 160 * 1024, "resources");
 };
@@ -1203,13 +1210,13 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
   __shared__ __attribute__((aligned(1024))) char sring[C::LDS_X];
   __shared__ __attribute__((aligned(1024))) char sw0[C::WSTAGE];
   __shared__ __attribute__((aligned(1024))) char sw1[C::WSTAGE];
-  __shared__ __attribute__((aligned(16))) char szero[512];
+  __shared__ __attribute__((aligned(1024))) char sw2[C::WSTAGE];
   __shared__ __attribute__((aligned(16))) float sbias[C::COUT];
   __shared__ uint32_t smax[C::COUT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;                             // the wave's row in the strip
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // the wave's row in the strip
   const int l32 = lane & 31;
   const int g2 = lane >> 5;
   constexpr bool MAXV = MAXG > 0;
@@ -1220,7 +1227,6 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     smax[i] = 0u;
     sbias[i] = BIAS ? args.bias[i] : 0.f;
   }
-  for (int i = tid; i < 512 / 16; i += C::NT) reinterpret_cast<uint4*>(szero)[i] = make_uint4(0, 0, 0, 0);
 
   // A rows: m = 16 p + c (p: which plane of the pair, c: output channel); the
   // 16-byte halves of a 32-byte row swap when bit 3 of c is set
@@ -1317,21 +1323,50 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     J.out_bytes = J.valid ? (int64_t)J.depth * J.out_cells * C::COUT * 4 : 0;
     return J;
   };
-  auto in_rsrc = [&](const Job& J, int c0) __attribute__((always_inline)) {
-    return make_rsrc(J.in + (int64_t)c0 * J.in_plane_b, J.in_bytes - (int64_t)c0 * J.in_plane_b);
+  // input planes from c0 up to the shard's last padded plane (depth + k - 2):
+  // reads past it return zeros, so plane bounds need no per-lane test
+  auto in_rsrc = [&](const Job& J, int c0, bool any = true) __attribute__((always_inline)) {
+    const int64_t left = (int64_t)(J.depth + C::KS - 1 - c0) * J.in_plane_b;
+    const int64_t rest = J.in_bytes - (int64_t)c0 * J.in_plane_b;
+    return make_rsrc(J.in + (int64_t)c0 * J.in_plane_b, any ? (left < rest ? left : rest) : 0);
   };
-  // 16-byte piece u of a run of planes starting at input plane a0 (relative
-  // to the shard's first output plane): offset from input plane c0 (or kOob)
-  // and ring slot
-  auto piece_off = [&](const Job& J, int u, int lim, int a0, int c0) __attribute__((always_inline)) -> uint32_t {
+  // 16-byte piece u of a run of planes starting a0 planes after the
+  // descriptor's base: offset, or kOob outside the strip's padded rows and
+  // columns.  Step-invariant within a job (the descriptor moves instead).
+  auto piece_off = [&](const Job& J, int u, int lim, int a0) __attribute__((always_inline)) -> uint32_t {
     const int rel = u / (C::SLICE * 2);
     const int pc = u - rel * C::SLICE * 2;
     const int q = pc >> 1, h = pc & 1;
     const int qr = q / C::SW, qc = q - qr * C::SW;
     const int gh = J.gh0 + qr, gw = J.gw0 + qc;
-    const int a = a0 + rel;
-    const bool ok = u < lim && gh < J.p1 && gw < J.p2 && a < J.depth + C::KS - 1;
-    return ok ? (uint32_t)(a - c0) * J.in_plane_b + (uint32_t)((gh * J.p2 + gw) * C::CIN * 2 + 16 * h) : kOob;
+    const bool ok = u < lim && gh < J.p1 && gw < J.p2;
+    return ok ? (uint32_t)(a0 + rel) * J.in_plane_b + (uint32_t)((gh * J.p2 + gw) * C::CIN * 2 + 16 * h) : kOob;
+  };
+  // 16-byte piece u of a step's TS new planes, ordered (row, plane, column,
+  // half) so that the first half of the pieces holds slice rows 0-3: those
+  // rows of the ring are free once row 3 of the kernel is done, rows 4-7 only
+  // at the end of the step.  Offset from the step's first plane (kOob outside
+  // the strip's padded rows and columns), and LDS position for ring slot
+  // base + plane.
+  auto step_off = [&](const Job& J, int u) __attribute__((always_inline)) -> uint32_t {
+    const int h = u & 1;
+    int t = u >> 1;
+    const int qc = t % C::SW;
+    t /= C::SW;
+    const int rel = t % C::TS, qr = t / C::TS;
+    const int gh = J.gh0 + qr, gw = J.gw0 + qc;
+    const bool ok = gh < J.p1 && gw < J.p2;
+    return ok ? (uint32_t)(C::RING + rel) * J.in_plane_b + (uint32_t)((gh * J.p2 + gw) * C::CB + 16 * h) : kOob;
+  };
+  auto step_lds = [&](int u, int base) __attribute__((always_inline)) -> int {
+    const int h = u & 1;
+    int t = u >> 1;
+    const int qc = t % C::SW;
+    t /= C::SW;
+    const int rel = t % C::TS, qr = t / C::TS;
+    int sl = base + rel;
+    sl -= sl >= C::RING ? C::RING : 0;
+    return sl * C::SLICE_B + (qr * C::SW + qc) * 32 + 16 * (h ^ ((qc >> 3) & 1));
   };
   auto piece_lds = [&](int u, int a0) __attribute__((always_inline)) -> int {
     const int rel = u / (C::SLICE * 2);
@@ -1341,8 +1376,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     return ((a0 + rel) % C::RING) * C::SLICE_B + q * 32 + 16 * (h ^ ((qc >> 3) & 1));
   };
   // weights of kernel row dy -> a stage, by LDS-DMA; packed [dy][dz][dx][cout][cin]
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(args.w, (int64_t)C::KS * C::WROW);
   auto fetch_w = [&](char* dst, int dy) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(reinterpret_cast<const char*>(args.w) + dy * C::WROW, C::WROW);
     typedef __attribute__((address_space(3))) void* lds_ptr;
 #pragma unroll
     for (int i = 0; i < C::JPW; ++i) {
@@ -1351,7 +1386,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
         const int slot = 64 * j + lane;
         const int row = slot >> 1, c = row & 15;
         const bool ok = row < C::WROW / 32;
-        const uint32_t off = ok ? (uint32_t)(dy * C::WROW + (row * 2 + ((slot & 1) ^ ((c >> 3) & 1))) * 16) : kOob;
+        const uint32_t off = ok ? (uint32_t)((row * 2 + ((slot & 1) ^ ((c >> 3) & 1))) * 16) : kOob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(dst + j * 1024), 16, off, 0, 0, 0);
       }
     }
@@ -1359,7 +1394,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
 
   Job J = make_job(j0);
   if (!J.valid) return;
-  fetch_w(sw0, 0);
+  fetch_w(sw0, 0);                                    // rows 0-2 of the first step; later rows are
+  fetch_w(sw1, 1);                                    // fetched one or two rows ahead of their use
+  fetch_w(sw2, 2);
   {  // first job's first TS + k - 1 planes
     const __amdgpu_buffer_rsrc_t rin0 = in_rsrc(J, 0);
     constexpr int PRO = (C::PRO_CHUNKS + C::NT - 1) / C::NT;
@@ -1367,7 +1404,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
 #pragma unroll
     for (int k = 0; k < PRO; ++k)
       v[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                          rin0, piece_off(J, tid + k * C::NT, C::PRO_CHUNKS, 0, 0), 0, 0));
+                                          rin0, piece_off(J, tid + k * C::NT, C::PRO_CHUNKS, 0), 0, 0));
 #pragma unroll
     for (int k = 0; k < PRO; ++k)
       if (tid + k * C::NT < C::PRO_CHUNKS) *reinterpret_cast<uint4*>(sring + piece_lds(tid + k * C::NT, 0)) = v[k];
@@ -1377,14 +1414,18 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
   __syncthreads();
 
   f32x16 acc[C::NPAIR];
+  bf16x8 av[2][C::NE];                                // stacked weights, double-buffered by phase parity
+  bf16x8 bv[C::NIN];                                  // input fragments, each reloaded after its last use
+  uint4 pf[C::PFH];                                   // half of the next step's planes
+  uint32_t pfo[C::PF];                                // their offsets from the step's first plane
+#pragma unroll
+  for (int k = 0; k < C::PF; ++k) pfo[k] = step_off(J, tid + k * C::NT);
   int job = j0;
   int cur = 0;                                        // first output plane of the step
-  // stage holding the current kernel row; with an odd number of rows per step
-  // the first row of a step alternates between the two stages
-  int sp = 0;
+  constexpr int NS = 4 * C::NPAIR;                    // stores of one step's epilogue
   for (;;) {
     const bool more = cur + C::TS < J.depth;
-    const __amdgpu_buffer_rsrc_t rin = in_rsrc(J, cur);
+    const __amdgpu_buffer_rsrc_t rin = in_rsrc(J, cur, more);   // no planes to fetch in a job's last step
     const __amdgpu_buffer_rsrc_t rout =
         make_rsrc(J.out + (int64_t)cur * J.out_plane_b, J.out_bytes - (int64_t)cur * J.out_plane_b);
     const int base = cur % C::RING;
@@ -1395,77 +1436,115 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
       sl -= sl >= C::RING ? C::RING : 0;
       sbase[r] = sl * C::SLICE_B + w * (C::SW * 32);
     }
-    // next step's planes -> registers, issued during kernel rows 0 and 1
-    uint4 pf[C::PF];
-    constexpr int PF0 = C::PF / 2, PF1 = C::PF - C::PF / 2;   // loads issued in rows 0 and 1
-    auto issue_pf = [&](int k) __attribute__((always_inline)) {
-      pf[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rin, piece_off(J, tid + k * C::NT, more ? C::STEP_CHUNKS : 0,
-                                                          cur + C::RING, cur), 0, 0));
+    // kernel row -> weight stage, the same in every step, so that every LDS
+    // address below names its stage at compile time
+    auto stage = [&](int row) __attribute__((always_inline)) -> char* {
+      return row % 3 == 0 ? sw0 : row % 3 == 1 ? sw1 : sw2;
     };
-#pragma unroll
-    for (int q = 0; q < C::NPAIR; ++q) acc[q] = f32x16{};
+    // one base array per read (the stage, whose tail is the zero block), so
+    // the compiler can tell it apart from the transfers into other stages
+    auto load_a = [&](int buf, int row, int dx, int e) __attribute__((always_inline)) {
+      const int dz = e - ap;
+      const int off = (dz >= 0 && dz < C::KS) ? (dz * C::KS + dx) * (16 * 32) + arow : C::WROW + 16 * g2;
+      av[buf][e] = *reinterpret_cast<const bf16x8*>(stage(row) + off);
+    };
+    // the row base goes through an opaque scalar so that the compiler forms
+    // each address right before its read instead of keeping one register per
+    // (plane, dx) alive across the whole step
+    auto load_b = [&](int i, int dy, int dx) __attribute__((always_inline)) {
+      int rb = sbase[i] + dy * (C::SW * 32);
+      asm volatile("" : "+s"(rb));
+      bv[i] = *reinterpret_cast<const bf16x8*>(sring + rb + bcol[dx]);
+    };
 
-    bf16x8 av[2][C::NE];
-    bf16x8 bv[C::NIN];
+    // step start (row 1's weights are on their way): rows 0-3 of the next
+    // step's planes, then the first phase's operands
+#pragma unroll
+    for (int k = 0; k < C::PFH; ++k)
+      pf[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rin, pfo[k], 0, 0));
+#pragma unroll
+    for (int e = 0; e < C::NE; ++e) load_a(0, 0, 0, e);
+#pragma unroll
+    for (int i = 0; i < C::NIN; ++i) load_b(i, 0, 0);
+
+    // KS * KS phases (dy, dx); phase p issues the LDS reads of phase p + 1
+    // between its MFMAs: input fragment i right after its last use, the
+    // stacked weights into the other buffer
 #pragma unroll
     for (int dy = 0; dy < C::KS; ++dy) {
-      char* const wcur = sp ? sw1 : sw0;
-      char* const wnxt = sp ? sw0 : sw1;
-      // the stage of this row is complete on every wave, and every wave is
-      // done with the previous row (whose stage the next fetch overwrites)
-      __builtin_amdgcn_sched_barrier(0);
-      if (dy == 0) {
-        // this row's weights were fetched before the previous step's 4 * NPAIR
-        // stores: those may stay in flight
-        constexpr int NS = 4 * C::NPAIR;
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (NS & 15) | ((NS >> 4) << 14));
-      } else if (dy == 1) {
-        if (PF0 == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
-        else __builtin_amdgcn_s_waitcnt(0x0F70 | (PF0 & 15) | ((PF0 >> 4) << 14));
-      } else if (dy == 2) {
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (PF1 & 15) | ((PF1 >> 4) << 14));
-      } else if (dy > 2) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-      }
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-      fetch_w(wnxt, dy + 1 < C::KS ? dy + 1 : 0);     // the last row fetches the next step's first
-      if (dy == 0) {
-#pragma unroll
-        for (int k = 0; k < PF0; ++k) issue_pf(k);
-      } else if (dy == 1) {
-#pragma unroll
-        for (int k = PF0; k < C::PF; ++k) issue_pf(k);
-      }
 #pragma unroll
       for (int dx = 0; dx < C::KS; ++dx) {
-        const int cb = dx & 1;
+        const int ph = dy * C::KS + dx;
+        const int cb = ph & 1;
+        const bool last = ph == C::KS * C::KS - 1;
+        const int ndy = dx + 1 < C::KS ? dy : dy + 1;
+        const int ndx = dx + 1 < C::KS ? dx + 1 : 0;
         __builtin_amdgcn_sched_barrier(0);
-        // A: stacked weights for every pair offset e (rows 0-15: tap e, rows 16-31: tap e-1)
+        if (dx == C::KS - 1 && dy + 1 < C::KS) {
+          // row dy + 1 must be complete on every wave before phase
+          // (dy + 1, 0)'s operands are read, and past the barrier every
+          // wave's reads of row dy's stage are done, so that stage takes the
+          // next row that uses it:
+          //   dy 0: row 3 -> stage 0     dy 1: row 4 -> stage 1
+          //   dy 2: next step's row 2 -> stage 2
+          //   dy 3: next step's row 0 -> stage 0 (row 1 follows at step start)
+          // Waits: row 1 was fetched just before the previous step's NS
+          // stores and this step's PFH plane loads; row 2 is older than row
+          // 1; rows 3 and 4 each have one later fetch (3 or 4 transfers per
+          // wave) behind them.
+          constexpr int JMIN = C::NJ / C::NWAVES;
+          constexpr int W0 = NS + C::PFH;
+          if (dy == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (W0 & 15) | ((W0 >> 4) << 14));
+          else if (dy >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (JMIN & 15) | ((JMIN >> 4) << 14));
+          __syncthreads();
+          __builtin_amdgcn_sched_barrier(0);
+          if (dy == 0) fetch_w(sw0, 3);
+          else if (dy == 1) fetch_w(sw1, 4);
+          else if (dy == 2) fetch_w(sw2, 2);
+          if (dy == 3) {
+            // ring rows 0-3 are done: the fetched rows 0-3 of the next
+            // step's planes go over the oldest planes, and rows 4-7 start
+            if (more) {
 #pragma unroll
-        for (int e = 0; e < C::NE; ++e) {
-          const int dz = e - ap;
-          const char* p = (dz >= 0 && dz < C::KS) ? wcur + (dz * C::KS + dx) * (16 * 32) + arow : szero + 16 * g2;
-          av[cb][e] = *reinterpret_cast<const bf16x8*>(p);
+              for (int k = 0; k < C::PFH; ++k)
+                *reinterpret_cast<uint4*>(sring + step_lds(tid + k * C::NT, base)) = pf[k];
+            }
+            fetch_w(sw0, 0);
+#pragma unroll
+            for (int k = 0; k < C::PFH; ++k)
+              pf[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rin, pfo[C::PFH + k], 0, 0));
+          }
         }
 #pragma unroll
-        for (int i = 0; i < C::NIN; ++i)
-          bv[i] = *reinterpret_cast<const bf16x8*>(sring + sbase[i] + dy * (C::SW * 32) + bcol[dx]);
-#pragma unroll
-        for (int i = 0; i < C::NIN; ++i)
+        for (int i = 0; i < C::NIN; ++i) {
 #pragma unroll
           for (int q = 0; q < C::NPAIR; ++q) {
             const int e = i - 2 * q;
-            if (e >= 0 && e < C::NE)
-              acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cb][e], bv[i], acc[q], 0, 0, 0);
+            if (e >= 0 && e < C::NE) {
+              if (ph == 0 && e == 0)
+                acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cb][e], bv[i], f32x16{}, 0, 0, 0);
+              else
+                acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cb][e], bv[i], acc[q], 0, 0, 0);
+            }
           }
-        __builtin_amdgcn_sched_barrier(0);
+          if (!last) {
+            load_b(i, ndy, ndx);
+            if (i < C::NE) load_a(cb ^ 1, ndy, ndx, i);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      sp ^= 1;
     }
 
-    // epilogue: pair q covers planes cur + 2q (rows 0-15) and cur + 2q + 1
+    // every wave is done with row 4's stage, and the next step's row 0
+    // (fetched at row 3) and planes are complete: row 1 goes to stage 1
+    // ahead of the stores, so that waiting for it never waits for them
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    fetch_w(sw1, 1);
+
+    // epilogue: pair q covers planes cur + 2q (rows 0-15) and cur + 2q + 1;
+    // planes past the shard fall outside the output descriptor's range
     {
       const int oh = J.h0 + w, ow = J.w0 + l32;
       const bool in_plane = oh < J.e1 && ow < J.e2;
@@ -1475,7 +1554,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int plane = cur + 2 * q + (jj >> 1);
-          const bool ok = in_plane && plane < J.depth;
+          const bool ok = in_plane;                   // planes past the shard: dropped by the range
+          const bool real = in_plane && plane < J.depth;
           const int co = 8 * (jj & 1) + 4 * g2;
           const uint32_t off = ok ? (uint32_t)((plane - cur) * J.out_plane_b + (cell * C::COUT + co) * 4) : kOob;
           f32x4 v;
@@ -1490,20 +1570,17 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int slot = (4 * (jj & 1) + i) / MG;
-              runmax[slot] = fmaxf(runmax[slot], ok ? fabsf(v[i]) : 0.f);
+              runmax[slot] = fmaxf(runmax[slot], real ? fabsf(v[i]) : 0.f);
             }
           }
         }
     }
 
-    // next step: fetched planes over the oldest TS; or the next job's ring
-    __syncthreads();
     if (more) {
+      // rows 4-7 of the fetched planes over the oldest TS
 #pragma unroll
-      for (int k = 0; k < C::PF; ++k) {
-        const int u = tid + k * C::NT;
-        if (u < C::STEP_CHUNKS) *reinterpret_cast<uint4*>(sring + piece_lds(u, cur + C::RING)) = pf[k];
-      }
+      for (int k = 0; k < C::PFH; ++k)
+        *reinterpret_cast<uint4*>(sring + step_lds(tid + (C::PFH + k) * C::NT, base)) = pf[k];
       __syncthreads();
       cur += C::TS;
     } else {
@@ -1516,13 +1593,15 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
       }
       J = N;
       cur = 0;
+#pragma unroll
+      for (int k = 0; k < C::PF; ++k) pfo[k] = step_off(J, tid + k * C::NT);
       const __amdgpu_buffer_rsrc_t rin0 = in_rsrc(J, 0);
       constexpr int PRO = (C::PRO_CHUNKS + C::NT - 1) / C::NT;
       uint4 v[PRO];
 #pragma unroll
       for (int k = 0; k < PRO; ++k)
         v[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rin0, piece_off(J, tid + k * C::NT, C::PRO_CHUNKS, 0, 0), 0, 0));
+                                            rin0, piece_off(J, tid + k * C::NT, C::PRO_CHUNKS, 0), 0, 0));
 #pragma unroll
       for (int k = 0; k < PRO; ++k)
         if (tid + k * C::NT < C::PRO_CHUNKS) *reinterpret_cast<uint4*>(sring + piece_lds(tid + k * C::NT, 0)) = v[k];
