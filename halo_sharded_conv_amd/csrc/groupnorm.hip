@@ -33,7 +33,8 @@ namespace st {
 namespace {
 
 constexpr int kNT = 256;        // threads per block
-constexpr int kIter = 16;       // vectors per thread per item (even: the apply pass takes halves)
+constexpr int kIter = 32;       // vectors per thread per item (a multiple of kPart)
+constexpr int kPart = 8;        // vectors per thread per apply work unit
 
 struct GnShard {
   const float* y;
@@ -70,6 +71,19 @@ template <> struct Vec<1> {
   using T = float;
   static __device__ __forceinline__ float get(const T& v, int) { return v; }
 };
+
+// streaming load (y is read once per pass): the non-temporal hint keeps
+// it from displacing lines that other blocks still need
+template <int VW>
+__device__ __forceinline__ typename Vec<VW>::T load_nt(const typename Vec<VW>::T* p, int64_t i) {
+  if constexpr (VW == 4) {
+    typedef float nf4 __attribute__((ext_vector_type(4)));
+    const nf4 t = __builtin_nontemporal_load(reinterpret_cast<const nf4*>(p) + i);
+    return make_float4(t.x, t.y, t.z, t.w);
+  } else {
+    return __builtin_nontemporal_load(p + i);
+  }
+}
 
 __device__ __forceinline__ void decode_item(const GnArgs& a, int item, int& s, int& n, int& k) {
   s = 0;
@@ -234,7 +248,10 @@ __global__ __launch_bounds__(kNT) void gn_stats(const GnArgs a) {
 #pragma unroll
     for (int i = 0; i < kIter; ++i) {
       const int64_t v = v0 + i * kNT;
-      val[i] = v < sh.vecs_per_n ? y[v] : typename V::T{};   // zeros contribute 0
+      // every load issues (clamped index; the tail is masked afterwards), so
+      // all of them are in flight before the first is used
+      const typename V::T t = load_nt<VW>(y, v < sh.vecs_per_n ? v : sh.vecs_per_n - 1);
+      val[i] = v < sh.vecs_per_n ? t : typename V::T{};   // zeros contribute 0
     }
 #pragma unroll
     for (int i = 0; i < kIter; ++i) {
@@ -289,14 +306,15 @@ __global__ __launch_bounds__(kNT) void gn_apply(const GnArgs a) {
   const int C = a.channels;
   int cur = -1;
   float4 p[VW];
-  // half items (kIter / 2 vectors per thread: more waves in flight), visited
-  // last item first so the pass begins on the part of y the statistics pass
-  // read last
-  constexpr int kHalf = kIter / 2;
-  for (int h = blockIdx.x; h < 2 * a.total_items; h += gridDim.x) {
-    const int hr = 2 * a.total_items - 1 - h;
+  // work units of kPart vectors per thread (a part of an item: more waves
+  // in flight), visited last unit first so the pass begins on the part of y
+  // the statistics pass read last
+  constexpr int kParts = kIter / kPart;
+  static_assert(kIter % kPart == 0, "whole parts per item");
+  for (int h = blockIdx.x; h < kParts * a.total_items; h += gridDim.x) {
+    const int hr = kParts * a.total_items - 1 - h;
     int s, n, k;
-    decode_item(a, hr >> 1, s, n, k);
+    decode_item(a, hr / kParts, s, n, k);
     const int key = s * a.batch + n;
     if (FIXED && key != cur) {
       const int c0 = (tid * VW) % C;
@@ -307,15 +325,15 @@ __global__ __launch_bounds__(kNT) void gn_apply(const GnArgs a) {
     const GnShard& sh = a.sh[s];
     const typename V::T* y = reinterpret_cast<const typename V::T*>(sh.y) + n * sh.vecs_per_n;
     typename V::T* z = reinterpret_cast<typename V::T*>(sh.z) + n * sh.vecs_per_n;
-    const int64_t v0 = (int64_t)k * kNT * kIter + (hr & 1) * kNT * kHalf + tid;
-    typename V::T val[kHalf];
+    const int64_t v0 = (int64_t)k * kNT * kIter + (hr % kParts) * kNT * kPart + tid;
+    typename V::T val[kPart];
 #pragma unroll
-    for (int i = 0; i < kHalf; ++i) {
+    for (int i = 0; i < kPart; ++i) {
       const int64_t v = v0 + i * kNT;
-      val[i] = v < sh.vecs_per_n ? y[v] : typename V::T{};
+      val[i] = load_nt<VW>(y, v < sh.vecs_per_n ? v : sh.vecs_per_n - 1);   // tail: stored by no lane
     }
 #pragma unroll
-    for (int i = 0; i < kHalf; ++i) {
+    for (int i = 0; i < kPart; ++i) {
       const int64_t v = v0 + i * kNT;
       if (v >= sh.vecs_per_n) break;
       float out[VW];
@@ -427,13 +445,14 @@ st_status prepare(const st_plan* y_plan, const float* const* y_bufs, float* cons
     g.items_per_n = (int32_t)((g.vecs_per_n + item_vecs - 1) / item_vecs);
     g.item_begin = (int32_t)items;
     items += (int64_t)g.items_per_n * a.batch;
-    if (items > INT32_MAX / 2) return err(ST_ERR_UNSUPPORTED, "volume too large");
+    if (items > INT32_MAX / (kIter / kPart)) return err(ST_ERR_UNSUPPORTED, "volume too large");
   }
   a.total_items = (int)items;
   return ST_OK;
 }
 
-int grid_of(const GnArgs& a) { return std::max(1, std::min(a.total_items, device_cus() * 8)); }
+// 4 blocks of 32 in-flight 16-byte loads per thread per CU
+int grid_of(const GnArgs& a) { return std::max(1, std::min(a.total_items, device_cus() * 4)); }
 
 template <int VW, bool FIXED>
 st_status launch_partials(GnArgs& a, bool need_max, hipStream_t st) {
@@ -449,7 +468,7 @@ st_status launch_partials(GnArgs& a, bool need_max, hipStream_t st) {
 
 template <int VW, bool FIXED>
 st_status launch_apply(GnArgs& a, hipStream_t st) {
-  const int grid = std::max(1, std::min(2 * a.total_items, device_cus() * 16));
+  const int grid = std::max(1, std::min((kIter / kPart) * a.total_items, device_cus() * 16));
   hipLaunchKernelGGL((gn_apply<VW, FIXED>), dim3(grid), dim3(kNT), 0, st, a);
   return launch_check("st_groupnorm_apply: launch");
 }
