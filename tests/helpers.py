@@ -38,6 +38,8 @@ def small_cases():
         "img64_b2": synth.small_variant(W["img2048_c64_k3_bf16"], (20, 130), ((8, 12), (130,)), batch=2),
         "vol32_grid": synth.small_variant(W["vol256_c32_k3_bf16"], (9, 19, 37), ((4, 5), (11, 8), (17, 20))),
         "vol16k5": synth.small_variant(W["vol512_c16_k5_bf16"], (23, 13, 40), ((2, 5, 3, 4, 2, 3, 2, 2), (13,), (40,))),
+        # two samples, shards deeper than one 8-plane step of the k5 kernel
+        "vol16k5_b2": synth.small_variant(W["vol512_c16_k5_bf16"], (21, 9, 33), ((9, 12), (9,), (33,)), batch=2),
         "grid256_small": synth.small_variant(W["grid1024x1792_c256_k3_bf16"], (5, 150), ((5,), (80, 70))),
     }
 

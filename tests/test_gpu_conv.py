@@ -81,7 +81,7 @@ def test_identity_kernel_exact(name):
     assert bits_equal(layer.y_host(), want)
 
 
-@pytest.mark.parametrize("name", ["vol32_full", "img64_b2", "vol32_grid", "vol16k5", "grid256_small"])
+@pytest.mark.parametrize("name", ["vol32_full", "img64_b2", "vol32_grid", "vol16k5", "vol16k5_b2", "grid256_small"])
 def test_shift_kernel_exact(name):
     """One-hot kernel at a corner tap: y[i] = x[i + t - p] with zeros entering
     at the global faces; crosses every shard seam, face, edge and corner."""
