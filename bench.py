@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--exchange", choices=("pack+unpack", "fused"), default="pack+unpack",
+                    help="halo exchange as two copies through a message buffer, or one fused copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the oracle's CPU sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -45,7 +47,7 @@ def parse():
 
 COPY_BYTES = 1 << 30                 # bytes read (and written) by --calibrate-copy
 STAGE_KERNELS = {                    # kernel-name fragments of each library stage
-    "halo_pack": ("halo_copy",), "halo_unpack": ("halo_copy",),
+    "halo_pack": ("halo_copy",), "halo_unpack": ("halo_copy",), "halo_exchange": ("halo_copy",),
     "conv": ("conv_rows", "conv_ring", "conv_mfma", "conv_direct"),
     "gn_partials": ("gn_max", "gn_stats"), "gn_apply": ("gn_apply",),
 }
@@ -53,6 +55,7 @@ STAGE_KERNELS = {                    # kernel-name fragments of each library sta
 
 STAGE_SOURCES = {                    # library sources that define each stage's kernels and launches
     "halo_pack": ("halo.hip", "plan.cpp", "internal.h"), "halo_unpack": ("halo.hip", "plan.cpp", "internal.h"),
+    "halo_exchange": ("halo.hip", "plan.cpp", "internal.h"),
     "conv": ("conv.hip", "internal.h"),
     "gn_partials": ("groupnorm.hip", "internal.h"), "gn_apply": ("groupnorm.hip", "internal.h"),
 }
@@ -159,6 +162,7 @@ def algorithmic(wl, layer):
     return {
         "halo_pack": {"bytes": 2 * payload},                 # read boxes, write message
         "halo_unpack": {"bytes": 2 * payload},               # read message, write margins
+        "halo_exchange": {"bytes": 2 * payload},             # read boxes, write margins
         "conv": {"bytes": x_bytes + y_bytes, "flops": wl.conv_flops},
         "gn_partials": {"bytes": y_bytes},
         "gn_combine": {"bytes": 0},
@@ -213,8 +217,11 @@ def main():
     layer.load_input(synth.make_input(wl))
     stream = torch.cuda.current_stream()
 
-    stages = [("halo_pack", lambda: layer.exchange_pack()), ("halo_unpack", lambda: layer.exchange_unpack()),
-              ("conv", layer.conv), ("gn_partials", layer.norm_partials), ("gn_combine", layer.norm_combine),
+    if args.exchange == "fused":
+        halo = [("halo_exchange", lambda: layer.exchange_fused())]
+    else:
+        halo = [("halo_pack", lambda: layer.exchange_pack()), ("halo_unpack", lambda: layer.exchange_unpack())]
+    stages = halo + [("conv", layer.conv), ("gn_partials", layer.norm_partials), ("gn_combine", layer.norm_combine),
               ("gn_apply", layer.norm_apply)]
 
     for _ in range(args.warmup):
@@ -282,7 +289,7 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "shape": [wl.batch, wl.cin, *wl.spatial], "cout": wl.cout,
-                   "kernel": wl.ksize, "shards": [list(s) for s in wl.shards], "halo": wl.halo,
+                   "kernel": wl.ksize, "shards": [list(s) for s in wl.shards], "halo": wl.halo, "exchange": args.exchange,
                    "groups": wl.groups, "accumulate": "f32", "outputs": "f32"},
         "roofline": roof,
         "kernels": kernels,

@@ -87,6 +87,7 @@ def _load() -> ctypes.CDLL:
         "st_plan_halo_box": (I32, [P, I32, ctypes.POINTER(_HaloBox)]),
         "st_halo_pack": (I32, [P, PP, P, P]),
         "st_halo_unpack": (I32, [P, P, PP, I32, P]),
+        "st_halo_exchange": (I32, [P, PP, I32, P]),
         "st_conv_weight_bytes": (SZ, [I32, I32, I32, I32, I32]),
         "st_conv_pack_weights": (I32, [I32, I32, I32, I32, I32, P, P, P]),
         "st_conv_sharded": (I32, [P, PP, P, P, I32, I32, P, PP, P, I32, P]),
@@ -253,6 +254,12 @@ def st_halo_unpack(plan: Plan, msg, shard_bufs, zero_global_margins: bool = True
                               _stream(stream)), "st_halo_unpack")
 
 
+
+def st_halo_exchange(plan: Plan, shard_bufs, zero_global_margins: bool = True, stream=None) -> None:
+    arr = _ptr_array(shard_bufs, "st_halo_exchange shard", _shard_bytes(plan))
+    _check(lib.st_halo_exchange(plan.handle, arr, int(bool(zero_global_margins)), _stream(stream)),
+           "st_halo_exchange")
+
 def st_conv_weight_bytes(ndim: int, cin: int, cout: int, ksize: int, dtype) -> int:
     return int(lib.st_conv_weight_bytes(ndim, cin, cout, ksize, DTYPES.get(dtype, dtype)))
 
@@ -339,7 +346,7 @@ def st_groupnorm_apply(y_plan: Plan, y_bufs, groups: int, z_bufs, workspace, str
 
 __all__ = [
     "lib", "LIB_PATH", "ShardConvError", "Plan", "ST_F32", "ST_BF16", "st_version",
-    "st_plan_shards", "st_halo_pack", "st_halo_unpack", "st_conv_weight_bytes",
+    "st_plan_shards", "st_halo_pack", "st_halo_unpack", "st_halo_exchange", "st_conv_weight_bytes",
     "st_conv_pack_weights", "st_conv_sharded", "st_groupnorm_workspace_bytes",
     "st_groupnorm_workspace_layout", "st_groupnorm_sharded", "st_groupnorm_partials",
     "st_groupnorm_combine", "st_groupnorm_apply",

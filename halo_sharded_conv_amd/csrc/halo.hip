@@ -6,7 +6,11 @@
 // convolution over the chunk sees the same neighbourhood as the unsharded
 // one.  With every shard in HBM the exchange is two bit-exact copies:
 // interior boxes -> contiguous message (pack), message -> neighbour margins
-// (unpack, plus zeros on the global faces).
+// (unpack, plus zeros on the global faces).  When sender and receiver share
+// one device the two fuse into one copy, interior -> neighbour margin, with
+// no message in between (exchange): half the bytes.  Boxes read only
+// interiors and write only margins, each margin cell by exactly one box, so
+// the boxes of one launch never touch each other's data.
 //
 // One launch covers every box.  Each box is a set of rows of contiguous
 // words (a W-run of cells times C channels); a block copies 1024 consecutive
@@ -37,8 +41,11 @@ __device__ __forceinline__ int find_box(const HaloDesc* d, int n, int64_t block)
   return lo;
 }
 
-// PACK: message <- sender interior.  !PACK: receiver margin <- message (or 0).
-template <int VEC, bool PACK>
+enum CopyMode { kPack, kUnpack, kExchange };
+
+// kPack: message <- sender interior.  kUnpack: receiver margin <- message (or
+// 0).  kExchange: receiver margin <- sender interior (or 0).
+template <int VEC, int MODE>
 __global__ __launch_bounds__(kHaloThreads) void halo_copy(const HaloDesc* __restrict__ descs,
                                                            int ndesc, ShardPtrs bufs,
                                                            char* __restrict__ msg) {
@@ -58,30 +65,36 @@ __global__ __launch_bounds__(kHaloThreads) void halo_copy(const HaloDesc* __rest
     const uint32_t r = row - n * (uint32_t)d.rows_dh;
     const uint32_t dd = r / (uint32_t)d.rows_h;
     const uint32_t hh = r - dd * (uint32_t)d.rows_h;
-    if (PACK) {
+    if (MODE == kPack) {
       const W* src = reinterpret_cast<const W*>(bufs.p[d.src]);
       const int64_t s = d.src_base + n * d.src_sn + dd * d.src_sd + hh * d.src_sh + col;
       reinterpret_cast<W*>(msg)[d.msg_base + u] = src[s];
     } else {
       W* dst = reinterpret_cast<W*>(bufs.p[d.dst]);
       const int64_t t = d.dst_base + n * d.dst_sn + dd * d.dst_sd + hh * d.dst_sh + col;
-      W v;
-      if (d.src >= 0) v = reinterpret_cast<const W*>(msg)[d.msg_base + u];
-      else v = W{};
+      W v = W{};
+      if (d.src >= 0) {
+        if (MODE == kUnpack) {
+          v = reinterpret_cast<const W*>(msg)[d.msg_base + u];
+        } else {
+          const W* src = reinterpret_cast<const W*>(bufs.p[d.src]);
+          v = src[d.src_base + n * d.src_sn + dd * d.src_sd + hh * d.src_sh + col];
+        }
+      }
       dst[t] = v;
     }
   }
 }
 
-template <bool PACK>
+template <int MODE>
 void launch(int vec, int64_t blocks, const HaloDesc* descs, int ndesc, const ShardPtrs& bufs,
             char* msg, hipStream_t stream) {
   const dim3 grid((unsigned)blocks), block(kHaloThreads);
   switch (vec) {
-    case 16: hipLaunchKernelGGL((halo_copy<16, PACK>), grid, block, 0, stream, descs, ndesc, bufs, msg); break;
-    case 8: hipLaunchKernelGGL((halo_copy<8, PACK>), grid, block, 0, stream, descs, ndesc, bufs, msg); break;
-    case 4: hipLaunchKernelGGL((halo_copy<4, PACK>), grid, block, 0, stream, descs, ndesc, bufs, msg); break;
-    default: hipLaunchKernelGGL((halo_copy<2, PACK>), grid, block, 0, stream, descs, ndesc, bufs, msg); break;
+    case 16: hipLaunchKernelGGL((halo_copy<16, MODE>), grid, block, 0, stream, descs, ndesc, bufs, msg); break;
+    case 8: hipLaunchKernelGGL((halo_copy<8, MODE>), grid, block, 0, stream, descs, ndesc, bufs, msg); break;
+    case 4: hipLaunchKernelGGL((halo_copy<4, MODE>), grid, block, 0, stream, descs, ndesc, bufs, msg); break;
+    default: hipLaunchKernelGGL((halo_copy<2, MODE>), grid, block, 0, stream, descs, ndesc, bufs, msg); break;
   }
 }
 
@@ -113,7 +126,7 @@ st_status st_halo_pack(st_plan* plan, const void* const* shard_bufs, void* msg, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   s = plan_device_table(plan, st);
   if (s != ST_OK) return s;
-  launch<true>(plan->vec, plan->blocks_real, plan->d_descs, (int)plan->n_real, bufs,
+  launch<kPack>(plan->vec, plan->blocks_real, plan->d_descs, (int)plan->n_real, bufs,
                static_cast<char*>(msg), st);
   return launch_check("st_halo_pack: launch");
 }
@@ -134,9 +147,34 @@ st_status st_halo_unpack(st_plan* plan, const void* msg, void* const* shard_bufs
   hipStream_t st = static_cast<hipStream_t>(stream);
   s = plan_device_table(plan, st);
   if (s != ST_OK) return s;
-  launch<false>(plan->vec, blocks, plan->d_descs, (int)nbox, bufs,
-                const_cast<char*>(static_cast<const char*>(msg)), st);
+  launch<kUnpack>(plan->vec, blocks, plan->d_descs, (int)nbox, bufs,
+                  const_cast<char*>(static_cast<const char*>(msg)), st);
   return launch_check("st_halo_unpack: launch");
+}
+
+st_status st_halo_exchange(st_plan* plan, void* const* shard_bufs, int32_t zero_global_margins, void* stream) {
+  if (!plan) return fail(ST_ERR_INVALID_ARG, "st_halo_exchange: NULL plan");
+  ShardPtrs bufs{};
+  st_status s = check_bufs(plan, reinterpret_cast<const void* const*>(shard_bufs), bufs, "st_halo_exchange");
+  if (s != ST_OK) return s;
+  // one launch reads some shards while writing others: their bytes must not
+  // overlap
+  const int64_t esz = plan->dtype == ST_F32 ? 4 : 2;
+  for (size_t i = 0; i < plan->shards.size(); ++i)
+    for (size_t j = i + 1; j < plan->shards.size(); ++j) {
+      const char *a = bufs.p[i], *b = bufs.p[j];
+      const int64_t na = plan->shards[i].elems * esz, nb = plan->shards[j].elems * esz;
+      if (a < b + nb && b < a + na)
+        return fail(ST_ERR_INVALID_ARG, "st_halo_exchange: shard buffers overlap");
+    }
+  const int64_t nbox = zero_global_margins ? plan->n_real + plan->n_zero : plan->n_real;
+  const int64_t blocks = zero_global_margins ? plan->blocks_all : plan->blocks_real;
+  if (nbox == 0) return ST_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  s = plan_device_table(plan, st);
+  if (s != ST_OK) return s;
+  launch<kExchange>(plan->vec, blocks, plan->d_descs, (int)nbox, bufs, nullptr, st);
+  return launch_check("st_halo_exchange: launch");
 }
 
 }  // extern "C"

@@ -16,7 +16,7 @@ import numpy as np
 from . import (ST_BF16, ST_F32, ShardConvError, st_conv_pack_weights, st_conv_sharded,
                st_conv_weight_bytes, st_groupnorm_apply, st_groupnorm_combine, st_groupnorm_partials,
                st_groupnorm_sharded, st_groupnorm_workspace_bytes, st_groupnorm_workspace_layout,
-               st_halo_pack, st_halo_unpack, st_plan_shards)
+               st_halo_exchange, st_halo_pack, st_halo_unpack, st_plan_shards)
 
 
 def _torch():
@@ -112,6 +112,9 @@ class ShardedConvGN:
     def exchange(self, zero_global_margins: bool = True, stream=None) -> None:
         st_halo_pack(self.in_plan, self.x_bufs, self.msg, stream)
         st_halo_unpack(self.in_plan, self.msg, self.x_bufs, zero_global_margins, stream)
+
+    def exchange_fused(self, zero_global_margins: bool = True, stream=None) -> None:
+        st_halo_exchange(self.in_plan, self.x_bufs, zero_global_margins, stream)
 
     def conv(self, stream=None) -> None:
         cfg = self.cfg

@@ -161,6 +161,20 @@ st_status st_halo_pack(st_plan* plan, const void* const* shard_bufs, void* msg, 
 st_status st_halo_unpack(st_plan* plan, const void* msg, void* const* shard_bufs,
                          int32_t zero_global_margins, void* stream);
 
+/*
+ * st_halo_exchange - st_halo_pack followed by st_halo_unpack, fused into one
+ * copy for shards that share one device: every sent box goes from the
+ * sender's interior straight into the receiver's margin, with no message
+ * buffer (half the bytes of the two-copy form).  Same section as
+ * st_halo_pack; the same bits land in every margin.
+ *   shard_bufs[num_shards]  padded shard buffers: interiors read, margins
+ *                            written (with zero_global_margins != 0 also the
+ *                            global-face margins, as zeros)
+ * Every shard buffer must be a distinct allocation (no two shards overlap).
+ */
+st_status st_halo_exchange(st_plan* plan, void* const* shard_bufs, int32_t zero_global_margins,
+                           void* stream);
+
 /* ------------------------------------------------------------------ conv */
 
 /*

@@ -111,6 +111,13 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert L.st_halo_pack(p.handle, aligned, ctypes.c_void_p(0x30008), s) == ALIGN
     assert L.st_halo_unpack(p.handle, None, aligned, 1, s) == INVALID
     assert L.st_halo_unpack(p.handle, ctypes.c_void_p(0x30008), aligned, 1, s) == ALIGN
+    assert L.st_halo_exchange(None, aligned, 1, s) == INVALID
+    assert L.st_halo_exchange(p.handle, None, 1, s) == INVALID
+    assert L.st_halo_exchange(p.handle, nulls, 1, s) == INVALID
+    assert L.st_halo_exchange(p.handle, misaligned, 1, s) == ALIGN
+    overlapping = PP(0x10000, 0x10010)   # padded shards are 6 x 10 x 8 bf16 = 960 bytes
+    assert L.st_halo_exchange(p.handle, overlapping, 1, s) == INVALID
+    assert "overlap" in hsc.lib.st_last_error().decode()
     # conv
     w = ctypes.c_void_p(0x40000)
     assert L.st_conv_sharded(p.handle, aligned, w, None, 16, 2, q.handle, aligned, None, 1, s) == UNSUPPORTED

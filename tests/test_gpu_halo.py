@@ -1,10 +1,12 @@
-"""Halo pack/unpack on the GPU: bit-exact against the oracle.
+"""Halo pack/unpack (and the fused exchange) on the GPU: bit-exact against
+the oracle.
 
 Shard interiors hold arbitrary bit patterns (NaN payloads, -0.0, subnormals,
 infinities); margins start as garbage.  After pack the message must equal the
 oracle's message byte for byte; after unpack every padded shard must equal
 the oracle's padded shard (neighbour cells in the margins, zeros on global
-faces) byte for byte.
+faces) byte for byte.  The fused exchange (no message) must leave the same
+bytes in every padded shard.
 """
 import numpy as np
 import pytest
@@ -31,7 +33,7 @@ def special_bits(n, dtype, rng):
     return bits
 
 
-def run_case(shards, h, C, dtype, N=1, seed=0, zero=True):
+def run_case(shards, h, C, dtype, N=1, seed=0, zero=True, fused=False):
     d = len(shards)
     spatial = [sum(s) for s in shards]
     rng = np.random.default_rng(seed)
@@ -49,19 +51,23 @@ def run_case(shards, h, C, dtype, N=1, seed=0, zero=True):
         dst = tuple([slice(None)] + [slice(h, h + e) for e in inf["extent"]])
         v[dst] = torch.from_numpy(np.ascontiguousarray(x[src]).view(sdt)).cuda()
         bufs.append(b)
-    msg = torch.full((max(16, plan.msg_bytes),), 0xAB, dtype=torch.uint8, device="cuda")
-    hsc.st_halo_pack(plan, bufs, msg)
-    torch.cuda.synchronize()
-    want = np.frombuffer(oracle.halo_message(x, shards, h), np.uint8)
-    got = msg.cpu().numpy()[:plan.msg_bytes]
-    # gaps between boxes are untouched by pack: compare box bytes only
-    for i in range(plan.num_halo_boxes):
-        b = plan.halo_box(i)
-        n = N * int(np.prod(b["ext"])) * C * (4 if dtype == "f32" else 2)
-        o = b["msg_offset"]
-        assert np.array_equal(got[o:o + n], want[o:o + n]), f"message box {i} differs"
-    hsc.st_halo_unpack(plan, msg, bufs, zero)
-    torch.cuda.synchronize()
+    if fused:
+        hsc.st_halo_exchange(plan, bufs, zero)
+        torch.cuda.synchronize()
+    else:
+        msg = torch.full((max(16, plan.msg_bytes),), 0xAB, dtype=torch.uint8, device="cuda")
+        hsc.st_halo_pack(plan, bufs, msg)
+        torch.cuda.synchronize()
+        want = np.frombuffer(oracle.halo_message(x, shards, h), np.uint8)
+        got = msg.cpu().numpy()[:plan.msg_bytes]
+        # gaps between boxes are untouched by pack: compare box bytes only
+        for i in range(plan.num_halo_boxes):
+            b = plan.halo_box(i)
+            n = N * int(np.prod(b["ext"])) * C * (4 if dtype == "f32" else 2)
+            o = b["msg_offset"]
+            assert np.array_equal(got[o:o + n], want[o:o + n]), f"message box {i} differs"
+        hsc.st_halo_unpack(plan, msg, bufs, zero)
+        torch.cuda.synchronize()
     for i, idx in enumerate(oracle.shard_grid(shards)):
         ref = oracle.padded_shard(x, shards, idx, h)
         got = bufs[i].cpu().numpy().view(npdt).reshape(ref.shape)
@@ -109,3 +115,24 @@ def test_halo_full_size(name):
     wl = synth.workload(name)
     say(f"full-size halo {name}")
     run_case([list(s) for s in wl.shards], wl.halo, wl.cin, wl.dtype, 1, seed=7)
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_fused_exchange_bit_exact(case):
+    shards, h, C, dtype, N = CASES[case]
+    say(f"fused exchange case {case}: shards={shards} h={h} C={C} {dtype} N={N}")
+    run_case(shards, h, C, dtype, N, seed=200 + case, fused=True)
+
+
+@pytest.mark.parametrize("case", [1, 2, 3])
+def test_fused_exchange_without_zero_fill_keeps_global_margins(case):
+    shards, h, C, dtype, N = CASES[case]
+    say(f"fused exchange no-zero case {case}")
+    run_case(shards, h, C, dtype, N, seed=300 + case, zero=False, fused=True)
+
+
+def test_fused_exchange_full_size():
+    """The 2x2x2 grid (faces, edges and corners) at full size."""
+    wl = synth.workload("vol256_c32_k3_bf16")
+    say("full-size fused exchange vol256_c32_k3_bf16")
+    run_case([list(s) for s in wl.shards], wl.halo, wl.cin, wl.dtype, 1, seed=8, fused=True)
