@@ -100,6 +100,39 @@ def conv_same(x: np.ndarray, w: np.ndarray, bias=None) -> np.ndarray:
     return conv_valid(zero_pad(x, (k - 1) // 2), w, bias)
 
 
+def conv_same_dgrad(dy: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Gradient of conv_same with respect to its input (its adjoint).
+
+    The backward pass that training at native resolution needs ("Technical
+    summary: ShardTensor", section 1 "Problem statement": training and
+    inference on high-resolution data; section 4 "Results and benchmarks":
+    ViT training at 2048^2, the StormScope training run):
+    from y[n, i, o] = sum_t sum_c w[o, c, t] * x[n, i + t - p, c],
+        dx[n, j, c] = sum_t sum_o w[o, c, t] * dy[n, j - t + p, o],
+    with dy taken as zero outside the grid.  dy: [N, *S, Cout] fp64, w:
+    [Cout, Cin, k, .., k] fp64; returns [N, *S, Cin] fp64.  One tap at a time,
+    lexicographic, each a plain matrix product over output channels.
+    """
+    d = dy.ndim - 2
+    cout, cin = w.shape[:2]
+    k = w.shape[2]
+    if k % 2 != 1:
+        raise ValueError("odd kernels only")
+    if dy.shape[-1] != cout:
+        raise ValueError("channel mismatch")
+    p = (k - 1) // 2
+    S = dy.shape[1:1 + d]
+    dyp = zero_pad(dy, p)                       # dyp[m] = dy[m - p]
+    dx = np.zeros((dy.shape[0], *S, cin), dtype=np.float64)
+    for t in _taps(k, d):
+        # dy[j - t + p] = dyp[j - t + 2p]: the window starting at 2p - t
+        window = dyp[(slice(None),) + tuple(slice(2 * p - t[a], 2 * p - t[a] + S[a]) for a in range(d))]
+        rows = np.ascontiguousarray(window).reshape(-1, cout)
+        wt = np.ascontiguousarray(w[(slice(None), slice(None)) + t])      # [Cout, Cin]
+        dx += (rows @ wt).reshape(dx.shape)
+    return dx
+
+
 def conv_same_slabbed(x_src, dtype: str, w: np.ndarray, bias=None, slab: int = 8):
     """conv_same evaluated one slab of the outermost spatial axis at a time.
 
@@ -332,6 +365,30 @@ def conv_bruteforce(x, w, bias=None):
                         acc += w[(o, c) + t] * x[(n, *src, c)]
                 y[(n, *pos, o)] = acc
     return y
+
+
+def conv_dgrad_bruteforce(dy, w):
+    """Scalar-loop input gradient of the 'same' cross-correlation (tiny inputs):
+    every output position scatters w[o, c, t] * dy[o] onto the input position
+    it read, exactly as the forward definition pairs them."""
+    dy = np.asarray(dy, np.float64)
+    w = np.asarray(w, np.float64)
+    n_, *spatial, cout = dy.shape
+    d = len(spatial)
+    cin, k = w.shape[1], w.shape[2]
+    p = (k - 1) // 2
+    dx = np.zeros((n_, *spatial, cin))
+    for n in range(n_):
+        for pos in itertools.product(*[range(s) for s in spatial]):
+            for t in itertools.product(range(k), repeat=d):
+                src = [pos[a] + t[a] - p for a in range(d)]
+                if any(src[a] < 0 or src[a] >= spatial[a] for a in range(d)):
+                    continue
+                for o in range(cout):
+                    g = dy[(n, *pos, o)]
+                    for c in range(cin):
+                        dx[(n, *src, c)] += w[(o, c) + t] * g
+    return dx
 
 
 def group_norm_bruteforce(y, groups, eps, gamma=None, beta=None):

@@ -159,7 +159,54 @@ def pin_sharded(conv, gn):
     return bool(ok)
 
 
+def pin_dgrad(dgrad, conv=oracle.conv_same):
+    """The input gradient against what fixes it independently: the adjoint
+    identity <conv(x), dy> = <x, dgrad(dy)> (every x and dy), scalar-loop
+    brute force on tiny volumes, and torch's fp64 autograd."""
+    ok = True
+    for d, k in [(2, 3), (2, 5), (3, 3), (3, 5)]:
+        r = rng(500 + 10 * d + k)
+        spatial = (5, 6, 7) if d == 3 else (9, 11)
+        x = r.standard_normal((2, *spatial, 3))
+        dy = r.standard_normal((2, *spatial, 4))
+        w = r.uniform(-1, 1, size=(4, 3) + (k,) * d)
+        y = conv(x, w)
+        lhs = float(np.sum(y * dy))
+        rhs = float(np.sum(x * dgrad(dy, w)))
+        ok &= abs(lhs - rhs) <= 1e-13 * float(np.sum(np.abs(y * dy)))   # rounding of the two sums only
+        small = (3, 4, 4) if d == 3 else (5, 6)
+        dys = r.standard_normal((1, *small, 4))
+        ok &= rel(dgrad(dys, w), oracle.conv_dgrad_bruteforce(dys, w)) <= 1e-13
+        xt = torch.from_numpy(np.moveaxis(x, -1, 1).copy()).requires_grad_(True)
+        f = torch.nn.functional.conv3d if d == 3 else torch.nn.functional.conv2d
+        yt = f(xt, torch.from_numpy(w), padding=k // 2)
+        yt.backward(torch.from_numpy(np.moveaxis(dy, -1, 1).copy()))
+        ok &= rel(dgrad(dy, w), np.moveaxis(xt.grad.numpy(), 1, -1)) <= 1e-12
+    return bool(ok)
+
+
 # ------------------------------------------------------------------- the pins
+
+def test_dgrad_pins():
+    assert pin_dgrad(oracle.conv_same_dgrad)
+
+
+@pytest.mark.parametrize("name", ["unflipped taps", "untransposed channels", "shift off by one"])
+def test_dgrad_pins_catch_mutants(name):
+    def unflipped(dy, w):
+        return oracle.conv_same(dy, np.swapaxes(w, 0, 1).copy())
+
+    def untransposed(dy, w):
+        if w.shape[0] == w.shape[1]:
+            return oracle.conv_same(dy, np.flip(w, axis=tuple(range(2, w.ndim))).copy())
+        return oracle.conv_same_dgrad(dy, w) * (1 + 1e-9)
+
+    def shifted(dy, w):
+        return np.roll(oracle.conv_same_dgrad(dy, w), 1, axis=1)
+
+    mutant = {"unflipped taps": unflipped, "untransposed channels": untransposed,
+              "shift off by one": shifted}[name]
+    assert not pin_dgrad(mutant), f"no pin caught the dgrad mutant '{name}'"
 
 def test_bruteforce():
     assert pin_bruteforce(oracle.conv_same, oracle.group_norm)
