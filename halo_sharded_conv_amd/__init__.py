@@ -90,6 +90,7 @@ def _load() -> ctypes.CDLL:
         "st_halo_exchange": (I32, [P, PP, I32, P]),
         "st_conv_weight_bytes": (SZ, [I32, I32, I32, I32, I32]),
         "st_conv_pack_weights": (I32, [I32, I32, I32, I32, I32, P, P, P]),
+        "st_conv_dgrad_weights": (I32, [I32, I32, I32, I32, I32, P, P, P]),
         "st_conv_sharded": (I32, [P, PP, P, P, I32, I32, P, PP, P, I32, P]),
         "st_groupnorm_workspace_bytes": (SZ, [P, I32]),
         "st_groupnorm_workspace_layout": (I32, [P, I32, ctypes.POINTER(_GnLayout)]),
@@ -275,6 +276,16 @@ def st_conv_pack_weights(ndim: int, cin: int, cout: int, ksize: int, dtype, weig
                                     _stream(stream)), "st_conv_pack_weights")
 
 
+def st_conv_dgrad_weights(ndim: int, cin: int, cout: int, ksize: int, dtype, weight, out,
+                          stream=None) -> None:
+    dt = DTYPES.get(dtype, dtype)
+    raw = cout * cin * ksize ** ndim * ESIZE[dt]
+    _check(lib.st_conv_dgrad_weights(ndim, cin, cout, ksize, dt,
+                                     ctypes.c_void_p(_dev_ptr(weight, "weight", raw)),
+                                     ctypes.c_void_p(_dev_ptr(out, "dgrad weight", raw)),
+                                     _stream(stream)), "st_conv_dgrad_weights")
+
+
 def st_conv_sharded(in_plan: Plan, in_bufs, packed_weight, bias, cout: int, ksize: int,
                     out_plan: Plan, y_bufs, ymax=None, groups: int = 1, stream=None) -> None:
     ins = _ptr_array(in_bufs, "st_conv_sharded input", _shard_bytes(in_plan))
@@ -346,7 +357,7 @@ def st_groupnorm_apply(y_plan: Plan, y_bufs, groups: int, z_bufs, workspace, str
 
 __all__ = [
     "lib", "LIB_PATH", "ShardConvError", "Plan", "ST_F32", "ST_BF16", "st_version",
-    "st_plan_shards", "st_halo_pack", "st_halo_unpack", "st_halo_exchange", "st_conv_weight_bytes",
+    "st_plan_shards", "st_halo_pack", "st_halo_unpack", "st_halo_exchange", "st_conv_weight_bytes", "st_conv_dgrad_weights",
     "st_conv_pack_weights", "st_conv_sharded", "st_groupnorm_workspace_bytes",
     "st_groupnorm_workspace_layout", "st_groupnorm_sharded", "st_groupnorm_partials",
     "st_groupnorm_combine", "st_groupnorm_apply",

@@ -242,6 +242,20 @@ __global__ void pack_w_pairs(const uint16_t* __restrict__ w, uint16_t* __restric
 }
 
 // [Cout][Cin][taps] -> [Cout][taps][Cin]
+// Input gradient: the convolution that maps dy (Cout channels) to dx (Cin
+// channels) has weights w'[c][o][t] = w[o][c][flip(t)], every tap axis
+// reversed; for taps in lexicographic order flip(t) = taps - 1 - t.
+template <typename T>
+__global__ void dgrad_weights(const T* __restrict__ w, T* __restrict__ out, int cin, int cout, int taps,
+                              int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int t = (int)(i % taps);
+  const int64_t co = i / taps;
+  const int o = (int)(co % cout), c = (int)(co / cout);
+  out[i] = w[((int64_t)o * cin + c) * taps + (taps - 1 - t)];
+}
+
 template <typename T>
 __global__ void pack_w_direct(const T* __restrict__ w, T* __restrict__ out, int cin, int cout,
                               int taps, int64_t total) {
@@ -1743,6 +1757,26 @@ st_status st_conv_pack_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t 
   hipLaunchKernelGGL(pack_w_direct<float>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
                      static_cast<const float*>(weight), static_cast<float*>(packed), cin, cout, taps, total);
   return launch_check("st_conv_pack_weights: launch");
+}
+
+st_status st_conv_dgrad_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t ksize, st_dtype dtype,
+                                const void* weight, void* out, void* stream) {
+  if ((ndim != 2 && ndim != 3) || cin < 1 || cout < 1 || ksize < 1 || ksize % 2 == 0)
+    return fail(ST_ERR_UNSUPPORTED, "st_conv_dgrad_weights: unsupported ndim/ksize");
+  if (dtype != ST_F32 && dtype != ST_BF16) return fail(ST_ERR_UNSUPPORTED, "st_conv_dgrad_weights: dtype");
+  if (!weight || !out) return fail(ST_ERR_INVALID_ARG, "st_conv_dgrad_weights: NULL pointer");
+  if (weight == out) return fail(ST_ERR_INVALID_ARG, "st_conv_dgrad_weights: in place is not supported");
+  const int taps = (int)taps_of(ndim, ksize);
+  const int64_t total = (int64_t)cout * cin * taps;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 gd((unsigned)((total + 255) / 256)), bd(256);
+  if (dtype == ST_BF16)
+    hipLaunchKernelGGL(dgrad_weights<uint16_t>, gd, bd, 0, st, static_cast<const uint16_t*>(weight),
+                       static_cast<uint16_t*>(out), cin, cout, taps, total);
+  else
+    hipLaunchKernelGGL(dgrad_weights<float>, gd, bd, 0, st, static_cast<const float*>(weight),
+                       static_cast<float*>(out), cin, cout, taps, total);
+  return launch_check("st_conv_dgrad_weights: launch");
 }
 
 st_status st_conv_sharded(const st_plan* in_plan, const void* const* in_bufs,

@@ -8,12 +8,13 @@ outside the library's kernels.
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 from typing import Optional, Sequence
 
 import numpy as np
 
-from . import (ST_BF16, ST_F32, ShardConvError, st_conv_pack_weights, st_conv_sharded,
+from . import (ST_BF16, ST_F32, ShardConvError, st_conv_dgrad_weights, st_conv_pack_weights, st_conv_sharded,
                st_conv_weight_bytes, st_groupnorm_apply, st_groupnorm_combine, st_groupnorm_partials,
                st_groupnorm_sharded, st_groupnorm_workspace_bytes, st_groupnorm_workspace_layout,
                st_halo_exchange, st_halo_pack, st_halo_unpack, st_plan_shards)
@@ -77,6 +78,20 @@ class ShardedConvGN:
         st_conv_pack_weights(cfg.ndim, cfg.cin, cfg.cout, cfg.ksize, self.dtype, raw, self.w_packed)
         self.bias = None if bias is None else self._host_to_dev(np.asarray(bias, np.float32))
         _torch().cuda.synchronize()
+
+    def set_weight_dgrad(self, w_forward: np.ndarray) -> None:
+        """For a layer built from dgrad_config(forward_cfg): its conv becomes the
+        input gradient of the forward conv.  w_forward: the forward weights
+        [Cout, Cin, k..] (Cout = this layer's cin); they are transposed and
+        flipped on the device, then packed."""
+        cfg = self.cfg
+        torch = _torch()
+        raw = self._host_to_dev(w_forward.reshape(-1))
+        wt = torch.empty_like(raw)
+        st_conv_dgrad_weights(cfg.ndim, cfg.cout, cfg.cin, cfg.ksize, self.dtype, raw, wt)
+        st_conv_pack_weights(cfg.ndim, cfg.cin, cfg.cout, cfg.ksize, self.dtype, wt, self.w_packed)
+        self.bias = None
+        torch.cuda.synchronize()
 
     def set_affine(self, gamma: Optional[np.ndarray], beta: Optional[np.ndarray]) -> None:
         self.gamma = None if gamma is None else self._host_to_dev(np.asarray(gamma, np.float32))
@@ -192,3 +207,10 @@ class ShardedConvGN:
     def padded_host(self, i: int) -> np.ndarray:
         v = self.padded_view(i).cpu().numpy()
         return v.view(np.uint16) if self.dtype == ST_BF16 else v
+
+
+def dgrad_config(cfg):
+    """The layer whose conv is the input gradient of cfg's conv: it reads dy
+    (cfg.cout channels, the same shards and halo; exchanged like x) and writes
+    dx (cfg.cin channels).  Its GroupNorm part is not used."""
+    return dataclasses.replace(cfg, name=f"{cfg.name}_dgrad", cin=cfg.cout, cout=cfg.cin, groups=1)

@@ -187,6 +187,24 @@ st_status st_conv_pack_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t 
                                st_dtype dtype, const void* weight, void* packed, void* stream);
 
 /*
+ * st_conv_dgrad_weights - the weights of the input-gradient convolution.
+ * Training at native resolution needs the backward pass ("Technical
+ * summary: ShardTensor", section 1 "Problem statement"; section 4 "Results
+ * and benchmarks", the ViT and StormScope training runs).  For the 'same',
+ * stride-1 cross-correlation y = conv(x, w), the gradient with respect to x is
+ * dx = conv(dy, w') with w'[c][o][t] = w[o][c][flip(t)] (channels swapped,
+ * every tap axis reversed), so the sharded input gradient is: exchange the
+ * halos of dy, then st_conv_sharded with cin' = Cout, cout' = Cin and w'
+ * packed by st_conv_pack_weights.
+ *   weight   [Cout][Cin][k]^ndim in `dtype` (read)
+ *   out      [Cin][Cout][k]^ndim in `dtype` (written; must not alias weight)
+ * Pure bit permutation.  Errors: ST_ERR_UNSUPPORTED (ndim, even k, dtype),
+ * ST_ERR_INVALID_ARG (NULL or aliased pointers).
+ */
+st_status st_conv_dgrad_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t ksize, st_dtype dtype,
+                                const void* weight, void* out, void* stream);
+
+/*
  * st_conv_sharded - per-shard convolution on the halo-padded chunks.
  * Section 2, "Implementation details", "Communication": with the halo in
  * place every shard's output equals the matching slice of the unsharded

@@ -138,6 +138,12 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert L.st_conv_pack_weights(2, 8, 16, 4, 1, w, w, s) == UNSUPPORTED
     assert L.st_conv_pack_weights(2, 8, 16, 3, 1, None, w, s) == INVALID
     assert L.st_conv_pack_weights(2, 8, 16, 3, 1, ctypes.c_void_p(0x40002), w, s) == ALIGN
+    w2 = ctypes.c_void_p(0x48000)
+    assert L.st_conv_dgrad_weights(4, 8, 16, 3, 1, w, w2, s) == UNSUPPORTED
+    assert L.st_conv_dgrad_weights(2, 8, 16, 2, 1, w, w2, s) == UNSUPPORTED
+    assert L.st_conv_dgrad_weights(2, 8, 16, 3, 9, w, w2, s) == UNSUPPORTED
+    assert L.st_conv_dgrad_weights(2, 8, 16, 3, 1, None, w2, s) == INVALID
+    assert L.st_conv_dgrad_weights(2, 8, 16, 3, 1, w, w, s) == INVALID
     # groupnorm
     need = L.st_groupnorm_workspace_bytes(q.handle, 4)
     assert need > 0
