@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sharded conv+GroupNorm voxels/s on 1 MI355X; % MFMA peak (conv), % HBM BW (halo/norm)"
+METRIC_DGRAD = "sharded conv input-gradient (halo exchange of dy + conv) voxels/s on 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 (256 CU x 2.4 GHz x 4096 flop/clk)
 FP32_PEAK_TFLOPS = 157.3
@@ -33,6 +34,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--pass", dest="pass_", choices=("forward", "dgrad"), default="forward",
+                    help="the layer's forward step, or the input gradient of its conv")
     ap.add_argument("--exchange", choices=("pack+unpack", "fused"), default="pack+unpack",
                     help="halo exchange as two copies through a message buffer, or one fused copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -170,8 +173,10 @@ def algorithmic(wl, layer):
     }
 
 
-def cpu_baseline(wl, rows):
-    """The oracle (fp64 numpy) on the first `rows` rows of the outermost axis."""
+def cpu_baseline(wl, rows, w_fwd=None):
+    """The oracle (fp64 numpy) on the first `rows` rows of the outermost axis:
+    conv + GroupNorm, or (w_fwd given: wl is the input-gradient layer) the
+    input gradient of the forward conv."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -181,15 +186,22 @@ def cpu_baseline(wl, rows):
     sub_shape = (rows,) + tuple(wl.spatial[1:])
     sub = synth.small_variant(wl, sub_shape, [(s,) for s in sub_shape], name_suffix="cpu_sample")
     x = synth.make_input(sub)
-    w = oracle.widen(synth.make_weight(wl), wl.dtype)
     t0 = time.perf_counter()
-    y = oracle.conv_same(oracle.widen(x, wl.dtype), w)
-    z = oracle.group_norm(y, wl.groups, wl.eps)
+    if w_fwd is None:
+        w = oracle.widen(synth.make_weight(wl), wl.dtype)
+        t0 = time.perf_counter()
+        y = oracle.conv_same(oracle.widen(x, wl.dtype), w)
+        z = oracle.group_norm(y, wl.groups, wl.eps)
+    else:
+        w = oracle.widen(w_fwd, wl.dtype)
+        t0 = time.perf_counter()
+        z = oracle.conv_same_dgrad(oracle.widen(x, wl.dtype), w)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": sub.voxels / dt, "unit": "voxels/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {rows} rows of the outermost axis ({sub.voxels} voxels, conv + GroupNorm in fp64 "
-                      f"numpy, {dt:.1f} s)", "seconds": round(dt, 2), "checksum": float(np.abs(z).sum())}
+            "sample": f"first {rows} rows of the outermost axis ({sub.voxels} voxels, "
+                      + ("conv + GroupNorm" if w_fwd is None else "input gradient of the conv")
+                      + f" in fp64 numpy, {dt:.1f} s)", "seconds": round(dt, 2), "checksum": float(np.abs(z).sum())}
 
 
 def main():
@@ -211,9 +223,17 @@ def main():
     from halo_sharded_conv_amd.layer import ShardedConvGN
 
     name = args.workload or synth.BENCH_WORKLOAD
-    wl = synth.workload(name)
-    layer = ShardedConvGN(wl)
-    layer.set_weight(synth.make_weight(wl))
+    wl_fwd = synth.workload(name)
+    if args.pass_ == "dgrad":
+        # input gradient of the layer's conv: dy (Cout channels) -> dx (Cin)
+        from halo_sharded_conv_amd.layer import dgrad_config
+        wl = dgrad_config(wl_fwd)
+        layer = ShardedConvGN(wl)
+        layer.set_weight_dgrad(synth.make_weight(wl_fwd))
+    else:
+        wl = wl_fwd
+        layer = ShardedConvGN(wl)
+        layer.set_weight(synth.make_weight(wl))
     layer.load_input(synth.make_input(wl))
     stream = torch.cuda.current_stream()
 
@@ -221,8 +241,10 @@ def main():
         halo = [("halo_exchange", lambda: layer.exchange_fused())]
     else:
         halo = [("halo_pack", lambda: layer.exchange_pack()), ("halo_unpack", lambda: layer.exchange_unpack())]
-    stages = halo + [("conv", layer.conv), ("gn_partials", layer.norm_partials), ("gn_combine", layer.norm_combine),
-              ("gn_apply", layer.norm_apply)]
+    stages = halo + [("conv", layer.conv)]
+    if args.pass_ == "forward":
+        stages += [("gn_partials", layer.norm_partials), ("gn_combine", layer.norm_combine),
+                   ("gn_apply", layer.norm_apply)]
 
     for _ in range(args.warmup):
         for _, fn in stages:
@@ -279,7 +301,7 @@ def main():
     roof["traffic"] = load_traffic(wl, dom)
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.pass_ == "forward" else METRIC_DGRAD,
         "value": wl.voxels / (ms_per_step * 1e-3),
         "unit": "voxels/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -289,14 +311,14 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "shape": [wl.batch, wl.cin, *wl.spatial], "cout": wl.cout,
-                   "kernel": wl.ksize, "shards": [list(s) for s in wl.shards], "halo": wl.halo, "exchange": args.exchange,
+                   "kernel": wl.ksize, "shards": [list(s) for s in wl.shards], "halo": wl.halo, "exchange": args.exchange, "pass": args.pass_,
                    "groups": wl.groups, "accumulate": "f32", "outputs": "f32"},
         "roofline": roof,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         rows = args.cpu_rows or max(1, min(wl.spatial[0], int(5.0e5 // (wl.voxels // wl.spatial[0]) + 1)))
-        out["cpu_baseline"] = cpu_baseline(wl, rows)
+        out["cpu_baseline"] = cpu_baseline(wl, rows, None if args.pass_ == "forward" else synth.make_weight(wl_fwd))
     print(json.dumps(out), flush=True)
 
 
