@@ -9,11 +9,12 @@ Python binding; the only code both sides use is the seeded input module
 Every function is pinned by CPU tests (brute force on tiny volumes, delta
 kernels, linearity, torch fp64 as an independent library, GroupNorm closed
 forms, sharded == unsharded; the input gradient by the adjoint identity,
-brute force and torch's fp64 autograd).  Nothing here is "parity unpinned".
+brute force and torch's fp64 autograd; the GroupNorm backward by torch's
+fp64 autograd and central finite differences).  Nothing here is "parity unpinned".
 """
 from .reference import (  # noqa: F401
     widen, zero_pad, conv_valid, conv_same, conv_same_dgrad, conv_same_slabbed, conv_at,
-    group_moments, group_norm, group_norm_apply, group_sums_onepass,
+    group_moments, group_norm, group_norm_apply, group_norm_backward, group_sums_onepass,
     shard_offsets, shard_grid, padded_shard, halo_message, halo_directions,
     sharded_forward, conv_bruteforce, conv_dgrad_bruteforce, group_norm_bruteforce,
 )

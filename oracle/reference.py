@@ -235,6 +235,38 @@ def group_norm(y: np.ndarray, groups: int, eps: float, gamma=None, beta=None) ->
     return group_norm_apply(y, groups, mean, var, eps, gamma, beta)
 
 
+def group_norm_backward(y: np.ndarray, dz: np.ndarray, groups: int, eps: float, gamma=None):
+    """Gradients of z = group_norm(y, groups, eps, gamma, beta) for an upstream
+    gradient dz: (dy, dgamma, dbeta).
+
+    The backward pass that training at native resolution needs ("Technical
+    summary: ShardTensor", section 1 "Problem statement"; section 4 "Results
+    and benchmarks", the training runs), for the GroupNorm read of the
+    forward pass.  Per (n, g), with M elements, mean mu, biased variance var,
+    r = 1 / sqrt(var + eps), yhat = (y - mu) * r and g = gamma_c * dz:
+        dy     = r * (g - mean_g(g) - yhat * mean_g(g * yhat))
+        dgamma = sum over n and positions of dz * yhat      (per channel)
+        dbeta  = sum over n and positions of dz             (per channel)
+    y, dz: [N, *S, C] fp64; returns dy [N, *S, C], dgamma [C], dbeta [C].
+    """
+    y = np.asarray(y, np.float64)
+    dz = np.asarray(dz, np.float64)
+    c = y.shape[-1]
+    gamma = np.ones(c) if gamma is None else np.asarray(gamma, np.float64)
+    mean, var = group_moments(y, groups)
+    r = 1.0 / np.sqrt(var + eps)                                # [N, G]
+    yg = _grouped(y, groups)                                    # [N, P, G, C/G]
+    dzg = _grouped(dz, groups)
+    yhat = (yg - mean[:, None, :, None]) * r[:, None, :, None]
+    gg = dzg * gamma.reshape(groups, c // groups)
+    m1 = gg.mean(axis=(1, 3))                                   # mean_g(g)
+    m2 = (gg * yhat).mean(axis=(1, 3))                          # mean_g(g * yhat)
+    dy = r[:, None, :, None] * (gg - m1[:, None, :, None] - yhat * m2[:, None, :, None])
+    dgamma = (dzg * yhat).sum(axis=(0, 1)).reshape(c)
+    dbeta = dzg.sum(axis=(0, 1)).reshape(c)
+    return dy.reshape(y.shape), dgamma, dbeta
+
+
 # ----------------------------------------------------------------------------
 # sharding shapes and halos (the method's data movement, stated on arrays)
 # ----------------------------------------------------------------------------

@@ -185,7 +185,73 @@ def pin_dgrad(dgrad, conv=oracle.conv_same):
     return bool(ok)
 
 
+def pin_gn_backward(gnb, gn=oracle.group_norm):
+    """GroupNorm backward against torch's fp64 autograd and central finite
+    differences of the loss <group_norm(y), dz> (independent of the formula)."""
+    ok = True
+    for shape, groups in [((2, 5, 6, 8), 4), ((1, 3, 4, 5, 6), 2), ((2, 7, 4), 1)]:
+        r = rng(700 + len(shape) + groups)
+        y = r.standard_normal(shape) * 1.5 + 0.3
+        dz = r.standard_normal(shape)
+        c = shape[-1]
+        gamma, beta = r.uniform(0.5, 1.5, c), r.uniform(-1, 1, c)
+        dy, dg, db = gnb(y, dz, groups, 1e-5, gamma)
+        yt = torch.from_numpy(np.moveaxis(y, -1, 1).copy()).requires_grad_(True)
+        gt = torch.from_numpy(gamma.copy()).requires_grad_(True)
+        bt = torch.from_numpy(beta.copy()).requires_grad_(True)
+        zt = torch.nn.functional.group_norm(yt, groups, gt, bt, eps=1e-5)
+        zt.backward(torch.from_numpy(np.moveaxis(dz, -1, 1).copy()))
+        ok &= rel(dy, np.moveaxis(yt.grad.numpy(), 1, -1)) <= 1e-11
+        ok &= rel(dg, gt.grad.numpy()) <= 1e-11 and rel(db, bt.grad.numpy()) <= 1e-11
+        # finite differences of L(y) = <gn(y), dz> at a few coordinates
+        for k in range(4):
+            idx = tuple(int(r.integers(0, s_)) for s_ in shape)
+            h = 1e-5
+            yp, ym = y.copy(), y.copy()
+            yp[idx] += h
+            ym[idx] -= h
+            fd = (np.sum(gn(yp, groups, 1e-5, gamma, beta) * dz) - np.sum(gn(ym, groups, 1e-5, gamma, beta) * dz)) / (2 * h)
+            ok &= abs(fd - dy[idx]) <= 1e-6 * max(1.0, abs(dy[idx]))
+    return bool(ok)
+
+
 # ------------------------------------------------------------------- the pins
+
+def test_gn_backward_pins():
+    assert pin_gn_backward(oracle.group_norm_backward)
+
+
+@pytest.mark.parametrize("name", ["mean term dropped", "yhat term dropped", "gamma ignored", "unbiased variance"])
+def test_gn_backward_pins_catch_mutants(name):
+    def no_mean(y, dz, g, eps, gamma=None):
+        dy, dg, db = oracle.group_norm_backward(y, dz, g, eps, gamma)
+        yg = dz.reshape(dz.shape[0], -1, g, dz.shape[-1] // g) * (1 if gamma is None else gamma).reshape(g, -1)
+        m1 = yg.mean(axis=(1, 3))
+        mean, var = oracle.group_moments(y, g)
+        r = 1.0 / np.sqrt(var + eps)
+        add = np.repeat(r * m1, dz.shape[-1] // g, axis=-1).reshape((dz.shape[0],) + (1,) * (dz.ndim - 2) + (-1,))
+        return dy + add, dg, db
+
+    def no_yhat(y, dz, g, eps, gamma=None):
+        mean, var = oracle.group_moments(y, g)
+        r = 1.0 / np.sqrt(var + eps)
+        c = dz.shape[-1]
+        gm = dz * (1 if gamma is None else gamma)
+        gg = gm.reshape(dz.shape[0], -1, g, c // g)
+        dy = r[:, None, :, None] * (gg - gg.mean(axis=(1, 3))[:, None, :, None])
+        _, dg, db = oracle.group_norm_backward(y, dz, g, eps, gamma)
+        return dy.reshape(dz.shape), dg, db
+
+    def no_gamma(y, dz, g, eps, gamma=None):
+        return oracle.group_norm_backward(y, dz, g, eps, None)
+
+    def unbiased(y, dz, g, eps, gamma=None):
+        m = y.size // (y.shape[0] * g)
+        return oracle.group_norm_backward(y * np.sqrt(m / (m - 1)), dz, g, eps, gamma)
+
+    mutant = {"mean term dropped": no_mean, "yhat term dropped": no_yhat, "gamma ignored": no_gamma,
+              "unbiased variance": unbiased}[name]
+    assert not pin_gn_backward(mutant), f"no pin caught the GroupNorm-backward mutant '{name}'"
 
 def test_dgrad_pins():
     assert pin_dgrad(oracle.conv_same_dgrad)
