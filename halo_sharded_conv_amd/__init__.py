@@ -98,6 +98,8 @@ def _load() -> ctypes.CDLL:
         "st_groupnorm_partials": (I32, [P, PP, P, I32, P, SZ, P]),
         "st_groupnorm_combine": (I32, [P, I32, ctypes.c_float, P, P, P, SZ, P]),
         "st_groupnorm_apply": (I32, [P, PP, I32, PP, P, SZ, P]),
+        "st_groupnorm_backward_workspace_bytes": (SZ, [P, I32]),
+        "st_groupnorm_backward": (I32, [P, PP, PP, P, P, I32, P, P, SZ, PP, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -355,10 +357,35 @@ def st_groupnorm_apply(y_plan: Plan, y_bufs, groups: int, z_bufs, workspace, str
            "st_groupnorm_apply")
 
 
+def st_groupnorm_backward_workspace_bytes(y_plan: Plan, groups: int) -> int:
+    return int(lib.st_groupnorm_backward_workspace_bytes(y_plan.handle, groups))
+
+
+def st_groupnorm_backward(y_plan: Plan, y_bufs, dz_bufs, ymax, dzmax, groups: int, gamma, fwd_workspace,
+                          dy_bufs, dgamma, dbeta, workspace, stream=None) -> None:
+    sizes = _shard_bytes(y_plan)
+    ys = _ptr_array(y_bufs, "st_groupnorm_backward y", sizes)
+    dzs = _ptr_array(dz_bufs, "st_groupnorm_backward dz", sizes)
+    dys = _ptr_array(dy_bufs, "st_groupnorm_backward dy", sizes)
+    ng = 4 * y_plan.batch * groups
+    ym = _dev_ptr(ymax, "ymax", ng) if ymax is not None else 0
+    dm = _dev_ptr(dzmax, "dzmax", ng) if dzmax is not None else 0
+    g = _dev_ptr(gamma, "gamma", 4 * y_plan.channels)
+    dg = _dev_ptr(dgamma, "dgamma", 4 * y_plan.channels)
+    db = _dev_ptr(dbeta, "dbeta", 4 * y_plan.channels)
+    fws, fnb = _ws(fwd_workspace)
+    ws, nb = _ws(workspace)
+    _check(lib.st_groupnorm_backward(y_plan.handle, ys, dzs, ctypes.c_void_p(ym), ctypes.c_void_p(dm), groups,
+                                     ctypes.c_void_p(g), ctypes.c_void_p(fws), fnb, dys, ctypes.c_void_p(dg),
+                                     ctypes.c_void_p(db), ctypes.c_void_p(ws), nb, _stream(stream)),
+           "st_groupnorm_backward")
+
+
 __all__ = [
     "lib", "LIB_PATH", "ShardConvError", "Plan", "ST_F32", "ST_BF16", "st_version",
     "st_plan_shards", "st_halo_pack", "st_halo_unpack", "st_halo_exchange", "st_conv_weight_bytes", "st_conv_dgrad_weights",
     "st_conv_pack_weights", "st_conv_sharded", "st_groupnorm_workspace_bytes",
     "st_groupnorm_workspace_layout", "st_groupnorm_sharded", "st_groupnorm_partials",
-    "st_groupnorm_combine", "st_groupnorm_apply",
+    "st_groupnorm_combine", "st_groupnorm_apply", "st_groupnorm_backward_workspace_bytes",
+    "st_groupnorm_backward",
 ]

@@ -38,7 +38,8 @@ constexpr int kPart = 8;        // vectors per thread per apply work unit
 
 struct GnShard {
   const float* y;
-  float* z;
+  float* z;                     // backward: dy
+  const float* dz;              // backward only: the gradient arriving at z
   int64_t vecs_per_n;           // vectors in one batch item of this shard
   int32_t item_begin;           // first item of this shard
   int32_t items_per_n;
@@ -353,6 +354,263 @@ __global__ __launch_bounds__(kNT) void gn_apply(const GnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- backward
+//
+// Gradients of z = GroupNorm(y) for an upstream gradient dz.  Per (n, g) with
+// r = rstd, yhat = (y - mean) * r and g_c = gamma_c * dz:
+//     dy = r * (g - mean_g(g) - yhat * mean_g(g * yhat))
+//     dgamma_c = sum_{n, positions} dz * yhat,   dbeta_c = sum_{n, positions} dz
+// Both group means come from two per-(n, channel) sums, S1 = sum dz and
+// S2 = sum dz * yhat:  mean_g(g) = sum_c gamma_c S1 / M and
+// mean_g(g * yhat) = sum_c gamma_c S2 / M.  The per-channel sums are exact in
+// the same way as the forward statistics: with m = max |dz| of the group
+// (2^(ed-1) <= m < 2^ed) and B >= max |yhat| (2^(eh-1) <= B < 2^eh), every
+// element contributes
+//     q1 = rint(dz        * 2^(52 - L - ed))         |q1| <= 2^(52-L)
+//     q2 = rint(dz * yhat * 2^(52 - L - ed - eh))    |q2| <= 2^(52-L)
+// (dz * yhat of two fp32 values is exact in fp64).  B comes from the forward
+// pass: |yhat| <= (max |y| + |mean|) * rstd, widened by 2^-20 for the two fp32
+// roundings of yhat.  So the sums, dgamma, dbeta and dy are the same bits for
+// every shard plan.
+//
+// Kernels: gn_fill (partials), gn_max on dz (unless the caller supplies
+// max |dz|), gnb_stats (per-shard S1, S2 per (n, c)), gnb_combine (sums over
+// shards; per-channel coefficients; dgamma, dbeta), gnb_apply
+//     dy = a_c * dz + k_g * (y - mean_g) + b_g
+// with a_c = r gamma_c, k_g = -r^2 mean_g(g yhat), b_g = -r mean_g(g).
+
+struct GnbArgs {
+  GnArgs g;                     // y = forward input of GroupNorm, z = dy, dz
+  const float* fstats;          // [N][G][2] (mean, rstd) of the forward pass
+  const uint32_t* dzmax;        // [N][G] bits of max |dz|
+  double* bpart;                // [S][N][C][2] exact (sum q1, sum q2)
+  int32_t* bscales;             // [N][G][2] exponents of q1, q2
+  float4* bchan;                // [N][C] (mean, a, k, b)
+  float* dgamma;                // [C] or NULL
+  float* dbeta;                 // [C] or NULL
+};
+
+__device__ __forceinline__ void bwd_scales(uint32_t dzbits, uint32_t ybits, float mean, float rstd, int lbits,
+                                           int& e1, int& e2) {
+  const float m = __uint_as_float(dzbits);
+  if (!(m > 0.f)) { e1 = 0; e2 = 0; return; }
+  int ed;
+  (void)frexpf(m, &ed);
+  e1 = 52 - lbits - ed;
+  const double bound = ((double)__uint_as_float(ybits) + fabs((double)mean)) * (double)rstd * (1.0 + 0x1p-20);
+  int eh = 0;
+  if (bound > 0.0 && bound < 0x1p1000) (void)frexp(bound, &eh);
+  e2 = 52 - lbits - ed - eh;
+}
+
+template <int VW, bool FIXED>
+__global__ __launch_bounds__(kNT) void gnb_stats(const GnbArgs b) {
+  using V = Vec<VW>;
+  const GnArgs& a = b.g;
+  constexpr int kHalf = kIter / 2;      // vectors of y and of dz in flight per thread
+  extern __shared__ double gnb_lds[];   // per channel: s1, s2, 2^e1, 2^e2, (mean, rstd)
+  const int tid = threadIdx.x;
+  const int C = a.channels;
+  double* s1 = gnb_lds;
+  double* s2 = gnb_lds + C;
+  double* sc1 = gnb_lds + 2 * C;
+  double* sc2 = gnb_lds + 3 * C;
+  float2* mr = reinterpret_cast<float2*>(gnb_lds + 4 * C);
+  const int gs = C / a.groups;
+  if (blockIdx.x == 0) {
+    for (int i = tid; i < a.batch * a.groups; i += kNT) {
+      int e1, e2;
+      bwd_scales(b.dzmax[i], a.ymax[i], b.fstats[2 * i], b.fstats[2 * i + 1], a.lbits, e1, e2);
+      b.bscales[2 * i + 0] = e1;
+      b.bscales[2 * i + 1] = e2;
+    }
+  }
+  for (int i = tid; i < C; i += kNT) { s1[i] = 0.0; s2[i] = 0.0; }
+  double acc1[VW], acc2[VW], f1[VW], f2[VW];
+  float mu[VW], rs[VW];
+#pragma unroll
+  for (int j = 0; j < VW; ++j) { acc1[j] = 0.0; acc2[j] = 0.0; }
+  int cur = -1, cur_s = 0, cur_n = 0;
+  auto flush = [&](int s, int n) {
+    __syncthreads();
+    if (FIXED) {
+      const int c0 = (tid * VW) % C;
+#pragma unroll
+      for (int j = 0; j < VW; ++j) {
+        atomicAdd(&s1[c0 + j], acc1[j]);
+        atomicAdd(&s2[c0 + j], acc2[j]);
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < C; c += kNT) {
+      double* p = b.bpart + (((size_t)s * a.batch + n) * C + c) * 2;
+      atomicAdd(p + 0, s1[c]);
+      atomicAdd(p + 1, s2[c]);
+    }
+    __syncthreads();
+    for (int i = tid; i < C; i += kNT) { s1[i] = 0.0; s2[i] = 0.0; }
+#pragma unroll
+    for (int j = 0; j < VW; ++j) { acc1[j] = 0.0; acc2[j] = 0.0; }
+  };
+  for (int item = blockIdx.x; item < a.total_items; item += gridDim.x) {
+    int s, n, k;
+    decode_item(a, item, s, n, k);
+    const int key = s * a.batch + n;
+    if (key != cur) {
+      if (cur >= 0) flush(cur_s, cur_n);
+      __syncthreads();
+      for (int c = tid; c < C; c += kNT) {
+        const int i = n * a.groups + c / gs;
+        int e1, e2;
+        bwd_scales(b.dzmax[i], a.ymax[i], b.fstats[2 * i], b.fstats[2 * i + 1], a.lbits, e1, e2);
+        sc1[c] = ldexp(1.0, e1);
+        sc2[c] = ldexp(1.0, e2);
+        mr[c] = make_float2(b.fstats[2 * i], b.fstats[2 * i + 1]);
+      }
+      __syncthreads();
+      if (FIXED) {
+        const int c0 = (tid * VW) % C;
+#pragma unroll
+        for (int j = 0; j < VW; ++j) {
+          f1[j] = sc1[c0 + j];
+          f2[j] = sc2[c0 + j];
+          mu[j] = mr[c0 + j].x;
+          rs[j] = mr[c0 + j].y;
+        }
+      }
+      cur = key;
+      cur_s = s;
+      cur_n = n;
+    }
+    const GnShard& sh = a.sh[s];
+    const typename V::T* y = reinterpret_cast<const typename V::T*>(sh.y) + n * sh.vecs_per_n;
+    const typename V::T* dz = reinterpret_cast<const typename V::T*>(sh.dz) + n * sh.vecs_per_n;
+#pragma unroll
+    for (int hb = 0; hb < kIter; hb += kHalf) {
+      const int64_t v0 = (int64_t)k * kNT * kIter + hb * kNT + tid;
+      typename V::T vy[kHalf], vd[kHalf];
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) {
+        const int64_t v = v0 + i * kNT;
+        const int64_t vc = v < sh.vecs_per_n ? v : sh.vecs_per_n - 1;
+        vy[i] = load_nt<VW>(y, vc);
+        vd[i] = load_nt<VW>(dz, vc);
+      }
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) {
+        const int64_t v = v0 + i * kNT;
+        const bool in = v < sh.vecs_per_n;
+#pragma unroll
+        for (int j = 0; j < VW; ++j) {
+          if (FIXED) {
+            const float yh = (V::get(vy[i], j) - mu[j]) * rs[j];
+            const double d = in ? (double)V::get(vd[i], j) : 0.0;   // the tail contributes 0
+            acc1[j] += rint(d * f1[j]);
+            acc2[j] += rint((d * (double)yh) * f2[j]);
+          } else if (in) {
+            const int c = (int)((v * VW + j) % C);
+            const float yh = (V::get(vy[i], j) - mr[c].x) * mr[c].y;
+            const double d = (double)V::get(vd[i], j);
+            atomicAdd(&s1[c], rint(d * sc1[c]));
+            atomicAdd(&s2[c], rint((d * (double)yh) * sc2[c]));
+          }
+        }
+      }
+    }
+  }
+  if (cur >= 0) flush(cur_s, cur_n);
+}
+
+__global__ void gnb_combine(const GnbArgs b) {
+  const GnArgs& a = b.g;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int C = a.channels, G = a.groups, N = a.batch, gs = C / G;
+  auto chan_sum = [&](int n, int c, int q) {   // exact per-(n, c) sum, scaled back
+    double t = 0.0;
+    for (int s = 0; s < a.nshards; ++s) t += b.bpart[(((size_t)s * N + n) * C + c) * 2 + q];
+    return ldexp(t, -b.bscales[2 * (n * G + c / gs) + q]);
+  };
+  if (i < N * G) {
+    const int n = i / G, g = i - n * G;
+    const double r = (double)b.fstats[2 * i + 1];
+    double t1 = 0.0, t2 = 0.0;
+    for (int c = g * gs; c < (g + 1) * gs; ++c) {
+      const double gam = a.gamma ? (double)a.gamma[c] : 1.0;
+      t1 += gam * chan_sum(n, c, 0);
+      t2 += gam * chan_sum(n, c, 1);
+    }
+    const double m1 = t1 / a.m_count, m2 = t2 / a.m_count;
+    const float kk = (float)(-r * r * m2), bb = (float)(-r * m1);
+    for (int c = g * gs; c < (g + 1) * gs; ++c) {
+      const double gam = a.gamma ? (double)a.gamma[c] : 1.0;
+      b.bchan[(size_t)n * C + c] = make_float4(b.fstats[2 * i], (float)(r * gam), kk, bb);
+    }
+  }
+  if (i < C) {
+    double db = 0.0, dg = 0.0;
+    for (int n = 0; n < N; ++n) {
+      db += chan_sum(n, i, 0);
+      dg += chan_sum(n, i, 1);
+    }
+    if (b.dbeta) b.dbeta[i] = (float)db;
+    if (b.dgamma) b.dgamma[i] = (float)dg;
+  }
+}
+
+template <int VW, bool FIXED>
+__global__ __launch_bounds__(kNT) void gnb_apply(const GnbArgs b) {
+  using V = Vec<VW>;
+  const GnArgs& a = b.g;
+  const int tid = threadIdx.x;
+  const int C = a.channels;
+  int cur = -1;
+  float4 p[VW];
+  constexpr int kParts = kIter / kPart;
+  for (int h = blockIdx.x; h < kParts * a.total_items; h += gridDim.x) {
+    const int hr = kParts * a.total_items - 1 - h;
+    int s, n, k;
+    decode_item(a, hr / kParts, s, n, k);
+    const int key = s * a.batch + n;
+    if (FIXED && key != cur) {
+      const int c0 = (tid * VW) % C;
+#pragma unroll
+      for (int j = 0; j < VW; ++j) p[j] = b.bchan[(size_t)n * C + c0 + j];
+      cur = key;
+    }
+    const GnShard& sh = a.sh[s];
+    const typename V::T* y = reinterpret_cast<const typename V::T*>(sh.y) + n * sh.vecs_per_n;
+    const typename V::T* dz = reinterpret_cast<const typename V::T*>(sh.dz) + n * sh.vecs_per_n;
+    typename V::T* dy = reinterpret_cast<typename V::T*>(sh.z) + n * sh.vecs_per_n;
+    const int64_t v0 = (int64_t)k * kNT * kIter + (hr % kParts) * kNT * kPart + tid;
+    typename V::T vy[kPart], vd[kPart];
+#pragma unroll
+    for (int i = 0; i < kPart; ++i) {
+      const int64_t v = v0 + i * kNT;
+      const int64_t vc = v < sh.vecs_per_n ? v : sh.vecs_per_n - 1;   // tail: stored by no lane
+      vy[i] = load_nt<VW>(y, vc);
+      vd[i] = load_nt<VW>(dz, vc);
+    }
+#pragma unroll
+    for (int i = 0; i < kPart; ++i) {
+      const int64_t v = v0 + i * kNT;
+      if (v >= sh.vecs_per_n) break;
+      float out[VW];
+#pragma unroll
+      for (int j = 0; j < VW; ++j) {
+        float4 q;
+        if (FIXED) q = p[j];
+        else q = b.bchan[(size_t)n * C + (int)((v * VW + j) % C)];
+        out[j] = fmaf(q.y, V::get(vd[i], j), fmaf(q.z, V::get(vy[i], j) - q.x, q.w));
+      }
+      if constexpr (VW == 4) {
+        typedef float nf4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(nf4{out[0], out[1], out[2], out[3]}, reinterpret_cast<nf4*>(&dy[v]));
+      }
+      else __builtin_nontemporal_store(out[0], &dy[v]);
+    }
+  }
+}
+
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 st_gn_layout layout_of(const st_plan* p, int groups) {
@@ -473,6 +731,47 @@ st_status launch_apply(GnArgs& a, hipStream_t st) {
   return launch_check("st_groupnorm_apply: launch");
 }
 
+
+// backward workspace: [S][N][C][2] double partials, [N][G] max |dz|,
+// [N][G][2] exponents, [N][C] float4 coefficients
+struct GnbLayout {
+  size_t part, dzmax, scales, chan, total;
+};
+GnbLayout bwd_layout_of(const st_plan* p, int groups) {
+  GnbLayout l{};
+  const size_t S = p->shards.size(), N = (size_t)p->batch, G = (size_t)groups, C = (size_t)p->channels;
+  size_t off = 0;
+  l.part = off;   off = align256(off + S * N * C * 2 * sizeof(double));
+  l.dzmax = off;  off = align256(off + N * G * sizeof(uint32_t));
+  l.scales = off; off = align256(off + N * G * 2 * sizeof(int32_t));
+  l.chan = off;   off = align256(off + N * C * sizeof(float4));
+  l.total = off;
+  return l;
+}
+
+template <int VW, bool FIXED>
+st_status launch_backward(GnbArgs& b, bool need_max, hipStream_t st) {
+  GnArgs& a = b.g;
+  const int grid = grid_of(a);
+  if (need_max) {
+    GnArgs m = a;                         // max |dz| with the forward's max kernel
+    for (int s = 0; s < m.nshards; ++s) m.sh[s].y = m.sh[s].dz;
+    m.ymax = const_cast<uint32_t*>(b.dzmax);
+    hipLaunchKernelGGL((gn_max<VW, FIXED>), dim3(grid), dim3(kNT), (size_t)a.channels * 4, st, m);
+    st_status s = launch_check("st_groupnorm_backward: max launch");
+    if (s != ST_OK) return s;
+  }
+  hipLaunchKernelGGL((gnb_stats<VW, FIXED>), dim3(grid), dim3(kNT), (size_t)a.channels * 40, st, b);
+  st_status s = launch_check("st_groupnorm_backward: stats launch");
+  if (s != ST_OK) return s;
+  const int nthreads = std::max(a.batch * a.groups, a.channels);
+  hipLaunchKernelGGL(gnb_combine, dim3((nthreads + 63) / 64), dim3(64), 0, st, b);
+  s = launch_check("st_groupnorm_backward: combine launch");
+  if (s != ST_OK) return s;
+  const int agrid = std::max(1, std::min((kIter / kPart) * a.total_items, device_cus() * 16));
+  hipLaunchKernelGGL((gnb_apply<VW, FIXED>), dim3(agrid), dim3(kNT), 0, st, b);
+  return launch_check("st_groupnorm_backward: apply launch");
+}
 }  // namespace
 }  // namespace st
 
@@ -562,6 +861,60 @@ st_status st_groupnorm_sharded(const st_plan* y_plan, const float* const* y_bufs
   s = st_groupnorm_combine(y_plan, groups, eps, gamma_or_null, beta_or_null, workspace, workspace_bytes, stream);
   if (s != ST_OK) return s;
   return st_groupnorm_apply(y_plan, y_bufs, groups, z_bufs, workspace, workspace_bytes, stream);
+}
+
+size_t st_groupnorm_backward_workspace_bytes(const st_plan* y_plan, int32_t groups) {
+  if (!y_plan || groups < 1) return 0;
+  return bwd_layout_of(y_plan, groups).total;
+}
+
+st_status st_groupnorm_backward(const st_plan* y_plan, const float* const* y_bufs, const float* const* dz_bufs,
+                                const uint32_t* ymax_or_null, const uint32_t* dzmax_or_null, int32_t groups,
+                                const float* gamma_or_null, const void* fwd_workspace,
+                                size_t fwd_workspace_bytes, float* const* dy_bufs, float* dgamma_or_null,
+                                float* dbeta_or_null, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "st_groupnorm_backward";
+  if (!y_bufs || !dz_bufs || !dy_bufs) return fail(ST_ERR_INVALID_ARG, std::string(who) + ": NULL buffer array");
+  GnbArgs b{};
+  int vw;
+  bool fixed;
+  // validates the plan, y, dy, gamma, ymax and the forward workspace
+  st_status s = prepare(y_plan, y_bufs, dy_bufs, ymax_or_null, groups, 0.f, gamma_or_null, nullptr,
+                        const_cast<void*>(fwd_workspace), fwd_workspace_bytes, who, b.g, vw, fixed);
+  if (s != ST_OK) return s;
+  for (size_t i = 0; i < y_plan->shards.size(); ++i) {
+    if (!dz_bufs[i]) return fail(ST_ERR_INVALID_ARG, std::string(who) + ": NULL dz buffer");
+    if (!aligned16(dz_bufs[i])) return fail(ST_ERR_ALIGNMENT, std::string(who) + ": dz buffers must be 16-byte aligned");
+    b.g.sh[i].dz = dz_bufs[i];
+  }
+  if ((dzmax_or_null && (reinterpret_cast<uintptr_t>(dzmax_or_null) & 3)) ||
+      (dgamma_or_null && (reinterpret_cast<uintptr_t>(dgamma_or_null) & 3)) ||
+      (dbeta_or_null && (reinterpret_cast<uintptr_t>(dbeta_or_null) & 3)))
+    return fail(ST_ERR_ALIGNMENT, std::string(who) + ": misaligned dzmax/dgamma/dbeta");
+  const GnbLayout l = bwd_layout_of(y_plan, groups);
+  if (!workspace || workspace_bytes < l.total)
+    return fail(ST_ERR_WORKSPACE, std::string(who) + ": workspace missing or too small");
+  if (!aligned16(workspace)) return fail(ST_ERR_ALIGNMENT, std::string(who) + ": workspace not 16-byte aligned");
+  if (workspace == fwd_workspace) return fail(ST_ERR_INVALID_ARG, std::string(who) + ": workspace must not be the forward workspace");
+  const st_gn_layout fl = layout_of(y_plan, groups);
+  char* ws = static_cast<char*>(workspace);
+  b.fstats = reinterpret_cast<const float*>(static_cast<const char*>(fwd_workspace) + fl.stats_offset);
+  b.dzmax = dzmax_or_null ? dzmax_or_null : reinterpret_cast<const uint32_t*>(ws + l.dzmax);
+  b.bpart = reinterpret_cast<double*>(ws + l.part);
+  b.bscales = reinterpret_cast<int32_t*>(ws + l.scales);
+  b.bchan = reinterpret_cast<float4*>(ws + l.chan);
+  b.dgamma = dgamma_or_null;
+  b.dbeta = dbeta_or_null;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // clear the partials (and the max scratch when this call computes it)
+  const int64_t words = (int64_t)(l.dzmax + (dzmax_or_null ? 0 : (size_t)b.g.batch * groups * 4)) / 4;
+  hipLaunchKernelGGL(gn_fill, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<uint32_t*>(workspace), words);
+  s = launch_check("st_groupnorm_backward: clear launch");
+  if (s != ST_OK) return s;
+  const bool need_max = dzmax_or_null == nullptr;
+  if (vw == 4) return fixed ? launch_backward<4, true>(b, need_max, st) : launch_backward<4, false>(b, need_max, st);
+  return fixed ? launch_backward<1, true>(b, need_max, st) : launch_backward<1, false>(b, need_max, st);
 }
 
 }  // extern "C"

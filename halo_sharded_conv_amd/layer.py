@@ -15,7 +15,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 from . import (ST_BF16, ST_F32, ShardConvError, st_conv_dgrad_weights, st_conv_pack_weights, st_conv_sharded,
-               st_conv_weight_bytes, st_groupnorm_apply, st_groupnorm_combine, st_groupnorm_partials,
+               st_conv_weight_bytes, st_groupnorm_apply, st_groupnorm_backward,
+               st_groupnorm_backward_workspace_bytes, st_groupnorm_combine, st_groupnorm_partials,
                st_groupnorm_sharded, st_groupnorm_workspace_bytes, st_groupnorm_workspace_layout,
                st_halo_exchange, st_halo_pack, st_halo_unpack, st_plan_shards)
 
@@ -150,6 +151,33 @@ class ShardedConvGN:
 
     def norm_apply(self, stream=None) -> None:
         st_groupnorm_apply(self.out_plan, self.y_bufs, self.cfg.groups, self.z_bufs, self.ws, stream)
+
+    # ---------------------------------------------------------- backward
+    def alloc_backward(self) -> None:
+        """Buffers of the GroupNorm backward pass: dz (upstream gradient at
+        z), dy (gradient at y), dgamma, dbeta and the backward workspace."""
+        torch = _torch()
+        cfg = self.cfg
+        self.dz_bufs = [torch.zeros_like(y) for y in self.y_bufs]
+        self.dy_bufs = [torch.empty_like(y) for y in self.y_bufs]
+        self.dgamma = torch.empty(cfg.cout, dtype=torch.float32, device=self.device)
+        self.dbeta = torch.empty(cfg.cout, dtype=torch.float32, device=self.device)
+        self.bws = torch.zeros(st_groupnorm_backward_workspace_bytes(self.out_plan, cfg.groups),
+                               dtype=torch.uint8, device=self.device)
+
+    def load_upstream_grad(self, dz: np.ndarray) -> None:
+        """dz: channels-last [N, *spatial, Cout] float32."""
+        for i in range(self.S):
+            self.out_view(self.dz_bufs, i).copy_(self._host_to_dev(dz[self._global_slices(i)]))
+        _torch().cuda.synchronize()
+
+    def norm_backward(self, dzmax=None, dy_bufs=None, stream=None) -> None:
+        """GroupNorm backward from the forward pass's y and workspace."""
+        cfg = self.cfg
+        st_groupnorm_backward(self.out_plan, self.y_bufs, self.dz_bufs, self.ymax if self.fuse_max else None,
+                              dzmax, cfg.groups, self.gamma, self.ws,
+                              self.dy_bufs if dy_bufs is None else dy_bufs, self.dgamma, self.dbeta, self.bws,
+                              stream)
 
     def step(self, stream=None) -> None:
         self.exchange(True, stream)

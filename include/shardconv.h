@@ -304,6 +304,45 @@ st_status st_groupnorm_apply(const st_plan* y_plan, const float* const* y_bufs, 
                              float* const* z_bufs, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * st_groupnorm_backward - gradients of st_groupnorm_sharded for an upstream
+ * gradient dz: dy (the gradient at the conv output y), dgamma and dbeta.
+ * Training at native resolution needs the backward pass ("Technical summary:
+ * ShardTensor", section 1 "Problem statement"; section 4 "Results and
+ * benchmarks", the training runs); like the forward statistics, the two
+ * per-group reductions of the backward pass are combined over all shards
+ * (section 2, "Implementation details", "Communication").  Per (n, group),
+ * with r = rstd, yhat = (y - mean) * r and g = gamma_c * dz:
+ *   dy     = r * (g - mean_group(g) - yhat * mean_group(g * yhat))
+ *   dgamma = sum over n and positions of dz * yhat   (per channel)
+ *   dbeta  = sum over n and positions of dz          (per channel)
+ * The per-(n, channel) sums of dz and dz * yhat are exact fixed-point sums
+ * (scaled by max |dz| and a bound on |yhat| from the forward pass), so dy,
+ * dgamma and dbeta are the same bits for every shard plan.
+ *
+ *   y_plan, y_bufs     the forward call's plan and input y (read)
+ *   dz_bufs            upstream gradient, same layout as y (read)
+ *   ymax_or_null       the ymax pointer the forward call got (NULL: the forward
+ *                      computed it into its workspace)
+ *   dzmax_or_null      [N][groups] bits of max |dz| per (n, group), e.g. from
+ *                      st_conv_sharded's fused max; NULL: computed here (one
+ *                      more read of dz)
+ *   groups, gamma_or_null   as in the forward call
+ *   fwd_workspace      the forward call's workspace, holding its (mean, rstd)
+ *                      (read; must not have been reused since)
+ *   dy_bufs            fp32 output, same layout as y; may alias dz_bufs or y_bufs
+ *   dgamma_or_null, dbeta_or_null   C floats each, or NULL (not computed)
+ *   workspace          >= st_groupnorm_backward_workspace_bytes(y_plan, groups)
+ *                      bytes, distinct from fwd_workspace
+ * The forward variance must be finite and var + eps > 0.
+ */
+size_t st_groupnorm_backward_workspace_bytes(const st_plan* y_plan, int32_t groups);
+st_status st_groupnorm_backward(const st_plan* y_plan, const float* const* y_bufs, const float* const* dz_bufs,
+                                const uint32_t* ymax_or_null, const uint32_t* dzmax_or_null, int32_t groups,
+                                const float* gamma_or_null, const void* fwd_workspace,
+                                size_t fwd_workspace_bytes, float* const* dy_bufs, float* dgamma_or_null,
+                                float* dbeta_or_null, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -219,6 +219,18 @@ def make_affine(wl: Workload, seed: Optional[int] = None):
     return gamma, beta
 
 
+def make_upstream_grad(wl: Workload, seed: int) -> np.ndarray:
+    """A gradient arriving at the layer's output, channels-last
+    [N, *spatial, Cout] float32 ~ N(0, 1), drawn in memory order from one
+    PCG64 stream (one slab of the outermost axis at a time)."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((wl.batch, *wl.spatial, wl.cout), np.float32)
+    for n in range(wl.batch):
+        for i in range(wl.spatial[0]):
+            out[n, i] = rng.standard_normal(size=wl.spatial[1:] + (wl.cout,), dtype=np.float32)
+    return out
+
+
 def _boundaries(sizes: Sequence[int]):
     off = np.concatenate([[0], np.cumsum(sizes)])
     return [int(v) for v in off]

@@ -157,6 +157,36 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert gn(q.handle, misaligned, None, 4, 1e-5, None, None, aligned, ws, need, s) == ALIGN
     assert gn(q.handle, aligned, None, 4, 1e-5, None, None, aligned, ctypes.c_void_p(0x60008), need, s) == ALIGN
     assert gn(q.handle, aligned, ctypes.c_void_p(0x70002), 4, 1e-5, None, None, aligned, ws, need, s) == ALIGN
+    # groupnorm backward
+    bneed = L.st_groupnorm_backward_workspace_bytes(q.handle, 4)
+    assert bneed > 0 and L.st_groupnorm_backward_workspace_bytes(None, 4) == 0
+    bws = ctypes.c_void_p(0x80000)
+    dzs = PP(0x90000, 0xA0000)
+    gb = L.st_groupnorm_backward
+    args = [q.handle, aligned, dzs, None, None, 4, None, ws, need, aligned, None, None, bws, bneed, s]
+
+    def gbw(**kw):
+        a = list(args)
+        names = ["plan", "y", "dz", "ymax", "dzmax", "groups", "gamma", "fws", "fnb", "dy", "dg", "db",
+                 "ws", "nb", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return gb(*a)
+    assert gbw(plan=None) == INVALID
+    assert gbw(dz=None) == INVALID
+    assert gbw(dz=nulls) == INVALID
+    assert gbw(dz=misaligned) == ALIGN
+    assert gbw(dy=misaligned) == ALIGN
+    assert gbw(groups=5) == INVALID
+    assert gbw(fnb=need - 1) == WORKSPACE
+    assert gbw(fws=None) == WORKSPACE
+    assert gbw(nb=bneed - 1) == WORKSPACE
+    assert gbw(ws=None) == WORKSPACE
+    assert gbw(ws=ctypes.c_void_p(0x80008)) == ALIGN
+    assert gbw(ws=ws, nb=max(need, bneed)) == INVALID
+    assert gbw(dzmax=ctypes.c_void_p(0x70002)) == ALIGN
+    assert gbw(dg=ctypes.c_void_p(0x70002)) == ALIGN
+    assert gbw(plan=p.handle) == BAD_SHAPE
 
 
 def test_workspace_layout_regions_are_disjoint():
