@@ -9,12 +9,14 @@ Python binding; the only code both sides use is the seeded input module
 Every function is pinned by CPU tests (brute force on tiny volumes, delta
 kernels, linearity, torch fp64 as an independent library, GroupNorm closed
 forms, sharded == unsharded; the input gradient by the adjoint identity,
-brute force and torch's fp64 autograd; the GroupNorm backward by torch's
+brute force and torch's fp64 autograd; the weight gradient by the adjoint
+identity in the weights, brute force and torch's fp64 autograd; the GroupNorm backward by torch's
 fp64 autograd and central finite differences).  Nothing here is "parity unpinned".
 """
 from .reference import (  # noqa: F401
-    widen, zero_pad, conv_valid, conv_same, conv_same_dgrad, conv_same_slabbed, conv_at,
+    widen, zero_pad, conv_valid, conv_same, conv_same_dgrad, conv_same_wgrad, conv_same_slabbed, conv_at,
     group_moments, group_norm, group_norm_apply, group_norm_backward, group_sums_onepass,
     shard_offsets, shard_grid, padded_shard, halo_message, halo_directions,
-    sharded_forward, conv_bruteforce, conv_dgrad_bruteforce, group_norm_bruteforce,
+    sharded_forward, conv_bruteforce, conv_dgrad_bruteforce, conv_wgrad_bruteforce,
+    group_norm_bruteforce,
 )

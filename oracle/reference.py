@@ -27,7 +27,10 @@ be a fixed representation of the logical NC(D)HW tensor).
 
 Nothing here is blocked, fused or reordered beyond the definitions: the conv
 accumulates one tap at a time in lexicographic tap order, each tap a plain
-matrix product over input channels.
+matrix product over input channels.  The backward pass (training at native
+resolution, section 1 "Problem statement" and the training runs of section
+4) is the derivative of the same definitions: the input gradient, the weight
+gradient and the GroupNorm backward, each pinned by tests/test_oracle.py.
 """
 from __future__ import annotations
 
@@ -131,6 +134,35 @@ def conv_same_dgrad(dy: np.ndarray, w: np.ndarray) -> np.ndarray:
         wt = np.ascontiguousarray(w[(slice(None), slice(None)) + t])      # [Cout, Cin]
         dx += (rows @ wt).reshape(dx.shape)
     return dx
+
+
+def conv_same_wgrad(x: np.ndarray, dy: np.ndarray, k: int) -> np.ndarray:
+    """Gradient of conv_same with respect to its weights.
+
+    The weight half of the backward pass (same passages as conv_same_dgrad).
+    y[n, i, o] = sum_t sum_c w[o, c, t] * x[n, i + t - p, c] is linear in w, so
+        dw[o, c, t] = sum_n sum_i dy[n, i, o] * x[n, i + t - p, c]
+    with x taken as zero outside the grid.  x: [N, *S, Cin] fp64, dy:
+    [N, *S, Cout] fp64; returns [Cout, Cin, k, .., k] fp64.  One tap at a
+    time, lexicographic, each a plain matrix product over all positions.
+    """
+    d = x.ndim - 2
+    if k % 2 != 1:
+        raise ValueError("odd kernels only")
+    if x.shape[:-1] != dy.shape[:-1]:
+        raise ValueError("x and dy must share batch and spatial extents")
+    cin, cout = x.shape[-1], dy.shape[-1]
+    p = (k - 1) // 2
+    S = x.shape[1:1 + d]
+    xp = zero_pad(x, p)                          # xp[m] = x[m - p]
+    g = np.ascontiguousarray(dy).reshape(-1, cout)
+    dw = np.zeros((cout, cin) + (k,) * d, dtype=np.float64)
+    for t in _taps(k, d):
+        # x[i + t - p] = xp[i + t]: the window starting at t
+        window = xp[(slice(None),) + tuple(slice(t[a], t[a] + S[a]) for a in range(d))]
+        cols = np.ascontiguousarray(window).reshape(-1, cin)
+        dw[(slice(None), slice(None)) + t] = g.T @ cols
+    return dw
 
 
 def conv_same_slabbed(x_src, dtype: str, w: np.ndarray, bias=None, slab: int = 8):
@@ -421,6 +453,29 @@ def conv_dgrad_bruteforce(dy, w):
                     for c in range(cin):
                         dx[(n, *src, c)] += w[(o, c) + t] * g
     return dx
+
+
+def conv_wgrad_bruteforce(x, dy, k):
+    """Scalar-loop weight gradient of the 'same' cross-correlation (tiny
+    inputs): every output position adds dy[o] * x[c] of the input cell that
+    tap t of the forward definition reads."""
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    n_, *spatial, cin = x.shape
+    cout = dy.shape[-1]
+    d = len(spatial)
+    p = (k - 1) // 2
+    dw = np.zeros((cout, cin) + (k,) * d)
+    for n in range(n_):
+        for pos in itertools.product(*[range(s) for s in spatial]):
+            for t in itertools.product(range(k), repeat=d):
+                src = [pos[a] + t[a] - p for a in range(d)]
+                if any(src[a] < 0 or src[a] >= spatial[a] for a in range(d)):
+                    continue
+                for o in range(cout):
+                    for c in range(cin):
+                        dw[(o, c) + t] += dy[(n, *pos, o)] * x[(n, *src, c)]
+    return dw
 
 
 def group_norm_bruteforce(y, groups, eps, gamma=None, beta=None):

@@ -185,6 +185,33 @@ def pin_dgrad(dgrad, conv=oracle.conv_same):
     return bool(ok)
 
 
+def pin_wgrad(wgrad, conv=oracle.conv_same):
+    """The weight gradient against what fixes it independently: the adjoint
+    identity in the weights <conv(x, w), dy> = <w, wgrad(x, dy)> (conv is
+    linear in w), scalar-loop brute force on tiny volumes, and torch's fp64
+    autograd with respect to the weight."""
+    ok = True
+    for d, k in [(2, 3), (2, 5), (3, 3), (3, 5)]:
+        r = rng(600 + 10 * d + k)
+        spatial = (5, 6, 7) if d == 3 else (9, 11)
+        x = r.standard_normal((2, *spatial, 3))
+        dy = r.standard_normal((2, *spatial, 4))
+        w = r.uniform(-1, 1, size=(4, 3) + (k,) * d)
+        y = conv(x, w)
+        lhs = float(np.sum(y * dy))
+        rhs = float(np.sum(w * wgrad(x, dy, k)))
+        ok &= abs(lhs - rhs) <= 1e-13 * float(np.sum(np.abs(y * dy)))
+        small = (3, 4, 4) if d == 3 else (5, 6)
+        xs, dys = r.standard_normal((2, *small, 3)), r.standard_normal((2, *small, 4))
+        ok &= rel(wgrad(xs, dys, k), oracle.conv_wgrad_bruteforce(xs, dys, k)) <= 1e-13
+        wt = torch.from_numpy(w.copy()).requires_grad_(True)
+        f = torch.nn.functional.conv3d if d == 3 else torch.nn.functional.conv2d
+        yt = f(torch.from_numpy(np.moveaxis(x, -1, 1).copy()), wt, padding=k // 2)
+        yt.backward(torch.from_numpy(np.moveaxis(dy, -1, 1).copy()))
+        ok &= rel(wgrad(x, dy, k), wt.grad.numpy()) <= 1e-12
+    return bool(ok)
+
+
 def pin_gn_backward(gnb, gn=oracle.group_norm):
     """GroupNorm backward against torch's fp64 autograd and central finite
     differences of the loss <group_norm(y), dz> (independent of the formula)."""
@@ -252,6 +279,32 @@ def test_gn_backward_pins_catch_mutants(name):
     mutant = {"mean term dropped": no_mean, "yhat term dropped": no_yhat, "gamma ignored": no_gamma,
               "unbiased variance": unbiased}[name]
     assert not pin_gn_backward(mutant), f"no pin caught the GroupNorm-backward mutant '{name}'"
+
+def test_wgrad_pins():
+    assert pin_wgrad(oracle.conv_same_wgrad)
+
+
+@pytest.mark.parametrize("name", ["flipped taps", "channels swapped", "shift off by one", "batch not summed"])
+def test_wgrad_pins_catch_mutants(name):
+    def flipped(x, dy, k):
+        dw = oracle.conv_same_wgrad(x, dy, k)
+        return np.flip(dw, axis=tuple(range(2, dw.ndim))).copy()
+
+    def swapped(x, dy, k):
+        dw = oracle.conv_same_wgrad(x, dy, k)
+        r = np.moveaxis(dw.reshape(dw.shape[0] * dw.shape[1], -1), 0, 0)
+        return r[::-1].reshape(dw.shape)      # o and c indices scrambled
+
+    def shifted(x, dy, k):
+        return oracle.conv_same_wgrad(np.roll(x, 1, axis=1), dy, k)
+
+    def one_sample(x, dy, k):
+        return oracle.conv_same_wgrad(x[:1], dy[:1], k)
+
+    mutant = {"flipped taps": flipped, "channels swapped": swapped, "shift off by one": shifted,
+              "batch not summed": one_sample}[name]
+    assert not pin_wgrad(mutant), f"no pin caught the wgrad mutant '{name}'"
+
 
 def test_dgrad_pins():
     assert pin_dgrad(oracle.conv_same_dgrad)
