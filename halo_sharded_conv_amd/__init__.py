@@ -92,6 +92,8 @@ def _load() -> ctypes.CDLL:
         "st_conv_pack_weights": (I32, [I32, I32, I32, I32, I32, P, P, P]),
         "st_conv_dgrad_weights": (I32, [I32, I32, I32, I32, I32, P, P, P]),
         "st_conv_sharded": (I32, [P, PP, P, P, I32, I32, P, PP, P, I32, P]),
+        "st_conv_wgrad_workspace_bytes": (SZ, [P, I32, I32]),
+        "st_conv_wgrad": (I32, [P, PP, P, PP, I32, P, P, SZ, P]),
         "st_groupnorm_workspace_bytes": (SZ, [P, I32]),
         "st_groupnorm_workspace_layout": (I32, [P, I32, ctypes.POINTER(_GnLayout)]),
         "st_groupnorm_sharded": (I32, [P, PP, P, I32, ctypes.c_float, P, P, PP, P, SZ, P]),
@@ -301,6 +303,21 @@ def st_conv_sharded(in_plan: Plan, in_bufs, packed_weight, bias, cout: int, ksiz
            "st_conv_sharded")
 
 
+def st_conv_wgrad_workspace_bytes(x_plan: Plan, cout: int, ksize: int) -> int:
+    return int(lib.st_conv_wgrad_workspace_bytes(x_plan.handle, cout, ksize))
+
+
+def st_conv_wgrad(x_plan: Plan, x_bufs, dy_plan: Plan, dy_bufs, ksize: int, dweight, workspace,
+                  stream=None) -> None:
+    xs = _ptr_array(x_bufs, "st_conv_wgrad x", _shard_bytes(x_plan))
+    dys = _ptr_array(dy_bufs, "st_conv_wgrad dy", _shard_bytes(dy_plan))
+    elems = dy_plan.channels * x_plan.channels * ksize ** x_plan.ndim
+    dw = _dev_ptr(dweight, "dweight", 4 * elems)
+    ws, nb = _ws(workspace)
+    _check(lib.st_conv_wgrad(x_plan.handle, xs, dy_plan.handle, dys, ksize, ctypes.c_void_p(dw),
+                             ctypes.c_void_p(ws), nb, _stream(stream)), "st_conv_wgrad")
+
+
 def st_groupnorm_workspace_bytes(y_plan: Plan, groups: int) -> int:
     return int(lib.st_groupnorm_workspace_bytes(y_plan.handle, groups))
 
@@ -387,5 +404,5 @@ __all__ = [
     "st_conv_pack_weights", "st_conv_sharded", "st_groupnorm_workspace_bytes",
     "st_groupnorm_workspace_layout", "st_groupnorm_sharded", "st_groupnorm_partials",
     "st_groupnorm_combine", "st_groupnorm_apply", "st_groupnorm_backward_workspace_bytes",
-    "st_groupnorm_backward",
+    "st_groupnorm_backward", "st_conv_wgrad_workspace_bytes", "st_conv_wgrad",
 ]

@@ -1,0 +1,443 @@
+// Weight gradient of the sharded convolution.
+//
+// Training at native resolution needs the backward pass ("Technical summary:
+// ShardTensor - domain parallelism for scientific machine learning", section 1
+// "Problem statement"; section 4 "Results and benchmarks", the ViT and
+// StormScope training runs).  For y[n, i, o] = sum_t sum_c w[o, c, t] *
+// x[n, i + t - p, c] the weight gradient is
+//     dw[o, c, t] = sum_n sum_i dy[n, i, o] * x[n, i + t - p, c],
+// a contraction over every position of every shard.  Each shard reads only its
+// own halo-padded x (the margins already hold the neighbours' cells and the
+// zero padding), so the shards contribute independent partial sums; the
+// partials are then reduced in a fixed order (the all-reduce a multi-device
+// run would do, section 2 "Implementation details", "Communication").
+//
+// Matrix-core kernel (bf16 operands, fp32 accumulation).  Work is cut into
+// output rows (n, d, h) of a shard and, along W, into chunks of 64 columns
+// u = i + tx (the x column a tap reads, shifted to start at 0):
+//   A[(tx, o)][u] = dy[i = u - tx][o]      (zero where i is outside the row)
+//   B[(r, c)][u]  = x[row r of the taps][u - p][c]
+// where r enumerates the taps off the W axis ((tz, ty) in 3D, ty in 2D).
+// Then C[(tx, o)][(r, c)] = sum_u A B^T = dw[o, c, (r, tx)]: every product of
+// the definition appears exactly once, and the contraction index u runs along
+// memory-contiguous positions.  Both operands are written to LDS transposed
+// (positions contiguous, one row per (tx, o) or (r, c)) so that a lane's 8
+// consecutive K values are one 16-byte read; A holds dy once per tx shift, so
+// every fragment read is aligned.
+//
+// A workgroup owns a tile of 32x32 output blocks and a fixed share of the
+// rows (row j goes to partition j mod GP), accumulating over all of them in
+// registers, then stores its partial dw.  The reduction sums the GP partials
+// in partition order in fp64: the result does not depend on the device, the
+// launch or timing, only on the shard plan (for another plan the rows fall
+// into other partitions and rounding differs within the fp32 accumulation).
+//
+// Other shapes and the fp32 path use a direct kernel: one thread per
+// (dw element, partition), fp32 FMA in row order.
+#include <algorithm>
+
+#include "internal.h"
+
+namespace st {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWgMaxShards = ST_MAX_SHARDS;
+
+struct WgShard {
+  const void* x;        // padded x shard
+  const void* dy;       // dy shard (own halo)
+  int64_t xs[3];        // element strides of x: d, h, w (c contiguous); batch stride xn
+  int64_t xn;
+  int64_t ds[3];        // element strides of dy
+  int64_t dn;
+  int32_t ext[3];       // interior extents (d, h, w); 2D: d = 1
+  int32_t xo[3];        // x buffer coordinate of tap 0 for output 0: halo_x - p per axis
+  int32_t dyo[3];       // dy buffer coordinate of output 0: halo_dy per axis
+  int32_t row_begin;    // first global row index of this shard
+  int32_t rows_per_n;   // ext[0] * ext[1]
+};
+
+struct WgArgs {
+  int32_t nshards, batch, total_rows, parts;
+  float* partial;       // [parts][Cout][Cin][taps]
+  WgShard sh[kWgMaxShards];
+};
+
+__device__ __forceinline__ void decode_row(const WgArgs& a, int row, int& s, int& n, int& d, int& h) {
+  s = 0;
+  while (s + 1 < a.nshards && a.sh[s + 1].row_begin <= row) ++s;
+  const int r = row - a.sh[s].row_begin;
+  n = r / a.sh[s].rows_per_n;
+  const int q = r - n * a.sh[s].rows_per_n;
+  d = q / a.sh[s].ext[1];
+  h = q - d * a.sh[s].ext[1];
+}
+
+// --------------------------------------------------------------------------
+// matrix-core kernel
+// --------------------------------------------------------------------------
+
+template <int NDIM_, int K_, int CIN_, int COUT_, int WGM_, int WGN_, int WM_, int WN_, int TILES_M_, int TILES_N_>
+struct WgCfg {
+  static constexpr int NDIM = NDIM_, K = K_, CIN = CIN_, COUT = COUT_;
+  static constexpr int WGM = WGM_, WGN = WGN_, WM = WM_, WN = WN_;
+  static constexpr int P = K / 2;
+  static constexpr int TAPS = NDIM == 3 ? K * K * K : K * K;
+  static constexpr int R = NDIM == 3 ? K * K : K;        // tap rows off the W axis
+  static constexpr int MR = K * COUT, NR = R * CIN;       // rows of A and of B
+  static constexpr int MB = (MR + 31) / 32, NB = (NR + 31) / 32;
+  static constexpr int TM = WGM * WM, TN = WGN * WN;     // blocks per tile
+  static constexpr int TILES_M = TILES_M_, TILES_N = TILES_N_;
+  static constexpr int NW = WGM * WGN, NT = 64 * NW;
+  static constexpr int COLS = 64;                        // chunk width along W
+  static constexpr int RS = COLS * 2 + 16;               // LDS row stride (bytes)
+  static constexpr int LA_ROWS = (TM < MB ? TM : MB) * 32;
+  static constexpr int LB_ROWS = (TN < NB ? TN : NB) * 32;
+  static constexpr int LDS = (LA_ROWS + LB_ROWS) * RS;
+  static constexpr int LA_ITEMS = LA_ROWS / 8 * COLS, LB_ITEMS = LB_ROWS / 8 * COLS;
+  static constexpr int A_PER = LA_ITEMS / NT, B_PER = LB_ITEMS / NT;
+  static_assert(COUT % 8 == 0 && CIN % 8 == 0, "channel octets");
+  static_assert(LA_ITEMS % NT == 0 && LB_ITEMS % NT == 0, "loader items divide the threads");
+  static_assert(TILES_M * TM >= MB && TILES_N * TN >= NB, "tiles cover the blocks");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void wgrad_mfma(const WgArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  char* const la = lds;
+  char* const lb = lds + C::LA_ROWS * C::RS;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int ntile = C::TILES_M * C::TILES_N;
+  const int tile = blockIdx.x % ntile;
+  const int part = blockIdx.x / ntile;
+  const int m0 = (tile / C::TILES_N) * C::TM * 32;        // first A row of the tile
+  const int n0 = (tile % C::TILES_N) * C::TN * 32;        // first B row of the tile
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+
+  // rows of A/B past the real ones only feed outputs that are never stored;
+  // zero them once so they hold no stale bits
+  for (int i = tid; i < C::LDS / 16; i += C::NT) reinterpret_cast<uint4*>(lds)[i] = make_uint4(0, 0, 0, 0);
+
+  f32x16 acc[C::WM][C::WN];
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) acc[i][j] = f32x16{};
+
+  uint4 ra[C::A_PER], rb[C::B_PER];
+  // fetch chunk (row, J0) into registers
+  auto fetch = [&](int s, int n, int d, int h, int j0) {
+    const WgShard& sh = a.sh[s];
+    const uint16_t* dyb = static_cast<const uint16_t*>(sh.dy) + (int64_t)n * sh.dn +
+                          (int64_t)(d + sh.dyo[0]) * sh.ds[0] + (int64_t)(h + sh.dyo[1]) * sh.ds[1];
+    const int W = sh.ext[2];
+#pragma unroll
+    for (int q = 0; q < C::A_PER; ++q) {
+      const int item = tid + q * C::NT;
+      const int ro = item / C::COLS, j = item % C::COLS;
+      const int m = m0 + ro * 8;
+      const int tx = m / C::COUT, o = m % C::COUT;
+      const int i = j0 + j - tx;
+      const bool ok = m < C::MR && i >= 0 && i < W;
+      const int64_t off = ok ? (int64_t)(i + sh.dyo[2]) * sh.ds[2] + o : 0;
+      const uint4 v = *reinterpret_cast<const uint4*>(dyb + off);
+      ra[q] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+    const uint16_t* xb = static_cast<const uint16_t*>(sh.x) + (int64_t)n * sh.xn;
+    const int uend = W + 2 * C::P;                         // columns u with an x cell
+#pragma unroll
+    for (int q = 0; q < C::B_PER; ++q) {
+      const int item = tid + q * C::NT;
+      const int ro = item / C::COLS, j = item % C::COLS;
+      const int nn = n0 + ro * 8;
+      const int r = nn / C::CIN, c = nn % C::CIN;
+      const int tz = C::NDIM == 3 ? r / C::K : 0;
+      const int ty = C::NDIM == 3 ? r % C::K : r;
+      const int u = j0 + j;
+      const bool ok = nn < C::NR && u < uend;
+      const int64_t off = ok ? (int64_t)(d + tz + sh.xo[0]) * sh.xs[0] + (int64_t)(h + ty + sh.xo[1]) * sh.xs[1] +
+                                   (int64_t)(u + sh.xo[2]) * sh.xs[2] + c
+                             : 0;
+      const uint4 v = *reinterpret_cast<const uint4*>(xb + off);
+      rb[q] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // registers -> LDS, transposed: 8 channels of one column go to 8 rows
+  auto store = [&]() {
+#pragma unroll
+    for (int q = 0; q < C::A_PER; ++q) {
+      const int item = tid + q * C::NT;
+      const int ro = item / C::COLS, j = item % C::COLS;
+      char* p = la + (ro * 8) * C::RS + j * 2;
+      const uint32_t w4[4] = {ra[q].x, ra[q].y, ra[q].z, ra[q].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint16_t*>(p + e * C::RS) = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+    }
+#pragma unroll
+    for (int q = 0; q < C::B_PER; ++q) {
+      const int item = tid + q * C::NT;
+      const int ro = item / C::COLS, j = item % C::COLS;
+      char* p = lb + (ro * 8) * C::RS + j * 2;
+      const uint32_t w4[4] = {rb[q].x, rb[q].y, rb[q].z, rb[q].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint16_t*>(p + e * C::RS) = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+    }
+  };
+  auto compute = [&](int nks) {
+    for (int ks = 0; ks < nks; ++ks) {
+      const int colb = (ks * 16 + 8 * g2) * 2;
+      bf16x8 av[C::WM], bv[C::WN];
+#pragma unroll
+      for (int i = 0; i < C::WM; ++i)
+        av[i] = *reinterpret_cast<const bf16x8*>(la + ((wm * C::WM + i) * 32 + l32) * C::RS + colb);
+#pragma unroll
+      for (int j = 0; j < C::WN; ++j)
+        bv[j] = *reinterpret_cast<const bf16x8*>(lb + ((wn * C::WN + j) * 32 + l32) * C::RS + colb);
+#pragma unroll
+      for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::WN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // this workgroup's chunks: rows part, part + parts, ...; every chunk of a row
+  int row = part, j0 = 0;
+  bool have = row < a.total_rows;
+  int s = 0, n = 0, d = 0, h = 0;
+  if (have) {
+    decode_row(a, row, s, n, d, h);
+    fetch(s, n, d, h, 0);
+  }
+  while (have) {
+    const int uend = a.sh[s].ext[2] + 2 * C::P;
+    const int ncols = min(C::COLS, uend - j0);
+    __syncthreads();                       // previous chunk's fragment reads are done
+    store();
+    __syncthreads();
+    // next chunk: prefetch while this one computes
+    int nj0 = j0 + C::COLS, nrow = row;
+    if (nj0 >= uend) { nj0 = 0; nrow = row + a.parts; }
+    const bool nhave = nrow < a.total_rows;
+    int ns = s, nn = n, nd = d, nh = h;
+    if (nhave) {
+      if (nrow != row) decode_row(a, nrow, ns, nn, nd, nh);
+      fetch(ns, nn, nd, nh, nj0);
+    }
+    compute((ncols + 15) / 16);
+    row = nrow; j0 = nj0; have = nhave; s = ns; n = nn; d = nd; h = nh;
+  }
+
+  // partial dw of this partition: C[(tx, o)][(r, c)] -> [o][c][r * K + tx]
+  float* out = a.partial + (size_t)part * C::COUT * C::CIN * C::TAPS;
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i) {
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      const int nn = n0 + (wn * C::WN + j) * 32 + l32;
+      if (nn >= C::NR) continue;
+      const int r = nn / C::CIN, c = nn % C::CIN;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + (wm * C::WM + i) * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+        if (m >= C::MR) continue;
+        const int tx = m / C::COUT, o = m % C::COUT;
+        out[((size_t)o * C::CIN + c) * C::TAPS + r * C::K + tx] = acc[i][j][e];
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// direct kernel (fp32, and bf16 shapes without a matrix-core instance)
+// --------------------------------------------------------------------------
+
+template <typename T> __device__ __forceinline__ float ld(const T* p, int64_t i);
+template <> __device__ __forceinline__ float ld<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, int64_t i) {
+  return __uint_as_float((uint32_t)p[i] << 16);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void wgrad_direct(const WgArgs a, int ndim, int k, int cin, int cout) {
+  const int64_t taps = ndim == 3 ? (int64_t)k * k * k : (int64_t)k * k;
+  const int64_t elems = (int64_t)cout * cin * taps;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int part = blockIdx.y;
+  if (e >= elems) return;
+  const int t = (int)(e % taps);
+  const int c = (int)((e / taps) % cin);
+  const int o = (int)(e / (taps * cin));
+  const int tx = t % k, ty = (t / k) % k, tz = ndim == 3 ? t / (k * k) : 0;
+  float acc = 0.f;
+  for (int row = part; row < a.total_rows; row += a.parts) {
+    int s, n, d, h;
+    decode_row(a, row, s, n, d, h);
+    const WgShard& sh = a.sh[s];
+    const T* dyr = static_cast<const T*>(sh.dy) + (int64_t)n * sh.dn + (int64_t)(d + sh.dyo[0]) * sh.ds[0] +
+                   (int64_t)(h + sh.dyo[1]) * sh.ds[1] + (int64_t)sh.dyo[2] * sh.ds[2] + o;
+    const T* xr = static_cast<const T*>(sh.x) + (int64_t)n * sh.xn + (int64_t)(d + tz + sh.xo[0]) * sh.xs[0] +
+                  (int64_t)(h + ty + sh.xo[1]) * sh.xs[1] + (int64_t)(tx + sh.xo[2]) * sh.xs[2] + c;
+    for (int i = 0; i < sh.ext[2]; ++i) acc = fmaf(ld(dyr, (int64_t)i * sh.ds[2]), ld(xr, (int64_t)i * sh.xs[2]), acc);
+  }
+  a.partial[(size_t)part * elems + e] = acc;
+}
+
+__global__ void wgrad_reduce(const float* __restrict__ partial, int parts, int64_t elems, float* __restrict__ dw) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= elems) return;
+  double t = 0.0;
+  for (int g = 0; g < parts; ++g) t += (double)partial[(size_t)g * elems + e];
+  dw[e] = (float)t;
+}
+
+// --------------------------------------------------------------------------
+// instances and launch
+// --------------------------------------------------------------------------
+
+// image 64->64 k3: 6x6 blocks, 2x2 waves of 3x3
+using WgImg64 = WgCfg<2, 3, 64, 64, 2, 2, 3, 3, 1, 1>;
+// 3D 32->32 k3: 3x9 blocks, 1x3 waves of 3x3
+using WgVol32 = WgCfg<3, 3, 32, 32, 1, 3, 3, 3, 1, 1>;
+// 3D 16->16 k5: 3x13 blocks in two tiles of 3x8, 1x4 waves of 3x2
+using WgVol16k5 = WgCfg<3, 5, 16, 16, 1, 4, 3, 2, 1, 2>;
+// image 256->256 k3: 24x24 blocks in 4x4 tiles of 6x6, 2x2 waves of 3x3
+using WgImg256 = WgCfg<2, 3, 256, 256, 2, 2, 3, 3, 4, 4>;
+
+constexpr int kPartitions = 512;   // partial sums (workgroups per tile set)
+
+struct WgInstance {
+  int ndim, cin, cout, k;
+  int parts;                       // partitions
+  int ntile;
+  int lds;
+  int nt;
+  void (*kernel)(WgArgs);
+};
+
+template <class C>
+WgInstance make_instance() {
+  const int ntile = C::TILES_M * C::TILES_N;
+  return WgInstance{C::NDIM, C::CIN, C::COUT, C::K, std::max(1, kPartitions / ntile), ntile, C::LDS, C::NT,
+                    wgrad_mfma<C>};
+}
+
+const WgInstance* find_instance(int ndim, int cin, int cout, int k) {
+  static const WgInstance table[] = {make_instance<WgImg64>(), make_instance<WgVol32>(),
+                                     make_instance<WgVol16k5>(), make_instance<WgImg256>()};
+  for (const WgInstance& w : table)
+    if (w.ndim == ndim && w.cin == cin && w.cout == cout && w.k == k) return &w;
+  return nullptr;
+}
+
+constexpr int kDirectParts = 64;
+
+int parts_of(const st_plan* x_plan, int cout, int k) {
+  const WgInstance* w = x_plan->dtype == ST_BF16
+                            ? find_instance(x_plan->ndim, (int)x_plan->channels, cout, k) : nullptr;
+  return w ? w->parts : kDirectParts;
+}
+
+int64_t wgrad_elems(const st_plan* x_plan, int cout, int k) {
+  int64_t taps = 1;
+  for (int i = 0; i < x_plan->ndim; ++i) taps *= k;
+  return (int64_t)cout * x_plan->channels * taps;
+}
+
+}  // namespace
+}  // namespace st
+
+using namespace st;
+
+extern "C" {
+
+size_t st_conv_wgrad_workspace_bytes(const st_plan* x_plan, int32_t cout, int32_t ksize) {
+  if (!x_plan || cout < 1 || ksize < 1 || ksize % 2 == 0) return 0;
+  return (size_t)parts_of(x_plan, cout, ksize) * (size_t)wgrad_elems(x_plan, cout, ksize) * sizeof(float);
+}
+
+st_status st_conv_wgrad(const st_plan* x_plan, const void* const* x_bufs, const st_plan* dy_plan,
+                        const void* const* dy_bufs, int32_t ksize, float* dweight, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  auto err = [](st_status s, const char* m) { return fail(s, std::string("st_conv_wgrad: ") + m); };
+  if (!x_plan || !dy_plan || !x_bufs || !dy_bufs || !dweight) return err(ST_ERR_INVALID_ARG, "NULL argument");
+  if (ksize < 1 || ksize % 2 == 0) return err(ST_ERR_UNSUPPORTED, "odd kernel sizes only");
+  const int p = ksize / 2;
+  if (dy_plan->ndim != x_plan->ndim || dy_plan->batch != x_plan->batch || dy_plan->dtype != x_plan->dtype)
+    return err(ST_ERR_BAD_SHAPE, "x and dy plans differ in ndim, batch or dtype");
+  if (dy_plan->shards.size() != x_plan->shards.size()) return err(ST_ERR_BAD_SHAPE, "x and dy plans differ in shards");
+  for (size_t s = 0; s < x_plan->shards.size(); ++s)
+    for (int ax = 0; ax < kAxes; ++ax)
+      if (x_plan->shards[s].ext[ax] != dy_plan->shards[s].ext[ax] || x_plan->shards[s].off[ax] != dy_plan->shards[s].off[ax])
+        return err(ST_ERR_BAD_SHAPE, "x and dy plans differ in shard sizes");
+  for (int a = 0; a < x_plan->ndim; ++a)
+    if (x_plan->halo[axis_of(x_plan, a)] < p) return err(ST_ERR_BAD_SHAPE, "x halo smaller than ksize/2");
+  const int cin = (int)x_plan->channels, cout = (int)dy_plan->channels;
+  const int64_t elems = wgrad_elems(x_plan, cout, ksize);
+  if (elems > INT32_MAX) return err(ST_ERR_UNSUPPORTED, "weight too large");
+  const WgInstance* inst = x_plan->dtype == ST_BF16 ? find_instance(x_plan->ndim, cin, cout, ksize) : nullptr;
+  const int parts = inst ? inst->parts : kDirectParts;
+  const size_t need = (size_t)parts * (size_t)elems * sizeof(float);
+  if (!workspace || workspace_bytes < need) return err(ST_ERR_WORKSPACE, "workspace missing or too small");
+  if (!aligned16(workspace) || !aligned16(dweight)) return err(ST_ERR_ALIGNMENT, "workspace and dweight must be 16-byte aligned");
+  WgArgs a{};
+  a.nshards = (int)x_plan->shards.size();
+  a.batch = (int)x_plan->batch;
+  a.parts = parts;
+  a.partial = static_cast<float*>(workspace);
+  int64_t rows = 0;
+  for (size_t s = 0; s < x_plan->shards.size(); ++s) {
+    if (!x_bufs[s] || !dy_bufs[s]) return err(ST_ERR_INVALID_ARG, "NULL shard buffer");
+    if (!aligned16(x_bufs[s]) || !aligned16(dy_bufs[s])) return err(ST_ERR_ALIGNMENT, "shard buffers must be 16-byte aligned");
+    const Shard& xs = x_plan->shards[s];
+    const Shard& ds = dy_plan->shards[s];
+    WgShard& w = a.sh[s];
+    w.x = x_bufs[s];
+    w.dy = dy_bufs[s];
+    w.xs[2] = cin;
+    w.xs[1] = xs.pad[2] * cin;
+    w.xs[0] = xs.pad[1] * w.xs[1];
+    w.xn = xs.pad[0] * w.xs[0];
+    w.ds[2] = cout;
+    w.ds[1] = ds.pad[2] * cout;
+    w.ds[0] = ds.pad[1] * w.ds[1];
+    w.dn = ds.pad[0] * w.ds[0];
+    for (int ax = 0; ax < kAxes; ++ax) {
+      w.ext[ax] = (int32_t)xs.ext[ax];
+      // a 2D plan's leading axis has extent 1 and halo 0: its tap offset is 0
+      const bool spatial_ax = ax >= kAxes - x_plan->ndim;
+      w.xo[ax] = spatial_ax ? x_plan->halo[ax] - p : 0;
+      w.dyo[ax] = dy_plan->halo[ax];
+    }
+    w.rows_per_n = (int32_t)(xs.ext[0] * xs.ext[1]);
+    w.row_begin = (int32_t)rows;
+    rows += (int64_t)a.batch * w.rows_per_n;
+    if (rows > INT32_MAX) return err(ST_ERR_UNSUPPORTED, "volume too large");
+  }
+  a.total_rows = (int)rows;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (inst) {
+    const int grid = inst->ntile * parts;
+    hipLaunchKernelGGL(inst->kernel, dim3(grid), dim3(inst->nt), (size_t)inst->lds, st, a);
+  } else if (x_plan->dtype == ST_F32) {
+    hipLaunchKernelGGL(wgrad_direct<float>, dim3((unsigned)((elems + 255) / 256), parts), dim3(256), 0, st, a,
+                       x_plan->ndim, ksize, cin, cout);
+  } else {
+    hipLaunchKernelGGL(wgrad_direct<uint16_t>, dim3((unsigned)((elems + 255) / 256), parts), dim3(256), 0, st, a,
+                       x_plan->ndim, ksize, cin, cout);
+  }
+  st_status s = launch_check("st_conv_wgrad: launch");
+  if (s != ST_OK) return s;
+  hipLaunchKernelGGL(wgrad_reduce, dim3((unsigned)((elems + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const float*>(workspace), parts, elems, dweight);
+  return launch_check("st_conv_wgrad: reduce launch");
+}
+
+}  // extern "C"

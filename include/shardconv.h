@@ -232,6 +232,30 @@ st_status st_conv_sharded(const st_plan* in_plan, const void* const* in_bufs,
                           float* const* y_bufs, uint32_t* ymax_or_null, int32_t groups,
                           void* stream);
 
+/*
+ * st_conv_wgrad - weight gradient of st_conv_sharded, summed over all shards.
+ * The weight half of the backward pass (same passages as
+ * st_conv_dgrad_weights); every shard contributes a partial sum from its own
+ * halo-padded input, and the partials are reduced in a fixed order (the
+ * all-reduce of section 2, "Implementation details", "Communication"):
+ *   dw[o, c, t] = sum_n sum_i dy[n, i, o] * x[n, i + t - ksize/2, c]
+ *
+ *   x_plan, x_bufs     the forward call's padded inputs (halo >= ksize/2 per
+ *                      axis, margins filled by the halo exchange) (read)
+ *   dy_plan, dy_bufs   gradient at y: same ndim, batch, dtype and shard sizes,
+ *                      C = Cout, any halo (only interiors are read)
+ *   dweight            [Cout][Cin][ksize]^ndim fp32 (written)
+ *   workspace          >= st_conv_wgrad_workspace_bytes(x_plan, cout, ksize)
+ *                      bytes: per-partition partial sums
+ * bf16 operands run on the matrix cores (fp32 accumulation) for the shapes
+ * with a tuned instance, every other shape and fp32 on fp32 FMA.  The
+ * result does not depend on timing or the device, only on the shard plan.
+ */
+size_t st_conv_wgrad_workspace_bytes(const st_plan* x_plan, int32_t cout, int32_t ksize);
+st_status st_conv_wgrad(const st_plan* x_plan, const void* const* x_bufs, const st_plan* dy_plan,
+                        const void* const* dy_bufs, int32_t ksize, float* dweight, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------- GroupNorm */
 
 /*

@@ -157,6 +157,24 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert gn(q.handle, misaligned, None, 4, 1e-5, None, None, aligned, ws, need, s) == ALIGN
     assert gn(q.handle, aligned, None, 4, 1e-5, None, None, aligned, ctypes.c_void_p(0x60008), need, s) == ALIGN
     assert gn(q.handle, aligned, ctypes.c_void_p(0x70002), 4, 1e-5, None, None, aligned, ws, need, s) == ALIGN
+    # weight gradient
+    qd = hsc.st_plan_shards(2, 1, 16, [8, 8], [[4, 4], [8]], [1, 1], "bf16")      # dy, any halo
+    need_w = L.st_conv_wgrad_workspace_bytes(p.handle, 16, 3)
+    assert need_w > 0 and L.st_conv_wgrad_workspace_bytes(p.handle, 16, 2) == 0
+    dw = ctypes.c_void_p(0xB0000)
+    wws = ctypes.c_void_p(0xC0000)
+    wg = L.st_conv_wgrad
+    assert wg(None, aligned, qd.handle, aligned, 3, dw, wws, need_w, s) == INVALID
+    assert wg(p.handle, aligned, qd.handle, aligned, 3, None, wws, need_w, s) == INVALID
+    assert wg(p.handle, aligned, qd.handle, aligned, 4, dw, wws, need_w, s) == UNSUPPORTED
+    assert wg(p.handle, aligned, qd.handle, aligned, 5, dw, wws, need_w, s) == BAD_SHAPE     # halo 1 < 2
+    assert wg(p.handle, aligned, q.handle, aligned, 3, dw, wws, need_w, s) == BAD_SHAPE      # dtype differs
+    assert wg(p.handle, aligned, q_bad.handle, aligned, 3, dw, wws, need_w, s) == BAD_SHAPE
+    assert wg(p.handle, aligned, qd.handle, aligned, 3, dw, wws, need_w - 1, s) == WORKSPACE
+    assert wg(p.handle, aligned, qd.handle, aligned, 3, dw, None, need_w, s) == WORKSPACE
+    assert wg(p.handle, misaligned, qd.handle, aligned, 3, dw, wws, need_w, s) == ALIGN
+    assert wg(p.handle, aligned, qd.handle, nulls, 3, dw, wws, need_w, s) == INVALID
+    assert wg(p.handle, aligned, qd.handle, aligned, 3, ctypes.c_void_p(0xB0004), wws, need_w, s) == ALIGN
     # groupnorm backward
     bneed = L.st_groupnorm_backward_workspace_bytes(q.handle, 4)
     assert bneed > 0 and L.st_groupnorm_backward_workspace_bytes(None, 4) == 0
