@@ -23,6 +23,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sharded conv+GroupNorm voxels/s on 1 MI355X; % MFMA peak (conv), % HBM BW (halo/norm)"
 METRIC_DGRAD = "sharded conv input-gradient (halo exchange of dy + conv) voxels/s on 1 MI355X"
+METRIC_BWD = ("sharded conv+GroupNorm backward (GroupNorm backward, halo exchange of dy, input gradient, "
+              "weight gradient) voxels/s on 1 MI355X")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 (256 CU x 2.4 GHz x 4096 flop/clk)
 FP32_PEAK_TFLOPS = 157.3
@@ -34,8 +36,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--pass", dest="pass_", choices=("forward", "dgrad"), default="forward",
-                    help="the layer's forward step, or the input gradient of its conv")
+    ap.add_argument("--pass", dest="pass_", choices=("forward", "dgrad", "backward"), default="forward",
+                    help="the layer's forward step, the input gradient of its conv, or its whole backward step")
     ap.add_argument("--exchange", choices=("pack+unpack", "fused"), default="pack+unpack",
                     help="halo exchange as two copies through a message buffer, or one fused copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -51,8 +53,9 @@ def parse():
 COPY_BYTES = 1 << 30                 # bytes read (and written) by --calibrate-copy
 STAGE_KERNELS = {                    # kernel-name fragments of each library stage
     "halo_pack": ("halo_copy",), "halo_unpack": ("halo_copy",), "halo_exchange": ("halo_copy",),
-    "conv": ("conv_rows", "conv_ring", "conv_mfma", "conv_direct"),
+    "conv": ("conv_rows", "conv_pairs", "conv_gemm", "conv_direct"),
     "gn_partials": ("gn_max", "gn_stats"), "gn_apply": ("gn_apply",),
+    "wgrad": ("wgrad_mfma", "wgrad_direct"), "gn_backward": ("gn_max", "gnb_"),
 }
 
 
@@ -61,6 +64,7 @@ STAGE_SOURCES = {                    # library sources that define each stage's 
     "halo_exchange": ("halo.hip", "plan.cpp", "internal.h"),
     "conv": ("conv.hip", "internal.h"),
     "gn_partials": ("groupnorm.hip", "internal.h"), "gn_apply": ("groupnorm.hip", "internal.h"),
+    "wgrad": ("wgrad.hip", "internal.h"), "gn_backward": ("groupnorm.hip", "internal.h"),
 }
 
 
@@ -170,13 +174,21 @@ def algorithmic(wl, layer):
         "gn_partials": {"bytes": y_bytes},
         "gn_combine": {"bytes": 0},
         "gn_apply": {"bytes": 2 * y_bytes},
+        # max |dz|, then (y, dz) for the sums, then (y, dz) -> dy
+        "gn_backward": {"bytes": 6 * y_bytes},
+        # x and dy (operand type) read, dw written
+        "wgrad": {"bytes": x_bytes + vox * wl.cout * esize + wl.cout * wl.cin * wl.taps * 4,
+                  "flops": wl.conv_flops},
     }
 
 
-def cpu_baseline(wl, rows, w_fwd=None):
+def cpu_baseline(wl, rows, w_fwd=None, backward=False):
     """The oracle (fp64 numpy) on the first `rows` rows of the outermost axis:
     conv + GroupNorm, or (w_fwd given: wl is the input-gradient layer) the
-    input gradient of the forward conv."""
+    input gradient of the forward conv, or (backward) the layer's backward
+    step: GroupNorm backward, input gradient and weight gradient."""
+    if backward:
+        return cpu_baseline_backward(wl, rows)
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -204,6 +216,33 @@ def cpu_baseline(wl, rows, w_fwd=None):
                       + f" in fp64 numpy, {dt:.1f} s)", "seconds": round(dt, 2), "checksum": float(np.abs(z).sum())}
 
 
+def cpu_baseline_backward(wl, rows):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import synth
+    from halo_sharded_conv_amd.layer import dgrad_config
+
+    sub_shape = (rows,) + tuple(wl.spatial[1:])
+    sub = synth.small_variant(wl, sub_shape, [(s,) for s in sub_shape], name_suffix="cpu_sample")
+    x = oracle.widen(synth.make_input(sub), wl.dtype)
+    w = oracle.widen(synth.make_weight(wl), wl.dtype)
+    y = oracle.conv_same(x, w)
+    dz = synth.make_upstream_grad(sub, seed=31)
+    dyc = oracle.widen(synth.make_input(dgrad_config(sub)), wl.dtype)
+    t0 = time.perf_counter()
+    dy, dg, db = oracle.group_norm_backward(y, dz, wl.groups, wl.eps)
+    dx = oracle.conv_same_dgrad(dyc, w)
+    dw = oracle.conv_same_wgrad(x, dyc, wl.ksize)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": sub.voxels / dt, "unit": "voxels/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} rows of the outermost axis ({sub.voxels} voxels, GroupNorm backward + input "
+                      f"gradient + weight gradient in fp64 numpy, {dt:.1f} s)", "seconds": round(dt, 2),
+            "checksum": float(np.abs(dy).sum() + np.abs(dx).sum() + np.abs(dw).sum())}
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -224,6 +263,8 @@ def main():
 
     name = args.workload or synth.BENCH_WORKLOAD
     wl_fwd = synth.workload(name)
+    if args.pass_ == "backward":
+        return bench_backward(args, wl_fwd)
     if args.pass_ == "dgrad":
         # input gradient of the layer's conv: dy (Cout channels) -> dx (Cin)
         from halo_sharded_conv_amd.layer import dgrad_config
@@ -246,11 +287,20 @@ def main():
         stages += [("gn_partials", layer.norm_partials), ("gn_combine", layer.norm_combine),
                    ("gn_apply", layer.norm_apply)]
 
+    per_kernel_ms, ms_per_step, gpu_ms = time_stages(args, stages, stream)
+
+    report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, METRIC if args.pass_ == "forward" else METRIC_DGRAD,
+           None if args.pass_ == "forward" else synth.make_weight(wl_fwd))
+
+
+def time_stages(args, stages, stream):
+    """Warm-up, then K timed steps; HIP events around every stage on its stream."""
+    import numpy as np
+    import torch
     for _ in range(args.warmup):
         for _, fn in stages:
             fn()
     torch.cuda.synchronize()
-
     ev = {k: [] for k, _ in stages}
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
@@ -268,10 +318,57 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(end) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
     per_kernel_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+    return per_kernel_ms, wall * 1e3 / args.steps, gpu_ms
 
+
+def bench_backward(args, wl_fwd):
+    """The layer's backward step: GroupNorm backward (dz -> dy at the conv
+    output), halo exchange of dy, input gradient (conv with the transposed,
+    flipped weights) and weight gradient.  The forward step runs once before
+    timing (it leaves y, the statistics and the exchanged x).  The conv
+    stages read a bf16 dy drawn like the forward input: casting the fp32
+    GroupNorm gradient to bf16 shards is not part of the library."""
+    import torch
+
+    import halo_sharded_conv_amd as hsc
+    import synth
+    from halo_sharded_conv_amd.layer import ShardedConvGN, dgrad_config
+
+    wl = wl_fwd
+    fwd = ShardedConvGN(wl)
+    w = synth.make_weight(wl)
+    fwd.set_weight(w)
+    fwd.load_input(synth.make_input(wl))
+    fwd.step()
+    fwd.alloc_backward()
+    fwd.load_upstream_grad(synth.make_upstream_grad(wl, seed=31))
+    bwd = ShardedConvGN(dgrad_config(wl))
+    bwd.set_weight_dgrad(w)
+    bwd.load_input(synth.make_input(dgrad_config(wl)))
+    dw = torch.empty(wl.cout * wl.cin * wl.taps, dtype=torch.float32, device="cuda")
+    wws = torch.empty(hsc.st_conv_wgrad_workspace_bytes(fwd.in_plan, wl.cout, wl.ksize), dtype=torch.uint8,
+                      device="cuda")
+    torch.cuda.synchronize()
+    if args.exchange == "fused":
+        halo = [("halo_exchange", lambda: bwd.exchange_fused())]
+    else:
+        halo = [("halo_pack", lambda: bwd.exchange_pack()), ("halo_unpack", lambda: bwd.exchange_unpack())]
+    stages = [("gn_backward", fwd.norm_backward)] + halo + [
+        ("conv", bwd.conv),
+        ("wgrad", lambda: hsc.st_conv_wgrad(fwd.in_plan, fwd.x_bufs, bwd.in_plan, bwd.x_bufs, wl.ksize, dw, wws))]
+    per_kernel_ms, ms_per_step, gpu_ms = time_stages(args, stages, torch.cuda.current_stream())
+    report(args, wl, fwd, per_kernel_ms, ms_per_step, gpu_ms, METRIC_BWD, None, dgrad_layer=bwd)
+
+
+def report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, metric, w_fwd, dgrad_layer=None):
+    """One JSON line: throughput, per-stage rates and the longest stage against its roofline."""
     alg = algorithmic(wl, layer)
+    if dgrad_layer is not None:
+        # the exchange and the conv run on the input-gradient layer
+        d_alg = algorithmic(dgrad_layer.cfg, dgrad_layer)
+        for k in ("halo_pack", "halo_unpack", "halo_exchange", "conv"):
+            alg[k] = d_alg[k]
     kernels = {}
     for k, ms in per_kernel_ms.items():
         rec = {"ms": round(ms, 5)}
@@ -285,15 +382,14 @@ def main():
         kernels[k] = rec
 
     dom = max(per_kernel_ms, key=per_kernel_ms.get)
-    ms = per_kernel_ms[dom]
-    if dom == "conv":
-        conv_ai = alg["conv"]["flops"] / alg["conv"]["bytes"]
+    if alg[dom].get("flops"):
+        ai = alg[dom]["flops"] / alg[dom]["bytes"]
         peak_t = FP32_PEAK_TFLOPS if wl.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
         ridge = peak_t * 1e12 / (HBM_PEAK_GBS * 1e9)
-        if conv_ai < ridge:
-            roof = {"bound": "hbm", "achieved": kernels["conv"]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        if ai < ridge:
+            roof = {"bound": "hbm", "achieved": kernels[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
         else:
-            roof = {"bound": "mfma", "achieved": kernels["conv"]["TFLOP/s"], "peak": peak_t, "unit": "TFLOP/s"}
+            roof = {"bound": "mfma", "achieved": kernels[dom]["TFLOP/s"], "peak": peak_t, "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": kernels[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
@@ -301,7 +397,7 @@ def main():
     roof["traffic"] = load_traffic(wl, dom)
 
     out = {
-        "metric": METRIC if args.pass_ == "forward" else METRIC_DGRAD,
+        "metric": metric,
         "value": wl.voxels / (ms_per_step * 1e-3),
         "unit": "voxels/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -318,7 +414,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         rows = args.cpu_rows or max(1, min(wl.spatial[0], int(5.0e5 // (wl.voxels // wl.spatial[0]) + 1)))
-        out["cpu_baseline"] = cpu_baseline(wl, rows, None if args.pass_ == "forward" else synth.make_weight(wl_fwd))
+        out["cpu_baseline"] = cpu_baseline(wl, rows, w_fwd, backward=args.pass_ == "backward")
     print(json.dumps(out), flush=True)
 
 
