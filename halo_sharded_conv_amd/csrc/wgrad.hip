@@ -25,8 +25,8 @@
 // consecutive K values are one 16-byte read; A holds dy once per tx shift, so
 // every fragment read is aligned.
 //
-// A workgroup owns a tile of 32x32 output blocks and a fixed share of the
-// rows (row j goes to partition j mod GP), accumulating over all of them in
+// A workgroup owns a tile of 32x32 output blocks and a fixed contiguous band
+// of the rows (partition p of GP), accumulating over all of them in
 // registers, then stores its partial dw.  The reduction sums the GP partials
 // in partition order in fp64: the result does not depend on the device, the
 // launch or timing, only on the shard plan (for another plan the rows fall
@@ -93,24 +93,84 @@ struct WgCfg {
   static constexpr int TILES_M = TILES_M_, TILES_N = TILES_N_;
   static constexpr int NW = WGM * WGN, NT = 64 * NW;
   static constexpr int COLS = 64;                        // chunk width along W
-  static constexpr int RS = COLS * 2 + 16;               // LDS row stride (bytes)
+  static constexpr int RS = COLS * 2;                    // LDS row stride (bytes), 16-byte slots permuted
+  static_assert(RS == 128, "8 slots of 16 bytes per row");
   static constexpr int LA_ROWS = (TM < MB ? TM : MB) * 32;
   static constexpr int LB_ROWS = (TN < NB ? TN : NB) * 32;
   static constexpr int LDS = (LA_ROWS + LB_ROWS) * RS;
-  static constexpr int LA_ITEMS = LA_ROWS / 8 * COLS, LB_ITEMS = LB_ROWS / 8 * COLS;
-  static constexpr int A_PER = LA_ITEMS / NT, B_PER = LB_ITEMS / NT;
+  // loader: one wave instruction moves OG channel octets of 64 / OG columns
+  static constexpr int OCT_A = LA_ROWS / 8, OCT_B = LB_ROWS / 8;
+  // an octet group stays inside one tap shift (A) or one tap row (B)
+  static constexpr int OG_A = COUT / 8 < 8 ? COUT / 8 : 8;
+  static constexpr int OG_B = CIN / 8 < 8 ? CIN / 8 : 8;
+  static constexpr int G_A = OCT_A / OG_A, G_B = OCT_B / OG_B;   // octet groups
+  static constexpr int JG_A = 64 / OG_A, JG_B = 64 / OG_B;       // columns per loader instruction
+  static constexpr int A_PER = OCT_A / NW, B_PER = OCT_B / NW;
   static_assert(COUT % 8 == 0 && CIN % 8 == 0, "channel octets");
-  static_assert(LA_ITEMS % NT == 0 && LB_ITEMS % NT == 0, "loader items divide the threads");
+  static_assert(OCT_A % NW == 0 && OCT_B % NW == 0, "loader instructions divide the waves");
+  static_assert(OCT_A % OG_A == 0 && OCT_B % OG_B == 0, "octet groups");
+  static_assert(COUT % (8 * OG_A) == 0 && CIN % (8 * OG_B) == 0 && (TM * 32) % (8 * OG_A) == 0 &&
+                (TN * 32) % (8 * OG_B) == 0, "octet groups do not straddle taps");
   static_assert(TILES_M * TM >= MB && TILES_N * TN >= NB, "tiles cover the blocks");
 };
 
+// 16-byte slot permutation of LDS row r (8 slots of a 128-byte row)
+__device__ __forceinline__ int wg_key(int r) { return ((r >> 1) ^ (r >> 3)) & 7; }
+
+struct WgChunk {
+  int row, j0;
+  bool valid;
+  // per row (uniform): dy at (n, d, h, column 0), x at (n, d, h) for tap
+  // (0, 0) and column u = 0, the shard's x strides and row length
+  const uint16_t* dyrow;
+  const uint16_t* xrow;
+  int32_t xs0, xs1, W;
+};
+
+// Partition p owns the contiguous band of rows [p * R / P, (p + 1) * R / P):
+// neighbouring output rows share x rows, which a band then reads from the
+// same L2.
+__device__ __forceinline__ int band_begin(const WgArgs& a, int p) {
+  return (int)(((int64_t)p * a.total_rows) / a.parts);
+}
+
+__device__ __forceinline__ WgChunk first_chunk(const WgArgs& a, int row, int row_end) {
+  WgChunk c{};
+  c.row = row;
+  c.j0 = 0;
+  c.valid = row < row_end;
+  int s = 0, n = 0, d = 0, h = 0;
+  if (c.valid) decode_row(a, row, s, n, d, h);
+  const WgShard& sh = a.sh[s];
+  c.dyrow = static_cast<const uint16_t*>(sh.dy) + (int64_t)n * sh.dn + (int64_t)(d + sh.dyo[0]) * sh.ds[0] +
+            (int64_t)(h + sh.dyo[1]) * sh.ds[1] + (int64_t)sh.dyo[2] * sh.ds[2];
+  c.xrow = static_cast<const uint16_t*>(sh.x) + (int64_t)n * sh.xn + (int64_t)(d + sh.xo[0]) * sh.xs[0] +
+           (int64_t)(h + sh.xo[1]) * sh.xs[1] + (int64_t)sh.xo[2] * sh.xs[2];
+  c.xs0 = (int32_t)sh.xs[0];
+  c.xs1 = (int32_t)sh.xs[1];
+  c.W = sh.ext[2];
+  return c;
+}
+
+// the chunk after c: 64 columns further along the row, else the band's next row
+template <int K>
+__device__ __forceinline__ WgChunk next_chunk(const WgArgs& a, WgChunk c, int cols, int row_end) {
+  if (!c.valid) return c;
+  if (c.j0 + cols < c.W + 2 * (K / 2)) {
+    c.j0 += cols;
+    return c;
+  }
+  return first_chunk(a, c.row + 1, row_end);
+}
+
 template <class C>
 __global__ __launch_bounds__(C::NT) void wgrad_mfma(const WgArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  char* const la = lds;
-  char* const lb = lds + C::LA_ROWS * C::RS;
+  // two LDS stages: the MFMAs read one while the other is written (1 KiB
+  // aligned: the slot permutation XORs address bits 4-6)
+  __shared__ __attribute__((aligned(1024))) char stage0[C::LDS];
+  __shared__ __attribute__((aligned(1024))) char stage1[C::LDS];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g2 = lane >> 5;
   const int ntile = C::TILES_M * C::TILES_N;
   const int tile = blockIdx.x % ntile;
@@ -119,120 +179,129 @@ __global__ __launch_bounds__(C::NT) void wgrad_mfma(const WgArgs a) {
   const int n0 = (tile % C::TILES_N) * C::TN * 32;        // first B row of the tile
   const int wm = wave / C::WGN, wn = wave % C::WGN;
 
-  // rows of A/B past the real ones only feed outputs that are never stored;
-  // zero them once so they hold no stale bits
-  for (int i = tid; i < C::LDS / 16; i += C::NT) reinterpret_cast<uint4*>(lds)[i] = make_uint4(0, 0, 0, 0);
-
   f32x16 acc[C::WM][C::WN];
 #pragma unroll
   for (int i = 0; i < C::WM; ++i)
 #pragma unroll
     for (int j = 0; j < C::WN; ++j) acc[i][j] = f32x16{};
 
-  uint4 ra[C::A_PER], rb[C::B_PER];
-  // fetch chunk (row, J0) into registers
-  auto fetch = [&](int s, int n, int d, int h, int j0) {
-    const WgShard& sh = a.sh[s];
-    const uint16_t* dyb = static_cast<const uint16_t*>(sh.dy) + (int64_t)n * sh.dn +
-                          (int64_t)(d + sh.dyo[0]) * sh.ds[0] + (int64_t)(h + sh.dyo[1]) * sh.ds[1];
-    const int W = sh.ext[2];
+  uint4 ra0[C::A_PER], rb0[C::B_PER], ra1[C::A_PER], rb1[C::B_PER];
+  // Loader instruction k (k = wave + q * NW) of a chunk covers octet group
+  // g = k % G (OG octet rows, all in one tap shift or tap row) at column group
+  // jg = k / G (64 / OG columns); lane l takes octet l % OG of column l / OG,
+  // so OG lanes read one contiguous run of channels.  Everything but the lane
+  // terms is wave-uniform.
+  auto fetch = [&](const WgChunk& ch, uint4 (&qa)[C::A_PER], uint4 (&qb)[C::B_PER]) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < C::A_PER; ++q) {
-      const int item = tid + q * C::NT;
-      const int ro = item / C::COLS, j = item % C::COLS;
-      const int m = m0 + ro * 8;
-      const int tx = m / C::COUT, o = m % C::COUT;
-      const int i = j0 + j - tx;
-      const bool ok = m < C::MR && i >= 0 && i < W;
-      const int64_t off = ok ? (int64_t)(i + sh.dyo[2]) * sh.ds[2] + o : 0;
-      const uint4 v = *reinterpret_cast<const uint4*>(dyb + off);
-      ra[q] = ok ? v : make_uint4(0, 0, 0, 0);
+      const int k = wave + q * C::NW;
+      const int mb = m0 + (k % C::G_A) * (8 * C::OG_A);          // first A row of the group
+      const int tx = mb / C::COUT;
+      const int i = ch.j0 + (k / C::G_A) * C::JG_A - tx + lane / C::OG_A;
+      const bool ok = ch.valid && mb < C::MR && (unsigned)i < (unsigned)ch.W;
+      const int off = ok ? i * C::COUT + (mb % C::COUT) + 8 * (lane % C::OG_A) : 0;
+      const uint4 v = *reinterpret_cast<const uint4*>(ch.dyrow + off);
+      qa[q] = ok ? v : make_uint4(0, 0, 0, 0);
     }
-    const uint16_t* xb = static_cast<const uint16_t*>(sh.x) + (int64_t)n * sh.xn;
-    const int uend = W + 2 * C::P;                         // columns u with an x cell
+    const int uend = ch.W + 2 * C::P;                       // columns u with an x cell
 #pragma unroll
     for (int q = 0; q < C::B_PER; ++q) {
-      const int item = tid + q * C::NT;
-      const int ro = item / C::COLS, j = item % C::COLS;
-      const int nn = n0 + ro * 8;
-      const int r = nn / C::CIN, c = nn % C::CIN;
+      const int k = wave + q * C::NW;
+      const int nb = n0 + (k % C::G_B) * (8 * C::OG_B);          // first B row of the group
+      const int r = nb / C::CIN;
       const int tz = C::NDIM == 3 ? r / C::K : 0;
       const int ty = C::NDIM == 3 ? r % C::K : r;
-      const int u = j0 + j;
-      const bool ok = nn < C::NR && u < uend;
-      const int64_t off = ok ? (int64_t)(d + tz + sh.xo[0]) * sh.xs[0] + (int64_t)(h + ty + sh.xo[1]) * sh.xs[1] +
-                                   (int64_t)(u + sh.xo[2]) * sh.xs[2] + c
-                             : 0;
-      const uint4 v = *reinterpret_cast<const uint4*>(xb + off);
-      rb[q] = ok ? v : make_uint4(0, 0, 0, 0);
+      const int u = ch.j0 + (k / C::G_B) * C::JG_B + lane / C::OG_B;
+      const bool ok = ch.valid && nb < C::NR && u < uend;
+      const int off = ok ? tz * ch.xs0 + ty * ch.xs1 + u * C::CIN + (nb % C::CIN) + 8 * (lane % C::OG_B) : 0;
+      const uint4 v = *reinterpret_cast<const uint4*>(ch.xrow + off);
+      qb[q] = ok ? v : make_uint4(0, 0, 0, 0);
     }
   };
-  // registers -> LDS, transposed: 8 channels of one column go to 8 rows
-  auto store = [&]() {
+  // registers -> LDS, transposed: the 8 channels of a column go to 8 rows.
+  // Row r keeps its 16-byte column slots permuted by key(r) = ((r >> 1) ^
+  // (r >> 3)) & 7, so that both the 8-row column writes and the 32-row
+  // fragment reads spread over the banks.  For r = 8 ro + e the key is
+  // (4 ro ^ ro ^ (e >> 1)) & 7, so one base address per item serves all 8 rows.
+  auto put = [&](char* base, int ro, int j, const uint4& v) __attribute__((always_inline)) {
+    const int slot = ((j >> 3) ^ ro ^ (ro << 2)) & 7;
+    char* p = base + ro * 8 * C::RS + (slot << 4) + (j & 7) * 2;
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      char* pe = reinterpret_cast<char*>(reinterpret_cast<uintptr_t>(p) ^ (uintptr_t)((e >> 1) << 4)) + e * C::RS;
+      *reinterpret_cast<uint16_t*>(pe) = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+    }
+  };
+  auto store = [&](char* st, const uint4 (&qa)[C::A_PER], const uint4 (&qb)[C::B_PER]) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < C::A_PER; ++q) {
-      const int item = tid + q * C::NT;
-      const int ro = item / C::COLS, j = item % C::COLS;
-      char* p = la + (ro * 8) * C::RS + j * 2;
-      const uint32_t w4[4] = {ra[q].x, ra[q].y, ra[q].z, ra[q].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint16_t*>(p + e * C::RS) = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+      const int k = wave + q * C::NW;
+      put(st, (k % C::G_A) * C::OG_A + lane % C::OG_A, (k / C::G_A) * C::JG_A + lane / C::OG_A, qa[q]);
     }
 #pragma unroll
     for (int q = 0; q < C::B_PER; ++q) {
-      const int item = tid + q * C::NT;
-      const int ro = item / C::COLS, j = item % C::COLS;
-      char* p = lb + (ro * 8) * C::RS + j * 2;
-      const uint32_t w4[4] = {rb[q].x, rb[q].y, rb[q].z, rb[q].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint16_t*>(p + e * C::RS) = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+      const int k = wave + q * C::NW;
+      put(st + C::LA_ROWS * C::RS, (k % C::G_B) * C::OG_B + lane % C::OG_B, (k / C::G_B) * C::JG_B + lane / C::OG_B,
+          qb[q]);
     }
   };
-  auto compute = [&](int nks) {
-    for (int ks = 0; ks < nks; ++ks) {
-      const int colb = (ks * 16 + 8 * g2) * 2;
-      bf16x8 av[C::WM], bv[C::WN];
+  auto kstep = [&](const char* st, int ks) __attribute__((always_inline)) {
+    const char* la = st;
+    const char* lb = st + C::LA_ROWS * C::RS;
+    const int slot = ks * 2 + g2;                          // 16-byte column slot of this lane
+    bf16x8 av[C::WM], bv[C::WN];
 #pragma unroll
-      for (int i = 0; i < C::WM; ++i)
-        av[i] = *reinterpret_cast<const bf16x8*>(la + ((wm * C::WM + i) * 32 + l32) * C::RS + colb);
+    for (int i = 0; i < C::WM; ++i) {
+      const int row = (wm * C::WM + i) * 32 + l32;
+      av[i] = *reinterpret_cast<const bf16x8*>(la + row * C::RS + ((slot ^ wg_key(row)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      const int row = (wn * C::WN + j) * 32 + l32;
+      bv[j] = *reinterpret_cast<const bf16x8*>(lb + row * C::RS + ((slot ^ wg_key(row)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i)
 #pragma unroll
       for (int j = 0; j < C::WN; ++j)
-        bv[j] = *reinterpret_cast<const bf16x8*>(lb + ((wn * C::WN + j) * 32 + l32) * C::RS + colb);
-#pragma unroll
-      for (int i = 0; i < C::WM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::WN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-    }
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
   };
 
-  // this workgroup's chunks: rows part, part + parts, ...; every chunk of a row
-  int row = part, j0 = 0;
-  bool have = row < a.total_rows;
-  int s = 0, n = 0, d = 0, h = 0;
-  if (have) {
-    decode_row(a, row, s, n, d, h);
-    fetch(s, n, d, h, 0);
-  }
-  while (have) {
-    const int uend = a.sh[s].ext[2] + 2 * C::P;
-    const int ncols = min(C::COLS, uend - j0);
-    __syncthreads();                       // previous chunk's fragment reads are done
-    store();
-    __syncthreads();
-    // next chunk: prefetch while this one computes
-    int nj0 = j0 + C::COLS, nrow = row;
-    if (nj0 >= uend) { nj0 = 0; nrow = row + a.parts; }
-    const bool nhave = nrow < a.total_rows;
-    int ns = s, nn = n, nd = d, nh = h;
-    if (nhave) {
-      if (nrow != row) decode_row(a, nrow, ns, nn, nd, nh);
-      fetch(ns, nn, nd, nh, nj0);
+  // chunks of this partition: c0 in stage0, c1 staged in registers
+  const int row_end = band_begin(a, part + 1);
+  WgChunk c0 = first_chunk(a, band_begin(a, part), row_end);
+  WgChunk c1 = next_chunk<C::K>(a, c0, C::COLS, row_end);
+  fetch(c0, ra0, rb0);
+  fetch(c1, ra1, rb1);
+  store(stage0, ra0, rb0);
+  __syncthreads();
+  // one chunk per phase; the loop body handles two so that stages and
+  // register sets alternate at compile time
+  auto phase = [&](auto P) __attribute__((always_inline)) {
+    constexpr int par = decltype(P)::value;
+    char* const cur = par ? stage1 : stage0;
+    char* const nxt = par ? stage0 : stage1;
+    const WgChunk c2 = next_chunk<C::K>(a, c1, C::COLS, row_end);
+    if constexpr (par == 0) fetch(c2, ra0, rb0);           // two chunks ahead
+    else fetch(c2, ra1, rb1);
+    const int nks = (min(C::COLS, c0.W + 2 * C::P - c0.j0) + 15) / 16;
+    kstep(cur, 0);
+    if (c1.valid) {                                         // the next chunk, during this one's MFMAs
+      if constexpr (par == 0) store(nxt, ra1, rb1);
+      else store(nxt, ra0, rb0);
     }
-    compute((ncols + 15) / 16);
-    row = nrow; j0 = nj0; have = nhave; s = ns; n = nn; d = nd; h = nh;
+#pragma unroll
+    for (int ks = 1; ks < C::COLS / 16; ++ks)
+      if (ks < nks) kstep(cur, ks);
+    __syncthreads();
+    c0 = c1;
+    c1 = c2;
+  };
+  while (c0.valid) {
+    phase(std::integral_constant<int, 0>{});
+    if (!c0.valid) break;
+    phase(std::integral_constant<int, 1>{});
   }
 
   // partial dw of this partition: C[(tx, o)][(r, c)] -> [o][c][r * K + tx]
@@ -311,7 +380,7 @@ using WgVol16k5 = WgCfg<3, 5, 16, 16, 1, 4, 3, 2, 1, 2>;
 // image 256->256 k3: 24x24 blocks in 4x4 tiles of 6x6, 2x2 waves of 3x3
 using WgImg256 = WgCfg<2, 3, 256, 256, 2, 2, 3, 3, 4, 4>;
 
-constexpr int kPartitions = 512;   // partial sums (workgroups per tile set)
+constexpr int kPartitions = 256;   // partial sums (workgroups per tile set): one per CU
 
 struct WgInstance {
   int ndim, cin, cout, k;
@@ -425,7 +494,7 @@ st_status st_conv_wgrad(const st_plan* x_plan, const void* const* x_bufs, const 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (inst) {
     const int grid = inst->ntile * parts;
-    hipLaunchKernelGGL(inst->kernel, dim3(grid), dim3(inst->nt), (size_t)inst->lds, st, a);
+    hipLaunchKernelGGL(inst->kernel, dim3(grid), dim3(inst->nt), 0, st, a);
   } else if (x_plan->dtype == ST_F32) {
     hipLaunchKernelGGL(wgrad_direct<float>, dim3((unsigned)((elems + 255) / 256), parts), dim3(256), 0, st, a,
                        x_plan->ndim, ksize, cin, cout);
