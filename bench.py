@@ -174,8 +174,8 @@ def algorithmic(wl, layer):
         "gn_partials": {"bytes": y_bytes},
         "gn_combine": {"bytes": 0},
         "gn_apply": {"bytes": 2 * y_bytes},
-        # max |dz|, then (y, dz) for the sums, then (y, dz) -> dy
-        "gn_backward": {"bytes": 6 * y_bytes},
+        # max |dz|, then (y, dz) for the sums, then (y, dz) -> dy in the conv's operand type
+        "gn_backward": {"bytes": 5 * y_bytes + vox * wl.cout * esize},
         # x and dy (operand type) read, dw written
         "wgrad": {"bytes": x_bytes + vox * wl.cout * esize + wl.cout * wl.cin * wl.taps * 4,
                   "flops": wl.conv_flops},
@@ -222,17 +222,16 @@ def cpu_baseline_backward(wl, rows):
 
     import oracle
     import synth
-    from halo_sharded_conv_amd.layer import dgrad_config
-
     sub_shape = (rows,) + tuple(wl.spatial[1:])
     sub = synth.small_variant(wl, sub_shape, [(s,) for s in sub_shape], name_suffix="cpu_sample")
     x = oracle.widen(synth.make_input(sub), wl.dtype)
     w = oracle.widen(synth.make_weight(wl), wl.dtype)
     y = oracle.conv_same(x, w)
     dz = synth.make_upstream_grad(sub, seed=31)
-    dyc = oracle.widen(synth.make_input(dgrad_config(sub)), wl.dtype)
     t0 = time.perf_counter()
     dy, dg, db = oracle.group_norm_backward(y, dz, wl.groups, wl.eps)
+    # the conv backward takes dy in the operand type
+    dyc = oracle.widen(synth.f32_to_bf16_bits(dy.astype(np.float32)), wl.dtype) if wl.dtype == "bf16" else dy
     dx = oracle.conv_same_dgrad(dyc, w)
     dw = oracle.conv_same_wgrad(x, dyc, wl.ksize)
     dt = time.perf_counter() - t0
@@ -324,11 +323,11 @@ def time_stages(args, stages, stream):
 
 def bench_backward(args, wl_fwd):
     """The layer's backward step: GroupNorm backward (dz -> dy at the conv
-    output), halo exchange of dy, input gradient (conv with the transposed,
-    flipped weights) and weight gradient.  The forward step runs once before
-    timing (it leaves y, the statistics and the exchanged x).  The conv
-    stages read a bf16 dy drawn like the forward input: casting the fp32
-    GroupNorm gradient to bf16 shards is not part of the library."""
+    output, written in the conv's operand type straight into the halo-padded
+    shards of the input-gradient conv), halo exchange of dy, input gradient
+    (conv with the transposed, flipped weights) and weight gradient.  The
+    forward step runs once before timing (it leaves y, the statistics and the
+    exchanged x)."""
     import torch
 
     import halo_sharded_conv_amd as hsc
@@ -345,7 +344,6 @@ def bench_backward(args, wl_fwd):
     fwd.load_upstream_grad(synth.make_upstream_grad(wl, seed=31))
     bwd = ShardedConvGN(dgrad_config(wl))
     bwd.set_weight_dgrad(w)
-    bwd.load_input(synth.make_input(dgrad_config(wl)))
     dw = torch.empty(wl.cout * wl.cin * wl.taps, dtype=torch.float32, device="cuda")
     wws = torch.empty(hsc.st_conv_wgrad_workspace_bytes(fwd.in_plan, wl.cout, wl.ksize), dtype=torch.uint8,
                       device="cuda")
@@ -354,7 +352,7 @@ def bench_backward(args, wl_fwd):
         halo = [("halo_exchange", lambda: bwd.exchange_fused())]
     else:
         halo = [("halo_pack", lambda: bwd.exchange_pack()), ("halo_unpack", lambda: bwd.exchange_unpack())]
-    stages = [("gn_backward", fwd.norm_backward)] + halo + [
+    stages = [("gn_backward", lambda: fwd.norm_backward(dy_bufs=bwd.x_bufs, dy_plan=bwd.in_plan))] + halo + [
         ("conv", bwd.conv),
         ("wgrad", lambda: hsc.st_conv_wgrad(fwd.in_plan, fwd.x_bufs, bwd.in_plan, bwd.x_bufs, wl.ksize, dw, wws))]
     per_kernel_ms, ms_per_step, gpu_ms = time_stages(args, stages, torch.cuda.current_stream())

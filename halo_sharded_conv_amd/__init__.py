@@ -101,7 +101,7 @@ def _load() -> ctypes.CDLL:
         "st_groupnorm_combine": (I32, [P, I32, ctypes.c_float, P, P, P, SZ, P]),
         "st_groupnorm_apply": (I32, [P, PP, I32, PP, P, SZ, P]),
         "st_groupnorm_backward_workspace_bytes": (SZ, [P, I32]),
-        "st_groupnorm_backward": (I32, [P, PP, PP, P, P, I32, P, P, SZ, PP, P, P, P, SZ, P]),
+        "st_groupnorm_backward": (I32, [P, PP, PP, P, P, I32, P, P, SZ, P, PP, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -379,11 +379,13 @@ def st_groupnorm_backward_workspace_bytes(y_plan: Plan, groups: int) -> int:
 
 
 def st_groupnorm_backward(y_plan: Plan, y_bufs, dz_bufs, ymax, dzmax, groups: int, gamma, fwd_workspace,
-                          dy_bufs, dgamma, dbeta, workspace, stream=None) -> None:
+                          dy_bufs, dgamma, dbeta, workspace, stream=None, dy_plan: Optional[Plan] = None) -> None:
+    """dy_plan None: dy in y's fp32 layout; else dy written into dy_plan's
+    (padded, fp32 or bf16) shard interiors."""
     sizes = _shard_bytes(y_plan)
     ys = _ptr_array(y_bufs, "st_groupnorm_backward y", sizes)
     dzs = _ptr_array(dz_bufs, "st_groupnorm_backward dz", sizes)
-    dys = _ptr_array(dy_bufs, "st_groupnorm_backward dy", sizes)
+    dys = _ptr_array(dy_bufs, "st_groupnorm_backward dy", sizes if dy_plan is None else _shard_bytes(dy_plan))
     ng = 4 * y_plan.batch * groups
     ym = _dev_ptr(ymax, "ymax", ng) if ymax is not None else 0
     dm = _dev_ptr(dzmax, "dzmax", ng) if dzmax is not None else 0
@@ -393,7 +395,8 @@ def st_groupnorm_backward(y_plan: Plan, y_bufs, dz_bufs, ymax, dzmax, groups: in
     fws, fnb = _ws(fwd_workspace)
     ws, nb = _ws(workspace)
     _check(lib.st_groupnorm_backward(y_plan.handle, ys, dzs, ctypes.c_void_p(ym), ctypes.c_void_p(dm), groups,
-                                     ctypes.c_void_p(g), ctypes.c_void_p(fws), fnb, dys, ctypes.c_void_p(dg),
+                                     ctypes.c_void_p(g), ctypes.c_void_p(fws), fnb,
+                                     dy_plan.handle if dy_plan is not None else None, dys, ctypes.c_void_p(dg),
                                      ctypes.c_void_p(db), ctypes.c_void_p(ws), nb, _stream(stream)),
            "st_groupnorm_backward")
 

@@ -379,8 +379,18 @@ __global__ __launch_bounds__(kNT) void gn_apply(const GnArgs a) {
 //     dy = a_c * dz + k_g * (y - mean_g) + b_g
 // with a_c = r gamma_c, k_g = -r^2 mean_g(g yhat), b_g = -r mean_g(g).
 
+// dy written into another shard layout (a padded plan, fp32 or bf16):
+// element (n, d, h, w, c) of a shard at p + n*sn + d*sd + h*sh + w*C + c
+struct GnbOut {
+  void* p;                      // the shard's interior origin
+  int64_t sn, sd, sh;           // element strides
+  int32_t H, W;                 // interior extents of the two inner spatial axes
+};
+
+enum GnbMode { kDyLikeY = 0, kDyPaddedF32 = 1, kDyPaddedBf16 = 2 };
+
 struct GnbArgs {
-  GnArgs g;                     // y = forward input of GroupNorm, z = dy, dz
+  GnArgs g;                     // y = forward input of GroupNorm, z = dy (kDyLikeY), dz
   const float* fstats;          // [N][G][2] (mean, rstd) of the forward pass
   const uint32_t* dzmax;        // [N][G] bits of max |dz|
   double* bpart;                // [S][N][C][2] exact (sum q1, sum q2)
@@ -388,7 +398,14 @@ struct GnbArgs {
   float4* bchan;                // [N][C] (mean, a, k, b)
   float* dgamma;                // [C] or NULL
   float* dbeta;                 // [C] or NULL
+  GnbOut out[ST_MAX_SHARDS];    // kDyPadded*: where dy goes
 };
+
+// fp32 -> bf16, round to nearest, ties to even (finite values)
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 
 __device__ __forceinline__ void bwd_scales(uint32_t dzbits, uint32_t ybits, float mean, float rstd, int lbits,
                                            int& e1, int& e2) {
@@ -557,7 +574,7 @@ __global__ void gnb_combine(const GnbArgs b) {
   }
 }
 
-template <int VW, bool FIXED>
+template <int VW, bool FIXED, int MODE>
 __global__ __launch_bounds__(kNT) void gnb_apply(const GnbArgs b) {
   using V = Vec<VW>;
   const GnArgs& a = b.g;
@@ -602,11 +619,33 @@ __global__ __launch_bounds__(kNT) void gnb_apply(const GnbArgs b) {
         else q = b.bchan[(size_t)n * C + (int)((v * VW + j) % C)];
         out[j] = fmaf(q.y, V::get(vd[i], j), fmaf(q.z, V::get(vy[i], j) - q.x, q.w));
       }
-      if constexpr (VW == 4) {
-        typedef float nf4 __attribute__((ext_vector_type(4)));
-        __builtin_nontemporal_store(nf4{out[0], out[1], out[2], out[3]}, reinterpret_cast<nf4*>(&dy[v]));
+      if constexpr (MODE == kDyLikeY) {
+        if constexpr (VW == 4) {
+          typedef float nf4 __attribute__((ext_vector_type(4)));
+          __builtin_nontemporal_store(nf4{out[0], out[1], out[2], out[3]}, reinterpret_cast<nf4*>(&dy[v]));
+        }
+        else __builtin_nontemporal_store(out[0], &dy[v]);
+      } else {
+        // the VW channels of this vector sit at one position (C % VW == 0)
+        const GnbOut& o = b.out[s];
+        const int64_t e0 = v * VW;
+        const int64_t pos = e0 / C;
+        const int c = (int)(e0 - pos * C);
+        const int64_t t = pos / o.W;
+        const int w = (int)(pos - t * o.W);
+        const int64_t d = t / o.H;
+        const int hh = (int)(t - d * o.H);
+        const int64_t off = n * o.sn + d * o.sd + hh * o.sh + (int64_t)w * C + c;
+        if constexpr (MODE == kDyPaddedF32) {
+          if constexpr (VW == 4) *reinterpret_cast<float4*>(static_cast<float*>(o.p) + off) =
+              make_float4(out[0], out[1], out[2], out[3]);
+          else static_cast<float*>(o.p)[off] = out[0];
+        } else {
+          if constexpr (VW == 4) *reinterpret_cast<uint2*>(static_cast<uint16_t*>(o.p) + off) =
+              make_uint2(bf16_rne(out[0]) | (bf16_rne(out[1]) << 16), bf16_rne(out[2]) | (bf16_rne(out[3]) << 16));
+          else static_cast<uint16_t*>(o.p)[off] = (uint16_t)bf16_rne(out[0]);
+        }
       }
-      else __builtin_nontemporal_store(out[0], &dy[v]);
     }
   }
 }
@@ -750,7 +789,7 @@ GnbLayout bwd_layout_of(const st_plan* p, int groups) {
 }
 
 template <int VW, bool FIXED>
-st_status launch_backward(GnbArgs& b, bool need_max, hipStream_t st) {
+st_status launch_backward(GnbArgs& b, bool need_max, int mode, hipStream_t st) {
   GnArgs& a = b.g;
   const int grid = grid_of(a);
   if (need_max) {
@@ -769,7 +808,9 @@ st_status launch_backward(GnbArgs& b, bool need_max, hipStream_t st) {
   s = launch_check("st_groupnorm_backward: combine launch");
   if (s != ST_OK) return s;
   const int agrid = std::max(1, std::min((kIter / kPart) * a.total_items, device_cus() * 16));
-  hipLaunchKernelGGL((gnb_apply<VW, FIXED>), dim3(agrid), dim3(kNT), 0, st, b);
+  if (mode == kDyPaddedBf16) hipLaunchKernelGGL((gnb_apply<VW, FIXED, kDyPaddedBf16>), dim3(agrid), dim3(kNT), 0, st, b);
+  else if (mode == kDyPaddedF32) hipLaunchKernelGGL((gnb_apply<VW, FIXED, kDyPaddedF32>), dim3(agrid), dim3(kNT), 0, st, b);
+  else hipLaunchKernelGGL((gnb_apply<VW, FIXED, kDyLikeY>), dim3(agrid), dim3(kNT), 0, st, b);
   return launch_check("st_groupnorm_backward: apply launch");
 }
 }  // namespace
@@ -871,17 +912,49 @@ size_t st_groupnorm_backward_workspace_bytes(const st_plan* y_plan, int32_t grou
 st_status st_groupnorm_backward(const st_plan* y_plan, const float* const* y_bufs, const float* const* dz_bufs,
                                 const uint32_t* ymax_or_null, const uint32_t* dzmax_or_null, int32_t groups,
                                 const float* gamma_or_null, const void* fwd_workspace,
-                                size_t fwd_workspace_bytes, float* const* dy_bufs, float* dgamma_or_null,
-                                float* dbeta_or_null, void* workspace, size_t workspace_bytes, void* stream) {
+                                size_t fwd_workspace_bytes, const st_plan* dy_plan_or_null, void* const* dy_bufs,
+                                float* dgamma_or_null, float* dbeta_or_null, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   const char* who = "st_groupnorm_backward";
-  if (!y_bufs || !dz_bufs || !dy_bufs) return fail(ST_ERR_INVALID_ARG, std::string(who) + ": NULL buffer array");
+  auto err = [&](st_status st, const char* m) { return fail(st, std::string(who) + ": " + m); };
+  if (!y_bufs || !dz_bufs || !dy_bufs) return err(ST_ERR_INVALID_ARG, "NULL buffer array");
   GnbArgs b{};
   int vw;
   bool fixed;
-  // validates the plan, y, dy, gamma, ymax and the forward workspace
-  st_status s = prepare(y_plan, y_bufs, dy_bufs, ymax_or_null, groups, 0.f, gamma_or_null, nullptr,
-                        const_cast<void*>(fwd_workspace), fwd_workspace_bytes, who, b.g, vw, fixed);
+  // validates the plan, y, gamma, ymax and the forward workspace (and dy when it has y's layout)
+  st_status s = prepare(y_plan, y_bufs, dy_plan_or_null ? nullptr : reinterpret_cast<float* const*>(dy_bufs),
+                        ymax_or_null, groups, 0.f, gamma_or_null, nullptr, const_cast<void*>(fwd_workspace),
+                        fwd_workspace_bytes, who, b.g, vw, fixed);
   if (s != ST_OK) return s;
+  int mode = kDyLikeY;
+  if (dy_plan_or_null) {
+    const st_plan* q = dy_plan_or_null;
+    if (q->ndim != y_plan->ndim || q->batch != y_plan->batch || q->channels != y_plan->channels ||
+        q->shards.size() != y_plan->shards.size())
+      return err(ST_ERR_BAD_SHAPE, "dy plan differs from the y plan in ndim, batch, channels or shards");
+    for (size_t i = 0; i < q->shards.size(); ++i)
+      for (int ax = 0; ax < kAxes; ++ax)
+        if (q->shards[i].ext[ax] != y_plan->shards[i].ext[ax] || q->shards[i].off[ax] != y_plan->shards[i].off[ax])
+          return err(ST_ERR_BAD_SHAPE, "dy plan differs from the y plan in shard sizes");
+    if (vw != 4 && q->dtype == ST_BF16) return err(ST_ERR_UNSUPPORTED, "bf16 dy needs C divisible by 4");
+    mode = q->dtype == ST_BF16 ? kDyPaddedBf16 : kDyPaddedF32;
+    const int64_t C = q->channels;
+    for (size_t i = 0; i < q->shards.size(); ++i) {
+      if (!dy_bufs[i]) return err(ST_ERR_INVALID_ARG, "NULL dy buffer");
+      if (!aligned16(dy_bufs[i])) return err(ST_ERR_ALIGNMENT, "dy buffers must be 16-byte aligned");
+      const Shard& sd = q->shards[i];
+      GnbOut& o = b.out[i];
+      o.sh = sd.pad[2] * C;
+      o.sd = sd.pad[1] * o.sh;
+      o.sn = sd.pad[0] * o.sd;
+      o.H = (int32_t)sd.ext[1];
+      o.W = (int32_t)sd.ext[2];
+      const int64_t origin = q->halo[0] * o.sd + q->halo[1] * o.sh + q->halo[2] * C;
+      o.p = static_cast<char*>(dy_bufs[i]) + origin * q->esize;
+      if (dy_bufs[i] == static_cast<const void*>(y_bufs[i]) || dy_bufs[i] == static_cast<const void*>(dz_bufs[i]))
+        return err(ST_ERR_INVALID_ARG, "dy in another layout must not alias y or dz");
+    }
+  }
   for (size_t i = 0; i < y_plan->shards.size(); ++i) {
     if (!dz_bufs[i]) return fail(ST_ERR_INVALID_ARG, std::string(who) + ": NULL dz buffer");
     if (!aligned16(dz_bufs[i])) return fail(ST_ERR_ALIGNMENT, std::string(who) + ": dz buffers must be 16-byte aligned");
@@ -913,8 +986,9 @@ st_status st_groupnorm_backward(const st_plan* y_plan, const float* const* y_buf
   s = launch_check("st_groupnorm_backward: clear launch");
   if (s != ST_OK) return s;
   const bool need_max = dzmax_or_null == nullptr;
-  if (vw == 4) return fixed ? launch_backward<4, true>(b, need_max, st) : launch_backward<4, false>(b, need_max, st);
-  return fixed ? launch_backward<1, true>(b, need_max, st) : launch_backward<1, false>(b, need_max, st);
+  if (vw == 4)
+    return fixed ? launch_backward<4, true>(b, need_max, mode, st) : launch_backward<4, false>(b, need_max, mode, st);
+  return fixed ? launch_backward<1, true>(b, need_max, mode, st) : launch_backward<1, false>(b, need_max, mode, st);
 }
 
 }  // extern "C"

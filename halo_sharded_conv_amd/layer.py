@@ -171,13 +171,15 @@ class ShardedConvGN:
             self.out_view(self.dz_bufs, i).copy_(self._host_to_dev(dz[self._global_slices(i)]))
         _torch().cuda.synchronize()
 
-    def norm_backward(self, dzmax=None, dy_bufs=None, stream=None) -> None:
-        """GroupNorm backward from the forward pass's y and workspace."""
+    def norm_backward(self, dzmax=None, dy_bufs=None, stream=None, dy_plan=None) -> None:
+        """GroupNorm backward from the forward pass's y and workspace.  With
+        dy_plan (e.g. the input-gradient layer's padded input plan) dy goes
+        straight into dy_bufs in that plan's layout and dtype."""
         cfg = self.cfg
         st_groupnorm_backward(self.out_plan, self.y_bufs, self.dz_bufs, self.ymax if self.fuse_max else None,
                               dzmax, cfg.groups, self.gamma, self.ws,
                               self.dy_bufs if dy_bufs is None else dy_bufs, self.dgamma, self.dbeta, self.bws,
-                              stream)
+                              stream, dy_plan=dy_plan)
 
     def step(self, stream=None) -> None:
         self.exchange(True, stream)

@@ -354,7 +354,14 @@ st_status st_groupnorm_apply(const st_plan* y_plan, const float* const* y_bufs, 
  *   groups, gamma_or_null   as in the forward call
  *   fwd_workspace      the forward call's workspace, holding its (mean, rstd)
  *                      (read; must not have been reused since)
- *   dy_bufs            fp32 output, same layout as y; may alias dz_bufs or y_bufs
+ *   dy_plan_or_null    NULL: dy_bufs are fp32 in y's layout (may alias dz_bufs or
+ *                      y_bufs).  Else the layout dy is written in, e.g. the
+ *                      padded bf16 plan the input-gradient conv reads: same
+ *                      ndim, batch, channels and shard sizes as y_plan, any
+ *                      halo, ST_F32 or ST_BF16 (rounded to nearest even; C
+ *                      divisible by 4); only interiors are written and dy must
+ *                      not alias y or dz
+ *   dy_bufs            dy output shards
  *   dgamma_or_null, dbeta_or_null   C floats each, or NULL (not computed)
  *   workspace          >= st_groupnorm_backward_workspace_bytes(y_plan, groups)
  *                      bytes, distinct from fwd_workspace
@@ -364,8 +371,9 @@ size_t st_groupnorm_backward_workspace_bytes(const st_plan* y_plan, int32_t grou
 st_status st_groupnorm_backward(const st_plan* y_plan, const float* const* y_bufs, const float* const* dz_bufs,
                                 const uint32_t* ymax_or_null, const uint32_t* dzmax_or_null, int32_t groups,
                                 const float* gamma_or_null, const void* fwd_workspace,
-                                size_t fwd_workspace_bytes, float* const* dy_bufs, float* dgamma_or_null,
-                                float* dbeta_or_null, void* workspace, size_t workspace_bytes, void* stream);
+                                size_t fwd_workspace_bytes, const st_plan* dy_plan_or_null, void* const* dy_bufs,
+                                float* dgamma_or_null, float* dbeta_or_null, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 #ifdef __cplusplus
 }

@@ -181,11 +181,11 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     bws = ctypes.c_void_p(0x80000)
     dzs = PP(0x90000, 0xA0000)
     gb = L.st_groupnorm_backward
-    args = [q.handle, aligned, dzs, None, None, 4, None, ws, need, aligned, None, None, bws, bneed, s]
+    args = [q.handle, aligned, dzs, None, None, 4, None, ws, need, None, aligned, None, None, bws, bneed, s]
 
     def gbw(**kw):
         a = list(args)
-        names = ["plan", "y", "dz", "ymax", "dzmax", "groups", "gamma", "fws", "fnb", "dy", "dg", "db",
+        names = ["plan", "y", "dz", "ymax", "dzmax", "groups", "gamma", "fws", "fnb", "dyplan", "dy", "dg", "db",
                  "ws", "nb", "stream"]
         for k, v in kw.items():
             a[names.index(k)] = v
@@ -205,6 +205,16 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert gbw(dzmax=ctypes.c_void_p(0x70002)) == ALIGN
     assert gbw(dg=ctypes.c_void_p(0x70002)) == ALIGN
     assert gbw(plan=p.handle) == BAD_SHAPE
+    # dy in another layout: same shards and channels, bf16 needs C % 4 == 0, no aliasing
+    dyp_ok = hsc.st_plan_shards(2, 1, 16, [8, 8], [[4, 4], [8]], [1, 1], "bf16")
+    dyp_ch = hsc.st_plan_shards(2, 1, 8, [8, 8], [[4, 4], [8]], [1, 1], "bf16")
+    dyp_sh = hsc.st_plan_shards(2, 1, 16, [8, 8], [[3, 5], [8]], [1, 1], "bf16")
+    dys = PP(0xD0000, 0xE0000)
+    assert gbw(dyplan=dyp_ch.handle, dy=dys) == BAD_SHAPE
+    assert gbw(dyplan=dyp_sh.handle, dy=dys) == BAD_SHAPE
+    assert gbw(dyplan=dyp_ok.handle, dy=aligned) == INVALID          # dy aliases y
+    assert gbw(dyplan=dyp_ok.handle, dy=PP(0xD0000, 0xE0008)) == ALIGN
+    assert gbw(dyplan=dyp_ok.handle, dy=PP(0xD0000, 0)) == INVALID
 
 
 def test_workspace_layout_regions_are_disjoint():

@@ -5,7 +5,9 @@ gradient dz, and writes dy, dgamma and dbeta.  Checks: all three against the
 oracle's group_norm_backward (fp64, pinned on the CPU) evaluated on the GPU's
 own y, within the fp32 tolerance; sharded equal to unsharded bit for bit;
 a caller-supplied max |dz| giving the same bits as the computed one; dy
-aliasing dz; a zero upstream gradient giving exact zeros.
+aliasing dz; a zero upstream gradient giving exact zeros; dy written straight
+into the input-gradient layer's padded bf16 (or fp32) shards equal to the
+rounded same-layout dy, margins untouched.
 """
 import numpy as np
 import pytest
@@ -97,3 +99,35 @@ def test_gn_backward_zero_gradient():
     layer = forward_backward(wl, x, w, dz)
     assert not np.any(layer.gather(layer.dy_bufs))
     assert not np.any(layer.dgamma.cpu().numpy()) and not np.any(layer.dbeta.cpu().numpy())
+
+
+@pytest.mark.parametrize("name", ["vol32_full", "img64_small", "img64_b2", "vol32_grid", "vol16k5",
+                                  "grid256_small"])
+def test_gn_backward_into_padded_input_gradient_shards(name):
+    """dy written straight into the input-gradient layer's halo-padded shards
+    (bf16 rounded to nearest even, or fp32): interiors equal the same-layout
+    fp32 dy (rounded on the host), margins are not touched."""
+    from halo_sharded_conv_amd.layer import dgrad_config
+    wl = CASES[name]
+    say(f"groupnorm backward into padded shards: {name}")
+    x, w = synth.make_input(wl), synth.make_weight(wl)
+    gamma, beta = synth.make_affine(wl, seed=19)
+    dz = synth.make_upstream_grad(wl, seed=37)
+    layer = forward_backward(wl, x, w, dz, gamma, beta)
+    want = layer.gather(layer.dy_bufs)
+    bwd = ShardedConvGN(dgrad_config(wl))
+    for t in bwd.x_bufs:
+        t.fill_(0x3F7B if t.dtype == torch.int16 else 0.625)   # sentinel margins
+    layer.norm_backward(dy_bufs=bwd.x_bufs, dy_plan=bwd.in_plan)
+    torch.cuda.synchronize()
+    h = wl.ksize // 2
+    for i in range(bwd.S):
+        pad = bwd.padded_host(i)
+        inner = tuple([slice(None)] + [slice(h, h + e) for e in bwd.info[i]["extent"]] + [slice(None)])
+        part = want[bwd._global_slices(i)]
+        expect = synth.f32_to_bf16_bits(part) if wl.dtype == "bf16" else part
+        assert bits_equal(pad[inner], expect)
+        mask = np.ones(pad.shape, bool)
+        mask[inner] = False
+        sentinel = np.uint16(0x3F7B) if wl.dtype == "bf16" else np.float32(0.625)
+        assert np.all(pad[mask] == sentinel)
