@@ -362,8 +362,16 @@ __global__ __launch_bounds__(256) void wgrad_direct(const WgArgs a, int ndim, in
 __global__ void wgrad_reduce(const float* __restrict__ partial, int parts, int64_t elems, float* __restrict__ dw) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= elems) return;
+  // 8 independent loads in flight, then added in partition order
   double t = 0.0;
-  for (int g = 0; g < parts; ++g) t += (double)partial[(size_t)g * elems + e];
+  for (int g0 = 0; g0 < parts; g0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = g0 + k < parts ? partial[(size_t)(g0 + k) * elems + e] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (g0 + k < parts) t += (double)v[k];
+  }
   dw[e] = (float)t;
 }
 
@@ -504,7 +512,7 @@ st_status st_conv_wgrad(const st_plan* x_plan, const void* const* x_bufs, const 
   }
   st_status s = launch_check("st_conv_wgrad: launch");
   if (s != ST_OK) return s;
-  hipLaunchKernelGGL(wgrad_reduce, dim3((unsigned)((elems + 255) / 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL(wgrad_reduce, dim3((unsigned)((elems + 63) / 64)), dim3(64), 0, st,
                      static_cast<const float*>(workspace), parts, elems, dweight);
   return launch_check("st_conv_wgrad: reduce launch");
 }
