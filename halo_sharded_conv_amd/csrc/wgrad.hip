@@ -185,7 +185,7 @@ __global__ __launch_bounds__(C::NT) void wgrad_mfma(const WgArgs a) {
 #pragma unroll
     for (int j = 0; j < C::WN; ++j) acc[i][j] = f32x16{};
 
-  uint4 ra0[C::A_PER], rb0[C::B_PER], ra1[C::A_PER], rb1[C::B_PER];
+  uint4 ra0[C::A_PER], rb0[C::B_PER];
   // Loader instruction k (k = wave + q * NW) of a chunk covers octet group
   // g = k % G (OG octet rows, all in one tap shift or tap row) at column group
   // jg = k / G (64 / OG columns); lane l takes octet l % OG of column l / OG,
@@ -246,11 +246,11 @@ __global__ __launch_bounds__(C::NT) void wgrad_mfma(const WgArgs a) {
           qb[q]);
     }
   };
-  auto kstep = [&](const char* st, int ks) __attribute__((always_inline)) {
+  // fragments of K step ks (8 consecutive columns per lane: one 16-byte slot)
+  auto frags = [&](const char* st, int ks, bf16x8 (&av)[C::WM], bf16x8 (&bv)[C::WN]) __attribute__((always_inline)) {
     const char* la = st;
     const char* lb = st + C::LA_ROWS * C::RS;
-    const int slot = ks * 2 + g2;                          // 16-byte column slot of this lane
-    bf16x8 av[C::WM], bv[C::WN];
+    const int slot = ks * 2 + g2;
 #pragma unroll
     for (int i = 0; i < C::WM; ++i) {
       const int row = (wm * C::WM + i) * 32 + l32;
@@ -261,6 +261,8 @@ __global__ __launch_bounds__(C::NT) void wgrad_mfma(const WgArgs a) {
       const int row = (wn * C::WN + j) * 32 + l32;
       bv[j] = *reinterpret_cast<const bf16x8*>(lb + row * C::RS + ((slot ^ wg_key(row)) << 4));
     }
+  };
+  auto mfmas = [&](const bf16x8 (&av)[C::WM], const bf16x8 (&bv)[C::WN]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::WM; ++i)
 #pragma unroll
@@ -268,32 +270,40 @@ __global__ __launch_bounds__(C::NT) void wgrad_mfma(const WgArgs a) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
   };
 
-  // chunks of this partition: c0 in stage0, c1 staged in registers
   const int row_end = band_begin(a, part + 1);
+  // chunks of this partition: c0 in stage0, c1 staged in registers
   WgChunk c0 = first_chunk(a, band_begin(a, part), row_end);
   WgChunk c1 = next_chunk<C::K>(a, c0, C::COLS, row_end);
   fetch(c0, ra0, rb0);
-  fetch(c1, ra1, rb1);
   store(stage0, ra0, rb0);
+  fetch(c1, ra0, rb0);
   __syncthreads();
-  // one chunk per phase; the loop body handles two so that stages and
-  // register sets alternate at compile time
+  // one chunk per phase; the loop body handles two so that the LDS stages
+  // alternate at compile time.  In a phase: K step 0's fragments, the next
+  // chunk's registers into the other stage, the chunk after that into the
+  // registers, and each K step's MFMAs with the next step's fragments in
+  // flight.
   auto phase = [&](auto P) __attribute__((always_inline)) {
     constexpr int par = decltype(P)::value;
     char* const cur = par ? stage1 : stage0;
     char* const nxt = par ? stage0 : stage1;
     const WgChunk c2 = next_chunk<C::K>(a, c1, C::COLS, row_end);
-    if constexpr (par == 0) fetch(c2, ra0, rb0);           // two chunks ahead
-    else fetch(c2, ra1, rb1);
     const int nks = (min(C::COLS, c0.W + 2 * C::P - c0.j0) + 15) / 16;
-    kstep(cur, 0);
-    if (c1.valid) {                                         // the next chunk, during this one's MFMAs
-      if constexpr (par == 0) store(nxt, ra1, rb1);
-      else store(nxt, ra0, rb0);
+    bf16x8 av0[C::WM], bv0[C::WN], av1[C::WM], bv1[C::WN];
+    frags(cur, 0, av0, bv0);
+    if (c1.valid) store(nxt, ra0, rb0);                    // the next chunk, while this one computes
+    fetch(c2, ra0, rb0);                                    // and the one after it
+    if (nks > 1) frags(cur, 1, av1, bv1);
+    mfmas(av0, bv0);
+    if (nks > 1) {
+      if (nks > 2) frags(cur, 2, av0, bv0);
+      mfmas(av1, bv1);
+      if (nks > 2) {
+        if (nks > 3) frags(cur, 3, av1, bv1);
+        mfmas(av0, bv0);
+        if (nks > 3) mfmas(av1, bv1);
+      }
     }
-#pragma unroll
-    for (int ks = 1; ks < C::COLS / 16; ++ks)
-      if (ks < nks) kstep(cur, ks);
     __syncthreads();
     c0 = c1;
     c1 = c2;
