@@ -300,6 +300,50 @@ def group_norm_backward(y: np.ndarray, dz: np.ndarray, groups: int, eps: float, 
 
 
 # ----------------------------------------------------------------------------
+# shape-changing ops: 'valid' pooling and the sharding shapes it implies
+# ----------------------------------------------------------------------------
+
+def pool_valid(x: np.ndarray, k: int, s: int, mode: str = "avg") -> np.ndarray:
+    """'Valid' pooling with a cubic window k and stride s on every spatial axis.
+
+    The shape-changing case of the dynamic sharding shapes ("Technical
+    summary: ShardTensor", section 2 "Design principles": every local chunk
+    carries its own shape, and an op may change it).  Output j along an axis
+    of extent n covers inputs [j*s, j*s + k), j = 0 .. (n - k) // s.
+    mode "avg": mean of the k^d window; "max": its maximum.
+    x: [N, *S, C] fp64; returns [N, *S', C].
+    """
+    d = x.ndim - 2
+    S = x.shape[1:1 + d]
+    if any(n < k for n in S):
+        raise ValueError("window larger than the volume")
+    out_S = tuple((n - k) // s + 1 for n in S)
+    acc = None
+    for t in _taps(k, d):
+        window = x[(slice(None),) + tuple(slice(t[a], t[a] + s * (out_S[a] - 1) + 1, s) for a in range(d))]
+        if acc is None:
+            acc = np.array(window, dtype=np.float64)
+        elif mode == "max":
+            acc = np.maximum(acc, window)
+        else:
+            acc = acc + window
+    return acc / float(k ** d) if mode == "avg" else acc
+
+
+def pooled_shard_sizes(sizes: Sequence[int], k: int, s: int) -> List[int]:
+    """Output sharding shape along one axis: output j belongs to the shard
+    whose interior holds the first cell of its window, j*s."""
+    n = int(sum(sizes))
+    n_out = (n - k) // s + 1
+    out = []
+    for a, e in zip(shard_offsets(sizes), sizes):
+        first = -(-a // s)                           # ceil(a / s)
+        end = min(-(-(a + e) // s), n_out)
+        out.append(end - first)
+    return out
+
+
+# ----------------------------------------------------------------------------
 # sharding shapes and halos (the method's data movement, stated on arrays)
 # ----------------------------------------------------------------------------
 
@@ -476,6 +520,22 @@ def conv_wgrad_bruteforce(x, dy, k):
                     for c in range(cin):
                         dw[(o, c) + t] += dy[(n, *pos, o)] * x[(n, *src, c)]
     return dw
+
+
+def pool_bruteforce(x, k, s, mode="avg"):
+    """Scalar-loop 'valid' pooling (tiny inputs)."""
+    x = np.asarray(x, np.float64)
+    n_, *spatial, c = x.shape
+    d = len(spatial)
+    out_S = [(n - k) // s + 1 for n in spatial]
+    y = np.zeros((n_, *out_S, c))
+    for n in range(n_):
+        for pos in itertools.product(*[range(m) for m in out_S]):
+            for ch in range(c):
+                vals = [x[(n, *[pos[a] * s + t[a] for a in range(d)], ch)]
+                        for t in itertools.product(range(k), repeat=d)]
+                y[(n, *pos, ch)] = max(vals) if mode == "max" else sum(vals) / len(vals)
+    return y
 
 
 def group_norm_bruteforce(y, groups, eps, gamma=None, beta=None):

@@ -306,6 +306,88 @@ def test_wgrad_pins_catch_mutants(name):
     assert not pin_wgrad(mutant), f"no pin caught the wgrad mutant '{name}'"
 
 
+def pin_pool(pool, sizes_fn=oracle.pooled_shard_sizes):
+    """'Valid' pooling against scalar brute force, torch's fp64 pooling, and
+    the method's own invariant: each shard pooled from its halo-padded chunk
+    (outputs owned by the shard holding their window's first cell) equals
+    the matching slice of the unsharded result.  A shape error counts as a
+    failed pin."""
+    try:
+        return _pin_pool(pool, sizes_fn)
+    except (ValueError, IndexError):
+        return False
+
+
+def _pin_pool(pool, sizes_fn):
+    ok = True
+    for d, k, s in [(2, 2, 2), (2, 3, 2), (3, 2, 2), (3, 3, 1), (2, 3, 3)]:
+        r = rng(800 + 100 * d + 10 * k + s)
+        spatial = (10, 9, 8) if d == 3 else (12, 13)
+        x = r.standard_normal((2, *spatial, 3))
+        for mode in ("avg", "max"):
+            y = pool(x, k, s, mode)
+            small = (4, 5, 5) if d == 3 else (6, 7)
+            xs = r.standard_normal((1, *small, 2))
+            ok &= rel(pool(xs, k, s, mode), oracle.pool_bruteforce(xs, k, s, mode)) <= 1e-13
+            xt = torch.from_numpy(np.moveaxis(x, -1, 1).copy())
+            if mode == "avg":
+                f = torch.nn.functional.avg_pool3d if d == 3 else torch.nn.functional.avg_pool2d
+            else:
+                f = torch.nn.functional.max_pool3d if d == 3 else torch.nn.functional.max_pool2d
+            ok &= rel(y, np.moveaxis(f(xt, k, s).numpy(), 1, -1)) <= 1e-13
+        # sharded form along axis 0 with uneven sizes (odd boundaries straddle windows)
+        sizes = [4, 3, spatial[0] - 7]
+        out_sizes = sizes_fn(sizes, k, s)
+        ok &= sum(out_sizes) == y.shape[1]
+        h = k - 1
+        xp = zero_pad_axis0(x, h)
+        o0 = 0
+        for a, e, m in zip(oracle.shard_offsets(sizes), sizes, out_sizes):
+            padded = xp[:, a: a + e + 2 * h]           # the shard's chunk with its halo along axis 0
+            first = -(-a // s)
+            lo = first * s - a + h                      # first owned window, in padded coordinates
+            if m == 0:                                  # a shard may own no window start
+                continue
+            ok &= lo + (m - 1) * s + k <= padded.shape[1]
+            chunk = padded[:, lo: lo + (m - 1) * s + k]
+            ok &= np.array_equal(pool(chunk, k, s, "max"), pool(x, k, s, "max")[:, o0:o0 + m])
+            o0 += m
+    return bool(ok)
+
+
+def zero_pad_axis0(x, h):
+    pad = [(0, 0)] * x.ndim
+    pad[1] = (h, h)
+    return np.pad(x, pad)
+
+
+def test_pool_pins():
+    assert pin_pool(oracle.pool_valid)
+
+
+@pytest.mark.parametrize("name", ["window off by one", "stride ignored", "sum not mean", "last shard owns"])
+def test_pool_pins_catch_mutants(name):
+    def window(x, k, s, mode="avg"):
+        return oracle.pool_valid(x, k + 1, s, mode) if min(x.shape[1:-1]) > k else oracle.pool_valid(x, k, s, mode) + 1
+
+    def stride1(x, k, s, mode="avg"):
+        return oracle.pool_valid(x, k, 1, mode)
+
+    def summed(x, k, s, mode="avg"):
+        y = oracle.pool_valid(x, k, s, mode)
+        return y * (k ** (x.ndim - 2)) if mode == "avg" else y
+
+    def last_owns(sizes, k, s):
+        out = oracle.pooled_shard_sizes(sizes, k, s)
+        return [o + (1 if i == len(out) - 1 else 0) for i, o in enumerate(out)]
+
+    if name == "last shard owns":
+        assert not pin_pool(oracle.pool_valid, last_owns)
+        return
+    mutant = {"window off by one": window, "stride ignored": stride1, "sum not mean": summed}[name]
+    assert not pin_pool(mutant), f"no pin caught the pooling mutant '{name}'"
+
+
 def test_dgrad_pins():
     assert pin_dgrad(oracle.conv_same_dgrad)
 
