@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sharded conv+GroupNorm voxels/s on 1 MI355X; % MFMA peak (conv), % HBM BW (halo/norm)"
 METRIC_DGRAD = "sharded conv input-gradient (halo exchange of dy + conv) voxels/s on 1 MI355X"
+METRIC_POOL = "sharded 2x downsampling (halo exchange + 'valid' average pooling, k=2 s=2) input voxels/s on 1 MI355X"
 METRIC_BWD = ("sharded conv+GroupNorm backward (GroupNorm backward, halo exchange of dy, input gradient, "
               "weight gradient) voxels/s on 1 MI355X")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -36,8 +37,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--pass", dest="pass_", choices=("forward", "dgrad", "backward"), default="forward",
-                    help="the layer's forward step, the input gradient of its conv, or its whole backward step")
+    ap.add_argument("--pass", dest="pass_", choices=("forward", "dgrad", "backward", "pool"), default="forward",
+                    help="the layer's forward step, the input gradient of its conv, its whole backward step, "
+                         "or a 2x average-pool downsampling of its input shards")
     ap.add_argument("--exchange", choices=("pack+unpack", "fused"), default="pack+unpack",
                     help="halo exchange as two copies through a message buffer, or one fused copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -55,7 +57,7 @@ STAGE_KERNELS = {                    # kernel-name fragments of each library sta
     "halo_pack": ("halo_copy",), "halo_unpack": ("halo_copy",), "halo_exchange": ("halo_copy",),
     "conv": ("conv_rows", "conv_pairs", "conv_gemm", "conv_direct"),
     "gn_partials": ("gn_max", "gn_stats"), "gn_apply": ("gn_apply",),
-    "wgrad": ("wgrad_mfma", "wgrad_direct"), "gn_backward": ("gn_max", "gnb_"),
+    "wgrad": ("wgrad_mfma", "wgrad_direct"), "gn_backward": ("gn_max", "gnb_"), "pool": ("pool_kernel",),
 }
 
 
@@ -65,6 +67,7 @@ STAGE_SOURCES = {                    # library sources that define each stage's 
     "conv": ("conv.hip", "internal.h"),
     "gn_partials": ("groupnorm.hip", "internal.h"), "gn_apply": ("groupnorm.hip", "internal.h"),
     "wgrad": ("wgrad.hip", "internal.h"), "gn_backward": ("groupnorm.hip", "internal.h"),
+    "pool": ("pool.hip", "internal.h"),
 }
 
 
@@ -264,6 +267,8 @@ def main():
     wl_fwd = synth.workload(name)
     if args.pass_ == "backward":
         return bench_backward(args, wl_fwd)
+    if args.pass_ == "pool":
+        return bench_pool(args, wl_fwd)
     if args.pass_ == "dgrad":
         # input gradient of the layer's conv: dy (Cout channels) -> dx (Cin)
         from halo_sharded_conv_amd.layer import dgrad_config
@@ -357,6 +362,73 @@ def bench_backward(args, wl_fwd):
         ("wgrad", lambda: hsc.st_conv_wgrad(fwd.in_plan, fwd.x_bufs, bwd.in_plan, bwd.x_bufs, wl.ksize, dw, wws))]
     per_kernel_ms, ms_per_step, gpu_ms = time_stages(args, stages, torch.cuda.current_stream())
     report(args, wl, fwd, per_kernel_ms, ms_per_step, gpu_ms, METRIC_BWD, None, dgrad_layer=bwd)
+
+
+def bench_pool(args, wl):
+    """Downsampling of the layer's input shards: halo exchange (halo 1 = k - 1)
+    and 'valid' 2x2(x2) average pooling into the output plan the library
+    derives, in the input's type."""
+    import numpy as np
+    import torch
+
+    import halo_sharded_conv_amd as hsc
+    import oracle
+    import synth
+
+    k = s = 2
+    d = wl.ndim
+    tdt = torch.float32 if wl.dtype == "f32" else torch.int16
+    p = hsc.st_plan_shards(d, wl.batch, wl.cin, wl.spatial, wl.shards, [k - 1] * d, wl.dtype)
+    q = hsc.st_plan_pooled(p, k, s)
+    bufs = [torch.zeros(p.shard_info(i)["elems"], dtype=tdt, device="cuda") for i in range(p.num_shards)]
+    x = synth.make_input(wl)
+    xs = x.view(np.int16) if x.dtype == np.uint16 else x
+    for i in range(p.num_shards):
+        inf = p.shard_info(i)
+        v = bufs[i].view(p.padded_shape(i))
+        v[tuple([slice(None)] + [slice(1, 1 + e) for e in inf["extent"]] + [slice(None)])].copy_(
+            torch.from_numpy(np.ascontiguousarray(xs[tuple([slice(None)] + [slice(o, o + e) for o, e in zip(inf["offset"], inf["extent"])])])))
+    msg = torch.zeros(max(16, p.msg_bytes), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty(q.shard_info(i)["elems"], dtype=tdt, device="cuda") for i in range(q.num_shards)]
+    torch.cuda.synchronize()
+    stages = [("halo_pack", lambda: hsc.st_halo_pack(p, bufs, msg)),
+              ("halo_unpack", lambda: hsc.st_halo_unpack(p, msg, bufs, True)),
+              ("pool", lambda: hsc.st_pool_sharded(p, bufs, k, s, "avg", q, outs))]
+    per_kernel_ms, ms_per_step, gpu_ms = time_stages(args, stages, torch.cuda.current_stream())
+    esize = 4 if wl.dtype == "f32" else 2
+    out_vox = wl.batch * int(np.prod([sum(a) for a in q.shards]))
+    alg = {"halo_pack": 2 * p.msg_bytes, "halo_unpack": 2 * p.msg_bytes,
+           "pool": wl.voxels * wl.cin * esize + out_vox * wl.cin * esize}
+    kernels = {}
+    for key, ms in per_kernel_ms.items():
+        gbs = alg[key] / (ms * 1e-3) / 1e9
+        kernels[key] = {"ms": round(ms, 5), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roof = {"bound": "hbm", "achieved": kernels["pool"]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kernels["pool"]["GB/s"] / HBM_PEAK_GBS, 4), "kernel": "pool",
+            "traffic": load_traffic(wl, "pool")}
+    out = {"metric": METRIC_POOL, "value": wl.voxels / (ms_per_step * 1e-3), "unit": "voxels/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "gpu_ms_per_step": round(gpu_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic",
+           "config": {"workload": wl.name, "shape": [wl.batch, wl.cin, *wl.spatial], "pool": "avg k2 s2",
+                      "shards": [list(a) for a in wl.shards], "out_shards": [list(a) for a in q.shards],
+                      "pass": "pool"},
+           "roofline": roof, "kernels": kernels}
+    if not args.no_cpu_baseline:
+        rows = args.cpu_rows or max(2, min(wl.spatial[0], int(2.0e6 // (wl.voxels // wl.spatial[0]) + 1)) // 2 * 2)
+        sub_shape = (rows,) + tuple(wl.spatial[1:])
+        sub = synth.small_variant(wl, sub_shape, [(n,) for n in sub_shape], name_suffix="cpu_sample")
+        xsub = oracle.widen(synth.make_input(sub), wl.dtype)
+        from threadpoolctl import threadpool_info
+        t0 = time.perf_counter()
+        y = oracle.pool_valid(xsub, k, s, "avg")
+        dt = time.perf_counter() - t0
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        out["cpu_baseline"] = {"value": sub.voxels / dt, "unit": "voxels/s", "cores": threads, "kind": "oracle",
+                               "sample": f"first {rows} rows of the outermost axis ({sub.voxels} voxels, 'valid' "
+                                         f"average pooling in fp64 numpy, {dt:.2f} s)", "seconds": round(dt, 3),
+                               "checksum": float(np.abs(y).sum())}
+    print(json.dumps(out), flush=True)
 
 
 def report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, metric, w_fwd, dgrad_layer=None):

@@ -92,6 +92,8 @@ def _load() -> ctypes.CDLL:
         "st_conv_pack_weights": (I32, [I32, I32, I32, I32, I32, P, P, P]),
         "st_conv_dgrad_weights": (I32, [I32, I32, I32, I32, I32, P, P, P]),
         "st_conv_sharded": (I32, [P, PP, P, P, I32, I32, P, PP, P, I32, P]),
+        "st_plan_pooled": (I32, [P, I32, I32, ctypes.POINTER(I32), I32, ctypes.POINTER(P)]),
+        "st_pool_sharded": (I32, [P, PP, I32, I32, I32, P, PP, P]),
         "st_conv_wgrad_workspace_bytes": (SZ, [P, I32, I32]),
         "st_conv_wgrad": (I32, [P, PP, P, PP, I32, P, P, SZ, P]),
         "st_groupnorm_workspace_bytes": (SZ, [P, I32]),
@@ -303,6 +305,37 @@ def st_conv_sharded(in_plan: Plan, in_bufs, packed_weight, bias, cout: int, ksiz
            "st_conv_sharded")
 
 
+def st_plan_pooled(in_plan: Plan, ksize: int, stride: int, out_halo=None, out_dtype=None) -> Plan:
+    """Output plan of a 'valid' pooling; its shard sizes are derived by the library."""
+    dt = in_plan.dtype if out_dtype is None else DTYPES.get(out_dtype, out_dtype)
+    hl = (ctypes.c_int32 * 3)(*(list(out_halo) + [0] * (3 - len(out_halo)))) if out_halo is not None else None
+    out = ctypes.c_void_p()
+    _check(lib.st_plan_pooled(in_plan.handle, ksize, stride, hl, dt, ctypes.byref(out)), "st_plan_pooled")
+    halo = tuple(out_halo) if out_halo is not None else (0,) * in_plan.ndim
+    probe = Plan(out.value, in_plan.ndim, in_plan.batch, in_plan.channels, dt, (), halo)
+    # per-axis shard sizes from the shard table (shards are row-major over the grid)
+    n = probe.num_shards
+    infos = [probe.shard_info(i) for i in range(n)]
+    sizes = []
+    for a in range(in_plan.ndim):
+        seen = {}
+        for inf in infos:
+            seen.setdefault(inf["grid"][a], inf["extent"][a])
+        sizes.append(tuple(seen[g] for g in sorted(seen)))
+    probe.shards = tuple(sizes)
+    return probe
+
+
+def st_pool_sharded(in_plan: Plan, in_bufs, ksize: int, stride: int, mode: str, out_plan: Plan, out_bufs,
+                    stream=None) -> None:
+    """mode 'avg' or 'max'."""
+    ins = _ptr_array(in_bufs, "st_pool_sharded input", _shard_bytes(in_plan))
+    outs = _ptr_array(out_bufs, "st_pool_sharded output", _shard_bytes(out_plan))
+    m = {"avg": 0, "max": 1}[mode]
+    _check(lib.st_pool_sharded(in_plan.handle, ins, ksize, stride, m, out_plan.handle, outs, _stream(stream)),
+           "st_pool_sharded")
+
+
 def st_conv_wgrad_workspace_bytes(x_plan: Plan, cout: int, ksize: int) -> int:
     return int(lib.st_conv_wgrad_workspace_bytes(x_plan.handle, cout, ksize))
 
@@ -407,5 +440,6 @@ __all__ = [
     "st_conv_pack_weights", "st_conv_sharded", "st_groupnorm_workspace_bytes",
     "st_groupnorm_workspace_layout", "st_groupnorm_sharded", "st_groupnorm_partials",
     "st_groupnorm_combine", "st_groupnorm_apply", "st_groupnorm_backward_workspace_bytes",
-    "st_groupnorm_backward", "st_conv_wgrad_workspace_bytes", "st_conv_wgrad",
+    "st_groupnorm_backward", "st_conv_wgrad_workspace_bytes", "st_conv_wgrad", "st_plan_pooled",
+    "st_pool_sharded",
 ]

@@ -256,6 +256,42 @@ st_status st_conv_wgrad(const st_plan* x_plan, const void* const* x_bufs, const 
                         const void* const* dy_bufs, int32_t ksize, float* dweight, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------ shape-changing ops */
+
+/*
+ * st_plan_pooled - the output plan of a 'valid' pooling of in_plan's shards.
+ * Section 2, "Design principles" of the ShardTensor summary: each local chunk
+ * carries its own shape ("sharding shapes"), so an op that changes shapes
+ * derives the output chunks from the input ones.  Window ksize, stride on
+ * every spatial axis; output j along an axis of extent n covers inputs
+ * [j*stride, j*stride + ksize), j = 0 .. (n - ksize) / stride, and belongs to
+ * the shard whose interior holds j*stride.
+ *   out_halo_or_null   ndim halo widths of the output plan (NULL: 0)
+ *   out_dtype          element type of the output shards
+ *   out                receives the plan (release with st_plan_destroy)
+ * Errors: ST_ERR_BAD_SHAPE (window larger than the volume),
+ * ST_ERR_SHARD_TOO_SMALL (a shard holds no window start: it would own no
+ * output), ST_ERR_INVALID_ARG.
+ */
+st_status st_plan_pooled(const st_plan* in_plan, int32_t ksize, int32_t stride, const int32_t* out_halo_or_null,
+                         st_dtype out_dtype, st_plan** out);
+
+/*
+ * st_pool_sharded - 'valid' pooling of every shard from its halo-padded chunk.
+ * Same passage as st_plan_pooled.
+ *   in_plan, in_bufs   input shards after their halo exchange; halo >= ksize - 1
+ *                      along every split axis (ST_ERR_BAD_SHAPE otherwise)
+ *   mode               0: average of the ksize^d window, 1: maximum
+ *   out_plan, out_bufs the plan st_plan_pooled returned for (in_plan, ksize,
+ *                      stride) (any output halo; only interiors are written)
+ *                      and its shards; dtype the input's or ST_F32
+ * Windows are read in lexicographic order and accumulated in fp32 (bf16
+ * outputs rounded to nearest even), so an output's bits do not depend on the
+ * shard plan.
+ */
+st_status st_pool_sharded(const st_plan* in_plan, const void* const* in_bufs, int32_t ksize, int32_t stride,
+                          int32_t mode, const st_plan* out_plan, void* const* out_bufs, void* stream);
+
 /* ------------------------------------------------------------- GroupNorm */
 
 /*

@@ -175,6 +175,21 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert wg(p.handle, misaligned, qd.handle, aligned, 3, dw, wws, need_w, s) == ALIGN
     assert wg(p.handle, aligned, qd.handle, nulls, 3, dw, wws, need_w, s) == INVALID
     assert wg(p.handle, aligned, qd.handle, aligned, 3, ctypes.c_void_p(0xB0004), wws, need_w, s) == ALIGN
+    # pooling: derived plan and its errors
+    pp = hsc.st_plan_shards(2, 1, 16, [8, 8], [[1, 1, 6], [8]], [1, 1], "bf16")
+    out = ctypes.c_void_p()
+    assert L.st_plan_pooled(pp.handle, 2, 2, None, 1, ctypes.byref(out)) == TOO_SMALL   # shard 1 holds no window start
+    assert L.st_plan_pooled(p.handle, 9, 2, None, 1, ctypes.byref(out)) == BAD_SHAPE     # window larger than the volume
+    assert L.st_plan_pooled(p.handle, 2, 0, None, 1, ctypes.byref(out)) == INVALID
+    assert L.st_plan_pooled(None, 2, 2, None, 1, ctypes.byref(out)) == INVALID
+    pq = hsc.st_plan_pooled(p, 2, 2)
+    assert pq.shards == ((2, 2), (4,))
+    assert L.st_pool_sharded(p.handle, aligned, 2, 2, 2, pq.handle, aligned, s) == INVALID   # mode
+    assert L.st_pool_sharded(p.handle, aligned, 3, 2, 0, pq.handle, aligned, s) == BAD_SHAPE  # not its pooled plan
+    assert L.st_pool_sharded(p.handle, misaligned, 2, 2, 0, pq.handle, aligned, s) == ALIGN
+    p0 = hsc.st_plan_shards(2, 1, 8, [8, 8], [[4, 4], [8]], [0, 0], "bf16")                # no halo
+    pq0 = hsc.st_plan_pooled(p0, 3, 2)
+    assert L.st_pool_sharded(p0.handle, aligned, 3, 2, 0, pq0.handle, aligned, s) == BAD_SHAPE
     # groupnorm backward
     bneed = L.st_groupnorm_backward_workspace_bytes(q.handle, 4)
     assert bneed > 0 and L.st_groupnorm_backward_workspace_bytes(None, 4) == 0
