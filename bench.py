@@ -4,10 +4,12 @@
 
 One step = halo pack + halo unpack + per-shard conv (all shards, one grouped
 launch) + GroupNorm (partials, combine, apply) over the whole sharded volume,
-inputs already resident in HBM.  Prints one JSON line.  Each library call of
-the timed steps is bracketed with HIP events on the stream it runs on, giving
-per-kernel average durations; the longest one is reported in `roofline`
-against its algorithmic bytes (or flops) per launch.  The CPU baseline is the
+inputs already resident in HBM.  Prints one JSON line.  The forward step is
+timed as a replayed HIP graph of those launches (--graph on, the default);
+per-kernel average durations come from the same number of eager steps, each
+library call bracketed with HIP events on the stream it runs on, and the
+longest one is reported in `roofline` against its algorithmic bytes (or
+flops) per launch.  The CPU baseline is the
 fp64 oracle timed on a bounded slab of the same workload on the host.
 """
 from __future__ import annotations
@@ -42,6 +44,9 @@ def parse():
                          "or a 2x average-pool downsampling of its input shards")
     ap.add_argument("--exchange", choices=("pack+unpack", "fused"), default="pack+unpack",
                     help="halo exchange as two copies through a message buffer, or one fused copy")
+    ap.add_argument("--graph", choices=("on", "off"), default="on",
+                    help="forward pass: time the step as a replayed HIP graph (per-stage times come from "
+                         "an eager run of the same steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the oracle's CPU sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -292,9 +297,13 @@ def main():
                    ("gn_apply", layer.norm_apply)]
 
     per_kernel_ms, ms_per_step, gpu_ms = time_stages(args, stages, stream)
+    eager_ms = ms_per_step
+    if args.pass_ == "forward" and args.graph == "on":
+        ms_per_step, gpu_ms = time_graph(args, stages)
 
     report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, METRIC if args.pass_ == "forward" else METRIC_DGRAD,
-           None if args.pass_ == "forward" else synth.make_weight(wl_fwd))
+           None if args.pass_ == "forward" else synth.make_weight(wl_fwd),
+           eager_ms=eager_ms if args.pass_ == "forward" and args.graph == "on" else None)
 
 
 def time_stages(args, stages, stream):
@@ -364,6 +373,37 @@ def bench_backward(args, wl_fwd):
     report(args, wl, fwd, per_kernel_ms, ms_per_step, gpu_ms, METRIC_BWD, None, dgrad_layer=bwd)
 
 
+def time_graph(args, stages):
+    """The step captured once in a HIP graph, W replays untimed, then K
+    replays bracketed by synchronisations (host clock) and events."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _, fn in stages:
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _, fn in stages:
+            fn()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / args.steps, start.elapsed_time(end) / args.steps
+
+
 def bench_pool(args, wl):
     """Downsampling of the layer's input shards: halo exchange (halo 1 = k - 1)
     and 'valid' 2x2(x2) average pooling into the output plan the library
@@ -431,7 +471,7 @@ def bench_pool(args, wl):
     print(json.dumps(out), flush=True)
 
 
-def report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, metric, w_fwd, dgrad_layer=None):
+def report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, metric, w_fwd, dgrad_layer=None, eager_ms=None):
     """One JSON line: throughput, per-stage rates and the longest stage against its roofline."""
     alg = algorithmic(wl, layer)
     if dgrad_layer is not None:
@@ -478,10 +518,13 @@ def report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, metric, w_fwd, d
         "data": "synthetic",
         "config": {"workload": wl.name, "shape": [wl.batch, wl.cin, *wl.spatial], "cout": wl.cout,
                    "kernel": wl.ksize, "shards": [list(s) for s in wl.shards], "halo": wl.halo, "exchange": args.exchange, "pass": args.pass_,
-                   "groups": wl.groups, "accumulate": "f32", "outputs": "f32"},
+                   "groups": wl.groups, "accumulate": "f32", "outputs": "f32",
+                   "launch": "hip graph replay" if eager_ms is not None else "eager"},
         "roofline": roof,
         "kernels": kernels,
     }
+    if eager_ms is not None:
+        out["eager_ms_per_step"] = round(eager_ms, 4)
     if not args.no_cpu_baseline:
         rows = args.cpu_rows or max(1, min(wl.spatial[0], int(5.0e5 // (wl.voxels // wl.spatial[0]) + 1)))
         out["cpu_baseline"] = cpu_baseline(wl, rows, w_fwd, backward=args.pass_ == "backward")
