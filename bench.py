@@ -45,8 +45,8 @@ def parse():
     ap.add_argument("--exchange", choices=("pack+unpack", "fused"), default="pack+unpack",
                     help="halo exchange as two copies through a message buffer, or one fused copy")
     ap.add_argument("--graph", choices=("on", "off"), default="on",
-                    help="forward pass: time the step as a replayed HIP graph (per-stage times come from "
-                         "an eager run of the same steps)")
+                    help="time the step as a replayed HIP graph (per-stage times come from an eager run of "
+                         "the same steps); the input-gradient pass always runs eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the oracle's CPU sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -370,7 +370,11 @@ def bench_backward(args, wl_fwd):
         ("conv", bwd.conv),
         ("wgrad", lambda: hsc.st_conv_wgrad(fwd.in_plan, fwd.x_bufs, bwd.in_plan, bwd.x_bufs, wl.ksize, dw, wws))]
     per_kernel_ms, ms_per_step, gpu_ms = time_stages(args, stages, torch.cuda.current_stream())
-    report(args, wl, fwd, per_kernel_ms, ms_per_step, gpu_ms, METRIC_BWD, None, dgrad_layer=bwd)
+    eager_ms = ms_per_step
+    if args.graph == "on":
+        ms_per_step, gpu_ms = time_graph(args, stages)
+    report(args, wl, fwd, per_kernel_ms, ms_per_step, gpu_ms, METRIC_BWD, None, dgrad_layer=bwd,
+           eager_ms=eager_ms if args.graph == "on" else None)
 
 
 def time_graph(args, stages):
@@ -435,6 +439,9 @@ def bench_pool(args, wl):
               ("halo_unpack", lambda: hsc.st_halo_unpack(p, msg, bufs, True)),
               ("pool", lambda: hsc.st_pool_sharded(p, bufs, k, s, "avg", q, outs))]
     per_kernel_ms, ms_per_step, gpu_ms = time_stages(args, stages, torch.cuda.current_stream())
+    eager_ms = ms_per_step
+    if args.graph == "on":
+        ms_per_step, gpu_ms = time_graph(args, stages)
     esize = 4 if wl.dtype == "f32" else 2
     out_vox = wl.batch * int(np.prod([sum(a) for a in q.shards]))
     alg = {"halo_pack": 2 * p.msg_bytes, "halo_unpack": 2 * p.msg_bytes,
@@ -452,8 +459,10 @@ def bench_pool(args, wl):
            "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic",
            "config": {"workload": wl.name, "shape": [wl.batch, wl.cin, *wl.spatial], "pool": "avg k2 s2",
                       "shards": [list(a) for a in wl.shards], "out_shards": [list(a) for a in q.shards],
-                      "pass": "pool"},
+                      "pass": "pool", "launch": "hip graph replay" if args.graph == "on" else "eager"},
            "roofline": roof, "kernels": kernels}
+    if args.graph == "on":
+        out["eager_ms_per_step"] = round(eager_ms, 4)
     if not args.no_cpu_baseline:
         rows = args.cpu_rows or max(2, min(wl.spatial[0], int(2.0e6 // (wl.voxels // wl.spatial[0]) + 1)) // 2 * 2)
         sub_shape = (rows,) + tuple(wl.spatial[1:])
