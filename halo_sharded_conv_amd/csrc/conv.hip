@@ -1675,15 +1675,70 @@ constexpr Instance inst_pairs() {
 using GemmImg256 = GemmCfg<256, 256, 3, 4, 96, 128>;
 // 3D 16->16 k5: 4x32 strips, 8 output planes per step (4 pairs per wave), whole shard depth per job
 using PairsVol16k5 = PairsCfg<16, 16, 5, 4, 32, 8>;
-// 2D 64->64 k3: 64-column strips, 8 rows per step (4 per wave), 32 rows per job, 4 waves,
-// two passes over K per step (32 output channels each)
+// 2D 64->64 k3: 64-column strips, 8 rows per step (4 per wave), 32 or 24 rows per job, 4
+// waves, two passes over K per step (32 output channels each)
 using RowsImg64 = RowsCfg<2, 64, 64, 3, 1, 64, 8, 32, 4, 2>;
+using RowsImg64J24 = RowsCfg<2, 64, 64, 3, 1, 64, 8, 24, 4, 2>;
 // 3D 32->32 k3: 4x32 strips, 4 planes per step (all per wave), 16 planes per job, 4 waves
 using RowsVol32 = RowsCfg<3, 32, 32, 3, 4, 32, 4, 16, 4, 1>;
 
+// The streaming kernel deals its jobs statically (a contiguous eighth per XCD,
+// strided over that XCD's workgroups), so the slowest workgroup sets the
+// time.  rows_deal_cost replays that deal for a job height and returns the
+// most slices any workgroup streams, counting each job's k - 1 prologue
+// slices.  The job height does not change any output: each output's
+// accumulation order depends only on its taps.
+template <class C>
+int64_t rows_deal_cost(const st_plan* p, int cus) {
+  constexpr int RA = C::NDIM == 3 ? 0 : 1;
+  std::vector<int32_t> cost;
+  for (const Shard& sd : p->shards) {
+    const int64_t rows = sd.ext[RA];
+    const int64_t chunks = (rows + C::RC - 1) / C::RC;
+    const int64_t strips = (C::NDIM == 3 ? (sd.ext[1] + C::BH - 1) / C::BH : 1) * ((sd.ext[2] + C::BW - 1) / C::BW);
+    for (int64_t n = 0; n < p->batch; ++n)
+      for (int64_t c = 0; c < chunks; ++c) {
+        const int64_t r = std::min<int64_t>(C::RC, rows - c * C::RC);
+        const int32_t steps = (int32_t)((r + C::TS - 1) / C::TS);
+        for (int64_t t = 0; t < strips; ++t) cost.push_back(steps * C::TS + C::KS - 1);
+        if (cost.size() > (1u << 22)) return INT64_MAX;          // too many jobs to replay: no preference
+      }
+  }
+  const int64_t total = (int64_t)cost.size();
+  int grid = (int)std::min<int64_t>(total, cus);
+  if (grid >= 8) grid &= ~7;
+  if (grid < 1) return 0;
+  std::vector<int64_t> load(grid, 0);
+  if (grid >= 8 && (grid & 7) == 0) {
+    const int per = grid >> 3;
+    for (int x = 0; x < 8; ++x) {
+      const int64_t b = total * x / 8, e = total * (x + 1) / 8;
+      for (int64_t j = b; j < e; ++j) load[x + 8 * (int)((j - b) % per)] += cost[j];
+    }
+  } else {
+    for (int64_t j = 0; j < total; ++j) load[j % grid] += cost[j];
+  }
+  return *std::max_element(load.begin(), load.end());
+}
+
+// image 64->64: the job height with the better-balanced deal for this plan
+st_status run_rows_img64(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
+  const int cus = device_cus();
+  if (rows_deal_cost<RowsImg64J24>(in_plan, cus) < rows_deal_cost<RowsImg64>(in_plan, cus))
+    return run_rows<RowsImg64J24>(a, in_plan, stream);
+  return run_rows<RowsImg64>(a, in_plan, stream);
+}
+
+template <class C>
+constexpr Instance inst_rows_with(st_status (*run)(ConvArgs&, const st_plan*, hipStream_t)) {
+  Instance i = inst_rows<C>();
+  i.run = run;
+  return i;
+}
+
 // one matrix-core instance per supported (ndim, cin, cout, k)
 const Instance kInstances[] = {
-    inst_rows<RowsImg64>(),
+    inst_rows_with<RowsImg64>(&run_rows_img64),
     inst_rows<RowsVol32>(),
     inst_pairs<PairsVol16k5>(),
     inst_gemm<GemmImg256>(),
