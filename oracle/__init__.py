@@ -11,13 +11,14 @@ kernels, linearity, torch fp64 as an independent library, GroupNorm closed
 forms, sharded == unsharded; the input gradient by the adjoint identity,
 brute force and torch's fp64 autograd; the weight gradient by the adjoint
 identity in the weights, brute force and torch's fp64 autograd; the GroupNorm backward by torch's
-fp64 autograd and central finite differences; pooling by brute force, torch's
-fp64 pooling, and the sharded form).  Nothing here is "parity unpinned".
+fp64 autograd and central finite differences; pooling and the strided conv by
+brute force, torch's fp64 ops, and the sharded form).  Nothing here is "parity unpinned".
 """
 from .reference import (  # noqa: F401
     widen, zero_pad, conv_valid, conv_same, conv_same_dgrad, conv_same_wgrad, conv_same_slabbed, conv_at,
     group_moments, group_norm, group_norm_apply, group_norm_backward, group_sums_onepass,
-    pool_valid, pooled_shard_sizes, pool_bruteforce,
+    pool_valid, pooled_shard_sizes, pool_bruteforce, conv_strided, strided_shard_sizes,
+    conv_strided_bruteforce,
     shard_offsets, shard_grid, padded_shard, halo_message, halo_directions,
     sharded_forward, conv_bruteforce, conv_dgrad_bruteforce, conv_wgrad_bruteforce,
     group_norm_bruteforce,

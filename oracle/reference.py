@@ -330,6 +330,50 @@ def pool_valid(x: np.ndarray, k: int, s: int, mode: str = "avg") -> np.ndarray:
     return acc / float(k ** d) if mode == "avg" else acc
 
 
+def conv_strided(x: np.ndarray, w: np.ndarray, s: int, bias=None) -> np.ndarray:
+    """Strided cross-correlation with zero padding p = (k-1)/2: the
+    shape-changing (downsampling) convolution.
+
+    y[n, j, o] = b[o] + sum_t sum_c w[o, c, t] * x[n, j*s + t - p, c], for
+    j = 0 .. (n_in + 2p - k) // s on every spatial axis (x zero outside the
+    grid).  s = 1 is conv_same.  x: [N, *S, Cin]; w: [Cout, Cin, k, .., k].
+    One tap at a time, lexicographic, each a plain matrix product over input
+    channels.
+    """
+    d = x.ndim - 2
+    cout, cin = w.shape[:2]
+    k = w.shape[2]
+    if k % 2 != 1:
+        raise ValueError("odd kernels only")
+    p = (k - 1) // 2
+    S = x.shape[1:1 + d]
+    out_S = tuple((n + 2 * p - k) // s + 1 for n in S)
+    xp = zero_pad(x, p)
+    y = np.zeros((x.shape[0], *out_S, cout), dtype=np.float64)
+    if bias is not None:
+        y += np.asarray(bias, np.float64)
+    for t in _taps(k, d):
+        window = xp[(slice(None),) + tuple(slice(t[a], t[a] + s * (out_S[a] - 1) + 1, s) for a in range(d))]
+        rows = np.ascontiguousarray(window).reshape(-1, cin)
+        wt = np.ascontiguousarray(w[(slice(None), slice(None)) + t]).T      # [Cin, Cout]
+        y += (rows @ wt).reshape(y.shape)
+    return y
+
+
+def strided_shard_sizes(sizes: Sequence[int], k: int, s: int) -> List[int]:
+    """Output sharding shape of conv_strided along one axis: output j belongs
+    to the shard whose interior holds its window's centre, input j*s."""
+    n = int(sum(sizes))
+    p = (k - 1) // 2
+    n_out = (n + 2 * p - k) // s + 1
+    out = []
+    for a, e in zip(shard_offsets(sizes), sizes):
+        first = -(-a // s)
+        end = min(-(-(a + e) // s), n_out)
+        out.append(end - first)
+    return out
+
+
 def pooled_shard_sizes(sizes: Sequence[int], k: int, s: int) -> List[int]:
     """Output sharding shape along one axis: output j belongs to the shard
     whose interior holds the first cell of its window, j*s."""
@@ -520,6 +564,30 @@ def conv_wgrad_bruteforce(x, dy, k):
                     for c in range(cin):
                         dw[(o, c) + t] += dy[(n, *pos, o)] * x[(n, *src, c)]
     return dw
+
+
+def conv_strided_bruteforce(x, w, s, bias=None):
+    """Scalar-loop strided 'same'-padded cross-correlation (tiny inputs)."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    n_, *spatial, cin = x.shape
+    d = len(spatial)
+    cout, k = w.shape[0], w.shape[2]
+    p = (k - 1) // 2
+    out_S = [(m + 2 * p - k) // s + 1 for m in spatial]
+    y = np.zeros((n_, *out_S, cout))
+    for n in range(n_):
+        for pos in itertools.product(*[range(m) for m in out_S]):
+            for o in range(cout):
+                acc = 0.0 if bias is None else float(bias[o])
+                for t in itertools.product(range(k), repeat=d):
+                    src = [pos[a] * s + t[a] - p for a in range(d)]
+                    if any(src[a] < 0 or src[a] >= spatial[a] for a in range(d)):
+                        continue
+                    for c in range(cin):
+                        acc += w[(o, c) + t] * x[(n, *src, c)]
+                y[(n, *pos, o)] = acc
+    return y
 
 
 def pool_bruteforce(x, k, s, mode="avg"):

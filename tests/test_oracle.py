@@ -388,6 +388,77 @@ def test_pool_pins_catch_mutants(name):
     assert not pin_pool(mutant), f"no pin caught the pooling mutant '{name}'"
 
 
+def pin_strided(conv, sizes_fn=oracle.strided_shard_sizes):
+    """The strided conv against scalar brute force, torch's fp64 conv with
+    stride and padding, the stride-1 case (conv_same), and the sharded form:
+    each shard's owned outputs (window centre in its interior) computed from
+    its halo-padded chunk equal the matching slice of the unsharded result."""
+    try:
+        ok = True
+        for d, k, s in [(2, 3, 2), (2, 5, 2), (3, 3, 2), (2, 3, 3), (3, 3, 1)]:
+            r = rng(900 + 100 * d + 10 * k + s)
+            spatial = (10, 9, 8) if d == 3 else (12, 13)
+            x = r.standard_normal((2, *spatial, 3))
+            w = r.uniform(-1, 1, size=(4, 3) + (k,) * d)
+            b = r.uniform(-1, 1, size=4)
+            y = conv(x, w, s, b)
+            small = (4, 5, 5) if d == 3 else (6, 7)
+            xs = r.standard_normal((1, *small, 3))
+            ok &= rel(conv(xs, w, s, b), oracle.conv_strided_bruteforce(xs, w, s, b)) <= 1e-13
+            f = torch.nn.functional.conv3d if d == 3 else torch.nn.functional.conv2d
+            yt = f(torch.from_numpy(np.moveaxis(x, -1, 1).copy()), torch.from_numpy(w), torch.from_numpy(b),
+                   stride=s, padding=k // 2)
+            ok &= rel(y, np.moveaxis(yt.numpy(), 1, -1)) <= 1e-12
+            if s == 1:
+                ok &= rel(y, oracle.conv_same(x, w, b)) <= 1e-13
+            sizes = [4, 3, spatial[0] - 7]
+            out_sizes = sizes_fn(sizes, k, s)
+            ok &= sum(out_sizes) == y.shape[1]
+            h = k // 2
+            xp = zero_pad_axis0(x, h)
+            o0 = 0
+            for a, e, m in zip(oracle.shard_offsets(sizes), sizes, out_sizes):
+                if m == 0:
+                    continue
+                padded = xp[:, a: a + e + 2 * h]         # the shard's chunk with its halo along axis 0
+                first = -(-a // s)
+                lo = first * s - a                        # first owned window, in padded coordinates
+                ok &= lo + (m - 1) * s + k <= padded.shape[1]
+                chunk = padded[:, lo: lo + (m - 1) * s + k]
+                # torch: no padding along axis 0 (the halo is in the chunk), 'same' padding elsewhere
+                pad = (0,) + (h,) * (d - 1)
+                part = f(torch.from_numpy(np.moveaxis(chunk, -1, 1).copy()), torch.from_numpy(w),
+                         torch.from_numpy(b), stride=s, padding=pad)
+                ok &= rel(np.moveaxis(part.numpy(), 1, -1), y[:, o0:o0 + m]) <= 1e-12
+                o0 += m
+        return bool(ok)
+    except (ValueError, IndexError, RuntimeError):
+        return False
+
+
+def test_strided_pins():
+    assert pin_strided(oracle.conv_strided)
+
+
+@pytest.mark.parametrize("name", ["stride ignored", "no padding offset", "owner by window start"])
+def test_strided_pins_catch_mutants(name):
+    def stride1(x, w, s, b=None):
+        return oracle.conv_strided(x, w, 1, b)
+
+    def nopad(x, w, s, b=None):
+        y = oracle.conv_strided(x, w, s, b)
+        return np.roll(y, 1, axis=1)
+
+    def start_owner(sizes, k, s):
+        return oracle.pooled_shard_sizes(sizes, k, s)
+
+    if name == "owner by window start":
+        assert not pin_strided(oracle.conv_strided, start_owner)
+        return
+    mutant = {"stride ignored": stride1, "no padding offset": nopad}[name]
+    assert not pin_strided(mutant), f"no pin caught the strided-conv mutant '{name}'"
+
+
 def test_dgrad_pins():
     assert pin_dgrad(oracle.conv_same_dgrad)
 
