@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sharded conv+GroupNorm voxels/s on 1 MI355X; % MFMA peak (conv), % HBM BW (halo/norm)"
 METRIC_DGRAD = "sharded conv input-gradient (halo exchange of dy + conv) voxels/s on 1 MI355X"
+METRIC_STRIDED = "sharded stride-2 conv (halo exchange + strided 'same' conv, fp32 FMA) input voxels/s on 1 MI355X"
 METRIC_POOL = "sharded 2x downsampling (halo exchange + 'valid' average pooling, k=2 s=2) input voxels/s on 1 MI355X"
 METRIC_BWD = ("sharded conv+GroupNorm backward (GroupNorm backward, halo exchange of dy, input gradient, "
               "weight gradient) voxels/s on 1 MI355X")
@@ -39,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--pass", dest="pass_", choices=("forward", "dgrad", "backward", "pool"), default="forward",
+    ap.add_argument("--pass", dest="pass_", choices=("forward", "dgrad", "backward", "pool", "strided"),
+                    default="forward",
                     help="the layer's forward step, the input gradient of its conv, its whole backward step, "
                          "or a 2x average-pool downsampling of its input shards")
     ap.add_argument("--exchange", choices=("pack+unpack", "fused"), default="pack+unpack",
@@ -72,7 +74,7 @@ STAGE_SOURCES = {                    # library sources that define each stage's 
     "conv": ("conv.hip", "internal.h"),
     "gn_partials": ("groupnorm.hip", "internal.h"), "gn_apply": ("groupnorm.hip", "internal.h"),
     "wgrad": ("wgrad.hip", "internal.h"), "gn_backward": ("groupnorm.hip", "internal.h"),
-    "pool": ("pool.hip", "internal.h"),
+    "pool": ("pool.hip", "internal.h"), "strided": ("strided.hip", "internal.h"),
 }
 
 
@@ -274,6 +276,8 @@ def main():
         return bench_backward(args, wl_fwd)
     if args.pass_ == "pool":
         return bench_pool(args, wl_fwd)
+    if args.pass_ == "strided":
+        return bench_strided(args, wl_fwd)
     if args.pass_ == "dgrad":
         # input gradient of the layer's conv: dy (Cout channels) -> dx (Cin)
         from halo_sharded_conv_amd.layer import dgrad_config
@@ -406,6 +410,62 @@ def time_graph(args, stages):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return wall * 1e3 / args.steps, start.elapsed_time(end) / args.steps
+
+
+def bench_strided(args, wl):
+    """Downsampling conv of the layer's input shards: halo exchange and a
+    stride-2 'same' conv with the layer's weights into the fp32 output plan
+    the library derives."""
+    import numpy as np
+    import torch
+
+    import halo_sharded_conv_amd as hsc
+    import oracle
+    import synth
+    from halo_sharded_conv_amd.layer import ShardedConvGN
+
+    s = 2
+    layer = ShardedConvGN(wl)
+    layer.load_input(synth.make_input(wl))
+    w = synth.make_weight(wl)
+    wf = oracle.widen(w, wl.dtype).astype(np.float32) if wl.dtype == "bf16" else w
+    wt = torch.from_numpy(np.ascontiguousarray(np.moveaxis(wf.reshape(wl.cout, wl.cin, -1), 2, 0).swapaxes(1, 2))).cuda()
+    q = hsc.st_plan_strided(layer.in_plan, wl.ksize, s, wl.cout)
+    outs = [torch.empty(q.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(q.num_shards)]
+    torch.cuda.synchronize()
+    stages = [("halo_pack", lambda: layer.exchange_pack()), ("halo_unpack", lambda: layer.exchange_unpack()),
+              ("strided", lambda: hsc.st_conv_strided_sharded(layer.in_plan, layer.x_bufs, wt, None, wl.ksize, s,
+                                                              q, outs))]
+    per_kernel_ms, ms_per_step, gpu_ms = time_stages(args, stages, torch.cuda.current_stream())
+    eager_ms = ms_per_step
+    if args.graph == "on":
+        ms_per_step, gpu_ms = time_graph(args, stages)
+    esize = 4 if wl.dtype == "f32" else 2
+    out_vox = wl.batch * int(np.prod([sum(a) for a in q.shards]))
+    flops = 2 * out_vox * wl.cin * wl.cout * wl.taps
+    alg = {"halo_pack": 2 * layer.in_plan.msg_bytes, "halo_unpack": 2 * layer.in_plan.msg_bytes,
+           "strided": wl.voxels * wl.cin * esize + out_vox * wl.cout * 4}
+    kernels = {}
+    for key, ms in per_kernel_ms.items():
+        gbs = alg[key] / (ms * 1e-3) / 1e9
+        kernels[key] = {"ms": round(ms, 5), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    tf = flops / (per_kernel_ms["strided"] * 1e-3) / 1e12
+    kernels["strided"].update({"TFLOP/s": round(tf, 2), "fp32_frac": round(tf / FP32_PEAK_TFLOPS, 4)})
+    # fp32 FMA on the vector units: the ALU roofline (157.3 TFLOP/s fp32 vector peak)
+    roof = {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / FP32_PEAK_TFLOPS, 4), "kernel": "strided", "traffic": load_traffic(wl, "strided")}
+    out = {"metric": METRIC_STRIDED, "value": wl.voxels / (ms_per_step * 1e-3), "unit": "voxels/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "gpu_ms_per_step": round(gpu_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": wl.name, "shape": [wl.batch, wl.cin, *wl.spatial], "cout": wl.cout,
+                      "kernel": wl.ksize, "stride": s, "operands": wl.dtype, "shards": [list(a) for a in wl.shards],
+                      "out_shards": [list(a) for a in q.shards], "pass": "strided",
+                      "launch": "hip graph replay" if args.graph == "on" else "eager"},
+           "roofline": roof, "kernels": kernels}
+    if args.graph == "on":
+        out["eager_ms_per_step"] = round(eager_ms, 4)
+    print(json.dumps(out), flush=True)
 
 
 def bench_pool(args, wl):

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libshardconv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["plan.cpp", "halo.hip", "conv.hip", "wgrad.hip", "groupnorm.hip", "pool.hip"]
+SOURCES = ["plan.cpp", "halo.hip", "conv.hip", "wgrad.hip", "groupnorm.hip", "pool.hip", "strided.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,0 +1,244 @@
+// Shape-changing sharded op: strided convolution (downsampling conv).
+//
+// "Technical summary: ShardTensor - domain parallelism for scientific machine
+// learning", section 2 "Design principles": each local chunk carries its own
+// shape, so an op that changes shapes derives the output chunks from the
+// input ones.  For a 'same'-padded cross-correlation with odd window k,
+// padding p = k/2 and stride s, output j along an axis reads inputs
+// [j*s - p, j*s + p]; it belongs to the shard whose interior holds the
+// window's centre j*s, so a shard with interior [a, a + e) owns outputs
+// [ceil(a / s), min(ceil((a + e) / s), n_out)) and reads at most p cells
+// beyond its interior on either side: the conv's usual halo of k/2 suffices.
+//
+// st_plan_strided derives the output plan; st_conv_strided_sharded runs one
+// launch over every shard on fp32 FMA: a thread takes one output position
+// and up to 64 output channels (blockIdx.y picks the channel block), reads
+// the window's input cells once and the weights as wave-uniform values, and
+// accumulates in a fixed order (taps lexicographic, input channels
+// ascending), so an output's bits do not depend on the shard plan.
+#include <algorithm>
+#include <cstdio>
+
+#include "internal.h"
+
+namespace st {
+namespace {
+
+constexpr int kOB = 64;             // output channels per thread (one block row of blockIdx.y)
+
+struct StrShard {
+  const char* in;                   // padded input shard at (n=0, window 0's first cell)
+  float* out;                       // output interior origin
+  int64_t is[3], isn;               // input element strides (d, h, w) and batch stride
+  int64_t os[3], osn;               // output element strides
+  int32_t oext[3];                  // output interior extents (d, h, w)
+  int64_t begin;                    // first output position of this shard
+};
+
+struct StrArgs {
+  int32_t nshards, batch, cin, cout, k, stride, ndim;
+  int64_t total;                    // output positions over all shards and samples
+  const float* w;                   // [taps][Cin][Cout] fp32
+  const float* bias;                // [Cout] or NULL
+  StrShard sh[ST_MAX_SHARDS];
+};
+
+template <typename T> __device__ __forceinline__ float ld1(const T* p);
+template <> __device__ __forceinline__ float ld1<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p) {
+  return __uint_as_float((uint32_t)*p << 16);
+}
+
+// OB output channels per thread (OB = min(64, Cout) rounded to what divides Cout)
+template <typename TI, int OB>
+__global__ __launch_bounds__(256) void conv_strided_kernel(const StrArgs a) {
+  const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int o0 = blockIdx.y * OB;
+  if (item >= a.total) return;
+  int s = 0;
+  while (s + 1 < a.nshards && a.sh[s + 1].begin <= item) ++s;
+  const StrShard& sh = a.sh[s];
+  int64_t r = item - sh.begin;
+  const int ow = (int)(r % sh.oext[2]);
+  r /= sh.oext[2];
+  const int oh = (int)(r % sh.oext[1]);
+  r /= sh.oext[1];
+  const int od = (int)(r % sh.oext[0]);
+  const int n = (int)(r / sh.oext[0]);
+  const TI* base = reinterpret_cast<const TI*>(sh.in) + n * sh.isn + (int64_t)od * a.stride * sh.is[0] +
+                   (int64_t)oh * a.stride * sh.is[1] + (int64_t)ow * a.stride * sh.is[2];
+  float acc[OB];
+#pragma unroll
+  for (int i = 0; i < OB; ++i) acc[i] = a.bias ? a.bias[o0 + i] : 0.f;
+  const int kd = a.ndim == 3 ? a.k : 1;
+  const float* wt = a.w + o0;
+  for (int tz = 0; tz < kd; ++tz)
+    for (int ty = 0; ty < a.k; ++ty)
+      for (int tx = 0; tx < a.k; ++tx) {
+        const TI* px = base + tz * sh.is[0] + ty * sh.is[1] + tx * sh.is[2];
+        for (int c = 0; c < a.cin; ++c) {
+          const float x = ld1<TI>(px + c);
+#pragma unroll
+          for (int i = 0; i < OB; ++i) acc[i] = fmaf(wt[i], x, acc[i]);
+          wt += a.cout;
+        }
+      }
+  float* o = sh.out + n * sh.osn + od * sh.os[0] + oh * sh.os[1] + ow * sh.os[2] + o0;
+#pragma unroll
+  for (int i = 0; i < OB; ++i) o[i] = acc[i];
+}
+
+// output sizes along one internal axis: output j owns the window centred at j*s
+bool strided_sizes(const std::vector<int64_t>& in, int64_t k, int64_t s, std::vector<int64_t>& out,
+                   std::vector<int64_t>& first) {
+  int64_t n = 0;
+  for (int64_t v : in) n += v;
+  const int64_t p = k / 2;
+  if (n + 2 * p < k) return false;
+  const int64_t n_out = (n + 2 * p - k) / s + 1;
+  out.clear();
+  first.clear();
+  int64_t a = 0;
+  for (int64_t e : in) {
+    const int64_t f = (a + s - 1) / s;
+    out.push_back(std::min((a + e + s - 1) / s, n_out) - f);
+    first.push_back(f);
+    a += e;
+  }
+  return true;
+}
+
+}  // namespace
+}  // namespace st
+
+using namespace st;
+
+extern "C" {
+
+st_status st_plan_strided(const st_plan* in_plan, int32_t ksize, int32_t stride, int32_t cout,
+                          const int32_t* out_halo_or_null, st_plan** out) {
+  auto err = [](st_status s, const std::string& m) { return fail(s, "st_plan_strided: " + m); };
+  if (!in_plan || !out) return err(ST_ERR_INVALID_ARG, "NULL argument");
+  *out = nullptr;
+  if (ksize < 1 || ksize % 2 == 0) return err(ST_ERR_UNSUPPORTED, "odd kernel sizes only");
+  if (stride < 1 || cout < 1) return err(ST_ERR_INVALID_ARG, "stride and cout must be >= 1");
+  const int nd = in_plan->ndim;
+  int64_t spatial[ST_MAX_NDIM];
+  int32_t counts[ST_MAX_NDIM], halo[ST_MAX_NDIM];
+  std::vector<int64_t> concat;
+  for (int a = 0; a < nd; ++a) {
+    std::vector<int64_t> sz, first;
+    if (!strided_sizes(in_plan->sizes[axis_of(in_plan, a)], ksize, stride, sz, first))
+      return err(ST_ERR_BAD_SHAPE, "window larger than the padded volume");
+    int64_t tot = 0;
+    for (size_t i = 0; i < sz.size(); ++i) {
+      if (sz[i] < 1) {
+        char buf[160];
+        std::snprintf(buf, sizeof buf, "axis %d shard %zu holds no window centre", a, i);
+        return err(ST_ERR_SHARD_TOO_SMALL, buf);
+      }
+      tot += sz[i];
+      concat.push_back(sz[i]);
+    }
+    spatial[a] = tot;
+    counts[a] = (int32_t)sz.size();
+    halo[a] = out_halo_or_null ? out_halo_or_null[a] : 0;
+  }
+  return st_plan_shards(nd, in_plan->batch, cout, spatial, counts, concat.data(), halo, ST_F32, out);
+}
+
+st_status st_conv_strided_sharded(const st_plan* in_plan, const void* const* in_bufs, const float* weight_tco,
+                                  const float* bias_or_null, int32_t ksize, int32_t stride,
+                                  const st_plan* out_plan, float* const* out_bufs, void* stream) {
+  auto err = [](st_status s, const std::string& m) { return fail(s, "st_conv_strided_sharded: " + m); };
+  if (!in_plan || !out_plan || !in_bufs || !out_bufs || !weight_tco)
+    return err(ST_ERR_INVALID_ARG, "NULL argument");
+  if (ksize < 1 || ksize % 2 == 0) return err(ST_ERR_UNSUPPORTED, "odd kernel sizes only");
+  if (stride < 1) return err(ST_ERR_INVALID_ARG, "stride must be >= 1");
+  if (out_plan->dtype != ST_F32) return err(ST_ERR_BAD_SHAPE, "outputs are fp32");
+  if (out_plan->ndim != in_plan->ndim || out_plan->batch != in_plan->batch ||
+      out_plan->shards.size() != in_plan->shards.size())
+    return err(ST_ERR_BAD_SHAPE, "output plan does not match the input plan");
+  if ((reinterpret_cast<uintptr_t>(weight_tco) & 3) || (bias_or_null && (reinterpret_cast<uintptr_t>(bias_or_null) & 3)))
+    return err(ST_ERR_ALIGNMENT, "misaligned weight or bias");
+  StrArgs a{};
+  a.nshards = (int)in_plan->shards.size();
+  a.batch = (int)in_plan->batch;
+  a.cin = (int)in_plan->channels;
+  a.cout = (int)out_plan->channels;
+  a.k = ksize;
+  a.stride = stride;
+  a.ndim = in_plan->ndim;
+  a.w = weight_tco;
+  a.bias = bias_or_null;
+  const int p = ksize / 2;
+  std::vector<int64_t> first[kAxes];
+  for (int ax = 0; ax < kAxes; ++ax) {
+    if (ax < kAxes - in_plan->ndim) {
+      first[ax].assign(in_plan->nshards[ax], 0);
+      continue;
+    }
+    std::vector<int64_t> sz;
+    if (!strided_sizes(in_plan->sizes[ax], ksize, stride, sz, first[ax]))
+      return err(ST_ERR_BAD_SHAPE, "window larger than the padded volume");
+    if (sz != out_plan->sizes[ax]) return err(ST_ERR_BAD_SHAPE, "output plan is not the strided plan of the input");
+  }
+  const int ie = in_plan->esize;
+  int64_t total = 0;
+  for (size_t i = 0; i < in_plan->shards.size(); ++i) {
+    if (!in_bufs[i] || !out_bufs[i]) return err(ST_ERR_INVALID_ARG, "NULL shard buffer");
+    if (!aligned16(in_bufs[i]) || !aligned16(out_bufs[i])) return err(ST_ERR_ALIGNMENT, "shard buffers must be 16-byte aligned");
+    const Shard& si = in_plan->shards[i];
+    const Shard& so = out_plan->shards[i];
+    StrShard& q = a.sh[i];
+    q.is[2] = a.cin;
+    q.is[1] = si.pad[2] * a.cin;
+    q.is[0] = si.pad[1] * q.is[1];
+    q.isn = si.pad[0] * q.is[0];
+    q.os[2] = a.cout;
+    q.os[1] = so.pad[2] * a.cout;
+    q.os[0] = so.pad[1] * q.os[1];
+    q.osn = so.pad[0] * q.os[0];
+    int64_t in_off = 0, out_off = 0;
+    for (int ax = 0; ax < kAxes; ++ax) {
+      const bool sp = ax >= kAxes - in_plan->ndim;
+      // first owned window's first cell (centre f*s, minus p) in padded coordinates
+      const int64_t lo = sp ? first[ax][si.grid[ax]] * stride - p - si.off[ax] + in_plan->halo[ax] : 0;
+      const int64_t hi = sp ? lo + (so.ext[ax] - 1) * stride + ksize : 1;
+      if (lo < 0 || hi > si.pad[ax]) return err(ST_ERR_BAD_SHAPE, "input halo smaller than ksize/2");
+      in_off += lo * q.is[ax];
+      out_off += out_plan->halo[ax] * q.os[ax];
+      q.oext[ax] = (int32_t)so.ext[ax];
+    }
+    q.in = static_cast<const char*>(in_bufs[i]) + in_off * ie;
+    q.out = out_bufs[i] + out_off;
+    q.begin = total;
+    total += a.batch * (int64_t)so.ext[0] * so.ext[1] * so.ext[2];
+  }
+  a.total = total;
+  if (total == 0) return ST_OK;
+  int ob = 1;
+  for (int c : {64, 32, 16, 8, 4, 2, 1})
+    if (a.cout % c == 0) { ob = c; break; }
+  const dim3 grid((unsigned)((total + 255) / 256), (unsigned)(a.cout / ob)), block(256);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = in_plan->dtype == ST_BF16;
+#define ST_STR_LAUNCH(OB)                                                                            \
+  do {                                                                                               \
+    if (bf) hipLaunchKernelGGL((conv_strided_kernel<uint16_t, OB>), grid, block, 0, st, a);          \
+    else hipLaunchKernelGGL((conv_strided_kernel<float, OB>), grid, block, 0, st, a);                \
+  } while (0)
+  switch (ob) {
+    case 64: ST_STR_LAUNCH(64); break;
+    case 32: ST_STR_LAUNCH(32); break;
+    case 16: ST_STR_LAUNCH(16); break;
+    case 8: ST_STR_LAUNCH(8); break;
+    case 4: ST_STR_LAUNCH(4); break;
+    case 2: ST_STR_LAUNCH(2); break;
+    default: ST_STR_LAUNCH(1); break;
+  }
+#undef ST_STR_LAUNCH
+  return launch_check("st_conv_strided_sharded: launch");
+}
+
+}  // extern "C"

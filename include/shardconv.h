@@ -292,6 +292,40 @@ st_status st_plan_pooled(const st_plan* in_plan, int32_t ksize, int32_t stride, 
 st_status st_pool_sharded(const st_plan* in_plan, const void* const* in_bufs, int32_t ksize, int32_t stride,
                           int32_t mode, const st_plan* out_plan, void* const* out_bufs, void* stream);
 
+/*
+ * st_plan_strided - the output plan of a strided 'same'-padded convolution of
+ * in_plan's shards (the downsampling conv).  Same passage as st_plan_pooled.
+ * Odd window ksize, padding ksize/2, stride on every spatial axis: output j
+ * along an axis of extent n reads inputs [j*stride - ksize/2, j*stride +
+ * ksize/2], j = 0 .. (n + 2*(ksize/2) - ksize) / stride, and belongs to the
+ * shard whose interior holds the window's centre j*stride.
+ *   cout               channels of the output plan
+ *   out_halo_or_null   ndim halo widths of the output plan (NULL: 0)
+ *   out                receives the fp32 output plan (st_plan_destroy)
+ * Errors: ST_ERR_SHARD_TOO_SMALL (a shard holds no window centre: it would
+ * own no output), ST_ERR_BAD_SHAPE, ST_ERR_UNSUPPORTED (even ksize),
+ * ST_ERR_INVALID_ARG.
+ */
+st_status st_plan_strided(const st_plan* in_plan, int32_t ksize, int32_t stride, int32_t cout,
+                          const int32_t* out_halo_or_null, st_plan** out);
+
+/*
+ * st_conv_strided_sharded - strided convolution of every shard from its
+ * halo-padded chunk (after the halo exchange; halo >= ksize/2 per split axis):
+ *   y[n, j, o] = bias[o] + sum_t sum_c W[o, c, t] * x[n, j*stride + t - ksize/2, c]
+ *   in_plan, in_bufs   padded input shards (fp32 or bf16 operands)
+ *   weight_tco         [taps][Cin][Cout] fp32 weights (taps lexicographic;
+ *                      bf16 weights widened exactly), read only
+ *   bias_or_null       Cout floats or NULL
+ *   out_plan, out_bufs the plan st_plan_strided returned for (in_plan, ksize,
+ *                      stride, Cout) and its fp32 shards (only interiors written)
+ * fp32 FMA in a fixed order (taps lexicographic, input channels ascending),
+ * so an output's bits do not depend on the shard plan.
+ */
+st_status st_conv_strided_sharded(const st_plan* in_plan, const void* const* in_bufs, const float* weight_tco,
+                                  const float* bias_or_null, int32_t ksize, int32_t stride,
+                                  const st_plan* out_plan, float* const* out_bufs, void* stream);
+
 /* ------------------------------------------------------------- GroupNorm */
 
 /*
