@@ -24,7 +24,6 @@
 namespace st {
 namespace {
 
-constexpr int kOB = 64;             // output channels per thread (one block row of blockIdx.y)
 
 struct StrShard {
   const char* in;                   // padded input shard at (n=0, window 0's first cell)
@@ -43,14 +42,29 @@ struct StrArgs {
   StrShard sh[ST_MAX_SHARDS];
 };
 
-template <typename T> __device__ __forceinline__ float ld1(const T* p);
-template <> __device__ __forceinline__ float ld1<float>(const float* p) { return *p; }
-template <> __device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p) {
-  return __uint_as_float((uint32_t)*p << 16);
+// CV consecutive input channels as fp32 (one 16-byte load when CV > 1)
+template <typename T, int CV> __device__ __forceinline__ void ldc(const T* p, float (&x)[CV]);
+template <> __device__ __forceinline__ void ldc<float, 1>(const float* p, float (&x)[1]) { x[0] = *p; }
+template <> __device__ __forceinline__ void ldc<float, 4>(const float* p, float (&x)[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+template <> __device__ __forceinline__ void ldc<uint16_t, 1>(const uint16_t* p, float (&x)[1]) {
+  x[0] = __uint_as_float((uint32_t)*p << 16);
+}
+template <> __device__ __forceinline__ void ldc<uint16_t, 8>(const uint16_t* p, float (&x)[8]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
 }
 
-// OB output channels per thread (OB = min(64, Cout) rounded to what divides Cout)
-template <typename TI, int OB>
+// OB output channels per thread (the largest of 64, 32, ... that divides Cout);
+// CV input channels per load (16 bytes when Cin allows)
+template <typename TI, int OB, int CV>
 __global__ __launch_bounds__(256) void conv_strided_kernel(const StrArgs a) {
   const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int o0 = blockIdx.y * OB;
@@ -76,11 +90,15 @@ __global__ __launch_bounds__(256) void conv_strided_kernel(const StrArgs a) {
     for (int ty = 0; ty < a.k; ++ty)
       for (int tx = 0; tx < a.k; ++tx) {
         const TI* px = base + tz * sh.is[0] + ty * sh.is[1] + tx * sh.is[2];
-        for (int c = 0; c < a.cin; ++c) {
-          const float x = ld1<TI>(px + c);
+        for (int c = 0; c < a.cin; c += CV) {
+          float x[CV];
+          ldc<TI, CV>(px + c, x);
 #pragma unroll
-          for (int i = 0; i < OB; ++i) acc[i] = fmaf(wt[i], x, acc[i]);
-          wt += a.cout;
+          for (int v = 0; v < CV; ++v) {
+#pragma unroll
+            for (int i = 0; i < OB; ++i) acc[i] = fmaf(wt[i], x[v], acc[i]);
+            wt += a.cout;
+          }
         }
       }
   float* o = sh.out + n * sh.osn + od * sh.os[0] + oh * sh.os[1] + ow * sh.os[2] + o0;
@@ -223,10 +241,13 @@ st_status st_conv_strided_sharded(const st_plan* in_plan, const void* const* in_
   const dim3 grid((unsigned)((total + 255) / 256), (unsigned)(a.cout / ob)), block(256);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = in_plan->dtype == ST_BF16;
+  const bool vec = bf ? a.cin % 8 == 0 : a.cin % 4 == 0;
 #define ST_STR_LAUNCH(OB)                                                                            \
   do {                                                                                               \
-    if (bf) hipLaunchKernelGGL((conv_strided_kernel<uint16_t, OB>), grid, block, 0, st, a);          \
-    else hipLaunchKernelGGL((conv_strided_kernel<float, OB>), grid, block, 0, st, a);                \
+    if (bf && vec) hipLaunchKernelGGL((conv_strided_kernel<uint16_t, OB, 8>), grid, block, 0, st, a); \
+    else if (bf) hipLaunchKernelGGL((conv_strided_kernel<uint16_t, OB, 1>), grid, block, 0, st, a);  \
+    else if (vec) hipLaunchKernelGGL((conv_strided_kernel<float, OB, 4>), grid, block, 0, st, a);    \
+    else hipLaunchKernelGGL((conv_strided_kernel<float, OB, 1>), grid, block, 0, st, a);             \
   } while (0)
   switch (ob) {
     case 64: ST_STR_LAUNCH(64); break;
