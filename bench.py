@@ -465,6 +465,21 @@ def bench_strided(args, wl):
            "roofline": roof, "kernels": kernels}
     if args.graph == "on":
         out["eager_ms_per_step"] = round(eager_ms, 4)
+    if not args.no_cpu_baseline:
+        rows = args.cpu_rows or max(s, min(wl.spatial[0], int(1.0e6 // (wl.voxels // wl.spatial[0]) + 1)) // s * s)
+        sub_shape = (rows,) + tuple(wl.spatial[1:])
+        sub = synth.small_variant(wl, sub_shape, [(n,) for n in sub_shape], name_suffix="cpu_sample")
+        xsub = oracle.widen(synth.make_input(sub), wl.dtype)
+        wsub = oracle.widen(w, wl.dtype)
+        from threadpoolctl import threadpool_info
+        t0 = time.perf_counter()
+        y = oracle.conv_strided(xsub, wsub, s)
+        dt = time.perf_counter() - t0
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        out["cpu_baseline"] = {"value": sub.voxels / dt, "unit": "voxels/s", "cores": threads, "kind": "oracle",
+                               "sample": f"first {rows} rows of the outermost axis ({sub.voxels} input voxels, "
+                                         f"stride-{s} conv in fp64 numpy, {dt:.2f} s)", "seconds": round(dt, 3),
+                               "checksum": float(np.abs(y).sum())}
     print(json.dumps(out), flush=True)
 
 

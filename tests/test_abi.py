@@ -190,6 +190,21 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     p0 = hsc.st_plan_shards(2, 1, 8, [8, 8], [[4, 4], [8]], [0, 0], "bf16")                # no halo
     pq0 = hsc.st_plan_pooled(p0, 3, 2)
     assert L.st_pool_sharded(p0.handle, aligned, 3, 2, 0, pq0.handle, aligned, s) == BAD_SHAPE
+    # strided conv: derived plan and its errors
+    assert L.st_plan_strided(pp.handle, 3, 2, 8, None, ctypes.byref(out)) == TOO_SMALL    # a shard holds no centre
+    assert L.st_plan_strided(p.handle, 4, 2, 8, None, ctypes.byref(out)) == UNSUPPORTED
+    assert L.st_plan_strided(p.handle, 3, 0, 8, None, ctypes.byref(out)) == INVALID
+    sq = hsc.st_plan_strided(p, 3, 2, 16)
+    assert sq.shards == ((2, 2), (4,)) and sq.channels == 16
+    wt = ctypes.c_void_p(0xF0000)
+    cs = L.st_conv_strided_sharded
+    assert cs(p.handle, aligned, None, None, 3, 2, sq.handle, aligned, s) == INVALID
+    assert cs(p.handle, aligned, wt, None, 3, 3, sq.handle, aligned, s) == BAD_SHAPE          # not its strided plan
+    assert cs(p.handle, aligned, wt, None, 2, 2, sq.handle, aligned, s) == UNSUPPORTED
+    assert cs(p.handle, misaligned, wt, None, 3, 2, sq.handle, aligned, s) == ALIGN
+    assert cs(p.handle, aligned, wt, None, 3, 2, p.handle, aligned, s) == BAD_SHAPE            # bf16 output plan
+    sq0 = hsc.st_plan_strided(p0, 3, 2, 8)
+    assert cs(p0.handle, aligned, wt, None, 3, 2, sq0.handle, aligned, s) == BAD_SHAPE         # input halo 0 < 1
     # groupnorm backward
     bneed = L.st_groupnorm_backward_workspace_bytes(q.handle, 4)
     assert bneed > 0 and L.st_groupnorm_backward_workspace_bytes(None, 4) == 0
