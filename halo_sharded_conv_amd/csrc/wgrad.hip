@@ -80,7 +80,8 @@ __device__ __forceinline__ void decode_row(const WgArgs& a, int row, int& s, int
 // matrix-core kernel
 // --------------------------------------------------------------------------
 
-template <int NDIM_, int K_, int CIN_, int COUT_, int WGM_, int WGN_, int WM_, int WN_, int TILES_M_, int TILES_N_>
+template <int NDIM_, int K_, int CIN_, int COUT_, int WGM_, int WGN_, int WM_, int WN_, int TILES_M_, int TILES_N_,
+          int LW_ = 0>
 struct WgCfg {
   static constexpr int NDIM = NDIM_, K = K_, CIN = CIN_, COUT = COUT_;
   static constexpr int WGM = WGM_, WGN = WGN_, WM = WM_, WN = WN_;
@@ -91,7 +92,8 @@ struct WgCfg {
   static constexpr int MB = (MR + 31) / 32, NB = (NR + 31) / 32;
   static constexpr int TM = WGM * WM, TN = WGN * WN;     // blocks per tile
   static constexpr int TILES_M = TILES_M_, TILES_N = TILES_N_;
-  static constexpr int NW = WGM * WGN, NT = 64 * NW;
+  static constexpr int NWC = WGM * WGN;                  // waves with MFMA work
+  static constexpr int NW = NWC + LW_, NT = 64 * NW;    // plus LW_ waves that only load
   static constexpr int COLS = 64;                        // chunk width along W
   static constexpr int RS = COLS * 2;                    // LDS row stride (bytes), 16-byte slots permuted
   static_assert(RS == 128, "8 slots of 16 bytes per row");
@@ -177,7 +179,8 @@ __global__ __launch_bounds__(C::NT) void wgrad_mfma(const WgArgs a) {
   const int part = blockIdx.x / ntile;
   const int m0 = (tile / C::TILES_N) * C::TM * 32;        // first A row of the tile
   const int n0 = (tile % C::TILES_N) * C::TN * 32;        // first B row of the tile
-  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int wm = (wave % C::NWC) / C::WGN, wn = (wave % C::NWC) % C::WGN;
+  const bool mma = wave < C::NWC;                       // a loader-only wave skips the MFMAs
 
   f32x16 acc[C::WM][C::WN];
 #pragma unroll
@@ -290,18 +293,20 @@ __global__ __launch_bounds__(C::NT) void wgrad_mfma(const WgArgs a) {
     const WgChunk c2 = next_chunk<C::K>(a, c1, C::COLS, row_end);
     const int nks = (min(C::COLS, c0.W + 2 * C::P - c0.j0) + 15) / 16;
     bf16x8 av0[C::WM], bv0[C::WN], av1[C::WM], bv1[C::WN];
-    frags(cur, 0, av0, bv0);
+    if (mma) frags(cur, 0, av0, bv0);
     if (c1.valid) store(nxt, ra0, rb0);                    // the next chunk, while this one computes
     fetch(c2, ra0, rb0);                                    // and the one after it
-    if (nks > 1) frags(cur, 1, av1, bv1);
-    mfmas(av0, bv0);
-    if (nks > 1) {
-      if (nks > 2) frags(cur, 2, av0, bv0);
-      mfmas(av1, bv1);
-      if (nks > 2) {
-        if (nks > 3) frags(cur, 3, av1, bv1);
-        mfmas(av0, bv0);
-        if (nks > 3) mfmas(av1, bv1);
+    if (mma) {
+      if (nks > 1) frags(cur, 1, av1, bv1);
+      mfmas(av0, bv0);
+      if (nks > 1) {
+        if (nks > 2) frags(cur, 2, av0, bv0);
+        mfmas(av1, bv1);
+        if (nks > 2) {
+          if (nks > 3) frags(cur, 3, av1, bv1);
+          mfmas(av0, bv0);
+          if (nks > 3) mfmas(av1, bv1);
+        }
       }
     }
     __syncthreads();
@@ -315,6 +320,7 @@ __global__ __launch_bounds__(C::NT) void wgrad_mfma(const WgArgs a) {
   }
 
   // partial dw of this partition: C[(tx, o)][(r, c)] -> [o][c][r * K + tx]
+  if (!mma) return;
   float* out = a.partial + (size_t)part * C::COUT * C::CIN * C::TAPS;
 #pragma unroll
   for (int i = 0; i < C::WM; ++i) {
@@ -391,8 +397,8 @@ __global__ void wgrad_reduce(const float* __restrict__ partial, int parts, int64
 
 // image 64->64 k3: 6x6 blocks, 2x2 waves of 3x3
 using WgImg64 = WgCfg<2, 3, 64, 64, 2, 2, 3, 3, 1, 1>;
-// 3D 32->32 k3: 3x9 blocks, 1x3 waves of 3x3
-using WgVol32 = WgCfg<3, 3, 32, 32, 1, 3, 3, 3, 1, 1>;
+// 3D 32->32 k3: 3x9 blocks, 1x3 waves of 3x3, and a fourth wave that only loads
+using WgVol32 = WgCfg<3, 3, 32, 32, 1, 3, 3, 3, 1, 1, 1>;
 // 3D 16->16 k5: 3x13 blocks in two tiles of 3x8, 1x4 waves of 3x2
 using WgVol16k5 = WgCfg<3, 5, 16, 16, 1, 4, 3, 2, 1, 2>;
 // image 256->256 k3: 24x24 blocks in 4x4 tiles of 6x6, 2x2 waves of 3x3
