@@ -12,7 +12,9 @@ read back), so each error belongs to one stage:
     fp32 dy before rounding; the padded bf16 dy equals its rounding);
   * dx vs oracle.conv_same_dgrad, dw vs oracle.conv_same_wgrad (1e-2);
   * the 2x average pooling of the input vs oracle.pool_valid (bf16 rounding
-    bound) and the derived output shard sizes vs oracle.pooled_shard_sizes.
+    bound) and the derived output shard sizes vs oracle.pooled_shard_sizes;
+  * the stride-2 conv of the input vs oracle.conv_strided over the whole
+    output (1e-5), with the derived shard sizes.
 """
 import numpy as np
 import pytest
@@ -104,3 +106,30 @@ def test_full_size_pooling():
     excess = np.abs(g - want) - (2.0 ** -8 * np.abs(want) + 1e-6 * rms)
     say(f"  max|err|/rms {rel_err(g, want):.2e}; worst excess over the bf16 rounding bound {excess.max():.2e}")
     assert excess.max() <= 0.0
+
+
+def test_full_size_strided_conv():
+    wl = synth.workload(NAME)
+    say(f"full-size stride-2 conv {NAME}")
+    x, w = synth.make_input(wl), synth.make_weight(wl)
+    layer = ShardedConvGN(wl)
+    layer.load_input(x)
+    layer.exchange()
+    q = hsc.st_plan_strided(layer.in_plan, wl.ksize, 2, wl.cout)
+    for a in range(wl.ndim):
+        assert list(q.shards[a]) == oracle.strided_shard_sizes(wl.shards[a], wl.ksize, 2)
+    wf = oracle.widen(w, wl.dtype)
+    wt = torch.from_numpy(np.ascontiguousarray(
+        np.moveaxis(wf.astype(np.float32).reshape(wl.cout, wl.cin, -1), 2, 0).swapaxes(1, 2))).cuda()
+    outs = [torch.empty(q.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(q.num_shards)]
+    hsc.st_conv_strided_sharded(layer.in_plan, layer.x_bufs, wt, None, wl.ksize, 2, q, outs)
+    torch.cuda.synchronize()
+    got = np.empty((wl.batch, *[sum(a) for a in q.shards], wl.cout), np.float32)
+    for i in range(q.num_shards):
+        inf = q.shard_info(i)
+        got[tuple([slice(None)] + [slice(o, o + e) for o, e in zip(inf["offset"], inf["extent"])])] = \
+            outs[i].view(q.padded_shape(i)).cpu().numpy()
+    want = oracle.conv_strided(oracle.widen(x, wl.dtype), wf, 2)
+    err = rel_err(got, want)
+    say(f"  max|err|/rms {err:.2e} (tolerance 1e-5)")
+    assert err <= 1e-5
