@@ -18,7 +18,7 @@ from .reference import (  # noqa: F401
     widen, zero_pad, conv_valid, conv_same, conv_same_dgrad, conv_same_wgrad, conv_same_slabbed, conv_at,
     group_moments, group_norm, group_norm_apply, group_norm_backward, group_sums_onepass,
     pool_valid, pooled_shard_sizes, pool_bruteforce, conv_strided, strided_shard_sizes,
-    conv_strided_bruteforce,
+    conv_strided_bruteforce, conv_transposed, conv_transposed_bruteforce,
     shard_offsets, shard_grid, padded_shard, halo_message, halo_directions,
     sharded_forward, conv_bruteforce, conv_dgrad_bruteforce, conv_wgrad_bruteforce,
     group_norm_bruteforce,

@@ -360,6 +360,40 @@ def conv_strided(x: np.ndarray, w: np.ndarray, s: int, bias=None) -> np.ndarray:
     return y
 
 
+def conv_transposed(y: np.ndarray, w: np.ndarray, s: int) -> np.ndarray:
+    """Transposed (upsampling) convolution: the adjoint of conv_strided.
+
+    With w [Cout, Cin, k, .., k] and p = (k-1)/2, every input cell i of y
+    (Cout channels) adds sum_o w[o, c, t] * y[n, i, o] to output cell
+    j = i*s + t - p (Cin channels) for every tap t; the output has s times the
+    input's extent on every axis (cells j outside it are dropped).  So
+    <conv_strided(x, w, s), y> = <x, conv_transposed(y, w, s)> for x of that
+    extent.  One tap at a time, lexicographic, each a plain matrix product
+    over the input channels.
+    """
+    d = y.ndim - 2
+    cout, cin = w.shape[:2]
+    k = w.shape[2]
+    if k % 2 != 1:
+        raise ValueError("odd kernels only")
+    if y.shape[-1] != cout:
+        raise ValueError("channel mismatch")
+    p = (k - 1) // 2
+    S = y.shape[1:1 + d]
+    out_S = tuple(n * s for n in S)
+    # scatter into an output padded by p on both sides, then crop
+    big = np.zeros((y.shape[0], *[m + 2 * p + s for m in out_S], cin), dtype=np.float64)
+    rows = np.ascontiguousarray(y).reshape(-1, cout)
+    for t in _taps(k, d):
+        wt = np.ascontiguousarray(w[(slice(None), slice(None)) + t])        # [Cout, Cin]
+        contrib = (rows @ wt).reshape(y.shape[:-1] + (cin,))
+        # j + p = i*s + t in the padded output
+        idx = (slice(None),) + tuple(slice(t[a], t[a] + s * (S[a] - 1) + 1, s) for a in range(d))
+        big[idx] += contrib
+    crop = (slice(None),) + tuple(slice(p, p + out_S[a]) for a in range(d))
+    return big[crop]
+
+
 def strided_shard_sizes(sizes: Sequence[int], k: int, s: int) -> List[int]:
     """Output sharding shape of conv_strided along one axis: output j belongs
     to the shard whose interior holds its window's centre, input j*s."""
@@ -588,6 +622,29 @@ def conv_strided_bruteforce(x, w, s, bias=None):
                         acc += w[(o, c) + t] * x[(n, *src, c)]
                 y[(n, *pos, o)] = acc
     return y
+
+
+def conv_transposed_bruteforce(y, w, s):
+    """Scalar-loop transposed convolution (tiny inputs): each input cell
+    scatters w[o, c, t] * y[o] onto output cell i*s + t - p."""
+    y = np.asarray(y, np.float64)
+    w = np.asarray(w, np.float64)
+    n_, *spatial, cout = y.shape
+    d = len(spatial)
+    cin, k = w.shape[1], w.shape[2]
+    p = (k - 1) // 2
+    out_S = [m * s for m in spatial]
+    x = np.zeros((n_, *out_S, cin))
+    for n in range(n_):
+        for pos in itertools.product(*[range(m) for m in spatial]):
+            for t in itertools.product(range(k), repeat=d):
+                dst = [pos[a] * s + t[a] - p for a in range(d)]
+                if any(dst[a] < 0 or dst[a] >= out_S[a] for a in range(d)):
+                    continue
+                for o in range(cout):
+                    for c in range(cin):
+                        x[(n, *dst, c)] += w[(o, c) + t] * y[(n, *pos, o)]
+    return x
 
 
 def pool_bruteforce(x, k, s, mode="avg"):

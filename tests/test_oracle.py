@@ -436,6 +436,66 @@ def pin_strided(conv, sizes_fn=oracle.strided_shard_sizes):
         return False
 
 
+def pin_transposed(convt, conv=oracle.conv_strided):
+    """The transposed conv against the adjoint identity with the strided conv
+    <conv_strided(x, w, s), y> = <x, conv_transposed(y, w, s)>, scalar-loop
+    brute force, torch's fp64 conv_transpose (padding k/2, output padding
+    s - 1) and the sharded form: a shard's outputs [a*s, (a+e)*s) computed
+    from its halo-padded input chunk equal the slice of the whole result."""
+    try:
+        ok = True
+        for d, k, s in [(2, 3, 2), (2, 5, 2), (3, 3, 2), (2, 3, 3), (3, 3, 1)]:
+            r = rng(950 + 100 * d + 10 * k + s)
+            spatial = (5, 4, 6) if d == 3 else (7, 6)
+            y = r.standard_normal((2, *spatial, 4))
+            w = r.uniform(-1, 1, size=(4, 3) + (k,) * d)
+            xt = convt(y, w, s)
+            x = r.standard_normal(xt.shape)
+            lhs = float(np.sum(conv(x, w, s) * y))
+            rhs = float(np.sum(x * xt))
+            ok &= abs(lhs - rhs) <= 1e-12 * float(np.sum(np.abs(conv(x, w, s) * y)))
+            ys = r.standard_normal((1, *[max(2, m - 3) for m in spatial], 4))
+            ok &= rel(convt(ys, w, s), oracle.conv_transposed_bruteforce(ys, w, s)) <= 1e-13
+            f = torch.nn.functional.conv_transpose3d if d == 3 else torch.nn.functional.conv_transpose2d
+            tt = f(torch.from_numpy(np.moveaxis(y, -1, 1).copy()), torch.from_numpy(w), stride=s, padding=k // 2,
+                   output_padding=s - 1)
+            ok &= rel(xt, np.moveaxis(tt.numpy(), 1, -1)) <= 1e-12
+            # sharded along axis 0: shard [a, a+e) of y owns outputs [a*s, (a+e)*s)
+            sizes = [2, 3, spatial[0] - 5]
+            h = k // 2
+            yp = zero_pad_axis0(y, h)
+            for a, e in zip(oracle.shard_offsets(sizes), sizes):
+                if e == 0:
+                    continue
+                chunk = yp[:, a: a + e + 2 * h]          # the shard's input with its halo along axis 0
+                part = convt(chunk, w, s)[:, h * s: h * s + e * s]
+                ok &= rel(part, xt[:, a * s: (a + e) * s]) <= 1e-12
+        return bool(ok)
+    except (ValueError, IndexError, RuntimeError):
+        return False
+
+
+def test_transposed_pins():
+    assert pin_transposed(oracle.conv_transposed)
+
+
+@pytest.mark.parametrize("name", ["taps not flipped", "stride ignored", "no crop offset"])
+def test_transposed_pins_catch_mutants(name):
+    def unflipped(y, w, s):
+        return oracle.conv_transposed(y, np.flip(w, axis=tuple(range(2, w.ndim))).copy(), s)
+
+    def stride1(y, w, s):
+        out = oracle.conv_transposed(y, w, 1)
+        reps = [1] + [s] * (y.ndim - 2) + [1]
+        return np.kron(out, np.ones(reps)) if s > 1 else out
+
+    def shifted(y, w, s):
+        return np.roll(oracle.conv_transposed(y, w, s), 1, axis=1)
+
+    mutant = {"taps not flipped": unflipped, "stride ignored": stride1, "no crop offset": shifted}[name]
+    assert not pin_transposed(mutant), f"no pin caught the transposed-conv mutant '{name}'"
+
+
 def test_strided_pins():
     assert pin_strided(oracle.conv_strided)
 
