@@ -26,6 +26,8 @@ sys.path.insert(0, ROOT)
 METRIC = "sharded conv+GroupNorm voxels/s on 1 MI355X; % MFMA peak (conv), % HBM BW (halo/norm)"
 METRIC_DGRAD = "sharded conv input-gradient (halo exchange of dy + conv) voxels/s on 1 MI355X"
 METRIC_STRIDED = "sharded stride-2 conv (halo exchange + strided 'same' conv, fp32 FMA) input voxels/s on 1 MI355X"
+METRIC_TRANSPOSED = ("sharded stride-2 transposed conv (halo exchange + upsampling conv, fp32 FMA) output voxels/s "
+                     "on 1 MI355X")
 METRIC_POOL = "sharded 2x downsampling (halo exchange + 'valid' average pooling, k=2 s=2) input voxels/s on 1 MI355X"
 METRIC_BWD = ("sharded conv+GroupNorm backward (GroupNorm backward, halo exchange of dy, input gradient, "
               "weight gradient) voxels/s on 1 MI355X")
@@ -40,10 +42,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--pass", dest="pass_", choices=("forward", "dgrad", "backward", "pool", "strided"),
+    ap.add_argument("--pass", dest="pass_", choices=("forward", "dgrad", "backward", "pool", "strided", "transposed"),
                     default="forward",
                     help="the layer's forward step, the input gradient of its conv, its whole backward step, "
-                         "or a 2x average-pool downsampling of its input shards")
+                         "a 2x average-pool downsampling or a stride-2 conv of its input shards, or a stride-2 "
+                         "transposed conv from half its resolution up to it")
     ap.add_argument("--exchange", choices=("pack+unpack", "fused"), default="pack+unpack",
                     help="halo exchange as two copies through a message buffer, or one fused copy")
     ap.add_argument("--graph", choices=("on", "off"), default="on",
@@ -65,6 +68,7 @@ STAGE_KERNELS = {                    # kernel-name fragments of each library sta
     "conv": ("conv_rows", "conv_pairs", "conv_gemm", "conv_direct"),
     "gn_partials": ("gn_max", "gn_stats"), "gn_apply": ("gn_apply",),
     "wgrad": ("wgrad_mfma", "wgrad_direct"), "gn_backward": ("gn_max", "gnb_"), "pool": ("pool_kernel",),
+    "strided": ("conv_strided",), "transposed": ("conv_transposed",),
 }
 
 
@@ -75,6 +79,7 @@ STAGE_SOURCES = {                    # library sources that define each stage's 
     "gn_partials": ("groupnorm.hip", "internal.h"), "gn_apply": ("groupnorm.hip", "internal.h"),
     "wgrad": ("wgrad.hip", "internal.h"), "gn_backward": ("groupnorm.hip", "internal.h"),
     "pool": ("pool.hip", "internal.h"), "strided": ("strided.hip", "internal.h"),
+    "transposed": ("strided.hip", "internal.h"),
 }
 
 
@@ -278,6 +283,8 @@ def main():
         return bench_pool(args, wl_fwd)
     if args.pass_ == "strided":
         return bench_strided(args, wl_fwd)
+    if args.pass_ == "transposed":
+        return bench_transposed(args, wl_fwd)
     if args.pass_ == "dgrad":
         # input gradient of the layer's conv: dy (Cout channels) -> dx (Cin)
         from halo_sharded_conv_amd.layer import dgrad_config
@@ -480,6 +487,90 @@ def bench_strided(args, wl):
                                "sample": f"first {rows} rows of the outermost axis ({sub.voxels} input voxels, "
                                          f"stride-{s} conv in fp64 numpy, {dt:.2f} s)", "seconds": round(dt, 3),
                                "checksum": float(np.abs(y).sum())}
+    print(json.dumps(out), flush=True)
+
+
+def bench_transposed(args, wl_out):
+    """Upsampling conv of a decoder stage: an input at half the layer's
+    resolution (every shard's extents halved, Cin channels, the layer's
+    operand type, halo ksize/2), halo exchange, and a stride-2 transposed conv
+    into the fp32 output plan the library derives, which has the layer's
+    volume and sharding shapes."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import halo_sharded_conv_amd as hsc
+    import oracle
+    import synth
+    from halo_sharded_conv_amd.layer import ShardedConvGN
+
+    s = 2
+    if any(e % s for a in wl_out.shards for e in a):
+        raise SystemExit(f"{wl_out.name}: shard sizes are not multiples of the stride")
+    wl = dataclasses.replace(wl_out, name=wl_out.name + "_half", spatial=tuple(n // s for n in wl_out.spatial),
+                             shards=tuple(tuple(e // s for e in a) for a in wl_out.shards))
+    layer = ShardedConvGN(wl)
+    layer.load_input(synth.make_input(wl))
+    w = synth.make_weight(wl)                                   # [Cout][Cin][k..]: read as W[o = Cin side][c]
+    wf = (oracle.widen(w, wl.dtype) if wl.dtype == "bf16" else w).astype(np.float32)
+    wf = np.ascontiguousarray(np.swapaxes(wf, 0, 1))             # W [Cy = Cin][Cx = Cout][k..]
+    wt = torch.from_numpy(np.ascontiguousarray(np.moveaxis(wf.reshape(wl.cin, wl.cout, -1), 2, 0))).cuda()
+    q = hsc.st_plan_transposed(layer.in_plan, wl.ksize, s, wl.cout)
+    outs = [torch.empty(q.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(q.num_shards)]
+    torch.cuda.synchronize()
+    stages = [("halo_pack", lambda: layer.exchange_pack()), ("halo_unpack", lambda: layer.exchange_unpack()),
+              ("transposed", lambda: hsc.st_conv_transposed_sharded(layer.in_plan, layer.x_bufs, wt, None, wl.ksize,
+                                                                    s, q, outs))]
+    per_kernel_ms, ms_per_step, gpu_ms = time_stages(args, stages, torch.cuda.current_stream())
+    eager_ms = ms_per_step
+    if args.graph == "on":
+        ms_per_step, gpu_ms = time_graph(args, stages)
+    esize = 4 if wl.dtype == "f32" else 2
+    out_vox = wl.batch * int(np.prod([sum(a) for a in q.shards]))
+    # taps that reach an output, summed over the s^d phases of one input cell
+    p = wl.ksize // 2
+    per_axis = sum(len(range((r + p) % s, wl.ksize, s)) for r in range(s))
+    flops = 2 * wl.voxels * per_axis ** wl.ndim * wl.cin * wl.cout
+    alg = {"halo_pack": 2 * layer.in_plan.msg_bytes, "halo_unpack": 2 * layer.in_plan.msg_bytes,
+           "transposed": wl.voxels * wl.cin * esize + out_vox * wl.cout * 4}
+    kernels = {}
+    for key, ms in per_kernel_ms.items():
+        gbs = alg[key] / (ms * 1e-3) / 1e9
+        kernels[key] = {"ms": round(ms, 5), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    tf = flops / (per_kernel_ms["transposed"] * 1e-3) / 1e12
+    kernels["transposed"].update({"TFLOP/s": round(tf, 2), "fp32_frac": round(tf / FP32_PEAK_TFLOPS, 4)})
+    roof = {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / FP32_PEAK_TFLOPS, 4), "kernel": "transposed",
+            "traffic": load_traffic(wl_out, "transposed")}
+    out = {"metric": METRIC_TRANSPOSED, "value": out_vox / (ms_per_step * 1e-3), "unit": "voxels/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "gpu_ms_per_step": round(gpu_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": wl_out.name, "input_shape": [wl.batch, wl.cin, *wl.spatial], "cout": wl.cout,
+                      "kernel": wl.ksize, "stride": s, "operands": wl.dtype,
+                      "in_shards": [list(a) for a in wl.shards], "out_shards": [list(a) for a in q.shards],
+                      "pass": "transposed", "launch": "hip graph replay" if args.graph == "on" else "eager"},
+           "roofline": roof, "kernels": kernels}
+    if args.graph == "on":
+        out["eager_ms_per_step"] = round(eager_ms, 4)
+    if not args.no_cpu_baseline:
+        rows = args.cpu_rows or max(1, min(wl.spatial[0], int(0.5e6 // (wl.voxels // wl.spatial[0]) + 1)))
+        sub_shape = (rows,) + tuple(wl.spatial[1:])
+        sub = synth.small_variant(wl, sub_shape, [(n,) for n in sub_shape], name_suffix="cpu_sample")
+        ysub = oracle.widen(synth.make_input(sub), wl.dtype)
+        from threadpoolctl import threadpool_info
+        t0 = time.perf_counter()
+        x = oracle.conv_transposed(ysub, wf.astype(np.float64), s)
+        dt = time.perf_counter() - t0
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        out["cpu_baseline"] = {"value": x.shape[0] * int(np.prod(x.shape[1:-1])) / dt, "unit": "voxels/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"first {rows} rows of the input's outermost axis ({sub.voxels} input, "
+                                         f"{sub.voxels * s ** wl.ndim} output voxels, transposed conv in fp64 "
+                                         f"numpy, {dt:.2f} s)", "seconds": round(dt, 3),
+                               "checksum": float(np.abs(x).sum())}
     print(json.dumps(out), flush=True)
 
 

@@ -96,6 +96,8 @@ def _load() -> ctypes.CDLL:
         "st_pool_sharded": (I32, [P, PP, I32, I32, I32, P, PP, P]),
         "st_plan_strided": (I32, [P, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(P)]),
         "st_conv_strided_sharded": (I32, [P, PP, P, P, I32, I32, P, PP, P]),
+        "st_plan_transposed": (I32, [P, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(P)]),
+        "st_conv_transposed_sharded": (I32, [P, PP, P, P, I32, I32, P, PP, P]),
         "st_conv_wgrad_workspace_bytes": (SZ, [P, I32, I32]),
         "st_conv_wgrad": (I32, [P, PP, P, PP, I32, P, P, SZ, P]),
         "st_groupnorm_workspace_bytes": (SZ, [P, I32]),
@@ -373,6 +375,28 @@ def st_conv_strided_sharded(in_plan: Plan, in_bufs, weight_tco, bias, ksize: int
                                        out_plan.handle, outs, _stream(stream)), "st_conv_strided_sharded")
 
 
+def st_plan_transposed(in_plan: Plan, ksize: int, stride: int, cout: int, out_halo=None) -> Plan:
+    """fp32 output plan of a transposed (upsampling) conv: every shard's extents times stride."""
+    hl = (ctypes.c_int32 * 3)(*(list(out_halo) + [0] * (3 - len(out_halo)))) if out_halo is not None else None
+    out = ctypes.c_void_p()
+    _check(lib.st_plan_transposed(in_plan.handle, ksize, stride, cout, hl, ctypes.byref(out)), "st_plan_transposed")
+    return _plan_from_handle(out.value, in_plan.ndim, in_plan.batch, cout, ST_F32,
+                             tuple(out_halo) if out_halo is not None else (0,) * in_plan.ndim)
+
+
+def st_conv_transposed_sharded(in_plan: Plan, in_bufs, weight_tio, bias, ksize: int, stride: int, out_plan: Plan,
+                               out_bufs, stream=None) -> None:
+    """weight_tio: fp32 device tensor [taps][Cin][Cout], Cin = in_plan.channels."""
+    ins = _ptr_array(in_bufs, "st_conv_transposed_sharded input", _shard_bytes(in_plan))
+    outs = _ptr_array(out_bufs, "st_conv_transposed_sharded output", _shard_bytes(out_plan))
+    taps = ksize ** in_plan.ndim
+    w = _dev_ptr(weight_tio, "weight_tio", 4 * taps * in_plan.channels * out_plan.channels)
+    b = _dev_ptr(bias, "bias", 4 * out_plan.channels)
+    _check(lib.st_conv_transposed_sharded(in_plan.handle, ins, ctypes.c_void_p(w), ctypes.c_void_p(b), ksize,
+                                          stride, out_plan.handle, outs, _stream(stream)),
+           "st_conv_transposed_sharded")
+
+
 def st_conv_wgrad_workspace_bytes(x_plan: Plan, cout: int, ksize: int) -> int:
     return int(lib.st_conv_wgrad_workspace_bytes(x_plan.handle, cout, ksize))
 
@@ -478,5 +502,6 @@ __all__ = [
     "st_groupnorm_workspace_layout", "st_groupnorm_sharded", "st_groupnorm_partials",
     "st_groupnorm_combine", "st_groupnorm_apply", "st_groupnorm_backward_workspace_bytes",
     "st_groupnorm_backward", "st_conv_wgrad_workspace_bytes", "st_conv_wgrad", "st_plan_pooled",
-    "st_pool_sharded", "st_plan_strided", "st_conv_strided_sharded",
+    "st_pool_sharded", "st_plan_strided", "st_conv_strided_sharded", "st_plan_transposed",
+    "st_conv_transposed_sharded",
 ]

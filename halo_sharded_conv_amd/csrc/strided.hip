@@ -16,6 +16,16 @@
 // the window's input cells once and the weights as wave-uniform values, and
 // accumulates in a fixed order (taps lexicographic, input channels
 // ascending), so an output's bits do not depend on the shard plan.
+//
+// Its adjoint, the transposed (upsampling) convolution, is the same section's
+// rule run the other way: input cell i scatters onto outputs i*s + t - p, the
+// output has s times the input's extent, and a shard with interior [a, a + e)
+// owns outputs [a*s, (a + e)*s).  An output j = q*s + r (phase r in [0, s))
+// gathers from the taps t = r + p (mod s), i.e. input cells q + (r + p - t)/s,
+// all within p cells of q, so the input's halo of k/2 again suffices.
+// st_plan_transposed derives the output plan; st_conv_transposed_sharded runs
+// one launch with one phase per blockIdx.z, so the tap set is uniform over a
+// block and the weights stay wave-uniform.
 #include <algorithm>
 #include <cstdio>
 
@@ -23,6 +33,8 @@
 
 namespace st {
 namespace {
+
+constexpr int kMaxTransposedStride = 8;
 
 
 struct StrShard {
@@ -104,6 +116,102 @@ __global__ __launch_bounds__(256) void conv_strided_kernel(const StrArgs a) {
   float* o = sh.out + n * sh.osn + od * sh.os[0] + oh * sh.os[1] + ow * sh.os[2] + o0;
 #pragma unroll
   for (int i = 0; i < OB; ++i) o[i] = acc[i];
+}
+
+struct TrShard {
+  const char* in;                   // padded input shard at the interior origin (n=0)
+  float* out;                       // output interior origin
+  int64_t is[3], isn;               // input element strides (d, h, w) and batch stride
+  int64_t os[3], osn;               // output element strides
+  int32_t iext[3];                  // input interior extents (d, h, w)
+  int64_t begin;                    // first input position of this shard
+};
+
+struct TrArgs {
+  int32_t nshards, batch, cin, cout, k, stride, ndim;
+  int64_t total;                    // input positions over all shards and samples (per phase)
+  const float* w;                   // [taps][Cin][Cout] fp32, Cin = the input's channels
+  const float* bias;                // [Cout] or NULL
+  TrShard sh[ST_MAX_SHARDS];
+};
+
+// Gather form of the transposed conv: blockIdx.z is the output phase
+// (rd, rh, rw), a thread takes input position q and writes output q*s + r for
+// OB output channels (blockIdx.y picks the block).  Taps of the phase in
+// lexicographic order, input channels ascending, fp32 FMA.
+template <typename TI, int OB, int CV>
+__global__ __launch_bounds__(256) void conv_transposed_kernel(const TrArgs a) {
+  const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int o0 = blockIdx.y * OB;
+  if (item >= a.total) return;
+  const int s = a.stride, k = a.k, p = k / 2;
+  const bool v3 = a.ndim == 3;
+  const int sd = v3 ? s : 1, kd = v3 ? k : 1, pd = kd / 2;
+  const int ph = blockIdx.z;
+  const int rw = ph % s, rh = (ph / s) % s, rd = v3 ? ph / (s * s) : 0;
+  // first tap of the phase per axis and the input offset it reads
+  const int t0w = (rw + p) % s, t0h = (rh + p) % s, t0d = (rd + pd) % sd;
+  const int dw = (rw + p - t0w) / s, dh = (rh + p - t0h) / s, dd = (rd + pd - t0d) / sd;
+  int sh_i = 0;
+  while (sh_i + 1 < a.nshards && a.sh[sh_i + 1].begin <= item) ++sh_i;
+  const TrShard& sh = a.sh[sh_i];
+  int64_t r = item - sh.begin;
+  const int qw = (int)(r % sh.iext[2]);
+  r /= sh.iext[2];
+  const int qh = (int)(r % sh.iext[1]);
+  r /= sh.iext[1];
+  const int qd = (int)(r % sh.iext[0]);
+  const int n = (int)(r / sh.iext[0]);
+  const TI* base = reinterpret_cast<const TI*>(sh.in) + n * sh.isn + (int64_t)(qd + dd) * sh.is[0] +
+                   (int64_t)(qh + dh) * sh.is[1] + (int64_t)(qw + dw) * sh.is[2];
+  float acc[OB];
+#pragma unroll
+  for (int i = 0; i < OB; ++i) acc[i] = a.bias ? a.bias[o0 + i] : 0.f;
+  const int64_t tap_stride = (int64_t)a.cin * a.cout;
+  for (int tz = t0d, mz = 0; tz < kd; tz += sd, ++mz)
+    for (int ty = t0h, my = 0; ty < k; ty += s, ++my)
+      for (int tx = t0w, mx = 0; tx < k; tx += s, ++mx) {
+        // tap t reads input cell q + (r + p - t)/s: one cell back per step of s
+        const TI* px = base - mz * sh.is[0] - my * sh.is[1] - mx * sh.is[2];
+        const float* wt = a.w + ((tz * k + ty) * k + tx) * tap_stride + o0;
+        for (int c = 0; c < a.cin; c += CV) {
+          float x[CV];
+          ldc<TI, CV>(px + c, x);
+#pragma unroll
+          for (int v = 0; v < CV; ++v) {
+#pragma unroll
+            for (int i = 0; i < OB; ++i) acc[i] = fmaf(wt[i], x[v], acc[i]);
+            wt += a.cout;
+          }
+        }
+      }
+  float* o = sh.out + n * sh.osn + (int64_t)(qd * sd + rd) * sh.os[0] + (int64_t)(qh * s + rh) * sh.os[1] +
+             (int64_t)(qw * s + rw) * sh.os[2] + o0;
+  if constexpr (OB % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < OB; i += 4)
+      *reinterpret_cast<float4*>(o + i) = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < OB; ++i) o[i] = acc[i];
+  }
+}
+
+// input offsets (relative to q) an output phase of the transposed conv reads
+// along one axis, over all phases: [lo, hi]; false when no phase has a tap
+bool transposed_reach(int k, int s, int& lo, int& hi) {
+  const int p = k / 2;
+  bool any = false;
+  lo = 0;
+  hi = 0;
+  for (int r = 0; r < s; ++r)
+    for (int t = (r + p) % s; t < k; t += s) {
+      const int off = (r + p - t) / s;
+      if (!any) { lo = hi = off; any = true; }
+      lo = std::min(lo, off);
+      hi = std::max(hi, off);
+    }
+  return any;
 }
 
 // output sizes along one internal axis: output j owns the window centred at j*s
@@ -260,6 +368,127 @@ st_status st_conv_strided_sharded(const st_plan* in_plan, const void* const* in_
   }
 #undef ST_STR_LAUNCH
   return launch_check("st_conv_strided_sharded: launch");
+}
+
+st_status st_plan_transposed(const st_plan* in_plan, int32_t ksize, int32_t stride, int32_t cout,
+                             const int32_t* out_halo_or_null, st_plan** out) {
+  auto err = [](st_status s, const std::string& m) { return fail(s, "st_plan_transposed: " + m); };
+  if (!in_plan || !out) return err(ST_ERR_INVALID_ARG, "NULL argument");
+  *out = nullptr;
+  if (ksize < 1 || ksize % 2 == 0) return err(ST_ERR_UNSUPPORTED, "odd kernel sizes only");
+  if (stride < 1 || stride > kMaxTransposedStride || cout < 1)
+    return err(ST_ERR_INVALID_ARG, "stride must be in [1, 8] and cout >= 1");
+  const int nd = in_plan->ndim;
+  int64_t spatial[ST_MAX_NDIM];
+  int32_t counts[ST_MAX_NDIM], halo[ST_MAX_NDIM];
+  std::vector<int64_t> concat;
+  for (int a = 0; a < nd; ++a) {
+    int64_t tot = 0;
+    const auto& sz = in_plan->sizes[axis_of(in_plan, a)];
+    for (int64_t e : sz) {
+      tot += e * stride;
+      concat.push_back(e * stride);
+    }
+    spatial[a] = tot;
+    counts[a] = (int32_t)sz.size();
+    halo[a] = out_halo_or_null ? out_halo_or_null[a] : 0;
+  }
+  return st_plan_shards(nd, in_plan->batch, cout, spatial, counts, concat.data(), halo, ST_F32, out);
+}
+
+st_status st_conv_transposed_sharded(const st_plan* in_plan, const void* const* in_bufs, const float* weight_tio,
+                                     const float* bias_or_null, int32_t ksize, int32_t stride,
+                                     const st_plan* out_plan, float* const* out_bufs, void* stream) {
+  auto err = [](st_status s, const std::string& m) { return fail(s, "st_conv_transposed_sharded: " + m); };
+  if (!in_plan || !out_plan || !in_bufs || !out_bufs || !weight_tio)
+    return err(ST_ERR_INVALID_ARG, "NULL argument");
+  if (ksize < 1 || ksize % 2 == 0) return err(ST_ERR_UNSUPPORTED, "odd kernel sizes only");
+  if (stride < 1 || stride > kMaxTransposedStride) return err(ST_ERR_INVALID_ARG, "stride must be in [1, 8]");
+  if (out_plan->dtype != ST_F32) return err(ST_ERR_BAD_SHAPE, "outputs are fp32");
+  if (out_plan->ndim != in_plan->ndim || out_plan->batch != in_plan->batch ||
+      out_plan->shards.size() != in_plan->shards.size())
+    return err(ST_ERR_BAD_SHAPE, "output plan does not match the input plan");
+  if ((reinterpret_cast<uintptr_t>(weight_tio) & 3) || (bias_or_null && (reinterpret_cast<uintptr_t>(bias_or_null) & 3)))
+    return err(ST_ERR_ALIGNMENT, "misaligned weight or bias");
+  TrArgs a{};
+  a.nshards = (int)in_plan->shards.size();
+  a.batch = (int)in_plan->batch;
+  a.cin = (int)in_plan->channels;
+  a.cout = (int)out_plan->channels;
+  a.k = ksize;
+  a.stride = stride;
+  a.ndim = in_plan->ndim;
+  a.w = weight_tio;
+  a.bias = bias_or_null;
+  for (int ax = kAxes - in_plan->ndim; ax < kAxes; ++ax) {
+    const auto& si = in_plan->sizes[ax];
+    const auto& so = out_plan->sizes[ax];
+    bool same = si.size() == so.size();
+    for (size_t i = 0; same && i < si.size(); ++i) same = so[i] == si[i] * stride;
+    if (!same) return err(ST_ERR_BAD_SHAPE, "output plan is not the transposed plan of the input");
+  }
+  int lo = 0, hi = 0;
+  const bool any_tap = transposed_reach(ksize, stride, lo, hi);
+  const int ie = in_plan->esize;
+  int64_t total = 0;
+  for (size_t i = 0; i < in_plan->shards.size(); ++i) {
+    if (!in_bufs[i] || !out_bufs[i]) return err(ST_ERR_INVALID_ARG, "NULL shard buffer");
+    if (!aligned16(in_bufs[i]) || !aligned16(out_bufs[i])) return err(ST_ERR_ALIGNMENT, "shard buffers must be 16-byte aligned");
+    const Shard& si = in_plan->shards[i];
+    const Shard& so = out_plan->shards[i];
+    TrShard& q = a.sh[i];
+    q.is[2] = a.cin;
+    q.is[1] = si.pad[2] * a.cin;
+    q.is[0] = si.pad[1] * q.is[1];
+    q.isn = si.pad[0] * q.is[0];
+    q.os[2] = a.cout;
+    q.os[1] = so.pad[2] * a.cout;
+    q.os[0] = so.pad[1] * q.os[1];
+    q.osn = so.pad[0] * q.os[0];
+    int64_t in_off = 0, out_off = 0;
+    for (int ax = 0; ax < kAxes; ++ax) {
+      const bool sp = ax >= kAxes - in_plan->ndim;
+      const int64_t h = in_plan->halo[ax];
+      // every read cell lies in [q + lo, q + hi] for q in the interior
+      if (sp && any_tap && si.ext[ax] > 0 && (h + lo < 0 || h + si.ext[ax] - 1 + hi >= si.pad[ax]))
+        return err(ST_ERR_BAD_SHAPE, "input halo smaller than ksize/2");
+      in_off += h * q.is[ax];
+      out_off += out_plan->halo[ax] * q.os[ax];
+      q.iext[ax] = (int32_t)si.ext[ax];
+    }
+    q.in = static_cast<const char*>(in_bufs[i]) + in_off * ie;
+    q.out = out_bufs[i] + out_off;
+    q.begin = total;
+    total += a.batch * (int64_t)si.ext[0] * si.ext[1] * si.ext[2];
+  }
+  a.total = total;
+  if (total == 0) return ST_OK;
+  int ob = 1;
+  for (int c : {64, 32, 16, 8, 4, 2, 1})
+    if (a.cout % c == 0) { ob = c; break; }
+  int phases = stride * stride * (a.ndim == 3 ? stride : 1);
+  const dim3 grid((unsigned)((total + 255) / 256), (unsigned)(a.cout / ob), (unsigned)phases), block(256);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = in_plan->dtype == ST_BF16;
+  const bool vec = bf ? a.cin % 8 == 0 : a.cin % 4 == 0;
+#define ST_TR_LAUNCH(OB)                                                                                \
+  do {                                                                                                  \
+    if (bf && vec) hipLaunchKernelGGL((conv_transposed_kernel<uint16_t, OB, 8>), grid, block, 0, st, a); \
+    else if (bf) hipLaunchKernelGGL((conv_transposed_kernel<uint16_t, OB, 1>), grid, block, 0, st, a);  \
+    else if (vec) hipLaunchKernelGGL((conv_transposed_kernel<float, OB, 4>), grid, block, 0, st, a);    \
+    else hipLaunchKernelGGL((conv_transposed_kernel<float, OB, 1>), grid, block, 0, st, a);             \
+  } while (0)
+  switch (ob) {
+    case 64: ST_TR_LAUNCH(64); break;
+    case 32: ST_TR_LAUNCH(32); break;
+    case 16: ST_TR_LAUNCH(16); break;
+    case 8: ST_TR_LAUNCH(8); break;
+    case 4: ST_TR_LAUNCH(4); break;
+    case 2: ST_TR_LAUNCH(2); break;
+    default: ST_TR_LAUNCH(1); break;
+  }
+#undef ST_TR_LAUNCH
+  return launch_check("st_conv_transposed_sharded: launch");
 }
 
 }  // extern "C"

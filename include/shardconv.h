@@ -326,6 +326,48 @@ st_status st_conv_strided_sharded(const st_plan* in_plan, const void* const* in_
                                   const float* bias_or_null, int32_t ksize, int32_t stride,
                                   const st_plan* out_plan, float* const* out_bufs, void* stream);
 
+/*
+ * st_plan_transposed - the output plan of a transposed (upsampling)
+ * convolution of in_plan's shards, the adjoint of the strided convolution.
+ * Same passage as st_plan_pooled: input cell i scatters onto outputs
+ * i*stride + t - ksize/2, the output has stride times the input's extent on
+ * every spatial axis, and the shard with interior [a, a + e) owns outputs
+ * [a*stride, (a + e)*stride).
+ *   stride             1 .. 8
+ *   cout               channels of the output plan
+ *   out_halo_or_null   ndim halo widths of the output plan (NULL: 0)
+ *   out                receives the fp32 output plan (st_plan_destroy)
+ * Errors: ST_ERR_UNSUPPORTED (even ksize), ST_ERR_INVALID_ARG.
+ */
+st_status st_plan_transposed(const st_plan* in_plan, int32_t ksize, int32_t stride, int32_t cout,
+                             const int32_t* out_halo_or_null, st_plan** out);
+
+/*
+ * st_conv_transposed_sharded - transposed convolution of every shard from its
+ * halo-padded chunk (after the halo exchange).  Output q*stride + r reads the
+ * input cells q + (r + ksize/2 - t)/stride over the taps t = r + ksize/2
+ * (mod stride); the halo must cover that reach on both sides (ksize/2 always
+ * does; stride 2 with ksize 3 or 5 needs 1):
+ *   x[n, j, c] = bias[c] + sum over (i, t) with i*stride + t - ksize/2 = j of
+ *                sum_o W[o, c, t] * y[n, i, o]
+ * so that <conv_strided(x, W), y> = <x, conv_transposed(y, W)> without bias.
+ *   in_plan, in_bufs   padded input shards y (fp32 or bf16 operands), in_plan
+ *                      channels = the strided conv's output channels
+ *   weight_tio         [taps][Cin][Cout] fp32, weight_tio[t][o][c] = W[o, c, t]
+ *                      (Cin = in_plan channels), read only
+ *   bias_or_null       Cout floats or NULL
+ *   out_plan, out_bufs the plan st_plan_transposed returned for (in_plan,
+ *                      ksize, stride, Cout) and its fp32 shards (only
+ *                      interiors written)
+ * fp32 FMA in a fixed order (the output phase's taps lexicographic, input
+ * channels ascending), so an output's bits do not depend on the shard plan.
+ * Errors: ST_ERR_BAD_SHAPE (out_plan is not the transposed plan, halo too
+ * small), ST_ERR_ALIGNMENT, ST_ERR_INVALID_ARG, ST_ERR_UNSUPPORTED.
+ */
+st_status st_conv_transposed_sharded(const st_plan* in_plan, const void* const* in_bufs, const float* weight_tio,
+                                     const float* bias_or_null, int32_t ksize, int32_t stride,
+                                     const st_plan* out_plan, float* const* out_bufs, void* stream);
+
 /* ------------------------------------------------------------- GroupNorm */
 
 /*

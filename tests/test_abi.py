@@ -205,6 +205,25 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert cs(p.handle, aligned, wt, None, 3, 2, p.handle, aligned, s) == BAD_SHAPE            # bf16 output plan
     sq0 = hsc.st_plan_strided(p0, 3, 2, 8)
     assert cs(p0.handle, aligned, wt, None, 3, 2, sq0.handle, aligned, s) == BAD_SHAPE         # input halo 0 < 1
+    # transposed conv: derived plan and its errors
+    assert L.st_plan_transposed(p.handle, 4, 2, 8, None, ctypes.byref(out)) == UNSUPPORTED
+    assert L.st_plan_transposed(p.handle, 3, 0, 8, None, ctypes.byref(out)) == INVALID
+    assert L.st_plan_transposed(p.handle, 3, 9, 8, None, ctypes.byref(out)) == INVALID
+    assert L.st_plan_transposed(p.handle, 3, 2, 0, None, ctypes.byref(out)) == INVALID
+    tq = hsc.st_plan_transposed(p, 3, 2, 16)
+    assert tq.shards == ((8, 8), (16,)) and tq.channels == 16
+    ct = L.st_conv_transposed_sharded
+    assert ct(p.handle, aligned, None, None, 3, 2, tq.handle, aligned, s) == INVALID
+    assert ct(p.handle, aligned, wt, None, 3, 3, tq.handle, aligned, s) == BAD_SHAPE          # not its transposed plan
+    assert ct(p.handle, aligned, wt, None, 2, 2, tq.handle, aligned, s) == UNSUPPORTED
+    assert ct(p.handle, misaligned, wt, None, 3, 2, tq.handle, aligned, s) == ALIGN
+    assert ct(p.handle, aligned, ctypes.c_void_p(0xF0002), None, 3, 2, tq.handle, aligned, s) == ALIGN
+    assert ct(p.handle, aligned, wt, None, 3, 2, p.handle, aligned, s) == BAD_SHAPE            # bf16 output plan
+    assert ct(p.handle, nulls, wt, None, 3, 2, tq.handle, aligned, s) == INVALID
+    tq0 = hsc.st_plan_transposed(p0, 3, 2, 8)
+    assert ct(p0.handle, aligned, wt, None, 3, 2, tq0.handle, aligned, s) == BAD_SHAPE         # input halo 0 < 1
+    tq7 = hsc.st_plan_transposed(p, 7, 2, 16)      # k 7, stride 2 reads cells q-1 .. q+2
+    assert ct(p.handle, aligned, wt, None, 7, 2, tq7.handle, aligned, s) == BAD_SHAPE          # halo 1 < 2
     # groupnorm backward
     bneed = L.st_groupnorm_backward_workspace_bytes(q.handle, 4)
     assert bneed > 0 and L.st_groupnorm_backward_workspace_bytes(None, 4) == 0
