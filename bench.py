@@ -25,9 +25,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sharded conv+GroupNorm voxels/s on 1 MI355X; % MFMA peak (conv), % HBM BW (halo/norm)"
 METRIC_DGRAD = "sharded conv input-gradient (halo exchange of dy + conv) voxels/s on 1 MI355X"
-METRIC_STRIDED = "sharded stride-2 conv (halo exchange + strided 'same' conv, fp32 FMA) input voxels/s on 1 MI355X"
-METRIC_TRANSPOSED = ("sharded stride-2 transposed conv (halo exchange + upsampling conv, fp32 FMA) output voxels/s "
-                     "on 1 MI355X")
+METRIC_STRIDED = "sharded stride-2 conv (halo exchange + strided 'same' conv) input voxels/s on 1 MI355X"
+METRIC_TRANSPOSED = "sharded stride-2 transposed conv (halo exchange + upsampling conv) output voxels/s on 1 MI355X"
 METRIC_POOL = "sharded 2x downsampling (halo exchange + 'valid' average pooling, k=2 s=2) input voxels/s on 1 MI355X"
 METRIC_BWD = ("sharded conv+GroupNorm backward (GroupNorm backward, halo exchange of dy, input gradient, "
               "weight gradient) voxels/s on 1 MI355X")
@@ -419,6 +418,26 @@ def time_graph(args, stages):
     return wall * 1e3 / args.steps, start.elapsed_time(end) / args.steps
 
 
+def shape_change_roofline(wl, key, ms, flops, alg_bytes, kernels, traffic):
+    """Roofline of the strided / transposed conv kernel.  bf16 shapes with
+    Cin % 16 == 0 and Cout % 32 == 0 run on the matrix cores, where their
+    arithmetic intensity (~60-100 flop/byte) is below MI355X's ridge (~315):
+    HBM-bound.  The rest run on fp32 FMA: the ALU roofline against the 157.3
+    TFLOP/s fp32 vector peak."""
+    tf = flops / (ms * 1e-3) / 1e12
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    mfma = wl.dtype == "bf16" and wl.cin % 16 == 0 and wl.cout % 32 == 0
+    kernels[key].update({"TFLOP/s": round(tf, 2),
+                         ("mfma_frac" if mfma else "fp32_frac"):
+                             round(tf / (MFMA_BF16_PEAK_TFLOPS if mfma else FP32_PEAK_TFLOPS), 4),
+                         "path": "bf16 MFMA" if mfma else "fp32 FMA"})
+    if mfma:
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": key, "traffic": traffic}
+    return {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / FP32_PEAK_TFLOPS, 4), "kernel": key, "traffic": traffic}
+
+
 def bench_strided(args, wl):
     """Downsampling conv of the layer's input shards: halo exchange and a
     stride-2 'same' conv with the layer's weights into the fp32 output plan
@@ -456,15 +475,12 @@ def bench_strided(args, wl):
     for key, ms in per_kernel_ms.items():
         gbs = alg[key] / (ms * 1e-3) / 1e9
         kernels[key] = {"ms": round(ms, 5), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-    tf = flops / (per_kernel_ms["strided"] * 1e-3) / 1e12
-    kernels["strided"].update({"TFLOP/s": round(tf, 2), "fp32_frac": round(tf / FP32_PEAK_TFLOPS, 4)})
-    # fp32 FMA on the vector units: the ALU roofline (157.3 TFLOP/s fp32 vector peak)
-    roof = {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tf / FP32_PEAK_TFLOPS, 4), "kernel": "strided", "traffic": load_traffic(wl, "strided")}
+    roof = shape_change_roofline(wl, "strided", per_kernel_ms["strided"], flops, alg["strided"], kernels,
+                                 load_traffic(wl, "strided"))
     out = {"metric": METRIC_STRIDED, "value": wl.voxels / (ms_per_step * 1e-3), "unit": "voxels/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "gpu_ms_per_step": round(gpu_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "f32", "data": "synthetic",
+           "dtype": "bf16" if roof["bound"] == "hbm" else "f32", "data": "synthetic",
            "config": {"workload": wl.name, "shape": [wl.batch, wl.cin, *wl.spatial], "cout": wl.cout,
                       "kernel": wl.ksize, "stride": s, "operands": wl.dtype, "shards": [list(a) for a in wl.shards],
                       "out_shards": [list(a) for a in q.shards], "pass": "strided",
@@ -539,15 +555,12 @@ def bench_transposed(args, wl_out):
     for key, ms in per_kernel_ms.items():
         gbs = alg[key] / (ms * 1e-3) / 1e9
         kernels[key] = {"ms": round(ms, 5), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-    tf = flops / (per_kernel_ms["transposed"] * 1e-3) / 1e12
-    kernels["transposed"].update({"TFLOP/s": round(tf, 2), "fp32_frac": round(tf / FP32_PEAK_TFLOPS, 4)})
-    roof = {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tf / FP32_PEAK_TFLOPS, 4), "kernel": "transposed",
-            "traffic": load_traffic(wl_out, "transposed")}
+    roof = shape_change_roofline(wl, "transposed", per_kernel_ms["transposed"], flops, alg["transposed"], kernels,
+                                 load_traffic(wl_out, "transposed"))
     out = {"metric": METRIC_TRANSPOSED, "value": out_vox / (ms_per_step * 1e-3), "unit": "voxels/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "gpu_ms_per_step": round(gpu_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "f32", "data": "synthetic",
+           "dtype": "bf16" if roof["bound"] == "hbm" else "f32", "data": "synthetic",
            "config": {"workload": wl_out.name, "input_shape": [wl.batch, wl.cin, *wl.spatial], "cout": wl.cout,
                       "kernel": wl.ksize, "stride": s, "operands": wl.dtype,
                       "in_shards": [list(a) for a in wl.shards], "out_shards": [list(a) for a in q.shards],

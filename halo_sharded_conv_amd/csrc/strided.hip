@@ -214,6 +214,272 @@ bool transposed_reach(int k, int s, int& lo, int& hi) {
   return any;
 }
 
+// --------------------------------------------------------------------------
+// matrix-core path (bf16 operands): implicit GEMM per output phase
+// --------------------------------------------------------------------------
+//
+// M = output channels (A = weights, staged once per workgroup in LDS in
+// fragment order), N = 32 output positions per block (B = input cells, one
+// 16-byte load of 8 channels per lane straight from the padded shard),
+// K = taps x input channels, v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation.  A wave owns NB x 32 consecutive positions of one shard and
+// MB x 32 output channels; every output sums its K steps in the same order
+// (bias first, taps lexicographic, channels ascending in blocks of 16), so its
+// bits do not depend on the shard plan.  The transposed conv runs every
+// output phase of a position block in turn in the same wave (the phases read
+// overlapping input cells, which then stay in L1/L2).
+
+typedef __bf16 sx_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float sx_f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kSxNB = 2;                        // 32-position blocks per wave
+constexpr int kSxWaves = 4;
+
+struct SxShard {
+  const uint16_t* in;               // strided: first window's first cell; transposed: interior origin
+  float* out;                       // output interior origin
+  int64_t is[3], isn;               // input element strides
+  int64_t os[3], osn;               // output element strides
+  int32_t ext[3];                   // position extents (strided: outputs; transposed: inputs)
+  int64_t positions;                // batch x ext product
+  int64_t tile_begin;               // first wave tile of this shard
+};
+
+struct SxArgs {
+  int32_t nshards, cin, cout, k, stride, ndim, taps, iters;
+  int64_t tiles;                    // wave tiles over all shards
+  const float* w;                   // [taps][Cin][Cout] fp32 (bf16 values)
+  const float* bias;                // [Cout] or NULL
+  SxShard sh[ST_MAX_SHARDS];
+};
+
+__device__ __forceinline__ uint16_t sx_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int MB, int KG, bool TR, int CAP>
+__global__ __launch_bounds__(256) void conv_sx_mfma(const SxArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t wl[CAP / 2];   // [taps][Cin/16][MB][64 lanes][8]
+  const int KC = a.cin >> 4;
+  const int ob = blockIdx.y * MB * 32;
+  {
+    // weights of this channel block, read in global order 4 output channels
+    // (16 bytes) at a time, rounded to bf16, written to their fragment slots
+    // (4 consecutive output channels are 4 consecutive lanes' slots)
+    const int per_tap4 = a.cin * MB * 8;
+    const int total4 = a.taps * per_tap4;
+#pragma unroll 4
+    for (int f = threadIdx.x; f < total4; f += blockDim.x) {
+      const int t = f / per_tap4;
+      const int rem = f - t * per_tap4;
+      const int c = rem / (MB * 8);
+      const int o = (rem - c * (MB * 8)) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(a.w + ((int64_t)t * a.cin + c) * a.cout + ob + o);
+      const int l = ((c >> 3) & 1) * 32 + (o & 31);
+      uint16_t* d = wl + ((((t * KC + (c >> 4)) * MB + (o >> 5)) * 64 + l) << 3) + (c & 7);
+      d[0] = sx_rne(v.x);
+      d[8] = sx_rne(v.y);
+      d[16] = sx_rne(v.z);
+      d[24] = sx_rne(v.w);
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int s = a.stride, k = a.k, p = k / 2;
+  const bool v3 = a.ndim == 3;
+  const int sd = v3 ? s : 1, kd = v3 ? k : 1, pd = kd / 2;
+  const int phases = TR ? s * s * sd : 1;
+  // XCD-aware order: consecutive logical workgroups share one XCD's L2
+  int g = blockIdx.x;
+  if ((gridDim.x & 7) == 0) g = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  for (int it = 0; it < a.iters; ++it) {
+    const int64_t tile = ((int64_t)g * a.iters + it) * kSxWaves + wave;
+    if (tile >= a.tiles) break;
+    int si = 0;
+    while (si + 1 < a.nshards && a.sh[si + 1].tile_begin <= tile) ++si;
+    const SxShard& sh = a.sh[si];
+    const int64_t p0 = (tile - sh.tile_begin) * (kSxNB * 32);
+    int pz[kSxNB], py[kSxNB], px[kSxNB], pn[kSxNB];
+    bool ok[kSxNB];
+#pragma unroll
+    for (int nb = 0; nb < kSxNB; ++nb) {
+      const int64_t q = p0 + nb * 32 + l32;
+      ok[nb] = q < sh.positions;
+      int64_t r = ok[nb] ? q : 0;
+      px[nb] = (int)(r % sh.ext[2]);
+      r /= sh.ext[2];
+      py[nb] = (int)(r % sh.ext[1]);
+      r /= sh.ext[1];
+      pz[nb] = (int)(r % sh.ext[0]);
+      pn[nb] = (int)(r / sh.ext[0]);
+    }
+    for (int ph = 0; ph < phases; ++ph) {
+      // taps of this phase: per axis from t0 in steps of s (all taps for the strided conv)
+      const int rw = TR ? ph % s : 0, rh = TR ? (ph / s) % s : 0, rd = TR && v3 ? ph / (s * s) : 0;
+      const int t0w = TR ? (rw + p) % s : 0, t0h = TR ? (rh + p) % s : 0, t0d = TR ? (rd + pd) % sd : 0;
+      const int tstep = TR ? s : 1, tstepd = TR ? sd : 1;
+      const int dw = TR ? (rw + p - t0w) / s : 0, dh = TR ? (rh + p - t0h) / s : 0, dd = TR ? (rd + pd - t0d) / sd : 0;
+      const uint16_t* bp[kSxNB];
+      float* op[kSxNB];
+#pragma unroll
+      for (int nb = 0; nb < kSxNB; ++nb) {
+        if (TR) {
+          bp[nb] = sh.in + pn[nb] * sh.isn + (int64_t)(pz[nb] + dd) * sh.is[0] + (int64_t)(py[nb] + dh) * sh.is[1] +
+                   (int64_t)(px[nb] + dw) * sh.is[2] + hf * 8;
+          op[nb] = sh.out + pn[nb] * sh.osn + (int64_t)(pz[nb] * sd + rd) * sh.os[0] +
+                   (int64_t)(py[nb] * s + rh) * sh.os[1] + (int64_t)(px[nb] * s + rw) * sh.os[2];
+        } else {
+          bp[nb] = sh.in + pn[nb] * sh.isn + (int64_t)pz[nb] * s * sh.is[0] + (int64_t)py[nb] * s * sh.is[1] +
+                   (int64_t)px[nb] * s * sh.is[2] + hf * 8;
+          op[nb] = sh.out + pn[nb] * sh.osn + (int64_t)pz[nb] * sh.os[0] + (int64_t)py[nb] * sh.os[1] +
+                   (int64_t)px[nb] * sh.os[2];
+        }
+      }
+      sx_f32x16 acc[MB][kSxNB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float b = a.bias ? a.bias[ob + mb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3)] : 0.f;
+#pragma unroll
+          for (int nb = 0; nb < kSxNB; ++nb) acc[mb][nb][e] = b;
+        }
+      // K steps: (tap of the phase, block of KG x 16 channels), taps lexicographic;
+      // the next step's input fragments are loaded before this step's MFMAs
+      const int nz = (kd - t0d + tstepd - 1) / tstepd, ny = (k - t0h + tstep - 1) / tstep,
+                nx = (k - t0w + tstep - 1) / tstep;
+      const int cg = KC / KG;
+      const int nsteps = nz * ny * nx * cg;
+      auto step_at = [&](int st, int64_t& off, int& wbase) __attribute__((always_inline)) {
+        const int m = st / cg, c0 = (st - m * cg) * KG;
+        const int mx = m % nx, my = (m / nx) % ny, mz = m / (nx * ny);
+        const int tz = t0d + mz * tstepd, ty = t0h + my * tstep, tx = t0w + mx * tstep;
+        // strided: cell j*s + t - p (base at the window's first cell);
+        // transposed: cell q + (r + p - t)/s, one back per step of s
+        off = (TR ? -(mz * sh.is[0] + my * sh.is[1] + mx * sh.is[2]) : tz * sh.is[0] + ty * sh.is[1] + tx * sh.is[2]) +
+              c0 * 16;
+        wbase = (((tz * k + ty) * k + tx) * KC + c0) * MB * 512;
+      };
+      auto load_b = [&](int64_t off, sx_bf16x8 (&bv)[KG][kSxNB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kc = 0; kc < KG; ++kc)
+#pragma unroll
+          for (int nb = 0; nb < kSxNB; ++nb)
+            bv[kc][nb] = *reinterpret_cast<const sx_bf16x8*>(bp[nb] + off + kc * 16);
+      };
+      auto mma = [&](int wbase, const sx_bf16x8 (&bv)[KG][kSxNB]) __attribute__((always_inline)) {
+        const uint16_t* wt = wl + wbase + lane * 8;
+#pragma unroll
+        for (int kc = 0; kc < KG; ++kc)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const sx_bf16x8 av = *reinterpret_cast<const sx_bf16x8*>(wt + (kc * MB + mb) * 512);
+#pragma unroll
+            for (int nb = 0; nb < kSxNB; ++nb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[kc][nb], acc[mb][nb], 0, 0, 0);
+          }
+      };
+      if (nsteps > 0) {
+        sx_bf16x8 b0[KG][kSxNB], b1[KG][kSxNB];
+        int64_t off;
+        int w0, w1;
+        step_at(0, off, w0);
+        load_b(off, b0);
+        int st = 0;
+        for (; st + 2 <= nsteps; st += 2) {
+          step_at(st + 1, off, w1);
+          load_b(off, b1);
+          mma(w0, b0);
+          if (st + 2 < nsteps) {
+            step_at(st + 2, off, w0);
+            load_b(off, b0);
+          }
+          mma(w1, b1);
+        }
+        if (st < nsteps) mma(w0, b0);
+      }
+#pragma unroll
+      for (int nb = 0; nb < kSxNB; ++nb) {
+        if (!ok[nb]) continue;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4*>(op[nb] + ob + mb * 32 + 8 * j + 4 * hf) =
+                make_float4(acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1], acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]);
+      }
+    }
+  }
+}
+
+constexpr int kSxCapSmall = 80 * 1024;          // two workgroups per CU
+constexpr int kSxCapLarge = 160 * 1024;         // one workgroup per CU
+
+// Launches the matrix-core path when the layer fits it; false leaves the call
+// to the fp32 FMA kernels.  `in` of every shard as the FMA kernel's (strided:
+// first window's first cell; transposed: interior origin), ext = position
+// extents.
+template <bool TR>
+bool launch_sx_mfma(const SxShard* shards, int nshards, int batch, int cin, int cout, int k, int stride, int ndim,
+                    const float* w, const float* bias, hipStream_t st) {
+  if (cin % 16 != 0 || cout % 32 != 0 || (reinterpret_cast<uintptr_t>(w) & 15)) return false;
+  const int taps = ndim == 3 ? k * k * k : k * k;
+  int mb = cout % 64 == 0 ? 2 : 1;
+  int64_t need = (int64_t)taps * cin * mb * 32 * 2;
+  if (need > kSxCapLarge && mb == 2) {
+    mb = 1;
+    need /= 2;
+  }
+  if (need > kSxCapLarge) return false;
+  SxArgs a{};
+  a.nshards = nshards;
+  a.cin = cin;
+  a.cout = cout;
+  a.k = k;
+  a.stride = stride;
+  a.ndim = ndim;
+  a.taps = taps;
+  a.w = w;
+  a.bias = bias;
+  int64_t tiles = 0;
+  for (int i = 0; i < nshards; ++i) {
+    a.sh[i] = shards[i];
+    a.sh[i].positions = batch * (int64_t)shards[i].ext[0] * shards[i].ext[1] * shards[i].ext[2];
+    a.sh[i].tile_begin = tiles;
+    tiles += (a.sh[i].positions + kSxNB * 32 - 1) / (kSxNB * 32);
+  }
+  a.tiles = tiles;
+  if (tiles == 0) return true;
+  const int64_t groups = (tiles + kSxWaves - 1) / kSxWaves;
+  // persistent: as many workgroups as fit at once (two per CU with <= 80 KiB
+  // of weights, else one), each staging the weights once
+  const bool small = need <= kSxCapSmall;
+  int64_t grid = std::min<int64_t>(groups, small ? 512 : 256);
+  grid = (grid + 7) / 8 * 8;
+  a.iters = (int)((groups + grid - 1) / grid);
+  const int kg = cin % 64 == 0 ? 4 : cin % 32 == 0 ? 2 : 1;
+  const dim3 g3((unsigned)grid, (unsigned)(cout / (mb * 32))), block(kSxWaves * 64);
+#define ST_SX(MB_, KG_, CAP_) hipLaunchKernelGGL((conv_sx_mfma<MB_, KG_, TR, CAP_>), g3, block, 0, st, a)
+#define ST_SX_KG(MB_, CAP_)           \
+  do {                                \
+    if (kg == 4) ST_SX(MB_, 4, CAP_); \
+    else if (kg == 2) ST_SX(MB_, 2, CAP_); \
+    else ST_SX(MB_, 1, CAP_);         \
+  } while (0)
+  if (mb == 2) {
+    if (small) ST_SX_KG(2, kSxCapSmall);
+    else ST_SX_KG(2, kSxCapLarge);
+  } else {
+    if (small) ST_SX_KG(1, kSxCapSmall);
+    else ST_SX_KG(1, kSxCapLarge);
+  }
+#undef ST_SX_KG
+#undef ST_SX
+  return true;
+}
+
 // output sizes along one internal axis: output j owns the window centred at j*s
 bool strided_sizes(const std::vector<int64_t>& in, int64_t k, int64_t s, std::vector<int64_t>& out,
                    std::vector<int64_t>& first) {
@@ -343,12 +609,29 @@ st_status st_conv_strided_sharded(const st_plan* in_plan, const void* const* in_
   }
   a.total = total;
   if (total == 0) return ST_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = in_plan->dtype == ST_BF16;
+  if (bf) {
+    SxShard sx[ST_MAX_SHARDS];
+    for (int i = 0; i < a.nshards; ++i) {
+      sx[i] = SxShard{};
+      sx[i].in = reinterpret_cast<const uint16_t*>(a.sh[i].in);
+      sx[i].out = a.sh[i].out;
+      for (int ax = 0; ax < 3; ++ax) {
+        sx[i].is[ax] = a.sh[i].is[ax];
+        sx[i].os[ax] = a.sh[i].os[ax];
+        sx[i].ext[ax] = a.sh[i].oext[ax];
+      }
+      sx[i].isn = a.sh[i].isn;
+      sx[i].osn = a.sh[i].osn;
+    }
+    if (launch_sx_mfma<false>(sx, a.nshards, a.batch, a.cin, a.cout, a.k, a.stride, a.ndim, a.w, a.bias, st))
+      return launch_check("st_conv_strided_sharded: launch");
+  }
   int ob = 1;
   for (int c : {64, 32, 16, 8, 4, 2, 1})
     if (a.cout % c == 0) { ob = c; break; }
   const dim3 grid((unsigned)((total + 255) / 256), (unsigned)(a.cout / ob)), block(256);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool bf = in_plan->dtype == ST_BF16;
   const bool vec = bf ? a.cin % 8 == 0 : a.cin % 4 == 0;
 #define ST_STR_LAUNCH(OB)                                                                            \
   do {                                                                                               \
@@ -463,13 +746,30 @@ st_status st_conv_transposed_sharded(const st_plan* in_plan, const void* const* 
   }
   a.total = total;
   if (total == 0) return ST_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = in_plan->dtype == ST_BF16;
+  if (bf) {
+    SxShard sx[ST_MAX_SHARDS];
+    for (int i = 0; i < a.nshards; ++i) {
+      sx[i] = SxShard{};
+      sx[i].in = reinterpret_cast<const uint16_t*>(a.sh[i].in);
+      sx[i].out = a.sh[i].out;
+      for (int ax = 0; ax < 3; ++ax) {
+        sx[i].is[ax] = a.sh[i].is[ax];
+        sx[i].os[ax] = a.sh[i].os[ax];
+        sx[i].ext[ax] = a.sh[i].iext[ax];
+      }
+      sx[i].isn = a.sh[i].isn;
+      sx[i].osn = a.sh[i].osn;
+    }
+    if (launch_sx_mfma<true>(sx, a.nshards, a.batch, a.cin, a.cout, a.k, a.stride, a.ndim, a.w, a.bias, st))
+      return launch_check("st_conv_transposed_sharded: launch");
+  }
   int ob = 1;
   for (int c : {64, 32, 16, 8, 4, 2, 1})
     if (a.cout % c == 0) { ob = c; break; }
   int phases = stride * stride * (a.ndim == 3 ? stride : 1);
   const dim3 grid((unsigned)((total + 255) / 256), (unsigned)(a.cout / ob), (unsigned)phases), block(256);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool bf = in_plan->dtype == ST_BF16;
   const bool vec = bf ? a.cin % 8 == 0 : a.cin % 4 == 0;
 #define ST_TR_LAUNCH(OB)                                                                                \
   do {                                                                                                  \

@@ -315,12 +315,18 @@ st_status st_plan_strided(const st_plan* in_plan, int32_t ksize, int32_t stride,
  *   y[n, j, o] = bias[o] + sum_t sum_c W[o, c, t] * x[n, j*stride + t - ksize/2, c]
  *   in_plan, in_bufs   padded input shards (fp32 or bf16 operands)
  *   weight_tco         [taps][Cin][Cout] fp32 weights (taps lexicographic;
- *                      bf16 weights widened exactly), read only
+ *                      bf16 weights widened exactly), read only.  With bf16
+ *                      input shards the values must be bf16 ones: the
+ *                      matrix-core path rounds them to bf16 (nearest even)
  *   bias_or_null       Cout floats or NULL
  *   out_plan, out_bufs the plan st_plan_strided returned for (in_plan, ksize,
  *                      stride, Cout) and its fp32 shards (only interiors written)
- * fp32 FMA in a fixed order (taps lexicographic, input channels ascending),
- * so an output's bits do not depend on the shard plan.
+ * bf16 input shards with Cin % 16 == 0, Cout % 32 == 0 and the weights of
+ * a 64- (or 32-) channel output block within 160 KiB run on the matrix cores
+ * (bf16 products, fp32 accumulation); every other case on fp32 FMA.  Either
+ * way each output sums bias, then taps lexicographic, input channels
+ * ascending, in an order fixed by the layer shape, so its bits do not depend
+ * on the shard plan.
  */
 st_status st_conv_strided_sharded(const st_plan* in_plan, const void* const* in_bufs, const float* weight_tco,
                                   const float* bias_or_null, int32_t ksize, int32_t stride,
@@ -354,13 +360,15 @@ st_status st_plan_transposed(const st_plan* in_plan, int32_t ksize, int32_t stri
  *   in_plan, in_bufs   padded input shards y (fp32 or bf16 operands), in_plan
  *                      channels = the strided conv's output channels
  *   weight_tio         [taps][Cin][Cout] fp32, weight_tio[t][o][c] = W[o, c, t]
- *                      (Cin = in_plan channels), read only
+ *                      (Cin = in_plan channels), read only; bf16 values with
+ *                      bf16 input shards (as for st_conv_strided_sharded)
  *   bias_or_null       Cout floats or NULL
  *   out_plan, out_bufs the plan st_plan_transposed returned for (in_plan,
  *                      ksize, stride, Cout) and its fp32 shards (only
  *                      interiors written)
- * fp32 FMA in a fixed order (the output phase's taps lexicographic, input
- * channels ascending), so an output's bits do not depend on the shard plan.
+ * Matrix cores or fp32 FMA under the same conditions as the strided conv;
+ * each output sums bias, then its phase's taps lexicographic, input channels
+ * ascending, so its bits do not depend on the shard plan.
  * Errors: ST_ERR_BAD_SHAPE (out_plan is not the transposed plan, halo too
  * small), ST_ERR_ALIGNMENT, ST_ERR_INVALID_ARG, ST_ERR_UNSUPPORTED.
  */

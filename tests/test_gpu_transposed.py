@@ -28,9 +28,11 @@ TOL_TRANSPOSED = 1e-5      # fp32 products and accumulation
 
 
 def make_w(wl, cx, seed):
-    """W [Cy][Cx][k..k] with Cy the input's channels (the strided conv's outputs)."""
+    """W [Cy][Cx][k..k] with Cy the input's channels (the strided conv's
+    outputs), bf16 values (the weights of bf16 layers are bf16)."""
     r = np.random.default_rng(seed)
-    return r.uniform(-1, 1, size=(wl.cin, cx) + (wl.ksize,) * wl.ndim).astype(np.float32)
+    w = r.uniform(-1, 1, size=(wl.cin, cx) + (wl.ksize,) * wl.ndim).astype(np.float32)
+    return oracle.widen(synth.f32_to_bf16_bits(w), "bf16").astype(np.float32)
 
 
 def weight_tio(w):
