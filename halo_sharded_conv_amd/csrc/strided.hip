@@ -234,6 +234,7 @@ typedef float sx_f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kSxNB = 2;                        // 32-position blocks per wave
 constexpr int kSxWaves = 4;
+constexpr int kSxDepth = 3;                     // K steps of input fragments held per wave
 
 struct SxShard {
   const uint16_t* in;               // strided: first window's first cell; transposed: interior origin
@@ -381,24 +382,31 @@ __global__ __launch_bounds__(256) void conv_sx_mfma(const SxArgs a) {
               acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[kc][nb], acc[mb][nb], 0, 0, 0);
           }
       };
-      if (nsteps > 0) {
-        sx_bf16x8 b0[KG][kSxNB], b1[KG][kSxNB];
-        int64_t off;
-        int w0, w1;
-        step_at(0, off, w0);
-        load_b(off, b0);
-        int st = 0;
-        for (; st + 2 <= nsteps; st += 2) {
-          step_at(st + 1, off, w1);
-          load_b(off, b1);
-          mma(w0, b0);
-          if (st + 2 < nsteps) {
-            step_at(st + 2, off, w0);
-            load_b(off, b0);
+      // ring of kSxDepth fragment sets: kSxDepth - 1 steps in flight ahead of the MFMAs
+      {
+        sx_bf16x8 bf[kSxDepth][KG][kSxNB];
+        int wb[kSxDepth];
+#pragma unroll
+        for (int i = 0; i < kSxDepth - 1; ++i)
+          if (i < nsteps) {
+            int64_t off;
+            step_at(i, off, wb[i]);
+            load_b(off, bf[i]);
           }
-          mma(w1, b1);
+        for (int st = 0; st < nsteps; st += kSxDepth) {
+#pragma unroll
+          for (int b = 0; b < kSxDepth; ++b) {
+            if (st + b < nsteps) {
+              const int nx_ = st + b + kSxDepth - 1;
+              if (nx_ < nsteps) {
+                int64_t off;
+                step_at(nx_, off, wb[(b + kSxDepth - 1) % kSxDepth]);
+                load_b(off, bf[(b + kSxDepth - 1) % kSxDepth]);
+              }
+              mma(wb[b], bf[b]);
+            }
+          }
         }
-        if (st < nsteps) mma(w0, b0);
       }
 #pragma unroll
       for (int nb = 0; nb < kSxNB; ++nb) {
