@@ -14,7 +14,9 @@ read back), so each error belongs to one stage:
   * the 2x average pooling of the input vs oracle.pool_valid (bf16 rounding
     bound) and the derived output shard sizes vs oracle.pooled_shard_sizes;
   * the stride-2 conv of the input vs oracle.conv_strided over the whole
-    output (1e-5), with the derived shard sizes.
+    output (1e-5), with the derived shard sizes;
+  * the stride-2 transposed conv from half resolution vs
+    oracle.conv_transposed over the whole 2048 x 2048 output (1e-5).
 """
 import numpy as np
 import pytest
@@ -130,6 +132,41 @@ def test_full_size_strided_conv():
         got[tuple([slice(None)] + [slice(o, o + e) for o, e in zip(inf["offset"], inf["extent"])])] = \
             outs[i].view(q.padded_shape(i)).cpu().numpy()
     want = oracle.conv_strided(oracle.widen(x, wl.dtype), wf, 2)
+    err = rel_err(got, want)
+    say(f"  max|err|/rms {err:.2e} (tolerance 1e-5)")
+    assert err <= 1e-5
+
+
+def test_full_size_transposed_conv():
+    """The bench's upsampling workload: the image workload at half resolution
+    (every shard halved) up to 2048 x 2048 with the layer's sharding shapes,
+    bias included, over the whole output."""
+    import dataclasses
+    wl_out = synth.workload(NAME)
+    wl = dataclasses.replace(wl_out, name=wl_out.name + "_half", spatial=tuple(n // 2 for n in wl_out.spatial),
+                             shards=tuple(tuple(e // 2 for e in a) for a in wl_out.shards))
+    say(f"full-size stride-2 transposed conv {wl.name} -> {NAME}")
+    y, w = synth.make_input(wl), synth.make_weight(wl)
+    layer = ShardedConvGN(wl)
+    layer.load_input(y)
+    layer.exchange()
+    q = hsc.st_plan_transposed(layer.in_plan, wl.ksize, 2, wl.cout)
+    assert q.shards == tuple(tuple(a) for a in wl_out.shards)
+    wf = np.swapaxes(oracle.widen(w, wl.dtype), 0, 1)               # W [Cy = Cin][Cx = Cout][k..]
+    wt = torch.from_numpy(np.ascontiguousarray(
+        np.moveaxis(wf.astype(np.float32).reshape(wl.cin, wl.cout, -1), 2, 0))).cuda()
+    bias = np.random.default_rng(7).uniform(-1, 1, wl.cout).astype(np.float32)
+    outs = [torch.empty(q.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(q.num_shards)]
+    hsc.st_conv_transposed_sharded(layer.in_plan, layer.x_bufs, wt, torch.from_numpy(bias).cuda(), wl.ksize, 2,
+                                   q, outs)
+    torch.cuda.synchronize()
+    got = np.empty((wl.batch, *[sum(a) for a in q.shards], wl.cout), np.float32)
+    for i in range(q.num_shards):
+        inf = q.shard_info(i)
+        got[tuple([slice(None)] + [slice(o, o + e) for o, e in zip(inf["offset"], inf["extent"])])] = \
+            outs[i].view(q.padded_shape(i)).cpu().numpy()
+    del outs
+    want = oracle.conv_transposed(oracle.widen(y, wl.dtype), np.ascontiguousarray(wf), 2) + bias
     err = rel_err(got, want)
     say(f"  max|err|/rms {err:.2e} (tolerance 1e-5)")
     assert err <= 1e-5
