@@ -75,3 +75,100 @@ def test_random_plan(seed):
     ey, ez = rel_err(a.y_host(), y_ref), rel_err(a.z_host(), z_ref)
     say(f"  max|err|/rms y {ey:.2e} z {ez:.2e}")
     assert ey <= TOL[wl.dtype] and ez <= TOL[wl.dtype]
+
+
+def _gather(q, outs, batch, dtype=np.float32):
+    got = np.empty((batch, *[sum(a) for a in q.shards], q.channels), dtype)
+    for i in range(q.num_shards):
+        inf = q.shard_info(i)
+        v = outs[i].view(q.padded_shape(i)).cpu().numpy()
+        got[tuple([slice(None)] + [slice(o, o + e) for o, e in zip(inf["offset"], inf["extent"])])] = \
+            v.view(dtype) if v.dtype != dtype else v
+    return got
+
+
+def _shape_ops(wl, x, w, bias):
+    """Stride-2 conv, stride-2 transposed conv and 2x average pooling of the
+    layer's exchanged input shards; None for an op whose derived plan leaves a
+    shard without outputs (the planner's documented rejection)."""
+    import halo_sharded_conv_amd as hsc
+    layer = ShardedConvGN(wl)
+    layer.load_input(x)
+    layer.exchange()
+    wf = oracle.widen(w, wl.dtype).astype(np.float32)
+    res = {}
+    b = torch.from_numpy(bias).cuda()
+    try:
+        q = hsc.st_plan_strided(layer.in_plan, wl.ksize, 2, wl.cout)
+        outs = [torch.empty(q.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(q.num_shards)]
+        wt = torch.from_numpy(np.ascontiguousarray(np.moveaxis(wf.reshape(wl.cout, wl.cin, -1), 2, 0).swapaxes(1, 2)))
+        hsc.st_conv_strided_sharded(layer.in_plan, layer.x_bufs, wt.cuda(), b, wl.ksize, 2, q, outs)
+        res["strided"] = (q, outs)
+    except hsc.ShardConvError as e:
+        assert e.status == 3, e                       # ST_ERR_SHARD_TOO_SMALL
+        res["strided"] = None
+    # transposed: W[o = Cin side][c = Cout side] read from the same weights
+    wtr = np.ascontiguousarray(np.swapaxes(wf, 0, 1))
+    q = hsc.st_plan_transposed(layer.in_plan, wl.ksize, 2, wl.cout)
+    outs = [torch.empty(q.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(q.num_shards)]
+    wt = torch.from_numpy(np.ascontiguousarray(np.moveaxis(wtr.reshape(wl.cin, wl.cout, -1), 2, 0)))
+    hsc.st_conv_transposed_sharded(layer.in_plan, layer.x_bufs, wt.cuda(), b, wl.ksize, 2, q, outs)
+    res["transposed"] = (q, outs, wtr)
+    try:
+        q = hsc.st_plan_pooled(layer.in_plan, 2, 2)
+        tdt = torch.int16 if wl.dtype == "bf16" else torch.float32
+        outs = [torch.empty(q.shard_info(i)["elems"], dtype=tdt, device="cuda") for i in range(q.num_shards)]
+        hsc.st_pool_sharded(layer.in_plan, layer.x_bufs, 2, 2, "avg", q, outs)
+        res["pool"] = (q, outs)
+    except hsc.ShardConvError as e:
+        assert e.status == 3, e
+        res["pool"] = None
+    torch.cuda.synchronize()
+    return res
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_plan_shape_changing_ops(seed):
+    """The same random plans through the shape-changing ops: derived shard
+    sizes as the oracle's rules give them, sharded == unsharded bit for bit,
+    and the oracle's tolerance (fp32 sums for the convs, one bf16 rounding for
+    bf16 pooling)."""
+    wl = draw(seed)
+    say(f"random plan {seed}, shape-changing ops: {wl.name} N={wl.batch} spatial={wl.spatial} shards={wl.shards}")
+    x, w = synth.make_input(wl), synth.make_weight(wl)
+    bias = np.random.default_rng(seed + 50).uniform(-1, 1, wl.cout).astype(np.float32)
+    a = _shape_ops(wl, x, w, bias)
+    u = _shape_ops(wl.unsharded(), x, w, bias)
+    xf = oracle.widen(x, wl.dtype)
+    wf = oracle.widen(w, wl.dtype)
+    if a["strided"] is None:
+        assert any(0 in oracle.strided_shard_sizes(wl.shards[ax], wl.ksize, 2) for ax in range(wl.ndim))
+    else:
+        q, outs = a["strided"]
+        for ax in range(wl.ndim):
+            assert list(q.shards[ax]) == oracle.strided_shard_sizes(wl.shards[ax], wl.ksize, 2)
+        got = _gather(q, outs, wl.batch)
+        assert bits_equal(got, _gather(*u["strided"], wl.batch))
+        e = rel_err(got, oracle.conv_strided(xf, wf, 2, bias))
+        say(f"  strided max|err|/rms {e:.2e}")
+        assert e <= 1e-5
+    q, outs, wtr = a["transposed"]
+    got = _gather(q, outs, wl.batch)
+    assert bits_equal(got, _gather(*u["transposed"][:2], wl.batch))
+    e = rel_err(got, oracle.conv_transposed(xf, wtr.astype(np.float64), 2) + bias)
+    say(f"  transposed max|err|/rms {e:.2e}")
+    assert e <= 1e-5
+    if a["pool"] is None:
+        assert any(0 in oracle.pooled_shard_sizes(wl.shards[ax], 2, 2) for ax in range(wl.ndim))
+    else:
+        q, outs = a["pool"]
+        for ax in range(wl.ndim):
+            assert list(q.shards[ax]) == oracle.pooled_shard_sizes(wl.shards[ax], 2, 2)
+        dt = np.uint16 if wl.dtype == "bf16" else np.float32
+        got = _gather(q, outs, wl.batch, dt)
+        assert bits_equal(got, _gather(*u["pool"], wl.batch, dt))
+        want = oracle.pool_valid(xf, 2, 2, "avg")
+        g = oracle.widen(got, wl.dtype)
+        rms = float(np.sqrt(np.mean(want * want)))
+        ulp = 2.0 ** -8 if wl.dtype == "bf16" else 2.0 ** -20
+        assert np.all(np.abs(g - want) <= ulp * np.abs(want) + 1e-6 * rms)
