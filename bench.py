@@ -420,10 +420,10 @@ def time_graph(args, stages):
 
 def shape_change_roofline(wl, key, ms, flops, alg_bytes, kernels, traffic):
     """Roofline of the strided / transposed conv kernel.  bf16 shapes with
-    Cin % 16 == 0 and Cout % 32 == 0 run on the matrix cores, where their
-    arithmetic intensity (~60-100 flop/byte) is below MI355X's ridge (~315):
-    HBM-bound.  The rest run on fp32 FMA: the ALU roofline against the 157.3
-    TFLOP/s fp32 vector peak."""
+    Cin % 16 == 0 and Cout % 32 == 0 run on the matrix cores: HBM-bound below
+    MI355X's ridge (~315 flop/byte; the 32- and 64-channel layers, 60-100),
+    MFMA-bound above it (256 channels).  The rest run on fp32 FMA: the ALU
+    roofline against the 157.3 TFLOP/s fp32 vector peak."""
     tf = flops / (ms * 1e-3) / 1e12
     gbs = alg_bytes / (ms * 1e-3) / 1e9
     mfma = wl.dtype == "bf16" and wl.cin % 16 == 0 and wl.cout % 32 == 0
@@ -431,6 +431,10 @@ def shape_change_roofline(wl, key, ms, flops, alg_bytes, kernels, traffic):
                          ("mfma_frac" if mfma else "fp32_frac"):
                              round(tf / (MFMA_BF16_PEAK_TFLOPS if mfma else FP32_PEAK_TFLOPS), 4),
                          "path": "bf16 MFMA" if mfma else "fp32 FMA"})
+    if mfma and flops / alg_bytes >= MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        # above the ridge (256-channel layers): the matrix cores bound it
+        return {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "kernel": key, "traffic": traffic}
     if mfma:
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": key, "traffic": traffic}
@@ -480,7 +484,7 @@ def bench_strided(args, wl):
     out = {"metric": METRIC_STRIDED, "value": wl.voxels / (ms_per_step * 1e-3), "unit": "voxels/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "gpu_ms_per_step": round(gpu_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "bf16" if roof["bound"] == "hbm" else "f32", "data": "synthetic",
+           "dtype": "f32" if roof["bound"] == "alu" else "bf16", "data": "synthetic",
            "config": {"workload": wl.name, "shape": [wl.batch, wl.cin, *wl.spatial], "cout": wl.cout,
                       "kernel": wl.ksize, "stride": s, "operands": wl.dtype, "shards": [list(a) for a in wl.shards],
                       "out_shards": [list(a) for a in q.shards], "pass": "strided",
@@ -560,7 +564,7 @@ def bench_transposed(args, wl_out):
     out = {"metric": METRIC_TRANSPOSED, "value": out_vox / (ms_per_step * 1e-3), "unit": "voxels/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "gpu_ms_per_step": round(gpu_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "bf16" if roof["bound"] == "hbm" else "f32", "data": "synthetic",
+           "dtype": "f32" if roof["bound"] == "alu" else "bf16", "data": "synthetic",
            "config": {"workload": wl_out.name, "input_shape": [wl.batch, wl.cin, *wl.spatial], "cout": wl.cout,
                       "kernel": wl.ksize, "stride": s, "operands": wl.dtype,
                       "in_shards": [list(a) for a in wl.shards], "out_shards": [list(a) for a in q.shards],
