@@ -11,11 +11,13 @@
 // beyond its interior on either side: the conv's usual halo of k/2 suffices.
 //
 // st_plan_strided derives the output plan; st_conv_strided_sharded runs one
-// launch over every shard on fp32 FMA: a thread takes one output position
-// and up to 64 output channels (blockIdx.y picks the channel block), reads
-// the window's input cells once and the weights as wave-uniform values, and
-// accumulates in a fixed order (taps lexicographic, input channels
-// ascending), so an output's bits do not depend on the shard plan.
+// launch over every shard: on the matrix cores for bf16 shapes whose channel
+// counts fit the 32x32x16 tile (conv_sx_mfma, further down), else on fp32
+// FMA (a thread takes one output position and up to 64 output channels,
+// blockIdx.y picks the channel block, reads the window's input cells once and
+// the weights as wave-uniform values).  Both accumulate in a fixed order
+// (taps lexicographic, input channels ascending), so an output's bits do not
+// depend on the shard plan.
 //
 // Its adjoint, the transposed (upsampling) convolution, is the same section's
 // rule run the other way: input cell i scatters onto outputs i*s + t - p, the
@@ -24,8 +26,9 @@
 // gathers from the taps t = r + p (mod s), i.e. input cells q + (r + p - t)/s,
 // all within p cells of q, so the input's halo of k/2 again suffices.
 // st_plan_transposed derives the output plan; st_conv_transposed_sharded runs
-// one launch with one phase per blockIdx.z, so the tap set is uniform over a
-// block and the weights stay wave-uniform.
+// the same matrix-core kernel with every phase of a position block in one
+// wave, or the fp32 FMA kernel with one phase per blockIdx.z, so the tap set
+// is uniform over a block and the weights stay wave-uniform.
 #include <algorithm>
 #include <cstdio>
 
