@@ -420,13 +420,15 @@ def time_graph(args, stages):
 
 def shape_change_roofline(wl, key, ms, flops, alg_bytes, kernels, traffic):
     """Roofline of the strided / transposed conv kernel.  bf16 shapes with
-    Cin % 16 == 0 and Cout % 32 == 0 run on the matrix cores: HBM-bound below
+    Cin % 16 == 0, Cout % 16 == 0 and the weights of a 32-channel block within
+    160 KiB run on the matrix cores: HBM-bound below
     MI355X's ridge (~315 flop/byte; the 32- and 64-channel layers, 60-100),
     MFMA-bound above it (256 channels).  The rest run on fp32 FMA: the ALU
     roofline against the 157.3 TFLOP/s fp32 vector peak."""
     tf = flops / (ms * 1e-3) / 1e12
     gbs = alg_bytes / (ms * 1e-3) / 1e9
-    mfma = wl.dtype == "bf16" and wl.cin % 16 == 0 and wl.cout % 32 == 0
+    mfma = (wl.dtype == "bf16" and wl.cin % 16 == 0 and wl.cout % 16 == 0
+            and wl.taps * wl.cin * 32 * 2 <= 160 * 1024)
     kernels[key].update({"TFLOP/s": round(tf, 2),
                          ("mfma_frac" if mfma else "fp32_frac"):
                              round(tf / (MFMA_BF16_PEAK_TFLOPS if mfma else FP32_PEAK_TFLOPS), 4),

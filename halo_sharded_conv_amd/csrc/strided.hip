@@ -11,8 +11,8 @@
 // beyond its interior on either side: the conv's usual halo of k/2 suffices.
 //
 // st_plan_strided derives the output plan; st_conv_strided_sharded runs one
-// launch over every shard: on the matrix cores for bf16 shapes whose channel
-// counts fit the 32x32x16 tile (conv_sx_mfma, further down), else on fp32
+// launch over every shard: on the matrix cores for bf16 shapes with Cin % 16
+// == 0 and Cout % 16 == 0 (conv_sx_mfma, further down), else on fp32
 // FMA (a thread takes one output position and up to 64 output channels,
 // blockIdx.y picks the channel block, reads the window's input cells once and
 // the weights as wave-uniform values).  Both accumulate in a fixed order
@@ -279,7 +279,9 @@ __global__ __launch_bounds__(256) void conv_sx_mfma(const SxArgs a) {
       const int rem = f - t * per_tap4;
       const int c = rem / (MB * 8);
       const int o = (rem - c * (MB * 8)) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(a.w + ((int64_t)t * a.cin + c) * a.cout + ob + o);
+      // rows past Cout (a 16-channel layer in a 32-row tile) hold zeros
+      const float4 v = ob + o < a.cout ? *reinterpret_cast<const float4*>(a.w + ((int64_t)t * a.cin + c) * a.cout + ob + o)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
       const int l = ((c >> 3) & 1) * 32 + (o & 31);
       uint16_t* d = wl + ((((t * KC + (c >> 4)) * MB + (o >> 5)) * 64 + l) << 3) + (c & 7);
       d[0] = sx_rne(v.x);
@@ -346,7 +348,8 @@ __global__ __launch_bounds__(256) void conv_sx_mfma(const SxArgs a) {
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float b = a.bias ? a.bias[ob + mb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3)] : 0.f;
+          const int row = ob + mb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+          const float b = a.bias && row < a.cout ? a.bias[row] : 0.f;
 #pragma unroll
           for (int nb = 0; nb < kSxNB; ++nb) acc[mb][nb][e] = b;
         }
@@ -418,8 +421,9 @@ __global__ __launch_bounds__(256) void conv_sx_mfma(const SxArgs a) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<float4*>(op[nb] + ob + mb * 32 + 8 * j + 4 * hf) =
-                make_float4(acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1], acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]);
+            if (ob + mb * 32 + 8 * j + 4 * hf < a.cout)
+              *reinterpret_cast<float4*>(op[nb] + ob + mb * 32 + 8 * j + 4 * hf) =
+                  make_float4(acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1], acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]);
       }
     }
   }
@@ -435,7 +439,8 @@ constexpr int kSxCapLarge = 160 * 1024;         // one workgroup per CU
 template <bool TR>
 bool launch_sx_mfma(const SxShard* shards, int nshards, int batch, int cin, int cout, int k, int stride, int ndim,
                     const float* w, const float* bias, hipStream_t st) {
-  if (cin % 16 != 0 || cout % 32 != 0 || (reinterpret_cast<uintptr_t>(w) & 15)) return false;
+  // Cout a multiple of 16: a 16-channel layer fills half of one 32-row tile
+  if (cin % 16 != 0 || cout % 16 != 0 || (reinterpret_cast<uintptr_t>(w) & 15)) return false;
   const int taps = ndim == 3 ? k * k * k : k * k;
   int mb = cout % 64 == 0 ? 2 : 1;
   int64_t need = (int64_t)taps * cin * mb * 32 * 2;
@@ -471,7 +476,7 @@ bool launch_sx_mfma(const SxShard* shards, int nshards, int batch, int cin, int 
   grid = (grid + 7) / 8 * 8;
   a.iters = (int)((groups + grid - 1) / grid);
   const int kg = cin % 64 == 0 ? 4 : cin % 32 == 0 ? 2 : 1;
-  const dim3 g3((unsigned)grid, (unsigned)(cout / (mb * 32))), block(kSxWaves * 64);
+  const dim3 g3((unsigned)grid, (unsigned)((cout + mb * 32 - 1) / (mb * 32))), block(kSxWaves * 64);
 #define ST_SX(MB_, KG_, CAP_) hipLaunchKernelGGL((conv_sx_mfma<MB_, KG_, TR, CAP_>), g3, block, 0, st, a)
 #define ST_SX_KG(MB_, CAP_)           \
   do {                                \

@@ -321,7 +321,7 @@ st_status st_plan_strided(const st_plan* in_plan, int32_t ksize, int32_t stride,
  *   bias_or_null       Cout floats or NULL
  *   out_plan, out_bufs the plan st_plan_strided returned for (in_plan, ksize,
  *                      stride, Cout) and its fp32 shards (only interiors written)
- * bf16 input shards with Cin % 16 == 0, Cout % 32 == 0 and the weights of
+ * bf16 input shards with Cin % 16 == 0, Cout % 16 == 0 and the weights of
  * a 64- (or 32-) channel output block within 160 KiB run on the matrix cores
  * (bf16 products, fp32 accumulation); every other case on fp32 FMA.  Either
  * way each output sums bias, then taps lexicographic, input channels

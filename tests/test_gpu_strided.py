@@ -8,6 +8,8 @@ strided_shard_sizes; y against oracle.conv_strided within the fp32
 tolerance (bf16 operands multiply exactly in fp32, so 1e-5 holds for them
 too); sharded equal to unsharded bit for bit.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -21,6 +23,8 @@ from helpers import bits_equal, direct_cases, rel_err, say, small_cases
 pytestmark = pytest.mark.gpu
 
 CASES = {**small_cases(), **direct_cases()}
+# 64 -> 48 channels: a 32-row tile and a half-filled one on the matrix cores
+CASES["img_c64to48"] = dataclasses.replace(CASES["img64_small"], name="img_c64to48", cout=48, groups=4)
 TOL_STRIDED = 1e-5      # fp32 accumulation of exact products
 
 
@@ -48,7 +52,7 @@ def run_strided(wl, x, w, bias, s):
 
 
 SPECS = [("img64_small", 2), ("img64_b2", 2), ("vol32_grid", 2), ("vol16k5", 2), ("vol32_full", 2),
-         ("grid256_small", 2), ("img_c5to12_k3", 2), ("vol_c3to4_k5", 3), ("vol32_b2", 3)]
+         ("grid256_small", 2), ("img_c5to12_k3", 2), ("vol_c3to4_k5", 3), ("vol32_b2", 3), ("img_c64to48", 2)]
 
 
 @pytest.mark.parametrize("name,s", SPECS)

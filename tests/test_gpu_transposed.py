@@ -24,6 +24,8 @@ from helpers import bits_equal, direct_cases, rel_err, say, small_cases
 pytestmark = pytest.mark.gpu
 
 CASES = {**small_cases(), **direct_cases()}
+# 64 -> 48 channels: a 32-row tile and a half-filled one on the matrix cores
+CASES["img_c64to48"] = dataclasses.replace(CASES["img64_small"], name="img_c64to48", cout=48, groups=4)
 TOL_TRANSPOSED = 1e-5      # fp32 products and accumulation
 
 
@@ -65,7 +67,7 @@ def run_transposed(wl, y, w, bias, s):
 
 SPECS = [("img64_small", 2), ("img64_b2", 2), ("vol32_grid", 2), ("vol16k5", 2), ("vol32_full", 2),
          ("grid256_small", 2), ("img_c5to12_k3", 2), ("vol_c3to4_k5", 3), ("vol32_b2", 3), ("img64_small", 1),
-         ("img_c5to12_k3", 4)]
+         ("img_c5to12_k3", 4), ("img_c64to48", 2)]
 
 
 @pytest.mark.parametrize("name,s", SPECS)
