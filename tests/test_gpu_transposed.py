@@ -67,7 +67,8 @@ def run_transposed(wl, y, w, bias, s):
 
 SPECS = [("img64_small", 2), ("img64_b2", 2), ("vol32_grid", 2), ("vol16k5", 2), ("vol32_full", 2),
          ("grid256_small", 2), ("img_c5to12_k3", 2), ("vol_c3to4_k5", 3), ("vol32_b2", 3), ("img64_small", 1),
-         ("img_c5to12_k3", 4), ("img_c64to48", 2)]
+         ("img_c5to12_k3", 4), ("img_c64to48", 2),
+         ("img64_small", 4), ("vol32_grid", 3)]     # matrix-core path with tapless phases; 27 phases in 3D
 
 
 @pytest.mark.parametrize("name,s", SPECS)
