@@ -52,7 +52,8 @@ def run_strided(wl, x, w, bias, s):
 
 
 SPECS = [("img64_small", 2), ("img64_b2", 2), ("vol32_grid", 2), ("vol16k5", 2), ("vol32_full", 2),
-         ("grid256_small", 2), ("img_c5to12_k3", 2), ("vol_c3to4_k5", 3), ("vol32_b2", 3), ("img_c64to48", 2)]
+         ("grid256_small", 2), ("img_c5to12_k3", 2), ("vol_c3to4_k5", 3), ("vol32_b2", 3), ("img_c64to48", 2),
+         ("img64_small", 1), ("vol16k5", 1)]      # stride 1: the 'same' conv
 
 
 @pytest.mark.parametrize("name,s", SPECS)
@@ -65,6 +66,8 @@ def test_strided_matches_oracle(name, s):
     for a in range(wl.ndim):
         assert list(q.shards[a]) == oracle.strided_shard_sizes(wl.shards[a], wl.ksize, s)
     want = oracle.conv_strided(oracle.widen(x, wl.dtype), oracle.widen(w, wl.dtype), s, bias)
+    if s == 1:      # stride 1 is the 'same' conv of the forward layer
+        assert got.shape == want.shape == x.shape[:-1] + (wl.cout,)
     err = rel_err(got, want)
     say(f"  max|err|/rms = {err:.2e} (tolerance {TOL_STRIDED:.0e})")
     assert err <= TOL_STRIDED
