@@ -31,6 +31,7 @@
 // is uniform over a block and the weights stay wave-uniform.
 #include <algorithm>
 #include <cstdio>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -234,8 +235,10 @@ bool transposed_reach(int k, int s, int& lo, int& hi) {
 
 typedef __bf16 sx_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float sx_f32x16 __attribute__((ext_vector_type(16)));
+typedef float sx_f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSxNB = 2;                        // 32-position blocks per wave
+constexpr int kSxTile = 64;                     // positions per wave tile
+constexpr bool kSxPrefer16 = true;              // 16x16x32 fragments where Cin % 32 == 0
 constexpr int kSxWaves = 4;
 constexpr int kSxDepth = 3;                     // K steps of input fragments held per wave
 
@@ -262,28 +265,36 @@ __device__ __forceinline__ uint16_t sx_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-template <int MB, int KG, bool TR, int CAP>
-__global__ __launch_bounds__(256) void conv_sx_mfma(const SxArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t wl[CAP / 2];   // [taps][Cin/16][MB][64 lanes][8]
-  const int KC = a.cin >> 4;
-  const int ob = blockIdx.y * MB * 32;
+// FR = 32: v_mfma_f32_32x32x16_bf16 (lane holds 8 of 16 K for position
+// lane % 32); FR = 16: v_mfma_f32_16x16x32_bf16 (8 of 32 K for position
+// lane % 16), whose B loads cover 16 cells x 64 bytes instead of 32 cells x
+// 32 bytes per instruction.  A wave owns 64 positions and MB x FR channels.
+template <int FR, int MB, int KG, bool TR, int CAP>
+__global__ __launch_bounds__(256, CAP <= 80 * 1024 ? 2 : 1) void conv_sx_mfma(const SxArgs a) {
+  using acc_t = typename std::conditional<FR == 32, sx_f32x16, sx_f32x4>::type;
+  constexpr int KS = FR == 32 ? 16 : 32;          // channels per K step
+  constexpr int NBK = 64 / FR;                    // position blocks per wave
+  constexpr int NACC = FR == 32 ? 16 : 4;         // accumulators per block and lane
+  __shared__ __attribute__((aligned(16))) uint16_t wl[CAP / 2];   // [taps][Cin/KS][MB][64 lanes][8]
+  const int KC = a.cin / KS;
+  const int ob = blockIdx.y * MB * FR;
   {
     // weights of this channel block, read in global order 4 output channels
     // (16 bytes) at a time, rounded to bf16, written to their fragment slots
     // (4 consecutive output channels are 4 consecutive lanes' slots)
-    const int per_tap4 = a.cin * MB * 8;
+    const int per_tap4 = a.cin * MB * FR / 4;
     const int total4 = a.taps * per_tap4;
 #pragma unroll 4
     for (int f = threadIdx.x; f < total4; f += blockDim.x) {
       const int t = f / per_tap4;
       const int rem = f - t * per_tap4;
-      const int c = rem / (MB * 8);
-      const int o = (rem - c * (MB * 8)) * 4;
+      const int c = rem / (MB * FR / 4);
+      const int o = (rem - c * (MB * FR / 4)) * 4;
       // rows past Cout (a 16-channel layer in a 32-row tile) hold zeros
       const float4 v = ob + o < a.cout ? *reinterpret_cast<const float4*>(a.w + ((int64_t)t * a.cin + c) * a.cout + ob + o)
                                        : make_float4(0.f, 0.f, 0.f, 0.f);
-      const int l = ((c >> 3) & 1) * 32 + (o & 31);
-      uint16_t* d = wl + ((((t * KC + (c >> 4)) * MB + (o >> 5)) * 64 + l) << 3) + (c & 7);
+      const int l = ((c % KS) >> 3) * FR + (o % FR);
+      uint16_t* d = wl + ((((t * KC + c / KS) * MB + o / FR) * 64 + l) << 3) + (c & 7);
       d[0] = sx_rne(v.x);
       d[8] = sx_rne(v.y);
       d[16] = sx_rne(v.z);
@@ -292,7 +303,7 @@ __global__ __launch_bounds__(256) void conv_sx_mfma(const SxArgs a) {
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, hf = lane >> 5;
+  const int lp = lane % FR, grp = lane / FR;      // position in the block, K group of 8
   const int s = a.stride, k = a.k, p = k / 2;
   const bool v3 = a.ndim == 3;
   const int sd = v3 ? s : 1, kd = v3 ? k : 1, pd = kd / 2;
@@ -306,12 +317,12 @@ __global__ __launch_bounds__(256) void conv_sx_mfma(const SxArgs a) {
     int si = 0;
     while (si + 1 < a.nshards && a.sh[si + 1].tile_begin <= tile) ++si;
     const SxShard& sh = a.sh[si];
-    const int64_t p0 = (tile - sh.tile_begin) * (kSxNB * 32);
-    int pz[kSxNB], py[kSxNB], px[kSxNB], pn[kSxNB];
-    bool ok[kSxNB];
+    const int64_t p0 = (tile - sh.tile_begin) * 64;
+    int pz[NBK], py[NBK], px[NBK], pn[NBK];
+    bool ok[NBK];
 #pragma unroll
-    for (int nb = 0; nb < kSxNB; ++nb) {
-      const int64_t q = p0 + nb * 32 + l32;
+    for (int nb = 0; nb < NBK; ++nb) {
+      const int64_t q = p0 + nb * FR + lp;
       ok[nb] = q < sh.positions;
       int64_t r = ok[nb] ? q : 0;
       px[nb] = (int)(r % sh.ext[2]);
@@ -327,33 +338,35 @@ __global__ __launch_bounds__(256) void conv_sx_mfma(const SxArgs a) {
       const int t0w = TR ? (rw + p) % s : 0, t0h = TR ? (rh + p) % s : 0, t0d = TR ? (rd + pd) % sd : 0;
       const int tstep = TR ? s : 1, tstepd = TR ? sd : 1;
       const int dw = TR ? (rw + p - t0w) / s : 0, dh = TR ? (rh + p - t0h) / s : 0, dd = TR ? (rd + pd - t0d) / sd : 0;
-      const uint16_t* bp[kSxNB];
-      float* op[kSxNB];
+      const uint16_t* bp[NBK];
+      float* op[NBK];
 #pragma unroll
-      for (int nb = 0; nb < kSxNB; ++nb) {
+      for (int nb = 0; nb < NBK; ++nb) {
         if (TR) {
           bp[nb] = sh.in + pn[nb] * sh.isn + (int64_t)(pz[nb] + dd) * sh.is[0] + (int64_t)(py[nb] + dh) * sh.is[1] +
-                   (int64_t)(px[nb] + dw) * sh.is[2] + hf * 8;
+                   (int64_t)(px[nb] + dw) * sh.is[2] + grp * 8;
           op[nb] = sh.out + pn[nb] * sh.osn + (int64_t)(pz[nb] * sd + rd) * sh.os[0] +
                    (int64_t)(py[nb] * s + rh) * sh.os[1] + (int64_t)(px[nb] * s + rw) * sh.os[2];
         } else {
           bp[nb] = sh.in + pn[nb] * sh.isn + (int64_t)pz[nb] * s * sh.is[0] + (int64_t)py[nb] * s * sh.is[1] +
-                   (int64_t)px[nb] * s * sh.is[2] + hf * 8;
+                   (int64_t)px[nb] * s * sh.is[2] + grp * 8;
           op[nb] = sh.out + pn[nb] * sh.osn + (int64_t)pz[nb] * sh.os[0] + (int64_t)py[nb] * sh.os[1] +
                    (int64_t)px[nb] * sh.os[2];
         }
       }
-      sx_f32x16 acc[MB][kSxNB];
+      // accumulator e of a lane is row 8(e/4) + 4 grp + e%4 (FR 32) or
+      // 4 grp + e (FR 16) of the block, column lp
+      acc_t acc[MB][NBK];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = ob + mb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+        for (int e = 0; e < NACC; ++e) {
+          const int row = ob + mb * FR + 8 * (e >> 2) + 4 * grp + (e & 3);
           const float b = a.bias && row < a.cout ? a.bias[row] : 0.f;
 #pragma unroll
-          for (int nb = 0; nb < kSxNB; ++nb) acc[mb][nb][e] = b;
+          for (int nb = 0; nb < NBK; ++nb) acc[mb][nb][e] = b;
         }
-      // K steps: (tap of the phase, block of KG x 16 channels), taps lexicographic;
+      // K steps: (tap of the phase, block of KG x KS channels), taps lexicographic;
       // the next step's input fragments are loaded before this step's MFMAs
       const int nz = (kd - t0d + tstepd - 1) / tstepd, ny = (k - t0h + tstep - 1) / tstep,
                 nx = (k - t0w + tstep - 1) / tstep;
@@ -366,17 +379,17 @@ __global__ __launch_bounds__(256) void conv_sx_mfma(const SxArgs a) {
         // strided: cell j*s + t - p (base at the window's first cell);
         // transposed: cell q + (r + p - t)/s, one back per step of s
         off = (TR ? -(mz * sh.is[0] + my * sh.is[1] + mx * sh.is[2]) : tz * sh.is[0] + ty * sh.is[1] + tx * sh.is[2]) +
-              c0 * 16;
+              c0 * KS;
         wbase = (((tz * k + ty) * k + tx) * KC + c0) * MB * 512;
       };
-      auto load_b = [&](int64_t off, sx_bf16x8 (&bv)[KG][kSxNB]) __attribute__((always_inline)) {
+      auto load_b = [&](int64_t off, sx_bf16x8 (&bv)[KG][NBK]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kc = 0; kc < KG; ++kc)
 #pragma unroll
-          for (int nb = 0; nb < kSxNB; ++nb)
-            bv[kc][nb] = *reinterpret_cast<const sx_bf16x8*>(bp[nb] + off + kc * 16);
+          for (int nb = 0; nb < NBK; ++nb)
+            bv[kc][nb] = *reinterpret_cast<const sx_bf16x8*>(bp[nb] + off + kc * KS);
       };
-      auto mma = [&](int wbase, const sx_bf16x8 (&bv)[KG][kSxNB]) __attribute__((always_inline)) {
+      auto mma = [&](int wbase, const sx_bf16x8 (&bv)[KG][NBK]) __attribute__((always_inline)) {
         const uint16_t* wt = wl + wbase + lane * 8;
 #pragma unroll
         for (int kc = 0; kc < KG; ++kc)
@@ -384,13 +397,17 @@ __global__ __launch_bounds__(256) void conv_sx_mfma(const SxArgs a) {
           for (int mb = 0; mb < MB; ++mb) {
             const sx_bf16x8 av = *reinterpret_cast<const sx_bf16x8*>(wt + (kc * MB + mb) * 512);
 #pragma unroll
-            for (int nb = 0; nb < kSxNB; ++nb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[kc][nb], acc[mb][nb], 0, 0, 0);
+            for (int nb = 0; nb < NBK; ++nb) {
+              if constexpr (FR == 32)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[kc][nb], acc[mb][nb], 0, 0, 0);
+              else
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[kc][nb], acc[mb][nb], 0, 0, 0);
+            }
           }
       };
       // ring of kSxDepth fragment sets: kSxDepth - 1 steps in flight ahead of the MFMAs
       {
-        sx_bf16x8 bf[kSxDepth][KG][kSxNB];
+        sx_bf16x8 bf[kSxDepth][KG][NBK];
         int wb[kSxDepth];
 #pragma unroll
         for (int i = 0; i < kSxDepth - 1; ++i)
@@ -415,14 +432,14 @@ __global__ __launch_bounds__(256) void conv_sx_mfma(const SxArgs a) {
         }
       }
 #pragma unroll
-      for (int nb = 0; nb < kSxNB; ++nb) {
+      for (int nb = 0; nb < NBK; ++nb) {
         if (!ok[nb]) continue;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (ob + mb * 32 + 8 * j + 4 * hf < a.cout)
-              *reinterpret_cast<float4*>(op[nb] + ob + mb * 32 + 8 * j + 4 * hf) =
+          for (int j = 0; j < NACC / 4; ++j)
+            if (ob + mb * FR + 8 * j + 4 * grp < a.cout)
+              *reinterpret_cast<float4*>(op[nb] + ob + mb * FR + 8 * j + 4 * grp) =
                   make_float4(acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1], acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]);
       }
     }
@@ -442,10 +459,12 @@ bool launch_sx_mfma(const SxShard* shards, int nshards, int batch, int cin, int 
   // Cout a multiple of 16: a 16-channel layer fills half of one 32-row tile
   if (cin % 16 != 0 || cout % 16 != 0 || (reinterpret_cast<uintptr_t>(w) & 15)) return false;
   const int taps = ndim == 3 ? k * k * k : k * k;
-  int mb = cout % 64 == 0 ? 2 : 1;
-  int64_t need = (int64_t)taps * cin * mb * 32 * 2;
-  if (need > kSxCapLarge && mb == 2) {
-    mb = 1;
+  // 16x16x32 fragments when Cin % 32 == 0 (wider B loads), else 32x32x16
+  const int fr = kSxPrefer16 && cin % 32 == 0 ? 16 : 32;
+  int mb = fr == 16 ? (cout % 64 == 0 ? 4 : cout % 32 == 0 ? 2 : 1) : (cout % 64 == 0 ? 2 : 1);
+  int64_t need = (int64_t)taps * cin * mb * fr * 2;
+  while (need > kSxCapLarge && mb > 1) {
+    mb /= 2;
     need /= 2;
   }
   if (need > kSxCapLarge) return false;
@@ -464,7 +483,7 @@ bool launch_sx_mfma(const SxShard* shards, int nshards, int batch, int cin, int 
     a.sh[i] = shards[i];
     a.sh[i].positions = batch * (int64_t)shards[i].ext[0] * shards[i].ext[1] * shards[i].ext[2];
     a.sh[i].tile_begin = tiles;
-    tiles += (a.sh[i].positions + kSxNB * 32 - 1) / (kSxNB * 32);
+    tiles += (a.sh[i].positions + kSxTile - 1) / kSxTile;
   }
   a.tiles = tiles;
   if (tiles == 0) return true;
@@ -475,23 +494,41 @@ bool launch_sx_mfma(const SxShard* shards, int nshards, int batch, int cin, int 
   int64_t grid = std::min<int64_t>(groups, small ? 512 : 256);
   grid = (grid + 7) / 8 * 8;
   a.iters = (int)((groups + grid - 1) / grid);
-  const int kg = cin % 64 == 0 ? 4 : cin % 32 == 0 ? 2 : 1;
-  const dim3 g3((unsigned)grid, (unsigned)((cout + mb * 32 - 1) / (mb * 32))), block(kSxWaves * 64);
-#define ST_SX(MB_, KG_, CAP_) hipLaunchKernelGGL((conv_sx_mfma<MB_, KG_, TR, CAP_>), g3, block, 0, st, a)
-#define ST_SX_KG(MB_, CAP_)           \
-  do {                                \
-    if (kg == 4) ST_SX(MB_, 4, CAP_); \
-    else if (kg == 2) ST_SX(MB_, 2, CAP_); \
-    else ST_SX(MB_, 1, CAP_);         \
+  // K steps loaded together: 64 channels when Cin allows
+  const int ks = fr == 16 ? 32 : 16;
+  const int kg = cin % 64 == 0 ? 64 / ks : cin % 32 == 0 ? 32 / ks : 1;
+  const dim3 g3((unsigned)grid, (unsigned)((cout + mb * fr - 1) / (mb * fr))), block(kSxWaves * 64);
+#define ST_SX(FR_, MB_, KG_, CAP_) hipLaunchKernelGGL((conv_sx_mfma<FR_, MB_, KG_, TR, CAP_>), g3, block, 0, st, a)
+#define ST_SX_CAP(FR_, MB_, KG_)                  \
+  do {                                            \
+    if (small) ST_SX(FR_, MB_, KG_, kSxCapSmall); \
+    else ST_SX(FR_, MB_, KG_, kSxCapLarge);       \
   } while (0)
-  if (mb == 2) {
-    if (small) ST_SX_KG(2, kSxCapSmall);
-    else ST_SX_KG(2, kSxCapLarge);
+#define ST_SX_KG(FR_, MB_)                   \
+  do {                                       \
+    if (kg == 4) ST_SX_CAP(FR_, MB_, 4);     \
+    else if (kg == 2) ST_SX_CAP(FR_, MB_, 2); \
+    else ST_SX_CAP(FR_, MB_, 1);             \
+  } while (0)
+  if (fr == 16) {
+    // kg is 1 or 2 here
+    if (mb == 4) {
+      if (kg == 2) ST_SX_CAP(16, 4, 2);
+      else ST_SX_CAP(16, 4, 1);
+    } else if (mb == 2) {
+      if (kg == 2) ST_SX_CAP(16, 2, 2);
+      else ST_SX_CAP(16, 2, 1);
+    } else {
+      if (kg == 2) ST_SX_CAP(16, 1, 2);
+      else ST_SX_CAP(16, 1, 1);
+    }
+  } else if (mb == 2) {
+    ST_SX_KG(32, 2);
   } else {
-    if (small) ST_SX_KG(1, kSxCapSmall);
-    else ST_SX_KG(1, kSxCapLarge);
+    ST_SX_KG(32, 1);
   }
 #undef ST_SX_KG
+#undef ST_SX_CAP
 #undef ST_SX
   return true;
 }
