@@ -311,9 +311,14 @@ __global__ __launch_bounds__(256, CAP <= 80 * 1024 ? 2 : 1) void conv_sx_mfma(co
   // XCD-aware order: consecutive logical workgroups share one XCD's L2
   int g = blockIdx.x;
   if ((gridDim.x & 7) == 0) g = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  // the workgroup's tile groups in the order 0, h, 1, h + 1, ... (h = half):
+  // a block two rows tall takes its two rows' matching column segments back
+  // to back, so the input rows they share are still in L2
+  const int half = (a.iters + 1) >> 1;
   for (int it = 0; it < a.iters; ++it) {
-    const int64_t tile = ((int64_t)g * a.iters + it) * kSxWaves + wave;
-    if (tile >= a.tiles) break;
+    const int itp = (it & 1) ? half + (it >> 1) : (it >> 1);
+    const int64_t tile = ((int64_t)g * a.iters + itp) * kSxWaves + wave;
+    if (tile >= a.tiles) continue;
     int si = 0;
     while (si + 1 < a.nshards && a.sh[si + 1].tile_begin <= tile) ++si;
     const SxShard& sh = a.sh[si];
