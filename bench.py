@@ -51,12 +51,17 @@ def parse():
     ap.add_argument("--graph", choices=("on", "off"), default="on",
                     help="time the step as a replayed HIP graph (per-stage times come from an eager run of "
                          "the same steps); the input-gradient pass always runs eagerly")
+    ap.add_argument("--cold", choices=("on", "off"), default="on",
+                    help="after the timed steps, time each stage again over the same number of steps with a "
+                         "1 GiB buffer written between steps (caches flushed); reports median and min per stage")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the oracle's CPU sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling the HBM byte counters)")
     ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter files into a traffic record")
+    ap.add_argument("--record-stage", default="conv", choices=("conv", "strided", "transposed", "pool"),
+                    help="the stage whose kernels --record-traffic counts")
     ap.add_argument("--record-out", default=None, help="where --record-traffic writes its JSON")
     return ap.parse_args()
 
@@ -67,7 +72,7 @@ STAGE_KERNELS = {                    # kernel-name fragments of each library sta
     "conv": ("conv_rows", "conv_pairs", "conv_gemm", "conv_direct"),
     "gn_partials": ("gn_max", "gn_stats"), "gn_apply": ("gn_apply",),
     "wgrad": ("wgrad_mfma", "wgrad_direct"), "gn_backward": ("gn_max", "gnb_"), "pool": ("pool_kernel",),
-    "strided": ("conv_strided",), "transposed": ("conv_transposed",),
+    "strided": ("conv_sx_mfma", "conv_strided"), "transposed": ("conv_sx_mfma", "conv_transposed"),
 }
 
 
@@ -123,7 +128,7 @@ def record_traffic(args):
     import synth
     fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.record_traffic
     wl = synth.workload(args.workload or synth.BENCH_WORKLOAD)
-    stage = "conv"
+    stage = args.record_stage
     f = _counter_means(fetch_csv, STAGE_KERNELS[stage])["FETCH_SIZE"]
     w = _counter_means(write_csv, STAGE_KERNELS[stage])["WRITE_SIZE"]
     # the copy is the elementwise dispatch that reads; the fill before it only writes
@@ -138,7 +143,7 @@ def record_traffic(args):
         "fetch_scale": f_scale, "write_scale": w_scale,
         "traffic_bytes": f[0] * 1024.0 * f_scale + w[0] * 1024.0 * w_scale,
     }
-    out = args.record_out or os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    out = args.record_out or traffic_path(wl, stage)
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
@@ -159,10 +164,17 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}))
 
 
+def traffic_path(wl, stage):
+    """Where the traffic record of one stage on one workload lives (the conv's
+    carries no stage suffix)."""
+    suffix = "" if stage == "conv" else f"_{stage}"
+    return os.path.join(ROOT, "profiles", f"traffic_{wl.name}{suffix}.json")
+
+
 def load_traffic(wl, stage):
     """Measured HBM bytes per launch of `stage`, or None when no record exists
     or the kernels changed since it was taken."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    p = traffic_path(wl, stage)
     if not os.path.exists(p):
         return None
     with open(p) as fh:
@@ -310,10 +322,11 @@ def main():
     eager_ms = ms_per_step
     if args.pass_ == "forward" and args.graph == "on":
         ms_per_step, gpu_ms = time_graph(args, stages)
+    cold = time_stages_cold(args, stages, stream) if args.cold == "on" else None
 
     report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, METRIC if args.pass_ == "forward" else METRIC_DGRAD,
            None if args.pass_ == "forward" else synth.make_weight(wl_fwd),
-           eager_ms=eager_ms if args.pass_ == "forward" and args.graph == "on" else None)
+           eager_ms=eager_ms if args.pass_ == "forward" and args.graph == "on" else None, cold=cold)
 
 
 def time_stages(args, stages, stream):
@@ -343,6 +356,42 @@ def time_stages(args, stages, stream):
     gpu_ms = start.elapsed_time(end) / args.steps
     per_kernel_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
     return per_kernel_ms, wall * 1e3 / args.steps, gpu_ms
+
+
+FLUSH_BYTES = 1 << 30                # written between cold steps: 4x the 256 MB Infinity Cache
+
+
+def time_stages_cold(args, stages, stream):
+    """K more eager steps, each after a 1 GiB write that evicts L2 and the
+    Infinity Cache, so no stage starts with its operands cache-resident; HIP
+    events around every stage and around the step, median and min over the
+    steps.  The flush itself is outside every event pair."""
+    import numpy as np
+    import torch
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    ev = {k: [] for k, _ in stages}
+    steps = []
+    for i in range(args.steps):
+        flush.fill_(float(i))
+        s0 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for k, fn in stages:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev[k].append((a, b))
+        s1 = torch.cuda.Event(enable_timing=True)
+        s1.record(stream)
+        steps.append((s0, s1))
+    torch.cuda.synchronize()
+    del flush
+    out = {k: {"median_ms": round(float(np.median([a.elapsed_time(b) for a, b in v])), 5),
+               "min_ms": round(float(np.min([a.elapsed_time(b) for a, b in v])), 5)} for k, v in ev.items()}
+    t = [a.elapsed_time(b) for a, b in steps]
+    out["step"] = {"median_ms": round(float(np.median(t)), 5), "min_ms": round(float(np.min(t)), 5)}
+    return out
 
 
 def bench_backward(args, wl_fwd):
@@ -665,7 +714,8 @@ def bench_pool(args, wl):
     print(json.dumps(out), flush=True)
 
 
-def report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, metric, w_fwd, dgrad_layer=None, eager_ms=None):
+def report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, metric, w_fwd, dgrad_layer=None, eager_ms=None,
+           cold=None):
     """One JSON line: throughput, per-stage rates and the longest stage against its roofline."""
     alg = algorithmic(wl, layer)
     if dgrad_layer is not None:
@@ -719,6 +769,8 @@ def report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, metric, w_fwd, d
     }
     if eager_ms is not None:
         out["eager_ms_per_step"] = round(eager_ms, 4)
+    if cold is not None:
+        out["cold_eager"] = cold
     if not args.no_cpu_baseline:
         rows = args.cpu_rows or max(1, min(wl.spatial[0], int(5.0e5 // (wl.voxels // wl.spatial[0]) + 1)))
         out["cpu_baseline"] = cpu_baseline(wl, rows, w_fwd, backward=args.pass_ == "backward")
