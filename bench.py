@@ -482,6 +482,8 @@ def shape_change_roofline(wl, key, ms, flops, alg_bytes, kernels, traffic):
                          ("mfma_frac" if mfma else "fp32_frac"):
                              round(tf / (MFMA_BF16_PEAK_TFLOPS if mfma else FP32_PEAK_TFLOPS), 4),
                          "path": "bf16 MFMA" if mfma else "fp32 FMA"})
+    peak_tf = MFMA_BF16_PEAK_TFLOPS if mfma else FP32_PEAK_TFLOPS
+    kernels[key]["attainable_frac"] = round(tf / min(peak_tf, flops / alg_bytes * HBM_PEAK_GBS / 1e3), 4)
     if mfma and flops / alg_bytes >= MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
         # above the ridge (256-channel layers): the matrix cores bound it
         return {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -733,6 +735,10 @@ def report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, metric, w_fwd, d
             peak = FP32_PEAK_TFLOPS if wl.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
             rec["TFLOP/s"] = round(alg[k]["flops"] / (ms * 1e-3) / 1e12, 2)
             rec["mfma_frac"] = round(rec["TFLOP/s"] / peak, 4)
+            if alg[k].get("bytes"):
+                # attainable roofline: min(compute peak, arithmetic intensity x HBM peak)
+                attain = min(peak, alg[k]["flops"] / alg[k]["bytes"] * HBM_PEAK_GBS / 1e3)
+                rec["attainable_frac"] = round(rec["TFLOP/s"] / attain, 4)
         kernels[k] = rec
 
     dom = max(per_kernel_ms, key=per_kernel_ms.get)
