@@ -52,8 +52,9 @@ def parse():
                     help="time the step as a replayed HIP graph (per-stage times come from an eager run of "
                          "the same steps); the input-gradient pass always runs eagerly")
     ap.add_argument("--cold", choices=("on", "off"), default="on",
-                    help="after the timed steps, time each stage again over the same number of steps with a "
-                         "1 GiB buffer written between steps (caches flushed); reports median and min per stage")
+                    help="forward and input-gradient passes: after the timed steps, time each stage again over "
+                         "the same number of steps with a 1 GiB buffer written between steps (caches flushed); "
+                         "reports median and min per stage")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the oracle's CPU sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -322,7 +323,7 @@ def main():
     eager_ms = ms_per_step
     if args.pass_ == "forward" and args.graph == "on":
         ms_per_step, gpu_ms = time_graph(args, stages)
-    cold = time_stages_cold(args, stages, stream) if args.cold == "on" else None
+    cold = time_stages_cold(args, stages, stream) if args.cold == "on" and args.steps > 0 else None
 
     report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, METRIC if args.pass_ == "forward" else METRIC_DGRAD,
            None if args.pass_ == "forward" else synth.make_weight(wl_fwd),
