@@ -750,7 +750,9 @@ def report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, metric, w_fwd, d
         if ai < ridge:
             roof = {"bound": "hbm", "achieved": kernels[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
         else:
-            roof = {"bound": "mfma", "achieved": kernels[dom]["TFLOP/s"], "peak": peak_t, "unit": "TFLOP/s"}
+            # fp32 layers run on the vector ALUs (fp32 FMA), bf16 layers on the matrix cores
+            roof = {"bound": "alu" if wl.dtype == "f32" else "mfma", "achieved": kernels[dom]["TFLOP/s"],
+                    "peak": peak_t, "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": kernels[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
