@@ -103,6 +103,7 @@ def _load() -> ctypes.CDLL:
         "st_groupnorm_workspace_bytes": (SZ, [P, I32]),
         "st_groupnorm_workspace_layout": (I32, [P, I32, ctypes.POINTER(_GnLayout)]),
         "st_groupnorm_sharded": (I32, [P, PP, P, I32, ctypes.c_float, P, P, PP, P, SZ, P]),
+        "st_groupnorm_sharded_noalloc": (I32, [P, PP, P, I32, ctypes.c_float, P, P, PP, P]),
         "st_groupnorm_partials": (I32, [P, PP, P, I32, P, SZ, P]),
         "st_groupnorm_combine": (I32, [P, I32, ctypes.c_float, P, P, P, SZ, P]),
         "st_groupnorm_apply": (I32, [P, PP, I32, PP, P, SZ, P]),
@@ -438,6 +439,21 @@ def st_groupnorm_sharded(y_plan: Plan, y_bufs, ymax, groups: int, eps: float, ga
                                     ws_bytes, _stream(stream)), "st_groupnorm_sharded")
 
 
+def st_groupnorm_sharded_noalloc(y_plan: Plan, y_bufs, ymax, groups: int, eps: float, gamma, beta,
+                                 z_bufs, stream=None) -> None:
+    """st_groupnorm_sharded with the library's static scratch as workspace
+    (no device allocation; calls that overlap on one GPU race)."""
+    sizes = _shard_bytes(y_plan)
+    ys = _ptr_array(y_bufs, "st_groupnorm_sharded_noalloc y", sizes)
+    zs = _ptr_array(z_bufs, "st_groupnorm_sharded_noalloc z", sizes)
+    ym = _dev_ptr(ymax, "ymax", 4 * y_plan.batch * groups) if ymax is not None else 0
+    g = _dev_ptr(gamma, "gamma", 4 * y_plan.channels)
+    b = _dev_ptr(beta, "beta", 4 * y_plan.channels)
+    _check(lib.st_groupnorm_sharded_noalloc(y_plan.handle, ys, ctypes.c_void_p(ym), groups, float(eps),
+                                            ctypes.c_void_p(g), ctypes.c_void_p(b), zs, _stream(stream)),
+           "st_groupnorm_sharded_noalloc")
+
+
 def _ws(workspace):
     ws = _dev_ptr(workspace, "workspace")
     return ws, (workspace.numel() * workspace.element_size() if workspace is not None else 0)
@@ -499,7 +515,7 @@ __all__ = [
     "lib", "LIB_PATH", "ShardConvError", "Plan", "ST_F32", "ST_BF16", "st_version",
     "st_plan_shards", "st_halo_pack", "st_halo_unpack", "st_halo_exchange", "st_conv_weight_bytes", "st_conv_dgrad_weights",
     "st_conv_pack_weights", "st_conv_sharded", "st_groupnorm_workspace_bytes",
-    "st_groupnorm_workspace_layout", "st_groupnorm_sharded", "st_groupnorm_partials",
+    "st_groupnorm_workspace_layout", "st_groupnorm_sharded", "st_groupnorm_sharded_noalloc", "st_groupnorm_partials",
     "st_groupnorm_combine", "st_groupnorm_apply", "st_groupnorm_backward_workspace_bytes",
     "st_groupnorm_backward", "st_conv_wgrad_workspace_bytes", "st_conv_wgrad", "st_plan_pooled",
     "st_pool_sharded", "st_plan_strided", "st_conv_strided_sharded", "st_plan_transposed",

@@ -26,6 +26,8 @@
 //   gn_combine sum over shards; mean, var, rstd in fp64 -> fp32
 //   gn_apply   z = (y - mean_g) * (rstd_g * gamma_c) + beta_c
 #include <algorithm>
+#include <mutex>
+#include <string>
 
 #include "internal.h"
 
@@ -814,6 +816,39 @@ st_status launch_backward(GnbArgs& b, bool need_max, int mode, hipStream_t st) {
   return launch_check("st_groupnorm_backward: apply launch");
 }
 }  // namespace
+
+// Scratch of st_groupnorm_sharded_noalloc: the whole GroupNorm workspace
+// (per-shard partials, max |y|, statistics, exponents, per-channel
+// coefficients) in a static device array, so that entry point allocates
+// nothing.  Every GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = ST_GN_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoAllocScratchBytes % 256 == 0, "whole 256-byte blocks");
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64] = {};   // device address of `scratch` per device index
+
+st_status scratch_address(void** out) {
+  int dev = -1;
+  st_status s = hip_check(hipGetDevice(&dev), "st_groupnorm_sharded_noalloc: hipGetDevice");
+  if (s != ST_OK) return s;
+  if (dev < 0 || dev >= 64) return fail(ST_ERR_UNSUPPORTED, "st_groupnorm_sharded_noalloc: device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    s = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)),
+                  "st_groupnorm_sharded_noalloc: hipGetSymbolAddress(scratch)");
+    if (s != ST_OK) return s;
+    if (!p) return fail(ST_ERR_HIP, "st_groupnorm_sharded_noalloc: no device address for the scratch array");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return ST_OK;
+}
+}  // namespace
 }  // namespace st
 
 using namespace st;
@@ -902,6 +937,26 @@ st_status st_groupnorm_sharded(const st_plan* y_plan, const float* const* y_bufs
   s = st_groupnorm_combine(y_plan, groups, eps, gamma_or_null, beta_or_null, workspace, workspace_bytes, stream);
   if (s != ST_OK) return s;
   return st_groupnorm_apply(y_plan, y_bufs, groups, z_bufs, workspace, workspace_bytes, stream);
+}
+
+st_status st_groupnorm_sharded_noalloc(const st_plan* y_plan, const float* const* y_bufs,
+                                       const uint32_t* ymax_or_null, int32_t groups, float eps,
+                                       const float* gamma_or_null, const float* beta_or_null,
+                                       float* const* z_bufs, void* stream) {
+  if (!y_plan) return fail(ST_ERR_INVALID_ARG, "st_groupnorm_sharded_noalloc: NULL plan");
+  if (groups < 1 || y_plan->channels % groups)
+    return fail(ST_ERR_INVALID_ARG, "st_groupnorm_sharded_noalloc: groups must divide C");
+  // size check first: an oversized request makes no GPU call at all
+  const size_t need = layout_of(y_plan, groups).total_bytes;
+  if (need > kNoAllocScratchBytes)
+    return fail(ST_ERR_WORKSPACE, "st_groupnorm_sharded_noalloc: needs " + std::to_string(need) +
+                                      " bytes of scratch, the static scratch holds " +
+                                      std::to_string(kNoAllocScratchBytes));
+  void* ws = nullptr;
+  st_status s = scratch_address(&ws);
+  if (s != ST_OK) return s;
+  return st_groupnorm_sharded(y_plan, y_bufs, ymax_or_null, groups, eps, gamma_or_null, beta_or_null, z_bufs, ws,
+                              kNoAllocScratchBytes, stream);
 }
 
 size_t st_groupnorm_backward_workspace_bytes(const st_plan* y_plan, int32_t groups) {

@@ -424,6 +424,29 @@ st_status st_groupnorm_sharded(const st_plan* y_plan, const float* const* y_bufs
                                void* stream);
 
 /*
+ * st_groupnorm_sharded_noalloc - st_groupnorm_sharded for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments (without the
+ * workspace), semantics and output bits as st_groupnorm_sharded.  The
+ * workspace is a static device array of ST_GN_NOALLOC_SCRATCH_BYTES that each
+ * GPU the library runs on holds until the process ends; the call makes no
+ * hipMalloc, hipFree or other allocation.  The first call on a device looks
+ * up that device's scratch address once.
+ * Errors: those of st_groupnorm_sharded, and ST_ERR_WORKSPACE (returned
+ * before any GPU call) when st_groupnorm_workspace_bytes(y_plan, groups)
+ * exceeds ST_GN_NOALLOC_SCRATCH_BYTES.
+ * Every call on one GPU uses that GPU's one scratch array, which keeps the
+ * last call's contents (the partial sums are cleared at the start of each
+ * call): calls that overlap on one GPU (several streams or host threads)
+ * race, and the caller must serialise them.
+ */
+#define ST_GN_NOALLOC_SCRATCH_BYTES (1u << 20)
+st_status st_groupnorm_sharded_noalloc(const st_plan* y_plan, const float* const* y_bufs,
+                                       const uint32_t* ymax_or_null, int32_t groups, float eps,
+                                       const float* gamma_or_null, const float* beta_or_null,
+                                       float* const* z_bufs, void* stream);
+
+/*
  * The three steps of st_groupnorm_sharded as separate calls, in this order
  * on one stream (same plan, groups and workspace).  Between partials and
  * combine is where a multi-device run would all-reduce the per-shard
