@@ -12,7 +12,11 @@ forms, sharded == unsharded; the input gradient by the adjoint identity,
 brute force and torch's fp64 autograd; the weight gradient by the adjoint
 identity in the weights, brute force and torch's fp64 autograd; the GroupNorm backward by torch's
 fp64 autograd and central finite differences; pooling and the strided conv by
-brute force, torch's fp64 ops, and the sharded form).  Nothing here is "parity unpinned".
+brute force, torch's fp64 ops, and the sharded form; the transposed conv by
+the adjoint identity with the strided conv, brute force and torch's fp64
+conv_transpose; `widen` for bf16 by torch's own bfloat16 -> float64
+conversion over every finite bit pattern, and for fp32 by the exact round
+trip).
 """
 from .reference import (  # noqa: F401
     widen, zero_pad, conv_valid, conv_same, conv_same_dgrad, conv_same_wgrad, conv_same_slabbed, conv_at,

@@ -770,3 +770,67 @@ def test_pins_catch_mutants(name):
         pin_groupnorm_closed_forms(gn),
     ]
     assert not all(results), f"no pin caught the mutant '{name}'"
+
+
+# ---------------------------------------------------------------- widen
+
+
+def _bf16_patterns():
+    """Every finite bf16 bit pattern: normals, subnormals, +-0 (exponent 0xFF,
+    i.e. Inf and NaN, left out)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits >> np.uint16(7)) & np.uint16(0xFF)) != 0xFF
+    return bits[finite]
+
+
+def _pin_widen_bf16(widen_fn) -> bool:
+    """widen(bits, 'bf16') against torch's own bfloat16 -> float64 conversion
+    (an independent implementation) over every finite pattern, plus values
+    fixed by the bf16 format: 0x3F80 = 1, 0xC000 = -2, 0x0001 = 2^-133 (the
+    smallest subnormal), 0x8000 = -0.0, 0x7F7F = (2 - 2^-7) * 2^127."""
+    bits = _bf16_patterns()
+    want = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    got = widen_fn(bits, "bf16")
+    if got.dtype != np.float64 or not np.array_equal(got.view(np.uint64), want.view(np.uint64)):
+        return False
+    fixed = {0x3F80: 1.0, 0xC000: -2.0, 0x0001: 2.0 ** -133, 0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127}
+    for b, v in fixed.items():
+        if widen_fn(np.array([b], np.uint16), "bf16")[0] != v:
+            return False
+    neg0 = widen_fn(np.array([0x8000], np.uint16), "bf16")[0]
+    return neg0 == 0.0 and np.signbit(neg0)
+
+
+def test_widen_bf16_matches_torch_on_every_finite_pattern():
+    assert _pin_widen_bf16(oracle.widen)
+
+
+def test_widen_f32_is_exact():
+    """fp32 -> fp64 is exact: the value survives the round trip bit for bit,
+    subnormals and -0.0 included."""
+    r = np.random.default_rng(3)
+    a = np.concatenate([r.integers(0, 1 << 32, 100000, dtype=np.uint64).astype(np.uint32),
+                        np.array([0x80000000, 0x00000001, 0x007FFFFF], np.uint32)]).view(np.float32)
+    a = a[np.isfinite(a)]
+    w = oracle.widen(a, "f32")
+    assert w.dtype == np.float64
+    assert np.array_equal(w.astype(np.float32).view(np.uint32), a.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["byte-swapped", "shift 15", "low half", "rounded via fp16"])
+def test_widen_bf16_pin_catches_mutants(name):
+    def byte_swapped(a, dtype):
+        return (a.byteswap().astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+    def shift15(a, dtype):
+        return (a.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+
+    def low_half(a, dtype):
+        return a.astype(np.uint32).view(np.float32).astype(np.float64)
+
+    def via_fp16(a, dtype):
+        return a.view(np.float16).astype(np.float64)
+
+    mutant = {"byte-swapped": byte_swapped, "shift 15": shift15, "low half": low_half,
+              "rounded via fp16": via_fp16}[name]
+    assert not _pin_widen_bf16(mutant), f"the widen pin did not catch the mutant '{name}'"
