@@ -56,6 +56,9 @@ def parse():
                          "the same number of steps with a 1 GiB buffer written between steps (caches flushed); "
                          "reports median and min per stage")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--nested", choices=("on", "off"), default="on",
+                    help="with no --workload: also time every other workload's forward step and nest its "
+                         "figures in the headline line")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the oracle's CPU sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling the HBM byte counters)")
@@ -297,6 +300,41 @@ def main():
         return bench_strided(args, wl_fwd)
     if args.pass_ == "transposed":
         return bench_transposed(args, wl_fwd)
+    out = bench_layer(args, wl_fwd, cold=args.cold == "on", cpu=not args.no_cpu_baseline)
+    if args.pass_ == "forward" and args.workload is None and args.nested == "on":
+        # the other workloads of the layer, same step and timing, one entry each
+        nested = {wl_fwd.name: summary(out)}
+        for other in synth.WORKLOADS:
+            if other != wl_fwd.name:
+                nested[other] = summary(bench_layer(args, synth.workload(other), cold=False, cpu=False))
+        out["workloads"] = nested
+    print(json.dumps(out), flush=True)
+
+
+def progress(msg):
+    """A progress line on stderr (stdout carries only the JSON record)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def summary(rec):
+    """The per-workload figures nested in the headline line."""
+    keep = ("value", "ms_per_step", "gpu_ms_per_step", "eager_ms_per_step", "roofline", "kernels")
+    out = {k: rec[k] for k in keep if k in rec}
+    out["config"] = {k: rec["config"][k] for k in ("shape", "cout", "kernel", "shards", "groups")}
+    return out
+
+
+def bench_layer(args, wl_fwd, cold, cpu):
+    """One forward (or input-gradient) step of a workload: build its layer,
+    time its stages eagerly and the step as a replayed graph; returns the
+    record."""
+    import gc
+
+    import torch
+
+    import synth
+    from halo_sharded_conv_amd.layer import ShardedConvGN
+    progress(f"{wl_fwd.name} ({args.pass_}): generating the input")
     if args.pass_ == "dgrad":
         # input gradient of the layer's conv: dy (Cout channels) -> dx (Cin)
         from halo_sharded_conv_amd.layer import dgrad_config
@@ -309,6 +347,7 @@ def main():
         layer.set_weight(synth.make_weight(wl))
     layer.load_input(synth.make_input(wl))
     stream = torch.cuda.current_stream()
+    progress(f"{wl_fwd.name}: timing {args.warmup} + {args.steps} steps")
 
     if args.exchange == "fused":
         halo = [("halo_exchange", lambda: layer.exchange_fused())]
@@ -323,11 +362,18 @@ def main():
     eager_ms = ms_per_step
     if args.pass_ == "forward" and args.graph == "on":
         ms_per_step, gpu_ms = time_graph(args, stages)
-    cold = time_stages_cold(args, stages, stream) if args.cold == "on" and args.steps > 0 else None
+    cold_rec = time_stages_cold(args, stages, stream) if cold and args.steps > 0 else None
 
-    report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, METRIC if args.pass_ == "forward" else METRIC_DGRAD,
-           None if args.pass_ == "forward" else synth.make_weight(wl_fwd),
-           eager_ms=eager_ms if args.pass_ == "forward" and args.graph == "on" else None, cold=cold)
+    rec = report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms,
+                 METRIC if args.pass_ == "forward" else METRIC_DGRAD,
+                 None if args.pass_ == "forward" else synth.make_weight(wl_fwd),
+                 eager_ms=eager_ms if args.pass_ == "forward" and args.graph == "on" else None, cold=cold_rec,
+                 cpu=cpu)
+    del layer, stages, halo
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
 
 
 def time_stages(args, stages, stream):
@@ -433,8 +479,8 @@ def bench_backward(args, wl_fwd):
     eager_ms = ms_per_step
     if args.graph == "on":
         ms_per_step, gpu_ms = time_graph(args, stages)
-    report(args, wl, fwd, per_kernel_ms, ms_per_step, gpu_ms, METRIC_BWD, None, dgrad_layer=bwd,
-           eager_ms=eager_ms if args.graph == "on" else None)
+    print(json.dumps(report(args, wl, fwd, per_kernel_ms, ms_per_step, gpu_ms, METRIC_BWD, None, dgrad_layer=bwd,
+                            eager_ms=eager_ms if args.graph == "on" else None)), flush=True)
 
 
 def time_graph(args, stages):
@@ -504,22 +550,22 @@ def bench_strided(args, wl):
     import torch
 
     import halo_sharded_conv_amd as hsc
-    import oracle
     import synth
     from halo_sharded_conv_amd.layer import ShardedConvGN
 
     s = 2
     layer = ShardedConvGN(wl)
     layer.load_input(synth.make_input(wl))
-    w = synth.make_weight(wl)
-    wf = oracle.widen(w, wl.dtype).astype(np.float32) if wl.dtype == "bf16" else w
-    wt = torch.from_numpy(np.ascontiguousarray(np.moveaxis(wf.reshape(wl.cout, wl.cin, -1), 2, 0).swapaxes(1, 2))).cuda()
+    w = synth.make_weight(wl)                                   # raw [Cout][Cin][k..] in the operand type
+    wt = torch.from_numpy(np.ascontiguousarray(w.view(np.int16) if w.dtype == np.uint16 else w).reshape(-1)).cuda()
     q = hsc.st_plan_strided(layer.in_plan, wl.ksize, s, wl.cout)
     outs = [torch.empty(q.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(q.num_shards)]
+    ws = torch.empty(hsc.st_conv_strided_workspace_bytes(layer.in_plan, wl.cout, wl.ksize), dtype=torch.uint8,
+                     device="cuda")
     torch.cuda.synchronize()
     stages = [("halo_pack", lambda: layer.exchange_pack()), ("halo_unpack", lambda: layer.exchange_unpack()),
               ("strided", lambda: hsc.st_conv_strided_sharded(layer.in_plan, layer.x_bufs, wt, None, wl.ksize, s,
-                                                              q, outs))]
+                                                              q, outs, ws))]
     per_kernel_ms, ms_per_step, gpu_ms = time_stages(args, stages, torch.cuda.current_stream())
     eager_ms = ms_per_step
     if args.graph == "on":
@@ -547,20 +593,7 @@ def bench_strided(args, wl):
     if args.graph == "on":
         out["eager_ms_per_step"] = round(eager_ms, 4)
     if not args.no_cpu_baseline:
-        rows = args.cpu_rows or max(s, min(wl.spatial[0], int(1.0e6 // (wl.voxels // wl.spatial[0]) + 1)) // s * s)
-        sub_shape = (rows,) + tuple(wl.spatial[1:])
-        sub = synth.small_variant(wl, sub_shape, [(n,) for n in sub_shape], name_suffix="cpu_sample")
-        xsub = oracle.widen(synth.make_input(sub), wl.dtype)
-        wsub = oracle.widen(w, wl.dtype)
-        from threadpoolctl import threadpool_info
-        t0 = time.perf_counter()
-        y = oracle.conv_strided(xsub, wsub, s)
-        dt = time.perf_counter() - t0
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        out["cpu_baseline"] = {"value": sub.voxels / dt, "unit": "voxels/s", "cores": threads, "kind": "oracle",
-                               "sample": f"first {rows} rows of the outermost axis ({sub.voxels} input voxels, "
-                                         f"stride-{s} conv in fp64 numpy, {dt:.2f} s)", "seconds": round(dt, 3),
-                               "checksum": float(np.abs(y).sum())}
+        out["cpu_baseline"] = cpu_baseline_strided(args, wl, w, s)
     print(json.dumps(out), flush=True)
 
 
@@ -576,7 +609,6 @@ def bench_transposed(args, wl_out):
     import torch
 
     import halo_sharded_conv_amd as hsc
-    import oracle
     import synth
     from halo_sharded_conv_amd.layer import ShardedConvGN
 
@@ -587,16 +619,19 @@ def bench_transposed(args, wl_out):
                              shards=tuple(tuple(e // s for e in a) for a in wl_out.shards))
     layer = ShardedConvGN(wl)
     layer.load_input(synth.make_input(wl))
-    w = synth.make_weight(wl)                                   # [Cout][Cin][k..]: read as W[o = Cin side][c]
-    wf = (oracle.widen(w, wl.dtype) if wl.dtype == "bf16" else w).astype(np.float32)
-    wf = np.ascontiguousarray(np.swapaxes(wf, 0, 1))             # W [Cy = Cin][Cx = Cout][k..]
-    wt = torch.from_numpy(np.ascontiguousarray(np.moveaxis(wf.reshape(wl.cin, wl.cout, -1), 2, 0))).cuda()
+    w = synth.make_weight(wl)                                   # [Cout][Cin][k..] bits
+    # the transposed conv's weight [in = Cin][out = Cout]: the same bits with
+    # the two channel axes swapped
+    wtr = np.ascontiguousarray(np.swapaxes(w, 0, 1))
+    wt = torch.from_numpy(np.ascontiguousarray(wtr.view(np.int16) if wtr.dtype == np.uint16 else wtr).reshape(-1)).cuda()
     q = hsc.st_plan_transposed(layer.in_plan, wl.ksize, s, wl.cout)
     outs = [torch.empty(q.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(q.num_shards)]
+    ws = torch.empty(hsc.st_conv_transposed_workspace_bytes(layer.in_plan, wl.cout, wl.ksize), dtype=torch.uint8,
+                     device="cuda")
     torch.cuda.synchronize()
     stages = [("halo_pack", lambda: layer.exchange_pack()), ("halo_unpack", lambda: layer.exchange_unpack()),
               ("transposed", lambda: hsc.st_conv_transposed_sharded(layer.in_plan, layer.x_bufs, wt, None, wl.ksize,
-                                                                    s, q, outs))]
+                                                                    s, q, outs, ws))]
     per_kernel_ms, ms_per_step, gpu_ms = time_stages(args, stages, torch.cuda.current_stream())
     eager_ms = ms_per_step
     if args.graph == "on":
@@ -627,21 +662,7 @@ def bench_transposed(args, wl_out):
     if args.graph == "on":
         out["eager_ms_per_step"] = round(eager_ms, 4)
     if not args.no_cpu_baseline:
-        rows = args.cpu_rows or max(1, min(wl.spatial[0], int(0.5e6 // (wl.voxels // wl.spatial[0]) + 1)))
-        sub_shape = (rows,) + tuple(wl.spatial[1:])
-        sub = synth.small_variant(wl, sub_shape, [(n,) for n in sub_shape], name_suffix="cpu_sample")
-        ysub = oracle.widen(synth.make_input(sub), wl.dtype)
-        from threadpoolctl import threadpool_info
-        t0 = time.perf_counter()
-        x = oracle.conv_transposed(ysub, wf.astype(np.float64), s)
-        dt = time.perf_counter() - t0
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        out["cpu_baseline"] = {"value": x.shape[0] * int(np.prod(x.shape[1:-1])) / dt, "unit": "voxels/s",
-                               "cores": threads, "kind": "oracle",
-                               "sample": f"first {rows} rows of the input's outermost axis ({sub.voxels} input, "
-                                         f"{sub.voxels * s ** wl.ndim} output voxels, transposed conv in fp64 "
-                                         f"numpy, {dt:.2f} s)", "seconds": round(dt, 3),
-                               "checksum": float(np.abs(x).sum())}
+        out["cpu_baseline"] = cpu_baseline_transposed(args, wl, wtr, s)
     print(json.dumps(out), flush=True)
 
 
@@ -653,7 +674,6 @@ def bench_pool(args, wl):
     import torch
 
     import halo_sharded_conv_amd as hsc
-    import oracle
     import synth
 
     k = s = 2
@@ -701,24 +721,77 @@ def bench_pool(args, wl):
     if args.graph == "on":
         out["eager_ms_per_step"] = round(eager_ms, 4)
     if not args.no_cpu_baseline:
-        rows = args.cpu_rows or max(2, min(wl.spatial[0], int(2.0e6 // (wl.voxels // wl.spatial[0]) + 1)) // 2 * 2)
-        sub_shape = (rows,) + tuple(wl.spatial[1:])
-        sub = synth.small_variant(wl, sub_shape, [(n,) for n in sub_shape], name_suffix="cpu_sample")
-        xsub = oracle.widen(synth.make_input(sub), wl.dtype)
-        from threadpoolctl import threadpool_info
-        t0 = time.perf_counter()
-        y = oracle.pool_valid(xsub, k, s, "avg")
-        dt = time.perf_counter() - t0
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        out["cpu_baseline"] = {"value": sub.voxels / dt, "unit": "voxels/s", "cores": threads, "kind": "oracle",
-                               "sample": f"first {rows} rows of the outermost axis ({sub.voxels} voxels, 'valid' "
-                                         f"average pooling in fp64 numpy, {dt:.2f} s)", "seconds": round(dt, 3),
-                               "checksum": float(np.abs(y).sum())}
+        out["cpu_baseline"] = cpu_baseline_pool(args, wl, k, s)
     print(json.dumps(out), flush=True)
 
 
+
+def _threads():
+    from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+
+
+def cpu_baseline_strided(args, wl, w, s):
+    """The oracle's stride-s conv on the first rows of the input."""
+    import numpy as np
+
+    import oracle
+    import synth
+    rows = args.cpu_rows or max(s, min(wl.spatial[0], int(1.0e6 // (wl.voxels // wl.spatial[0]) + 1)) // s * s)
+    sub_shape = (rows,) + tuple(wl.spatial[1:])
+    sub = synth.small_variant(wl, sub_shape, [(n,) for n in sub_shape], name_suffix="cpu_sample")
+    xsub = oracle.widen(synth.make_input(sub), wl.dtype)
+    wsub = oracle.widen(w, wl.dtype)
+    t0 = time.perf_counter()
+    y = oracle.conv_strided(xsub, wsub, s)
+    dt = time.perf_counter() - t0
+    return {"value": sub.voxels / dt, "unit": "voxels/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"first {rows} rows of the outermost axis ({sub.voxels} input voxels, "
+                      f"stride-{s} conv in fp64 numpy, {dt:.2f} s)", "seconds": round(dt, 3),
+            "checksum": float(np.abs(y).sum())}
+
+
+def cpu_baseline_transposed(args, wl, wtr, s):
+    """The oracle's stride-s transposed conv on the first rows of the input."""
+    import numpy as np
+
+    import oracle
+    import synth
+    rows = args.cpu_rows or max(1, min(wl.spatial[0], int(0.5e6 // (wl.voxels // wl.spatial[0]) + 1)))
+    sub_shape = (rows,) + tuple(wl.spatial[1:])
+    sub = synth.small_variant(wl, sub_shape, [(n,) for n in sub_shape], name_suffix="cpu_sample")
+    ysub = oracle.widen(synth.make_input(sub), wl.dtype)
+    wtr64 = oracle.widen(wtr, wl.dtype)
+    t0 = time.perf_counter()
+    x = oracle.conv_transposed(ysub, wtr64, s)
+    dt = time.perf_counter() - t0
+    return {"value": x.shape[0] * int(np.prod(x.shape[1:-1])) / dt, "unit": "voxels/s", "cores": _threads(),
+            "kind": "oracle",
+            "sample": f"first {rows} rows of the input's outermost axis ({sub.voxels} input, "
+                      f"{sub.voxels * s ** wl.ndim} output voxels, transposed conv in fp64 numpy, {dt:.2f} s)",
+            "seconds": round(dt, 3), "checksum": float(np.abs(x).sum())}
+
+
+def cpu_baseline_pool(args, wl, k, s):
+    """The oracle's 'valid' average pooling on the first rows of the input."""
+    import numpy as np
+
+    import oracle
+    import synth
+    rows = args.cpu_rows or max(2, min(wl.spatial[0], int(2.0e6 // (wl.voxels // wl.spatial[0]) + 1)) // 2 * 2)
+    sub_shape = (rows,) + tuple(wl.spatial[1:])
+    sub = synth.small_variant(wl, sub_shape, [(n,) for n in sub_shape], name_suffix="cpu_sample")
+    xsub = oracle.widen(synth.make_input(sub), wl.dtype)
+    t0 = time.perf_counter()
+    y = oracle.pool_valid(xsub, k, s, "avg")
+    dt = time.perf_counter() - t0
+    return {"value": sub.voxels / dt, "unit": "voxels/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"first {rows} rows of the outermost axis ({sub.voxels} voxels, 'valid' "
+                      f"average pooling in fp64 numpy, {dt:.2f} s)", "seconds": round(dt, 3),
+            "checksum": float(np.abs(y).sum())}
+
 def report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, metric, w_fwd, dgrad_layer=None, eager_ms=None,
-           cold=None):
+           cold=None, cpu=True):
     """One JSON line: throughput, per-stage rates and the longest stage against its roofline."""
     alg = algorithmic(wl, layer)
     if dgrad_layer is not None:
@@ -780,10 +853,19 @@ def report(args, wl, layer, per_kernel_ms, ms_per_step, gpu_ms, metric, w_fwd, d
         out["eager_ms_per_step"] = round(eager_ms, 4)
     if cold is not None:
         out["cold_eager"] = cold
-    if not args.no_cpu_baseline:
-        rows = args.cpu_rows or max(1, min(wl.spatial[0], int(5.0e5 // (wl.voxels // wl.spatial[0]) + 1)))
-        out["cpu_baseline"] = cpu_baseline(wl, rows, w_fwd, backward=args.pass_ == "backward")
-    print(json.dumps(out), flush=True)
+    if cpu and not args.no_cpu_baseline:
+        progress(f"{wl.name}: oracle CPU baseline on {cpu_rows(args, wl)} rows")
+        out["cpu_baseline"] = cpu_baseline(wl, cpu_rows(args, wl), w_fwd, backward=args.pass_ == "backward")
+    return out
+
+
+def cpu_rows(args, wl):
+    """Rows of the outermost axis in the oracle's CPU sample: about 300 GFLOP
+    of fp64 conv (~10-30 s on the host), at least one row."""
+    if args.cpu_rows:
+        return args.cpu_rows
+    per_row = wl.conv_flops // wl.spatial[0]
+    return max(1, min(wl.spatial[0], int(300e9 // per_row)))
 
 
 if __name__ == "__main__":

@@ -91,13 +91,17 @@ def _load() -> ctypes.CDLL:
         "st_conv_weight_bytes": (SZ, [I32, I32, I32, I32, I32]),
         "st_conv_pack_weights": (I32, [I32, I32, I32, I32, I32, P, P, P]),
         "st_conv_dgrad_weights": (I32, [I32, I32, I32, I32, I32, P, P, P]),
-        "st_conv_sharded": (I32, [P, PP, P, P, I32, I32, P, PP, P, I32, P]),
+        "st_conv_workspace_bytes": (SZ, [P, I32, I32]),
+        "st_conv_sharded": (I32, [P, PP, P, P, I32, I32, PP, P, I32, P, SZ, P]),
+        "st_conv_sharded_packed": (I32, [P, PP, P, P, I32, I32, PP, P, I32, P]),
         "st_plan_pooled": (I32, [P, I32, I32, ctypes.POINTER(I32), I32, ctypes.POINTER(P)]),
         "st_pool_sharded": (I32, [P, PP, I32, I32, I32, P, PP, P]),
         "st_plan_strided": (I32, [P, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(P)]),
-        "st_conv_strided_sharded": (I32, [P, PP, P, P, I32, I32, P, PP, P]),
+        "st_conv_strided_workspace_bytes": (SZ, [P, I32, I32]),
+        "st_conv_strided_sharded": (I32, [P, PP, P, P, I32, I32, P, PP, P, SZ, P]),
         "st_plan_transposed": (I32, [P, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(P)]),
-        "st_conv_transposed_sharded": (I32, [P, PP, P, P, I32, I32, P, PP, P]),
+        "st_conv_transposed_workspace_bytes": (SZ, [P, I32, I32]),
+        "st_conv_transposed_sharded": (I32, [P, PP, P, P, I32, I32, P, PP, P, SZ, P]),
         "st_conv_wgrad_workspace_bytes": (SZ, [P, I32, I32]),
         "st_conv_wgrad": (I32, [P, PP, P, PP, I32, P, P, SZ, P]),
         "st_groupnorm_workspace_bytes": (SZ, [P, I32]),
@@ -297,17 +301,49 @@ def st_conv_dgrad_weights(ndim: int, cin: int, cout: int, ksize: int, dtype, wei
                                      _stream(stream)), "st_conv_dgrad_weights")
 
 
-def st_conv_sharded(in_plan: Plan, in_bufs, packed_weight, bias, cout: int, ksize: int,
-                    out_plan: Plan, y_bufs, ymax=None, groups: int = 1, stream=None) -> None:
+def _y_bytes(in_plan: Plan, cout: int) -> List[int]:
+    """Bytes of each shard's unpadded fp32 conv output [N][extent...][cout]."""
+    out = []
+    for i in range(in_plan.num_shards):
+        n = in_plan.batch * cout * 4
+        for e in in_plan.shard_info(i)["extent"]:
+            n *= e
+        out.append(n)
+    return out
+
+
+def st_conv_workspace_bytes(in_plan: Plan, cout: int, ksize: int) -> int:
+    return int(lib.st_conv_workspace_bytes(in_plan.handle, cout, ksize))
+
+
+def st_conv_sharded(in_plan: Plan, in_bufs, weight, bias, cout: int, ksize: int, y_bufs, ymax=None,
+                    groups: int = 1, workspace=None, stream=None) -> None:
+    """weight: raw [Cout][Cin][k..] in the plan's dtype (bf16 as int16/uint16
+    bits); workspace: >= st_conv_workspace_bytes bytes."""
     ins = _ptr_array(in_bufs, "st_conv_sharded input", _shard_bytes(in_plan))
-    outs = _ptr_array(y_bufs, "st_conv_sharded y", _shard_bytes(out_plan))
+    outs = _ptr_array(y_bufs, "st_conv_sharded y", _y_bytes(in_plan, cout))
+    raw = cout * in_plan.channels * ksize ** in_plan.ndim * ESIZE[in_plan.dtype]
+    w = _dev_ptr(weight, "weight", raw)
+    b = _dev_ptr(bias, "bias", 4 * cout)
+    ym = _dev_ptr(ymax, "ymax", 4 * in_plan.batch * groups) if ymax is not None else 0
+    ws, nb = _ws(workspace)
+    _check(lib.st_conv_sharded(in_plan.handle, ins, ctypes.c_void_p(w), ctypes.c_void_p(b), cout, ksize, outs,
+                               ctypes.c_void_p(ym), groups, ctypes.c_void_p(ws), nb, _stream(stream)),
+           "st_conv_sharded")
+
+
+def st_conv_sharded_packed(in_plan: Plan, in_bufs, packed_weight, bias, cout: int, ksize: int, y_bufs, ymax=None,
+                           groups: int = 1, stream=None) -> None:
+    """packed_weight: from st_conv_pack_weights."""
+    ins = _ptr_array(in_bufs, "st_conv_sharded_packed input", _shard_bytes(in_plan))
+    outs = _ptr_array(y_bufs, "st_conv_sharded_packed y", _y_bytes(in_plan, cout))
     need_w = st_conv_weight_bytes(in_plan.ndim, in_plan.channels, cout, ksize, in_plan.dtype)
     w = _dev_ptr(packed_weight, "packed weight", need_w)
     b = _dev_ptr(bias, "bias", 4 * cout)
     ym = _dev_ptr(ymax, "ymax", 4 * in_plan.batch * groups) if ymax is not None else 0
-    _check(lib.st_conv_sharded(in_plan.handle, ins, ctypes.c_void_p(w), ctypes.c_void_p(b), cout, ksize,
-                               out_plan.handle, outs, ctypes.c_void_p(ym), groups, _stream(stream)),
-           "st_conv_sharded")
+    _check(lib.st_conv_sharded_packed(in_plan.handle, ins, ctypes.c_void_p(w), ctypes.c_void_p(b), cout, ksize,
+                                      outs, ctypes.c_void_p(ym), groups, _stream(stream)),
+           "st_conv_sharded_packed")
 
 
 def st_plan_pooled(in_plan: Plan, ksize: int, stride: int, out_halo=None, out_dtype=None) -> Plan:
@@ -364,16 +400,22 @@ def st_plan_strided(in_plan: Plan, ksize: int, stride: int, cout: int, out_halo=
                              tuple(out_halo) if out_halo is not None else (0,) * in_plan.ndim)
 
 
-def st_conv_strided_sharded(in_plan: Plan, in_bufs, weight_tco, bias, ksize: int, stride: int, out_plan: Plan,
-                            out_bufs, stream=None) -> None:
-    """weight_tco: fp32 device tensor [taps][Cin][Cout]."""
+def st_conv_strided_workspace_bytes(in_plan: Plan, cout: int, ksize: int) -> int:
+    return int(lib.st_conv_strided_workspace_bytes(in_plan.handle, cout, ksize))
+
+
+def st_conv_strided_sharded(in_plan: Plan, in_bufs, weight, bias, ksize: int, stride: int, out_plan: Plan,
+                            out_bufs, workspace, stream=None) -> None:
+    """weight: raw [Cout][Cin][k..] in the input plan's dtype."""
     ins = _ptr_array(in_bufs, "st_conv_strided_sharded input", _shard_bytes(in_plan))
     outs = _ptr_array(out_bufs, "st_conv_strided_sharded output", _shard_bytes(out_plan))
     taps = ksize ** in_plan.ndim
-    w = _dev_ptr(weight_tco, "weight_tco", 4 * taps * in_plan.channels * out_plan.channels)
+    w = _dev_ptr(weight, "weight", ESIZE[in_plan.dtype] * taps * in_plan.channels * out_plan.channels)
     b = _dev_ptr(bias, "bias", 4 * out_plan.channels)
+    ws, nb = _ws(workspace)
     _check(lib.st_conv_strided_sharded(in_plan.handle, ins, ctypes.c_void_p(w), ctypes.c_void_p(b), ksize, stride,
-                                       out_plan.handle, outs, _stream(stream)), "st_conv_strided_sharded")
+                                       out_plan.handle, outs, ctypes.c_void_p(ws), nb, _stream(stream)),
+           "st_conv_strided_sharded")
 
 
 def st_plan_transposed(in_plan: Plan, ksize: int, stride: int, cout: int, out_halo=None) -> Plan:
@@ -385,16 +427,21 @@ def st_plan_transposed(in_plan: Plan, ksize: int, stride: int, cout: int, out_ha
                              tuple(out_halo) if out_halo is not None else (0,) * in_plan.ndim)
 
 
-def st_conv_transposed_sharded(in_plan: Plan, in_bufs, weight_tio, bias, ksize: int, stride: int, out_plan: Plan,
-                               out_bufs, stream=None) -> None:
-    """weight_tio: fp32 device tensor [taps][Cin][Cout], Cin = in_plan.channels."""
+def st_conv_transposed_workspace_bytes(in_plan: Plan, cout: int, ksize: int) -> int:
+    return int(lib.st_conv_transposed_workspace_bytes(in_plan.handle, cout, ksize))
+
+
+def st_conv_transposed_sharded(in_plan: Plan, in_bufs, weight, bias, ksize: int, stride: int, out_plan: Plan,
+                               out_bufs, workspace, stream=None) -> None:
+    """weight: raw [Cin][Cout][k..] (Cin = in_plan.channels) in the input plan's dtype."""
     ins = _ptr_array(in_bufs, "st_conv_transposed_sharded input", _shard_bytes(in_plan))
     outs = _ptr_array(out_bufs, "st_conv_transposed_sharded output", _shard_bytes(out_plan))
     taps = ksize ** in_plan.ndim
-    w = _dev_ptr(weight_tio, "weight_tio", 4 * taps * in_plan.channels * out_plan.channels)
+    w = _dev_ptr(weight, "weight", ESIZE[in_plan.dtype] * taps * in_plan.channels * out_plan.channels)
     b = _dev_ptr(bias, "bias", 4 * out_plan.channels)
+    ws, nb = _ws(workspace)
     _check(lib.st_conv_transposed_sharded(in_plan.handle, ins, ctypes.c_void_p(w), ctypes.c_void_p(b), ksize,
-                                          stride, out_plan.handle, outs, _stream(stream)),
+                                          stride, out_plan.handle, outs, ctypes.c_void_p(ws), nb, _stream(stream)),
            "st_conv_transposed_sharded")
 
 
@@ -514,7 +561,8 @@ def st_groupnorm_backward(y_plan: Plan, y_bufs, dz_bufs, ymax, dzmax, groups: in
 __all__ = [
     "lib", "LIB_PATH", "ShardConvError", "Plan", "ST_F32", "ST_BF16", "st_version",
     "st_plan_shards", "st_halo_pack", "st_halo_unpack", "st_halo_exchange", "st_conv_weight_bytes", "st_conv_dgrad_weights",
-    "st_conv_pack_weights", "st_conv_sharded", "st_groupnorm_workspace_bytes",
+    "st_conv_pack_weights", "st_conv_workspace_bytes", "st_conv_sharded", "st_conv_sharded_packed",
+    "st_groupnorm_workspace_bytes", "st_conv_strided_workspace_bytes", "st_conv_transposed_workspace_bytes",
     "st_groupnorm_workspace_layout", "st_groupnorm_sharded", "st_groupnorm_sharded_noalloc", "st_groupnorm_partials",
     "st_groupnorm_combine", "st_groupnorm_apply", "st_groupnorm_backward_workspace_bytes",
     "st_groupnorm_backward", "st_conv_wgrad_workspace_bytes", "st_conv_wgrad", "st_plan_pooled",

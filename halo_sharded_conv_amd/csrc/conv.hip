@@ -61,6 +61,7 @@ struct ConvArgs {
   uint32_t* ymax;             // or null
   ConvShardArg sh[ST_MAX_SHARDS];
 };
+static_assert(sizeof(ConvArgs) <= kMaxKernargBytes, "kernel argument struct too large");
 
 __global__ void fill_u32(uint32_t* __restrict__ p, uint32_t v, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -88,6 +89,7 @@ struct DirectArgs {
   uint32_t* ymax;
   DirectShardArg sh[ST_MAX_SHARDS];
 };
+static_assert(sizeof(DirectArgs) <= kMaxKernargBytes, "kernel argument struct too large");
 
 __device__ __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
 __device__ __forceinline__ float ld(const uint16_t* p, size_t i) {
@@ -191,9 +193,12 @@ __global__ __launch_bounds__(256) void conv_direct(const DirectArgs a) {
 // --------------------------------------------------------------------------
 
 // [Cout][Cin][taps] -> [Cin/CK][Cout][KVP], k index = tap*CK + (cin % CK)
+// Every packing kernel also zeroes clr[0, nclr) (the max |y| accumulator of
+// the conv that follows), so packing and that clear take one launch.
 __global__ void pack_w_mfma(const uint16_t* __restrict__ w, uint16_t* __restrict__ out, int cin,
-                            int cout, int taps, int ck, int kvp, int64_t total) {
+                            int cout, int taps, int ck, int kvp, int64_t total, uint32_t* clr, int nclr) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nclr) clr[i] = 0u;
   if (i >= total) return;
   const int vk = (int)(i % kvp);
   const int64_t r = i / kvp;
@@ -210,8 +215,9 @@ __global__ void pack_w_mfma(const uint16_t* __restrict__ w, uint16_t* __restrict
 // [Cout][Cin][taps] -> [Cout/bn][Cin/ck][taps][bn][ck]: each (cout block, K chunk)
 // slab is contiguous and already in the order its LDS stage holds it
 __global__ void pack_w_gemm(const uint16_t* __restrict__ w, uint16_t* __restrict__ out, int cin, int cout,
-                            int taps, int ck, int bn, int64_t total) {
+                            int taps, int ck, int bn, int64_t total, uint32_t* clr, int nclr) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nclr) clr[i] = 0u;
   if (i >= total) return;
   const int c = (int)(i % ck);
   int64_t r = i / ck;
@@ -227,8 +233,9 @@ __global__ void pack_w_gemm(const uint16_t* __restrict__ w, uint16_t* __restrict
 // [Cout][Cin][kd][kh][kw] -> [kh][kd][kw][Cout][Cin]: the weights of one kernel
 // row dy are contiguous
 __global__ void pack_w_pairs(const uint16_t* __restrict__ w, uint16_t* __restrict__ out, int cin, int cout,
-                             int ks, int64_t total) {
+                             int ks, int64_t total, uint32_t* clr, int nclr) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nclr) clr[i] = 0u;
   if (i >= total) return;
   const int c = (int)(i % cin);
   int64_t r = i / cin;
@@ -258,8 +265,9 @@ __global__ void dgrad_weights(const T* __restrict__ w, T* __restrict__ out, int 
 
 template <typename T>
 __global__ void pack_w_direct(const T* __restrict__ w, T* __restrict__ out, int cin, int cout,
-                              int taps, int64_t total) {
+                              int taps, int64_t total, uint32_t* clr, int nclr) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nclr) clr[i] = 0u;
   if (i >= total) return;
   const int c = (int)(i % cin);
   const int t = (int)((i / cin) % taps);
@@ -1752,140 +1760,76 @@ const Instance* find_instance(int ndim, int cin, int cout, int ks) {
 
 int64_t taps_of(int ndim, int ks) { return ndim == 3 ? (int64_t)ks * ks * ks : (int64_t)ks * ks; }
 
-}  // namespace
-}  // namespace st
-
-using namespace st;
-
-extern "C" {
-
-size_t st_conv_weight_bytes(int32_t ndim, int32_t cin, int32_t cout, int32_t ksize, st_dtype dtype) {
-  if ((ndim != 2 && ndim != 3) || cin < 1 || cout < 1 || ksize < 1 || ksize % 2 == 0) return 0;
-  if (dtype != ST_F32 && dtype != ST_BF16) return 0;
-  const int64_t taps = taps_of(ndim, ksize);
-  if (dtype == ST_BF16) {
-    if (const Instance* i = find_instance(ndim, cin, cout, ksize))
-      return (size_t)(cin / i->ck) * cout * i->kvp * 2;
-    return (size_t)cout * taps * cin * 2;
-  }
-  return (size_t)cout * taps * cin * 4;
-}
-
-st_status st_conv_pack_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t ksize,
-                               st_dtype dtype, const void* weight, void* packed, void* stream) {
-  const size_t bytes = st_conv_weight_bytes(ndim, cin, cout, ksize, dtype);
-  if (bytes == 0) return fail(ST_ERR_UNSUPPORTED, "st_conv_pack_weights: unsupported ndim/ksize/dtype");
-  if (!weight || !packed) return fail(ST_ERR_INVALID_ARG, "st_conv_pack_weights: NULL pointer");
-  if (!aligned16(weight) || !aligned16(packed))
-    return fail(ST_ERR_ALIGNMENT, "st_conv_pack_weights: pointers must be 16-byte aligned");
-  hipStream_t st = static_cast<hipStream_t>(stream);
+// Packs raw [Cout][Cin][k^d] weights into the layout of the kernel that runs
+// this shape and zeroes clr[0, nclr) in the same launch.
+st_status pack_weights(int ndim, int cin, int cout, int ksize, st_dtype dtype, const void* weight, void* packed,
+                       uint32_t* clr, int nclr, hipStream_t st, const char* who) {
   const int taps = (int)taps_of(ndim, ksize);
+  const std::string what = std::string(who) + ": weight packing launch";
+  auto grid = [&](int64_t total) { return dim3((unsigned)((std::max<int64_t>(total, nclr) + 255) / 256)); };
   if (dtype == ST_BF16) {
+    const uint16_t* w = static_cast<const uint16_t*>(weight);
+    uint16_t* out = static_cast<uint16_t*>(packed);
     if (const Instance* i = find_instance(ndim, cin, cout, ksize)) {
       if (i->kind == 2) {
         const int64_t total = (int64_t)cout * taps * cin;
-        hipLaunchKernelGGL(pack_w_pairs, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                           static_cast<const uint16_t*>(weight), static_cast<uint16_t*>(packed), cin, cout,
-                           ksize, total);
-        return launch_check("st_conv_pack_weights: launch");
+        hipLaunchKernelGGL(pack_w_pairs, grid(total), dim3(256), 0, st, w, out, cin, cout, ksize, total, clr, nclr);
+        return launch_check(what.c_str());
       }
       if (i->kind == 1) {
         const int64_t total = (int64_t)cout * taps * cin;
-        hipLaunchKernelGGL(pack_w_gemm, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                           static_cast<const uint16_t*>(weight), static_cast<uint16_t*>(packed), cin, cout,
-                           taps, i->ck, i->bn, total);
-        return launch_check("st_conv_pack_weights: launch");
+        hipLaunchKernelGGL(pack_w_gemm, grid(total), dim3(256), 0, st, w, out, cin, cout, taps, i->ck, i->bn, total,
+                           clr, nclr);
+        return launch_check(what.c_str());
       }
       const int64_t total = (int64_t)(cin / i->ck) * cout * i->kvp;
-      hipLaunchKernelGGL(pack_w_mfma, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                         static_cast<const uint16_t*>(weight), static_cast<uint16_t*>(packed), cin, cout,
-                         taps, i->ck, i->kvp, total);
-      return launch_check("st_conv_pack_weights: launch");
+      hipLaunchKernelGGL(pack_w_mfma, grid(total), dim3(256), 0, st, w, out, cin, cout, taps, i->ck, i->kvp, total,
+                         clr, nclr);
+      return launch_check(what.c_str());
     }
     const int64_t total = (int64_t)cout * taps * cin;
-    hipLaunchKernelGGL(pack_w_direct<uint16_t>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(weight), static_cast<uint16_t*>(packed), cin, cout, taps,
-                       total);
-    return launch_check("st_conv_pack_weights: launch");
+    hipLaunchKernelGGL(pack_w_direct<uint16_t>, grid(total), dim3(256), 0, st, w, out, cin, cout, taps, total, clr,
+                       nclr);
+    return launch_check(what.c_str());
   }
   const int64_t total = (int64_t)cout * taps * cin;
-  hipLaunchKernelGGL(pack_w_direct<float>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                     static_cast<const float*>(weight), static_cast<float*>(packed), cin, cout, taps, total);
-  return launch_check("st_conv_pack_weights: launch");
+  hipLaunchKernelGGL(pack_w_direct<float>, grid(total), dim3(256), 0, st, static_cast<const float*>(weight),
+                     static_cast<float*>(packed), cin, cout, taps, total, clr, nclr);
+  return launch_check(what.c_str());
 }
 
-st_status st_conv_dgrad_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t ksize, st_dtype dtype,
-                                const void* weight, void* out, void* stream) {
-  if ((ndim != 2 && ndim != 3) || cin < 1 || cout < 1 || ksize < 1 || ksize % 2 == 0)
-    return fail(ST_ERR_UNSUPPORTED, "st_conv_dgrad_weights: unsupported ndim/ksize");
-  if (dtype != ST_F32 && dtype != ST_BF16) return fail(ST_ERR_UNSUPPORTED, "st_conv_dgrad_weights: dtype");
-  if (!weight || !out) return fail(ST_ERR_INVALID_ARG, "st_conv_dgrad_weights: NULL pointer");
-  if (weight == out) return fail(ST_ERR_INVALID_ARG, "st_conv_dgrad_weights: in place is not supported");
-  const int taps = (int)taps_of(ndim, ksize);
-  const int64_t total = (int64_t)cout * cin * taps;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 gd((unsigned)((total + 255) / 256)), bd(256);
-  if (dtype == ST_BF16)
-    hipLaunchKernelGGL(dgrad_weights<uint16_t>, gd, bd, 0, st, static_cast<const uint16_t*>(weight),
-                       static_cast<uint16_t*>(out), cin, cout, taps, total);
-  else
-    hipLaunchKernelGGL(dgrad_weights<float>, gd, bd, 0, st, static_cast<const float*>(weight),
-                       static_cast<float*>(out), cin, cout, taps, total);
-  return launch_check("st_conv_dgrad_weights: launch");
-}
-
-st_status st_conv_sharded(const st_plan* in_plan, const void* const* in_bufs,
-                          const void* packed_weight, const float* bias_or_null,
-                          int32_t cout, int32_t ksize, const st_plan* out_plan,
-                          float* const* y_bufs, uint32_t* ymax_or_null, int32_t groups,
-                          void* stream) {
-  if (!in_plan || !out_plan || !in_bufs || !y_bufs || !packed_weight)
-    return fail(ST_ERR_INVALID_ARG, "st_conv_sharded: NULL argument");
-  if (ksize < 1 || ksize % 2 == 0) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: kernel size must be odd");
-  if (cout < 1) return fail(ST_ERR_INVALID_ARG, "st_conv_sharded: cout < 1");
+// Host checks shared by the conv entry points; nothing is enqueued.
+st_status conv_check(const char* who, const st_plan* in_plan, const void* const* in_bufs, const void* weight,
+                     const float* bias, int32_t cout, int32_t ksize, float* const* y_bufs, const uint32_t* ymax,
+                     int32_t groups) {
+  auto err = [&](st_status s, const char* m) { return fail(s, std::string(who) + ": " + m); };
+  if (!in_plan || !in_bufs || !y_bufs || !weight) return err(ST_ERR_INVALID_ARG, "NULL argument");
+  if (ksize < 1 || ksize % 2 == 0) return err(ST_ERR_UNSUPPORTED, "kernel size must be odd");
+  if (cout < 1) return err(ST_ERR_INVALID_ARG, "cout < 1");
   const int ndim = in_plan->ndim;
-  // geometry checks: same shards, halo wide enough, output plan fp32 halo 0
-  if (out_plan->ndim != ndim || out_plan->batch != in_plan->batch ||
-      out_plan->shards.size() != in_plan->shards.size())
-    return fail(ST_ERR_BAD_SHAPE, "st_conv_sharded: output plan does not match the input plan");
-  if (out_plan->dtype != ST_F32 || out_plan->channels != cout)
-    return fail(ST_ERR_BAD_SHAPE, "st_conv_sharded: output plan must be fp32 with C = cout");
-  for (int a = 0; a < kAxes; ++a) {
-    if (out_plan->halo[a] != 0) return fail(ST_ERR_BAD_SHAPE, "st_conv_sharded: output plan must have halo 0");
-    if (out_plan->sizes[a] != in_plan->sizes[a])
-      return fail(ST_ERR_BAD_SHAPE, "st_conv_sharded: output shard sizes differ from the input's");
-    const bool real = a >= kAxes - ndim;
-    if (real && in_plan->halo[a] < ksize / 2)
-      return fail(ST_ERR_BAD_SHAPE, "st_conv_sharded: input halo narrower than ksize/2");
-  }
-  if (ymax_or_null) {
-    if (groups < 1 || cout % groups != 0)
-      return fail(ST_ERR_INVALID_ARG, "st_conv_sharded: groups must divide cout");
-  }
-  if (!aligned16(packed_weight) || (bias_or_null && !aligned16(bias_or_null)) ||
-      (ymax_or_null && (reinterpret_cast<uintptr_t>(ymax_or_null) & 3)))
-    return fail(ST_ERR_ALIGNMENT, "st_conv_sharded: misaligned weight/bias/ymax");
+  for (int a = kAxes - ndim; a < kAxes; ++a)
+    if (in_plan->halo[a] < ksize / 2) return err(ST_ERR_BAD_SHAPE, "input halo narrower than ksize/2");
+  if (ymax && (groups < 1 || cout % groups != 0)) return err(ST_ERR_INVALID_ARG, "groups must divide cout");
+  if (!aligned16(weight) || (bias && !aligned16(bias)) || (ymax && (reinterpret_cast<uintptr_t>(ymax) & 3)))
+    return err(ST_ERR_ALIGNMENT, "misaligned weight/bias/ymax");
   for (size_t s = 0; s < in_plan->shards.size(); ++s) {
-    if (!in_bufs[s] || !y_bufs[s]) return fail(ST_ERR_INVALID_ARG, "st_conv_sharded: NULL shard buffer");
+    if (!in_bufs[s] || !y_bufs[s]) return err(ST_ERR_INVALID_ARG, "NULL shard buffer");
     if (!aligned16(in_bufs[s]) || !aligned16(y_bufs[s]))
-      return fail(ST_ERR_ALIGNMENT, "st_conv_sharded: shard buffers must be 16-byte aligned");
-  }
-  for (size_t s = 0; s < in_plan->shards.size(); ++s)
+      return err(ST_ERR_ALIGNMENT, "shard buffers must be 16-byte aligned");
     for (int a = 0; a < kAxes; ++a)
-      if (in_plan->shards[s].pad[a] > INT32_MAX / 2)
-        return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: extent too large");
-
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int cin = (int)in_plan->channels;
-  if (ymax_or_null) {
-    const int n = (int)(in_plan->batch * groups);
-    hipLaunchKernelGGL(fill_u32, dim3((n + 255) / 256), dim3(256), 0, st, ymax_or_null, 0u, n);
-    st_status s = launch_check("st_conv_sharded: ymax clear");
-    if (s != ST_OK) return s;
+      if (in_plan->shards[s].pad[a] > INT32_MAX / 2) return err(ST_ERR_UNSUPPORTED, "extent too large");
   }
+  return ST_OK;
+}
 
-  const Instance* inst =
-      in_plan->dtype == ST_BF16 ? find_instance(ndim, cin, cout, ksize) : nullptr;
+// Launches the conv of every shard from packed weights (arguments checked).
+// y of shard s: unpadded channels-last fp32 [N][ext...][cout].
+st_status conv_run(const st_plan* in_plan, const void* const* in_bufs, const void* packed_weight,
+                   const float* bias_or_null, int32_t cout, int32_t ksize, float* const* y_bufs,
+                   uint32_t* ymax_or_null, int32_t groups, hipStream_t st) {
+  const int ndim = in_plan->ndim;
+  const int cin = (int)in_plan->channels;
+  const Instance* inst = in_plan->dtype == ST_BF16 ? find_instance(ndim, cin, cout, ksize) : nullptr;
   if (inst) {
     ConvArgs a{};
     a.nshards = (int)in_plan->shards.size();
@@ -1949,6 +1893,100 @@ st_status st_conv_sharded(const st_plan* in_plan, const void* const* in_bufs,
   else
     hipLaunchKernelGGL(conv_direct<uint16_t>, dim3((unsigned)blocks), dim3(256), shmem, st, a);
   return launch_check("st_conv_sharded: conv_direct launch");
+}
+
+}  // namespace
+}  // namespace st
+
+using namespace st;
+
+extern "C" {
+
+size_t st_conv_weight_bytes(int32_t ndim, int32_t cin, int32_t cout, int32_t ksize, st_dtype dtype) {
+  if ((ndim != 2 && ndim != 3) || cin < 1 || cout < 1 || ksize < 1 || ksize % 2 == 0) return 0;
+  if (dtype != ST_F32 && dtype != ST_BF16) return 0;
+  const int64_t taps = taps_of(ndim, ksize);
+  if (dtype == ST_BF16) {
+    if (const Instance* i = find_instance(ndim, cin, cout, ksize))
+      return (size_t)(cin / i->ck) * cout * i->kvp * 2;
+    return (size_t)cout * taps * cin * 2;
+  }
+  return (size_t)cout * taps * cin * 4;
+}
+
+st_status st_conv_pack_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t ksize,
+                               st_dtype dtype, const void* weight, void* packed, void* stream) {
+  const size_t bytes = st_conv_weight_bytes(ndim, cin, cout, ksize, dtype);
+  if (bytes == 0) return fail(ST_ERR_UNSUPPORTED, "st_conv_pack_weights: unsupported ndim/ksize/dtype");
+  if (!weight || !packed) return fail(ST_ERR_INVALID_ARG, "st_conv_pack_weights: NULL pointer");
+  if (!aligned16(weight) || !aligned16(packed))
+    return fail(ST_ERR_ALIGNMENT, "st_conv_pack_weights: pointers must be 16-byte aligned");
+  return pack_weights(ndim, cin, cout, ksize, dtype, weight, packed, nullptr, 0, static_cast<hipStream_t>(stream),
+                      "st_conv_pack_weights");
+}
+
+st_status st_conv_dgrad_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t ksize, st_dtype dtype,
+                                const void* weight, void* out, void* stream) {
+  if ((ndim != 2 && ndim != 3) || cin < 1 || cout < 1 || ksize < 1 || ksize % 2 == 0)
+    return fail(ST_ERR_UNSUPPORTED, "st_conv_dgrad_weights: unsupported ndim/ksize");
+  if (dtype != ST_F32 && dtype != ST_BF16) return fail(ST_ERR_UNSUPPORTED, "st_conv_dgrad_weights: dtype");
+  if (!weight || !out) return fail(ST_ERR_INVALID_ARG, "st_conv_dgrad_weights: NULL pointer");
+  if (weight == out) return fail(ST_ERR_INVALID_ARG, "st_conv_dgrad_weights: in place is not supported");
+  const int taps = (int)taps_of(ndim, ksize);
+  const int64_t total = (int64_t)cout * cin * taps;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 gd((unsigned)((total + 255) / 256)), bd(256);
+  if (dtype == ST_BF16)
+    hipLaunchKernelGGL(dgrad_weights<uint16_t>, gd, bd, 0, st, static_cast<const uint16_t*>(weight),
+                       static_cast<uint16_t*>(out), cin, cout, taps, total);
+  else
+    hipLaunchKernelGGL(dgrad_weights<float>, gd, bd, 0, st, static_cast<const float*>(weight),
+                       static_cast<float*>(out), cin, cout, taps, total);
+  return launch_check("st_conv_dgrad_weights: launch");
+}
+
+size_t st_conv_workspace_bytes(const st_plan* in_plan, int32_t cout, int32_t ksize) {
+  if (!in_plan) return 0;
+  const size_t w = st_conv_weight_bytes(in_plan->ndim, (int32_t)in_plan->channels, cout, ksize, in_plan->dtype);
+  return w == 0 ? 0 : (w + 255) / 256 * 256;
+}
+
+st_status st_conv_sharded(const st_plan* in_plan, const void* const* in_bufs, const void* weight,
+                          const float* bias_or_null, int32_t cout, int32_t ksize, float* const* y_bufs,
+                          uint32_t* ymax_or_null, int32_t groups, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  static const char* who = "st_conv_sharded";
+  st_status s = conv_check(who, in_plan, in_bufs, weight, bias_or_null, cout, ksize, y_bufs, ymax_or_null, groups);
+  if (s != ST_OK) return s;
+  const size_t need = st_conv_workspace_bytes(in_plan, cout, ksize);
+  if (need == 0) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: unsupported ndim/ksize/dtype");
+  if (!workspace || workspace_bytes < need)
+    return fail(ST_ERR_WORKSPACE, "st_conv_sharded: workspace missing or smaller than st_conv_workspace_bytes");
+  if (!aligned16(workspace)) return fail(ST_ERR_ALIGNMENT, "st_conv_sharded: workspace not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // one launch packs the weights into the workspace and clears max |y|
+  const int nclr = ymax_or_null ? (int)(in_plan->batch * groups) : 0;
+  s = pack_weights(in_plan->ndim, (int)in_plan->channels, cout, ksize, in_plan->dtype, weight, workspace,
+                   ymax_or_null, nclr, st, who);
+  if (s != ST_OK) return s;
+  return conv_run(in_plan, in_bufs, workspace, bias_or_null, cout, ksize, y_bufs, ymax_or_null, groups, st);
+}
+
+st_status st_conv_sharded_packed(const st_plan* in_plan, const void* const* in_bufs, const void* packed_weight,
+                                 const float* bias_or_null, int32_t cout, int32_t ksize, float* const* y_bufs,
+                                 uint32_t* ymax_or_null, int32_t groups, void* stream) {
+  static const char* who = "st_conv_sharded_packed";
+  st_status s = conv_check(who, in_plan, in_bufs, packed_weight, bias_or_null, cout, ksize, y_bufs, ymax_or_null,
+                           groups);
+  if (s != ST_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (ymax_or_null) {
+    const int n = (int)(in_plan->batch * groups);
+    hipLaunchKernelGGL(fill_u32, dim3((n + 255) / 256), dim3(256), 0, st, ymax_or_null, 0u, n);
+    s = launch_check("st_conv_sharded_packed: ymax clear");
+    if (s != ST_OK) return s;
+  }
+  return conv_run(in_plan, in_bufs, packed_weight, bias_or_null, cout, ksize, y_bufs, ymax_or_null, groups, st);
 }
 
 }  // extern "C"

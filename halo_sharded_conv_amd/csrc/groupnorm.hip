@@ -62,6 +62,7 @@ struct GnArgs {
   const float* beta;
   GnShard sh[ST_MAX_SHARDS];
 };
+static_assert(sizeof(GnArgs) <= kMaxKernargBytes, "kernel argument struct too large");
 
 template <int VW> struct Vec;
 template <> struct Vec<4> {
@@ -402,6 +403,7 @@ struct GnbArgs {
   float* dbeta;                 // [C] or NULL
   GnbOut out[ST_MAX_SHARDS];    // kDyPadded*: where dy goes
 };
+static_assert(sizeof(GnbArgs) <= kMaxKernargBytes, "kernel argument struct too large");
 
 // fp32 -> bf16, round to nearest, ties to even (finite values)
 __device__ __forceinline__ uint32_t bf16_rne(float f) {

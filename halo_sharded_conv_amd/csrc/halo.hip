@@ -25,6 +25,7 @@ namespace {
 struct ShardPtrs {
   char* p[ST_MAX_SHARDS];
 };
+static_assert(sizeof(ShardPtrs) <= kMaxKernargBytes, "kernel argument struct too large");
 
 template <int VEC> struct Word;
 template <> struct Word<16> { using T = uint4; };

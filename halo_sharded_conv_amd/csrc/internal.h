@@ -86,6 +86,13 @@ constexpr int kHaloThreads = 256;
 constexpr int kHaloWordsPerThread = 4;
 constexpr int64_t kHaloWordsPerBlock = kHaloThreads * kHaloWordsPerThread;
 
+// Every kernel receives its per-shard table by value, sized for
+// ST_MAX_SHARDS whatever the plan's shard count, so each argument struct has
+// one fixed size, checked at compile time against this bound.  The largest,
+// the weight gradient's (~8.2 KB), is what every launch of that kernel
+// passes, at any shard count, so the GPU tests exercise the full sizes.
+constexpr size_t kMaxKernargBytes = 12 * 1024;
+
 // Uploads the descriptor table on first use (on the current device).
 st_status plan_device_table(st_plan* p, hipStream_t stream);
 // Public axis a of an ndim plan maps to internal axis a + (3 - ndim).

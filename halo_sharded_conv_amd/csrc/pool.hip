@@ -40,6 +40,7 @@ struct PoolArgs {
   int64_t total;
   PoolShard sh[ST_MAX_SHARDS];
 };
+static_assert(sizeof(PoolArgs) <= kMaxKernargBytes, "kernel argument struct too large");
 
 // VEC consecutive channels as fp32 (one 16-byte load for VEC > 1)
 template <typename T, int VEC> __device__ __forceinline__ void ldv(const T* p, float (&x)[VEC]);

@@ -31,6 +31,7 @@
 // is uniform over a block and the weights stay wave-uniform.
 #include <algorithm>
 #include <cstdio>
+#include <string>
 #include <type_traits>
 
 #include "internal.h"
@@ -57,6 +58,7 @@ struct StrArgs {
   const float* bias;                // [Cout] or NULL
   StrShard sh[ST_MAX_SHARDS];
 };
+static_assert(sizeof(StrArgs) <= kMaxKernargBytes, "kernel argument struct too large");
 
 // CV consecutive input channels as fp32 (one 16-byte load when CV > 1)
 template <typename T, int CV> __device__ __forceinline__ void ldc(const T* p, float (&x)[CV]);
@@ -138,6 +140,7 @@ struct TrArgs {
   const float* bias;                // [Cout] or NULL
   TrShard sh[ST_MAX_SHARDS];
 };
+static_assert(sizeof(TrArgs) <= kMaxKernargBytes, "kernel argument struct too large");
 
 // Gather form of the transposed conv: blockIdx.z is the output phase
 // (rd, rh, rw), a thread takes input position q and writes output q*s + r for
@@ -259,6 +262,7 @@ struct SxArgs {
   const float* bias;                // [Cout] or NULL
   SxShard sh[ST_MAX_SHARDS];
 };
+static_assert(sizeof(SxArgs) <= kMaxKernargBytes, "kernel argument struct too large");
 
 __device__ __forceinline__ uint16_t sx_rne(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -558,6 +562,56 @@ bool strided_sizes(const std::vector<int64_t>& in, int64_t k, int64_t s, std::ve
   return true;
 }
 
+
+// Raw weights -> the fp32 [taps][A][B] layout both kernels read (A = the
+// op's input channels, B = its output channels), widening bf16 exactly.
+// Strided conv: raw [B][A][taps] ([Cout][Cin], PyTorch's conv order);
+// transposed conv: raw [A][B][taps] ([in][out], PyTorch's conv_transpose
+// order).
+template <typename T>
+__global__ void pack_w_tab(const T* __restrict__ w, float* __restrict__ out, int a_ch, int b_ch, int taps,
+                           int a_major, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int j = (int)(i % b_ch);
+  const int64_t r = i / b_ch;
+  const int ia = (int)(r % a_ch);
+  const int t = (int)(r / a_ch);
+  const int64_t src = a_major ? ((int64_t)ia * b_ch + j) * taps + t : ((int64_t)j * a_ch + ia) * taps + t;
+  if constexpr (std::is_same<T, uint16_t>::value) out[i] = __uint_as_float((uint32_t)w[src] << 16);
+  else out[i] = w[src];
+}
+
+size_t tab_workspace_bytes(const st_plan* in_plan, int32_t cout, int32_t ksize) {
+  if (!in_plan || cout < 1 || ksize < 1 || ksize % 2 == 0) return 0;
+  int64_t taps = 1;
+  for (int a = 0; a < in_plan->ndim; ++a) taps *= ksize;
+  const size_t b = (size_t)taps * (size_t)in_plan->channels * (size_t)cout * 4;
+  return (b + 255) / 256 * 256;
+}
+
+// Checks the workspace and enqueues the packing of the raw weights into it.
+st_status pack_tab(const st_plan* in_plan, int32_t cout, int32_t ksize, const void* weight, bool a_major,
+                   void* workspace, size_t workspace_bytes, hipStream_t st, const char* who) {
+  const size_t need = tab_workspace_bytes(in_plan, cout, ksize);
+  if (!workspace || workspace_bytes < need)
+    return fail(ST_ERR_WORKSPACE, std::string(who) + ": workspace missing or too small");
+  if (!aligned16(workspace) || !aligned16(weight))
+    return fail(ST_ERR_ALIGNMENT, std::string(who) + ": weight and workspace must be 16-byte aligned");
+  int taps = 1;
+  for (int a = 0; a < in_plan->ndim; ++a) taps *= ksize;
+  const int a_ch = (int)in_plan->channels;
+  const int64_t total = (int64_t)taps * a_ch * cout;
+  const dim3 gd((unsigned)((total + 255) / 256)), bd(256);
+  if (in_plan->dtype == ST_BF16)
+    hipLaunchKernelGGL(pack_w_tab<uint16_t>, gd, bd, 0, st, static_cast<const uint16_t*>(weight),
+                       static_cast<float*>(workspace), a_ch, (int)cout, taps, a_major ? 1 : 0, total);
+  else
+    hipLaunchKernelGGL(pack_w_tab<float>, gd, bd, 0, st, static_cast<const float*>(weight),
+                       static_cast<float*>(workspace), a_ch, (int)cout, taps, a_major ? 1 : 0, total);
+  return launch_check((std::string(who) + ": weight packing launch").c_str());
+}
+
 }  // namespace
 }  // namespace st
 
@@ -597,20 +651,28 @@ st_status st_plan_strided(const st_plan* in_plan, int32_t ksize, int32_t stride,
   return st_plan_shards(nd, in_plan->batch, cout, spatial, counts, concat.data(), halo, ST_F32, out);
 }
 
-st_status st_conv_strided_sharded(const st_plan* in_plan, const void* const* in_bufs, const float* weight_tco,
+size_t st_conv_strided_workspace_bytes(const st_plan* in_plan, int32_t cout, int32_t ksize) {
+  return tab_workspace_bytes(in_plan, cout, ksize);
+}
+
+st_status st_conv_strided_sharded(const st_plan* in_plan, const void* const* in_bufs, const void* weight,
                                   const float* bias_or_null, int32_t ksize, int32_t stride,
-                                  const st_plan* out_plan, float* const* out_bufs, void* stream) {
+                                  const st_plan* out_plan, float* const* out_bufs, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   auto err = [](st_status s, const std::string& m) { return fail(s, "st_conv_strided_sharded: " + m); };
-  if (!in_plan || !out_plan || !in_bufs || !out_bufs || !weight_tco)
+  if (!in_plan || !out_plan || !in_bufs || !out_bufs || !weight)
     return err(ST_ERR_INVALID_ARG, "NULL argument");
+  const float* weight_tco = static_cast<const float*>(workspace);
   if (ksize < 1 || ksize % 2 == 0) return err(ST_ERR_UNSUPPORTED, "odd kernel sizes only");
   if (stride < 1) return err(ST_ERR_INVALID_ARG, "stride must be >= 1");
   if (out_plan->dtype != ST_F32) return err(ST_ERR_BAD_SHAPE, "outputs are fp32");
   if (out_plan->ndim != in_plan->ndim || out_plan->batch != in_plan->batch ||
       out_plan->shards.size() != in_plan->shards.size())
     return err(ST_ERR_BAD_SHAPE, "output plan does not match the input plan");
-  if ((reinterpret_cast<uintptr_t>(weight_tco) & 3) || (bias_or_null && (reinterpret_cast<uintptr_t>(bias_or_null) & 3)))
-    return err(ST_ERR_ALIGNMENT, "misaligned weight or bias");
+  if (bias_or_null && (reinterpret_cast<uintptr_t>(bias_or_null) & 3)) return err(ST_ERR_ALIGNMENT, "misaligned bias");
+  if (!workspace || workspace_bytes < tab_workspace_bytes(in_plan, (int32_t)out_plan->channels, ksize))
+    return err(ST_ERR_WORKSPACE, "workspace missing or smaller than st_conv_strided_workspace_bytes");
+  if (!aligned16(workspace) || !aligned16(weight)) return err(ST_ERR_ALIGNMENT, "misaligned weight or workspace");
   StrArgs a{};
   a.nshards = (int)in_plan->shards.size();
   a.batch = (int)in_plan->batch;
@@ -668,6 +730,9 @@ st_status st_conv_strided_sharded(const st_plan* in_plan, const void* const* in_
   a.total = total;
   if (total == 0) return ST_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  st_status ps = pack_tab(in_plan, a.cout, ksize, weight, false, workspace, workspace_bytes, st,
+                          "st_conv_strided_sharded");
+  if (ps != ST_OK) return ps;
   const bool bf = in_plan->dtype == ST_BF16;
   if (bf) {
     SxShard sx[ST_MAX_SHARDS];
@@ -737,20 +802,28 @@ st_status st_plan_transposed(const st_plan* in_plan, int32_t ksize, int32_t stri
   return st_plan_shards(nd, in_plan->batch, cout, spatial, counts, concat.data(), halo, ST_F32, out);
 }
 
-st_status st_conv_transposed_sharded(const st_plan* in_plan, const void* const* in_bufs, const float* weight_tio,
+size_t st_conv_transposed_workspace_bytes(const st_plan* in_plan, int32_t cout, int32_t ksize) {
+  return tab_workspace_bytes(in_plan, cout, ksize);
+}
+
+st_status st_conv_transposed_sharded(const st_plan* in_plan, const void* const* in_bufs, const void* weight,
                                      const float* bias_or_null, int32_t ksize, int32_t stride,
-                                     const st_plan* out_plan, float* const* out_bufs, void* stream) {
+                                     const st_plan* out_plan, float* const* out_bufs, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
   auto err = [](st_status s, const std::string& m) { return fail(s, "st_conv_transposed_sharded: " + m); };
-  if (!in_plan || !out_plan || !in_bufs || !out_bufs || !weight_tio)
+  if (!in_plan || !out_plan || !in_bufs || !out_bufs || !weight)
     return err(ST_ERR_INVALID_ARG, "NULL argument");
+  const float* weight_tio = static_cast<const float*>(workspace);
   if (ksize < 1 || ksize % 2 == 0) return err(ST_ERR_UNSUPPORTED, "odd kernel sizes only");
   if (stride < 1 || stride > kMaxTransposedStride) return err(ST_ERR_INVALID_ARG, "stride must be in [1, 8]");
   if (out_plan->dtype != ST_F32) return err(ST_ERR_BAD_SHAPE, "outputs are fp32");
   if (out_plan->ndim != in_plan->ndim || out_plan->batch != in_plan->batch ||
       out_plan->shards.size() != in_plan->shards.size())
     return err(ST_ERR_BAD_SHAPE, "output plan does not match the input plan");
-  if ((reinterpret_cast<uintptr_t>(weight_tio) & 3) || (bias_or_null && (reinterpret_cast<uintptr_t>(bias_or_null) & 3)))
-    return err(ST_ERR_ALIGNMENT, "misaligned weight or bias");
+  if (bias_or_null && (reinterpret_cast<uintptr_t>(bias_or_null) & 3)) return err(ST_ERR_ALIGNMENT, "misaligned bias");
+  if (!workspace || workspace_bytes < tab_workspace_bytes(in_plan, (int32_t)out_plan->channels, ksize))
+    return err(ST_ERR_WORKSPACE, "workspace missing or smaller than st_conv_transposed_workspace_bytes");
+  if (!aligned16(workspace) || !aligned16(weight)) return err(ST_ERR_ALIGNMENT, "misaligned weight or workspace");
   TrArgs a{};
   a.nshards = (int)in_plan->shards.size();
   a.batch = (int)in_plan->batch;
@@ -805,6 +878,9 @@ st_status st_conv_transposed_sharded(const st_plan* in_plan, const void* const* 
   a.total = total;
   if (total == 0) return ST_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  st_status ps = pack_tab(in_plan, a.cout, ksize, weight, true, workspace, workspace_bytes, st,
+                          "st_conv_transposed_sharded");
+  if (ps != ST_OK) return ps;
   const bool bf = in_plan->dtype == ST_BF16;
   if (bf) {
     SxShard sx[ST_MAX_SHARDS];

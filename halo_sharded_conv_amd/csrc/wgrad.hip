@@ -65,6 +65,7 @@ struct WgArgs {
   float* partial;       // [parts][Cout][Cin][taps]
   WgShard sh[kWgMaxShards];
 };
+static_assert(sizeof(WgArgs) <= kMaxKernargBytes, "kernel argument struct too large");
 
 __device__ __forceinline__ void decode_row(const WgArgs& a, int row, int& s, int& n, int& d, int& h) {
   s = 0;

@@ -14,8 +14,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-from . import (ST_BF16, ST_F32, ShardConvError, st_conv_dgrad_weights, st_conv_pack_weights, st_conv_sharded,
-               st_conv_weight_bytes, st_groupnorm_apply, st_groupnorm_backward,
+from . import (ST_BF16, ST_F32, ShardConvError, st_conv_dgrad_weights, st_conv_sharded,
+               st_conv_workspace_bytes, st_groupnorm_apply, st_groupnorm_backward,
                st_groupnorm_backward_workspace_bytes, st_groupnorm_combine, st_groupnorm_partials,
                st_groupnorm_sharded, st_groupnorm_workspace_bytes, st_groupnorm_workspace_layout,
                st_halo_exchange, st_halo_pack, st_halo_unpack, st_plan_shards)
@@ -51,10 +51,13 @@ class ShardedConvGN:
         tdt = torch.float32 if self.dtype == ST_F32 else torch.int16
         self.x_bufs = [torch.zeros(i["elems"], dtype=tdt, device=self.device) for i in self.info]
         self.msg = torch.zeros(max(16, self.in_plan.msg_bytes), dtype=torch.uint8, device=self.device)
-        wb = st_conv_weight_bytes(d, cfg.cin, cfg.cout, cfg.ksize, self.dtype)
+        wb = st_conv_workspace_bytes(self.in_plan, cfg.cout, cfg.ksize)
         if wb == 0:
             raise ShardConvError(4, "unsupported conv shape")
-        self.w_packed = torch.zeros(wb, dtype=torch.uint8, device=self.device)
+        # raw weights [Cout][Cin][k..] in the operand type, and the conv's
+        # workspace (the weights packed for its kernel, rewritten every call)
+        self.w_raw = torch.zeros(cfg.cout * cfg.cin * cfg.ksize ** d, dtype=tdt, device=self.device)
+        self.conv_ws = torch.zeros(wb, dtype=torch.uint8, device=self.device)
         self.out_info = [self.out_plan.shard_info(i) for i in range(self.S)]
         self.y_bufs = [torch.empty(i["elems"], dtype=torch.float32, device=self.device) for i in self.out_info]
         self.z_bufs = self.y_bufs if alias_z else [torch.empty_like(y) for y in self.y_bufs]
@@ -74,9 +77,7 @@ class ShardedConvGN:
 
     def set_weight(self, w: np.ndarray, bias: Optional[np.ndarray] = None) -> None:
         """w: [Cout, Cin, k..] float32 (fp32 layer) or uint16 bf16 bits."""
-        cfg = self.cfg
-        raw = self._host_to_dev(w.reshape(-1))
-        st_conv_pack_weights(cfg.ndim, cfg.cin, cfg.cout, cfg.ksize, self.dtype, raw, self.w_packed)
+        self.w_raw.copy_(self._host_to_dev(w.reshape(-1)))
         self.bias = None if bias is None else self._host_to_dev(np.asarray(bias, np.float32))
         _torch().cuda.synchronize()
 
@@ -84,13 +85,11 @@ class ShardedConvGN:
         """For a layer built from dgrad_config(forward_cfg): its conv becomes the
         input gradient of the forward conv.  w_forward: the forward weights
         [Cout, Cin, k..] (Cout = this layer's cin); they are transposed and
-        flipped on the device, then packed."""
+        flipped on the device."""
         cfg = self.cfg
         torch = _torch()
         raw = self._host_to_dev(w_forward.reshape(-1))
-        wt = torch.empty_like(raw)
-        st_conv_dgrad_weights(cfg.ndim, cfg.cout, cfg.cin, cfg.ksize, self.dtype, raw, wt)
-        st_conv_pack_weights(cfg.ndim, cfg.cin, cfg.cout, cfg.ksize, self.dtype, wt, self.w_packed)
+        st_conv_dgrad_weights(cfg.ndim, cfg.cout, cfg.cin, cfg.ksize, self.dtype, raw, self.w_raw)
         self.bias = None
         torch.cuda.synchronize()
 
@@ -134,8 +133,8 @@ class ShardedConvGN:
 
     def conv(self, stream=None) -> None:
         cfg = self.cfg
-        st_conv_sharded(self.in_plan, self.x_bufs, self.w_packed, self.bias, cfg.cout, cfg.ksize,
-                        self.out_plan, self.y_bufs, self.ymax if self.fuse_max else None, cfg.groups, stream)
+        st_conv_sharded(self.in_plan, self.x_bufs, self.w_raw, self.bias, cfg.cout, cfg.ksize, self.y_bufs,
+                        self.ymax if self.fuse_max else None, cfg.groups, self.conv_ws, stream)
 
     def norm(self, stream=None) -> None:
         cfg = self.cfg

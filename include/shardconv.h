@@ -178,9 +178,11 @@ st_status st_halo_exchange(st_plan* plan, void* const* shard_bufs, int32_t zero_
 /* ------------------------------------------------------------------ conv */
 
 /*
- * Packed weights.  Weights are given as [Cout][Cin][k]^ndim (PyTorch's
- * logical order) in `dtype` and repacked once into the layout the kernels
- * read.  st_conv_weight_bytes returns 0 for unsupported arguments.
+ * Packed weights, for st_conv_sharded_packed.  Weights are given as
+ * [Cout][Cin][k]^ndim (PyTorch's logical order) in `dtype` and repacked into
+ * the layout the kernel for that shape reads.  st_conv_weight_bytes returns 0
+ * for unsupported arguments.  st_conv_sharded does this packing itself, into
+ * its workspace, on every call.
  */
 size_t st_conv_weight_bytes(int32_t ndim, int32_t cin, int32_t cout, int32_t ksize, st_dtype dtype);
 st_status st_conv_pack_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t ksize,
@@ -194,8 +196,9 @@ st_status st_conv_pack_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t 
  * stride-1 cross-correlation y = conv(x, w), the gradient with respect to x is
  * dx = conv(dy, w') with w'[c][o][t] = w[o][c][flip(t)] (channels swapped,
  * every tap axis reversed), so the sharded input gradient is: exchange the
- * halos of dy, then st_conv_sharded with cin' = Cout, cout' = Cin and w'
- * packed by st_conv_pack_weights.
+ * halos of dy, then st_conv_sharded with cin' = Cout, cout' = Cin and
+ * weight w' (or st_conv_sharded_packed with w' packed by
+ * st_conv_pack_weights).
  *   weight   [Cout][Cin][k]^ndim in `dtype` (read)
  *   out      [Cin][Cout][k]^ndim in `dtype` (written; must not alias weight)
  * Pure bit permutation.  Errors: ST_ERR_UNSUPPORTED (ndim, even k, dtype),
@@ -214,23 +217,43 @@ st_status st_conv_dgrad_weights(int32_t ndim, int32_t cin, int32_t cout, int32_t
  * padding ksize/2 supplied by the shard margins:
  *   y[n, i, o] = bias[o] + sum_t sum_c W[o, c, t] * x[n, i + t - ksize/2, c]
  *
- *   in_plan, in_bufs   padded input shards, C = Cin, halo >= ksize/2 per axis
- *   packed_weight      from st_conv_pack_weights (same ndim, cin, cout, ksize, dtype)
+ *   in_plan, in_bufs   padded input shards, C = Cin, halo >= ksize/2 per
+ *                      spatial axis (read; only cells within ksize/2 of an
+ *                      interior are touched)
+ *   weight             [Cout][Cin][ksize]^ndim in in_plan's dtype (PyTorch's
+ *                      order; read)
  *   bias_or_null       Cout floats or NULL (zero bias)
- *   out_plan, y_bufs   fp32 outputs: a plan with the same shard sizes, batch,
- *                      C = Cout, halo 0, dtype ST_F32
+ *   y_bufs             fp32 outputs, one per shard: unpadded channels-last
+ *                      [N][extent...][Cout] over that shard's interior
+ *                      (written)
  *   ymax_or_null       if not NULL: [N][groups] uint32 receiving the bit
  *                      pattern of max |y| per (n, group) over all shards
  *                      (groups: contiguous blocks of Cout/groups channels)
+ *   workspace          >= st_conv_workspace_bytes(in_plan, cout, ksize)
+ *                      bytes, 16-byte aligned: the weights packed for the
+ *                      kernel that runs this shape (overwritten each call)
  * bf16 operands accumulate in fp32 on the matrix cores; fp32 operands use
  * fp32 FMA.  Each output's accumulation order depends only on its kernel
  * taps, so a shard's output is bitwise independent of the shard plan.
+ * Errors: ST_ERR_UNSUPPORTED (even ksize, unsupported dtype), ST_ERR_BAD_SHAPE
+ * (halo narrower than ksize/2), ST_ERR_WORKSPACE, ST_ERR_ALIGNMENT,
+ * ST_ERR_INVALID_ARG (NULL pointers, groups not dividing Cout), ST_ERR_HIP.
  */
-st_status st_conv_sharded(const st_plan* in_plan, const void* const* in_bufs,
-                          const void* packed_weight, const float* bias_or_null,
-                          int32_t cout, int32_t ksize, const st_plan* out_plan,
-                          float* const* y_bufs, uint32_t* ymax_or_null, int32_t groups,
+size_t st_conv_workspace_bytes(const st_plan* in_plan, int32_t cout, int32_t ksize);
+st_status st_conv_sharded(const st_plan* in_plan, const void* const* in_bufs, const void* weight,
+                          const float* bias_or_null, int32_t cout, int32_t ksize, float* const* y_bufs,
+                          uint32_t* ymax_or_null, int32_t groups, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * st_conv_sharded_packed - st_conv_sharded from weights packed beforehand by
+ * st_conv_pack_weights (same ndim, Cin, Cout, ksize and dtype), for callers
+ * that keep one set of weights over many calls; no workspace.  Same
+ * passage, arguments, outputs and errors as st_conv_sharded.
+ */
+st_status st_conv_sharded_packed(const st_plan* in_plan, const void* const* in_bufs, const void* packed_weight,
+                                 const float* bias_or_null, int32_t cout, int32_t ksize, float* const* y_bufs,
+                                 uint32_t* ymax_or_null, int32_t groups, void* stream);
 
 /*
  * st_conv_wgrad - weight gradient of st_conv_sharded, summed over all shards.
@@ -313,24 +336,29 @@ st_status st_plan_strided(const st_plan* in_plan, int32_t ksize, int32_t stride,
  * st_conv_strided_sharded - strided convolution of every shard from its
  * halo-padded chunk (after the halo exchange; halo >= ksize/2 per split axis):
  *   y[n, j, o] = bias[o] + sum_t sum_c W[o, c, t] * x[n, j*stride + t - ksize/2, c]
- *   in_plan, in_bufs   padded input shards (fp32 or bf16 operands)
- *   weight_tco         [taps][Cin][Cout] fp32 weights (taps lexicographic;
- *                      bf16 weights widened exactly), read only.  With bf16
- *                      input shards the values must be bf16 ones: the
- *                      matrix-core path rounds them to bf16 (nearest even)
+ *   in_plan, in_bufs   padded input shards (fp32 or bf16 operands; read)
+ *   weight             W as [Cout][Cin][ksize]^ndim in in_plan's dtype
+ *                      (PyTorch's conv order; read)
  *   bias_or_null       Cout floats or NULL
  *   out_plan, out_bufs the plan st_plan_strided returned for (in_plan, ksize,
  *                      stride, Cout) and its fp32 shards (only interiors written)
+ *   workspace          >= st_conv_strided_workspace_bytes(in_plan, Cout,
+ *                      ksize) bytes, 16-byte aligned: the weights widened to
+ *                      fp32 and reordered [taps][Cin][Cout] (overwritten)
  * bf16 input shards with Cin % 16 == 0, Cout % 16 == 0 and the weights of
  * a 64- (or 32-) channel output block within 160 KiB run on the matrix cores
  * (bf16 products, fp32 accumulation); every other case on fp32 FMA.  Either
  * way each output sums bias, then taps lexicographic, input channels
  * ascending, in an order fixed by the layer shape, so its bits do not depend
  * on the shard plan.
+ * Errors: ST_ERR_BAD_SHAPE (out_plan is not the strided plan, halo too small),
+ * ST_ERR_WORKSPACE, ST_ERR_ALIGNMENT, ST_ERR_INVALID_ARG, ST_ERR_UNSUPPORTED.
  */
-st_status st_conv_strided_sharded(const st_plan* in_plan, const void* const* in_bufs, const float* weight_tco,
+size_t st_conv_strided_workspace_bytes(const st_plan* in_plan, int32_t cout, int32_t ksize);
+st_status st_conv_strided_sharded(const st_plan* in_plan, const void* const* in_bufs, const void* weight,
                                   const float* bias_or_null, int32_t ksize, int32_t stride,
-                                  const st_plan* out_plan, float* const* out_bufs, void* stream);
+                                  const st_plan* out_plan, float* const* out_bufs, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * st_plan_transposed - the output plan of a transposed (upsampling)
@@ -357,24 +385,30 @@ st_status st_plan_transposed(const st_plan* in_plan, int32_t ksize, int32_t stri
  *   x[n, j, c] = bias[c] + sum over (i, t) with i*stride + t - ksize/2 = j of
  *                sum_o W[o, c, t] * y[n, i, o]
  * so that <conv_strided(x, W), y> = <x, conv_transposed(y, W)> without bias.
- *   in_plan, in_bufs   padded input shards y (fp32 or bf16 operands), in_plan
- *                      channels = the strided conv's output channels
- *   weight_tio         [taps][Cin][Cout] fp32, weight_tio[t][o][c] = W[o, c, t]
- *                      (Cin = in_plan channels), read only; bf16 values with
- *                      bf16 input shards (as for st_conv_strided_sharded)
+ *   in_plan, in_bufs   padded input shards y (fp32 or bf16 operands; read),
+ *                      in_plan channels = the strided conv's output channels
+ *   weight             W as [Cin][Cout][ksize]^ndim in in_plan's dtype, Cin =
+ *                      in_plan channels (PyTorch's conv_transpose order: the
+ *                      same array as the matching strided conv's weight; read)
  *   bias_or_null       Cout floats or NULL
  *   out_plan, out_bufs the plan st_plan_transposed returned for (in_plan,
  *                      ksize, stride, Cout) and its fp32 shards (only
  *                      interiors written)
+ *   workspace          >= st_conv_transposed_workspace_bytes(in_plan, Cout,
+ *                      ksize) bytes, 16-byte aligned: the weights widened to
+ *                      fp32 and reordered [taps][Cin][Cout] (overwritten)
  * Matrix cores or fp32 FMA under the same conditions as the strided conv;
  * each output sums bias, then its phase's taps lexicographic, input channels
  * ascending, so its bits do not depend on the shard plan.
  * Errors: ST_ERR_BAD_SHAPE (out_plan is not the transposed plan, halo too
- * small), ST_ERR_ALIGNMENT, ST_ERR_INVALID_ARG, ST_ERR_UNSUPPORTED.
+ * small), ST_ERR_WORKSPACE, ST_ERR_ALIGNMENT, ST_ERR_INVALID_ARG,
+ * ST_ERR_UNSUPPORTED.
  */
-st_status st_conv_transposed_sharded(const st_plan* in_plan, const void* const* in_bufs, const float* weight_tio,
+size_t st_conv_transposed_workspace_bytes(const st_plan* in_plan, int32_t cout, int32_t ksize);
+st_status st_conv_transposed_sharded(const st_plan* in_plan, const void* const* in_bufs, const void* weight,
                                      const float* bias_or_null, int32_t ksize, int32_t stride,
-                                     const st_plan* out_plan, float* const* out_bufs, void* stream);
+                                     const st_plan* out_plan, float* const* out_bufs, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------- GroupNorm */
 

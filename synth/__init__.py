@@ -156,8 +156,9 @@ WORKLOADS = {
         ((1024,), (900, 892)), 105, 205, x_kind="channel_affine", xc_seed=405),
 }
 
-# The workload the throughput figure is quoted on (the 2D 2048^2 image layer).
-BENCH_WORKLOAD = "img2048_c64_k3_bf16"
+# The workload the throughput figure is quoted on: the largest volume that
+# one GPU holds, 1x16x512^3 with the 5^3 stencil (2^27 output voxels).
+BENCH_WORKLOAD = "vol512_c16_k5_bf16"
 
 
 def workload(name: str) -> Workload:

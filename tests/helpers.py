@@ -70,3 +70,18 @@ def bits_equal(a, b) -> bool:
 def torch_bits_equal(t1, t2) -> bool:
     import torch
     return bool(torch.equal(t1.view(torch.int32), t2.view(torch.int32)))
+
+
+def dev_raw(a):
+    """A host array as a GPU tensor of the same bits (bf16 patterns stay
+    uint16 bit patterns, viewed as int16): what the library is handed."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a.reshape(-1).copy()).cuda()
+
+
+def dev_workspace(nbytes: int):
+    import torch
+    return torch.empty(max(16, int(nbytes)), dtype=torch.uint8, device="cuda")

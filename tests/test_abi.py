@@ -118,19 +118,30 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     overlapping = PP(0x10000, 0x10010)   # padded shards are 6 x 10 x 8 bf16 = 960 bytes
     assert L.st_halo_exchange(p.handle, overlapping, 1, s) == INVALID
     assert "overlap" in hsc.lib.st_last_error().decode()
-    # conv
+    # conv: raw weights plus a workspace (the packed weights)
     w = ctypes.c_void_p(0x40000)
-    assert L.st_conv_sharded(p.handle, aligned, w, None, 16, 2, q.handle, aligned, None, 1, s) == UNSUPPORTED
-    assert L.st_conv_sharded(p.handle, aligned, w, None, 16, 5, q.handle, aligned, None, 1, s) == BAD_SHAPE
-    assert L.st_conv_sharded(p.handle, aligned, w, None, 32, 3, q.handle, aligned, None, 1, s) == BAD_SHAPE
-    assert L.st_conv_sharded(p.handle, aligned, w, None, 16, 3, q_bad.handle, aligned, None, 1, s) == BAD_SHAPE
-    assert L.st_conv_sharded(p.handle, aligned, w, None, 16, 3, p.handle, aligned, None, 1, s) == BAD_SHAPE
-    assert L.st_conv_sharded(p.handle, aligned, w, None, 16, 3, q.handle, aligned,
-                             ctypes.c_void_p(0x50000), 3, s) == INVALID
-    assert L.st_conv_sharded(p.handle, aligned, ctypes.c_void_p(0x40008), None, 16, 3, q.handle, aligned,
-                             None, 1, s) == ALIGN
-    assert L.st_conv_sharded(p.handle, misaligned, w, None, 16, 3, q.handle, aligned, None, 1, s) == ALIGN
-    assert L.st_conv_sharded(None, aligned, w, None, 16, 3, q.handle, aligned, None, 1, s) == INVALID
+    cws = ctypes.c_void_p(0xD0000)
+    cneed = L.st_conv_workspace_bytes(p.handle, 16, 3)
+    assert cneed >= L.st_conv_weight_bytes(2, 8, 16, 3, 1) and cneed % 256 == 0
+    assert L.st_conv_workspace_bytes(p.handle, 16, 2) == 0 and L.st_conv_workspace_bytes(None, 16, 3) == 0
+    cv = L.st_conv_sharded
+    assert cv(p.handle, aligned, w, None, 16, 2, aligned, None, 1, cws, cneed, s) == UNSUPPORTED
+    assert cv(p.handle, aligned, w, None, 16, 5, aligned, None, 1, cws, cneed, s) == BAD_SHAPE    # halo 1 < 2
+    assert cv(p.handle, aligned, w, None, 16, 3, aligned, ctypes.c_void_p(0x50000), 3, cws, cneed, s) == INVALID
+    assert cv(p.handle, aligned, ctypes.c_void_p(0x40008), None, 16, 3, aligned, None, 1, cws, cneed, s) == ALIGN
+    assert cv(p.handle, misaligned, w, None, 16, 3, aligned, None, 1, cws, cneed, s) == ALIGN
+    assert cv(p.handle, aligned, w, None, 16, 3, misaligned, None, 1, cws, cneed, s) == ALIGN
+    assert cv(p.handle, nulls, w, None, 16, 3, aligned, None, 1, cws, cneed, s) == INVALID
+    assert cv(None, aligned, w, None, 16, 3, aligned, None, 1, cws, cneed, s) == INVALID
+    assert cv(p.handle, aligned, None, None, 16, 3, aligned, None, 1, cws, cneed, s) == INVALID
+    assert cv(p.handle, aligned, w, None, 16, 3, aligned, None, 1, cws, cneed - 1, s) == WORKSPACE
+    assert cv(p.handle, aligned, w, None, 16, 3, aligned, None, 1, None, cneed, s) == WORKSPACE
+    assert cv(p.handle, aligned, w, None, 16, 3, aligned, None, 1, ctypes.c_void_p(0xD0008), cneed, s) == ALIGN
+    cp = L.st_conv_sharded_packed
+    assert cp(p.handle, aligned, w, None, 16, 2, aligned, None, 1, s) == UNSUPPORTED
+    assert cp(p.handle, aligned, w, None, 16, 5, aligned, None, 1, s) == BAD_SHAPE
+    assert cp(p.handle, aligned, ctypes.c_void_p(0x40008), None, 16, 3, aligned, None, 1, s) == ALIGN
+    assert cp(None, aligned, w, None, 16, 3, aligned, None, 1, s) == INVALID
     # weights
     assert L.st_conv_weight_bytes(2, 8, 16, 2, 1) == 0
     assert L.st_conv_weight_bytes(4, 8, 16, 3, 1) == 0
@@ -197,14 +208,21 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     sq = hsc.st_plan_strided(p, 3, 2, 16)
     assert sq.shards == ((2, 2), (4,)) and sq.channels == 16
     wt = ctypes.c_void_p(0xF0000)
+    tws = ctypes.c_void_p(0xE0000)
+    sneed = L.st_conv_strided_workspace_bytes(p.handle, 16, 3)
+    assert sneed == -(-9 * 8 * 16 * 4 // 256) * 256
+    assert L.st_conv_strided_workspace_bytes(p.handle, 16, 4) == 0
     cs = L.st_conv_strided_sharded
-    assert cs(p.handle, aligned, None, None, 3, 2, sq.handle, aligned, s) == INVALID
-    assert cs(p.handle, aligned, wt, None, 3, 3, sq.handle, aligned, s) == BAD_SHAPE          # not its strided plan
-    assert cs(p.handle, aligned, wt, None, 2, 2, sq.handle, aligned, s) == UNSUPPORTED
-    assert cs(p.handle, misaligned, wt, None, 3, 2, sq.handle, aligned, s) == ALIGN
-    assert cs(p.handle, aligned, wt, None, 3, 2, p.handle, aligned, s) == BAD_SHAPE            # bf16 output plan
+    assert cs(p.handle, aligned, None, None, 3, 2, sq.handle, aligned, tws, sneed, s) == INVALID
+    assert cs(p.handle, aligned, wt, None, 3, 3, sq.handle, aligned, tws, sneed, s) == BAD_SHAPE   # not its plan
+    assert cs(p.handle, aligned, wt, None, 2, 2, sq.handle, aligned, tws, sneed, s) == UNSUPPORTED
+    assert cs(p.handle, misaligned, wt, None, 3, 2, sq.handle, aligned, tws, sneed, s) == ALIGN
+    assert cs(p.handle, aligned, wt, None, 3, 2, p.handle, aligned, tws, sneed, s) == BAD_SHAPE     # bf16 output plan
+    assert cs(p.handle, aligned, wt, None, 3, 2, sq.handle, aligned, tws, sneed - 4, s) == WORKSPACE
+    assert cs(p.handle, aligned, wt, None, 3, 2, sq.handle, aligned, None, sneed, s) == WORKSPACE
+    assert cs(p.handle, aligned, ctypes.c_void_p(0xF0002), None, 3, 2, sq.handle, aligned, tws, sneed, s) == ALIGN
     sq0 = hsc.st_plan_strided(p0, 3, 2, 8)
-    assert cs(p0.handle, aligned, wt, None, 3, 2, sq0.handle, aligned, s) == BAD_SHAPE         # input halo 0 < 1
+    assert cs(p0.handle, aligned, wt, None, 3, 2, sq0.handle, aligned, tws, sneed, s) == BAD_SHAPE  # halo 0 < 1
     # transposed conv: derived plan and its errors
     assert L.st_plan_transposed(p.handle, 4, 2, 8, None, ctypes.byref(out)) == UNSUPPORTED
     assert L.st_plan_transposed(p.handle, 3, 0, 8, None, ctypes.byref(out)) == INVALID
@@ -212,18 +230,20 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert L.st_plan_transposed(p.handle, 3, 2, 0, None, ctypes.byref(out)) == INVALID
     tq = hsc.st_plan_transposed(p, 3, 2, 16)
     assert tq.shards == ((8, 8), (16,)) and tq.channels == 16
+    tneed = L.st_conv_transposed_workspace_bytes(p.handle, 16, 7)
     ct = L.st_conv_transposed_sharded
-    assert ct(p.handle, aligned, None, None, 3, 2, tq.handle, aligned, s) == INVALID
-    assert ct(p.handle, aligned, wt, None, 3, 3, tq.handle, aligned, s) == BAD_SHAPE          # not its transposed plan
-    assert ct(p.handle, aligned, wt, None, 2, 2, tq.handle, aligned, s) == UNSUPPORTED
-    assert ct(p.handle, misaligned, wt, None, 3, 2, tq.handle, aligned, s) == ALIGN
-    assert ct(p.handle, aligned, ctypes.c_void_p(0xF0002), None, 3, 2, tq.handle, aligned, s) == ALIGN
-    assert ct(p.handle, aligned, wt, None, 3, 2, p.handle, aligned, s) == BAD_SHAPE            # bf16 output plan
-    assert ct(p.handle, nulls, wt, None, 3, 2, tq.handle, aligned, s) == INVALID
+    assert ct(p.handle, aligned, None, None, 3, 2, tq.handle, aligned, tws, tneed, s) == INVALID
+    assert ct(p.handle, aligned, wt, None, 3, 3, tq.handle, aligned, tws, tneed, s) == BAD_SHAPE   # not its plan
+    assert ct(p.handle, aligned, wt, None, 2, 2, tq.handle, aligned, tws, tneed, s) == UNSUPPORTED
+    assert ct(p.handle, misaligned, wt, None, 3, 2, tq.handle, aligned, tws, tneed, s) == ALIGN
+    assert ct(p.handle, aligned, ctypes.c_void_p(0xF0002), None, 3, 2, tq.handle, aligned, tws, tneed, s) == ALIGN
+    assert ct(p.handle, aligned, wt, None, 3, 2, p.handle, aligned, tws, tneed, s) == BAD_SHAPE     # bf16 output plan
+    assert ct(p.handle, nulls, wt, None, 3, 2, tq.handle, aligned, tws, tneed, s) == INVALID
+    assert ct(p.handle, aligned, wt, None, 3, 2, tq.handle, aligned, None, tneed, s) == WORKSPACE
     tq0 = hsc.st_plan_transposed(p0, 3, 2, 8)
-    assert ct(p0.handle, aligned, wt, None, 3, 2, tq0.handle, aligned, s) == BAD_SHAPE         # input halo 0 < 1
+    assert ct(p0.handle, aligned, wt, None, 3, 2, tq0.handle, aligned, tws, tneed, s) == BAD_SHAPE  # halo 0 < 1
     tq7 = hsc.st_plan_transposed(p, 7, 2, 16)      # k 7, stride 2 reads cells q-1 .. q+2
-    assert ct(p.handle, aligned, wt, None, 7, 2, tq7.handle, aligned, s) == BAD_SHAPE          # halo 1 < 2
+    assert ct(p.handle, aligned, wt, None, 7, 2, tq7.handle, aligned, tws, tneed, s) == BAD_SHAPE   # halo 1 < 2
     # groupnorm backward
     bneed = L.st_groupnorm_backward_workspace_bytes(q.handle, 4)
     assert bneed > 0 and L.st_groupnorm_backward_workspace_bytes(None, 4) == 0

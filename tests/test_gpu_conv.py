@@ -120,3 +120,25 @@ def test_conv_plan_independent_of_uneven_splits():
         say(f"plan {shards}")
         got = run(base.with_shards(shards), x, w).y_host()
         assert bits_equal(got, ref)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_packed_entry_point_gives_the_same_bits(name):
+    """st_conv_sharded_packed on weights packed once by st_conv_pack_weights
+    writes the same y and max |y| as st_conv_sharded, which packs the raw
+    weights into its workspace on every call."""
+    import halo_sharded_conv_amd as hsc
+    wl = CASES[name]
+    say(f"packed entry point == raw-weight entry point: {name}")
+    x, w = synth.make_input(wl), synth.make_weight(wl)
+    layer = run(wl, x, w)
+    packed = torch.zeros(hsc.st_conv_weight_bytes(wl.ndim, wl.cin, wl.cout, wl.ksize, wl.dtype), dtype=torch.uint8,
+                         device="cuda")
+    hsc.st_conv_pack_weights(wl.ndim, wl.cin, wl.cout, wl.ksize, wl.dtype, layer.w_raw, packed)
+    ys = [torch.full_like(y, float("nan")) for y in layer.y_bufs]
+    ymax = torch.full_like(layer.ymax, -1)
+    hsc.st_conv_sharded_packed(layer.in_plan, layer.x_bufs, packed, None, wl.cout, wl.ksize, ys, ymax, wl.groups)
+    torch.cuda.synchronize()
+    for a, b in zip(layer.y_bufs, ys):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(layer.ymax, ymax)

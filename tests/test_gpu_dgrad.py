@@ -2,7 +2,7 @@
 
 The input-gradient layer reads dy with the forward layer's shards and halo,
 exchanges its halos like x, and runs the sharded conv with the transposed,
-tap-flipped weights (st_conv_dgrad_weights, then st_conv_pack_weights).
+tap-flipped weights (st_conv_dgrad_weights, then st_conv_sharded).
 Checks: the weight transform bit for bit; dx against the oracle's
 conv_same_dgrad (the adjoint of conv_same, pinned on the CPU) within the
 forward tolerance; sharded dx equal to unsharded dx bit for bit.

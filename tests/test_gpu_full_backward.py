@@ -26,7 +26,7 @@ import halo_sharded_conv_amd as hsc
 import oracle
 import synth
 from halo_sharded_conv_amd.layer import ShardedConvGN, dgrad_config
-from helpers import TOL, bits_equal, rel_err, say
+from helpers import TOL, bits_equal, dev_raw, dev_workspace, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -120,18 +120,16 @@ def test_full_size_strided_conv():
     q = hsc.st_plan_strided(layer.in_plan, wl.ksize, 2, wl.cout)
     for a in range(wl.ndim):
         assert list(q.shards[a]) == oracle.strided_shard_sizes(wl.shards[a], wl.ksize, 2)
-    wf = oracle.widen(w, wl.dtype)
-    wt = torch.from_numpy(np.ascontiguousarray(
-        np.moveaxis(wf.astype(np.float32).reshape(wl.cout, wl.cin, -1), 2, 0).swapaxes(1, 2))).cuda()
     outs = [torch.empty(q.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(q.num_shards)]
-    hsc.st_conv_strided_sharded(layer.in_plan, layer.x_bufs, wt, None, wl.ksize, 2, q, outs)
+    ws = dev_workspace(hsc.st_conv_strided_workspace_bytes(layer.in_plan, wl.cout, wl.ksize))
+    hsc.st_conv_strided_sharded(layer.in_plan, layer.x_bufs, dev_raw(w), None, wl.ksize, 2, q, outs, ws)
     torch.cuda.synchronize()
     got = np.empty((wl.batch, *[sum(a) for a in q.shards], wl.cout), np.float32)
     for i in range(q.num_shards):
         inf = q.shard_info(i)
         got[tuple([slice(None)] + [slice(o, o + e) for o, e in zip(inf["offset"], inf["extent"])])] = \
             outs[i].view(q.padded_shape(i)).cpu().numpy()
-    want = oracle.conv_strided(oracle.widen(x, wl.dtype), wf, 2)
+    want = oracle.conv_strided(oracle.widen(x, wl.dtype), oracle.widen(w, wl.dtype), 2)
     err = rel_err(got, want)
     say(f"  max|err|/rms {err:.2e} (tolerance 1e-5)")
     assert err <= 1e-5
@@ -152,13 +150,12 @@ def test_full_size_transposed_conv():
     layer.exchange()
     q = hsc.st_plan_transposed(layer.in_plan, wl.ksize, 2, wl.cout)
     assert q.shards == tuple(tuple(a) for a in wl_out.shards)
-    wf = np.swapaxes(oracle.widen(w, wl.dtype), 0, 1)               # W [Cy = Cin][Cx = Cout][k..]
-    wt = torch.from_numpy(np.ascontiguousarray(
-        np.moveaxis(wf.astype(np.float32).reshape(wl.cin, wl.cout, -1), 2, 0))).cuda()
+    wtr = np.ascontiguousarray(np.swapaxes(w, 0, 1))                # W [in = Cin][out = Cout][k..], raw bits
     bias = np.random.default_rng(7).uniform(-1, 1, wl.cout).astype(np.float32)
     outs = [torch.empty(q.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(q.num_shards)]
-    hsc.st_conv_transposed_sharded(layer.in_plan, layer.x_bufs, wt, torch.from_numpy(bias).cuda(), wl.ksize, 2,
-                                   q, outs)
+    ws = dev_workspace(hsc.st_conv_transposed_workspace_bytes(layer.in_plan, wl.cout, wl.ksize))
+    hsc.st_conv_transposed_sharded(layer.in_plan, layer.x_bufs, dev_raw(wtr), torch.from_numpy(bias).cuda(),
+                                   wl.ksize, 2, q, outs, ws)
     torch.cuda.synchronize()
     got = np.empty((wl.batch, *[sum(a) for a in q.shards], wl.cout), np.float32)
     for i in range(q.num_shards):
@@ -166,7 +163,7 @@ def test_full_size_transposed_conv():
         got[tuple([slice(None)] + [slice(o, o + e) for o, e in zip(inf["offset"], inf["extent"])])] = \
             outs[i].view(q.padded_shape(i)).cpu().numpy()
     del outs
-    want = oracle.conv_transposed(oracle.widen(y, wl.dtype), np.ascontiguousarray(wf), 2) + bias
+    want = oracle.conv_transposed(oracle.widen(y, wl.dtype), oracle.widen(wtr, wl.dtype), 2) + bias
     err = rel_err(got, want)
     say(f"  max|err|/rms {err:.2e} (tolerance 1e-5)")
     assert err <= 1e-5

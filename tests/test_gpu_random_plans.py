@@ -17,7 +17,7 @@ import torch
 import oracle
 import synth
 from halo_sharded_conv_amd.layer import ShardedConvGN
-from helpers import TOL, bits_equal, oracle_forward, rel_err, say
+from helpers import TOL, bits_equal, dev_raw, dev_workspace, oracle_forward, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -95,24 +95,25 @@ def _shape_ops(wl, x, w, bias):
     layer = ShardedConvGN(wl)
     layer.load_input(x)
     layer.exchange()
-    wf = oracle.widen(w, wl.dtype).astype(np.float32)
     res = {}
+    wd = dev_raw(w)
     b = torch.from_numpy(bias).cuda()
     try:
         q = hsc.st_plan_strided(layer.in_plan, wl.ksize, 2, wl.cout)
         outs = [torch.empty(q.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(q.num_shards)]
-        wt = torch.from_numpy(np.ascontiguousarray(np.moveaxis(wf.reshape(wl.cout, wl.cin, -1), 2, 0).swapaxes(1, 2)))
-        hsc.st_conv_strided_sharded(layer.in_plan, layer.x_bufs, wt.cuda(), b, wl.ksize, 2, q, outs)
+        ws = dev_workspace(hsc.st_conv_strided_workspace_bytes(layer.in_plan, wl.cout, wl.ksize))
+        hsc.st_conv_strided_sharded(layer.in_plan, layer.x_bufs, wd, b, wl.ksize, 2, q, outs, ws)
         res["strided"] = (q, outs)
     except hsc.ShardConvError as e:
         assert e.status == 3, e                       # ST_ERR_SHARD_TOO_SMALL
         res["strided"] = None
-    # transposed: W[o = Cin side][c = Cout side] read from the same weights
-    wtr = np.ascontiguousarray(np.swapaxes(wf, 0, 1))
+    # transposed: W [in = Cin side][out = Cout side], the same weight bits
+    # with their two channel axes swapped
+    wtr = np.ascontiguousarray(np.swapaxes(w, 0, 1))
     q = hsc.st_plan_transposed(layer.in_plan, wl.ksize, 2, wl.cout)
     outs = [torch.empty(q.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(q.num_shards)]
-    wt = torch.from_numpy(np.ascontiguousarray(np.moveaxis(wtr.reshape(wl.cin, wl.cout, -1), 2, 0)))
-    hsc.st_conv_transposed_sharded(layer.in_plan, layer.x_bufs, wt.cuda(), b, wl.ksize, 2, q, outs)
+    ws = dev_workspace(hsc.st_conv_transposed_workspace_bytes(layer.in_plan, wl.cout, wl.ksize))
+    hsc.st_conv_transposed_sharded(layer.in_plan, layer.x_bufs, dev_raw(wtr), b, wl.ksize, 2, q, outs, ws)
     res["transposed"] = (q, outs, wtr)
     try:
         q = hsc.st_plan_pooled(layer.in_plan, 2, 2)
@@ -155,7 +156,7 @@ def test_random_plan_shape_changing_ops(seed):
     q, outs, wtr = a["transposed"]
     got = _gather(q, outs, wl.batch)
     assert bits_equal(got, _gather(*u["transposed"][:2], wl.batch))
-    e = rel_err(got, oracle.conv_transposed(xf, wtr.astype(np.float64), 2) + bias)
+    e = rel_err(got, oracle.conv_transposed(xf, oracle.widen(wtr, wl.dtype), 2) + bias)
     say(f"  transposed max|err|/rms {e:.2e}")
     assert e <= 1e-5
     if a["pool"] is None:

@@ -18,7 +18,7 @@ import halo_sharded_conv_amd as hsc
 import oracle
 import synth
 from halo_sharded_conv_amd.layer import ShardedConvGN
-from helpers import bits_equal, direct_cases, rel_err, say, small_cases
+from helpers import bits_equal, dev_raw, dev_workspace, direct_cases, rel_err, say, small_cases
 
 pytestmark = pytest.mark.gpu
 
@@ -28,12 +28,6 @@ CASES["img_c64to48"] = dataclasses.replace(CASES["img64_small"], name="img_c64to
 TOL_STRIDED = 1e-5      # fp32 accumulation of exact products
 
 
-def weight_tco(w, wl):
-    wf = oracle.widen(w, wl.dtype).astype(np.float32)            # exact widening
-    t = np.moveaxis(wf.reshape(wl.cout, wl.cin, -1), 2, 0)        # [taps][Cout][Cin]
-    return torch.from_numpy(np.ascontiguousarray(np.swapaxes(t, 1, 2))).cuda()   # [taps][Cin][Cout]
-
-
 def run_strided(wl, x, w, bias, s):
     layer = ShardedConvGN(wl)                     # padded input shards with halo ksize // 2
     layer.load_input(x)
@@ -41,7 +35,9 @@ def run_strided(wl, x, w, bias, s):
     q = hsc.st_plan_strided(layer.in_plan, wl.ksize, s, wl.cout)
     outs = [torch.empty(q.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(q.num_shards)]
     b = None if bias is None else torch.from_numpy(np.asarray(bias, np.float32)).cuda()
-    hsc.st_conv_strided_sharded(layer.in_plan, layer.x_bufs, weight_tco(w, wl), b, wl.ksize, s, q, outs)
+    ws = dev_workspace(hsc.st_conv_strided_workspace_bytes(layer.in_plan, wl.cout, wl.ksize))
+    # the synth bits go to the library as they are: it widens and reorders them
+    hsc.st_conv_strided_sharded(layer.in_plan, layer.x_bufs, dev_raw(w), b, wl.ksize, s, q, outs, ws)
     torch.cuda.synchronize()
     got = np.empty((wl.batch, *[sum(a) for a in q.shards], wl.cout), np.float32)
     for i in range(q.num_shards):

@@ -19,7 +19,7 @@ import halo_sharded_conv_amd as hsc
 import oracle
 import synth
 from halo_sharded_conv_amd.layer import ShardedConvGN
-from helpers import bits_equal, direct_cases, rel_err, say, small_cases
+from helpers import bits_equal, dev_raw, dev_workspace, direct_cases, rel_err, say, small_cases
 
 pytestmark = pytest.mark.gpu
 
@@ -31,15 +31,11 @@ TOL_TRANSPOSED = 1e-5      # fp32 products and accumulation
 
 def make_w(wl, cx, seed):
     """W [Cy][Cx][k..k] with Cy the input's channels (the strided conv's
-    outputs), bf16 values (the weights of bf16 layers are bf16)."""
+    outputs), in the layer's operand type: float32, or bf16 bit patterns
+    (uint16) rounded from the float32 draws."""
     r = np.random.default_rng(seed)
     w = r.uniform(-1, 1, size=(wl.cin, cx) + (wl.ksize,) * wl.ndim).astype(np.float32)
-    return oracle.widen(synth.f32_to_bf16_bits(w), "bf16").astype(np.float32)
-
-
-def weight_tio(w):
-    cy, cx = w.shape[:2]
-    return torch.from_numpy(np.ascontiguousarray(np.moveaxis(w.reshape(cy, cx, -1), 2, 0))).cuda()
+    return synth.f32_to_bf16_bits(w) if wl.dtype == "bf16" else w
 
 
 def gather_plan(q, outs, batch):
@@ -60,7 +56,9 @@ def run_transposed(wl, y, w, bias, s):
     outs = [torch.full((q.shard_info(i)["elems"],), 7.0, dtype=torch.float32, device="cuda")
             for i in range(q.num_shards)]
     b = None if bias is None else torch.from_numpy(np.asarray(bias, np.float32)).cuda()
-    hsc.st_conv_transposed_sharded(layer.in_plan, layer.x_bufs, weight_tio(w), b, wl.ksize, s, q, outs)
+    ws = dev_workspace(hsc.st_conv_transposed_workspace_bytes(layer.in_plan, cx, wl.ksize))
+    # the raw weight bits go to the library, which widens and reorders them
+    hsc.st_conv_transposed_sharded(layer.in_plan, layer.x_bufs, dev_raw(w), b, wl.ksize, s, q, outs, ws)
     torch.cuda.synchronize()
     return layer, q, gather_plan(q, outs, wl.batch)
 
@@ -81,7 +79,7 @@ def test_transposed_matches_oracle(name, s):
     layer, q, got = run_transposed(wl, y, w, bias, s)
     for a in range(wl.ndim):
         assert list(q.shards[a]) == [e * s for e in wl.shards[a]]
-    want = oracle.conv_transposed(oracle.widen(y, wl.dtype), w.astype(np.float64), s) + bias
+    want = oracle.conv_transposed(oracle.widen(y, wl.dtype), oracle.widen(w, wl.dtype), s) + bias
     err = rel_err(got, want)
     say(f"  max|err|/rms = {err:.2e} (tolerance {TOL_TRANSPOSED:.0e})")
     assert err <= TOL_TRANSPOSED
@@ -119,9 +117,13 @@ def test_transposed_is_adjoint_of_strided_on_gpu(name):
     xl.exchange()
     sq = hsc.st_plan_strided(xl.in_plan, wl.ksize, s, wl.cin)
     outs = [torch.empty(sq.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(sq.num_shards)]
-    # strided weight [taps][Cx][Cy]: W[o, c, t] is the weight from x channel c to y channel o
-    wt = torch.from_numpy(np.ascontiguousarray(np.moveaxis(w.reshape(wl.cin, wl.cout, -1), 2, 0).swapaxes(1, 2))).cuda()
-    hsc.st_conv_strided_sharded(xl.in_plan, xl.x_bufs, wt, None, wl.ksize, s, sq, outs)
+    # the strided conv from x (Cx channels) to y (Cy) takes W in conv order
+    # [out = Cy][in = Cx]: the same array; this fp32 layer gets its fp32
+    # values (torch widens the bf16 patterns exactly)
+    wd = dev_raw(w)
+    wd = wd.view(torch.bfloat16).float() if wl.dtype == "bf16" else wd
+    ws = dev_workspace(hsc.st_conv_strided_workspace_bytes(xl.in_plan, wl.cin, wl.ksize))
+    hsc.st_conv_strided_sharded(xl.in_plan, xl.x_bufs, wd, None, wl.ksize, s, sq, outs, ws)
     torch.cuda.synchronize()
     ys = gather_plan(sq, outs, wl.batch)
     yw = oracle.widen(y, wl.dtype)
