@@ -1216,7 +1216,6 @@ struct PairsCfg {
   // every stage ends in a zero block that stands for absent taps
   static_assert(WSTAGE - WROW >= 32, "room for the zero block");
   static constexpr int STEP_CHUNKS = TS * SLICE * 2;  // 16-byte pieces of a step's new planes
-  static constexpr int PRO_CHUNKS = RING * SLICE * 2;
   static constexpr int PF = (STEP_CHUNKS + NT - 1) / NT;
   static constexpr int PFH = PF / 2;                  // loads per half: slice rows 0-3, then rows 4-7
   static_assert(SH == 8 && STEP_CHUNKS == 2 * PFH * NT, "halves of whole slice rows");
@@ -1352,18 +1351,6 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     const int64_t rest = J.in_bytes - (int64_t)c0 * J.in_plane_b;
     return make_rsrc(J.in + (int64_t)c0 * J.in_plane_b, any ? (left < rest ? left : rest) : 0);
   };
-  // 16-byte piece u of a run of planes starting a0 planes after the
-  // descriptor's base: offset, or kOob outside the strip's padded rows and
-  // columns.  Step-invariant within a job (the descriptor moves instead).
-  auto piece_off = [&](const Job& J, int u, int lim, int a0) __attribute__((always_inline)) -> uint32_t {
-    const int rel = u / (C::SLICE * 2);
-    const int pc = u - rel * C::SLICE * 2;
-    const int q = pc >> 1, h = pc & 1;
-    const int qr = q / C::SW, qc = q - qr * C::SW;
-    const int gh = J.gh0 + qr, gw = J.gw0 + qc;
-    const bool ok = u < lim && gh < J.p1 && gw < J.p2;
-    return ok ? (uint32_t)(a0 + rel) * J.in_plane_b + (uint32_t)((gh * J.p2 + gw) * C::CIN * 2 + 16 * h) : kOob;
-  };
   // 16-byte piece u of a step's TS new planes, ordered (row, plane, column,
   // half) so that the first half of the pieces holds slice rows 0-3: those
   // rows of the ring are free once row 3 of the kernel is done, rows 4-7 only
@@ -1390,13 +1377,6 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     sl -= sl >= C::RING ? C::RING : 0;
     return sl * C::SLICE_B + (qr * C::SW + qc) * 32 + 16 * (h ^ ((qc >> 3) & 1));
   };
-  auto piece_lds = [&](int u, int a0) __attribute__((always_inline)) -> int {
-    const int rel = u / (C::SLICE * 2);
-    const int pc = u - rel * C::SLICE * 2;
-    const int q = pc >> 1, h = pc & 1;
-    const int qc = q % C::SW;
-    return ((a0 + rel) % C::RING) * C::SLICE_B + q * 32 + 16 * (h ^ ((qc >> 3) & 1));
-  };
   // weights of kernel row dy -> a stage, by LDS-DMA; packed [dy][dz][dx][cout][cin]
   auto fetch_w = [&](char* dst, int dy) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(reinterpret_cast<const char*>(args.w) + dy * C::WROW, C::WROW);
@@ -1414,23 +1394,38 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     }
   };
 
+  // a job's first RING planes -> ring slots 0 .. RING-1 by LDS-DMA: the ring
+  // is RING * SLICE_B = whole KiB, and transfer j of 1 KiB fills LDS bytes
+  // [j KiB, (j+1) KiB); each lane fetches the 16 bytes its position holds
+  // (the swizzled half of its cell), out-of-strip lanes read zeros
+  auto prologue = [&](const Job& Jb) __attribute__((always_inline)) {
+    static_assert(C::LDS_X % 1024 == 0, "ring in whole KiB");
+    constexpr int NCH = C::LDS_X / 1024;
+    const __amdgpu_buffer_rsrc_t rin0 = in_rsrc(Jb, 0);
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+#pragma unroll
+    for (int k = 0; k < (NCH + C::NWAVES - 1) / C::NWAVES; ++k) {
+      const int j = w + k * C::NWAVES;
+      if (j < NCH) {
+        const int p = 64 * j + lane;                  // 16-byte position in the ring
+        const int sl = p / (C::SLICE * 2), pc = p - sl * C::SLICE * 2;
+        const int q = pc >> 1, qr = q / C::SW, qc = q - qr * C::SW;
+        const int h = (pc & 1) ^ ((qc >> 3) & 1);
+        const int gh = Jb.gh0 + qr, gw = Jb.gw0 + qc;
+        const uint32_t off = (gh < Jb.p1 && gw < Jb.p2)
+                                 ? (uint32_t)sl * Jb.in_plane_b + (uint32_t)((gh * Jb.p2 + gw) * C::CB + 16 * h)
+                                 : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rin0, (lds_ptr)(sring + j * 1024), 16, off, 0, 0, 0);
+      }
+    }
+  };
+
   Job J = make_job(j0);
   if (!J.valid) return;
   fetch_w(sw0, 0);                                    // rows 0-2 of the first step; later rows are
   fetch_w(sw1, 1);                                    // fetched one or two rows ahead of their use
   fetch_w(sw2, 2);
-  {  // first job's first TS + k - 1 planes
-    const __amdgpu_buffer_rsrc_t rin0 = in_rsrc(J, 0);
-    constexpr int PRO = (C::PRO_CHUNKS + C::NT - 1) / C::NT;
-    uint4 v[PRO];
-#pragma unroll
-    for (int k = 0; k < PRO; ++k)
-      v[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                          rin0, piece_off(J, tid + k * C::NT, C::PRO_CHUNKS, 0), 0, 0));
-#pragma unroll
-    for (int k = 0; k < PRO; ++k)
-      if (tid + k * C::NT < C::PRO_CHUNKS) *reinterpret_cast<uint4*>(sring + piece_lds(tid + k * C::NT, 0)) = v[k];
-  }
+  prologue(J);                                        // first job's first TS + k - 1 planes
   __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
   if (MAXV) cur_n = J.n;
   __syncthreads();
@@ -1599,11 +1594,13 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     }
 
     if (more) {
-      // rows 4-7 of the fetched planes over the oldest TS
+      // rows 4-7 of the fetched planes over the oldest TS.  No barrier
+      // follows: until its first barrier the next step reads only slice
+      // rows 0-3 (wave w reads row w + dy, dy = 0), and every wave's writes
+      // are complete (lgkmcnt(0)) before that barrier.
 #pragma unroll
       for (int k = 0; k < C::PFH; ++k)
         *reinterpret_cast<uint4*>(sring + step_lds(tid + (C::PFH + k) * C::NT, base)) = pf[k];
-      __syncthreads();
       cur += C::TS;
     } else {
       job += jstride;
@@ -1617,16 +1614,10 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
       cur = 0;
 #pragma unroll
       for (int k = 0; k < C::PF; ++k) pfo[k] = step_off(J, tid + k * C::NT);
-      const __amdgpu_buffer_rsrc_t rin0 = in_rsrc(J, 0);
-      constexpr int PRO = (C::PRO_CHUNKS + C::NT - 1) / C::NT;
-      uint4 v[PRO];
-#pragma unroll
-      for (int k = 0; k < PRO; ++k)
-        v[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rin0, piece_off(J, tid + k * C::NT, C::PRO_CHUNKS, 0), 0, 0));
-#pragma unroll
-      for (int k = 0; k < PRO; ++k)
-        if (tid + k * C::NT < C::PRO_CHUNKS) *reinterpret_cast<uint4*>(sring + piece_lds(tid + k * C::NT, 0)) = v[k];
+      // the new job's first planes go over the whole ring (every wave is
+      // past the step's last reads: the barrier after the K loop)
+      prologue(J);
+      __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
       __syncthreads();
     }
   }
