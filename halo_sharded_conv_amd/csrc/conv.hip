@@ -84,32 +84,59 @@ struct DirectArgs {
   int32_t nshards, cin, cout, ks, taps, groups;
   int32_t origin[3];
   int64_t total_pos;
-  const void* w;            // [Cout][taps][Cin]
+  const float* w;           // [taps][Cin][Cout] fp32
   const float* bias;
   uint32_t* ymax;
   DirectShardArg sh[ST_MAX_SHARDS];
 };
 static_assert(sizeof(DirectArgs) <= kMaxKernargBytes, "kernel argument struct too large");
 
-__device__ __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
-__device__ __forceinline__ float ld(const uint16_t* p, size_t i) {
-  return __uint_as_float(((uint32_t)p[i]) << 16);
+// CV consecutive input channels of one cell as fp32 (one 16-byte load when CV > 1)
+template <typename T, int CV> __device__ __forceinline__ void ld_cells(const T* p, float (&x)[CV]);
+template <> __device__ __forceinline__ void ld_cells<float, 1>(const float* p, float (&x)[1]) { x[0] = *p; }
+template <> __device__ __forceinline__ void ld_cells<float, 4>(const float* p, float (&x)[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+template <> __device__ __forceinline__ void ld_cells<uint16_t, 1>(const uint16_t* p, float (&x)[1]) {
+  x[0] = __uint_as_float((uint32_t)*p << 16);
+}
+template <> __device__ __forceinline__ void ld_cells<uint16_t, 8>(const uint16_t* p, float (&x)[8]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(u[i] << 16);
+    x[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  }
 }
 
-template <typename T>
+// Direct kernel (fp32 operands, and bf16 shapes off the matrix-core grid): a
+// thread owns one output position and OB consecutive output channels, reads
+// CV input channels per load and the weights [taps][Cin][Cout] from LDS (WL)
+// or from L1/L2 (larger layers).  Each output sums its taps lexicographic,
+// channels ascending, one fp32 FMA at a time, whatever thread, tile or shard
+// computes it.
+template <typename T, int OB, int CV, bool WL>
 __global__ __launch_bounds__(256) void conv_direct(const DirectArgs a) {
-  extern __shared__ uint32_t dmax[];   // cout entries
+  extern __shared__ __attribute__((aligned(16))) float dsm[];   // [taps * cin * cout] (WL), then cout max slots
   const int tid = threadIdx.x;
+  const int wn = WL ? a.taps * a.cin * a.cout : 0;
+  uint32_t* dmax = reinterpret_cast<uint32_t*>(dsm + wn);
+  if (WL)
+    for (int i = tid; i < wn; i += 256) dsm[i] = a.w[i];
   for (int i = tid; i < a.cout; i += 256) dmax[i] = 0u;
   __syncthreads();
+  const float* wsrc = WL ? dsm : a.w;
+  const int ncb = a.cout / OB;
   const int64_t gid = (int64_t)blockIdx.x * 256 + tid;
-  // shard lookup is uniform per block only when a block does not straddle
-  // shards, so it is done per thread
-  if (gid < a.total_pos) {
+  const int64_t pos = gid / ncb;
+  const int ob0 = (int)(gid - pos * ncb) * OB;
+  if (pos < a.total_pos) {
     int s = 0;
-    while (s + 1 < a.nshards && a.sh[s + 1].pos_begin <= gid) ++s;
+    while (s + 1 < a.nshards && a.sh[s + 1].pos_begin <= pos) ++s;
     const DirectShardArg& sh = a.sh[s];
-    int64_t r = gid - sh.pos_begin;
+    int64_t r = pos - sh.pos_begin;
     const int64_t per_n = (int64_t)sh.ext[0] * sh.ext[1] * sh.ext[2];
     const int n = (int)(r / per_n);
     r -= n * per_n;
@@ -118,44 +145,55 @@ __global__ __launch_bounds__(256) void conv_direct(const DirectArgs a) {
     const int oh = (int)(r / sh.ext[2]);
     const int ow = (int)(r - (int64_t)oh * sh.ext[2]);
     const T* in = static_cast<const T*>(sh.in);
-    const T* w = static_cast<const T*>(a.w);
     const int kd_n = a.taps / (a.ks * a.ks);
-    const size_t cell_out = (((size_t)n * sh.ext[0] + od) * sh.ext[1] + oh) * sh.ext[2] + ow;
-    for (int o0 = 0; o0 < a.cout; o0 += 8) {
-      float acc[8];
+    float acc[OB];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-      for (int kd = 0; kd < kd_n; ++kd)
-        for (int kh = 0; kh < a.ks; ++kh)
-          for (int kw = 0; kw < a.ks; ++kw) {
-            const int t = (kd * a.ks + kh) * a.ks + kw;
-            const size_t cell = (((size_t)n * sh.pad[0] + od + kd + a.origin[0]) * sh.pad[1] +
-                                 oh + kh + a.origin[1]) * sh.pad[2] + ow + kw + a.origin[2];
-            for (int c = 0; c < a.cin; ++c) {
-              const float xv = ld(in, cell * a.cin + c);
+    for (int j = 0; j < OB; ++j) acc[j] = 0.f;
+    for (int kd = 0; kd < kd_n; ++kd)
+      for (int kh = 0; kh < a.ks; ++kh)
+        for (int kw = 0; kw < a.ks; ++kw) {
+          const int t = (kd * a.ks + kh) * a.ks + kw;
+          const size_t cell = (((size_t)n * sh.pad[0] + od + kd + a.origin[0]) * sh.pad[1] + oh + kh + a.origin[1]) *
+                                  sh.pad[2] + ow + kw + a.origin[2];
+          const T* xp = in + cell * a.cin;
+          const float* wt = wsrc + (size_t)t * a.cin * a.cout + ob0;
+          for (int c = 0; c < a.cin; c += CV) {
+            float xv[CV];
+            ld_cells<T, CV>(xp + c, xv);
 #pragma unroll
-              for (int j = 0; j < 8; ++j)
-                if (o0 + j < a.cout)
-                  acc[j] = fmaf(ld(w, ((size_t)(o0 + j) * a.taps + t) * a.cin + c), xv, acc[j]);
+            for (int v = 0; v < CV; ++v) {
+              const float* wc = wt + (size_t)(c + v) * a.cout;
+              if (OB == 4) {
+                const float4 w4 = *reinterpret_cast<const float4*>(wc);
+                acc[0] = fmaf(w4.x, xv[v], acc[0]);
+                acc[1] = fmaf(w4.y, xv[v], acc[1]);
+                acc[2] = fmaf(w4.z, xv[v], acc[2]);
+                acc[3] = fmaf(w4.w, xv[v], acc[3]);
+              } else {
+#pragma unroll
+                for (int j = 0; j < OB; ++j) acc[j] = fmaf(wc[j], xv[v], acc[j]);
+              }
             }
           }
+        }
+    const size_t cell_out = (((size_t)n * sh.ext[0] + od) * sh.ext[1] + oh) * sh.ext[2] + ow;
+    float* yp = sh.out + cell_out * a.cout + ob0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (o0 + j >= a.cout) break;
-        float v = acc[j];
-        if (a.bias) v += a.bias[o0 + j];
-        sh.out[cell_out * a.cout + o0 + j] = v;
-        if (a.ymax) atomicMax(&dmax[o0 + j], __float_as_uint(fabsf(v)));
-      }
+    for (int j = 0; j < OB; ++j) {
+      if (a.bias) acc[j] += a.bias[ob0 + j];
+      if (a.ymax) atomicMax(&dmax[ob0 + j], __float_as_uint(fabsf(acc[j])));
     }
+    if (OB == 4) *reinterpret_cast<float4*>(yp) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    else
+#pragma unroll
+      for (int j = 0; j < OB; ++j) yp[j] = acc[j];
   }
   if (!a.ymax) return;
   __syncthreads();
-  // one atomic per (block, group); the block may straddle two batch items or
-  // shards, so the batch index is resolved per position run below
-  const int64_t first = (int64_t)blockIdx.x * 256;
-  const int64_t last = min(first + 256, a.total_pos) - 1;
-  // batch item of the first and last position of the block
+  // one atomic per (block, group); a block may straddle two batch items or
+  // shards, so the batch index is resolved per position below
+  const int64_t first = (int64_t)blockIdx.x * 256 / ncb;
+  const int64_t last = min(((int64_t)blockIdx.x * 256 + 255) / ncb, a.total_pos - 1);
   auto batch_of = [&](int64_t g) {
     int s = 0;
     while (s + 1 < a.nshards && a.sh[s + 1].pos_begin <= g) ++s;
@@ -170,22 +208,50 @@ __global__ __launch_bounds__(256) void conv_direct(const DirectArgs a) {
       for (int c = g * gs; c < (g + 1) * gs; ++c) m = max(m, dmax[c]);
       atomicMax(&a.ymax[n0 * a.groups + g], m);
     }
+  } else if (pos < a.total_pos) {
+    // rare (a block spanning two batch items): attribute each output
+    // directly, from the values just stored by this thread
+    const int n = batch_of(pos);
+    int s = 0;
+    while (s + 1 < a.nshards && a.sh[s + 1].pos_begin <= pos) ++s;
+    const int64_t per_n = (int64_t)a.sh[s].ext[0] * a.sh[s].ext[1] * a.sh[s].ext[2];
+    const int64_t r = pos - a.sh[s].pos_begin - (int64_t)n * per_n;
+    const float* y = a.sh[s].out + (((size_t)n * per_n) + r) * a.cout + ob0;
+    for (int j = 0; j < OB; ++j) atomicMax(&a.ymax[n * a.groups + (ob0 + j) / gs], __float_as_uint(fabsf(y[j])));
   }
-  if (n0 != n1) {
-    // rare (a block spanning two batch items): attribute each position
-    // directly
-    __syncthreads();
-    if (gid < a.total_pos) {
-      const int n = batch_of(gid);
-      int s = 0;
-      while (s + 1 < a.nshards && a.sh[s + 1].pos_begin <= gid) ++s;
-      const int64_t per_n = (int64_t)a.sh[s].ext[0] * a.sh[s].ext[1] * a.sh[s].ext[2];
-      const int64_t r = gid - a.sh[s].pos_begin - (int64_t)n * per_n;
-      const float* y = a.sh[s].out + (((size_t)n * per_n) + r) * a.cout;
-      for (int c = 0; c < a.cout; ++c)
-        atomicMax(&a.ymax[n * a.groups + c / gs], __float_as_uint(fabsf(y[c])));
-    }
+}
+
+// max |y| per (n, group) over every shard's fp32 output, for the conv path
+// that does not fuse it (the matrix-core 'same' conv of shapes without a
+// tuned kernel).  blockIdx.y = shard * batch + n; a thread keeps the running
+// max of its 4 channels (cout % 4 == 0) over the positions it visits.
+struct YmaxArgs {
+  int32_t nshards, batch, cout, groups;
+  uint32_t* ymax;
+  const float* y[ST_MAX_SHARDS];
+  int64_t positions[ST_MAX_SHARDS];   // per sample
+};
+static_assert(sizeof(YmaxArgs) <= kMaxKernargBytes, "kernel argument struct too large");
+
+__global__ __launch_bounds__(256) void ymax_pass(const YmaxArgs a) {
+  const int s = blockIdx.y / a.batch, n = blockIdx.y - s * a.batch;
+  const int cq = a.cout / 4;
+  const int per_block = 256 / cq;                  // positions per block row
+  const int q = threadIdx.x % cq, pr = threadIdx.x / cq;
+  if (pr >= per_block) return;
+  const int64_t P = a.positions[s];
+  const float4* y = reinterpret_cast<const float4*>(a.y[s] + (size_t)n * P * a.cout);
+  float m[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t p = (int64_t)blockIdx.x * per_block + pr; p < P; p += (int64_t)gridDim.x * per_block) {
+    const float4 v = y[p * cq + q];
+    m[0] = fmaxf(m[0], fabsf(v.x));
+    m[1] = fmaxf(m[1], fabsf(v.y));
+    m[2] = fmaxf(m[2], fabsf(v.z));
+    m[3] = fmaxf(m[3], fabsf(v.w));
   }
+  const int gs = a.cout / a.groups;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) atomicMax(&a.ymax[n * a.groups + (4 * q + j) / gs], __float_as_uint(m[j]));
 }
 
 // --------------------------------------------------------------------------
@@ -263,17 +329,6 @@ __global__ void dgrad_weights(const T* __restrict__ w, T* __restrict__ out, int 
   out[i] = w[((int64_t)o * cin + c) * taps + (taps - 1 - t)];
 }
 
-template <typename T>
-__global__ void pack_w_direct(const T* __restrict__ w, T* __restrict__ out, int cin, int cout,
-                              int taps, int64_t total, uint32_t* clr, int nclr) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nclr) clr[i] = 0u;
-  if (i >= total) return;
-  const int c = (int)(i % cin);
-  const int t = (int)((i / cin) % taps);
-  const int o = (int)(i / ((int64_t)cin * taps));
-  out[i] = w[((int64_t)o * cin + c) * taps + t];
-}
 
 // --------------------------------------------------------------------------
 // helpers of the v_mfma_f32_32x32x16_bf16 kernels
@@ -1778,15 +1833,10 @@ st_status pack_weights(int ndim, int cin, int cout, int ksize, st_dtype dtype, c
                          clr, nclr);
       return launch_check(what.c_str());
     }
-    const int64_t total = (int64_t)cout * taps * cin;
-    hipLaunchKernelGGL(pack_w_direct<uint16_t>, grid(total), dim3(256), 0, st, w, out, cin, cout, taps, total, clr,
-                       nclr);
-    return launch_check(what.c_str());
   }
-  const int64_t total = (int64_t)cout * taps * cin;
-  hipLaunchKernelGGL(pack_w_direct<float>, grid(total), dim3(256), 0, st, static_cast<const float*>(weight),
-                     static_cast<float*>(packed), cin, cout, taps, total, clr, nclr);
-  return launch_check(what.c_str());
+  // every other shape (the matrix-core 'same' conv and the direct kernel):
+  // fp32 [taps][Cin][Cout]
+  return pack_tab_launch(weight, dtype, static_cast<float*>(packed), cin, cout, taps, false, clr, nclr, st, who);
 }
 
 // Host checks shared by the conv entry points; nothing is enqueued.
@@ -1846,6 +1896,35 @@ st_status conv_run(const st_plan* in_plan, const void* const* in_bufs, const voi
     return inst->run(a, in_plan, st);
   }
 
+  if (in_plan->dtype == ST_BF16 && cout <= 1024 && sx_same_fits(ndim, cin, cout, ksize)) {
+    // the matrix-core implicit GEMM of the strided conv at stride 1, then
+    // max |y| in a pass of its own
+    st_status s = sx_same_conv(in_plan, in_bufs, static_cast<const float*>(packed_weight), bias_or_null, cout, ksize,
+                               y_bufs, st);
+    if (s != ST_OK || !ymax_or_null) return s;
+    YmaxArgs m{};
+    m.nshards = (int)in_plan->shards.size();
+    m.batch = (int)in_plan->batch;
+    m.cout = cout;
+    m.groups = groups;
+    m.ymax = ymax_or_null;
+    int64_t most = 0;
+    for (size_t i = 0; i < in_plan->shards.size(); ++i) {
+      const Shard& sd = in_plan->shards[i];
+      m.y[i] = y_bufs[i];
+      m.positions[i] = sd.ext[0] * sd.ext[1] * sd.ext[2];
+      most = std::max(most, m.positions[i]);
+    }
+    const int per_block = 256 / (cout / 4);
+    const int64_t gx = std::min<int64_t>((most + per_block - 1) / per_block,
+                                         std::max<int64_t>(1, 4 * device_cus() / (m.nshards * m.batch)));
+    if (most == 0) return ST_OK;
+    if ((int64_t)m.nshards * m.batch > 65535) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: batch too large");
+    hipLaunchKernelGGL(ymax_pass, dim3((unsigned)std::max<int64_t>(1, gx), (unsigned)(m.nshards * m.batch)), dim3(256),
+                       0, st, m);
+    return launch_check("st_conv_sharded: max |y| launch");
+  }
+
   DirectArgs a{};
   a.nshards = (int)in_plan->shards.size();
   a.cin = cin;
@@ -1857,7 +1936,7 @@ st_status conv_run(const st_plan* in_plan, const void* const* in_bufs, const voi
     const bool real = ax >= kAxes - ndim;
     a.origin[ax] = real ? in_plan->halo[ax] - ksize / 2 : 0;
   }
-  a.w = packed_weight;
+  a.w = static_cast<const float*>(packed_weight);
   a.bias = bias_or_null;
   a.ymax = ymax_or_null;
   int64_t pos = 0;
@@ -1875,14 +1954,36 @@ st_status conv_run(const st_plan* in_plan, const void* const* in_bufs, const voi
   }
   a.total_pos = pos;
   if (pos == 0) return ST_OK;
-  const int64_t blocks = (pos + 255) / 256;
+  // a thread per (position, 4 output channels) when Cout allows; 16-byte
+  // input loads when Cin allows; weights in LDS when they fit
+  const int ob = cout % 4 == 0 ? 4 : 1;
+  const int64_t blocks = (pos * (cout / ob) + 255) / 256;
   if (blocks > INT32_MAX) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: volume too large for the direct kernel");
-  const size_t shmem = (size_t)cout * 4;
+  const size_t wbytes = (size_t)a.taps * cin * cout * 4;
+  const bool wl = wbytes + (size_t)cout * 4 <= 64 * 1024;
+  const size_t shmem = (wl ? wbytes : 0) + (size_t)cout * 4;
   if (shmem > 64 * 1024) return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: cout too large for the direct kernel");
-  if (in_plan->dtype == ST_F32)
-    hipLaunchKernelGGL(conv_direct<float>, dim3((unsigned)blocks), dim3(256), shmem, st, a);
-  else
-    hipLaunchKernelGGL(conv_direct<uint16_t>, dim3((unsigned)blocks), dim3(256), shmem, st, a);
+  const bool bf = in_plan->dtype == ST_BF16;
+  const bool vec = bf ? cin % 8 == 0 : cin % 4 == 0;
+  const dim3 gd((unsigned)blocks), bd(256);
+#define ST_DIRECT(T_, CV_)                                                                              \
+  do {                                                                                                  \
+    if (ob == 4) {                                                                                      \
+      if (wl) hipLaunchKernelGGL((conv_direct<T_, 4, CV_, true>), gd, bd, shmem, st, a);                  \
+      else hipLaunchKernelGGL((conv_direct<T_, 4, CV_, false>), gd, bd, shmem, st, a);                    \
+    } else {                                                                                            \
+      if (wl) hipLaunchKernelGGL((conv_direct<T_, 1, CV_, true>), gd, bd, shmem, st, a);                  \
+      else hipLaunchKernelGGL((conv_direct<T_, 1, CV_, false>), gd, bd, shmem, st, a);                    \
+    }                                                                                                   \
+  } while (0)
+  if (bf) {
+    if (vec) ST_DIRECT(uint16_t, 8);
+    else ST_DIRECT(uint16_t, 1);
+  } else {
+    if (vec) ST_DIRECT(float, 4);
+    else ST_DIRECT(float, 1);
+  }
+#undef ST_DIRECT
   return launch_check("st_conv_sharded: conv_direct launch");
 }
 
@@ -1897,11 +1998,9 @@ size_t st_conv_weight_bytes(int32_t ndim, int32_t cin, int32_t cout, int32_t ksi
   if ((ndim != 2 && ndim != 3) || cin < 1 || cout < 1 || ksize < 1 || ksize % 2 == 0) return 0;
   if (dtype != ST_F32 && dtype != ST_BF16) return 0;
   const int64_t taps = taps_of(ndim, ksize);
-  if (dtype == ST_BF16) {
-    if (const Instance* i = find_instance(ndim, cin, cout, ksize))
-      return (size_t)(cin / i->ck) * cout * i->kvp * 2;
-    return (size_t)cout * taps * cin * 2;
-  }
+  if (dtype == ST_BF16)
+    if (const Instance* i = find_instance(ndim, cin, cout, ksize)) return (size_t)(cin / i->ck) * cout * i->kvp * 2;
+  // every other shape: fp32 [taps][Cin][Cout]
   return (size_t)cout * taps * cin * 4;
 }
 

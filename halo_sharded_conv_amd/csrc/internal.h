@@ -93,6 +93,19 @@ constexpr int64_t kHaloWordsPerBlock = kHaloThreads * kHaloWordsPerThread;
 // passes, at any shard count, so the GPU tests exercise the full sizes.
 constexpr size_t kMaxKernargBytes = 12 * 1024;
 
+// Weights [B][A][taps] (a_major false: [Cout][Cin], PyTorch's conv order) or
+// [A][B][taps] (a_major true) in `dtype` -> fp32 [taps][A][B]; the same
+// launch zeroes clr[0, nclr).  (strided.hip)
+st_status pack_tab_launch(const void* weight, st_dtype dtype, float* out, int a_ch, int b_ch, int taps, bool a_major,
+                          uint32_t* clr, int nclr, hipStream_t st, const char* who);
+// The stride-1 'same' conv of bf16 shards on the matrix cores (strided.hip's
+// implicit GEMM at stride 1) for shapes without a tuned kernel: Cin % 16 ==
+// 0, Cout % 16 == 0 and one channel block of weights within LDS.  Weights
+// fp32 [taps][Cin][Cout] (bf16 values); y unpadded channels-last fp32.
+bool sx_same_fits(int ndim, int cin, int cout, int ksize);
+st_status sx_same_conv(const st_plan* in_plan, const void* const* in_bufs, const float* w_tco, const float* bias,
+                       int cout, int ksize, float* const* y_bufs, hipStream_t st);
+
 // Uploads the descriptor table on first use (on the current device).
 st_status plan_device_table(st_plan* p, hipStream_t stream);
 // Public axis a of an ndim plan maps to internal axis a + (3 - ndim).

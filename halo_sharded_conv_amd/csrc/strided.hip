@@ -570,8 +570,9 @@ bool strided_sizes(const std::vector<int64_t>& in, int64_t k, int64_t s, std::ve
 // order).
 template <typename T>
 __global__ void pack_w_tab(const T* __restrict__ w, float* __restrict__ out, int a_ch, int b_ch, int taps,
-                           int a_major, int64_t total) {
+                           int a_major, int64_t total, uint32_t* clr, int nclr) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nclr) clr[i] = 0u;                        // e.g. the max |y| of the conv that follows
   if (i >= total) return;
   const int j = (int)(i % b_ch);
   const int64_t r = i / b_ch;
@@ -602,17 +603,64 @@ st_status pack_tab(const st_plan* in_plan, int32_t cout, int32_t ksize, const vo
   for (int a = 0; a < in_plan->ndim; ++a) taps *= ksize;
   const int a_ch = (int)in_plan->channels;
   const int64_t total = (int64_t)taps * a_ch * cout;
-  const dim3 gd((unsigned)((total + 255) / 256)), bd(256);
-  if (in_plan->dtype == ST_BF16)
-    hipLaunchKernelGGL(pack_w_tab<uint16_t>, gd, bd, 0, st, static_cast<const uint16_t*>(weight),
-                       static_cast<float*>(workspace), a_ch, (int)cout, taps, a_major ? 1 : 0, total);
-  else
-    hipLaunchKernelGGL(pack_w_tab<float>, gd, bd, 0, st, static_cast<const float*>(weight),
-                       static_cast<float*>(workspace), a_ch, (int)cout, taps, a_major ? 1 : 0, total);
-  return launch_check((std::string(who) + ": weight packing launch").c_str());
+  return pack_tab_launch(weight, in_plan->dtype, static_cast<float*>(workspace), a_ch, (int)cout, taps, a_major,
+                         nullptr, 0, st, who);
 }
 
 }  // namespace
+
+st_status pack_tab_launch(const void* weight, st_dtype dtype, float* out, int a_ch, int b_ch, int taps, bool a_major,
+                          uint32_t* clr, int nclr, hipStream_t st, const char* who) {
+  const int64_t total = (int64_t)taps * a_ch * b_ch;
+  const dim3 gd((unsigned)((std::max<int64_t>(total, nclr) + 255) / 256)), bd(256);
+  if (dtype == ST_BF16)
+    hipLaunchKernelGGL(pack_w_tab<uint16_t>, gd, bd, 0, st, static_cast<const uint16_t*>(weight), out, a_ch, b_ch,
+                       taps, a_major ? 1 : 0, total, clr, nclr);
+  else
+    hipLaunchKernelGGL(pack_w_tab<float>, gd, bd, 0, st, static_cast<const float*>(weight), out, a_ch, b_ch, taps,
+                       a_major ? 1 : 0, total, clr, nclr);
+  return launch_check((std::string(who) + ": weight packing launch").c_str());
+}
+
+bool sx_same_fits(int ndim, int cin, int cout, int ksize) {
+  if (cin % 16 != 0 || cout % 16 != 0 || ksize < 1 || ksize % 2 == 0) return false;
+  const int taps = ndim == 3 ? ksize * ksize * ksize : ksize * ksize;
+  const int fr = kSxPrefer16 && cin % 32 == 0 ? 16 : 32;
+  return (int64_t)taps * cin * fr * 2 <= kSxCapLarge;     // one FR-channel block of weights in LDS
+}
+
+st_status sx_same_conv(const st_plan* in_plan, const void* const* in_bufs, const float* w_tco, const float* bias,
+                       int cout, int ksize, float* const* y_bufs, hipStream_t st) {
+  const int p = ksize / 2;
+  const int cin = (int)in_plan->channels;
+  SxShard sx[ST_MAX_SHARDS];
+  for (size_t i = 0; i < in_plan->shards.size(); ++i) {
+    const Shard& si = in_plan->shards[i];
+    SxShard& q = sx[i];
+    q = SxShard{};
+    q.is[2] = cin;
+    q.is[1] = si.pad[2] * cin;
+    q.is[0] = si.pad[1] * q.is[1];
+    q.isn = si.pad[0] * q.is[0];
+    q.os[2] = cout;
+    q.os[1] = si.ext[2] * cout;
+    q.os[0] = si.ext[1] * q.os[1];
+    q.osn = si.ext[0] * q.os[0];
+    int64_t in_off = 0;
+    for (int ax = 0; ax < kAxes; ++ax) {
+      const bool sp = ax >= kAxes - in_plan->ndim;
+      in_off += (sp ? in_plan->halo[ax] - p : 0) * q.is[ax];
+      q.ext[ax] = (int32_t)si.ext[ax];
+    }
+    q.in = static_cast<const uint16_t*>(in_bufs[i]) + in_off;
+    q.out = y_bufs[i];
+  }
+  if (!launch_sx_mfma<false>(sx, (int)in_plan->shards.size(), (int)in_plan->batch, cin, cout, ksize, 1,
+                             in_plan->ndim, w_tco, bias, st))
+    return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: shape does not fit the matrix-core 'same' conv");
+  return launch_check("st_conv_sharded: conv_sx_mfma launch");
+}
+
 }  // namespace st
 
 using namespace st;

@@ -196,6 +196,23 @@ class ShardedConvGN:
             out[self._global_slices(i)] = self.out_view(bufs, i).cpu().numpy()
         return out
 
+    def gather_rows(self, bufs, r0: int, r1: int) -> np.ndarray:
+        """Rows [r0, r1) of the outermost spatial axis of an output tensor,
+        assembled from the shards that hold them: [N, r1 - r0, *rest, Cout]."""
+        cfg = self.cfg
+        out = np.empty((cfg.batch, r1 - r0, *cfg.spatial[1:], cfg.cout), np.float32)
+        for i in range(self.S):
+            inf = self.info[i]
+            o0, e0 = inf["offset"][0], inf["extent"][0]
+            a, b = max(r0, o0), min(r1, o0 + e0)
+            if a >= b:
+                continue
+            part = self.out_view(bufs, i)[:, a - o0:b - o0].cpu().numpy()
+            sl = [slice(None), slice(a - r0, b - r0)] + [slice(o, o + e) for o, e in
+                                                         zip(inf["offset"][1:], inf["extent"][1:])]
+            out[tuple(sl)] = part
+        return out
+
     def y_host(self) -> np.ndarray:
         return self.gather(self.y_bufs)
 

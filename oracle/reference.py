@@ -165,19 +165,22 @@ def conv_same_wgrad(x: np.ndarray, dy: np.ndarray, k: int) -> np.ndarray:
     return dw
 
 
-def conv_same_slabbed(x_src, dtype: str, w: np.ndarray, bias=None, slab: int = 8):
+def conv_same_slabbed(x_src, dtype: str, w: np.ndarray, bias=None, slab: int = 8, start: int = 0,
+                      stop=None):
     """conv_same evaluated one slab of the outermost spatial axis at a time.
 
     x_src is the (possibly bf16-bit) channels-last input; each output slab is
     the same definition restricted to those output positions, computed from
     the input rows it needs (zeros outside the volume).  Yields
-    (start, y_slab).  This only bounds memory for the largest volumes.
+    (start, y_slab) for the output rows [start, stop) of that axis (default:
+    all of them).  This only bounds memory for the largest volumes.
     """
     k = w.shape[2]
     p = (k - 1) // 2
     n0 = x_src.shape[1]
-    for s0 in range(0, n0, slab):
-        s1 = min(n0, s0 + slab)
+    stop = n0 if stop is None else min(n0, stop)
+    for s0 in range(start, stop, slab):
+        s1 = min(stop, s0 + slab)
         lo, hi = s0 - p, s1 + p
         part = widen(x_src[:, max(0, lo):min(n0, hi)], dtype)
         pad_lo, pad_hi = max(0, -lo), max(0, hi - n0)

@@ -45,13 +45,23 @@ def small_cases():
 
 
 def direct_cases():
-    """bf16 shapes without a matrix-core instance (direct kernel)."""
+    """bf16 shapes without a tuned kernel: channel counts off the matrix-core
+    grid (the direct kernel) and on it (the matrix-core implicit GEMM of the
+    strided conv at stride 1, with max |y| in a pass of its own)."""
     base = synth.WORKLOADS["img2048_c64_k3_bf16"]
+    vol = synth.WORKLOADS["vol512_c16_k5_bf16"]
     a = dataclasses.replace(base, name="img_c5to12_k3", cin=5, cout=12, groups=3, spatial=(13, 17),
                             shards=((6, 7), (9, 8)))
-    b = dataclasses.replace(synth.WORKLOADS["vol512_c16_k5_bf16"], name="vol_c3to4_k5", cin=3, cout=4,
+    b = dataclasses.replace(vol, name="vol_c3to4_k5", cin=3, cout=4,
                             groups=2, spatial=(7, 8, 9), shards=((3, 4), (8,), (2, 7)))
-    return {"img_c5to12_k3": a, "vol_c3to4_k5": b}
+    c = dataclasses.replace(base, name="img_c48to80_k3", cin=48, cout=80, groups=5, spatial=(19, 70),
+                            shards=((7, 12), (33, 37)), batch=2)
+    d = dataclasses.replace(synth.WORKLOADS["vol256_c32_k3_bf16"], name="vol_c128to128_k3", cin=128, cout=128,
+                            groups=8, spatial=(9, 10, 11), shards=((4, 5), (10,), (6, 5)))
+    e = dataclasses.replace(base, name="img_c32to48_k5", cin=32, cout=48, groups=3, ksize=5, spatial=(17, 40),
+                            shards=((8, 9), (21, 19)))
+    return {"img_c5to12_k3": a, "vol_c3to4_k5": b, "img_c48to80_k3": c, "vol_c128to128_k3": d,
+            "img_c32to48_k5": e}
 
 
 def oracle_forward(wl, x, w, bias=None, gamma=None, beta=None):

@@ -1,6 +1,7 @@
-"""The backward step and the pooled downsampling at full size, in the launch
-configuration the benchmark times (the image workload, 1x64x2048x2048 bf16
-on four uneven H shards).
+"""The backward step and the shape-changing ops at full size, in the launch
+configuration the benchmark times, on the image workload (1x64x2048x2048
+bf16 on four uneven H shards) and on the 256^3 volume (1x32x256^3 bf16 on a
+2 x 2 x 2 grid of uneven shards: faces, edges and corners).
 
 Backward chain as `bench.py --pass backward` runs it: the sharded forward
 step, GroupNorm backward writing bf16 dy straight into the input-gradient
@@ -15,8 +16,8 @@ read back), so each error belongs to one stage:
     bound) and the derived output shard sizes vs oracle.pooled_shard_sizes;
   * the stride-2 conv of the input vs oracle.conv_strided over the whole
     output (1e-5), with the derived shard sizes;
-  * the stride-2 transposed conv from half resolution vs
-    oracle.conv_transposed over the whole 2048 x 2048 output (1e-5).
+  * the stride-2 transposed conv from half resolution (every shard halved)
+    vs oracle.conv_transposed over the whole output (1e-5).
 """
 import numpy as np
 import pytest
@@ -30,10 +31,11 @@ from helpers import TOL, bits_equal, dev_raw, dev_workspace, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
-NAME = "img2048_c64_k3_bf16"
+NAMES = ["img2048_c64_k3_bf16", "vol256_c32_k3_bf16"]
 
 
-def test_full_size_backward_chain():
+@pytest.mark.parametrize("NAME", NAMES)
+def test_full_size_backward_chain(NAME):
     wl = synth.workload(NAME)
     say(f"full-size backward {NAME}: inputs")
     x, w = synth.make_input(wl), synth.make_weight(wl)
@@ -83,7 +85,8 @@ def test_full_size_backward_chain():
     assert e_dx <= TOL[wl.dtype] and e_dw <= TOL[wl.dtype]
 
 
-def test_full_size_pooling():
+@pytest.mark.parametrize("NAME", NAMES)
+def test_full_size_pooling(NAME):
     wl = synth.workload(NAME)
     say(f"full-size 2x average pooling {NAME}")
     x = synth.make_input(wl)
@@ -110,7 +113,8 @@ def test_full_size_pooling():
     assert excess.max() <= 0.0
 
 
-def test_full_size_strided_conv():
+@pytest.mark.parametrize("NAME", NAMES)
+def test_full_size_strided_conv(NAME):
     wl = synth.workload(NAME)
     say(f"full-size stride-2 conv {NAME}")
     x, w = synth.make_input(wl), synth.make_weight(wl)
@@ -135,21 +139,31 @@ def test_full_size_strided_conv():
     assert err <= 1e-5
 
 
-def test_full_size_transposed_conv():
-    """The bench's upsampling workload: the image workload at half resolution
-    (every shard halved) up to 2048 x 2048 with the layer's sharding shapes,
+def half_shards(sizes):
+    """Per-axis shard sizes of a half-resolution input: every shard halved
+    (rounded down), the last one taking the rest."""
+    n = sum(sizes) // 2
+    head = [e // 2 for e in sizes[:-1]]
+    return tuple(head + [n - sum(head)])
+
+
+@pytest.mark.parametrize("NAME", NAMES)
+def test_full_size_transposed_conv(NAME):
+    """The bench's upsampling workload: the layer at half resolution (every
+    shard halved) up to full size (the image workload's sharding shapes; on
+    the 256^3 grid, whose extents are odd, the halved shards times two),
     bias included, over the whole output."""
     import dataclasses
     wl_out = synth.workload(NAME)
     wl = dataclasses.replace(wl_out, name=wl_out.name + "_half", spatial=tuple(n // 2 for n in wl_out.spatial),
-                             shards=tuple(tuple(e // 2 for e in a) for a in wl_out.shards))
-    say(f"full-size stride-2 transposed conv {wl.name} -> {NAME}")
+                             shards=tuple(half_shards(a) for a in wl_out.shards))
+    say(f"full-size stride-2 transposed conv {wl.name} {wl.shards} -> {NAME}")
     y, w = synth.make_input(wl), synth.make_weight(wl)
     layer = ShardedConvGN(wl)
     layer.load_input(y)
     layer.exchange()
     q = hsc.st_plan_transposed(layer.in_plan, wl.ksize, 2, wl.cout)
-    assert q.shards == tuple(tuple(a) for a in wl_out.shards)
+    assert q.shards == tuple(tuple(2 * e for e in a) for a in wl.shards)
     wtr = np.ascontiguousarray(np.swapaxes(w, 0, 1))                # W [in = Cin][out = Cout][k..], raw bits
     bias = np.random.default_rng(7).uniform(-1, 1, wl.cout).astype(np.float32)
     outs = [torch.empty(q.shard_info(i)["elems"], dtype=torch.float32, device="cuda") for i in range(q.num_shards)]

@@ -616,6 +616,11 @@ def test_slabbed_conv_matches_full_conv():
         y = oracle.conv_same(oracle.widen(x, "bf16"), w)
         parts = [ys for _, ys in oracle.conv_same_slabbed(x, "bf16", w, None, slab=3)]
         assert np.array_equal(np.concatenate(parts, axis=1), y)
+        # a row range: exactly those rows of the full conv, boundary rows included
+        for lo, hi in [(0, 2), (4, 9), (9, 11), (10, 30)]:
+            got = [(s0, ys) for s0, ys in oracle.conv_same_slabbed(x, "bf16", w, None, slab=2, start=lo, stop=hi)]
+            assert got[0][0] == lo
+            assert np.array_equal(np.concatenate([ys for _, ys in got], axis=1), y[:, lo:min(hi, sp[0])])
 
 
 # ------------------------------------------------------------ halo reference
