@@ -341,8 +341,28 @@ __global__ void dgrad_weights(const T* __restrict__ w, T* __restrict__ out, int 
 //
 // Output layout of a 32x32 block in a lane: column (position) = lane % 32,
 // rows (channels) 8j + 4*(lane/32) + i for accumulator element 4j + i.
+//
+// Stores of conv_rows and conv_pairs: the quads j = 2c and 2c + 1 of a block
+// (channels 16c .. 16c + 15) go out as one pair.  Stored as they are (as
+// conv_gemm does: its epilogue is a small part of a tile, and the swap's
+// extra registers made it spill), each store instruction would
+// write 32 bytes into each of 32 cells; swap16 first trades the odd 16-lane
+// rows of the first quad with the even rows of the second (one
+// v_permlane16_swap per element), after which lane 16 r + t holds channels
+// 16c + 4 SWAP_QUAD(r) .. + 3 of position t (first quad) and of position
+// 16 + t (second quad), so each instruction writes 16 whole 64-byte runs.
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define SWAP_QUAD(r) ((((r) & 1) << 1) | ((r) >> 1))
+
+__device__ __forceinline__ void swap16(f32x4& x, f32x4& y) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[i]), __float_as_uint(y[i]), false, false);
+    x[i] = __uint_as_float(r[0]);
+    y[i] = __uint_as_float(r[1]);
+  }
+}
 constexpr uint32_t kOob = 0x80000000u;        // offset beyond every num_records used
 constexpr uint32_t kBufFlags = 0x00020000u;   // raw buffer, 32-bit data format
 
@@ -678,34 +698,50 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NT / 2
       }
     };
 
-    // epilogue pieces: output row t, channel block mb, channel quad jj
+    // epilogue pairs: output row t, channel block mb, channel half jp (quads
+    // 2 jp and 2 jp + 1), stored after swap16 as 16 positions each
     const int oh = C::NDIM == 3 ? J.h0 + ph : 0;
     const int ow = J.w0 + pw;
-    const bool in_plane = (C::NDIM == 2 || oh < J.e1) && ow < J.e2;
-    auto store_piece = [&](int t, int mb, int jj) __attribute__((always_inline)) {
+    const bool row_in = C::NDIM == 2 || oh < J.e1;
+    const bool in_plane = row_in && ow < J.e2;          // this lane's position before the swap
+    const int t16 = lane & 15;
+    const int owx = ow - l32 + t16;                    // positions after the swap: owx, owx + 16
+    const bool okx_plane = row_in && owx < J.e2, oky_plane = row_in && owx + 16 < J.e2;
+    const int co_sw = 4 * SWAP_QUAD(lane >> 4);
+    auto store_pair = [&](int t, int mb, int jp) __attribute__((always_inline)) {
       const int osl = cur + t0 + t;
-      const bool ok = in_plane && osl < J.s_end;
-      const int64_t cell = (int64_t)(osl - J.s_begin) * J.out_cells + (C::NDIM == 3 ? (int64_t)oh * J.e2 : 0) + ow;
-      const uint32_t cbase = ok ? (uint32_t)((cell * C::COUT + co_lane) * 4) : kOob;
-      const int co = mb * 32 + 8 * jj;                // relative to co_lane
-      f32x4 v;
+      const bool live = osl < J.s_end;
+      const bool ok = in_plane && live;
+      const int64_t row_cell = (int64_t)(osl - J.s_begin) * J.out_cells + (C::NDIM == 3 ? (int64_t)oh * J.e2 : 0);
+      f32x4 v[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = acc[t][mb][4 * jj + i];
-      if (BIAS) {
-        const float4 bv4 = *reinterpret_cast<const float4*>(&sbias[co_lane + co]);
-        v[0] += bv4.x; v[1] += bv4.y; v[2] += bv4.z; v[3] += bv4.w;
-      }
-      __builtin_amdgcn_raw_buffer_store_b128(v, J.rout, cbase + (uint32_t)(co * 4), 0, 0);
-      if (MAXV) {
+      for (int h = 0; h < 2; ++h) {
+        const int jj = 2 * jp + h;
+        const int co = mb * 32 + 8 * jj;              // relative to co_lane
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          runmax[mb][(4 * jj + i) / MG] = fmaxf(runmax[mb][(4 * jj + i) / MG], ok ? fabsf(v[i]) : 0.f);
+        for (int i = 0; i < 4; ++i) v[h][i] = acc[t][mb][4 * jj + i];
+        if (BIAS) {
+          const float4 bv4 = *reinterpret_cast<const float4*>(&sbias[co_lane + co]);
+          v[h][0] += bv4.x; v[h][1] += bv4.y; v[h][2] += bv4.z; v[h][3] += bv4.w;
+        }
+        if (MAXV) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            runmax[mb][(4 * jj + i) / MG] = fmaxf(runmax[mb][(4 * jj + i) / MG], ok ? fabsf(v[h][i]) : 0.f);
+        }
       }
+      swap16(v[0], v[1]);
+      const uint32_t cx = (uint32_t)(((row_cell + owx) * C::COUT + co_sw) * 4);
+      const uint32_t co4 = (uint32_t)((mb * 32 + 16 * jp) * 4);       // kOob + co4 stays out of range
+      const uint32_t ox = live && okx_plane ? cx : kOob;
+      const uint32_t oy = live && oky_plane ? cx + 16 * C::COUT * 4 : kOob;
+      __builtin_amdgcn_raw_buffer_store_b128(v[0], J.rout, ox + co4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v[1], J.rout, oy + co4, 0, 0);
     };
-    constexpr int NST = C::RW * MH * 4;               // stores of one pass
+    constexpr int NSP = C::RW * MH * 2;               // store pairs of one pass
     auto store_pass = [&](int hh, int q0, int q1) __attribute__((always_inline)) {
 #pragma unroll
-      for (int q = q0; q < q1; ++q) store_piece(q / (MH * 4), hh * MH + (q / 4) % MH, q % 4);
+      for (int q = q0; q < q1; ++q) store_pair(q / (MH * 2), hh * MH + (q / 2) % MH, q % 2);
     };
 
     bf16x8 av[2][C::KS][MH], bv[2][C::NIN];
@@ -728,7 +764,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NT / 2
 #pragma unroll
         for (int k = i * C::PF / PF_CHUNKS; k < (i + 1) * C::PF / PF_CHUNKS; ++k) issue_pf(k);
       }
-      if (hh > 0) store_pass(hh - 1, i * NST / NK, (i + 1) * NST / NK);
+      if (hh > 0) store_pass(hh - 1, i * NSP / NK, (i + 1) * NSP / NK);
       if (ii + 1 < NKT) load_ops(ii + 1, av[cb ^ 1], bv[cb ^ 1]);
 #pragma unroll
       for (int tr = 0; tr < C::KS; ++tr)
@@ -741,7 +777,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NT / 2
       // interleave: the next chunk's reads (and the previous pass's stores)
       // spread over this chunk's MFMAs
       if (ii + 1 < NKT) {
-        const int nst = hh > 0 ? (i + 1) * NST / NK - i * NST / NK : 0;
+        const int nst = hh > 0 ? 2 * ((i + 1) * NSP / NK - i * NSP / NK) : 0;
 #pragma unroll
         for (int g = 0; g < NRD; ++g) {
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // one LDS read
@@ -757,7 +793,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NT / 2
     }
 
     // 3. the last pass's results: bias, range-checked fp32 stores, running max
-    store_pass(NH - 1, 0, NST);
+    store_pass(NH - 1, 0, NSP);
 
     // 4. every wave is done with the ring: the fetched slices replace the TS
     // oldest ones (or the whole ring for the next job)
@@ -1616,35 +1652,49 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     fetch_w(sw1, 1);
 
     // epilogue: pair q covers planes cur + 2q (rows 0-15) and cur + 2q + 1;
-    // planes past the shard fall outside the output descriptor's range
+    // planes past the shard fall outside the output descriptor's range.
+    // Bias and the running max are taken in the MFMA layout, then swap16
+    // turns each plane's two channel quads into two stores of 16 whole
+    // 64-byte cells (1 KiB in a row).
     {
-      const int oh = J.h0 + w, ow = J.w0 + l32;
-      const bool in_plane = oh < J.e1 && ow < J.e2;
-      const int64_t cell = (int64_t)oh * J.e2 + ow;
+      const int oh = J.h0 + w;
+      const int64_t row_cell = (int64_t)oh * J.e2 + J.w0;
+      const bool row_in = oh < J.e1;
+      const bool in_plane = row_in && J.w0 + l32 < J.e2;      // this lane's position before the swap
+      const int t16 = lane & 15, r16 = lane >> 4;
+      const int sch = SWAP_QUAD(r16);                       // channel quad after the swap
+      const bool okx = row_in && J.w0 + t16 < J.e2;
+      const bool oky = row_in && J.w0 + 16 + t16 < J.e2;
 #pragma unroll
       for (int q = 0; q < C::NPAIR; ++q)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int plane = cur + 2 * q + (jj >> 1);
-          const bool ok = in_plane;                   // planes past the shard: dropped by the range
+        for (int p = 0; p < 2; ++p) {
+          const int plane = cur + 2 * q + p;
           const bool real = in_plane && plane < J.depth;
-          const int co = 8 * (jj & 1) + 4 * g2;
-          const uint32_t off = ok ? (uint32_t)((plane - cur) * J.out_plane_b + (cell * C::COUT + co) * 4) : kOob;
-          f32x4 v;
+          f32x4 v[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = acc[q][4 * jj + i];
-          if (BIAS) {
-            const float4 b4 = *reinterpret_cast<const float4*>(&sbias[co]);
-            v[0] += b4.x; v[1] += b4.y; v[2] += b4.z; v[3] += b4.w;
-          }
-          __builtin_amdgcn_raw_buffer_store_b128(v, rout, off, 0, 0);
-          if (MAXV) {
+          for (int h = 0; h < 2; ++h) {
+            const int co = 8 * h + 4 * g2;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int slot = (4 * (jj & 1) + i) / MG;
-              runmax[slot] = fmaxf(runmax[slot], real ? fabsf(v[i]) : 0.f);
+            for (int i = 0; i < 4; ++i) v[h][i] = acc[q][8 * p + 4 * h + i];
+            if (BIAS) {
+              const float4 b4 = *reinterpret_cast<const float4*>(&sbias[co]);
+              v[h][0] += b4.x; v[h][1] += b4.y; v[h][2] += b4.z; v[h][3] += b4.w;
+            }
+            if (MAXV) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int slot = (4 * h + i) / MG;
+                runmax[slot] = fmaxf(runmax[slot], real ? fabsf(v[h][i]) : 0.f);
+              }
             }
           }
+          swap16(v[0], v[1]);
+          const uint32_t pb = (uint32_t)(plane - cur) * J.out_plane_b + (uint32_t)(sch * 16);
+          const uint32_t offx = okx ? pb + (uint32_t)((row_cell + t16) * (C::COUT * 4)) : kOob;
+          const uint32_t offy = oky ? pb + (uint32_t)((row_cell + 16 + t16) * (C::COUT * 4)) : kOob;
+          __builtin_amdgcn_raw_buffer_store_b128(v[0], rout, offx, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(v[1], rout, offy, 0, 0);
         }
     }
 
