@@ -195,14 +195,18 @@ def algorithmic(wl, layer):
     vox = wl.voxels
     x_bytes = vox * wl.cin * esize
     y_bytes = vox * wl.cout * 4
-    payload = layer.in_plan.msg_bytes
+    plan = layer.in_plan
+    payload = plan.msg_bytes
+    # zeros written into the margins on the global faces (the conv's padding)
+    zero_bytes = 0
+    for i in range(plan.num_halo_boxes, plan.num_halo_boxes + plan.num_zero_boxes):
+        zero_bytes += plan.batch * int(np.prod(plan.halo_box(i)["ext"])) * wl.cin * esize
     return {
         "halo_pack": {"bytes": 2 * payload},                 # read boxes, write message
-        "halo_unpack": {"bytes": 2 * payload},               # read message, write margins
-        "halo_exchange": {"bytes": 2 * payload},             # read boxes, write margins
+        "halo_unpack": {"bytes": 2 * payload + zero_bytes},  # read message, write margins and zero faces
+        "halo_exchange": {"bytes": 2 * payload + zero_bytes},   # read boxes, write margins and zero faces
         "conv": {"bytes": x_bytes + y_bytes, "flops": wl.conv_flops},
         "gn_partials": {"bytes": y_bytes},
-        "gn_combine": {"bytes": 0},
         "gn_apply": {"bytes": 2 * y_bytes},
         # max |dz|, then (y, dz) for the sums, then (y, dz) -> dy in the conv's operand type
         "gn_backward": {"bytes": 5 * y_bytes + vox * wl.cout * esize},
@@ -355,8 +359,7 @@ def bench_layer(args, wl_fwd, cold, cpu):
         halo = [("halo_pack", lambda: layer.exchange_pack()), ("halo_unpack", lambda: layer.exchange_unpack())]
     stages = halo + [("conv", layer.conv)]
     if args.pass_ == "forward":
-        stages += [("gn_partials", layer.norm_partials), ("gn_combine", layer.norm_combine),
-                   ("gn_apply", layer.norm_apply)]
+        stages += [("gn_partials", layer.norm_partials), ("gn_apply", layer.norm_combine_apply)]
 
     per_kernel_ms, ms_per_step, gpu_ms = time_stages(args, stages, stream)
     eager_ms = ms_per_step

@@ -111,6 +111,7 @@ def _load() -> ctypes.CDLL:
         "st_groupnorm_partials": (I32, [P, PP, P, I32, P, SZ, P]),
         "st_groupnorm_combine": (I32, [P, I32, ctypes.c_float, P, P, P, SZ, P]),
         "st_groupnorm_apply": (I32, [P, PP, I32, PP, P, SZ, P]),
+        "st_groupnorm_combine_apply": (I32, [P, PP, I32, ctypes.c_float, P, P, PP, P, SZ, P]),
         "st_groupnorm_backward_workspace_bytes": (SZ, [P, I32]),
         "st_groupnorm_backward": (I32, [P, PP, PP, P, P, I32, P, P, SZ, P, PP, P, P, P, SZ, P]),
     }
@@ -529,6 +530,19 @@ def st_groupnorm_apply(y_plan: Plan, y_bufs, groups: int, z_bufs, workspace, str
     ws, nb = _ws(workspace)
     _check(lib.st_groupnorm_apply(y_plan.handle, ys, groups, zs, ctypes.c_void_p(ws), nb, _stream(stream)),
            "st_groupnorm_apply")
+
+
+def st_groupnorm_combine_apply(y_plan: Plan, y_bufs, groups: int, eps: float, gamma, beta, z_bufs, workspace,
+                               stream=None) -> None:
+    sizes = _shard_bytes(y_plan)
+    ys = _ptr_array(y_bufs, "st_groupnorm_combine_apply y", sizes)
+    zs = _ptr_array(z_bufs, "st_groupnorm_combine_apply z", sizes)
+    g = _dev_ptr(gamma, "gamma", 4 * y_plan.channels)
+    b = _dev_ptr(beta, "beta", 4 * y_plan.channels)
+    ws, nb = _ws(workspace)
+    _check(lib.st_groupnorm_combine_apply(y_plan.handle, ys, groups, float(eps), ctypes.c_void_p(g),
+                                          ctypes.c_void_p(b), zs, ctypes.c_void_p(ws), nb, _stream(stream)),
+           "st_groupnorm_combine_apply")
 
 
 def st_groupnorm_backward_workspace_bytes(y_plan: Plan, groups: int) -> int:

@@ -24,7 +24,8 @@
 //   gn_max     max |y| per (n, group)   (only when the conv did not fuse it)
 //   gn_stats   per-shard sum q1, sum q2 per (n, group)
 //   gn_combine sum over shards; mean, var, rstd in fp64 -> fp32
-//   gn_apply   z = (y - mean_g) * (rstd_g * gamma_c) + beta_c
+//   gn_apply   z = (y - mean_g) * (rstd_g * gamma_c) + beta_c, optionally
+//              with the combine in its prologue (one launch fewer)
 #include <algorithm>
 #include <mutex>
 #include <string>
@@ -277,9 +278,9 @@ __global__ __launch_bounds__(kNT) void gn_stats(const GnArgs a) {
   if (cur >= 0) flush(cur_s, cur_n);
 }
 
-__global__ void gn_combine(const GnArgs a) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= a.batch * a.groups) return;
+// (mean, rstd) of group i = n * G + g from the per-shard partials, in fp64;
+// the shard sums are exact integers, so their order does not matter
+__device__ __forceinline__ void group_moments(const GnArgs& a, int i, double& mean, double& rstd) {
   const int n = i / a.groups, g = i - n * a.groups;
   double t1 = 0.0, t2 = 0.0;
   for (int s = 0; s < a.nshards; ++s) {
@@ -288,11 +289,19 @@ __global__ void gn_combine(const GnArgs a) {
     t2 += p[1];
   }
   const int e1 = a.scales[2 * i + 0], e2 = a.scales[2 * i + 1];
-  const double mean = ldexp(t1, -e1) / a.m_count;
+  mean = ldexp(t1, -e1) / a.m_count;
   const double ey2 = ldexp(t2, -e2) / a.m_count;
   double var = ey2 - mean * mean;
   if (var < 0.0) var = 0.0;
-  const double rstd = 1.0 / sqrt(var + a.eps);
+  rstd = 1.0 / sqrt(var + a.eps);
+}
+
+__global__ void gn_combine(const GnArgs a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.batch * a.groups) return;
+  const int n = i / a.groups, g = i - n * a.groups;
+  double mean, rstd;
+  group_moments(a, i, mean, rstd);
   a.stats[2 * i + 0] = (float)mean;
   a.stats[2 * i + 1] = (float)rstd;
   const int gs = a.channels / a.groups;
@@ -303,11 +312,29 @@ __global__ void gn_combine(const GnArgs a) {
   }
 }
 
-template <int VW, bool FIXED>
+// COMBINE (with FIXED): the combine runs in the prologue of every workgroup
+// (one thread per (n, group) into LDS, workgroup 0 also writes the
+// statistics), so the three-kernel chain is two launches; each lane then
+// forms its channels' coefficients exactly as gn_combine does.
+template <int VW, bool FIXED, bool COMBINE>
 __global__ __launch_bounds__(kNT) void gn_apply(const GnArgs a) {
   using V = Vec<VW>;
+  static_assert(!COMBINE || FIXED, "the fused combine serves the per-lane coefficient path");
+  extern __shared__ double2 smom[];                   // COMBINE: [N * G] (mean, rstd)
   const int tid = threadIdx.x;
   const int C = a.channels;
+  if constexpr (COMBINE) {
+    for (int i = tid; i < a.batch * a.groups; i += kNT) {
+      double mean, rstd;
+      group_moments(a, i, mean, rstd);
+      smom[i] = make_double2(mean, rstd);
+      if (blockIdx.x == 0) {
+        a.stats[2 * i + 0] = (float)mean;
+        a.stats[2 * i + 1] = (float)rstd;
+      }
+    }
+    __syncthreads();
+  }
   int cur = -1;
   float4 p[VW];
   // work units of kPart vectors per thread (a part of an item: more waves
@@ -322,8 +349,18 @@ __global__ __launch_bounds__(kNT) void gn_apply(const GnArgs a) {
     const int key = s * a.batch + n;
     if (FIXED && key != cur) {
       const int c0 = (tid * VW) % C;
+      const int gs = C / a.groups;
 #pragma unroll
-      for (int j = 0; j < VW; ++j) p[j] = a.chan[(size_t)n * C + c0 + j];
+      for (int j = 0; j < VW; ++j) {
+        if constexpr (COMBINE) {
+          const int c = c0 + j;
+          const double2 m = smom[n * a.groups + c / gs];
+          const double gam = a.gamma ? (double)a.gamma[c] : 1.0;
+          p[j] = make_float4((float)m.x, (float)(m.y * gam), a.beta ? a.beta[c] : 0.f, 0.f);
+        } else {
+          p[j] = a.chan[(size_t)n * C + c0 + j];
+        }
+      }
       cur = key;
     }
     const GnShard& sh = a.sh[s];
@@ -767,14 +804,17 @@ st_status launch_partials(GnArgs& a, bool need_max, hipStream_t st) {
   return launch_check("st_groupnorm_partials: stats launch");
 }
 
-template <int VW, bool FIXED>
+template <int VW, bool FIXED, bool COMBINE = false>
 st_status launch_apply(GnArgs& a, hipStream_t st) {
   // 32 workgroups per CU: 1-2% faster than 8 or 16 on the 512^3, 256^3 and
   // 2048^2 outputs (8-vector parts; 4 and 16 were slower)
   const int grid = std::max(1, std::min((kIter / kPart) * a.total_items, device_cus() * 32));
-  hipLaunchKernelGGL((gn_apply<VW, FIXED>), dim3(grid), dim3(kNT), 0, st, a);
+  const size_t shmem = COMBINE ? (size_t)a.batch * a.groups * sizeof(double2) : 0;
+  hipLaunchKernelGGL((gn_apply<VW, FIXED, COMBINE>), dim3(grid), dim3(kNT), shmem, st, a);
   return launch_check("st_groupnorm_apply: launch");
 }
+// the fused combine keeps N * G moments (16 bytes each) in LDS
+constexpr int kMaxFusedGroups = 256;   // 4 KiB: 32 workgroups per CU still fit
 
 
 // backward workspace: [S][N][C][2] double partials, [N][G] max |dz|,
@@ -923,6 +963,25 @@ st_status st_groupnorm_apply(const st_plan* y_plan, const float* const* y_bufs, 
   return fixed ? launch_apply<1, true>(a, st) : launch_apply<1, false>(a, st);
 }
 
+st_status st_groupnorm_combine_apply(const st_plan* y_plan, const float* const* y_bufs, int32_t groups,
+                                     float eps, const float* gamma_or_null, const float* beta_or_null,
+                                     float* const* z_bufs, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  if (!y_bufs || !z_bufs) return fail(ST_ERR_INVALID_ARG, "st_groupnorm_combine_apply: NULL buffer array");
+  GnArgs a;
+  int vw;
+  bool fixed;
+  st_status s = prepare(y_plan, y_bufs, z_bufs, nullptr, groups, eps, gamma_or_null, beta_or_null, workspace,
+                        workspace_bytes, "st_groupnorm_combine_apply", a, vw, fixed);
+  if (s != ST_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fixed && (int64_t)a.batch * a.groups <= kMaxFusedGroups)
+    return vw == 4 ? launch_apply<4, true, true>(a, st) : launch_apply<1, true, true>(a, st);
+  s = st_groupnorm_combine(y_plan, groups, eps, gamma_or_null, beta_or_null, workspace, workspace_bytes, stream);
+  if (s != ST_OK) return s;
+  return st_groupnorm_apply(y_plan, y_bufs, groups, z_bufs, workspace, workspace_bytes, stream);
+}
+
 st_status st_groupnorm_sharded(const st_plan* y_plan, const float* const* y_bufs,
                                const uint32_t* ymax_or_null, int32_t groups, float eps,
                                const float* gamma_or_null, const float* beta_or_null,
@@ -938,9 +997,8 @@ st_status st_groupnorm_sharded(const st_plan* y_plan, const float* const* y_bufs
   if (s != ST_OK) return s;
   s = st_groupnorm_partials(y_plan, y_bufs, ymax_or_null, groups, workspace, workspace_bytes, stream);
   if (s != ST_OK) return s;
-  s = st_groupnorm_combine(y_plan, groups, eps, gamma_or_null, beta_or_null, workspace, workspace_bytes, stream);
-  if (s != ST_OK) return s;
-  return st_groupnorm_apply(y_plan, y_bufs, groups, z_bufs, workspace, workspace_bytes, stream);
+  return st_groupnorm_combine_apply(y_plan, y_bufs, groups, eps, gamma_or_null, beta_or_null, z_bufs, workspace,
+                                    workspace_bytes, stream);
 }
 
 st_status st_groupnorm_sharded_noalloc(const st_plan* y_plan, const float* const* y_bufs,

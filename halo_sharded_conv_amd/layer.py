@@ -16,7 +16,8 @@ import numpy as np
 
 from . import (ST_BF16, ST_F32, ShardConvError, st_conv_dgrad_weights, st_conv_sharded,
                st_conv_workspace_bytes, st_groupnorm_apply, st_groupnorm_backward,
-               st_groupnorm_backward_workspace_bytes, st_groupnorm_combine, st_groupnorm_partials,
+               st_groupnorm_backward_workspace_bytes, st_groupnorm_combine, st_groupnorm_combine_apply,
+               st_groupnorm_partials,
                st_groupnorm_sharded, st_groupnorm_workspace_bytes, st_groupnorm_workspace_layout,
                st_halo_exchange, st_halo_pack, st_halo_unpack, st_plan_shards)
 
@@ -150,6 +151,11 @@ class ShardedConvGN:
 
     def norm_apply(self, stream=None) -> None:
         st_groupnorm_apply(self.out_plan, self.y_bufs, self.cfg.groups, self.z_bufs, self.ws, stream)
+
+    def norm_combine_apply(self, stream=None) -> None:
+        cfg = self.cfg
+        st_groupnorm_combine_apply(self.out_plan, self.y_bufs, cfg.groups, cfg.eps, self.gamma, self.beta,
+                                   self.z_bufs, self.ws, stream)
 
     # ---------------------------------------------------------- backward
     def alloc_backward(self) -> None:

@@ -494,6 +494,15 @@ st_status st_groupnorm_sharded_noalloc(const st_plan* y_plan, const float* const
  *                        rstd) per (n, group) and the per-channel
  *                        (mean, rstd*gamma, beta) the apply reads.
  * st_groupnorm_apply     z = (y - mean) * rstd * gamma + beta; z may alias y.
+ *
+ * st_groupnorm_combine_apply does combine and apply in one call (arguments
+ * of both; same outputs and bits, including the (mean, rstd) written to the
+ * workspace).  When every workgroup of the apply can form its channels'
+ * coefficients itself (the apply's per-lane coefficient layout: 1024 (C % 4
+ * == 0) or 256 values per workgroup pass, a multiple of C) and N * groups
+ * <= 256, the combine runs in the apply kernel's prologue and the call is
+ * one launch; otherwise it launches both kernels.  st_groupnorm_sharded is
+ * st_groupnorm_partials followed by this call.
  */
 st_status st_groupnorm_partials(const st_plan* y_plan, const float* const* y_bufs,
                                 const uint32_t* ymax_or_null, int32_t groups, void* workspace,
@@ -504,6 +513,10 @@ st_status st_groupnorm_combine(const st_plan* y_plan, int32_t groups, float eps,
 st_status st_groupnorm_apply(const st_plan* y_plan, const float* const* y_bufs, int32_t groups,
                              float* const* z_bufs, void* workspace, size_t workspace_bytes,
                              void* stream);
+st_status st_groupnorm_combine_apply(const st_plan* y_plan, const float* const* y_bufs, int32_t groups,
+                                     float eps, const float* gamma_or_null, const float* beta_or_null,
+                                     float* const* z_bufs, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /*
  * st_groupnorm_backward - gradients of st_groupnorm_sharded for an upstream

@@ -151,3 +151,24 @@ def test_all_zero_output():
     assert np.array_equal(layer.y_host(), np.zeros_like(layer.y_host()))
     z = layer.z_host()
     assert np.array_equal(z, np.broadcast_to(beta, z.shape))
+
+
+@pytest.mark.parametrize("name", ["vol32_b2", "img64_b2", "vol16k5", "img_c5to12_k3", "grid256_small"])
+def test_combined_apply_matches_three_calls(name):
+    """st_groupnorm_sharded folds the combine into the apply's prologue when
+    the per-lane coefficient path applies; z and the stored (mean, rstd) must
+    be the same bits as partials, combine and apply called one by one."""
+    wl = CASES[name]
+    say(f"combine folded into apply vs three calls: {name}")
+    x, w = synth.make_input(wl), synth.make_weight(wl)
+    gamma, beta = synth.make_affine(wl, seed=5)
+    a = run(wl, x, w, None, gamma, beta)
+    b = run(wl, x, w, None, gamma, beta)
+    for zb in b.z_bufs:
+        zb.fill_(float("nan"))
+    b.norm_partials()
+    b.norm_combine()
+    b.norm_apply()
+    torch.cuda.synchronize()
+    assert bits_equal(a.z_host(), b.z_host())
+    assert bits_equal(a.gn_state()["stats"], b.gn_state()["stats"])
