@@ -83,6 +83,7 @@ def _load() -> ctypes.CDLL:
         "st_plan_msg_bytes": (I64, [P]),
         "st_plan_num_halo_boxes": (I64, [P]),
         "st_plan_num_zero_boxes": (I64, [P]),
+        "st_plan_upload": (I32, [P, P]),
         "st_plan_shard_info": (I32, [P, I32, ctypes.POINTER(_ShardInfo)]),
         "st_plan_halo_box": (I32, [P, I32, ctypes.POINTER(_HaloBox)]),
         "st_halo_pack": (I32, [P, PP, P, P]),
@@ -180,6 +181,11 @@ class Plan:
     @property
     def num_zero_boxes(self) -> int:
         return int(lib.st_plan_num_zero_boxes(self.handle))
+
+    def upload(self, stream=None) -> None:
+        """Put the halo descriptor table on the current device now (needed
+        before a graph capture that contains the plan's first halo call)."""
+        _check(lib.st_plan_upload(self.handle, _stream(stream)), "st_plan_upload")
 
     def shard_info(self, i: int) -> dict:
         info = _ShardInfo()

@@ -313,6 +313,13 @@ st_status st_plan_destroy(st_plan* plan) {
   return s;
 }
 
+st_status st_plan_upload(st_plan* plan, void* stream) {
+  if (!plan) return fail(ST_ERR_INVALID_ARG, "st_plan_upload: NULL plan");
+  st_status s = plan_device_table(plan, static_cast<hipStream_t>(stream));
+  if (s != ST_OK) return s;
+  return hip_check(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "st_plan_upload: hipStreamSynchronize");
+}
+
 int64_t st_plan_num_shards(const st_plan* p) { return p ? (int64_t)p->shards.size() : -1; }
 int64_t st_plan_msg_bytes(const st_plan* p) { return p ? p->msg_bytes : -1; }
 int64_t st_plan_num_halo_boxes(const st_plan* p) { return p ? p->n_real : -1; }
@@ -378,6 +385,14 @@ st_status plan_device_table(st_plan* p, hipStream_t stream) {
     return ST_OK;
   }
   if (p->descs.empty()) { p->dev_id = dev; return ST_OK; }
+  // the first upload allocates: refuse it inside a graph capture rather than
+  // record an allocation and a pageable copy into the graph
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  s = hip_check(hipStreamIsCapturing(stream, &cap), "hipStreamIsCapturing");
+  if (s != ST_OK) return s;
+  if (cap != hipStreamCaptureStatusNone)
+    return fail(ST_ERR_UNSUPPORTED,
+                "the plan's descriptor table is not on the device yet: call st_plan_upload before capturing");
   const size_t bytes = p->descs.size() * sizeof(HaloDesc);
   s = hip_check(hipMalloc(&p->d_descs, bytes), "plan descriptor table: hipMalloc");
   if (s != ST_OK) { p->d_descs = nullptr; return s; }

@@ -126,6 +126,17 @@ st_status st_plan_shards(int32_t ndim, int64_t batch, int64_t channels, const in
 /* Frees the plan and its device descriptor table (if one was uploaded). */
 st_status st_plan_destroy(st_plan* plan);
 
+/*
+ * st_plan_upload - put the plan's halo descriptor table on the current device
+ * now (one allocation owned by the plan, filled on `stream`; returns after
+ * the stream has drained).  The halo calls do this themselves on first use,
+ * except inside a HIP graph capture, where a plan not uploaded yet makes them
+ * fail with ST_ERR_UNSUPPORTED and enqueue nothing: call this before
+ * capturing.  Repeated calls on the same device do nothing; on another
+ * device: ST_ERR_INVALID_ARG.
+ */
+st_status st_plan_upload(st_plan* plan, void* stream);
+
 /* Plan queries; return -1 for a null plan. */
 int64_t st_plan_num_shards(const st_plan* plan);
 int64_t st_plan_msg_bytes(const st_plan* plan);
