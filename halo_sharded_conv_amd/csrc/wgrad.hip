@@ -20,10 +20,13 @@
 // where r enumerates the taps off the W axis ((tz, ty) in 3D, ty in 2D).
 // Then C[(tx, o)][(r, c)] = sum_u A B^T = dw[o, c, (r, tx)]: every product of
 // the definition appears exactly once, and the contraction index u runs along
-// memory-contiguous positions.  Both operands are written to LDS transposed
-// (positions contiguous, one row per (tx, o) or (r, c)) so that a lane's 8
-// consecutive K values are one 16-byte read; A holds dy once per tx shift, so
-// every fragment read is aligned.
+// memory-contiguous positions.  Two kernels take the operands to LDS:
+// wgrad_mfma (the 256-channel layer, tiled over M and N) stages them through
+// registers and writes them transposed (positions contiguous, one row per
+// (tx, o) or (r, c)) so that a lane's 8 consecutive K values are one 16-byte
+// read, A holding dy once per tx shift; wgrad_tr (the other layers) keeps
+// them in their memory layout, filled by LDS-DMA, and forms the fragments
+// with transposing LDS reads (below).
 //
 // A workgroup owns a tile of 32x32 output blocks and a fixed contiguous band
 // of the rows (partition p of GP), accumulating over all of them in
@@ -66,6 +69,14 @@ struct WgArgs {
   WgShard sh[kWgMaxShards];
 };
 static_assert(sizeof(WgArgs) <= kMaxKernargBytes, "kernel argument struct too large");
+
+// raw buffer descriptor over [base, base + bytes) (clamped to 2^31 - 1); an
+// offset at or past kWtOob reads zeros
+constexpr uint32_t kWtOob = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wt_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
 
 __device__ __forceinline__ void decode_row(const WgArgs& a, int row, int& s, int& n, int& d, int& h) {
   s = 0;
@@ -128,6 +139,7 @@ struct WgChunk {
   const uint16_t* dyrow;
   const uint16_t* xrow;
   int32_t xs0, xs1, W;
+  int64_t dy_left, x_left;   // bytes from dyrow / xrow to the end of the shard buffer
 };
 
 // Partition p owns the contiguous band of rows [p * R / P, (p + 1) * R / P):
@@ -152,6 +164,8 @@ __device__ __forceinline__ WgChunk first_chunk(const WgArgs& a, int row, int row
   c.xs0 = (int32_t)sh.xs[0];
   c.xs1 = (int32_t)sh.xs[1];
   c.W = sh.ext[2];
+  c.dy_left = ((int64_t)a.batch * sh.dn - (c.dyrow - static_cast<const uint16_t*>(sh.dy))) * 2;
+  c.x_left = ((int64_t)a.batch * sh.xn - (c.xrow - static_cast<const uint16_t*>(sh.x))) * 2;
   return c;
 }
 
@@ -342,6 +356,253 @@ __global__ __launch_bounds__(C::NT) void wgrad_mfma(const WgArgs a) {
 }
 
 // --------------------------------------------------------------------------
+// matrix-core kernel with natural-layout LDS tiles and transposing reads
+// --------------------------------------------------------------------------
+//
+// The same contraction C[(tx, o)][(r, c)] = sum_u A B^T, chunk by chunk along
+// W, with the operands kept in LDS as they lie in memory: the dy run of a
+// chunk ([u][o], the k - 1 positions before it included, so every tap shift
+// tx is an address offset) and one x run per tap row of the tile ([u][c]).
+// Both are filled by LDS-DMA straight from the shard buffers (no registers,
+// no ALU work; out-of-row positions read zeros through the buffer range),
+// and the MFMA fragments, which need 8 consecutive positions of one channel
+// per lane, come from two ds_read_b64_tr_b16 each: within a group of 16
+// lanes, source lane s reads 4 consecutive channels of position k0 + s/4,
+// and output lane i receives channel i of positions k0 .. k0 + 3.  Chunks,
+// K steps and partitions are those of wgrad_mfma, so each MFMA sees the
+// same operands in the same positions.
+
+template <int NDIM_, int K_, int CIN_, int COUT_, int WGM_, int WGN_, int WM_, int WN_, int TILES_N_, int LW_ = 0>
+struct WtCfg {
+  static constexpr int NDIM = NDIM_, K = K_, CIN = CIN_, COUT = COUT_;
+  static constexpr int WGM = WGM_, WGN = WGN_, WM = WM_, WN = WN_;
+  static constexpr int P = K / 2;
+  static constexpr int TAPS = NDIM == 3 ? K * K * K : K * K;
+  static constexpr int R = NDIM == 3 ? K * K : K;        // tap rows off the W axis
+  static constexpr int MR = K * COUT, NR = R * CIN;       // rows of A and of B
+  static constexpr int MB = (MR + 31) / 32, NB = (NR + 31) / 32;
+  static constexpr int TM = WGM * WM, TN = WGN * WN;     // blocks per tile
+  static constexpr int TILES_M = 1, TILES_N = TILES_N_;
+  static constexpr int NWC = WGM * WGN;                  // waves with MFMA work
+  static constexpr int NW = NWC + LW_, NT = 64 * NW;    // plus LW_ waves that only issue transfers
+  static constexpr int COLS = 64;                        // chunk width along W ...
+  static constexpr int CMAX = COLS + 16;                 // ... or up to 16 more: a row's last chunk takes its tail
+  static constexpr int DQ = CMAX + K - 1;                // dy positions of a chunk
+  static constexpr int DPITCH = COUT * 2, XPITCH = CIN * 2;
+  static constexpr int RT = TN * 32 / CIN;               // tap rows of a tile
+  static constexpr int D_BYTES = (DQ * DPITCH + 1023) / 1024 * 1024;
+  static constexpr int XR_BYTES = CMAX * XPITCH;         // one tap row's run
+  static constexpr int NJ = (D_BYTES + RT * XR_BYTES + 1023) / 1024;   // 1 KiB LDS-DMA transfers per stage
+  static constexpr int JPW = (NJ + NW - 1) / NW;         // per wave; every wave issues exactly JPW
+  static constexpr int STAGE = JPW * NW * 1024;          // (the padding transfers fill the stage's tail)
+  static constexpr int NSTAGE = 3;                       // chunks c (read), c + 1 (landed), c + 2 (in flight)
+  static constexpr int LDS = NSTAGE * STAGE;
+  static_assert(TM * 32 >= MR, "one tile spans every (tx, o) row");
+  static_assert(TILES_N * TN >= NB, "tiles cover the blocks");
+  static_assert(COUT % 16 == 0 && CIN % 16 == 0, "16 rows of a lane group share one tap shift / tap row");
+  static_assert((TN * 32) % CIN == 0, "tiles hold whole tap rows");
+  static_assert(XR_BYTES % 512 == 0, "tap-row runs in whole 16-byte slots of 32 rows");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void wgrad_tr(const WgArgs a) {
+  __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage2[C::STAGE];
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s* lds_v4s;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int tile = blockIdx.x % C::TILES_N;
+  const int part = blockIdx.x / C::TILES_N;
+  const int n0 = tile * C::TN * 32;                   // first B row of the tile
+  const int r0 = n0 / C::CIN;                         // its first tap row
+  const int wm = (wave % C::NWC) / C::WGN, wn = (wave % C::NWC) % C::WGN;
+  const bool mma = wave < C::NWC;
+
+  f32x16 acc[C::WM][C::WN];
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) acc[i][j] = f32x16{};
+
+  // fragment read offsets within a stage for K step 0 (a step adds 16
+  // positions): lane s of 16-lane group g reads position 8 (g >> 1) + s / 4
+  // (+ 4 for the second read) at the 4 channels 16 (g & 1) + 4 (s & 3) of
+  // its 32-row block
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int kq = 8 * (g16 >> 1) + (s16 >> 2);
+  const int rq = 16 * (g16 & 1) + 4 * (s16 & 3);
+  int aoff[C::WM], boff[C::WN];
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i) {
+    int mrow = (wm * C::WM + i) * 32 + rq;
+    mrow = mrow < C::MR ? mrow : 0;                   // padding rows read anything: their sums are not stored
+    const int tx = mrow / C::COUT, o = mrow % C::COUT;
+    aoff[i] = (kq + (C::K - 1) - tx) * C::DPITCH + o * 2;
+  }
+#pragma unroll
+  for (int j = 0; j < C::WN; ++j) {
+    const int nrow = (wn * C::WN + j) * 32 + rq;       // within the tile (tap rows r0 ..)
+    const int rl = nrow / C::CIN, c = nrow % C::CIN;
+    boff[j] = C::D_BYTES + rl * C::XR_BYTES + kq * C::XPITCH + c * 2;
+  }
+  auto frags = [&](const char* st, int ks, bf16x8 (&av)[C::WM], bf16x8 (&bv)[C::WN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i) {
+      const char* p = st + aoff[i] + ks * 16 * C::DPITCH;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)p);
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * C::DPITCH));
+      av[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      const char* p = st + boff[j] + ks * 16 * C::XPITCH;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)p);
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * C::XPITCH));
+      bv[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto mfmas = [&](const bf16x8 (&av)[C::WM], const bf16x8 (&bv)[C::WN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::WN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  };
+
+  // a chunk is COLS columns of its row, or the rest of the row when at most
+  // 16 more would remain (so no chunk holds only a row's last few columns)
+  auto chunk_len = [&](const WgChunk& ch) __attribute__((always_inline)) -> int {
+    const int rem = ch.W + 2 * C::P - ch.j0;
+    return rem <= C::CMAX ? rem : C::COLS;
+  };
+  auto next_of = [&](const WgChunk& ch, int row_end) __attribute__((always_inline)) -> WgChunk {
+    if (!ch.valid) return ch;
+    const int len = chunk_len(ch);
+    if (ch.j0 + len < ch.W + 2 * C::P) {
+      WgChunk n = ch;
+      n.j0 += len;
+      return n;
+    }
+    return first_chunk(a, ch.row + 1, row_end);
+  };
+  // one chunk into a stage by LDS-DMA.  Transfer j moves 1 KiB: lane l's 16
+  // bytes are slot 64 j + l of the stage.  dy slots: position q = slot /
+  // (DPITCH / 16) of the run that starts k - 1 before the chunk; x slots:
+  // tap row, then position, then 8-channel octet.  Out-of-row positions,
+  // tap rows past the kernel and the stage's padding slots get an
+  // out-of-range offset and land as zeros.  Every wave issues exactly JPW
+  // transfers (an invalid chunk's too: its descriptors have no range), so a
+  // wave's count of outstanding transfers per chunk is the constant JPW.
+  auto fetch = [&](char* dst, const WgChunk& ch) __attribute__((always_inline)) {
+    constexpr int DS = C::DPITCH / 16, XS = C::XPITCH / 16;
+    constexpr int D_SLOTS = C::D_BYTES / 16, XR_SLOTS = C::XR_BYTES / 16;
+    const char* dbase = reinterpret_cast<const char*>(ch.dyrow);
+    const char* xbase = reinterpret_cast<const char*>(ch.xrow);
+    // each row's descriptors start at its own pointer, so offsets stay small
+    const __amdgpu_buffer_rsrc_t rd = wt_rsrc(dbase, ch.valid ? ch.dy_left : 0);
+    const __amdgpu_buffer_rsrc_t rx = wt_rsrc(xbase, ch.valid ? ch.x_left : 0);
+    const int uend = ch.W + 2 * C::P;
+#pragma unroll
+    for (int q = 0; q < C::JPW; ++q) {
+      const int j = wave + q * C::NW;
+      const int slot = 64 * j + lane;
+      if (j * 64 < D_SLOTS) {
+        const int pos = slot / DS, oct = slot - pos * DS;
+        const int i = ch.j0 - (C::K - 1) + pos;
+        const bool ok = slot < D_SLOTS && pos < C::DQ && i >= 0 && i < ch.W;
+        const uint32_t off = ok ? (uint32_t)(i * C::DPITCH + oct * 16) : kWtOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr)(dst + j * 1024), 16, off, 0, 0, 0);
+      } else {
+        const int xs = slot - D_SLOTS;
+        const int rl = xs / XR_SLOTS, rem = xs - rl * XR_SLOTS;
+        const int u = ch.j0 + rem / XS, oct = rem % XS;
+        const int r = r0 + rl;
+        const int tz = C::NDIM == 3 ? r / C::K : 0, ty = C::NDIM == 3 ? r % C::K : r;
+        const bool ok = rl < C::RT && r < C::R && u < uend;
+        const uint32_t off = ok ? (uint32_t)((tz * ch.xs0 + ty * ch.xs1 + u * C::CIN) * 2 + oct * 16) : kWtOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(dst + j * 1024), 16, off, 0, 0, 0);
+      }
+    }
+  };
+  constexpr int VM_NEXT = 0x0F70 | (C::JPW & 15) | ((C::JPW >> 4) << 14);   // vmcnt(JPW): the newest chunk may fly
+
+  const int row_end = band_begin(a, part + 1);
+  WgChunk c0 = first_chunk(a, band_begin(a, part), row_end);
+  WgChunk c1 = next_of(c0, row_end);
+  fetch(stage0, c0);
+  fetch(stage1, c1);
+  __builtin_amdgcn_s_waitcnt(VM_NEXT);                // chunk 0 is in LDS
+  __syncthreads();
+  // one chunk per phase, three phases per loop turn so that the stages
+  // rotate at compile time: chunk c + 2's transfers go into the stage chunk
+  // c - 1 used while chunk c computes; at the phase's end chunk c + 1 has
+  // landed (vmcnt(JPW) leaves chunk c + 2 in flight) and a barrier makes it
+  // visible and frees chunk c's stage
+  auto phase = [&](auto PP) __attribute__((always_inline)) {
+    constexpr int par = decltype(PP)::value;
+    const char* const cur = par == 0 ? stage0 : par == 1 ? stage1 : stage2;
+    char* const far = par == 0 ? stage2 : par == 1 ? stage0 : stage1;
+    const WgChunk c2 = next_of(c1, row_end);
+    fetch(far, c2);
+    if (mma) {
+      const int nks = (chunk_len(c0) + 15) / 16;
+      bf16x8 av0[C::WM], bv0[C::WN], av1[C::WM], bv1[C::WN];
+      frags(cur, 0, av0, bv0);
+      frags(cur, 1, av1, bv1);                        // a chunk has at least 2 K steps unless its row is short
+      mfmas(av0, bv0);
+      if (nks > 2) frags(cur, 2, av0, bv0);
+      if (nks > 1) mfmas(av1, bv1);
+      if (nks > 2) {
+        if (nks > 3) frags(cur, 3, av1, bv1);
+        mfmas(av0, bv0);
+        if (nks > 3) {
+          if (nks > 4) frags(cur, 4, av0, bv0);
+          mfmas(av1, bv1);
+          if (nks > 4) mfmas(av0, bv0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(VM_NEXT);
+    __syncthreads();
+    c0 = c1;
+    c1 = c2;
+  };
+  while (c0.valid) {
+    phase(std::integral_constant<int, 0>{});
+    if (!c0.valid) break;
+    phase(std::integral_constant<int, 1>{});
+    if (!c0.valid) break;
+    phase(std::integral_constant<int, 2>{});
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0): no transfer outlives the kernel's LDS
+
+  // partial dw of this partition: C[(tx, o)][(r, c)] -> [o][c][r * K + tx]
+  if (!mma) return;
+  float* out = a.partial + (size_t)part * C::COUT * C::CIN * C::TAPS;
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i) {
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      const int nn = n0 + (wn * C::WN + j) * 32 + l32;
+      if (nn >= C::NR) continue;
+      const int r = nn / C::CIN, c = nn % C::CIN;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = (wm * C::WM + i) * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+        if (m >= C::MR) continue;
+        const int tx = m / C::COUT, o = m % C::COUT;
+        out[((size_t)o * C::CIN + c) * C::TAPS + r * C::K + tx] = acc[i][j][e];
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
 // direct kernel (fp32, and bf16 shapes without a matrix-core instance)
 // --------------------------------------------------------------------------
 
@@ -404,6 +665,10 @@ using WgVol32 = WgCfg<3, 3, 32, 32, 1, 3, 3, 3, 1, 1, 1>;
 using WgVol16k5 = WgCfg<3, 5, 16, 16, 1, 4, 3, 2, 1, 2>;
 // image 256->256 k3: 24x24 blocks in 4x4 tiles of 6x6, 2x2 waves of 3x3
 using WgImg256 = WgCfg<2, 3, 256, 256, 2, 2, 3, 3, 4, 4>;
+// transposing-read kernel: the same tilings (one tile along M)
+using WtImg64 = WtCfg<2, 3, 64, 64, 2, 2, 3, 3, 1>;
+using WtVol32 = WtCfg<3, 3, 32, 32, 1, 3, 3, 3, 1, 1>;
+using WtVol16k5 = WtCfg<3, 5, 16, 16, 1, 4, 3, 2, 2>;
 
 constexpr int kPartitions = 256;   // partial sums (workgroups per tile set): one per CU
 
@@ -423,9 +688,15 @@ WgInstance make_instance() {
                     wgrad_mfma<C>};
 }
 
+template <class C>
+WgInstance make_instance_tr() {
+  return WgInstance{C::NDIM, C::CIN, C::COUT, C::K, std::max(1, kPartitions / C::TILES_N), C::TILES_N, C::LDS, C::NT,
+                    wgrad_tr<C>};
+}
+
 const WgInstance* find_instance(int ndim, int cin, int cout, int k) {
-  static const WgInstance table[] = {make_instance<WgImg64>(), make_instance<WgVol32>(),
-                                     make_instance<WgVol16k5>(), make_instance<WgImg256>()};
+  static const WgInstance table[] = {make_instance_tr<WtImg64>(), make_instance_tr<WtVol32>(),
+                                     make_instance_tr<WtVol16k5>(), make_instance<WgImg256>()};
   for (const WgInstance& w : table)
     if (w.ndim == ndim && w.cin == cin && w.cout == cout && w.k == k) return &w;
   return nullptr;
