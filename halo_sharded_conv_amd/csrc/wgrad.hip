@@ -474,66 +474,134 @@ __global__ __launch_bounds__(C::NT) void wgrad_tr(const WgArgs a) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
   };
 
+  // Rows advance incrementally (h, then d, n and shard) from one decode at
+  // the band's start, and each row's pointers are formed by multiplication:
+  // no divisions per row.
+  struct TrChunk {
+    int valid, row, s, n, d, h, j0, W;
+    int32_t xs0, xs1;
+    const char* dyrow;       // dy at (n, d, h), output column 0
+    const char* xrow;        // x at tap (0, 0) of output row (n, d, h), column 0
+    int64_t dy_left, x_left; // bytes from there to the end of the shard buffer
+  };
+  auto set_row = [&](TrChunk& c) __attribute__((always_inline)) {
+    const WgShard& sh = a.sh[c.s];
+    const int64_t dyo = (int64_t)c.n * sh.dn + (int64_t)(c.d + sh.dyo[0]) * sh.ds[0] +
+                        (int64_t)(c.h + sh.dyo[1]) * sh.ds[1] + (int64_t)sh.dyo[2] * sh.ds[2];
+    const int64_t xo = (int64_t)c.n * sh.xn + (int64_t)(c.d + sh.xo[0]) * sh.xs[0] + (int64_t)(c.h + sh.xo[1]) * sh.xs[1] +
+                       (int64_t)sh.xo[2] * sh.xs[2];
+    c.dyrow = static_cast<const char*>(sh.dy) + dyo * 2;
+    c.xrow = static_cast<const char*>(sh.x) + xo * 2;
+    c.dy_left = ((int64_t)a.batch * sh.dn - dyo) * 2;
+    c.x_left = ((int64_t)a.batch * sh.xn - xo) * 2;
+    c.xs0 = (int32_t)sh.xs[0];
+    c.xs1 = (int32_t)sh.xs[1];
+    c.W = sh.ext[2];
+  };
+  const int row_end = band_begin(a, part + 1);
+  auto first_tr = [&]() __attribute__((always_inline)) -> TrChunk {
+    TrChunk c{};
+    c.row = band_begin(a, part);
+    c.valid = c.row < row_end;
+    if (c.valid) decode_row(a, c.row, c.s, c.n, c.d, c.h);
+    c.j0 = 0;
+    set_row(c);
+    return c;
+  };
   // a chunk is COLS columns of its row, or the rest of the row when at most
   // 16 more would remain (so no chunk holds only a row's last few columns)
-  auto chunk_len = [&](const WgChunk& ch) __attribute__((always_inline)) -> int {
+  auto chunk_len = [&](const TrChunk& ch) __attribute__((always_inline)) -> int {
     const int rem = ch.W + 2 * C::P - ch.j0;
     return rem <= C::CMAX ? rem : C::COLS;
   };
-  auto next_of = [&](const WgChunk& ch, int row_end) __attribute__((always_inline)) -> WgChunk {
+  auto next_of = [&](const TrChunk& ch) __attribute__((always_inline)) -> TrChunk {
     if (!ch.valid) return ch;
+    TrChunk c = ch;
     const int len = chunk_len(ch);
     if (ch.j0 + len < ch.W + 2 * C::P) {
-      WgChunk n = ch;
-      n.j0 += len;
-      return n;
+      c.j0 += len;
+      return c;
     }
-    return first_chunk(a, ch.row + 1, row_end);
+    c.j0 = 0;
+    c.row = ch.row + 1;
+    c.valid = c.row < row_end;
+    if (!c.valid) return c;
+    if (++c.h == a.sh[c.s].ext[1]) {
+      c.h = 0;
+      if (++c.d == a.sh[c.s].ext[0]) {
+        c.d = 0;
+        if (++c.n == a.batch) {
+          c.n = 0;
+          ++c.s;
+        }
+      }
+    }
+    set_row(c);
+    return c;
   };
-  // one chunk into a stage by LDS-DMA.  Transfer j moves 1 KiB: lane l's 16
+  // One chunk into a stage by LDS-DMA.  Transfer j moves 1 KiB: lane l's 16
   // bytes are slot 64 j + l of the stage.  dy slots: position q = slot /
-  // (DPITCH / 16) of the run that starts k - 1 before the chunk; x slots:
-  // tap row, then position, then 8-channel octet.  Out-of-row positions,
-  // tap rows past the kernel and the stage's padding slots get an
-  // out-of-range offset and land as zeros.  Every wave issues exactly JPW
-  // transfers (an invalid chunk's too: its descriptors have no range), so a
-  // wave's count of outstanding transfers per chunk is the constant JPW.
-  auto fetch = [&](char* dst, const WgChunk& ch) __attribute__((always_inline)) {
+  // (DPITCH / 16) of the run that starts k - 1 before the chunk (its byte
+  // offset in the dy row is (j0 - k + 1) DPITCH + 16 slot); x slots: tap row,
+  // then position, then 8-channel octet (offset 16 rem + tap-row offset +
+  // j0 XPITCH).  Out-of-row positions, tap rows past the kernel and the
+  // stage's padding slots get an out-of-range offset and land as zeros.  Every
+  // wave issues exactly JPW transfers (an invalid chunk's too: its
+  // descriptors have no range), so a wave's count of outstanding transfers
+  // per chunk is the constant JPW.  The per-lane parts are fixed per kernel.
+  int tpos[C::JPW];          // dy: position in the run; x: column in the chunk (-1: padding slot)
+  int tcon[C::JPW];          // dy: 16 slot; x: 16 rem
+  int ttz[C::JPW], tty[C::JPW];
+  {
     constexpr int DS = C::DPITCH / 16, XS = C::XPITCH / 16;
     constexpr int D_SLOTS = C::D_BYTES / 16, XR_SLOTS = C::XR_BYTES / 16;
-    const char* dbase = reinterpret_cast<const char*>(ch.dyrow);
-    const char* xbase = reinterpret_cast<const char*>(ch.xrow);
-    // each row's descriptors start at its own pointer, so offsets stay small
-    const __amdgpu_buffer_rsrc_t rd = wt_rsrc(dbase, ch.valid ? ch.dy_left : 0);
-    const __amdgpu_buffer_rsrc_t rx = wt_rsrc(xbase, ch.valid ? ch.x_left : 0);
-    const int uend = ch.W + 2 * C::P;
 #pragma unroll
     for (int q = 0; q < C::JPW; ++q) {
       const int j = wave + q * C::NW;
       const int slot = 64 * j + lane;
-      if (j * 64 < D_SLOTS) {
-        const int pos = slot / DS, oct = slot - pos * DS;
-        const int i = ch.j0 - (C::K - 1) + pos;
-        const bool ok = slot < D_SLOTS && pos < C::DQ && i >= 0 && i < ch.W;
-        const uint32_t off = ok ? (uint32_t)(i * C::DPITCH + oct * 16) : kWtOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr)(dst + j * 1024), 16, off, 0, 0, 0);
+      if (slot < D_SLOTS) {
+        const int pos = slot / DS;
+        tpos[q] = pos < C::DQ ? pos : -1;
+        tcon[q] = 16 * slot;
+        ttz[q] = tty[q] = 0;
       } else {
         const int xs = slot - D_SLOTS;
         const int rl = xs / XR_SLOTS, rem = xs - rl * XR_SLOTS;
-        const int u = ch.j0 + rem / XS, oct = rem % XS;
         const int r = r0 + rl;
-        const int tz = C::NDIM == 3 ? r / C::K : 0, ty = C::NDIM == 3 ? r % C::K : r;
-        const bool ok = rl < C::RT && r < C::R && u < uend;
-        const uint32_t off = ok ? (uint32_t)((tz * ch.xs0 + ty * ch.xs1 + u * C::CIN) * 2 + oct * 16) : kWtOob;
+        tpos[q] = rl < C::RT && r < C::R ? rem / XS : -1;
+        tcon[q] = 16 * rem;
+        ttz[q] = C::NDIM == 3 ? r / C::K : 0;
+        tty[q] = C::NDIM == 3 ? r % C::K : r;
+      }
+    }
+  }
+  auto fetch = [&](char* dst, const TrChunk& ch) __attribute__((always_inline)) {
+    constexpr int D_SLOTS = C::D_BYTES / 16;
+    const __amdgpu_buffer_rsrc_t rd = wt_rsrc(ch.dyrow, ch.valid ? ch.dy_left : 0);
+    const __amdgpu_buffer_rsrc_t rx = wt_rsrc(ch.xrow, ch.valid ? ch.x_left : 0);
+    const int i0 = ch.j0 - (C::K - 1);
+    const int uend = ch.W + 2 * C::P - ch.j0;       // columns of the chunk with an x cell
+    const uint32_t dbase = (uint32_t)(i0 * C::DPITCH), xbase = (uint32_t)(ch.j0 * C::XPITCH);
+#pragma unroll
+    for (int q = 0; q < C::JPW; ++q) {
+      const int j = wave + q * C::NW;
+      if (j * 64 < D_SLOTS) {                         // wave-uniform: a transfer is all dy or all x
+        const int i = i0 + tpos[q];
+        const bool ok = tpos[q] >= 0 && i >= 0 && i < ch.W;
+        const uint32_t off = ok ? dbase + (uint32_t)tcon[q] : kWtOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr)(dst + j * 1024), 16, off, 0, 0, 0);
+      } else {
+        const bool ok = tpos[q] >= 0 && tpos[q] < uend;
+        const uint32_t off =
+            ok ? xbase + (uint32_t)tcon[q] + (uint32_t)((ttz[q] * ch.xs0 + tty[q] * ch.xs1) * 2) : kWtOob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(dst + j * 1024), 16, off, 0, 0, 0);
       }
     }
   };
   constexpr int VM_NEXT = 0x0F70 | (C::JPW & 15) | ((C::JPW >> 4) << 14);   // vmcnt(JPW): the newest chunk may fly
 
-  const int row_end = band_begin(a, part + 1);
-  WgChunk c0 = first_chunk(a, band_begin(a, part), row_end);
-  WgChunk c1 = next_of(c0, row_end);
+  TrChunk c0 = first_tr();
+  TrChunk c1 = next_of(c0);
   fetch(stage0, c0);
   fetch(stage1, c1);
   __builtin_amdgcn_s_waitcnt(VM_NEXT);                // chunk 0 is in LDS
@@ -547,7 +615,7 @@ __global__ __launch_bounds__(C::NT) void wgrad_tr(const WgArgs a) {
     constexpr int par = decltype(PP)::value;
     const char* const cur = par == 0 ? stage0 : par == 1 ? stage1 : stage2;
     char* const far = par == 0 ? stage2 : par == 1 ? stage0 : stage1;
-    const WgChunk c2 = next_of(c1, row_end);
+    const TrChunk c2 = next_of(c1);
     fetch(far, c2);
     if (mma) {
       const int nks = (chunk_len(c0) + 15) / 16;
