@@ -20,13 +20,11 @@
 // where r enumerates the taps off the W axis ((tz, ty) in 3D, ty in 2D).
 // Then C[(tx, o)][(r, c)] = sum_u A B^T = dw[o, c, (r, tx)]: every product of
 // the definition appears exactly once, and the contraction index u runs along
-// memory-contiguous positions.  Two kernels take the operands to LDS:
-// wgrad_mfma (the 256-channel layer, tiled over M and N) stages them through
-// registers and writes them transposed (positions contiguous, one row per
-// (tx, o) or (r, c)) so that a lane's 8 consecutive K values are one 16-byte
-// read, A holding dy once per tx shift; wgrad_tr (the other layers) keeps
-// them in their memory layout, filled by LDS-DMA, and forms the fragments
-// with transposing LDS reads (below).
+// memory-contiguous positions.  The operands stay in LDS in their memory
+// layout (positions, then channels), filled by LDS-DMA, and the fragments,
+// which need 8 consecutive positions of one channel per lane, come from
+// transposing LDS reads; wgrad_tr works row by row, wgrad_grp over groups of
+// rows and channel tiles (below).
 //
 // A workgroup owns a tile of 32x32 output blocks and a fixed contiguous band
 // of the rows (partition p of GP), accumulating over all of them in
@@ -88,271 +86,11 @@ __device__ __forceinline__ void decode_row(const WgArgs& a, int row, int& s, int
   h = q - d * a.sh[s].ext[1];
 }
 
-// --------------------------------------------------------------------------
-// matrix-core kernel
-// --------------------------------------------------------------------------
-
-template <int NDIM_, int K_, int CIN_, int COUT_, int WGM_, int WGN_, int WM_, int WN_, int TILES_M_, int TILES_N_,
-          int LW_ = 0>
-struct WgCfg {
-  static constexpr int NDIM = NDIM_, K = K_, CIN = CIN_, COUT = COUT_;
-  static constexpr int WGM = WGM_, WGN = WGN_, WM = WM_, WN = WN_;
-  static constexpr int P = K / 2;
-  static constexpr int TAPS = NDIM == 3 ? K * K * K : K * K;
-  static constexpr int R = NDIM == 3 ? K * K : K;        // tap rows off the W axis
-  static constexpr int MR = K * COUT, NR = R * CIN;       // rows of A and of B
-  static constexpr int MB = (MR + 31) / 32, NB = (NR + 31) / 32;
-  static constexpr int TM = WGM * WM, TN = WGN * WN;     // blocks per tile
-  static constexpr int TILES_M = TILES_M_, TILES_N = TILES_N_;
-  static constexpr int NWC = WGM * WGN;                  // waves with MFMA work
-  static constexpr int NW = NWC + LW_, NT = 64 * NW;    // plus LW_ waves that only load
-  static constexpr int COLS = 64;                        // chunk width along W
-  static constexpr int RS = COLS * 2;                    // LDS row stride (bytes), 16-byte slots permuted
-  static_assert(RS == 128, "8 slots of 16 bytes per row");
-  static constexpr int LA_ROWS = (TM < MB ? TM : MB) * 32;
-  static constexpr int LB_ROWS = (TN < NB ? TN : NB) * 32;
-  static constexpr int LDS = (LA_ROWS + LB_ROWS) * RS;
-  // loader: one wave instruction moves OG channel octets of 64 / OG columns
-  static constexpr int OCT_A = LA_ROWS / 8, OCT_B = LB_ROWS / 8;
-  // an octet group stays inside one tap shift (A) or one tap row (B)
-  static constexpr int OG_A = COUT / 8 < 8 ? COUT / 8 : 8;
-  static constexpr int OG_B = CIN / 8 < 8 ? CIN / 8 : 8;
-  static constexpr int G_A = OCT_A / OG_A, G_B = OCT_B / OG_B;   // octet groups
-  static constexpr int JG_A = 64 / OG_A, JG_B = 64 / OG_B;       // columns per loader instruction
-  static constexpr int A_PER = OCT_A / NW, B_PER = OCT_B / NW;
-  static_assert(COUT % 8 == 0 && CIN % 8 == 0, "channel octets");
-  static_assert(OCT_A % NW == 0 && OCT_B % NW == 0, "loader instructions divide the waves");
-  static_assert(OCT_A % OG_A == 0 && OCT_B % OG_B == 0, "octet groups");
-  static_assert(COUT % (8 * OG_A) == 0 && CIN % (8 * OG_B) == 0 && (TM * 32) % (8 * OG_A) == 0 &&
-                (TN * 32) % (8 * OG_B) == 0, "octet groups do not straddle taps");
-  static_assert(TILES_M * TM >= MB && TILES_N * TN >= NB, "tiles cover the blocks");
-};
-
-// 16-byte slot permutation of LDS row r (8 slots of a 128-byte row)
-__device__ __forceinline__ int wg_key(int r) { return ((r >> 1) ^ (r >> 3)) & 7; }
-
-struct WgChunk {
-  int row, j0;
-  bool valid;
-  // per row (uniform): dy at (n, d, h, column 0), x at (n, d, h) for tap
-  // (0, 0) and column u = 0, the shard's x strides and row length
-  const uint16_t* dyrow;
-  const uint16_t* xrow;
-  int32_t xs0, xs1, W;
-  int64_t dy_left, x_left;   // bytes from dyrow / xrow to the end of the shard buffer
-};
-
 // Partition p owns the contiguous band of rows [p * R / P, (p + 1) * R / P):
 // neighbouring output rows share x rows, which a band then reads from the
 // same L2.
 __device__ __forceinline__ int band_begin(const WgArgs& a, int p) {
   return (int)(((int64_t)p * a.total_rows) / a.parts);
-}
-
-__device__ __forceinline__ WgChunk first_chunk(const WgArgs& a, int row, int row_end) {
-  WgChunk c{};
-  c.row = row;
-  c.j0 = 0;
-  c.valid = row < row_end;
-  int s = 0, n = 0, d = 0, h = 0;
-  if (c.valid) decode_row(a, row, s, n, d, h);
-  const WgShard& sh = a.sh[s];
-  c.dyrow = static_cast<const uint16_t*>(sh.dy) + (int64_t)n * sh.dn + (int64_t)(d + sh.dyo[0]) * sh.ds[0] +
-            (int64_t)(h + sh.dyo[1]) * sh.ds[1] + (int64_t)sh.dyo[2] * sh.ds[2];
-  c.xrow = static_cast<const uint16_t*>(sh.x) + (int64_t)n * sh.xn + (int64_t)(d + sh.xo[0]) * sh.xs[0] +
-           (int64_t)(h + sh.xo[1]) * sh.xs[1] + (int64_t)sh.xo[2] * sh.xs[2];
-  c.xs0 = (int32_t)sh.xs[0];
-  c.xs1 = (int32_t)sh.xs[1];
-  c.W = sh.ext[2];
-  c.dy_left = ((int64_t)a.batch * sh.dn - (c.dyrow - static_cast<const uint16_t*>(sh.dy))) * 2;
-  c.x_left = ((int64_t)a.batch * sh.xn - (c.xrow - static_cast<const uint16_t*>(sh.x))) * 2;
-  return c;
-}
-
-// the chunk after c: 64 columns further along the row, else the band's next row
-template <int K>
-__device__ __forceinline__ WgChunk next_chunk(const WgArgs& a, WgChunk c, int cols, int row_end) {
-  if (!c.valid) return c;
-  if (c.j0 + cols < c.W + 2 * (K / 2)) {
-    c.j0 += cols;
-    return c;
-  }
-  return first_chunk(a, c.row + 1, row_end);
-}
-
-template <class C>
-__global__ __launch_bounds__(C::NT) void wgrad_mfma(const WgArgs a) {
-  // two LDS stages: the MFMAs read one while the other is written (1 KiB
-  // aligned: the slot permutation XORs address bits 4-6)
-  __shared__ __attribute__((aligned(1024))) char stage0[C::LDS];
-  __shared__ __attribute__((aligned(1024))) char stage1[C::LDS];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, g2 = lane >> 5;
-  const int ntile = C::TILES_M * C::TILES_N;
-  const int tile = blockIdx.x % ntile;
-  const int part = blockIdx.x / ntile;
-  const int m0 = (tile / C::TILES_N) * C::TM * 32;        // first A row of the tile
-  const int n0 = (tile % C::TILES_N) * C::TN * 32;        // first B row of the tile
-  const int wm = (wave % C::NWC) / C::WGN, wn = (wave % C::NWC) % C::WGN;
-  const bool mma = wave < C::NWC;                       // a loader-only wave skips the MFMAs
-
-  f32x16 acc[C::WM][C::WN];
-#pragma unroll
-  for (int i = 0; i < C::WM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::WN; ++j) acc[i][j] = f32x16{};
-
-  uint4 ra0[C::A_PER], rb0[C::B_PER];
-  // Loader instruction k (k = wave + q * NW) of a chunk covers octet group
-  // g = k % G (OG octet rows, all in one tap shift or tap row) at column group
-  // jg = k / G (64 / OG columns); lane l takes octet l % OG of column l / OG,
-  // so OG lanes read one contiguous run of channels.  Everything but the lane
-  // terms is wave-uniform.
-  auto fetch = [&](const WgChunk& ch, uint4 (&qa)[C::A_PER], uint4 (&qb)[C::B_PER]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < C::A_PER; ++q) {
-      const int k = wave + q * C::NW;
-      const int mb = m0 + (k % C::G_A) * (8 * C::OG_A);          // first A row of the group
-      const int tx = mb / C::COUT;
-      const int i = ch.j0 + (k / C::G_A) * C::JG_A - tx + lane / C::OG_A;
-      const bool ok = ch.valid && mb < C::MR && (unsigned)i < (unsigned)ch.W;
-      const int off = ok ? i * C::COUT + (mb % C::COUT) + 8 * (lane % C::OG_A) : 0;
-      const uint4 v = *reinterpret_cast<const uint4*>(ch.dyrow + off);
-      qa[q] = ok ? v : make_uint4(0, 0, 0, 0);
-    }
-    const int uend = ch.W + 2 * C::P;                       // columns u with an x cell
-#pragma unroll
-    for (int q = 0; q < C::B_PER; ++q) {
-      const int k = wave + q * C::NW;
-      const int nb = n0 + (k % C::G_B) * (8 * C::OG_B);          // first B row of the group
-      const int r = nb / C::CIN;
-      const int tz = C::NDIM == 3 ? r / C::K : 0;
-      const int ty = C::NDIM == 3 ? r % C::K : r;
-      const int u = ch.j0 + (k / C::G_B) * C::JG_B + lane / C::OG_B;
-      const bool ok = ch.valid && nb < C::NR && u < uend;
-      const int off = ok ? tz * ch.xs0 + ty * ch.xs1 + u * C::CIN + (nb % C::CIN) + 8 * (lane % C::OG_B) : 0;
-      const uint4 v = *reinterpret_cast<const uint4*>(ch.xrow + off);
-      qb[q] = ok ? v : make_uint4(0, 0, 0, 0);
-    }
-  };
-  // registers -> LDS, transposed: the 8 channels of a column go to 8 rows.
-  // Row r keeps its 16-byte column slots permuted by key(r) = ((r >> 1) ^
-  // (r >> 3)) & 7, so that both the 8-row column writes and the 32-row
-  // fragment reads spread over the banks.  For r = 8 ro + e the key is
-  // (4 ro ^ ro ^ (e >> 1)) & 7, so one base address per item serves all 8 rows.
-  auto put = [&](char* base, int ro, int j, const uint4& v) __attribute__((always_inline)) {
-    const int slot = ((j >> 3) ^ ro ^ (ro << 2)) & 7;
-    char* p = base + ro * 8 * C::RS + (slot << 4) + (j & 7) * 2;
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      char* pe = reinterpret_cast<char*>(reinterpret_cast<uintptr_t>(p) ^ (uintptr_t)((e >> 1) << 4)) + e * C::RS;
-      *reinterpret_cast<uint16_t*>(pe) = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-    }
-  };
-  auto store = [&](char* st, const uint4 (&qa)[C::A_PER], const uint4 (&qb)[C::B_PER]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < C::A_PER; ++q) {
-      const int k = wave + q * C::NW;
-      put(st, (k % C::G_A) * C::OG_A + lane % C::OG_A, (k / C::G_A) * C::JG_A + lane / C::OG_A, qa[q]);
-    }
-#pragma unroll
-    for (int q = 0; q < C::B_PER; ++q) {
-      const int k = wave + q * C::NW;
-      put(st + C::LA_ROWS * C::RS, (k % C::G_B) * C::OG_B + lane % C::OG_B, (k / C::G_B) * C::JG_B + lane / C::OG_B,
-          qb[q]);
-    }
-  };
-  // fragments of K step ks (8 consecutive columns per lane: one 16-byte slot)
-  auto frags = [&](const char* st, int ks, bf16x8 (&av)[C::WM], bf16x8 (&bv)[C::WN]) __attribute__((always_inline)) {
-    const char* la = st;
-    const char* lb = st + C::LA_ROWS * C::RS;
-    const int slot = ks * 2 + g2;
-#pragma unroll
-    for (int i = 0; i < C::WM; ++i) {
-      const int row = (wm * C::WM + i) * 32 + l32;
-      av[i] = *reinterpret_cast<const bf16x8*>(la + row * C::RS + ((slot ^ wg_key(row)) << 4));
-    }
-#pragma unroll
-    for (int j = 0; j < C::WN; ++j) {
-      const int row = (wn * C::WN + j) * 32 + l32;
-      bv[j] = *reinterpret_cast<const bf16x8*>(lb + row * C::RS + ((slot ^ wg_key(row)) << 4));
-    }
-  };
-  auto mfmas = [&](const bf16x8 (&av)[C::WM], const bf16x8 (&bv)[C::WN]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < C::WM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::WN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-  };
-
-  const int row_end = band_begin(a, part + 1);
-  // chunks of this partition: c0 in stage0, c1 staged in registers
-  WgChunk c0 = first_chunk(a, band_begin(a, part), row_end);
-  WgChunk c1 = next_chunk<C::K>(a, c0, C::COLS, row_end);
-  fetch(c0, ra0, rb0);
-  store(stage0, ra0, rb0);
-  fetch(c1, ra0, rb0);
-  __syncthreads();
-  // one chunk per phase; the loop body handles two so that the LDS stages
-  // alternate at compile time.  In a phase: K step 0's fragments, the next
-  // chunk's registers into the other stage, the chunk after that into the
-  // registers, and each K step's MFMAs with the next step's fragments in
-  // flight.
-  auto phase = [&](auto P) __attribute__((always_inline)) {
-    constexpr int par = decltype(P)::value;
-    char* const cur = par ? stage1 : stage0;
-    char* const nxt = par ? stage0 : stage1;
-    const WgChunk c2 = next_chunk<C::K>(a, c1, C::COLS, row_end);
-    const int nks = (min(C::COLS, c0.W + 2 * C::P - c0.j0) + 15) / 16;
-    bf16x8 av0[C::WM], bv0[C::WN], av1[C::WM], bv1[C::WN];
-    if (mma) frags(cur, 0, av0, bv0);
-    if (c1.valid) store(nxt, ra0, rb0);                    // the next chunk, while this one computes
-    fetch(c2, ra0, rb0);                                    // and the one after it
-    if (mma) {
-      if (nks > 1) frags(cur, 1, av1, bv1);
-      mfmas(av0, bv0);
-      if (nks > 1) {
-        if (nks > 2) frags(cur, 2, av0, bv0);
-        mfmas(av1, bv1);
-        if (nks > 2) {
-          if (nks > 3) frags(cur, 3, av1, bv1);
-          mfmas(av0, bv0);
-          if (nks > 3) mfmas(av1, bv1);
-        }
-      }
-    }
-    __syncthreads();
-    c0 = c1;
-    c1 = c2;
-  };
-  while (c0.valid) {
-    phase(std::integral_constant<int, 0>{});
-    if (!c0.valid) break;
-    phase(std::integral_constant<int, 1>{});
-  }
-
-  // partial dw of this partition: C[(tx, o)][(r, c)] -> [o][c][r * K + tx]
-  if (!mma) return;
-  float* out = a.partial + (size_t)part * C::COUT * C::CIN * C::TAPS;
-#pragma unroll
-  for (int i = 0; i < C::WM; ++i) {
-#pragma unroll
-    for (int j = 0; j < C::WN; ++j) {
-      const int nn = n0 + (wn * C::WN + j) * 32 + l32;
-      if (nn >= C::NR) continue;
-      const int r = nn / C::CIN, c = nn % C::CIN;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + (wm * C::WM + i) * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
-        if (m >= C::MR) continue;
-        const int tx = m / C::COUT, o = m % C::COUT;
-        out[((size_t)o * C::CIN + c) * C::TAPS + r * C::K + tx] = acc[i][j][e];
-      }
-    }
-  }
 }
 
 // --------------------------------------------------------------------------
@@ -368,9 +106,9 @@ __global__ __launch_bounds__(C::NT) void wgrad_mfma(const WgArgs a) {
 // and the MFMA fragments, which need 8 consecutive positions of one channel
 // per lane, come from two ds_read_b64_tr_b16 each: within a group of 16
 // lanes, source lane s reads 4 consecutive channels of position k0 + s/4,
-// and output lane i receives channel i of positions k0 .. k0 + 3.  Chunks,
-// K steps and partitions are those of wgrad_mfma, so each MFMA sees the
-// same operands in the same positions.
+// and output lane i receives channel i of positions k0 .. k0 + 3.  A chunk is
+// 64 columns of a row (a row's tail of up to 16 more joins its last chunk);
+// a partition sums its rows in order, chunk by chunk and K step by K step.
 
 template <int NDIM_, int K_, int CIN_, int COUT_, int WGM_, int WGN_, int WM_, int WN_, int TILES_N_, int LW_ = 0>
 struct WtCfg {
@@ -671,6 +409,309 @@ __global__ __launch_bounds__(C::NT) void wgrad_tr(const WgArgs a) {
 }
 
 // --------------------------------------------------------------------------
+// matrix-core kernel over row groups and channel tiles
+// --------------------------------------------------------------------------
+//
+// wgrad_tr's operand handling (memory-layout runs in LDS by LDS-DMA,
+// fragments by transposing reads), with two changes.  (1) A chunk step covers
+// G consecutive output rows h0 .. h0 + G - 1 of one (shard, n, d): output row
+// g reads x rows (d + tz, h0 + g + ty), so the step loads the K (G + K - 1)
+// x runs (tz, h0 + t), t < G + K - 1, once for all G rows instead of K^2
+// runs per row.  (2) A workgroup's tile is OT output channels x every tap
+// shift (M) by CT input channels x RT tap rows (N), so layers with more
+// channels than one tile holds split into channel ranges, each tile reading
+// only its channels.  A partition's sums run group by group, chunk by chunk,
+// row by row and K step by K step: a fixed order for a given shard plan.
+
+template <int NDIM_, int K_, int CIN_, int COUT_, int OT_, int CT_, int G_, int COLS_, int WGM_, int WGN_, int WM_,
+          int WN_, int LW_ = 0>
+struct WrCfg {
+  static constexpr int NDIM = NDIM_, K = K_, CIN = CIN_, COUT = COUT_;
+  static constexpr int OT = OT_, CT = CT_, G = G_;
+  static constexpr int WGM = WGM_, WGN = WGN_, WM = WM_, WN = WN_;
+  static constexpr int P = K / 2;
+  static constexpr int TAPS = NDIM == 3 ? K * K * K : K * K;
+  static constexpr int R = NDIM == 3 ? K * K : K;        // tap rows (tz, ty)
+  static constexpr int KZ = NDIM == 3 ? K : 1;           // tz values
+  static constexpr int MRT = K * OT, NRT = R * CT;       // tile rows of A (tx, o) and of B (r, c)
+  static constexpr int TM = WGM * WM, TN = WGN * WN;     // blocks per tile
+  static constexpr int TILES_O = COUT / OT, TILES_C = CIN / CT, NTILE = TILES_O * TILES_C;
+  static constexpr int NWC = WGM * WGN, NW = NWC + LW_, NT = 64 * NW;
+  static constexpr int COLS = COLS_, CMAX = COLS + 16;   // a row's last chunk takes up to 16 more columns
+  static constexpr int NKS = CMAX / 16;                  // K steps of the widest chunk
+  static constexpr int DQ = CMAX + K - 1;                // dy positions of a chunk
+  static constexpr int DPT = OT * 2, XPT = CT * 2;       // bytes per position in LDS
+  static constexpr int HR = G + K - 1;                   // x rows per tz of a group
+  static constexpr int D_RUN = DQ * DPT;                 // one output row's dy run
+  static constexpr int X_RUN = CMAX * XPT;               // one x run
+  static constexpr int D_BYTES = (G * D_RUN + 1023) / 1024 * 1024;
+  static constexpr int NJ = (D_BYTES + KZ * HR * X_RUN + 1023) / 1024;
+  static constexpr int JPW = (NJ + NW - 1) / NW;         // transfers per wave, every wave the same
+  static constexpr int STAGE = JPW * NW * 1024;
+  static constexpr int LDS = 2 * STAGE;
+  static_assert(TM * 32 >= MRT && TN * 32 >= NRT, "one tile of blocks spans the tile's rows");
+  static_assert(COUT % OT == 0 && CIN % CT == 0 && OT % 16 == 0 && CT % 16 == 0,
+                "channel tiles in whole 16-channel groups (one lane group reads one tap shift / tap row)");
+  static_assert(DPT % 16 == 0 && XPT % 16 == 0 && D_RUN % 16 == 0, "16-byte slots");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void wgrad_grp(const WgArgs a) {
+  __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s* lds_v4s;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int tile = blockIdx.x % C::NTILE;
+  const int part = blockIdx.x / C::NTILE;
+  const int o0 = (tile / C::TILES_C) * C::OT;         // the tile's output channels
+  const int c0 = (tile % C::TILES_C) * C::CT;         // and input channels
+  const int wm = (wave % C::NWC) / C::WGN, wn = (wave % C::NWC) % C::WGN;
+  const bool mma = wave < C::NWC;
+
+  f32x16 acc[C::WM][C::WN];
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) acc[i][j] = f32x16{};
+
+  // fragment offsets for output row 0 of a group and K step 0 (a row adds
+  // D_RUN / X_RUN, a K step 16 positions): lane s of 16-lane group q reads
+  // position 8 (q >> 1) + s / 4 (+ 4 for its second read) at the 4 channels
+  // 16 (q & 1) + 4 (s & 3) of its 32-row block
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int kq = 8 * (g16 >> 1) + (s16 >> 2);
+  const int rq = 16 * (g16 & 1) + 4 * (s16 & 3);
+  int aoff[C::WM], boff[C::WN];
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i) {
+    int mrow = (wm * C::WM + i) * 32 + rq;
+    mrow = mrow < C::MRT ? mrow : 0;                  // padding rows read anything: their sums are not stored
+    const int tx = mrow / C::OT, oi = mrow % C::OT;
+    aoff[i] = (kq + (C::K - 1) - tx) * C::DPT + oi * 2;
+  }
+#pragma unroll
+  for (int j = 0; j < C::WN; ++j) {
+    int nrow = (wn * C::WN + j) * 32 + rq;
+    nrow = nrow < C::NRT ? nrow : 0;
+    const int r = nrow / C::CT, ci = nrow % C::CT;
+    const int tz = C::NDIM == 3 ? r / C::K : 0, ty = C::NDIM == 3 ? r % C::K : r;
+    boff[j] = C::D_BYTES + (tz * C::HR + ty) * C::X_RUN + kq * C::XPT + ci * 2;
+  }
+  auto frags = [&](const char* st, int g, int ks, bf16x8 (&av)[C::WM], bf16x8 (&bv)[C::WN])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i) {
+      const char* p = st + aoff[i] + g * C::D_RUN + ks * 16 * C::DPT;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)p);
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * C::DPT));
+      av[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      const char* p = st + boff[j] + g * C::X_RUN + ks * 16 * C::XPT;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)p);
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * C::XPT));
+      bv[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto mfmas = [&](const bf16x8 (&av)[C::WM], const bf16x8 (&bv)[C::WN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::WN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  };
+
+  // A step: rows h0 .. h0 + ng - 1 (ng <= G) of one (shard, n, d) in the band,
+  // columns [j0, j0 + len) of them.  Rows advance incrementally from one
+  // decode at the band's start.
+  struct Step {
+    int valid, row, ng, s, n, d, h, j0, W;
+    int32_t xs0, xs1;
+    const char* dyrow;       // dy at (n, d, h), output column 0
+    const char* xrow;        // x at tap (0, 0) of output row (n, d, h), column 0
+    int64_t dy_left, x_left; // bytes from there to the end of the shard buffer
+  };
+  const int row_end = band_begin(a, part + 1);
+  auto set_rows = [&](Step& c) __attribute__((always_inline)) {
+    const WgShard& sh = a.sh[c.s];
+    c.ng = min(min(C::G, sh.ext[1] - c.h), row_end - c.row);
+    const int64_t dyo = (int64_t)c.n * sh.dn + (int64_t)(c.d + sh.dyo[0]) * sh.ds[0] +
+                        (int64_t)(c.h + sh.dyo[1]) * sh.ds[1] + (int64_t)sh.dyo[2] * sh.ds[2];
+    const int64_t xo = (int64_t)c.n * sh.xn + (int64_t)(c.d + sh.xo[0]) * sh.xs[0] + (int64_t)(c.h + sh.xo[1]) * sh.xs[1] +
+                       (int64_t)sh.xo[2] * sh.xs[2];
+    c.dyrow = static_cast<const char*>(sh.dy) + dyo * 2;
+    c.xrow = static_cast<const char*>(sh.x) + xo * 2;
+    c.dy_left = ((int64_t)a.batch * sh.dn - dyo) * 2;
+    c.x_left = ((int64_t)a.batch * sh.xn - xo) * 2;
+    c.xs0 = (int32_t)sh.xs[0];
+    c.xs1 = (int32_t)sh.xs[1];
+    c.W = sh.ext[2];
+  };
+  auto first_step = [&]() __attribute__((always_inline)) -> Step {
+    Step c{};
+    c.row = band_begin(a, part);
+    c.valid = c.row < row_end;
+    if (c.valid) decode_row(a, c.row, c.s, c.n, c.d, c.h);
+    c.j0 = 0;
+    set_rows(c);
+    return c;
+  };
+  auto chunk_len = [&](const Step& c) __attribute__((always_inline)) -> int {
+    const int rem = c.W + 2 * C::P - c.j0;
+    return rem <= C::CMAX ? rem : C::COLS;
+  };
+  auto next_of = [&](const Step& c) __attribute__((always_inline)) -> Step {
+    if (!c.valid) return c;
+    Step n = c;
+    const int len = chunk_len(c);
+    if (c.j0 + len < c.W + 2 * C::P) {
+      n.j0 += len;
+      return n;
+    }
+    n.j0 = 0;
+    n.row = c.row + c.ng;
+    n.valid = n.row < row_end;
+    if (!n.valid) return n;
+    n.h += c.ng;
+    if (n.h == a.sh[n.s].ext[1]) {
+      n.h = 0;
+      if (++n.d == a.sh[n.s].ext[0]) {
+        n.d = 0;
+        if (++n.n == a.batch) {
+          n.n = 0;
+          ++n.s;
+        }
+      }
+    }
+    set_rows(n);
+    return n;
+  };
+
+  // One step into a stage by LDS-DMA: the ng dy runs ([position][OT
+  // channels], positions j0 - k + 1 ..), then the x runs (tz, t) for t < HR
+  // ([position][CT channels], positions j0 ..).  Transfer j moves 1 KiB:
+  // lane l's 16 bytes are slot 64 j + l.  Positions outside a row, rows past
+  // the group or the shard and the stage's padding slots get an out-of-range
+  // offset and land as zeros; every wave issues exactly JPW transfers (an
+  // invalid step's too), so its count of outstanding transfers per step is
+  // the constant JPW.  The per-lane parts are fixed per kernel.
+  int tq[C::JPW];            // dy: output row g; x: tz * HR + t (-1: padding slot)
+  int tp[C::JPW];            // position within the run
+  int tc[C::JPW];            // byte offset of the slot's 8 channels within its position
+  {
+    constexpr int DSL = C::DPT / 16, XSL = C::XPT / 16;
+    constexpr int D_SLOTS = C::D_BYTES / 16, RUN_D = C::D_RUN / 16, RUN_X = C::X_RUN / 16;
+#pragma unroll
+    for (int q = 0; q < C::JPW; ++q) {
+      const int slot = 64 * (wave + q * C::NW) + lane;
+      if (slot < D_SLOTS) {
+        const int g = slot / RUN_D, rem = slot - g * RUN_D;
+        tq[q] = g < C::G ? g : -1;
+        tp[q] = rem / DSL;
+        tc[q] = (o0 + 8 * (rem % DSL)) * 2;
+      } else {
+        const int xs = slot - D_SLOTS;
+        const int run = xs / RUN_X, rem = xs - run * RUN_X;
+        tq[q] = run < C::KZ * C::HR ? run : -1;
+        tp[q] = rem / XSL;
+        tc[q] = (c0 + 8 * (rem % XSL)) * 2;
+      }
+    }
+  }
+  auto fetch = [&](char* dst, const Step& c) __attribute__((always_inline)) {
+    constexpr int D_SLOTS = C::D_BYTES / 16;
+    const __amdgpu_buffer_rsrc_t rd = wt_rsrc(c.dyrow, c.valid ? c.dy_left : 0);
+    const __amdgpu_buffer_rsrc_t rx = wt_rsrc(c.xrow, c.valid ? c.x_left : 0);
+    const int i0 = c.j0 - (C::K - 1);
+    const int uend = c.W + 2 * C::P - c.j0;          // chunk columns with an x cell
+    // x rows: tz planes down, t rows along H; a row exists up to the padded extent
+    const WgShard& sh = a.sh[c.s];
+    const int hrows = (int)(sh.xs[0] / sh.xs[1]) - (c.h + sh.xo[1]);   // padded rows from tap row 0
+#pragma unroll
+    for (int q = 0; q < C::JPW; ++q) {
+      const int j = wave + q * C::NW;
+      if (j * 64 < D_SLOTS) {                         // wave-uniform: a transfer is all dy or all x
+        const int i = i0 + tp[q];
+        const bool ok = tq[q] >= 0 && tq[q] < c.ng && tp[q] < C::DQ && i >= 0 && i < c.W;
+        const uint32_t off =
+            ok ? (uint32_t)(tq[q] * (int)(sh.ds[1] * 2) + i * (C::COUT * 2) + tc[q]) : kWtOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr)(dst + j * 1024), 16, off, 0, 0, 0);
+      } else {
+        const int tz = tq[q] / C::HR, t = tq[q] - tz * C::HR;
+        const bool ok = tq[q] >= 0 && t < c.ng + C::K - 1 && t < hrows && tp[q] < uend;
+        const uint32_t off =
+            ok ? (uint32_t)((tz * c.xs0 + t * c.xs1 + (c.j0 + tp[q]) * C::CIN) * 2 + tc[q]) : kWtOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(dst + j * 1024), 16, off, 0, 0, 0);
+      }
+    }
+  };
+
+  Step c0s = first_step();
+  fetch(stage0, c0s);
+  __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
+  __syncthreads();
+  // one step per phase, two phases per loop turn so that the stages alternate
+  // at compile time; inside a step the (row, K step) pairs are pipelined:
+  // the fragments of the next pair are read while the current pair's MFMAs run
+  auto phase = [&](auto PP) __attribute__((always_inline)) {
+    constexpr int par = decltype(PP)::value;
+    const char* const cur = par ? stage1 : stage0;
+    char* const nxt = par ? stage0 : stage1;
+    const Step c1s = next_of(c0s);
+    fetch(nxt, c1s);
+    if (mma) {
+      const int nks = (chunk_len(c0s) + 15) / 16;
+      const int ng = c0s.ng;
+      constexpr int NP = C::G * C::NKS;
+      bf16x8 av[2][C::WM], bv[2][C::WN];
+      frags(cur, 0, 0, av[0], bv[0]);
+#pragma unroll
+      for (int t = 0; t < NP; ++t) {
+        const int g = t / C::NKS, ks = t % C::NKS;
+        const int g1 = (t + 1) / C::NKS, ks1 = (t + 1) % C::NKS;
+        if (t + 1 < NP && g1 < ng && ks1 < nks) frags(cur, g1, ks1, av[(t + 1) & 1], bv[(t + 1) & 1]);
+        if (g < ng && ks < nks) mfmas(av[t & 1], bv[t & 1]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0): this wave's transfers are in LDS
+    __syncthreads();
+    c0s = c1s;
+  };
+  while (c0s.valid) {
+    phase(std::integral_constant<int, 0>{});
+    if (!c0s.valid) break;
+    phase(std::integral_constant<int, 1>{});
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  // partial dw of this partition: C[(tx, o)][(r, c)] -> [o][c][r * K + tx]
+  if (!mma) return;
+  float* out = a.partial + (size_t)part * C::COUT * C::CIN * C::TAPS;
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i) {
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      const int nn = (wn * C::WN + j) * 32 + l32;
+      if (nn >= C::NRT) continue;
+      const int r = nn / C::CT, c = c0 + nn % C::CT;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = (wm * C::WM + i) * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+        if (m >= C::MRT) continue;
+        const int tx = m / C::OT, o = o0 + m % C::OT;
+        out[((size_t)o * C::CIN + c) * C::TAPS + r * C::K + tx] = acc[i][j][e];
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
 // direct kernel (fp32, and bf16 shapes without a matrix-core instance)
 // --------------------------------------------------------------------------
 
@@ -725,18 +766,18 @@ __global__ void wgrad_reduce(const float* __restrict__ partial, int parts, int64
 // instances and launch
 // --------------------------------------------------------------------------
 
-// image 64->64 k3: 6x6 blocks, 2x2 waves of 3x3
-using WgImg64 = WgCfg<2, 3, 64, 64, 2, 2, 3, 3, 1, 1>;
-// 3D 32->32 k3: 3x9 blocks, 1x3 waves of 3x3, and a fourth wave that only loads
-using WgVol32 = WgCfg<3, 3, 32, 32, 1, 3, 3, 3, 1, 1, 1>;
-// 3D 16->16 k5: 3x13 blocks in two tiles of 3x8, 1x4 waves of 3x2
-using WgVol16k5 = WgCfg<3, 5, 16, 16, 1, 4, 3, 2, 1, 2>;
-// image 256->256 k3: 24x24 blocks in 4x4 tiles of 6x6, 2x2 waves of 3x3
-using WgImg256 = WgCfg<2, 3, 256, 256, 2, 2, 3, 3, 4, 4>;
-// transposing-read kernel: the same tilings (one tile along M)
-using WtImg64 = WtCfg<2, 3, 64, 64, 2, 2, 3, 3, 1>;
-using WtVol32 = WtCfg<3, 3, 32, 32, 1, 3, 3, 3, 1, 1>;
-using WtVol16k5 = WtCfg<3, 5, 16, 16, 1, 4, 3, 2, 2>;
+// Instances.  Row-by-row kernel (wgrad_tr) where its 64 (up to 80) column
+// chunks move fewer bytes per output than row groups would (k 3: a group of
+// 4 rows needs 6 of the 12 x runs, but in half-width chunks); row groups
+// (wgrad_grp) for k 5, where a group of 4 rows loads 40 x runs instead of
+// 100, and for the 256-channel layer, which needs channel tiles.  Same-box
+// A/B of the two kernels on each layer: image 0.51 / 0.84 ms, 256^3
+// 1.74 / 2.28 ms, 512^3 k5 20.6 / 14.3 ms, 256-channel grid (the earlier
+// register-staged kernel) 4.55 / 3.87 ms.
+using WtImg64 = WtCfg<2, 3, 64, 64, 2, 2, 3, 3, 1>;                     // 6 x 6 blocks, 2 x 2 waves of 3 x 3
+using WtVol32 = WtCfg<3, 3, 32, 32, 1, 3, 3, 3, 1, 1>;                  // 3 x 9 blocks, 1 x 3 waves + a loader
+using WrVol16k5 = WrCfg<3, 5, 16, 16, 16, 16, 4, 32, 1, 4, 3, 4>;      // 3 x 13 (of 16) blocks, 1 x 4 waves
+using WrImg256 = WrCfg<2, 3, 256, 256, 64, 64, 4, 32, 2, 2, 3, 3>;     // 4 x 4 channel tiles of 6 x 6 blocks
 
 constexpr int kPartitions = 256;   // partial sums (workgroups per tile set): one per CU
 
@@ -749,11 +790,11 @@ struct WgInstance {
   void (*kernel)(WgArgs);
 };
 
+
 template <class C>
-WgInstance make_instance() {
-  const int ntile = C::TILES_M * C::TILES_N;
-  return WgInstance{C::NDIM, C::CIN, C::COUT, C::K, std::max(1, kPartitions / ntile), ntile, C::LDS, C::NT,
-                    wgrad_mfma<C>};
+WgInstance make_instance_grp() {
+  return WgInstance{C::NDIM, C::CIN, C::COUT, C::K, std::max(1, kPartitions / C::NTILE), C::NTILE, C::LDS, C::NT,
+                    wgrad_grp<C>};
 }
 
 template <class C>
@@ -764,7 +805,7 @@ WgInstance make_instance_tr() {
 
 const WgInstance* find_instance(int ndim, int cin, int cout, int k) {
   static const WgInstance table[] = {make_instance_tr<WtImg64>(), make_instance_tr<WtVol32>(),
-                                     make_instance_tr<WtVol16k5>(), make_instance<WgImg256>()};
+                                     make_instance_grp<WrVol16k5>(), make_instance_grp<WrImg256>()};
   for (const WgInstance& w : table)
     if (w.ndim == ndim && w.cin == cin && w.cout == cout && w.k == k) return &w;
   return nullptr;
