@@ -28,6 +28,7 @@
 //              with the combine in its prologue (one launch fewer)
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 #include <string>
 
 #include "internal.h"
@@ -96,6 +97,24 @@ __device__ __forceinline__ void decode_item(const GnArgs& a, int item, int& s, i
   const int r = item - a.sh[s].item_begin;
   n = r / a.sh[s].items_per_n;
   k = r - n * a.sh[s].items_per_n;
+}
+
+// rint(d * f) for a power of two f and |d * f| <= 2^51 (d * f is exact): the
+// fused multiply-add fl(d * f + 1.5 * 2^52) rounds once, to the integer
+// nearest d * f with ties to even (1.5 * 2^52 is even and its ulp is 1), and
+// its bit pattern exceeds that of 1.5 * 2^52 by exactly that integer, also
+// across the exponent step at 2^53.  Lanes add the patterns as 64-bit
+// integers (one instruction) and subtract count * bits(1.5 * 2^52) once, so
+// each term costs one FMA and one integer add instead of a multiply, a
+// rounding and an fp64 add, with the same exact sum.
+constexpr double kRoundMagic = 6755399441055744.0;            // 1.5 * 2^52
+constexpr uint64_t kRoundMagicBits = 0x4338000000000000ull;
+__device__ __forceinline__ uint64_t rint_bits(double d, double f) {
+  return (uint64_t)__double_as_longlong(fma(d, f, kRoundMagic));
+}
+// the exact sum of `count` terms accumulated by rint_bits (|sum| < 2^53)
+__device__ __forceinline__ double rint_sum(uint64_t acc, uint64_t count) {
+  return (double)(int64_t)(acc - count * kRoundMagicBits);
 }
 
 // exponents (e1, e2) of a group from its max |y| (bits)
@@ -195,9 +214,9 @@ __global__ __launch_bounds__(kNT) void gn_stats(const GnArgs a) {
     }
   }
   for (int i = tid; i < C; i += kNT) { s1[i] = 0.0; s2[i] = 0.0; }
-  double acc1[VW], acc2[VW];
+  uint64_t acc1[VW], acc2[VW], cnt = 0;   // FIXED: rint_bits sums over cnt terms per channel
 #pragma unroll
-  for (int j = 0; j < VW; ++j) { acc1[j] = 0.0; acc2[j] = 0.0; }
+  for (int j = 0; j < VW; ++j) { acc1[j] = 0; acc2[j] = 0; }
   int cur = -1, cur_s = 0, cur_n = 0;
   double f1[VW], f2[VW];
   auto flush = [&](int s, int n) {
@@ -206,8 +225,8 @@ __global__ __launch_bounds__(kNT) void gn_stats(const GnArgs a) {
       const int c0 = (tid * VW) % C;
 #pragma unroll
       for (int j = 0; j < VW; ++j) {
-        atomicAdd(&s1[c0 + j], acc1[j]);
-        atomicAdd(&s2[c0 + j], acc2[j]);
+        atomicAdd(&s1[c0 + j], rint_sum(acc1[j], cnt));
+        atomicAdd(&s2[c0 + j], rint_sum(acc2[j], cnt));
       }
     }
     __syncthreads();
@@ -221,7 +240,8 @@ __global__ __launch_bounds__(kNT) void gn_stats(const GnArgs a) {
     __syncthreads();
     for (int i = tid; i < C; i += kNT) { s1[i] = 0.0; s2[i] = 0.0; }
 #pragma unroll
-    for (int j = 0; j < VW; ++j) { acc1[j] = 0.0; acc2[j] = 0.0; }
+    for (int j = 0; j < VW; ++j) { acc1[j] = 0; acc2[j] = 0; }
+    cnt = 0;
   };
   for (int item = blockIdx.x; item < a.total_items; item += gridDim.x) {
     int s, n, k;
@@ -249,31 +269,42 @@ __global__ __launch_bounds__(kNT) void gn_stats(const GnArgs a) {
     const GnShard& sh = a.sh[s];
     const typename V::T* y = reinterpret_cast<const typename V::T*>(sh.y) + n * sh.vecs_per_n;
     const int64_t v0 = (int64_t)k * kNT * kIter + tid;
-    typename V::T val[kIter];
+    // an item that ends inside the shard needs no clamps or masks
+    auto body = [&](auto tail_tag) {
+      constexpr bool kTail = decltype(tail_tag)::value;
+      typename V::T val[kIter];
 #pragma unroll
-    for (int i = 0; i < kIter; ++i) {
-      const int64_t v = v0 + i * kNT;
-      // every load issues (clamped index; the tail is masked afterwards), so
-      // all of them are in flight before the first is used
-      const typename V::T t = load_nt<VW>(y, v < sh.vecs_per_n ? v : sh.vecs_per_n - 1);
-      val[i] = v < sh.vecs_per_n ? t : typename V::T{};   // zeros contribute 0
-    }
-#pragma unroll
-    for (int i = 0; i < kIter; ++i) {
-      const int64_t v = v0 + i * kNT;
-#pragma unroll
-      for (int j = 0; j < VW; ++j) {
-        const double d = (double)V::get(val[i], j);
-        if (FIXED) {
-          acc1[j] += rint(d * f1[j]);
-          acc2[j] += rint((d * d) * f2[j]);
-        } else if (v < sh.vecs_per_n) {
-          const int c = (int)((v * VW + j) % C);
-          atomicAdd(&s1[c], rint(d * sc1[c]));
-          atomicAdd(&s2[c], rint((d * d) * sc2[c]));
+      for (int i = 0; i < kIter; ++i) {
+        const int64_t v = v0 + i * kNT;
+        // every load issues (clamped index; the tail is masked afterwards), so
+        // all of them are in flight before the first is used
+        if (kTail) {
+          const typename V::T t = load_nt<VW>(y, v < sh.vecs_per_n ? v : sh.vecs_per_n - 1);
+          val[i] = v < sh.vecs_per_n ? t : typename V::T{};   // zeros contribute 0
+        } else {
+          val[i] = load_nt<VW>(y, v);
         }
       }
-    }
+#pragma unroll
+      for (int i = 0; i < kIter; ++i) {
+        const int64_t v = v0 + i * kNT;
+#pragma unroll
+        for (int j = 0; j < VW; ++j) {
+          const double d = (double)V::get(val[i], j);
+          if (FIXED) {
+            acc1[j] += rint_bits(d, f1[j]);
+            acc2[j] += rint_bits(d, d * f2[j]);   // d * (d * 2^e2) = d^2 * 2^e2 exactly
+          } else if (!kTail || v < sh.vecs_per_n) {
+            const int c = (int)((v * VW + j) % C);
+            atomicAdd(&s1[c], rint(d * sc1[c]));
+            atomicAdd(&s2[c], rint((d * d) * sc2[c]));
+          }
+        }
+      }
+    };
+    if ((int64_t)(k + 1) * kNT * kIter <= sh.vecs_per_n) body(std::false_type{});
+    else body(std::true_type{});
+    cnt += kIter;
   }
   if (cur >= 0) flush(cur_s, cur_n);
 }
@@ -524,10 +555,11 @@ __global__ __launch_bounds__(kNT) void gnb_stats(const GnbArgs b) {
     }
   }
   for (int i = tid; i < C; i += kNT) { s1[i] = 0.0; s2[i] = 0.0; }
-  double acc1[VW], acc2[VW], f1[VW], f2[VW];
+  uint64_t acc1[VW], acc2[VW], cnt = 0;   // FIXED: rint_bits sums over cnt terms per channel
+  double f1[VW], f2[VW];
   float mu[VW], rs[VW];
 #pragma unroll
-  for (int j = 0; j < VW; ++j) { acc1[j] = 0.0; acc2[j] = 0.0; }
+  for (int j = 0; j < VW; ++j) { acc1[j] = 0; acc2[j] = 0; }
   int cur = -1, cur_s = 0, cur_n = 0;
   auto flush = [&](int s, int n) {
     __syncthreads();
@@ -535,8 +567,8 @@ __global__ __launch_bounds__(kNT) void gnb_stats(const GnbArgs b) {
       const int c0 = (tid * VW) % C;
 #pragma unroll
       for (int j = 0; j < VW; ++j) {
-        atomicAdd(&s1[c0 + j], acc1[j]);
-        atomicAdd(&s2[c0 + j], acc2[j]);
+        atomicAdd(&s1[c0 + j], rint_sum(acc1[j], cnt));
+        atomicAdd(&s2[c0 + j], rint_sum(acc2[j], cnt));
       }
     }
     __syncthreads();
@@ -548,7 +580,8 @@ __global__ __launch_bounds__(kNT) void gnb_stats(const GnbArgs b) {
     __syncthreads();
     for (int i = tid; i < C; i += kNT) { s1[i] = 0.0; s2[i] = 0.0; }
 #pragma unroll
-    for (int j = 0; j < VW; ++j) { acc1[j] = 0.0; acc2[j] = 0.0; }
+    for (int j = 0; j < VW; ++j) { acc1[j] = 0; acc2[j] = 0; }
+    cnt = 0;
   };
   for (int item = blockIdx.x; item < a.total_items; item += gridDim.x) {
     int s, n, k;
@@ -603,8 +636,8 @@ __global__ __launch_bounds__(kNT) void gnb_stats(const GnbArgs b) {
           if (FIXED) {
             const float yh = (V::get(vy[i], j) - mu[j]) * rs[j];
             const double d = in ? (double)V::get(vd[i], j) : 0.0;   // the tail contributes 0
-            acc1[j] += rint(d * f1[j]);
-            acc2[j] += rint((d * (double)yh) * f2[j]);
+            acc1[j] += rint_bits(d, f1[j]);
+            acc2[j] += rint_bits(d, (double)yh * f2[j]);   // d * (yh * 2^e2) exactly
           } else if (in) {
             const int c = (int)((v * VW + j) % C);
             const float yh = (V::get(vy[i], j) - mr[c].x) * mr[c].y;
@@ -615,6 +648,7 @@ __global__ __launch_bounds__(kNT) void gnb_stats(const GnbArgs b) {
         }
       }
     }
+    cnt += kIter;
   }
   if (cur >= 0) flush(cur_s, cur_n);
 }
