@@ -492,10 +492,26 @@ __global__ __launch_bounds__(kNT) void gn_apply_stream(const GnArgs a) {
 
 // dy written into another shard layout (a padded plan, fp32 or bf16):
 // element (n, d, h, w, c) of a shard at p + n*sn + d*sd + h*sh + w*C + c
+// n / d for 0 <= n < 2^31 as (n * m) >> p, with p = 31 + ceil(log2 d) and
+// m = ceil(2^p / d) < 2^32: the error n (m - 2^p / d) / 2^p stays below 1 / d,
+// so the floor is exact (the round-up multiplier method)
+struct FastDiv {
+  uint32_t m;
+  int32_t p;
+};
+FastDiv fast_div(uint32_t d) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  const int p = 31 + l;
+  return FastDiv{(uint32_t)(((1ull << p) + d - 1) / d), p};
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (uint32_t)(((uint64_t)n * f.m) >> f.p); }
+
 struct GnbOut {
   void* p;                      // the shard's interior origin
   int64_t sn, sd, sh;           // element strides
   int32_t H, W;                 // interior extents of the two inner spatial axes
+  FastDiv fH, fW;               // dividers by H and W
 };
 
 enum GnbMode { kDyLikeY = 0, kDyPaddedF32 = 1, kDyPaddedBf16 = 2 };
@@ -509,6 +525,7 @@ struct GnbArgs {
   float4* bchan;                // [N][C] (mean, a, k, b)
   float* dgamma;                // [C] or NULL
   float* dbeta;                 // [C] or NULL
+  FastDiv fCv;                  // divider by C / VW (vectors per position)
   GnbOut out[ST_MAX_SHARDS];    // kDyPadded*: where dy goes
 };
 static_assert(sizeof(GnbArgs) <= kMaxKernargBytes, "kernel argument struct too large");
@@ -765,6 +782,74 @@ __global__ __launch_bounds__(kNT) void gnb_apply(const GnbArgs b) {
   }
 }
 
+// The backward apply as one vector per lane and one workgroup per chunk of
+// kNT vectors in chunk order (the streaming layout of gn_apply_stream).  The
+// batch item's coefficients go through LDS.  A padded dy takes its position,
+// row and plane by multiply-shift division (every vector index of a batch
+// item is below 2^31 on this path).
+template <int VW, int MODE>
+__global__ __launch_bounds__(kNT) void gnb_apply_stream(const GnbArgs b) {
+  using V = Vec<VW>;
+  const GnArgs& a = b.g;
+  extern __shared__ float4 srow[];                    // [C] (mean, a, k, b) of batch item n
+  const int tid = threadIdx.x;
+  const int C = a.channels;
+  const int chunk = blockIdx.x;
+  int s, n, k;
+  decode_item(a, chunk / kIter, s, n, k);
+  const GnShard& sh = a.sh[s];
+  const int64_t first = ((int64_t)k * kIter + chunk % kIter) * kNT;
+  if (first >= sh.vecs_per_n) return;                 // past the item's last vector: the whole workgroup
+  const int64_t v = first + tid;
+  const bool in = v < sh.vecs_per_n;
+  const typename V::T* y = reinterpret_cast<const typename V::T*>(sh.y) + n * sh.vecs_per_n;
+  const typename V::T* dz = reinterpret_cast<const typename V::T*>(sh.dz) + n * sh.vecs_per_n;
+  const typename V::T vy = load_nt<VW>(y, in ? v : first);
+  const typename V::T vd = load_nt<VW>(dz, in ? v : first);
+  for (int i = tid; i < C; i += kNT) srow[i] = b.bchan[(size_t)n * C + i];
+  __syncthreads();
+  if (!in) return;
+  // the VW channels of a vector sit at one position (VW == 4 only when C % 4 == 0)
+  int c0;
+  uint32_t pu = 0;
+  if constexpr (MODE == kDyLikeY) {
+    c0 = (int)((v * VW) % C);
+  } else {
+    const uint32_t vv = (uint32_t)v;
+    pu = fdiv(vv, b.fCv);
+    c0 = (int)(vv - pu * (uint32_t)(C / VW)) * VW;
+  }
+  float out[VW];
+#pragma unroll
+  for (int j = 0; j < VW; ++j) {
+    const float4 q = srow[c0 + j];
+    out[j] = fmaf(q.y, V::get(vd, j), fmaf(q.z, V::get(vy, j) - q.x, q.w));
+  }
+  if constexpr (MODE == kDyLikeY) {
+    typename V::T* dy = reinterpret_cast<typename V::T*>(sh.z) + n * sh.vecs_per_n;
+    if constexpr (VW == 4) {
+      typedef float nf4 __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(nf4{out[0], out[1], out[2], out[3]}, reinterpret_cast<nf4*>(&dy[v]));
+    }
+    else __builtin_nontemporal_store(out[0], &dy[v]);
+  } else {
+    const GnbOut& o = b.out[s];
+    const uint32_t tu = fdiv(pu, o.fW), du = fdiv(tu, o.fH);
+    const int w = (int)(pu - tu * (uint32_t)o.W);
+    const int hh = (int)(tu - du * (uint32_t)o.H);
+    const int64_t off = n * o.sn + (int64_t)du * o.sd + hh * o.sh + (int64_t)w * C + c0;
+    if constexpr (MODE == kDyPaddedF32) {
+      if constexpr (VW == 4) *reinterpret_cast<float4*>(static_cast<float*>(o.p) + off) =
+          make_float4(out[0], out[1], out[2], out[3]);
+      else static_cast<float*>(o.p)[off] = out[0];
+    } else {
+      if constexpr (VW == 4) *reinterpret_cast<uint2*>(static_cast<uint16_t*>(o.p) + off) =
+          make_uint2(bf16_rne(out[0]) | (bf16_rne(out[1]) << 16), bf16_rne(out[2]) | (bf16_rne(out[3]) << 16));
+      else static_cast<uint16_t*>(o.p)[off] = (uint16_t)bf16_rne(out[0]);
+    }
+  }
+}
+
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 st_gn_layout layout_of(const st_plan* p, int groups) {
@@ -944,6 +1029,19 @@ st_status launch_backward(GnbArgs& b, bool need_max, int mode, hipStream_t st) {
   hipLaunchKernelGGL(gnb_combine, dim3((nthreads + 63) / 64), dim3(64), 0, st, b);
   s = launch_check("st_groupnorm_backward: combine launch");
   if (s != ST_OK) return s;
+  // the chunked apply: coefficients within LDS, chunks within a grid, and
+  // for a padded dy every vector index of a batch item below 2^31
+  bool stream = stream_fits(a);
+  if (mode != kDyLikeY)
+    for (int i = 0; i < a.nshards; ++i) stream = stream && a.sh[i].vecs_per_n < ((int64_t)1 << 31);
+  if (stream) {
+    const dim3 grid(a.total_items * kIter);
+    const size_t shmem = (size_t)a.channels * sizeof(float4);
+    if (mode == kDyPaddedBf16) hipLaunchKernelGGL((gnb_apply_stream<VW, kDyPaddedBf16>), grid, dim3(kNT), shmem, st, b);
+    else if (mode == kDyPaddedF32) hipLaunchKernelGGL((gnb_apply_stream<VW, kDyPaddedF32>), grid, dim3(kNT), shmem, st, b);
+    else hipLaunchKernelGGL((gnb_apply_stream<VW, kDyLikeY>), grid, dim3(kNT), shmem, st, b);
+    return launch_check("st_groupnorm_backward: apply launch");
+  }
   const int agrid = std::max(1, std::min((kIter / kPart) * a.total_items, device_cus() * 16));
   if (mode == kDyPaddedBf16) hipLaunchKernelGGL((gnb_apply<VW, FIXED, kDyPaddedBf16>), dim3(agrid), dim3(kNT), 0, st, b);
   else if (mode == kDyPaddedF32) hipLaunchKernelGGL((gnb_apply<VW, FIXED, kDyPaddedF32>), dim3(agrid), dim3(kNT), 0, st, b);
@@ -1151,6 +1249,7 @@ st_status st_groupnorm_backward(const st_plan* y_plan, const float* const* y_buf
     if (vw != 4 && q->dtype == ST_BF16) return err(ST_ERR_UNSUPPORTED, "bf16 dy needs C divisible by 4");
     mode = q->dtype == ST_BF16 ? kDyPaddedBf16 : kDyPaddedF32;
     const int64_t C = q->channels;
+    b.fCv = fast_div((uint32_t)(C / vw));
     for (size_t i = 0; i < q->shards.size(); ++i) {
       if (!dy_bufs[i]) return err(ST_ERR_INVALID_ARG, "NULL dy buffer");
       if (!aligned16(dy_bufs[i])) return err(ST_ERR_ALIGNMENT, "dy buffers must be 16-byte aligned");
@@ -1161,6 +1260,8 @@ st_status st_groupnorm_backward(const st_plan* y_plan, const float* const* y_buf
       o.sn = sd.pad[0] * o.sd;
       o.H = (int32_t)sd.ext[1];
       o.W = (int32_t)sd.ext[2];
+      o.fH = fast_div((uint32_t)o.H);
+      o.fW = fast_div((uint32_t)o.W);
       const int64_t origin = q->halo[0] * o.sd + q->halo[1] * o.sh + q->halo[2] * C;
       o.p = static_cast<char*>(dy_bufs[i]) + origin * q->esize;
       if (dy_bufs[i] == static_cast<const void*>(y_bufs[i]) || dy_bufs[i] == static_cast<const void*>(dz_bufs[i]))
