@@ -83,7 +83,7 @@ struct st_plan {
 
 namespace st {
 constexpr int kHaloThreads = 256;
-constexpr int kHaloWordsPerThread = 4;
+constexpr int kHaloWordsPerThread = 2;
 constexpr int64_t kHaloWordsPerBlock = kHaloThreads * kHaloWordsPerThread;
 
 // Every kernel receives its per-shard table by value, sized for

@@ -393,11 +393,19 @@ st_status plan_device_table(st_plan* p, hipStream_t stream) {
   if (cap != hipStreamCaptureStatusNone)
     return fail(ST_ERR_UNSUPPORTED,
                 "the plan's descriptor table is not on the device yet: call st_plan_upload before capturing");
-  const size_t bytes = p->descs.size() * sizeof(HaloDesc);
-  s = hip_check(hipMalloc(&p->d_descs, bytes), "plan descriptor table: hipMalloc");
+  // one allocation: the descriptors, then the box of every block of a launch
+  // over all boxes (a block reads its box index instead of searching)
+  std::vector<char> host(p->descs.size() * sizeof(HaloDesc) + (size_t)p->blocks_all * sizeof(int32_t));
+  std::memcpy(host.data(), p->descs.data(), p->descs.size() * sizeof(HaloDesc));
+  int32_t* box_of = reinterpret_cast<int32_t*>(host.data() + p->descs.size() * sizeof(HaloDesc));
+  for (size_t i = 0; i < p->descs.size(); ++i) {
+    const int64_t end = i + 1 < p->descs.size() ? p->descs[i + 1].block_begin : p->blocks_all;
+    for (int64_t b = p->descs[i].block_begin; b < end; ++b) box_of[b] = (int32_t)i;
+  }
+  s = hip_check(hipMalloc(&p->d_descs, host.size()), "plan descriptor table: hipMalloc");
   if (s != ST_OK) { p->d_descs = nullptr; return s; }
-  s = hip_check(hipMemcpyAsync(p->d_descs, p->descs.data(), bytes, hipMemcpyHostToDevice, stream),
-                "plan descriptor table: hipMemcpyAsync");
+  s = hip_check(hipMemcpy(p->d_descs, host.data(), host.size(), hipMemcpyHostToDevice),
+                "plan descriptor table: hipMemcpy");
   if (s != ST_OK) { (void)hipFree(p->d_descs); p->d_descs = nullptr; return s; }
   p->dev_id = dev;
   return ST_OK;
