@@ -39,6 +39,11 @@ namespace {
 constexpr int kNT = 256;        // threads per block
 constexpr int kIter = 32;       // vectors per thread per item (a multiple of kPart)
 constexpr int kPart = 8;        // vectors per thread per apply work unit
+// threads (and vectors) per chunk of the chunked apply kernels: 64 where the
+// batch item's coefficient row (C x 16 bytes) is at most a chunk, else 256
+constexpr int kStreamSmall = 64, kStreamLarge = 256;
+constexpr int stream_tpb(int C) { return C <= kStreamSmall ? kStreamSmall : kStreamLarge; }
+static_assert(kNT * kIter % kStreamLarge == 0 && kStreamLarge % kStreamSmall == 0, "whole chunks per item");
 
 struct GnShard {
   const float* y;
@@ -174,22 +179,34 @@ __global__ __launch_bounds__(kNT) void gn_max(const GnArgs a) {
     const GnShard& sh = a.sh[s];
     const typename V::T* y = reinterpret_cast<const typename V::T*>(sh.y) + n * sh.vecs_per_n;
     const int64_t v0 = (int64_t)k * kNT * kIter + tid;
-    typename V::T val[kIter];
+    // as in gn_stats: every load issues before the first is used, non-temporal,
+    // and only an item that ends past the shard clamps and masks
+    auto body = [&](auto tail_tag) {
+      constexpr bool kTail = decltype(tail_tag)::value;
+      typename V::T val[kIter];
 #pragma unroll
-    for (int i = 0; i < kIter; ++i) {
-      const int64_t v = v0 + i * kNT;
-      val[i] = v < sh.vecs_per_n ? y[v] : typename V::T{};
-    }
-#pragma unroll
-    for (int i = 0; i < kIter; ++i) {
-      const int64_t v = v0 + i * kNT;
-#pragma unroll
-      for (int j = 0; j < VW; ++j) {
-        const float f = fabsf(V::get(val[i], j));
-        if (FIXED) mx[j] = fmaxf(mx[j], f);
-        else if (v < sh.vecs_per_n) atomicMax(&smax[(int)((v * VW + j) % C)], __float_as_uint(f));
+      for (int i = 0; i < kIter; ++i) {
+        const int64_t v = v0 + i * kNT;
+        if (kTail) {
+          const typename V::T t = load_nt<VW>(y, v < sh.vecs_per_n ? v : sh.vecs_per_n - 1);
+          val[i] = v < sh.vecs_per_n ? t : typename V::T{};
+        } else {
+          val[i] = load_nt<VW>(y, v);
+        }
       }
-    }
+#pragma unroll
+      for (int i = 0; i < kIter; ++i) {
+        const int64_t v = v0 + i * kNT;
+#pragma unroll
+        for (int j = 0; j < VW; ++j) {
+          const float f = fabsf(V::get(val[i], j));
+          if (FIXED) mx[j] = fmaxf(mx[j], f);
+          else if (!kTail || v < sh.vecs_per_n) atomicMax(&smax[(int)((v * VW + j) % C)], __float_as_uint(f));
+        }
+      }
+    };
+    if ((int64_t)(k + 1) * kNT * kIter <= sh.vecs_per_n) body(std::false_type{});
+    else body(std::true_type{});
   }
   if (cur >= 0) flush(cur_n);
 }
@@ -432,24 +449,25 @@ __global__ __launch_bounds__(kNT) void gn_apply(const GnArgs a) {
 // read-and-write pass moves ~6.5-6.8 TB/s this way against ~5.3 TB/s with
 // 32 persistent workgroups per CU and 8 vectors per lane).  The coefficients
 // of the chunk's batch item go through LDS, loaded after y's load is issued.
-template <int VW, bool FIXED>
-__global__ __launch_bounds__(kNT) void gn_apply_stream(const GnArgs a) {
+template <int VW, bool FIXED, int TPB>
+__global__ __launch_bounds__(TPB) void gn_apply_stream(const GnArgs a) {
   using V = Vec<VW>;
   extern __shared__ float4 srow[];                    // [C] (mean, scale, beta, 0) of batch item n
   const int tid = threadIdx.x;
   const int C = a.channels;
   const int chunk = blockIdx.x;
   int s, n, k;
-  decode_item(a, chunk / kIter, s, n, k);
+  constexpr int kChunks = kNT * kIter / TPB;          // chunks per item
+  decode_item(a, chunk / kChunks, s, n, k);
   const GnShard& sh = a.sh[s];
-  const int64_t first = ((int64_t)k * kIter + chunk % kIter) * kNT;
+  const int64_t first = ((int64_t)k * kChunks + chunk % kChunks) * TPB;
   if (first >= sh.vecs_per_n) return;                 // past the item's last vector: the whole workgroup
   const int64_t v = first + tid;
   const bool in = v < sh.vecs_per_n;
   const typename V::T* y = reinterpret_cast<const typename V::T*>(sh.y) + n * sh.vecs_per_n;
   typename V::T* z = reinterpret_cast<typename V::T*>(sh.z) + n * sh.vecs_per_n;
   const typename V::T val = load_nt<VW>(y, in ? v : first);
-  for (int i = tid; i < C; i += kNT) srow[i] = a.chan[(size_t)n * C + i];
+  for (int i = tid; i < C; i += TPB) srow[i] = a.chan[(size_t)n * C + i];
   __syncthreads();
   if (!in) return;
   float out[VW];
@@ -787,8 +805,8 @@ __global__ __launch_bounds__(kNT) void gnb_apply(const GnbArgs b) {
 // batch item's coefficients go through LDS.  A padded dy takes its position,
 // row and plane by multiply-shift division (every vector index of a batch
 // item is below 2^31 on this path).
-template <int VW, int MODE>
-__global__ __launch_bounds__(kNT) void gnb_apply_stream(const GnbArgs b) {
+template <int VW, int MODE, int TPB>
+__global__ __launch_bounds__(TPB) void gnb_apply_stream(const GnbArgs b) {
   using V = Vec<VW>;
   const GnArgs& a = b.g;
   extern __shared__ float4 srow[];                    // [C] (mean, a, k, b) of batch item n
@@ -796,9 +814,10 @@ __global__ __launch_bounds__(kNT) void gnb_apply_stream(const GnbArgs b) {
   const int C = a.channels;
   const int chunk = blockIdx.x;
   int s, n, k;
-  decode_item(a, chunk / kIter, s, n, k);
+  constexpr int kChunks = kNT * kIter / TPB;          // chunks per item
+  decode_item(a, chunk / kChunks, s, n, k);
   const GnShard& sh = a.sh[s];
-  const int64_t first = ((int64_t)k * kIter + chunk % kIter) * kNT;
+  const int64_t first = ((int64_t)k * kChunks + chunk % kChunks) * TPB;
   if (first >= sh.vecs_per_n) return;                 // past the item's last vector: the whole workgroup
   const int64_t v = first + tid;
   const bool in = v < sh.vecs_per_n;
@@ -806,7 +825,7 @@ __global__ __launch_bounds__(kNT) void gnb_apply_stream(const GnbArgs b) {
   const typename V::T* dz = reinterpret_cast<const typename V::T*>(sh.dz) + n * sh.vecs_per_n;
   const typename V::T vy = load_nt<VW>(y, in ? v : first);
   const typename V::T vd = load_nt<VW>(dz, in ? v : first);
-  for (int i = tid; i < C; i += kNT) srow[i] = b.bchan[(size_t)n * C + i];
+  for (int i = tid; i < C; i += TPB) srow[i] = b.bchan[(size_t)n * C + i];
   __syncthreads();
   if (!in) return;
   // the VW channels of a vector sit at one position (VW == 4 only when C % 4 == 0)
@@ -967,13 +986,16 @@ st_status launch_partials(GnArgs& a, bool need_max, hipStream_t st) {
 // launches one workgroup per chunk
 constexpr int kMaxStreamChannels = 4096;   // 64 KiB
 bool stream_fits(const GnArgs& a) {
-  return a.channels <= kMaxStreamChannels && (int64_t)a.total_items * kIter <= INT32_MAX;
+  return a.channels <= kMaxStreamChannels && (int64_t)a.total_items * (kNT * kIter / kStreamSmall) <= INT32_MAX;
 }
 
-template <int VW, bool FIXED>
+template <int VW, int TPB>
 st_status launch_apply_stream(GnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((gn_apply_stream<VW, FIXED>), dim3(a.total_items * kIter), dim3(kNT),
-                     (size_t)a.channels * sizeof(float4), st, a);
+  const dim3 grid(a.total_items * (kNT * kIter / TPB));
+  const size_t shmem = (size_t)a.channels * sizeof(float4);
+  // a lane's channels stay fixed when a chunk holds whole positions
+  if ((VW * TPB) % a.channels == 0) hipLaunchKernelGGL((gn_apply_stream<VW, true, TPB>), grid, dim3(TPB), shmem, st, a);
+  else hipLaunchKernelGGL((gn_apply_stream<VW, false, TPB>), grid, dim3(TPB), shmem, st, a);
   return launch_check("st_groupnorm_apply: launch");
 }
 
@@ -1035,11 +1057,20 @@ st_status launch_backward(GnbArgs& b, bool need_max, int mode, hipStream_t st) {
   if (mode != kDyLikeY)
     for (int i = 0; i < a.nshards; ++i) stream = stream && a.sh[i].vecs_per_n < ((int64_t)1 << 31);
   if (stream) {
-    const dim3 grid(a.total_items * kIter);
     const size_t shmem = (size_t)a.channels * sizeof(float4);
-    if (mode == kDyPaddedBf16) hipLaunchKernelGGL((gnb_apply_stream<VW, kDyPaddedBf16>), grid, dim3(kNT), shmem, st, b);
-    else if (mode == kDyPaddedF32) hipLaunchKernelGGL((gnb_apply_stream<VW, kDyPaddedF32>), grid, dim3(kNT), shmem, st, b);
-    else hipLaunchKernelGGL((gnb_apply_stream<VW, kDyLikeY>), grid, dim3(kNT), shmem, st, b);
+    if (stream_tpb(a.channels) == kStreamSmall) {
+      constexpr int T = kStreamSmall;
+      const dim3 grid(a.total_items * (kNT * kIter / T));
+      if (mode == kDyPaddedBf16) hipLaunchKernelGGL((gnb_apply_stream<VW, kDyPaddedBf16, T>), grid, dim3(T), shmem, st, b);
+      else if (mode == kDyPaddedF32) hipLaunchKernelGGL((gnb_apply_stream<VW, kDyPaddedF32, T>), grid, dim3(T), shmem, st, b);
+      else hipLaunchKernelGGL((gnb_apply_stream<VW, kDyLikeY, T>), grid, dim3(T), shmem, st, b);
+    } else {
+      constexpr int T = kStreamLarge;
+      const dim3 grid(a.total_items * (kNT * kIter / T));
+      if (mode == kDyPaddedBf16) hipLaunchKernelGGL((gnb_apply_stream<VW, kDyPaddedBf16, T>), grid, dim3(T), shmem, st, b);
+      else if (mode == kDyPaddedF32) hipLaunchKernelGGL((gnb_apply_stream<VW, kDyPaddedF32, T>), grid, dim3(T), shmem, st, b);
+      else hipLaunchKernelGGL((gnb_apply_stream<VW, kDyLikeY, T>), grid, dim3(T), shmem, st, b);
+    }
     return launch_check("st_groupnorm_backward: apply launch");
   }
   const int agrid = std::max(1, std::min((kIter / kPart) * a.total_items, device_cus() * 16));
@@ -1149,8 +1180,9 @@ st_status st_groupnorm_apply(const st_plan* y_plan, const float* const* y_bufs, 
   if (s != ST_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (stream_fits(a)) {
-    if (vw == 4) return fixed ? launch_apply_stream<4, true>(a, st) : launch_apply_stream<4, false>(a, st);
-    return fixed ? launch_apply_stream<1, true>(a, st) : launch_apply_stream<1, false>(a, st);
+    const bool small = stream_tpb(a.channels) == kStreamSmall;
+    if (vw == 4) return small ? launch_apply_stream<4, kStreamSmall>(a, st) : launch_apply_stream<4, kStreamLarge>(a, st);
+    return small ? launch_apply_stream<1, kStreamSmall>(a, st) : launch_apply_stream<1, kStreamLarge>(a, st);
   }
   if (vw == 4) return fixed ? launch_apply<4, true>(a, st) : launch_apply<4, false>(a, st);
   return fixed ? launch_apply<1, true>(a, st) : launch_apply<1, false>(a, st);
