@@ -34,10 +34,26 @@ struct PoolShard {
   int64_t begin;           // first work item of this shard
 };
 
+// n / d for 0 <= n < 2^31 as (n * m) >> p with p = 31 + ceil(log2 d) and
+// m = ceil(2^p / d) < 2^32 (the round-up multiplier method: the error term
+// stays below 1 / d, so the floor is exact)
+struct PoolDiv {
+  uint32_t m;
+  int32_t p;
+};
+PoolDiv pool_div(uint32_t d) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  return PoolDiv{(uint32_t)(((1ull << (31 + l)) + d - 1) / d), 31 + l};
+}
+__device__ __forceinline__ uint32_t pdiv(uint32_t n, PoolDiv f) { return (uint32_t)(((uint64_t)n * f.m) >> f.p); }
+
 struct PoolArgs {
   int32_t nshards, batch, channels, vec, k, stride, ndim, mode;
   float inv_count;
   int64_t total;
+  PoolDiv dcv;                     // dividers by C / vec and by the output extents (w, h, d)
+  PoolDiv dext[ST_MAX_SHARDS][3];
   PoolShard sh[ST_MAX_SHARDS];
 };
 static_assert(sizeof(PoolArgs) <= kMaxKernargBytes, "kernel argument struct too large");
@@ -54,6 +70,29 @@ template <> __device__ __forceinline__ void ldv<uint16_t, 1>(const uint16_t* p, 
 }
 template <> __device__ __forceinline__ void ldv<uint16_t, 8>(const uint16_t* p, float (&x)[8]) {
   const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+template <typename T, int VEC> __device__ __forceinline__ void ldv_nt(const T* p, float (&x)[VEC]);
+template <> __device__ __forceinline__ void ldv_nt<float, 1>(const float* p, float (&x)[1]) {
+  x[0] = __builtin_nontemporal_load(p);
+}
+template <> __device__ __forceinline__ void ldv_nt<float, 4>(const float* p, float (&x)[4]) {
+  typedef float nf4 __attribute__((ext_vector_type(4)));
+  const nf4 v = __builtin_nontemporal_load(reinterpret_cast<const nf4*>(p));
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+template <> __device__ __forceinline__ void ldv_nt<uint16_t, 1>(const uint16_t* p, float (&x)[1]) {
+  x[0] = __uint_as_float((uint32_t)__builtin_nontemporal_load(p) << 16);
+}
+template <> __device__ __forceinline__ void ldv_nt<uint16_t, 8>(const uint16_t* p, float (&x)[8]) {
+  typedef unsigned int nu4 __attribute__((ext_vector_type(4)));
+  const nu4 v = __builtin_nontemporal_load(reinterpret_cast<const nu4*>(p));
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -124,6 +163,56 @@ __global__ __launch_bounds__(256) void pool_kernel(const PoolArgs a) {
 }
 
 // output sizes of one internal axis for the given input sizes
+// The common windows (k = 2 or 3, 2D or 3D): all K^ND taps' loads in flight
+// at once, and the work item split into channel vector, column, row, plane
+// and batch item by multiply-shift division (every shard's item count is
+// below 2^31 on this path).  2D loads are non-temporal: 2x2 pooling of the
+// 2048^2 image and of the 256-channel grid 0.138 -> 0.108 and 0.238 -> 0.189
+// ms against the general kernel (plain loads: 0.116, 0.202); on the 3D
+// volumes non-temporal loads were 4% slower and plain ones 0-5% faster.
+template <typename TI, typename TO, int VEC, bool MAX, int K, int ND>
+__global__ __launch_bounds__(256) void pool_fixed(const PoolArgs a) {
+  const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (item >= a.total) return;
+  int s = 0;
+  while (s + 1 < a.nshards && a.sh[s + 1].begin <= item) ++s;
+  const PoolShard& sh = a.sh[s];
+  const uint32_t r0 = (uint32_t)(item - sh.begin);
+  const uint32_t r1 = pdiv(r0, a.dcv);
+  const int c = (int)(r0 - r1 * (uint32_t)(a.channels / VEC)) * VEC;
+  const uint32_t r2 = pdiv(r1, a.dext[s][0]);
+  const int ow = (int)(r1 - r2 * (uint32_t)sh.oext[2]);
+  const uint32_t r3 = pdiv(r2, a.dext[s][1]);
+  const int oh = (int)(r2 - r3 * (uint32_t)sh.oext[1]);
+  const uint32_t r4 = pdiv(r3, a.dext[s][2]);
+  const int od = (int)(r3 - r4 * (uint32_t)sh.oext[0]);
+  const int n = (int)r4;
+  const TI* base = reinterpret_cast<const TI*>(sh.in) + n * sh.isn + (int64_t)od * a.stride * sh.is[0] +
+                   (int64_t)oh * a.stride * sh.is[1] + (int64_t)ow * a.stride * sh.is[2] + c;
+  constexpr int KD = ND == 3 ? K : 1;
+  float x[KD * K * K][VEC];
+#pragma unroll
+  for (int tz = 0; tz < KD; ++tz)
+#pragma unroll
+    for (int ty = 0; ty < K; ++ty)
+#pragma unroll
+      for (int tx = 0; tx < K; ++tx)
+        if constexpr (ND == 2) ldv_nt<TI, VEC>(base + ty * sh.is[1] + tx * sh.is[2], x[ty * K + tx]);
+        else ldv<TI, VEC>(base + tz * sh.is[0] + ty * sh.is[1] + tx * sh.is[2], x[(tz * K + ty) * K + tx]);
+  float acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = MAX ? -INFINITY : 0.f;
+#pragma unroll
+  for (int t = 0; t < KD * K * K; ++t)     // taps in the general kernel's order
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = MAX ? fmaxf(acc[v], x[t][v]) : acc[v] + x[t][v];
+  if (!MAX) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] *= a.inv_count;
+  }
+  stv<TO, VEC>(reinterpret_cast<TO*>(sh.out) + n * sh.osn + od * sh.os[0] + oh * sh.os[1] + ow * sh.os[2] + c, acc);
+}
+
 bool pooled_sizes(const std::vector<int64_t>& in, int64_t k, int64_t s, std::vector<int64_t>& out,
                   std::vector<int64_t>& first) {
   int64_t n = 0;
@@ -219,6 +308,7 @@ st_status st_pool_sharded(const st_plan* in_plan, const void* const* in_bufs, in
     if (sz != out_plan->sizes[ax]) return err(ST_ERR_BAD_SHAPE, "output plan is not the pooled plan of the input");
   }
   int64_t total = 0;
+  bool small = true;
   for (size_t i = 0; i < in_plan->shards.size(); ++i) {
     if (!in_bufs[i] || !out_bufs[i]) return err(ST_ERR_INVALID_ARG, "NULL shard buffer");
     if (!aligned16(in_bufs[i]) || !aligned16(out_bufs[i])) return err(ST_ERR_ALIGNMENT, "shard buffers must be 16-byte aligned");
@@ -250,17 +340,32 @@ st_status st_pool_sharded(const st_plan* in_plan, const void* const* in_bufs, in
     p.in = static_cast<const char*>(in_bufs[i]) + in_off * ie;
     p.out = static_cast<char*>(out_bufs[i]) + out_off * oe;
     p.begin = total;
-    total += a.batch * (int64_t)so.ext[0] * so.ext[1] * so.ext[2] * (a.channels / a.vec);
+    const int64_t items = a.batch * (int64_t)so.ext[0] * so.ext[1] * so.ext[2] * (a.channels / a.vec);
+    total += items;
+    small = small && items < ((int64_t)1 << 31);
+    for (int e = 0; e < 3; ++e) a.dext[i][e] = pool_div((uint32_t)std::max<int64_t>(1, so.ext[2 - e]));
   }
   a.total = total;
   if (total == 0) return ST_OK;
+  a.dcv = pool_div((uint32_t)(a.channels / a.vec));
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
   const bool mx = mode == 1;
   const bool bi = in_plan->dtype == ST_BF16, bo = out_plan->dtype == ST_BF16;
+  // k = 2 or 3 with every shard's items below 2^31: pool_fixed
+  const int fixed = small && (ksize == 2 || ksize == 3) ? ksize * 10 + in_plan->ndim : 0;
+#define ST_POOL_FIXED(TI, TO, V, MX)                                                                       \
+  do {                                                                                                     \
+    if (fixed == 22) hipLaunchKernelGGL((pool_fixed<TI, TO, V, MX, 2, 2>), grid, block, 0, st, a);         \
+    else if (fixed == 23) hipLaunchKernelGGL((pool_fixed<TI, TO, V, MX, 2, 3>), grid, block, 0, st, a);    \
+    else if (fixed == 32) hipLaunchKernelGGL((pool_fixed<TI, TO, V, MX, 3, 2>), grid, block, 0, st, a);    \
+    else hipLaunchKernelGGL((pool_fixed<TI, TO, V, MX, 3, 3>), grid, block, 0, st, a);                     \
+  } while (0)
 #define ST_POOL_LAUNCH(TI, TO, V)                                                                     \
   do {                                                                                                \
-    if (mx) hipLaunchKernelGGL((pool_kernel<TI, TO, V, true>), grid, block, 0, st, a);                \
+    if (fixed && mx) ST_POOL_FIXED(TI, TO, V, true);                                                  \
+    else if (fixed) ST_POOL_FIXED(TI, TO, V, false);                                                  \
+    else if (mx) hipLaunchKernelGGL((pool_kernel<TI, TO, V, true>), grid, block, 0, st, a);           \
     else hipLaunchKernelGGL((pool_kernel<TI, TO, V, false>), grid, block, 0, st, a);                  \
   } while (0)
   if (bi && bo) {
@@ -271,6 +376,7 @@ st_status st_pool_sharded(const st_plan* in_plan, const void* const* in_bufs, in
     if (a.vec == 4) ST_POOL_LAUNCH(float, float, 4); else ST_POOL_LAUNCH(float, float, 1);
   }
 #undef ST_POOL_LAUNCH
+#undef ST_POOL_FIXED
   return launch_check("st_pool_sharded: launch");
 }
 
