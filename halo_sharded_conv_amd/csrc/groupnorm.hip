@@ -787,13 +787,18 @@ __global__ __launch_bounds__(kNT) void gnb_apply(const GnbArgs b) {
         const int hh = (int)(t - d * o.H);
         const int64_t off = n * o.sn + d * o.sd + hh * o.sh + (int64_t)w * C + c;
         if constexpr (MODE == kDyPaddedF32) {
-          if constexpr (VW == 4) *reinterpret_cast<float4*>(static_cast<float*>(o.p) + off) =
-              make_float4(out[0], out[1], out[2], out[3]);
-          else static_cast<float*>(o.p)[off] = out[0];
+          if constexpr (VW == 4) {
+            typedef float nf4 __attribute__((ext_vector_type(4)));
+            __builtin_nontemporal_store(nf4{out[0], out[1], out[2], out[3]}, reinterpret_cast<nf4*>(static_cast<float*>(o.p) + off));
+          }
+          else __builtin_nontemporal_store(out[0], static_cast<float*>(o.p) + off);
         } else {
-          if constexpr (VW == 4) *reinterpret_cast<uint2*>(static_cast<uint16_t*>(o.p) + off) =
-              make_uint2(bf16_rne(out[0]) | (bf16_rne(out[1]) << 16), bf16_rne(out[2]) | (bf16_rne(out[3]) << 16));
-          else static_cast<uint16_t*>(o.p)[off] = (uint16_t)bf16_rne(out[0]);
+          if constexpr (VW == 4) {
+            typedef unsigned int nu2 __attribute__((ext_vector_type(2)));
+            __builtin_nontemporal_store(nu2{bf16_rne(out[0]) | (bf16_rne(out[1]) << 16), bf16_rne(out[2]) | (bf16_rne(out[3]) << 16)},
+                                        reinterpret_cast<nu2*>(static_cast<uint16_t*>(o.p) + off));
+          }
+          else __builtin_nontemporal_store((uint16_t)bf16_rne(out[0]), static_cast<uint16_t*>(o.p) + off);
         }
       }
     }
@@ -857,14 +862,20 @@ __global__ __launch_bounds__(TPB) void gnb_apply_stream(const GnbArgs b) {
     const int w = (int)(pu - tu * (uint32_t)o.W);
     const int hh = (int)(tu - du * (uint32_t)o.H);
     const int64_t off = n * o.sn + (int64_t)du * o.sd + hh * o.sh + (int64_t)w * C + c0;
+    // non-temporal stores, as for z: dy is read back only by the next pass
     if constexpr (MODE == kDyPaddedF32) {
-      if constexpr (VW == 4) *reinterpret_cast<float4*>(static_cast<float*>(o.p) + off) =
-          make_float4(out[0], out[1], out[2], out[3]);
-      else static_cast<float*>(o.p)[off] = out[0];
+      if constexpr (VW == 4) {
+        typedef float nf4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(nf4{out[0], out[1], out[2], out[3]}, reinterpret_cast<nf4*>(static_cast<float*>(o.p) + off));
+      }
+      else __builtin_nontemporal_store(out[0], static_cast<float*>(o.p) + off);
     } else {
-      if constexpr (VW == 4) *reinterpret_cast<uint2*>(static_cast<uint16_t*>(o.p) + off) =
-          make_uint2(bf16_rne(out[0]) | (bf16_rne(out[1]) << 16), bf16_rne(out[2]) | (bf16_rne(out[3]) << 16));
-      else static_cast<uint16_t*>(o.p)[off] = (uint16_t)bf16_rne(out[0]);
+      if constexpr (VW == 4) {
+        typedef unsigned int nu2 __attribute__((ext_vector_type(2)));
+        __builtin_nontemporal_store(nu2{bf16_rne(out[0]) | (bf16_rne(out[1]) << 16), bf16_rne(out[2]) | (bf16_rne(out[3]) << 16)},
+                                    reinterpret_cast<nu2*>(static_cast<uint16_t*>(o.p) + off));
+      }
+      else __builtin_nontemporal_store((uint16_t)bf16_rne(out[0]), static_cast<uint16_t*>(o.p) + off);
     }
   }
 }
