@@ -42,6 +42,10 @@ struct HaloDesc {
   int32_t rows_dh;        // rows per batch item = rows_d * rows_h
   int32_t upr;            // words per row
   int32_t pad0;
+  // multiply-shift dividers by upr, rows_dh and rows_h: q = (n * m) >> p for
+  // n < 2^31, with p = 31 + ceil(log2 d) and m = ceil(2^p / d)
+  uint32_t m_upr, m_rdh, m_rh;
+  int32_t p_upr, p_rdh, p_rh;
   int64_t units;          // words in the box: N * rows_dh * upr
   int64_t src_base, src_sn, src_sd, src_sh;   // word offsets/strides in the sender
   int64_t dst_base, dst_sn, dst_sd, dst_sh;   // word offsets/strides in the receiver

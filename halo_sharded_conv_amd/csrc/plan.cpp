@@ -265,7 +265,7 @@ st_status st_plan_shards(int32_t ndim, int64_t batch, int64_t channels, const in
     h.rows_dh = (int32_t)rows_dh;
     h.upr = (int32_t)upr;
     h.units = batch * rows_dh * upr;
-    if (upr > INT32_MAX || rows_dh > INT32_MAX || h.units > (int64_t)UINT32_MAX) {
+    if (upr > INT32_MAX || rows_dh > INT32_MAX || h.units > (int64_t)INT32_MAX) {
       delete p;
       return fail(ST_ERR_UNSUPPORTED, "st_plan_shards: halo box too large");
     }
@@ -288,6 +288,15 @@ st_status st_plan_shards(int32_t ndim, int64_t batch, int64_t channels, const in
       h.src_base = h.src_sn = h.src_sd = h.src_sh = 0;
       h.msg_base = -1;
     }
+    auto magic = [](int64_t d, uint32_t& m, int32_t& sh) {
+      int l = 0;
+      while ((1ll << l) < d) ++l;
+      sh = 31 + l;
+      m = (uint32_t)(((1ull << sh) + (uint64_t)d - 1) / (uint64_t)d);
+    };
+    magic(h.upr, h.m_upr, h.p_upr);
+    magic(h.rows_dh, h.m_rdh, h.p_rdh);
+    magic(h.rows_h, h.m_rh, h.p_rh);
     h.block_begin = blocks;
     blocks += (h.units + kHaloWordsPerBlock - 1) / kHaloWordsPerBlock;
     if ((int64_t)i + 1 == p->n_real) p->blocks_real = blocks;
