@@ -106,6 +106,30 @@ __device__ __forceinline__ uint32_t bf16_bits(float v) {    // nearest even (fin
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// non-temporal stores of the pooled output (read back only by a later pass)
+template <typename T, int VEC> __device__ __forceinline__ void stv_nt(T* p, const float (&x)[VEC]);
+template <> __device__ __forceinline__ void stv_nt<float, 1>(float* p, const float (&x)[1]) {
+  __builtin_nontemporal_store(x[0], p);
+}
+template <> __device__ __forceinline__ void stv_nt<float, 4>(float* p, const float (&x)[4]) {
+  typedef float nf4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(nf4{x[0], x[1], x[2], x[3]}, reinterpret_cast<nf4*>(p));
+}
+template <> __device__ __forceinline__ void stv_nt<float, 8>(float* p, const float (&x)[8]) {
+  typedef float nf4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(nf4{x[0], x[1], x[2], x[3]}, reinterpret_cast<nf4*>(p));
+  __builtin_nontemporal_store(nf4{x[4], x[5], x[6], x[7]}, reinterpret_cast<nf4*>(p) + 1);
+}
+template <> __device__ __forceinline__ void stv_nt<uint16_t, 1>(uint16_t* p, const float (&x)[1]) {
+  __builtin_nontemporal_store((uint16_t)bf16_bits(x[0]), p);
+}
+template <> __device__ __forceinline__ void stv_nt<uint16_t, 8>(uint16_t* p, const float (&x)[8]) {
+  typedef unsigned int nu4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(nu4{bf16_bits(x[0]) | (bf16_bits(x[1]) << 16), bf16_bits(x[2]) | (bf16_bits(x[3]) << 16),
+                                  bf16_bits(x[4]) | (bf16_bits(x[5]) << 16), bf16_bits(x[6]) | (bf16_bits(x[7]) << 16)},
+                              reinterpret_cast<nu4*>(p));
+}
+
 template <typename T, int VEC> __device__ __forceinline__ void stv(T* p, const float (&x)[VEC]);
 template <> __device__ __forceinline__ void stv<float, 1>(float* p, const float (&x)[1]) { *p = x[0]; }
 template <> __device__ __forceinline__ void stv<float, 4>(float* p, const float (&x)[4]) {
@@ -210,7 +234,7 @@ __global__ __launch_bounds__(256) void pool_fixed(const PoolArgs a) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] *= a.inv_count;
   }
-  stv<TO, VEC>(reinterpret_cast<TO*>(sh.out) + n * sh.osn + od * sh.os[0] + oh * sh.os[1] + ow * sh.os[2] + c, acc);
+  stv_nt<TO, VEC>(reinterpret_cast<TO*>(sh.out) + n * sh.osn + od * sh.os[0] + oh * sh.os[1] + ow * sh.os[2] + c, acc);
 }
 
 bool pooled_sizes(const std::vector<int64_t>& in, int64_t k, int64_t s, std::vector<int64_t>& out,

@@ -447,9 +447,12 @@ __global__ __launch_bounds__(256, CAP <= 80 * 1024 ? 2 : 1) void conv_sx_mfma(co
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int j = 0; j < NACC / 4; ++j)
-            if (ob + mb * FR + 8 * j + 4 * grp < a.cout)
-              *reinterpret_cast<float4*>(op[nb] + ob + mb * FR + 8 * j + 4 * grp) =
-                  make_float4(acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1], acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]);
+            if (ob + mb * FR + 8 * j + 4 * grp < a.cout) {
+              typedef float nf4 __attribute__((ext_vector_type(4)));
+              __builtin_nontemporal_store(
+                  nf4{acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1], acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]},
+                  reinterpret_cast<nf4*>(op[nb] + ob + mb * FR + 8 * j + 4 * grp));
+            }
       }
     }
   }
