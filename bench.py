@@ -75,7 +75,7 @@ STAGE_KERNELS = {                    # kernel-name fragments of each library sta
     "halo_pack": ("halo_copy",), "halo_unpack": ("halo_copy",), "halo_exchange": ("halo_copy",),
     "conv": ("conv_rows", "conv_pairs", "conv_gemm", "conv_direct"),
     "gn_partials": ("gn_max", "gn_stats"), "gn_apply": ("gn_apply",),
-    "wgrad": ("wgrad_tr", "wgrad_grp", "wgrad_direct"), "gn_backward": ("gn_max", "gnb_"), "pool": ("pool_kernel",),
+    "wgrad": ("wgrad_tr", "wgrad_grp", "wgrad_direct"), "gn_backward": ("gn_max", "gnb_"), "pool": ("pool_kernel", "pool_fixed"),
     "strided": ("conv_sx_mfma", "conv_strided"), "transposed": ("conv_sx_mfma", "conv_transposed"),
 }
 
