@@ -273,32 +273,39 @@ __device__ __forceinline__ uint16_t sx_rne(float f) {
 // lane % 32); FR = 16: v_mfma_f32_16x16x32_bf16 (8 of 32 K for position
 // lane % 16), whose B loads cover 16 cells x 64 bytes instead of 32 cells x
 // 32 bytes per instruction.  A wave owns 64 positions and MB x FR channels.
-template <int FR, int MB, int KG, bool TR, int CAP>
+// HALF (FR 32, MB 1, Cout 16): the tile's rows 16-31 are zeros, so LDS holds
+// only the 32 lane slots of rows 0-15 per fragment (half the bytes, which
+// lets a 3D k5 16-channel layer's weights fit two workgroups per CU) and
+// lanes of rows 16-31 take zero operands instead of reading them.
+template <int FR, int MB, int KG, bool TR, int CAP, bool HALF = false>
 __global__ __launch_bounds__(256, CAP <= 80 * 1024 ? 2 : 1) void conv_sx_mfma(const SxArgs a) {
   using acc_t = typename std::conditional<FR == 32, sx_f32x16, sx_f32x4>::type;
   constexpr int KS = FR == 32 ? 16 : 32;          // channels per K step
   constexpr int NBK = 64 / FR;                    // position blocks per wave
   constexpr int NACC = FR == 32 ? 16 : 4;         // accumulators per block and lane
-  __shared__ __attribute__((aligned(16))) uint16_t wl[CAP / 2];   // [taps][Cin/KS][MB][64 lanes][8]
+  static_assert(!HALF || (FR == 32 && MB == 1), "half tiles are single 32-row blocks");
+  constexpr int SLOTS = HALF ? 32 : 64;           // stored lane slots per fragment
+  constexpr int ROWS = HALF ? 16 : FR;            // stored rows per block
+  __shared__ __attribute__((aligned(16))) uint16_t wl[CAP / 2];   // [taps][Cin/KS][MB][SLOTS lanes][8]
   const int KC = a.cin / KS;
   const int ob = blockIdx.y * MB * FR;
   {
     // weights of this channel block, read in global order 4 output channels
     // (16 bytes) at a time, rounded to bf16, written to their fragment slots
     // (4 consecutive output channels are 4 consecutive lanes' slots)
-    const int per_tap4 = a.cin * MB * FR / 4;
+    const int per_tap4 = a.cin * MB * ROWS / 4;
     const int total4 = a.taps * per_tap4;
 #pragma unroll 4
     for (int f = threadIdx.x; f < total4; f += blockDim.x) {
       const int t = f / per_tap4;
       const int rem = f - t * per_tap4;
-      const int c = rem / (MB * FR / 4);
-      const int o = (rem - c * (MB * FR / 4)) * 4;
+      const int c = rem / (MB * ROWS / 4);
+      const int o = (rem - c * (MB * ROWS / 4)) * 4;
       // rows past Cout (a 16-channel layer in a 32-row tile) hold zeros
       const float4 v = ob + o < a.cout ? *reinterpret_cast<const float4*>(a.w + ((int64_t)t * a.cin + c) * a.cout + ob + o)
                                        : make_float4(0.f, 0.f, 0.f, 0.f);
-      const int l = ((c % KS) >> 3) * FR + (o % FR);
-      uint16_t* d = wl + ((((t * KC + c / KS) * MB + o / FR) * 64 + l) << 3) + (c & 7);
+      const int l = ((c % KS) >> 3) * ROWS + (o % FR);
+      uint16_t* d = wl + ((((t * KC + c / KS) * MB + o / FR) * SLOTS + l) << 3) + (c & 7);
       d[0] = sx_rne(v.x);
       d[8] = sx_rne(v.y);
       d[16] = sx_rne(v.z);
@@ -389,7 +396,7 @@ __global__ __launch_bounds__(256, CAP <= 80 * 1024 ? 2 : 1) void conv_sx_mfma(co
         // transposed: cell q + (r + p - t)/s, one back per step of s
         off = (TR ? -(mz * sh.is[0] + my * sh.is[1] + mx * sh.is[2]) : tz * sh.is[0] + ty * sh.is[1] + tx * sh.is[2]) +
               c0 * KS;
-        wbase = (((tz * k + ty) * k + tx) * KC + c0) * MB * 512;
+        wbase = (((tz * k + ty) * k + tx) * KC + c0) * MB * SLOTS * 8;
       };
       auto load_b = [&](int64_t off, sx_bf16x8 (&bv)[KG][NBK]) __attribute__((always_inline)) {
 #pragma unroll
@@ -398,13 +405,17 @@ __global__ __launch_bounds__(256, CAP <= 80 * 1024 ? 2 : 1) void conv_sx_mfma(co
           for (int nb = 0; nb < NBK; ++nb)
             bv[kc][nb] = *reinterpret_cast<const sx_bf16x8*>(bp[nb] + off + kc * KS);
       };
+      // HALF: lane (row lp, K group grp) reads slot grp * 16 + lp for rows < 16
+      const int slot = HALF ? grp * 16 + (lp & 15) : lane;
+      const bool zero_row = HALF && lp >= 16;
       auto mma = [&](int wbase, const sx_bf16x8 (&bv)[KG][NBK]) __attribute__((always_inline)) {
-        const uint16_t* wt = wl + wbase + lane * 8;
+        const uint16_t* wt = wl + wbase + slot * 8;
 #pragma unroll
         for (int kc = 0; kc < KG; ++kc)
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            const sx_bf16x8 av = *reinterpret_cast<const sx_bf16x8*>(wt + (kc * MB + mb) * 512);
+            sx_bf16x8 av = *reinterpret_cast<const sx_bf16x8*>(wt + (kc * MB + mb) * SLOTS * 8);
+            if (HALF && zero_row) av = sx_bf16x8{};
 #pragma unroll
             for (int nb = 0; nb < NBK; ++nb) {
               if constexpr (FR == 32)
@@ -474,7 +485,9 @@ bool launch_sx_mfma(const SxShard* shards, int nshards, int batch, int cin, int 
   // 16x16x32 fragments when Cin % 32 == 0 (wider B loads), else 32x32x16
   const int fr = kSxPrefer16 && cin % 32 == 0 ? 16 : 32;
   int mb = fr == 16 ? (cout % 64 == 0 ? 4 : cout % 32 == 0 ? 2 : 1) : (cout % 64 == 0 ? 2 : 1);
-  int64_t need = (int64_t)taps * cin * mb * fr * 2;
+  // a 16-channel layer stores only its 16 real rows of the 32-row tile
+  const bool half = fr == 32 && cout == 16;
+  int64_t need = (int64_t)taps * cin * mb * (half ? 16 : fr) * 2;
   while (need > kSxCapLarge && mb > 1) {
     mb /= 2;
     need /= 2;
@@ -536,6 +549,17 @@ bool launch_sx_mfma(const SxShard* shards, int nshards, int batch, int cin, int 
     }
   } else if (mb == 2) {
     ST_SX_KG(32, 2);
+  } else if (half) {
+    // Cin % 16 == 0 and cout 16: kg is 1, 2 or 4
+#define ST_SX_H(KG_)                                                                                               \
+  do {                                                                                                             \
+    if (small) hipLaunchKernelGGL((conv_sx_mfma<32, 1, KG_, TR, kSxCapSmall, true>), g3, block, 0, st, a);       \
+    else hipLaunchKernelGGL((conv_sx_mfma<32, 1, KG_, TR, kSxCapLarge, true>), g3, block, 0, st, a);             \
+  } while (0)
+    if (kg == 4) ST_SX_H(4);
+    else if (kg == 2) ST_SX_H(2);
+    else ST_SX_H(1);
+#undef ST_SX_H
   } else {
     ST_SX_KG(32, 1);
   }
