@@ -24,8 +24,10 @@
 //   gn_max     max |y| per (n, group)   (only when the conv did not fuse it)
 //   gn_stats   per-shard sum q1, sum q2 per (n, group)
 //   gn_combine sum over shards; mean, var, rstd in fp64 -> fp32
-//   gn_apply   z = (y - mean_g) * (rstd_g * gamma_c) + beta_c, optionally
-//              with the combine in its prologue (one launch fewer)
+//   gn_apply_stream  z = (y - mean_g) * (rstd_g * gamma_c) + beta_c, one
+//              workgroup per chunk of the output in chunk order
+//   gn_apply   the same as persistent workgroups, optionally with the
+//              combine in its prologue (one launch fewer: small outputs)
 #include <algorithm>
 #include <mutex>
 #include <type_traits>
@@ -504,7 +506,8 @@ __global__ __launch_bounds__(TPB) void gn_apply_stream(const GnArgs a) {
 //
 // Kernels: gn_fill (partials), gn_max on dz (unless the caller supplies
 // max |dz|), gnb_stats (per-shard S1, S2 per (n, c)), gnb_combine (sums over
-// shards; per-channel coefficients; dgamma, dbeta), gnb_apply
+// shards; per-channel coefficients; dgamma, dbeta), gnb_apply_stream (or the
+// persistent gnb_apply for batch items of 2^31 vectors or more)
 //     dy = a_c * dz + k_g * (y - mean_g) + b_g
 // with a_c = r gamma_c, k_g = -r^2 mean_g(g yhat), b_g = -r mean_g(g).
 
