@@ -133,3 +133,14 @@ def test_random_plans(data):
     C = data.draw(st_.sampled_from([1, 2, 3, 4, 8]))
     dtype = data.draw(st_.sampled_from(["f32", "bf16"]))
     check_plan(shards, h, C, dtype, N=data.draw(st_.integers(1, 2)), seed=data.draw(st_.integers(0, 99)))
+
+
+def test_halo_box_above_2_31_words_is_refused():
+    # the copy kernels split a box's word index with 32-bit multiply-shift
+    # division, valid below 2^31: an H-face box of 2^30 cells x 32 bytes
+    # (2^31 16-byte words) is refused at plan time, one word less is planned
+    import halo_sharded_conv_amd as hsc
+    with pytest.raises(hsc.ShardConvError, match="halo box too large"):
+        hsc.st_plan_shards(2, 1, 8, (4, 2 ** 30), ((2, 2), (2 ** 30,)), (1, 0), "f32")
+    p = hsc.st_plan_shards(2, 1, 8, (4, 2 ** 30 - 1), ((2, 2), (2 ** 30 - 1,)), (1, 0), "f32")
+    assert p.num_shards == 2
