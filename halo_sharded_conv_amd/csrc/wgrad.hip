@@ -26,7 +26,8 @@
 // transposing LDS reads; wgrad_tr works row by row, wgrad_grp over groups of
 // rows and channel tiles (below).
 //
-// A workgroup owns a tile of 32x32 output blocks and a fixed contiguous band
+// A workgroup owns a tile of output blocks (32 x 32, or 16 x 16 for the
+// row-group kernel's 16 x 16 x 32 form) and a fixed contiguous band
 // of the rows (partition p of GP), accumulating over all of them in
 // registers, then stores its partial dw.  The reduction sums the GP partials
 // in partition order in fp64: the result does not depend on the device, the
@@ -36,6 +37,7 @@
 // Other shapes and the fp32 path use a direct kernel: one thread per
 // (dw element, partition), fp32 FMA in row order.
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -43,6 +45,7 @@ namespace st {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWgMaxShards = ST_MAX_SHARDS;
@@ -423,12 +426,21 @@ __global__ __launch_bounds__(C::NT) void wgrad_tr(const WgArgs a) {
 // only its channels.  A partition's sums run group by group, chunk by chunk,
 // row by row and K step by K step: a fixed order for a given shard plan.
 
+// F16: v_mfma_f32_16x16x32_bf16 blocks of 16 rows and K steps of 32
+// positions instead of 32 x 32 x 16 (a 16-channel k5 layer's 80 x 400 tile
+// then needs no padding rows: 5 x 25 blocks, against 3 x 13 of 32 rows with
+// 35% of their products on padding); chunks then take no extra tail columns.
+// NSTG: LDS stages (3: the transfers of step c + 2 fly while step c computes).
 template <int NDIM_, int K_, int CIN_, int COUT_, int OT_, int CT_, int G_, int COLS_, int WGM_, int WGN_, int WM_,
-          int WN_, int LW_ = 0>
+          int WN_, int LW_ = 0, bool F16_ = false, int NSTG_ = 2>
 struct WrCfg {
   static constexpr int NDIM = NDIM_, K = K_, CIN = CIN_, COUT = COUT_;
   static constexpr int OT = OT_, CT = CT_, G = G_;
   static constexpr int WGM = WGM_, WGN = WGN_, WM = WM_, WN = WN_;
+  static constexpr bool F16 = F16_;
+  static constexpr int NSTG = NSTG_;
+  static constexpr int BM = F16 ? 16 : 32;               // rows per MFMA block
+  static constexpr int KSTEP = F16 ? 32 : 16;            // positions per K step
   static constexpr int P = K / 2;
   static constexpr int TAPS = NDIM == 3 ? K * K * K : K * K;
   static constexpr int R = NDIM == 3 ? K * K : K;        // tap rows (tz, ty)
@@ -437,8 +449,9 @@ struct WrCfg {
   static constexpr int TM = WGM * WM, TN = WGN * WN;     // blocks per tile
   static constexpr int TILES_O = COUT / OT, TILES_C = CIN / CT, NTILE = TILES_O * TILES_C;
   static constexpr int NWC = WGM * WGN, NW = NWC + LW_, NT = 64 * NW;
-  static constexpr int COLS = COLS_, CMAX = COLS + 16;   // a row's last chunk takes up to 16 more columns
-  static constexpr int NKS = CMAX / 16;                  // K steps of the widest chunk
+  // 32 x 32 x 16: a row's last chunk takes up to 16 more columns
+  static constexpr int COLS = COLS_, CMAX = COLS + (F16 ? 0 : 16);
+  static constexpr int NKS = CMAX / KSTEP;               // K steps of the widest chunk
   static constexpr int DQ = CMAX + K - 1;                // dy positions of a chunk
   static constexpr int DPT = OT * 2, XPT = CT * 2;       // bytes per position in LDS
   static constexpr int HR = G + K - 1;                   // x rows per tz of a group
@@ -448,8 +461,11 @@ struct WrCfg {
   static constexpr int NJ = (D_BYTES + KZ * HR * X_RUN + 1023) / 1024;
   static constexpr int JPW = (NJ + NW - 1) / NW;         // transfers per wave, every wave the same
   static constexpr int STAGE = JPW * NW * 1024;
-  static constexpr int LDS = 2 * STAGE;
-  static_assert(TM * 32 >= MRT && TN * 32 >= NRT, "one tile of blocks spans the tile's rows");
+  static constexpr int LDS = NSTG * STAGE;
+  static_assert(NSTG == 2 || NSTG == 3, "two or three stages");
+  static_assert(CMAX % KSTEP == 0, "whole K steps per chunk");
+  static_assert(OT % 16 == 0 && CT % 16 == 0, "a 16-row block never straddles a tap shift or tap row");
+  static_assert(TM * BM >= MRT && TN * BM >= NRT, "one tile of blocks spans the tile's rows");
   static_assert(COUT % OT == 0 && CIN % CT == 0 && OT % 16 == 0 && CT % 16 == 0,
                 "channel tiles in whole 16-channel groups (one lane group reads one tap shift / tap row)");
   static_assert(DPT % 16 == 0 && XPT % 16 == 0 && D_RUN % 16 == 0, "16-byte slots");
@@ -460,6 +476,8 @@ template <class C>
 __global__ __launch_bounds__(C::NT) void wgrad_grp(const WgArgs a) {
   __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage2[C::NSTG == 3 ? C::STAGE : 16];
+  using acc_t = typename std::conditional<C::F16, f32x4, f32x16>::type;
   typedef short v4s __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) v4s* lds_v4s;
   typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -473,30 +491,32 @@ __global__ __launch_bounds__(C::NT) void wgrad_grp(const WgArgs a) {
   const int wm = (wave % C::NWC) / C::WGN, wn = (wave % C::NWC) % C::WGN;
   const bool mma = wave < C::NWC;
 
-  f32x16 acc[C::WM][C::WN];
+  acc_t acc[C::WM][C::WN];
 #pragma unroll
   for (int i = 0; i < C::WM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::WN; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < C::WN; ++j) acc[i][j] = acc_t{};
 
   // fragment offsets for output row 0 of a group and K step 0 (a row adds
-  // D_RUN / X_RUN, a K step 16 positions): lane s of 16-lane group q reads
+  // D_RUN / X_RUN, a K step KSTEP positions): lane s of 16-lane group q reads
   // position 8 (q >> 1) + s / 4 (+ 4 for its second read) at the 4 channels
-  // 16 (q & 1) + 4 (s & 3) of its 32-row block
+  // 16 (q & 1) + 4 (s & 3) of its 32-row block; with 16-row blocks (F16)
+  // position 8 q + s / 4 at the channels 4 (s & 3), the 16 lanes of a group
+  // holding one K group of 8 positions of the block's 16 rows
   const int g16 = lane >> 4, s16 = lane & 15;
-  const int kq = 8 * (g16 >> 1) + (s16 >> 2);
-  const int rq = 16 * (g16 & 1) + 4 * (s16 & 3);
+  const int kq = C::F16 ? 8 * g16 + (s16 >> 2) : 8 * (g16 >> 1) + (s16 >> 2);
+  const int rq = C::F16 ? 4 * (s16 & 3) : 16 * (g16 & 1) + 4 * (s16 & 3);
   int aoff[C::WM], boff[C::WN];
 #pragma unroll
   for (int i = 0; i < C::WM; ++i) {
-    int mrow = (wm * C::WM + i) * 32 + rq;
+    int mrow = (wm * C::WM + i) * C::BM + rq;
     mrow = mrow < C::MRT ? mrow : 0;                  // padding rows read anything: their sums are not stored
     const int tx = mrow / C::OT, oi = mrow % C::OT;
     aoff[i] = (kq + (C::K - 1) - tx) * C::DPT + oi * 2;
   }
 #pragma unroll
   for (int j = 0; j < C::WN; ++j) {
-    int nrow = (wn * C::WN + j) * 32 + rq;
+    int nrow = (wn * C::WN + j) * C::BM + rq;
     nrow = nrow < C::NRT ? nrow : 0;
     const int r = nrow / C::CT, ci = nrow % C::CT;
     const int tz = C::NDIM == 3 ? r / C::K : 0, ty = C::NDIM == 3 ? r % C::K : r;
@@ -506,14 +526,14 @@ __global__ __launch_bounds__(C::NT) void wgrad_grp(const WgArgs a) {
       __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::WM; ++i) {
-      const char* p = st + aoff[i] + g * C::D_RUN + ks * 16 * C::DPT;
+      const char* p = st + aoff[i] + g * C::D_RUN + ks * C::KSTEP * C::DPT;
       const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)p);
       const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * C::DPT));
       av[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 #pragma unroll
     for (int j = 0; j < C::WN; ++j) {
-      const char* p = st + boff[j] + g * C::X_RUN + ks * 16 * C::XPT;
+      const char* p = st + boff[j] + g * C::X_RUN + ks * C::KSTEP * C::XPT;
       const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)p);
       const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * C::XPT));
       bv[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -523,8 +543,12 @@ __global__ __launch_bounds__(C::NT) void wgrad_grp(const WgArgs a) {
 #pragma unroll
     for (int i = 0; i < C::WM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::WN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < C::WN; ++j) {
+        if constexpr (C::F16)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      }
   };
 
   // A step: rows h0 .. h0 + ng - 1 (ng <= G) of one (shard, n, d) in the band,
@@ -652,21 +676,35 @@ __global__ __launch_bounds__(C::NT) void wgrad_grp(const WgArgs a) {
     }
   };
 
+  // two stages: step c + 1 flies while step c computes, and a phase ends with
+  // vmcnt(0); three: steps c + 1 and c + 2 fly, and vmcnt(JPW) leaves only the
+  // newest step's transfers outstanding at the phase's end
+  constexpr int VM_END = C::NSTG == 3 ? 0x0F70 | (C::JPW & 15) | ((C::JPW >> 4) << 14) : 0x0F70;
   Step c0s = first_step();
+  Step c1s = c0s;
   fetch(stage0, c0s);
-  __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
+  if constexpr (C::NSTG == 3) {
+    c1s = next_of(c0s);
+    fetch(stage1, c1s);
+    __builtin_amdgcn_s_waitcnt(VM_END);               // step 0 is in LDS
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
+  }
   __syncthreads();
-  // one step per phase, two phases per loop turn so that the stages alternate
+  // one step per phase, NSTG phases per loop turn so that the stages rotate
   // at compile time; inside a step the (row, K step) pairs are pipelined:
   // the fragments of the next pair are read while the current pair's MFMAs run
   auto phase = [&](auto PP) __attribute__((always_inline)) {
     constexpr int par = decltype(PP)::value;
-    const char* const cur = par ? stage1 : stage0;
-    char* const nxt = par ? stage0 : stage1;
-    const Step c1s = next_of(c0s);
-    fetch(nxt, c1s);
+    const char* const cur = par == 0 ? stage0 : par == 1 ? stage1 : stage2;
+    // the stage that receives the step NSTG - 1 ahead: the one step c - 1 used
+    char* const nxt = C::NSTG == 2 ? (par ? stage0 : stage1) : (par == 0 ? stage2 : par == 1 ? stage0 : stage1);
+    Step cn;
+    if constexpr (C::NSTG == 3) cn = next_of(c1s);
+    else cn = next_of(c0s);
+    fetch(nxt, cn);
     if (mma) {
-      const int nks = (chunk_len(c0s) + 15) / 16;
+      const int nks = (chunk_len(c0s) + C::KSTEP - 1) / C::KSTEP;
       const int ng = c0s.ng;
       constexpr int NP = C::G * C::NKS;
       bf16x8 av[2][C::WM], bv[2][C::WN];
@@ -679,14 +717,23 @@ __global__ __launch_bounds__(C::NT) void wgrad_grp(const WgArgs a) {
         if (g < ng && ks < nks) mfmas(av[t & 1], bv[t & 1]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0): this wave's transfers are in LDS
+    __builtin_amdgcn_s_waitcnt(VM_END);               // this wave's transfers of the next step are in LDS
     __syncthreads();
-    c0s = c1s;
+    if constexpr (C::NSTG == 3) {
+      c0s = c1s;
+      c1s = cn;
+    } else {
+      c0s = cn;
+    }
   };
   while (c0s.valid) {
     phase(std::integral_constant<int, 0>{});
     if (!c0s.valid) break;
     phase(std::integral_constant<int, 1>{});
+    if constexpr (C::NSTG == 3) {
+      if (!c0s.valid) break;
+      phase(std::integral_constant<int, 2>{});
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
@@ -697,12 +744,14 @@ __global__ __launch_bounds__(C::NT) void wgrad_grp(const WgArgs a) {
   for (int i = 0; i < C::WM; ++i) {
 #pragma unroll
     for (int j = 0; j < C::WN; ++j) {
-      const int nn = (wn * C::WN + j) * 32 + l32;
+      // accumulator e of a lane: column lane % BM, row 8 (e / 4) + 4 (lane / 32)
+      // + e % 4 of a 32-row block, or 4 (lane / 16) + e of a 16-row one
+      const int nn = (wn * C::WN + j) * C::BM + (C::F16 ? s16 : l32);
       if (nn >= C::NRT) continue;
       const int r = nn / C::CT, c = c0 + nn % C::CT;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = (wm * C::WM + i) * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+      for (int e = 0; e < (C::F16 ? 4 : 16); ++e) {
+        const int m = (wm * C::WM + i) * C::BM + (C::F16 ? 4 * g16 + e : 8 * (e >> 2) + 4 * g2 + (e & 3));
         if (m >= C::MRT) continue;
         const int tx = m / C::OT, o = o0 + m % C::OT;
         out[((size_t)o * C::CIN + c) * C::TAPS + r * C::K + tx] = acc[i][j][e];
@@ -766,18 +815,20 @@ __global__ void wgrad_reduce(const float* __restrict__ partial, int parts, int64
 // instances and launch
 // --------------------------------------------------------------------------
 
-// Instances.  Row-by-row kernel (wgrad_tr) where its 64 (up to 80) column
-// chunks move fewer bytes per output than row groups would (k 3: a group of
-// 4 rows needs 6 of the 12 x runs, but in half-width chunks); row groups
-// (wgrad_grp) for k 5, where a group of 4 rows loads 40 x runs instead of
-// 100, and for the 256-channel layer, which needs channel tiles.  Same-box
-// A/B of the two kernels on each layer: image 0.51 / 0.84 ms, 256^3
-// 1.74 / 2.28 ms, 512^3 k5 20.6 / 14.3 ms, 256-channel grid (the earlier
-// register-staged kernel) 4.55 / 3.87 ms.
+// Instances.  The image 64->64 layer runs the row-by-row kernel (wgrad_tr:
+// 64 to 80 column chunks, three stages); the others run row groups
+// (wgrad_grp) on 16 x 16 x 32 blocks with three stages: the 16-channel k5
+// layer's 80 x 400 tile needs no padding rows then (5 x 25 blocks of 16
+// against 3 x 13 of 32, 35% of whose products were padding), and the 256^3
+// and 256-channel layers gain from the third stage.  Same-box A/B against
+// the previous instances (wgrad_tr for the 256^3 layer, 32 x 32 x 16 row
+// groups with two stages for the other two): 256^3 1.75 -> 1.67 ms, 512^3 k5
+// 14.4 -> 10.7 ms, 256-channel grid 3.89 -> 2.88 ms; the image layer on
+// 16 x 16 x 32 row groups took 0.63 ms against wgrad_tr's 0.53.
 using WtImg64 = WtCfg<2, 3, 64, 64, 2, 2, 3, 3, 1>;                     // 6 x 6 blocks, 2 x 2 waves of 3 x 3
-using WtVol32 = WtCfg<3, 3, 32, 32, 1, 3, 3, 3, 1, 1>;                  // 3 x 9 blocks, 1 x 3 waves + a loader
-using WrVol16k5 = WrCfg<3, 5, 16, 16, 16, 16, 4, 32, 1, 4, 3, 4>;      // 3 x 13 (of 16) blocks, 1 x 4 waves
-using WrImg256 = WrCfg<2, 3, 256, 256, 64, 64, 4, 32, 2, 2, 3, 3>;     // 4 x 4 channel tiles of 6 x 6 blocks
+using WrVol32F = WrCfg<3, 3, 32, 32, 32, 32, 4, 32, 1, 4, 6, 5, 0, true, 3>;       // 6 x 18 blocks of 16, 1 x 4 waves
+using WrVol16k5F = WrCfg<3, 5, 16, 16, 16, 16, 4, 32, 1, 4, 5, 7, 0, true, 3>;     // 5 x 25 blocks of 16, 1 x 4 waves
+using WrImg256F = WrCfg<2, 3, 256, 256, 64, 64, 4, 32, 2, 2, 6, 6, 0, true, 3>;    // 4 x 4 tiles of 12 x 12 blocks
 
 constexpr int kPartitions = 256;   // partial sums (workgroups per tile set): one per CU
 
@@ -804,8 +855,8 @@ WgInstance make_instance_tr() {
 }
 
 const WgInstance* find_instance(int ndim, int cin, int cout, int k) {
-  static const WgInstance table[] = {make_instance_tr<WtImg64>(), make_instance_tr<WtVol32>(),
-                                     make_instance_grp<WrVol16k5>(), make_instance_grp<WrImg256>()};
+  static const WgInstance table[] = {make_instance_tr<WtImg64>(), make_instance_grp<WrVol32F>(),
+                                     make_instance_grp<WrVol16k5F>(), make_instance_grp<WrImg256F>()};
   for (const WgInstance& w : table)
     if (w.ndim == ndim && w.cin == cin && w.cout == cout && w.k == k) return &w;
   return nullptr;
