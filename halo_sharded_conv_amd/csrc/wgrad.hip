@@ -826,7 +826,7 @@ __global__ void wgrad_reduce(const float* __restrict__ partial, int parts, int64
 // 14.4 -> 10.7 ms, 256-channel grid 3.89 -> 2.88 ms; the image layer on
 // 16 x 16 x 32 row groups took 0.63 ms against wgrad_tr's 0.53.
 using WtImg64 = WtCfg<2, 3, 64, 64, 2, 2, 3, 3, 1>;                     // 6 x 6 blocks, 2 x 2 waves of 3 x 3
-using WrVol32F = WrCfg<3, 3, 32, 32, 32, 32, 4, 32, 1, 4, 6, 5, 0, true, 3>;       // 6 x 18 blocks of 16, 1 x 4 waves
+using WrVol32F = WrCfg<3, 3, 32, 32, 32, 32, 4, 32, 2, 2, 3, 9, 0, true, 3>;       // 6 x 18 blocks of 16, 2 x 2 waves of 3 x 9
 using WrVol16k5F = WrCfg<3, 5, 16, 16, 16, 16, 4, 32, 1, 4, 5, 7, 0, true, 3>;     // 5 x 25 blocks of 16, 1 x 4 waves
 using WrImg256F = WrCfg<2, 3, 256, 256, 64, 64, 4, 32, 2, 2, 6, 6, 0, true, 3>;    // 4 x 4 tiles of 12 x 12 blocks
 
