@@ -60,8 +60,12 @@ def direct_cases():
                             groups=8, spatial=(9, 10, 11), shards=((4, 5), (10,), (6, 5)))
     e = dataclasses.replace(base, name="img_c32to48_k5", cin=32, cout=48, groups=3, ksize=5, spatial=(17, 40),
                             shards=((8, 9), (21, 19)))
+    # channel counts that are not multiples of 4: one-channel vectors in the
+    # GroupNorm kernels, 4-byte halo words, one bf16 channel per conv load
+    f = dataclasses.replace(base, name="img_c6to10_k3", cin=6, cout=10, groups=5, spatial=(15, 37),
+                            shards=((7, 8), (20, 17)))
     return {"img_c5to12_k3": a, "vol_c3to4_k5": b, "img_c48to80_k3": c, "vol_c128to128_k3": d,
-            "img_c32to48_k5": e}
+            "img_c32to48_k5": e, "img_c6to10_k3": f}
 
 
 def oracle_forward(wl, x, w, bias=None, gamma=None, beta=None):

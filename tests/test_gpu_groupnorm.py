@@ -153,7 +153,7 @@ def test_all_zero_output():
     assert np.array_equal(z, np.broadcast_to(beta, z.shape))
 
 
-@pytest.mark.parametrize("name", ["vol32_b2", "img64_b2", "vol16k5", "img_c5to12_k3", "grid256_small"])
+@pytest.mark.parametrize("name", ["vol32_b2", "img64_b2", "vol16k5", "img_c5to12_k3", "grid256_small", "img_c6to10_k3"])
 def test_combined_apply_matches_three_calls(name):
     """st_groupnorm_sharded folds the combine into the apply's prologue when
     the per-lane coefficient path applies; z and the stored (mean, rstd) must
