@@ -73,7 +73,7 @@ def parse():
 COPY_BYTES = 1 << 30                 # bytes read (and written) by --calibrate-copy
 STAGE_KERNELS = {                    # kernel-name fragments of each library stage
     "halo_pack": ("halo_copy",), "halo_unpack": ("halo_copy",), "halo_exchange": ("halo_copy",),
-    "conv": ("conv_rows", "conv_pairs", "conv_gemm", "conv_direct"),
+    "conv": ("conv_rows", "conv_taps", "conv_gemm", "conv_direct"),
     "gn_partials": ("gn_max", "gn_stats"), "gn_apply": ("gn_apply",),
     "wgrad": ("wgrad_tr", "wgrad_grp", "wgrad_direct"), "gn_backward": ("gn_max", "gnb_"), "pool": ("pool_kernel", "pool_fixed"),
     "strided": ("conv_sx_mfma", "conv_strided"), "transposed": ("conv_sx_mfma", "conv_transposed"),

@@ -15,9 +15,9 @@
 // layer shape (the instance table at the end):
 //   conv_rows  streams a strip of the shard along its outermost axis with the
 //              weights resident in LDS; 32x32x16 MFMA (64->64 and 32->32 k3)
-//   conv_pairs streams a 3D strip over the whole shard depth with 16x16
-//              channel blocks stacked two output planes per MFMA and the
-//              weights streamed per kernel row (3D 16->16 k5)
+//   conv_taps  streams a 3D strip over the whole shard depth with two
+//              in-plane taps per K step of 16x16x32 MFMA and the weights
+//              streamed in five segments of tap pairs (3D 16->16 k5)
 //   conv_gemm  tiles with the weights streamed through LDS per 16-channel K
 //              chunk, for layers whose weights do not fit in LDS (2D 256->256)
 // Each output accumulates its K-steps in an order fixed by the layer shape
@@ -32,6 +32,7 @@
 // integer atomicMax on the float bits (order-free).
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "internal.h"
 
@@ -296,22 +297,37 @@ __global__ void pack_w_gemm(const uint16_t* __restrict__ w, uint16_t* __restrict
   out[i] = w[((int64_t)(cb * bn + m) * cin + cc * ck + c) * taps + t];
 }
 
-// [Cout][Cin][kd][kh][kw] -> [kh][kd][kw][Cout][Cin]: the weights of one kernel
-// row dy are contiguous
-__global__ void pack_w_pairs(const uint16_t* __restrict__ w, uint16_t* __restrict__ out, int cin, int cout,
-                             int ks, int64_t total, uint32_t* clr, int nclr) {
+// Tap pairs of the 3D k5 tap-pair kernel: in-plane tap dy * 5 + dx in half h
+// of pair p (-1: the empty half).  Pairs 0-1 hold the taps (0, 0..3), pairs
+// 11-12 the taps (4, 0..3), pairs 2-9 the rest in lexicographic order and
+// pair 10 the tap (4, 4) alone.
+__host__ __device__ constexpr int k5_pair_tap(int p, int h) {
+  return p < 10 ? 2 * p + h : p == 10 ? (h ? -1 : 24) : 20 + 2 * (p - 11) + h;
+}
+// weight segments of 2, 3, 3, 3 and 2 pairs: first pair, count, and the
+// segment of a pair
+__host__ __device__ constexpr int k5_seg_first(int s) { return s == 0 ? 0 : s == 4 ? 11 : 3 * s - 1; }
+__host__ __device__ constexpr int k5_seg_pairs(int s) { return s == 0 || s == 4 ? 2 : 3; }
+__host__ __device__ constexpr int k5_seg_of(int p) { return p < 2 ? 0 : p < 5 ? 1 : p < 8 ? 2 : p < 11 ? 3 : 4; }
+
+// [16][16][5][5][5] -> [segment 5][pair slot 3][dz 5][lane 64][8]: the 16x32 A
+// fragment of (pair, dz) in lane order, lane 16 kg + cout holding input
+// channels 8 (kg & 1) .. + 7 of the pair's tap kg >> 1; the empty half and
+// the unused slots of two-pair segments are zero
+__global__ void pack_w_taps(const uint16_t* __restrict__ w, uint16_t* __restrict__ out, int64_t total, uint32_t* clr,
+                            int nclr) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < nclr) clr[i] = 0u;
   if (i >= total) return;
-  const int c = (int)(i % cin);
-  int64_t r = i / cin;
-  const int o = (int)(r % cout);
-  r /= cout;
-  const int dx = (int)(r % ks);
-  r /= ks;
-  const int dz = (int)(r % ks);
-  const int dy = (int)(r / ks);
-  out[i] = w[((int64_t)o * cin + c) * ks * ks * ks + (dz * ks + dy) * ks + dx];
+  const int e = (int)(i & 7);
+  const int lane = (int)((i >> 3) & 63);
+  int r = (int)(i >> 9);
+  const int dz = r % 5;
+  r /= 5;
+  const int slot = r % 3, seg = r / 3;
+  const int kg = lane >> 4, o = lane & 15, c = 8 * (kg & 1) + e;
+  const int t = slot < k5_seg_pairs(seg) ? k5_pair_tap(k5_seg_first(seg) + slot, kg >> 1) : -1;
+  out[i] = t < 0 ? (uint16_t)0 : w[((int64_t)o * 16 + c) * 125 + dz * 25 + t];
 }
 
 // [Cout][Cin][taps] -> [Cout][taps][Cin]
@@ -342,7 +358,7 @@ __global__ void dgrad_weights(const T* __restrict__ w, T* __restrict__ out, int 
 // Output layout of a 32x32 block in a lane: column (position) = lane % 32,
 // rows (channels) 8j + 4*(lane/32) + i for accumulator element 4j + i.
 //
-// Stores of conv_rows and conv_pairs: the quads j = 2c and 2c + 1 of a block
+// Stores of conv_rows: the quads j = 2c and 2c + 1 of a block
 // (channels 16c .. 16c + 15) go out as one pair.  Stored as they are (as
 // conv_gemm does: its epilogue is a small part of a tile, and the swap's
 // extra registers made it spill), each store instruction would
@@ -389,7 +405,7 @@ struct Instance {
   st_status (*run)(ConvArgs&, const st_plan*, hipStream_t);
   int bn = 0;                 // cout block of the streamed-weight layout
   int kind = 0;               // weight layout: 0 [Cin/ck][Cout][kvp]; 1 [Cout/bn][Cin/ck][tap][bn][ck];
-                              // 2 [kh][kd][kw][Cout][Cin] (plane pairs)
+                              // 3 [segment][pair slot][dz][lane][8] (tap pairs)
 };
 
 int device_cus() {
@@ -1264,61 +1280,75 @@ constexpr Instance inst_gemm() {
 }
 
 // --------------------------------------------------------------------------
-// 3D layers with 16 output channels: output-plane pairs on 32x32x16 MFMA
+// 3D layers with 16 input and 16 output channels: tap pairs on 16x16x32 MFMA
 // --------------------------------------------------------------------------
 //
-// With Cout = 16 one 32-row MFMA block would be half empty.  Here its 32
-// rows are two neighbouring output planes o, o+1 x 16 channels: the A operand
-// of input plane i stacks the weights of taps dz = i - o and dz = i - o - 1
-// (a zero block where that tap does not exist), so one input fragment (B)
-// feeds both planes.  A wave owns one row of a BH x BW strip (BW = 32
-// positions) and RW consecutive output planes (RW / 2 pairs): per in-plane tap
-// (dy, dx) it reads RW + k - 1 input fragments and k + 1 stacked weight
-// fragments for 3 RW MFMAs (83% of them useful for k = 5).  Every output
-// accumulates taps in the order (dy, dx, dz), whether it is the first or the
-// second plane of its pair; the zero blocks add exact zeros.
+// A K step of v_mfma_f32_16x16x32_bf16 holds two in-plane taps (dy, dx) x 16
+// input channels; its 16 rows are the 16 output channels and its 16 columns
+// 16 positions along W.  A wave owns one row of a BH x 32 strip (two column
+// blocks) and RW consecutive output planes.  For one tap pair it reads the
+// fragments of the RW + k - 1 input planes (B, per column block) and one
+// weight fragment per depth tap dz (A), and issues one MFMA per (output
+// plane, dz, column block): each input fragment feeds the up to k output
+// planes it reaches and each weight fragment all RW of them.  The k^2
+// in-plane taps make ceil(k^2 / 2) pairs, one with an empty half (zero
+// weights): for k = 5, 13 pairs x 80 = 1040 MFMAs of 16 cycles per step,
+// 96% of their products useful.
+//
+// Every output accumulates the pairs in one fixed order (a pair's two taps
+// inside one MFMA, then dz upwards), wherever it lies, so sharded and
+// unsharded outputs agree bit for bit.  The pair order serves the ring: the
+// first two pairs hold the taps (0, 0..3), the last two (4, 0..3), and the
+// nine between them the rest in lexicographic order, (4, 4) last and alone.
 //
 // The ring in LDS holds the TS + k - 1 input planes of one step (TS = RW, all
-// waves on the same planes); the next step's TS planes are fetched into
-// registers during the step and written over the oldest ones between two
-// barriers.  The weights (the same for every job) are streamed per kernel row
-// dy from L2 into two LDS stages by LDS-DMA, the next row's while the current
-// one is used.  A job is one strip of a shard over its whole depth.
+// waves on the same planes).  The next step's TS planes are fetched into
+// registers during the step in two halves of slice rows and written over the
+// oldest planes: rows 0-3 once the pairs left in the step read kernel row 4
+// only, rows 4-7 at the step's end.  The weights (the same for every job)
+// stream from L2 into three LDS stages by LDS-DMA in five segments of 2, 3,
+// 3, 3 and 2 pairs, segments 0-4 of every step in stages 0, 1, 2, 0, 1, each
+// fetched one or two segments ahead of its use.  A job is one strip of a
+// shard over its whole depth.
 
-template <int CIN_, int COUT_, int KS_, int BH_, int BW_, int RW_>
-struct PairsCfg {
-  static constexpr int NDIM = 3, CIN = CIN_, COUT = COUT_, KS = KS_;
-  static constexpr int BH = BH_, BW = BW_, RW = RW_, TS = RW;
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>) in order:
+// a loop whose body must see its index as a constant (the pair loop below is
+// too large for the unroller's threshold)
+template <class F, int... P>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, P...>) {
+  (f(std::integral_constant<int, P>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int BH_, int RW_>
+struct TapsCfg {
+  static constexpr int NDIM = 3, CIN = 16, COUT = 16, KS = 5;
+  static constexpr int BH = BH_, BW = 32, RW = RW_, TS = RW;
   static constexpr int SH = BH + KS - 1, SW = BW + KS - 1, SLICE = SH * SW;
   static constexpr int CB = CIN * 2;                  // bytes per input cell
   static constexpr int SLICE_B = SLICE * CB;
   static constexpr int RING = TS + KS - 1;
-  static constexpr int NPAIR = RW / 2, NE = KS + 1, NIN = RW + KS - 1;
+  static constexpr int NIN = RW + KS - 1;             // input planes of one step
   static constexpr int NWAVES = BH, NT = NWAVES * 64;
-  static constexpr int TAPS = KS * KS * KS;
-  static constexpr int WROW = KS * KS * COUT * CB;    // weight bytes of one kernel row dy: [dz][dx][cout][cin]
-  static constexpr int WSTAGE = (WROW + 1023) / 1024 * 1024;
-  static constexpr int NJ = WSTAGE / 1024;            // 1 KiB LDS-DMA transfers per weight stage
-  static constexpr int JPW = (NJ + NWAVES - 1) / NWAVES;
+  static constexpr int NPAIRS = (KS * KS + 1) / 2, NSEG = 5, SLOTS = 3;
+  static constexpr int FRAG = 1024;                   // one A fragment: 64 lanes x 16 bytes
+  static constexpr int WSTAGE = SLOTS * KS * FRAG;    // a segment's weights, [pair][dz][lane][8]
   static constexpr int LDS_X = RING * SLICE_B;
-  static constexpr int NSTAGE = 3;                    // weight stages: rows 0-4 use stages 0, 1, 2, 0, 1
-  static constexpr int LDS = LDS_X + NSTAGE * WSTAGE;
-  // the transfers past a row's weights write zeros (out-of-range lanes), so
-  // every stage ends in a zero block that stands for absent taps
-  static_assert(WSTAGE - WROW >= 32, "room for the zero block");
+  static constexpr int LDS = LDS_X + 3 * WSTAGE;
   static constexpr int STEP_CHUNKS = TS * SLICE * 2;  // 16-byte pieces of a step's new planes
   static constexpr int PF = (STEP_CHUNKS + NT - 1) / NT;
   static constexpr int PFH = PF / 2;                  // loads per half: slice rows 0-3, then rows 4-7
-  static_assert(SH == 8 && STEP_CHUNKS == 2 * PFH * NT, "halves of whole slice rows");
-  static constexpr int CK = CIN, KVP = TAPS * CIN, TD = 1, TH = BH, TW = BW, NCB = 1;
-  static_assert(CIN == 16 && COUT == 16, "one 16-channel K step per tap and 2 x 16 output rows per MFMA");
-  static_assert(KS == 5, "the weight-stage schedule is written for five kernel rows");
-  static_assert(BW == 32 && RW % 2 == 0, "tiling");
-  static_assert(NT <= 1024 && LDS + COUT * 8 <= 160 * 1024, "resources");
+  static constexpr int CK = CIN, KVP = NSEG * WSTAGE / (COUT * 2), TD = 1, TH = BH, TW = BW, NCB = 1;
+  static_assert(SH == 8 && NWAVES == 4 && STEP_CHUNKS == 2 * PFH * NT, "halves of whole slice rows");
+  static_assert(k5_seg_first(NSEG - 1) + k5_seg_pairs(NSEG - 1) == NPAIRS, "segments cover the pairs");
+  static_assert(RW >= 1 && NT <= 1024 && LDS + COUT * 8 <= 160 * 1024, "resources");
 };
 
 template <class C, bool BIAS, int MAXG>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void conv_pairs(const ConvArgs args) {
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void conv_taps(const ConvArgs args) {
   __shared__ __attribute__((aligned(1024))) char sring[C::LDS_X];
   __shared__ __attribute__((aligned(1024))) char sw0[C::WSTAGE];
   __shared__ __attribute__((aligned(1024))) char sw1[C::WSTAGE];
@@ -1329,28 +1359,36 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // the wave's row in the strip
-  const int l32 = lane & 31;
-  const int g2 = lane >> 5;
+  const int l16 = lane & 15;                          // position within a 16-column block
+  const int kg = lane >> 4;                           // K group: tap kg >> 1 of a pair, input channels
+                                                      // 8 (kg & 1) ..; output channels 4 kg .. + 3
   constexpr bool MAXV = MAXG > 0;
   constexpr int MG = MAXG > 0 ? MAXG : 1;
-  constexpr int NMX = 8 / MG;                         // running-max slots per lane (8 channels)
+  constexpr int NMX = 4 / MG;                         // running-max slots per lane (4 channels)
 
   for (int i = tid; i < C::COUT; i += C::NT) {
     smax[i] = 0u;
     sbias[i] = BIAS ? args.bias[i] : 0.f;
   }
 
-  // A rows: m = 16 p + c (p: which plane of the pair, c: output channel); the
-  // 16-byte halves of a 32-byte row swap when bit 3 of c is set
-  const int ap = l32 >> 4, ac = l32 & 15;
-  const int arow = ac * 32 + 16 * (g2 ^ ((ac >> 3) & 1));   // within a (dz, dx) block of 16 rows
-  // B: cell column of this lane for each dx, and its swapped half
+  // B: this lane's cell column in a slice row for each dx, and the half of
+  // the cell it reads (the 16-byte halves swap when bit 3 of the column is set)
   int bcol[C::KS];
 #pragma unroll
   for (int dx = 0; dx < C::KS; ++dx) {
-    const int c = l32 + dx;
-    bcol[dx] = c * 32 + 16 * (g2 ^ ((c >> 3) & 1));
+    const int c = l16 + dx;
+    bcol[dx] = c * 32 + 16 * ((kg & 1) ^ ((c >> 3) & 1));
   }
+  const bool second = kg >= 2;                        // the lane reads the pair's second tap
+  // this lane's B offset from slice row w for pair p; the empty half reads
+  // the first tap's cells (finite values times zero weights)
+  auto pair_off = [&](int p) __attribute__((always_inline)) -> int {
+    const int ta = k5_pair_tap(p, 0), t1 = k5_pair_tap(p, 1);
+    const int tb = t1 < 0 ? ta : t1;
+    const int oa = (ta / C::KS) * (C::SW * 32) + bcol[ta % C::KS];
+    const int ob = (tb / C::KS) * (C::SW * 32) + bcol[tb % C::KS];
+    return second ? ob : oa;
+  };
 
   const int total = args.total_tiles;
   int j0 = blockIdx.x, jstride = gridDim.x, j_end = total;
@@ -1373,11 +1411,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
       v = fmaxf(v, __shfl_xor(v, 2));
       v = fmaxf(v, __shfl_xor(v, 4));
       v = fmaxf(v, __shfl_xor(v, 8));
-      v = fmaxf(v, __shfl_xor(v, 16));
       runmax[i] = 0.f;
-      // slot i: channels 8 (i*MG / 4) + 4 g2 + (i*MG) % 4 .. + MG - 1
-      const int e = i * MG;
-      if (l32 == 0) atomicMax(&smax[8 * (e >> 2) + 4 * g2 + (e & 3)], __float_as_uint(v));
+      // slot i: channels 4 kg + i MG .. + MG - 1, all in one group
+      if (l16 == 0) atomicMax(&smax[4 * kg + i * MG], __float_as_uint(v));
     }
     __syncthreads();
     const int gs = C::COUT / args.groups;
@@ -1389,6 +1425,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     __syncthreads();
     for (int i = tid; i < C::COUT; i += C::NT) smax[i] = 0u;
   };
+
 
   // A job: shard s, sample n, strip (h0, w0), all planes of the shard
   // job's buffers start at its sample's first plane; each step rebases them
@@ -1468,20 +1505,18 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     sl -= sl >= C::RING ? C::RING : 0;
     return sl * C::SLICE_B + (qr * C::SW + qc) * 32 + 16 * (h ^ ((qc >> 3) & 1));
   };
-  // weights of kernel row dy -> a stage, by LDS-DMA; packed [dy][dz][dx][cout][cin]
-  auto fetch_w = [&](char* dst, int dy) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(reinterpret_cast<const char*>(args.w) + dy * C::WROW, C::WROW);
+  // weights of segment s -> a stage, by LDS-DMA: the packed segments lie
+  // WSTAGE apart, already in LDS order
+  auto fetch_w = [&](char* dst, int s) __attribute__((always_inline)) {
+    const int nj = k5_seg_pairs(s) * C::KS;           // 1 KiB transfers
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(reinterpret_cast<const char*>(args.w) + s * C::WSTAGE, nj * 1024);
     typedef __attribute__((address_space(3))) void* lds_ptr;
 #pragma unroll
-    for (int i = 0; i < C::JPW; ++i) {
+    for (int i = 0; i < (C::SLOTS * C::KS + C::NWAVES - 1) / C::NWAVES; ++i) {
       const int j = w + i * C::NWAVES;
-      if (j < C::NJ) {
-        const int slot = 64 * j + lane;
-        const int row = slot >> 1, c = row & 15;
-        const bool ok = row < C::WROW / 32;
-        const uint32_t off = ok ? (uint32_t)((row * 2 + ((slot & 1) ^ ((c >> 3) & 1))) * 16) : kOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(dst + j * 1024), 16, off, 0, 0, 0);
-      }
+      if (j < nj)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr)(dst + j * 1024), 16, (uint32_t)(j * 1024 + lane * 16),
+                                                 0, 0, 0);
     }
   };
 
@@ -1511,26 +1546,27 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     }
   };
 
+
   Job J = make_job(j0);
   if (!J.valid) return;
-  fetch_w(sw0, 0);                                    // rows 0-2 of the first step; later rows are
-  fetch_w(sw1, 1);                                    // fetched one or two rows ahead of their use
+  fetch_w(sw0, 0);                                    // segments 0-2 of the first step; later ones
+  fetch_w(sw1, 1);                                    // are fetched one or two segments ahead
   fetch_w(sw2, 2);
   prologue(J);                                        // first job's first TS + k - 1 planes
   __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
   if (MAXV) cur_n = J.n;
   __syncthreads();
 
-  f32x16 acc[C::NPAIR];
-  bf16x8 av[2][C::NE];                                // stacked weights, double-buffered by phase parity
-  bf16x8 bv[C::NIN];                                  // input fragments, each reloaded after its last use
+  f32x4 acc[C::RW][2];                                // [output plane][column block]
+  bf16x8 av[2][C::KS];                                // weights per dz, double-buffered by pair parity
+  bf16x8 bv[C::NIN][2];                               // input fragments, each reloaded after its last use
   uint4 pf[C::PFH];                                   // half of the next step's planes
   uint32_t pfo[C::PF];                                // their offsets from the step's first plane
 #pragma unroll
   for (int k = 0; k < C::PF; ++k) pfo[k] = step_off(J, tid + k * C::NT);
   int job = j0;
   int cur = 0;                                        // first output plane of the step
-  constexpr int NS = 4 * C::NPAIR;                    // stores of one step's epilogue
+  constexpr int NS = 2 * C::RW;                       // stores of one step's epilogue
   for (;;) {
     const bool more = cur + C::TS < J.depth;
     const __amdgpu_buffer_rsrc_t rin = in_rsrc(J, cur, more);   // no planes to fetch in a job's last step
@@ -1544,167 +1580,155 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
       sl -= sl >= C::RING ? C::RING : 0;
       sbase[r] = sl * C::SLICE_B + w * (C::SW * 32);
     }
-    // kernel row -> weight stage, the same in every step, so that every LDS
+    // segment -> weight stage, the same in every step, so that every LDS
     // address below names its stage at compile time
-    auto stage = [&](int row) __attribute__((always_inline)) -> char* {
-      return row % 3 == 0 ? sw0 : row % 3 == 1 ? sw1 : sw2;
+    auto stage = [&](int s) __attribute__((always_inline)) -> char* {
+      return s % 3 == 0 ? sw0 : s % 3 == 1 ? sw1 : sw2;
     };
-    // one base array per read (the stage, whose tail is the zero block), so
-    // the compiler can tell it apart from the transfers into other stages
-    auto load_a = [&](int buf, int row, int dx, int e) __attribute__((always_inline)) {
-      const int dz = e - ap;
-      const int off = (dz >= 0 && dz < C::KS) ? (dz * C::KS + dx) * (16 * 32) + arow : C::WROW + 16 * g2;
-      av[buf][e] = *reinterpret_cast<const bf16x8*>(stage(row) + off);
+    auto load_a = [&](int buf, int p, int dz) __attribute__((always_inline)) {
+      const int s = k5_seg_of(p);
+      const int off = ((p - k5_seg_first(s)) * C::KS + dz) * C::FRAG + lane * 16;
+      av[buf][dz] = *reinterpret_cast<const bf16x8*>(stage(s) + off);
     };
-    // the row base goes through an opaque scalar so that the compiler forms
+    // the plane base goes through an opaque scalar so that the compiler forms
     // each address right before its read instead of keeping one register per
-    // (plane, dx) alive across the whole step
-    auto load_b = [&](int i, int dy, int dx) __attribute__((always_inline)) {
-      int rb = sbase[i] + dy * (C::SW * 32);
+    // (plane, pair) alive across the whole step
+    auto load_b = [&](int i, int nb, int po) __attribute__((always_inline)) {
+      int rb = sbase[i];
       asm volatile("" : "+s"(rb));
-      bv[i] = *reinterpret_cast<const bf16x8*>(sring + rb + bcol[dx]);
+      bv[i][nb] = *reinterpret_cast<const bf16x8*>(sring + rb + po + nb * 512);
     };
 
-    // step start (row 1's weights are on their way): rows 0-3 of the next
-    // step's planes, then the first phase's operands
+    // step start (segment 1's weights are on their way): rows 0-3 of the
+    // next step's planes, then pair 0's operands
 #pragma unroll
     for (int k = 0; k < C::PFH; ++k)
       pf[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rin, pfo[k], 0, 0));
+    {
+      const int po = pair_off(0);
 #pragma unroll
-    for (int e = 0; e < C::NE; ++e) load_a(0, 0, 0, e);
+      for (int dz = 0; dz < C::KS; ++dz) load_a(0, 0, dz);
 #pragma unroll
-    for (int i = 0; i < C::NIN; ++i) load_b(i, 0, 0);
-
-    // KS * KS phases (dy, dx); phase p issues the LDS reads of phase p + 1
-    // between its MFMAs: input fragment i right after its last use, the
-    // stacked weights into the other buffer
-#pragma unroll
-    for (int dy = 0; dy < C::KS; ++dy) {
-#pragma unroll
-      for (int dx = 0; dx < C::KS; ++dx) {
-        const int ph = dy * C::KS + dx;
-        const int cb = ph & 1;
-        const bool last = ph == C::KS * C::KS - 1;
-        const int ndy = dx + 1 < C::KS ? dy : dy + 1;
-        const int ndx = dx + 1 < C::KS ? dx + 1 : 0;
-        __builtin_amdgcn_sched_barrier(0);
-        if (dx == C::KS - 1 && dy + 1 < C::KS) {
-          // row dy + 1 must be complete on every wave before phase
-          // (dy + 1, 0)'s operands are read, and past the barrier every
-          // wave's reads of row dy's stage are done, so that stage takes the
-          // next row that uses it:
-          //   dy 0: row 3 -> stage 0     dy 1: row 4 -> stage 1
-          //   dy 2: next step's row 2 -> stage 2
-          //   dy 3: next step's row 0 -> stage 0 (row 1 follows at step start)
-          // Waits: row 1 was fetched just before the previous step's NS
-          // stores and this step's PFH plane loads; row 2 is older than row
-          // 1; rows 3 and 4 each have one later fetch (3 or 4 transfers per
-          // wave) behind them.
-          constexpr int JMIN = C::NJ / C::NWAVES;
-          constexpr int W0 = NS + C::PFH;
-          if (dy == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (W0 & 15) | ((W0 >> 4) << 14));
-          else if (dy >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (JMIN & 15) | ((JMIN >> 4) << 14));
-          __syncthreads();
-          __builtin_amdgcn_sched_barrier(0);
-          if (dy == 0) fetch_w(sw0, 3);
-          else if (dy == 1) fetch_w(sw1, 4);
-          else if (dy == 2) fetch_w(sw2, 2);
-          if (dy == 3) {
-            // ring rows 0-3 are done: the fetched rows 0-3 of the next
-            // step's planes go over the oldest planes, and rows 4-7 start
-            if (more) {
-#pragma unroll
-              for (int k = 0; k < C::PFH; ++k)
-                *reinterpret_cast<uint4*>(sring + step_lds(tid + k * C::NT, base)) = pf[k];
-            }
-            fetch_w(sw0, 0);
-#pragma unroll
-            for (int k = 0; k < C::PFH; ++k)
-              pf[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rin, pfo[C::PFH + k], 0, 0));
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < C::NIN; ++i) {
-#pragma unroll
-          for (int q = 0; q < C::NPAIR; ++q) {
-            const int e = i - 2 * q;
-            if (e >= 0 && e < C::NE) {
-              if (ph == 0 && e == 0)
-                acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cb][e], bv[i], f32x16{}, 0, 0, 0);
-              else
-                acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cb][e], bv[i], acc[q], 0, 0, 0);
-            }
-          }
-          if (!last) {
-            load_b(i, ndy, ndx);
-            if (i < C::NE) load_a(cb ^ 1, ndy, ndx, i);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int i = 0; i < C::NIN; ++i) {
+        load_b(i, 0, po);
+        load_b(i, 1, po);
       }
     }
 
-    // every wave is done with row 4's stage, and the next step's row 0
-    // (fetched at row 3) and planes are complete: row 1 goes to stage 1
-    // ahead of the stores, so that waiting for it never waits for them
+    // pair p issues the LDS reads of pair p + 1 between its MFMAs: input
+    // fragment (i, nb) right after its last use, the weights into the other
+    // buffer.  Inside a pair the compiler schedules freely (a scheduling
+    // barrier per input plane, as the 32x32 kernels keep, cost 3.5% here).
+    static_for<C::NPAIRS>([&](auto pc) __attribute__((always_inline)) {
+      constexpr int p = decltype(pc)::value;
+      const int cb = p & 1;
+      const bool last = p == C::NPAIRS - 1;
+      __builtin_amdgcn_sched_barrier(0);
+      const int s = k5_seg_of(p);
+      if (s < C::NSEG - 1 && p == k5_seg_first(s) + k5_seg_pairs(s) - 1) {
+        // the last pair of segment s: segment s + 1 must be complete on every
+        // wave before this pair reads the next pair's weights, and past the
+        // barrier every wave's reads of segment s's stage are done (this
+        // pair's operands are in registers), so that stage takes the next
+        // segment that uses it:
+        //   s 0: segment 3 -> stage 0     s 1: segment 4 -> stage 1
+        //   s 2: next step's segment 2 -> stage 2
+        //   s 3: next step's segment 0 -> stage 0 (segment 1 follows at step end)
+        // Waits: segment 1 was fetched just before the previous step's NS
+        // stores and this step's PFH plane loads; segment 2 is older than
+        // segment 1; segments 3 and 4 each have one later fetch (segment 4's
+        // or the next segment 2's, nj / 4 transfers per wave or more) behind them.
+        constexpr int W0 = NS + C::PFH;
+        constexpr int W3 = k5_seg_pairs(4) * C::KS / C::NWAVES;
+        constexpr int W4 = k5_seg_pairs(2) * C::KS / C::NWAVES;
+        if (s == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (W0 & 15) | ((W0 >> 4) << 14));
+        else if (s == 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (W3 & 15) | ((W3 >> 4) << 14));
+        else if (s == 3) __builtin_amdgcn_s_waitcnt(0x0F70 | (W4 & 15) | ((W4 >> 4) << 14));
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        if (s == 0) fetch_w(sw0, 3);
+        else if (s == 1) fetch_w(sw1, 4);
+        else if (s == 2) fetch_w(sw2, 2);
+        else {
+          // only kernel row 4 is left (slice rows w + 4): the fetched rows
+          // 0-3 of the next step's planes go over the oldest planes, and rows
+          // 4-7 start
+          if (more) {
+#pragma unroll
+            for (int k = 0; k < C::PFH; ++k)
+              *reinterpret_cast<uint4*>(sring + step_lds(tid + k * C::NT, base)) = pf[k];
+          }
+          fetch_w(sw0, 0);
+#pragma unroll
+          for (int k = 0; k < C::PFH; ++k)
+            pf[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rin, pfo[C::PFH + k], 0, 0));
+        }
+      }
+      const int po = last ? 0 : pair_off(p + 1);
+#pragma unroll
+      for (int i = 0; i < C::NIN; ++i) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+          for (int dz = 0; dz < C::KS; ++dz) {
+            const int o = i - dz;
+            if (o >= 0 && o < C::RW) {
+              if (p == 0 && dz == 0)
+                acc[o][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[cb][dz], bv[i][nb], f32x4{}, 0, 0, 0);
+              else
+                acc[o][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[cb][dz], bv[i][nb], acc[o][nb], 0, 0, 0);
+            }
+          }
+          if (!last) load_b(i, nb, po);
+        }
+        if (!last && i < C::KS) load_a(cb ^ 1, p + 1, i);
+      }
+    });
+
+    // every wave is done with segment 4's stage, and the next step's segment
+    // 0 (fetched at segment 3) and planes are complete: segment 1 goes to
+    // stage 1 ahead of the stores, so that waiting for it never waits for them
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     fetch_w(sw1, 1);
 
-    // epilogue: pair q covers planes cur + 2q (rows 0-15) and cur + 2q + 1;
-    // planes past the shard fall outside the output descriptor's range.
-    // Bias and the running max are taken in the MFMA layout, then swap16
-    // turns each plane's two channel quads into two stores of 16 whole
-    // 64-byte cells (1 KiB in a row).
+    // epilogue: lane (kg, l16) of acc[o][nb] holds output channels 4 kg .. + 3
+    // of position 16 nb + l16 in plane cur + o, so each store writes 16 whole
+    // 64-byte cells (1 KiB in a row); planes past the shard fall outside the
+    // output descriptor's range
     {
       const int oh = J.h0 + w;
       const int64_t row_cell = (int64_t)oh * J.e2 + J.w0;
       const bool row_in = oh < J.e1;
-      const bool in_plane = row_in && J.w0 + l32 < J.e2;      // this lane's position before the swap
-      const int t16 = lane & 15, r16 = lane >> 4;
-      const int sch = SWAP_QUAD(r16);                       // channel quad after the swap
-      const bool okx = row_in && J.w0 + t16 < J.e2;
-      const bool oky = row_in && J.w0 + 16 + t16 < J.e2;
+      float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (BIAS) b4 = *reinterpret_cast<const float4*>(&sbias[4 * kg]);
 #pragma unroll
-      for (int q = 0; q < C::NPAIR; ++q)
+      for (int nb = 0; nb < 2; ++nb) {
+        const bool col_in = row_in && J.w0 + 16 * nb + l16 < J.e2;
+        const uint32_t cell_b = (uint32_t)((row_cell + 16 * nb + l16) * (C::COUT * 4)) + 16 * kg;
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int plane = cur + 2 * q + p;
-          const bool real = in_plane && plane < J.depth;
-          f32x4 v[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int co = 8 * h + 4 * g2;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[h][i] = acc[q][8 * p + 4 * h + i];
-            if (BIAS) {
-              const float4 b4 = *reinterpret_cast<const float4*>(&sbias[co]);
-              v[h][0] += b4.x; v[h][1] += b4.y; v[h][2] += b4.z; v[h][3] += b4.w;
-            }
-            if (MAXV) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int slot = (4 * h + i) / MG;
-                runmax[slot] = fmaxf(runmax[slot], real ? fabsf(v[h][i]) : 0.f);
-              }
-            }
+        for (int o = 0; o < C::RW; ++o) {
+          f32x4 v = acc[o][nb];
+          if (BIAS) {
+            v[0] += b4.x; v[1] += b4.y; v[2] += b4.z; v[3] += b4.w;
           }
-          swap16(v[0], v[1]);
-          const uint32_t pb = (uint32_t)(plane - cur) * J.out_plane_b + (uint32_t)(sch * 16);
-          const uint32_t offx = okx ? pb + (uint32_t)((row_cell + t16) * (C::COUT * 4)) : kOob;
-          const uint32_t offy = oky ? pb + (uint32_t)((row_cell + 16 + t16) * (C::COUT * 4)) : kOob;
-          // non-temporal (cache policy NT): the 512^3 k5 step 14.34 -> 14.21 ms, the
-          // conv itself -0.4% (on the image layer's conv_rows the same hint cost 4.5%)
-          __builtin_amdgcn_raw_buffer_store_b128(v[0], rout, offx, 0, 2);
-          __builtin_amdgcn_raw_buffer_store_b128(v[1], rout, offy, 0, 2);
+          if (MAXV) {
+            const bool real = col_in && cur + o < J.depth;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) runmax[e / MG] = fmaxf(runmax[e / MG], real ? fabsf(v[e]) : 0.f);
+          }
+          const uint32_t off = col_in ? (uint32_t)o * J.out_plane_b + cell_b : kOob;
+          // non-temporal (cache policy NT), as the streamed outputs elsewhere
+          __builtin_amdgcn_raw_buffer_store_b128(v, rout, off, 0, 2);
         }
+      }
     }
 
     if (more) {
       // rows 4-7 of the fetched planes over the oldest TS.  No barrier
       // follows: until its first barrier the next step reads only slice
-      // rows 0-3 (wave w reads row w + dy, dy = 0), and every wave's writes
-      // are complete (lgkmcnt(0)) before that barrier.
+      // rows 0-3 (its first two pairs are kernel row 0: wave w reads row w),
+      // and every wave's writes are complete (lgkmcnt(0)) before that barrier.
 #pragma unroll
       for (int k = 0; k < C::PFH; ++k)
         *reinterpret_cast<uint4*>(sring + step_lds(tid + (C::PFH + k) * C::NT, base)) = pf[k];
@@ -1722,7 +1746,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
 #pragma unroll
       for (int k = 0; k < C::PF; ++k) pfo[k] = step_off(J, tid + k * C::NT);
       // the new job's first planes go over the whole ring (every wave is
-      // past the step's last reads: the barrier after the K loop)
+      // past the step's last reads: the barrier after the pairs)
       prologue(J);
       __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
       __syncthreads();
@@ -1732,7 +1756,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
 }
 
 template <class C>
-st_status run_pairs(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
+st_status run_taps(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
   int jobs = 0;
   for (size_t s = 0; s < in_plan->shards.size(); ++s) {
     const Shard& sd = in_plan->shards[s];
@@ -1741,7 +1765,7 @@ st_status run_pairs(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
     const int64_t in_plane_b = (int64_t)sd.pad[1] * sd.pad[2] * C::CIN * 2;
     const int64_t out_plane_b = (int64_t)sd.ext[1] * sd.ext[2] * C::COUT * 4;
     if (in_plane_b * (C::RING + C::TS) >= 0x7FFFFFFF || out_plane_b * C::TS >= 0x7FFFFFFF)
-      return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: shard planes too large for the plane-pair kernel");
+      return fail(ST_ERR_UNSUPPORTED, "st_conv_sharded: shard planes too large for the tap-pair kernel");
     sh.tiles_d = 1;
     sh.tiles_h = (int)((sd.ext[1] + C::BH - 1) / C::BH);
     sh.tiles_w = (int)((sd.ext[2] + C::BW - 1) / C::BW);
@@ -1758,29 +1782,29 @@ st_status run_pairs(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
   const int g = a.ymax == nullptr ? 0 : gs % 4 == 0 ? 4 : gs % 2 == 0 ? 2 : 1;
   const dim3 gd(grid), bd(C::NT);
   if (a.bias) {
-    if (g == 4) hipLaunchKernelGGL((conv_pairs<C, true, 4>), gd, bd, 0, stream, a);
-    else if (g == 2) hipLaunchKernelGGL((conv_pairs<C, true, 2>), gd, bd, 0, stream, a);
-    else if (g == 1) hipLaunchKernelGGL((conv_pairs<C, true, 1>), gd, bd, 0, stream, a);
-    else hipLaunchKernelGGL((conv_pairs<C, true, 0>), gd, bd, 0, stream, a);
+    if (g == 4) hipLaunchKernelGGL((conv_taps<C, true, 4>), gd, bd, 0, stream, a);
+    else if (g == 2) hipLaunchKernelGGL((conv_taps<C, true, 2>), gd, bd, 0, stream, a);
+    else if (g == 1) hipLaunchKernelGGL((conv_taps<C, true, 1>), gd, bd, 0, stream, a);
+    else hipLaunchKernelGGL((conv_taps<C, true, 0>), gd, bd, 0, stream, a);
   } else {
-    if (g == 4) hipLaunchKernelGGL((conv_pairs<C, false, 4>), gd, bd, 0, stream, a);
-    else if (g == 2) hipLaunchKernelGGL((conv_pairs<C, false, 2>), gd, bd, 0, stream, a);
-    else if (g == 1) hipLaunchKernelGGL((conv_pairs<C, false, 1>), gd, bd, 0, stream, a);
-    else hipLaunchKernelGGL((conv_pairs<C, false, 0>), gd, bd, 0, stream, a);
+    if (g == 4) hipLaunchKernelGGL((conv_taps<C, false, 4>), gd, bd, 0, stream, a);
+    else if (g == 2) hipLaunchKernelGGL((conv_taps<C, false, 2>), gd, bd, 0, stream, a);
+    else if (g == 1) hipLaunchKernelGGL((conv_taps<C, false, 1>), gd, bd, 0, stream, a);
+    else hipLaunchKernelGGL((conv_taps<C, false, 0>), gd, bd, 0, stream, a);
   }
-  return launch_check("st_conv_sharded: conv_pairs launch");
+  return launch_check("st_conv_sharded: conv_taps launch");
 }
 
 template <class C>
-constexpr Instance inst_pairs() {
+constexpr Instance inst_taps() {
   return Instance{C::NDIM, C::CIN, C::COUT, C::KS, C::CK, C::KVP, C::NT,
-                  1, C::BH, C::BW, 1, C::LDS, &run_pairs<C>, 0, 2};
+                  1, C::BH, C::BW, 1, C::LDS, &run_taps<C>, 0, 3};
 }
 
 // 2D 256->256 k3: 4x96 output tiles x 128 output channels, 16-channel K chunks
 using GemmImg256 = GemmCfg<256, 256, 3, 4, 96, 128>;
-// 3D 16->16 k5: 4x32 strips, 8 output planes per step (4 pairs per wave), whole shard depth per job
-using PairsVol16k5 = PairsCfg<16, 16, 5, 4, 32, 8>;
+// 3D 16->16 k5: 4x32 strips, 8 output planes per step, whole shard depth per job
+using TapsVol16k5 = TapsCfg<4, 8>;
 // 2D 64->64 k3: 64-column strips, 8 rows per step (4 per wave), 32 or 24 rows per job, 4
 // waves, two passes over K per step (32 output channels each)
 using RowsImg64 = RowsCfg<2, 64, 64, 3, 1, 64, 8, 32, 4, 2>;
@@ -1846,7 +1870,7 @@ constexpr Instance inst_rows_with(st_status (*run)(ConvArgs&, const st_plan*, hi
 const Instance kInstances[] = {
     inst_rows_with<RowsImg64>(&run_rows_img64),
     inst_rows<RowsVol32>(),
-    inst_pairs<PairsVol16k5>(),
+    inst_taps<TapsVol16k5>(),
     inst_gemm<GemmImg256>(),
 };
 
@@ -1869,9 +1893,9 @@ st_status pack_weights(int ndim, int cin, int cout, int ksize, st_dtype dtype, c
     const uint16_t* w = static_cast<const uint16_t*>(weight);
     uint16_t* out = static_cast<uint16_t*>(packed);
     if (const Instance* i = find_instance(ndim, cin, cout, ksize)) {
-      if (i->kind == 2) {
-        const int64_t total = (int64_t)cout * taps * cin;
-        hipLaunchKernelGGL(pack_w_pairs, grid(total), dim3(256), 0, st, w, out, cin, cout, ksize, total, clr, nclr);
+      if (i->kind == 3) {
+        const int64_t total = (int64_t)(cin / i->ck) * cout * i->kvp;
+        hipLaunchKernelGGL(pack_w_taps, grid(total), dim3(256), 0, st, w, out, total, clr, nclr);
         return launch_check(what.c_str());
       }
       if (i->kind == 1) {
