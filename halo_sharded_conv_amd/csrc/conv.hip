@@ -312,7 +312,7 @@ __host__ __device__ constexpr int k5_seg_of(int p) { return p < 2 ? 0 : p < 5 ? 
 
 // [16][16][5][5][5] -> [segment 5][pair slot 3][dz 5][lane 64][8]: the 16x32 A
 // fragment of (pair, dz) in lane order, lane 16 kg + cout holding input
-// channels 8 (kg & 1) .. + 7 of the pair's tap kg >> 1; the empty half and
+// channels 8 (kg >> 1) .. + 7 of the pair's tap kg & 1; the empty half and
 // the unused slots of two-pair segments are zero
 __global__ void pack_w_taps(const uint16_t* __restrict__ w, uint16_t* __restrict__ out, int64_t total, uint32_t* clr,
                             int nclr) {
@@ -325,8 +325,8 @@ __global__ void pack_w_taps(const uint16_t* __restrict__ w, uint16_t* __restrict
   const int dz = r % 5;
   r /= 5;
   const int slot = r % 3, seg = r / 3;
-  const int kg = lane >> 4, o = lane & 15, c = 8 * (kg & 1) + e;
-  const int t = slot < k5_seg_pairs(seg) ? k5_pair_tap(k5_seg_first(seg) + slot, kg >> 1) : -1;
+  const int kg = lane >> 4, o = lane & 15, c = 8 * (kg >> 1) + e;
+  const int t = slot < k5_seg_pairs(seg) ? k5_pair_tap(k5_seg_first(seg) + slot, kg & 1) : -1;
   out[i] = t < 0 ? (uint16_t)0 : w[((int64_t)o * 16 + c) * 125 + dz * 25 + t];
 }
 
@@ -1360,8 +1360,10 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // the wave's row in the strip
   const int l16 = lane & 15;                          // position within a 16-column block
-  const int kg = lane >> 4;                           // K group: tap kg >> 1 of a pair, input channels
-                                                      // 8 (kg & 1) ..; output channels 4 kg .. + 3
+  // K group: tap kg & 1 of a pair, input channels 8 (kg >> 1) .. + 7 (lanes
+  // 0-31 read the first halves of both taps' cells: 6.5x fewer LDS bank
+  // conflict cycles than tap-major K groups); output channels 4 kg .. + 3
+  const int kg = lane >> 4;
   constexpr bool MAXV = MAXG > 0;
   constexpr int MG = MAXG > 0 ? MAXG : 1;
   constexpr int NMX = 4 / MG;                         // running-max slots per lane (4 channels)
@@ -1377,9 +1379,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
 #pragma unroll
   for (int dx = 0; dx < C::KS; ++dx) {
     const int c = l16 + dx;
-    bcol[dx] = c * 32 + 16 * ((kg & 1) ^ ((c >> 3) & 1));
+    bcol[dx] = c * 32 + 16 * ((kg >> 1) ^ ((c >> 3) & 1));
   }
-  const bool second = kg >= 2;                        // the lane reads the pair's second tap
+  const bool second = (kg & 1) != 0;                  // the lane reads the pair's second tap
   // this lane's B offset from slice row w for pair p; the empty half reads
   // the first tap's cells (finite values times zero weights)
   auto pair_off = [&](int p) __attribute__((always_inline)) -> int {
