@@ -95,7 +95,7 @@ def test_unfused_max_gives_same_bits(name):
 
 @pytest.mark.parametrize("name,groups", [("img64_small", 64), ("img64_small", 16), ("img64_b2", 1),
                                          ("vol32_grid", 32), ("vol32_grid", 16), ("vol32_grid", 4),
-                                         ("vol16k5", 16), ("grid256_small", 128)])
+                                         ("vol16k5", 16), ("vol16k5", 8), ("grid256_small", 128)])
 def test_fused_max_every_group_size(name, groups):
     """The conv epilogue keeps its running max|y| per 1, 2 or 4 channels,
     whichever divides the group size; every granularity must give the same
