@@ -309,6 +309,29 @@ __host__ __device__ constexpr int k5_pair_tap(int p, int h) {
 __host__ __device__ constexpr int k5_seg_first(int s) { return s == 0 ? 0 : s == 4 ? 11 : 3 * s - 1; }
 __host__ __device__ constexpr int k5_seg_pairs(int s) { return s == 0 || s == 4 ? 2 : 3; }
 __host__ __device__ constexpr int k5_seg_of(int p) { return p < 2 ? 0 : p < 5 ? 1 : p < 8 ? 2 : p < 11 ? 3 : 4; }
+// the tables' contract: every in-plane tap in exactly one half; pairs 0-1
+// read kernel row 0 only and pairs 11-12 kernel row 4 only (the ring
+// protocol); the segments tile the 13 pairs in order
+constexpr bool k5_tables_ok() {
+  int seen[25] = {};
+  for (int p = 0; p < 13; ++p)
+    for (int h = 0; h < 2; ++h) {
+      const int t = k5_pair_tap(p, h);
+      if (t < -1 || t > 24) return false;
+      if (t >= 0) ++seen[t];
+      if (t >= 0 && p < 2 && t / 5 != 0) return false;
+      if (t >= 0 && p > 10 && t / 5 != 4) return false;
+    }
+  for (int t = 0; t < 25; ++t)
+    if (seen[t] != 1) return false;
+  for (int s = 0, p = 0; s < 5; p += k5_seg_pairs(s), ++s) {
+    if (k5_seg_first(s) != p) return false;
+    for (int q = p; q < p + k5_seg_pairs(s); ++q)
+      if (k5_seg_of(q) != s) return false;
+  }
+  return k5_seg_first(4) + k5_seg_pairs(4) == 13;
+}
+static_assert(k5_tables_ok(), "tap-pair and segment tables");
 
 // [16][16][5][5][5] -> [segment 5][pair slot 3][dz 5][lane 64][8]: the 16x32 A
 // fragment of (pair, dz) in lane order, lane 16 kg + cout holding input
