@@ -60,6 +60,7 @@ struct ConvArgs {
   const uint16_t* w;          // packed weights
   const float* bias;          // or null
   uint32_t* ymax;             // or null
+  int32_t xcd_begin[9];       // conv_taps: first job of each XCD's range, [8] = total_tiles
   ConvShardArg sh[ST_MAX_SHARDS];
 };
 static_assert(sizeof(ConvArgs) <= kMaxKernargBytes, "kernel argument struct too large");
@@ -1415,13 +1416,16 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     return second ? ob : oa;
   };
 
-  const int total = args.total_tiles;
-  int j0 = blockIdx.x, jstride = gridDim.x, j_end = total;
+  // jobs are dealt per XCD (workgroup b runs on XCD b mod 8): XCD x takes the
+  // contiguous range [xcd_begin[x], xcd_begin[x + 1]), which the host cuts at
+  // equal cost (a job streams its shard's whole depth, and shards differ in
+  // depth), strided over that XCD's workgroups
+  int j0 = blockIdx.x, jstride = gridDim.x, j_end = args.total_tiles;
   if (gridDim.x >= 8 && (gridDim.x & 7) == 0) {
     const int xcd = blockIdx.x & 7;
-    j0 = (int)((int64_t)total * xcd / 8) + (blockIdx.x >> 3);
+    j0 = args.xcd_begin[xcd] + (blockIdx.x >> 3);
     jstride = gridDim.x >> 3;
-    j_end = (int)((int64_t)total * (xcd + 1) / 8);
+    j_end = args.xcd_begin[xcd + 1];
   }
 
   float runmax[NMX];
@@ -1812,6 +1816,33 @@ st_status run_taps(ConvArgs& a, const st_plan* in_plan, hipStream_t stream) {
   if (jobs == 0) return ST_OK;
   int grid = std::min(jobs, device_cus());
   if (grid >= 8) grid &= ~7;
+  // cut the job list into 8 contiguous ranges of equal cost: a job costs its
+  // steps (its shard's depth over TS, rounded up) plus about a quarter step
+  // for the job switch; with the 512^3 volume's eight depth shards (54-79
+  // planes) equal job counts left the XCD of the deepest shard 19% above the
+  // mean
+  {
+    auto cost = [&](size_t s) { return 4 * (((int64_t)in_plan->shards[s].ext[0] + C::TS - 1) / C::TS) + 1; };
+    int64_t total_cost = 0;
+    for (size_t s = 0; s < in_plan->shards.size(); ++s)
+      total_cost += cost(s) * ((int64_t)in_plan->batch * a.sh[s].tiles_h * a.sh[s].tiles_w);
+    a.xcd_begin[0] = 0;
+    a.xcd_begin[8] = jobs;
+    for (int x = 1; x < 8; ++x) {
+      const int64_t target = total_cost * x / 8;
+      int64_t cum = 0;
+      int32_t at = jobs;
+      for (size_t s = 0; s < in_plan->shards.size(); ++s) {
+        const int64_t n = (int64_t)in_plan->batch * a.sh[s].tiles_h * a.sh[s].tiles_w, c = cost(s);
+        if (cum + n * c >= target) {
+          at = a.sh[s].tile_begin + (int32_t)std::min<int64_t>(n, (target - cum + c - 1) / c);
+          break;
+        }
+        cum += n * c;
+      }
+      a.xcd_begin[x] = std::max(a.xcd_begin[x - 1], std::min(at, jobs));
+    }
+  }
   const int gs = a.ymax ? C::COUT / a.groups : 0;
   const int g = a.ymax == nullptr ? 0 : gs % 4 == 0 ? 4 : gs % 2 == 0 ? 2 : 1;
   const dim3 gd(grid), bd(C::NT);
